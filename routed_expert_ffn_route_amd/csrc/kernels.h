@@ -1,0 +1,61 @@
+// kernels.h -- launch interfaces between the host library and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace moe {
+
+// Arguments of the single-launch batch-1 layer kernel.
+struct B1Args {
+  const float* x;                       // [H]
+  const void* router;                   // [E][H]
+  const void* gate;                     // [E][I][H]
+  const void* up;
+  const void* down_t;
+  const uint8_t* gate_s;                // MXFP4 scales or null
+  const uint8_t* up_s;
+  const uint8_t* down_s;
+  const void* sh_gate;                  // [NS][IS][H]
+  const void* sh_up;
+  const void* sh_down_t;
+  const int32_t* ids_in;                // given routing [k] or null
+  const float* w_in;
+  float* logits_ws;                     // [E]
+  int32_t* ids_ws;                      // [k]
+  float* w_ws;                          // [k]
+  float* partials;                      // [P][H]
+  float* y;                             // [H]
+  Ctrl* ctrl;
+  int H, E, k, I, NS, IS;
+  int route_inside;
+};
+
+hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int workgroups, int threads,
+                     hipStream_t s);
+int b1_lds_bytes(int H, int threads, int E, int k);
+
+// Routing: router GEMV for B tokens, then one workgroup per token for top-k + softmax.
+struct RouteArgs {
+  const float* x;          // [B][H] or null
+  const float* logits_in;  // [B][E] or null
+  const void* router;      // [E][H]
+  float* logits;           // [B][E] (workspace or caller's logits_out)
+  int32_t* ids;            // [B][k]
+  float* w;                // [B][k]
+  int H, E, k, B;
+};
+hipError_t launch_route(const RouteArgs& a, DT rt, hipStream_t s);
+
+// Touched-expert union: one workgroup.
+hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touched,
+                        int32_t* touched, int32_t* offsets, int32_t* slots, Ctrl* ctrl,
+                        hipStream_t s);
+int union_lds_bytes(int B, int E);
+
+// Load-time preparation: ||d_j||_2 of every row of a stacked [rows][H] tensor.
+hipError_t launch_row_norms(const void* rows_base, const uint8_t* scales, DT dt, size_t rows,
+                            int H, float* out, hipStream_t s);
+
+}  // namespace moe

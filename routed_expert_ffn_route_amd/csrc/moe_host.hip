@@ -1,0 +1,359 @@
+// moe_host.hip -- the C ABI: argument validation, workspace layout, launch selection.
+// Validation happens on the host before any HIP call; no call allocates device memory.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "../../include/moe_ffn.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status device_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxWorkgroups = 512;   // partial-sum rows reserved in the workspace
+constexpr int kThreads = 1024;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Layout {
+  size_t ctrl, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
+      union_slots, total;
+};
+
+bool desc_valid(const moe_layer_desc* d, std::string* why) {
+  char buf[256];
+  auto bad = [&](const char* m) {
+    if (why) *why = m;
+    return false;
+  };
+  if (!d) return bad("null descriptor");
+  if (d->hidden < 32 || d->hidden % 32 != 0 || d->hidden > 16384)
+    return bad("hidden must be a multiple of 32 in [32, 16384]");
+  if (d->n_experts < 1 || d->n_experts > 4096) return bad("n_experts must be in [1, 4096]");
+  if (d->top_k < 1 || d->top_k > d->n_experts) return bad("top_k must be in [1, n_experts]");
+  if (d->top_k > 32 && d->n_experts > 64)
+    return bad("top_k above 32 needs n_experts <= 64");
+  if (d->inter < 8 || d->inter % 8 != 0) return bad("inter must be a positive multiple of 8");
+  if (d->kind != MOE_EXPERT_SWIGLU && d->kind != MOE_EXPERT_LINEAR) return bad("bad kind");
+  if (d->max_batch < 1 || d->max_batch > 4096) return bad("max_batch must be in [1, 4096]");
+  if (d->router_dtype != MOE_DTYPE_NONE && d->router_dtype != MOE_F32 &&
+      d->router_dtype != MOE_BF16)
+    return bad("router_dtype must be NONE, F32 or BF16");
+  if (d->expert_dtype != MOE_F32 && d->expert_dtype != MOE_BF16 && d->expert_dtype != MOE_MXFP4)
+    return bad("expert_dtype must be F32, BF16 or MXFP4");
+  if (d->kind == MOE_EXPERT_SWIGLU) {
+    if (d->n_shared < 0 || d->n_shared > 4) return bad("n_shared must be in [0, 4]");
+    if (d->n_shared > 0) {
+      if (d->shared_inter < 8 || d->shared_inter % 8 != 0)
+        return bad("shared_inter must be a positive multiple of 8");
+      if (d->shared_dtype != MOE_F32 && d->shared_dtype != MOE_BF16)
+        return bad("shared_dtype must be F32 or BF16");
+    }
+  } else {
+    if (d->n_shared != 0) return bad("LINEAR experts take no shared experts");
+    if (d->expert_dtype == MOE_MXFP4) return bad("LINEAR experts are F32 or BF16");
+  }
+  (void)buf;
+  return true;
+}
+
+Layout layout_of(const moe_layer_desc* d) {
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t B = (size_t)d->max_batch, E = (size_t)d->n_experts, k = (size_t)d->top_k;
+  L.ctrl = take(sizeof(Ctrl));
+  L.logits = take(B * E * 4);
+  L.ids = take(B * k * 4);
+  L.w = take(B * k * 4);
+  L.dnorm = take(d->kind == MOE_EXPERT_SWIGLU ? E * (size_t)d->inter * 4 : 0);
+  L.partials = take((size_t)kMaxWorkgroups * (size_t)d->hidden * 4);
+  L.union_n = take(4);
+  L.union_touched = take(E * 4);
+  L.union_offsets = take((E + 1) * 4);
+  L.union_slots = take(B * k * 4);
+  L.total = o;
+  return L;
+}
+
+DT to_dt(int32_t v) { return v == MOE_BF16 ? DT::BF16 : v == MOE_MXFP4 ? DT::MXFP4 : DT::F32; }
+
+}  // namespace
+
+struct moe_layer_s {
+  moe_layer_desc d;
+  moe_weights w;
+  unsigned char* ws;
+  Layout L;
+  int device;
+  int workgroups;
+  int threads;
+  uint32_t magic;
+  template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+  Ctrl* ctrl() const { return at<Ctrl>(L.ctrl); }
+};
+
+static constexpr uint32_t kMagic = 0x4D6F4546u;
+
+static moe_status check_layer(moe_layer l) {
+  if (!l || l->magic != kMagic) return fail(MOE_ERR_ARG, "invalid or destroyed layer handle");
+  return MOE_OK;
+}
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_layer_workspace_bytes(const moe_layer_desc* desc) {
+  if (!desc_valid(desc, nullptr)) return 0;
+  return layout_of(desc).total;
+}
+
+moe_status moe_layer_create(const moe_layer_desc* desc, const moe_weights* weights,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            moe_layer* out) {
+  std::string why;
+  if (!out) return fail(MOE_ERR_ARG, "out is null");
+  if (!desc_valid(desc, &why)) return fail(MOE_ERR_ARG, "descriptor: %s", why.c_str());
+  if (!weights) return fail(MOE_ERR_ARG, "weights is null");
+  const moe_layer_desc& d = *desc;
+  const moe_weights& w = *weights;
+  if ((d.router_dtype == MOE_DTYPE_NONE) != (w.router == nullptr))
+    return fail(MOE_ERR_ARG, "router pointer must be given iff router_dtype is not NONE");
+  if (w.router && !aligned16(w.router)) return fail(MOE_ERR_ARG, "router is not 16-byte aligned");
+  if (d.kind == MOE_EXPERT_SWIGLU) {
+    if (!w.gate || !w.up || !w.down_t) return fail(MOE_ERR_ARG, "gate/up/down_t must be given");
+    if (!aligned16(w.gate) || !aligned16(w.up) || !aligned16(w.down_t))
+      return fail(MOE_ERR_ARG, "expert tensors must be 16-byte aligned");
+    const bool mx = d.expert_dtype == MOE_MXFP4;
+    if (mx != (w.gate_scale != nullptr) || mx != (w.up_scale != nullptr) ||
+        mx != (w.down_scale != nullptr))
+      return fail(MOE_ERR_ARG, "scales must be given iff expert_dtype is MXFP4");
+    if (d.n_shared > 0) {
+      if (!w.sh_gate || !w.sh_up || !w.sh_down_t)
+        return fail(MOE_ERR_ARG, "shared expert tensors must be given");
+      if (!aligned16(w.sh_gate) || !aligned16(w.sh_up) || !aligned16(w.sh_down_t))
+        return fail(MOE_ERR_ARG, "shared tensors must be 16-byte aligned");
+    }
+  } else {
+    if (!w.linear || !aligned16(w.linear))
+      return fail(MOE_ERR_ARG, "linear must be given and 16-byte aligned");
+  }
+  const Layout L = layout_of(&d);
+  if (!workspace || ((uintptr_t)workspace % kAlign) != 0)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be non-null and 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                L.total);
+
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
+  moe_layer l = new (std::nothrow) moe_layer_s;
+  if (!l) return fail(MOE_ERR_ARG, "out of host memory");
+  l->d = d;
+  l->w = w;
+  l->ws = reinterpret_cast<unsigned char*>(workspace);
+  l->L = L;
+  l->device = dev;
+  l->workgroups = cus < kMaxWorkgroups ? cus : kMaxWorkgroups;
+  l->threads = kThreads;
+  l->magic = kMagic;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  e = hipMemsetAsync(l->ctrl(), 0, sizeof(Ctrl), s);
+  if (e == hipSuccess && d.kind == MOE_EXPERT_SWIGLU)
+    e = launch_row_norms(w.down_t, w.down_scale, to_dt(d.expert_dtype),
+                         (size_t)d.n_experts * d.inter, d.hidden, l->at<float>(L.dnorm), s);
+  if (e != hipSuccess) {
+    l->magic = 0;
+    delete l;
+    return device_fail(e, "layer preparation");
+  }
+  *out = l;
+  return ok();
+}
+
+moe_status moe_layer_destroy(moe_layer layer) {
+  if (moe_status st = check_layer(layer)) return st;
+  layer->magic = 0;
+  delete layer;
+  return ok();
+}
+
+moe_status moe_layer_geometry(moe_layer layer, int32_t* workgroups, int32_t* threads) {
+  if (moe_status st = check_layer(layer)) return st;
+  if (workgroups) *workgroups = layer->workgroups;
+  if (threads) *threads = layer->threads;
+  return ok();
+}
+
+moe_status moe_layer_check(moe_layer layer, void* stream, int32_t* device_error) {
+  if (moe_status st = check_layer(layer)) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t err = 0;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(&err, &layer->ctrl()->err, 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && err) e = hipMemset(&layer->ctrl()->err, 0, 4);
+  if (e != hipSuccess) return device_fail(e, "moe_layer_check");
+  if (device_error) *device_error = (int32_t)err;
+  return ok();
+}
+
+moe_status moe_route(moe_layer layer, const float* x, const float* logits_in, int32_t B,
+                     int32_t* ids, float* w, float* logits_out, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const moe_layer_desc& d = layer->d;
+  if (B < 1 || B > d.max_batch) return fail(MOE_ERR_ARG, "B=%d outside [1, max_batch]", B);
+  if ((x == nullptr) == (logits_in == nullptr))
+    return fail(MOE_ERR_ARG, "exactly one of x and logits_in must be given");
+  if (x && d.router_dtype == MOE_DTYPE_NONE)
+    return fail(MOE_ERR_ARG, "routing from x needs a router");
+  if (!ids || !w) return fail(MOE_ERR_ARG, "ids and w must be given");
+  if ((x && !aligned16(x)) || (logits_in && !aligned16(logits_in)))
+    return fail(MOE_ERR_ARG, "x and logits_in must be 16-byte aligned");
+  RouteArgs a;
+  a.x = x;
+  a.logits_in = logits_in;
+  a.router = layer->w.router;
+  a.logits = logits_out ? logits_out : layer->at<float>(layer->L.logits);
+  a.ids = ids;
+  a.w = w;
+  a.H = d.hidden;
+  a.E = d.n_experts;
+  a.k = d.top_k;
+  a.B = B;
+  hipError_t e = launch_route(a, to_dt(d.router_dtype), reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "moe_route launch");
+  return ok();
+}
+
+moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int32_t* ids,
+                           const float* w, float* y, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const moe_layer_desc& d = layer->d;
+  if (!x || !y) return fail(MOE_ERR_ARG, "x and y must be given");
+  if (!aligned16(x) || !aligned16(y)) return fail(MOE_ERR_ARG, "x and y must be 16-byte aligned");
+  if (B < 1 || B > d.max_batch) return fail(MOE_ERR_ARG, "B=%d outside [1, max_batch]", B);
+  if ((ids == nullptr) != (w == nullptr))
+    return fail(MOE_ERR_ARG, "ids and w must both be given or both be null");
+  if (!ids && d.router_dtype == MOE_DTYPE_NONE)
+    return fail(MOE_ERR_ARG, "routing inside the call needs a router");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (d.kind == MOE_EXPERT_SWIGLU && B == 1) {
+    const DT et = to_dt(d.expert_dtype);
+    const DT st = d.n_shared > 0 ? to_dt(d.shared_dtype) : (et == DT::MXFP4 ? DT::BF16 : et);
+    const DT rt = d.router_dtype == MOE_DTYPE_NONE ? st : to_dt(d.router_dtype);
+    const bool combo_ok = (et == DT::F32 && st == DT::F32 && rt == DT::F32) ||
+                          (et == DT::BF16 && st == DT::BF16 && rt == DT::BF16) ||
+                          (et == DT::BF16 && st == DT::BF16 && rt == DT::F32) ||
+                          (et == DT::MXFP4 && st == DT::BF16 && rt == DT::BF16);
+    if (!combo_ok) return fail(MOE_ERR_UNSUPPORTED, "expert/shared/router dtype combination");
+    if (d.hidden > 8192) return fail(MOE_ERR_UNSUPPORTED, "batch-1 kernel needs hidden <= 8192");
+    if (b1_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k) > 160 * 1024)
+      return fail(MOE_ERR_UNSUPPORTED, "batch-1 kernel LDS exceeds 160 KiB");
+    B1Args a;
+    memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.router = layer->w.router;
+    a.gate = layer->w.gate;
+    a.up = layer->w.up;
+    a.down_t = layer->w.down_t;
+    a.gate_s = layer->w.gate_scale;
+    a.up_s = layer->w.up_scale;
+    a.down_s = layer->w.down_scale;
+    a.sh_gate = layer->w.sh_gate;
+    a.sh_up = layer->w.sh_up;
+    a.sh_down_t = layer->w.sh_down_t;
+    a.ids_in = ids;
+    a.w_in = w;
+    a.logits_ws = layer->at<float>(layer->L.logits);
+    a.ids_ws = layer->at<int32_t>(layer->L.ids);
+    a.w_ws = layer->at<float>(layer->L.w);
+    a.partials = layer->at<float>(layer->L.partials);
+    a.y = y;
+    a.ctrl = layer->ctrl();
+    a.H = d.hidden;
+    a.E = d.n_experts;
+    a.k = d.top_k;
+    a.I = d.inter;
+    a.NS = d.n_shared;
+    a.IS = d.shared_inter;
+    a.route_inside = ids == nullptr;
+    hipError_t e = launch_b1(a, et, st, rt, layer->workgroups, layer->threads, s);
+    if (e != hipSuccess) return device_fail(e, "batch-1 layer launch");
+    return ok();
+  }
+  return fail(MOE_ERR_UNSUPPORTED, "this kind/batch combination is not built yet");
+}
+
+moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* ids,
+                              const float* w, int32_t keep, int32_t mode, int32_t* kept,
+                              float* y, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  (void)x; (void)ids; (void)w; (void)keep; (void)mode; (void)kept; (void)y; (void)stream;
+  return fail(MOE_ERR_UNSUPPORTED, "channel selection is not built yet");
+}
+
+moe_status moe_union_experts(const int32_t* ids, int32_t B, int32_t k, int32_t E,
+                             int32_t* n_touched, int32_t* touched, int32_t* offsets,
+                             int32_t* slots, void* stream) {
+  if (!ids || !n_touched || !touched || !offsets || !slots)
+    return fail(MOE_ERR_ARG, "null pointer");
+  if (E < 1 || E > 4096 || k < 1 || k > E || B < 1 || B > 4096)
+    return fail(MOE_ERR_ARG, "sizes out of range");
+  if (union_lds_bytes(B, E) > 96 * 1024)
+    return fail(MOE_ERR_UNSUPPORTED, "E*ceil(B/32)*4 + 8E exceeds the 96 KiB LDS budget");
+  hipError_t e = launch_union(ids, B, k, E, n_touched, touched, offsets, slots, nullptr,
+                              reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "union launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,287 @@
+// route.hip -- batched routing (router logits, exact top-k, softmax over the selected
+// logits), the touched-expert union of a batch, and the load-time row-norm table.
+//
+// Routing: every token scores all E experts with the router, keeps the k largest logits
+// and weights them with a softmax over those k ("Mixture of Experts Changes the
+// Arithmetic", section "Two Numbers Instead of One": k of E experts per token, re-chosen
+// in every layer).  The order of the ids is the routing order: descending logit, ties to
+// the lower id.
+//
+// Union: the distinct experts a batch touches, E[1-(1-k/E)^B] on average for uniform
+// routing ("501B of which 23B are switched on", section 2), with each expert's token
+// list, so that a batched layer reads every touched expert once.
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// Router GEMV for B tokens: one team (256 threads) per router row, the row held in
+// registers and dotted with every token's x; 8 tokens reduced per LDS round.
+template <DT RT, int CPT>
+__global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
+  __shared__ float red[2][4][8];
+  const int t = threadIdx.x, lane = t & 63, wit = t >> 6;
+  const int nch = a.H / 8;
+  for (int e = blockIdx.x; e < a.E; e += gridDim.x) {
+    typename Fmt<RT>::Raw r[CPT];
+    const void* rp = row_ptr<RT>(a.router, (size_t)e, a.H);
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int ch = t + m * kTeam;
+      if (ch < nch) r[m] = Fmt<RT>::load(rp, nullptr, ch);
+      else __builtin_memset(&r[m], 0, sizeof(r[m]));
+    }
+    float w[CPT * 8];
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) Fmt<RT>::decode(r[m], &w[m * 8]);
+    int parity = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 8) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        acc[q] = 0.0f;
+        const int b = b0 + q;
+        if (b < a.B) {
+          const float* xb = a.x + (size_t)b * a.H;
+#pragma unroll
+          for (int m = 0; m < CPT; ++m) {
+            const int ch = t + m * kTeam;
+            if (ch < nch) {
+              const f32x4 lo = reinterpret_cast<const f32x4*>(xb)[2 * ch];
+              const f32x4 hi = reinterpret_cast<const f32x4*>(xb)[2 * ch + 1];
+              float s = acc[q];
+              s = fmaf(w[m * 8 + 0], lo.x, s); s = fmaf(w[m * 8 + 1], lo.y, s);
+              s = fmaf(w[m * 8 + 2], lo.z, s); s = fmaf(w[m * 8 + 3], lo.w, s);
+              s = fmaf(w[m * 8 + 4], hi.x, s); s = fmaf(w[m * 8 + 5], hi.y, s);
+              s = fmaf(w[m * 8 + 6], hi.z, s); s = fmaf(w[m * 8 + 7], hi.w, s);
+              acc[q] = s;
+            }
+          }
+        }
+      }
+      const float tot = wave_multi_sum<8>(acc, lane);
+      if (lane < 8) red[parity][wit][lane] = tot;
+      __syncthreads();
+      if (t < 8 && b0 + t < a.B) {
+        const float l = red[parity][0][t] + red[parity][1][t] + red[parity][2][t] +
+                        red[parity][3][t];
+        a.logits[(size_t)(b0 + t) * a.E + e] = l;
+      }
+      parity ^= 1;
+    }
+  }
+}
+
+// Top-k + softmax: one workgroup per token.
+__global__ __launch_bounds__(256) void topk_kernel(const float* logits, float* logits_copy,
+                                                   int E, int k, int B, int32_t* ids,
+                                                   float* w) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
+  uint64_t* tmp = keys + ((E + 63) & ~63);
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    const float* lb = logits + (size_t)b * E;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      const float l = lb[e];
+      keys[e] = make_key(l, (uint32_t)e);
+      if (logits_copy) logits_copy[(size_t)b * E + e] = l;
+    }
+    __syncthreads();
+    wg_topk_keys(keys, tmp, E, k);
+    if (threadIdx.x < kWave) {
+      const int i = threadIdx.x;
+      const float l0 = key_value(keys[0]);
+      const float ex = i < k ? expf(key_value(keys[i]) - l0) : 0.0f;
+      const float sum = wave_sum(ex);
+      if (i < k) {
+        ids[(size_t)b * k + i] = (int32_t)key_index(keys[i]);
+        w[(size_t)b * k + i] = ex / sum;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Union of the batch's experts in one workgroup: a bitmap of tokens per expert in LDS
+// (LDS atomics give a schedule-independent result), per-expert counts, a prefix sum, and
+// each (token, slot) placed by the rank of its token among the expert's tokens.
+__global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, int k, int E,
+                                                     int32_t* n_touched, int32_t* touched,
+                                                     int32_t* offsets, int32_t* slots,
+                                                     Ctrl* ctrl) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int W = (B + 31) / 32;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(smem);          // [E][W]
+  int32_t* cnt = reinterpret_cast<int32_t*>(bits + (size_t)E * W);  // [E]
+  int32_t* off = cnt + E;                                      // [E+1]
+  __shared__ int32_t part[1024];
+  __shared__ int32_t tpart[1024];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int i = tid; i < E * W; i += nt) bits[i] = 0u;
+  __syncthreads();
+  for (int f = tid; f < B * k; f += nt) {
+    const int e = ids[f], b = f / k;
+    if (e < 0 || e >= E) {
+      if (ctrl)
+        __hip_atomic_fetch_or(&ctrl->err, kErrBadId, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
+    const uint32_t old = atomicOr(&bits[e * W + b / 32], 1u << (b % 32));
+    if ((old >> (b % 32)) & 1u) {
+      if (ctrl)
+        __hip_atomic_fetch_or(&ctrl->err, kErrBadId, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) {
+    int c = 0;
+    for (int q = 0; q < W; ++q) c += __popc(bits[e * W + q]);
+    cnt[e] = c;
+  }
+  __syncthreads();
+  // Exclusive scan of counts (and of touched flags): contiguous segments per thread.
+  const int seg = (E + nt - 1) / nt;
+  const int e0 = tid * seg, e1 = min(E, e0 + seg);
+  int s = 0, ts = 0;
+  for (int e = e0; e < e1; ++e) { s += cnt[e]; ts += cnt[e] > 0; }
+  part[tid] = s;
+  tpart[tid] = ts;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0, trun = 0;
+    for (int i = 0; i < nt; ++i) {
+      const int v = part[i], tv = tpart[i];
+      part[i] = run; tpart[i] = trun;
+      run += v; trun += tv;
+    }
+    off[E] = run;
+    offsets[E] = run;
+    *n_touched = trun;
+  }
+  __syncthreads();
+  s = part[tid];
+  ts = tpart[tid];
+  for (int e = e0; e < e1; ++e) {
+    off[e] = s;
+    offsets[e] = s;
+    if (cnt[e] > 0) touched[ts++] = e;
+    s += cnt[e];
+  }
+  __syncthreads();
+  for (int f = tid; f < B * k; f += nt) {
+    const int e = ids[f], b = f / k;
+    if (e < 0 || e >= E) continue;
+    const uint32_t* be = bits + e * W;
+    int rank = __popc(be[b / 32] & ((1u << (b % 32)) - 1u));
+    for (int q = 0; q < b / 32; ++q) rank += __popc(be[q]);
+    slots[off[e] + rank] = f;
+  }
+}
+
+// ||row||_2 of every row, fp32 sum of squares; one team per row, grid-stride.
+template <DT dt, int CPT>
+__global__ __launch_bounds__(256) void row_norms_kernel(const void* base, const uint8_t* sc,
+                                                        size_t rows, int H, float* out) {
+  __shared__ float red[4];
+  const int t = threadIdx.x, nch = H / 8;
+  for (size_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const void* rp = row_ptr<dt>(base, r, H);
+    const uint8_t* sp = scale_row_ptr(sc, r, H);
+    float s = 0.0f;
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int ch = t + m * kTeam;
+      if (ch < nch) {
+        float v[8];
+        Fmt<dt>::decode(Fmt<dt>::load(rp, sp, ch), v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(v[i], v[i], s);
+      }
+    }
+    s = wave_sum(s);
+    if ((t & 63) == 0) red[t >> 6] = s;
+    __syncthreads();
+    if (t == 0) out[r] = sqrtf(red[0] + red[1] + red[2] + red[3]);
+    __syncthreads();
+  }
+}
+
+int cpt_for(int H) {
+  const int nch = H / 8;
+  const int c = (nch + kTeam - 1) / kTeam;
+  return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : c <= 8 ? 8 : 0;
+}
+
+template <DT RT>
+hipError_t launch_gemv(const RouteArgs& a, hipStream_t s) {
+  const int grid = a.E < 2048 ? a.E : 2048;
+  switch (cpt_for(a.H)) {
+    case 1: hipLaunchKernelGGL((router_gemv_kernel<RT, 1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((router_gemv_kernel<RT, 2>), dim3(grid), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((router_gemv_kernel<RT, 4>), dim3(grid), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((router_gemv_kernel<RT, 8>), dim3(grid), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <DT dt>
+hipError_t launch_norms_t(const void* base, const uint8_t* sc, size_t rows, int H, float* out,
+                          hipStream_t s) {
+  const int grid = rows < 65536 ? (int)rows : 65536;
+  switch (cpt_for(H)) {
+    case 1: hipLaunchKernelGGL((row_norms_kernel<dt, 1>), dim3(grid), dim3(256), 0, s, base, sc, rows, H, out); break;
+    case 2: hipLaunchKernelGGL((row_norms_kernel<dt, 2>), dim3(grid), dim3(256), 0, s, base, sc, rows, H, out); break;
+    case 4: hipLaunchKernelGGL((row_norms_kernel<dt, 4>), dim3(grid), dim3(256), 0, s, base, sc, rows, H, out); break;
+    case 8: hipLaunchKernelGGL((row_norms_kernel<dt, 8>), dim3(grid), dim3(256), 0, s, base, sc, rows, H, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, DT rt, hipStream_t s) {
+  const float* lsrc = a.logits_in;
+  if (!lsrc) {
+    hipError_t e = rt == DT::F32 ? launch_gemv<DT::F32>(a, s) : launch_gemv<DT::BF16>(a, s);
+    if (e != hipSuccess) return e;
+    lsrc = a.logits;
+  }
+  const int lds = (((a.E + 63) & ~63) + ((a.E + 63) / 64) * a.k + 64) * 8;
+  const int grid = a.B < 4096 ? a.B : 4096;
+  float* copy = (a.logits_in && a.logits) ? a.logits : nullptr;
+  hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(256), lds, s, lsrc, copy, a.E, a.k, a.B,
+                     a.ids, a.w);
+  return hipGetLastError();
+}
+
+int union_lds_bytes(int B, int E) {
+  return E * ((B + 31) / 32) * 4 + (2 * E + 1) * 4;
+}
+
+hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touched,
+                        int32_t* touched, int32_t* offsets, int32_t* slots, Ctrl* ctrl,
+                        hipStream_t s) {
+  const int lds = union_lds_bytes(B, E);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(union_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(union_kernel, dim3(1), dim3(1024), lds, s, ids, B, k, E, n_touched,
+                     touched, offsets, slots, ctrl);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_norms(const void* base, const uint8_t* sc, DT dt, size_t rows, int H,
+                            float* out, hipStream_t s) {
+  switch (dt) {
+    case DT::F32: return launch_norms_t<DT::F32>(base, sc, rows, H, out, s);
+    case DT::BF16: return launch_norms_t<DT::BF16>(base, sc, rows, H, out, s);
+    case DT::MXFP4: return launch_norms_t<DT::MXFP4>(base, sc, rows, H, out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -14,7 +14,10 @@ def build(verbose: bool = False) -> str:
     cmd = ["hipcc", *HIPCC_FLAGS, src, "-o", LIB + ".tmp", "-lpthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = [l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for synth.hip:\n" + "\n".join(noise))
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -1,0 +1,124 @@
+"""GPU parity of routing and the batch-1 layer kernel against the oracle (via the C ABI)."""
+import numpy as np
+import pytest
+
+from gpu_common import HostLayer, TOL_BF16, TOL_MXFP4, cuda_ok, pick_attempt, rel_err
+import synth
+from synth import tensors as T
+from synth.workloads import WORKLOADS
+from oracle import moe_oracle as O
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not cuda_ok(), reason="needs a GPU")]
+
+
+def _layer(wl, layer=0, max_batch=1):
+    import routed_expert_ffn_route_amd as M
+    desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, wl.n_shared, wl.I_shared,
+                       kind=M.SWIGLU if wl.kind == "swiglu" else M.LINEAR,
+                       router_dtype=wl.router_dtype, expert_dtype=wl.expert_dtype,
+                       shared_dtype=wl.shared_dtype, max_batch=max_batch)
+    return M.Layer(desc, T.device_layer(wl, layer))
+
+
+# Small shapes that span several channel tiles per workgroup and leave ragged tails:
+# H not a multiple of 2048, I and I_s not multiples of the per-workgroup channel batch.
+SMALL = [
+    T.reduced(WORKLOADS["tiny_f32"], wid=101, H=96, E=13, k=3, I=40, n_shared=2, I_shared=24,
+              shared_dtype="f32"),
+    T.reduced(WORKLOADS["qwen35_a3b_bf16"], wid=102, H=352, E=37, k=5, I=72, n_shared=1,
+              I_shared=56, layers=1),
+    T.reduced(WORKLOADS["qwen35_a3b_bf16"], wid=103, H=2048, E=64, k=8, I=96, n_shared=1,
+              I_shared=128, layers=1),
+    T.reduced(WORKLOADS["qwen35_a3b_bf16"], wid=104, H=4096, E=20, k=2, I=24, n_shared=0,
+              I_shared=0, layers=1),
+    T.reduced(WORKLOADS["qwen35_a3b_bf16"], wid=105, H=64, E=1, k=1, I=8, n_shared=0,
+              I_shared=0, layers=1),
+    T.reduced(WORKLOADS["qwen35_a3b_bf16"], wid=106, H=128, E=40, k=32, I=16, n_shared=1,
+              I_shared=8, layers=1),
+]
+
+
+def _run_token(L, wl, x_np, ids=None, w=None):
+    import torch
+    x = torch.from_numpy(x_np).cuda().reshape(1, -1)
+    y = torch.empty_like(x)
+    L.forward(x, y, ids=ids, w=w)
+    assert L.check() == 0
+    return y.cpu().numpy()[0]
+
+
+def _route(L, wl, x_np):
+    import torch
+    x = torch.from_numpy(x_np).cuda().reshape(1, -1)
+    ids = torch.empty((1, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, wl.k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((1, wl.E), dtype=torch.float32, device="cuda")
+    L.route(x=x, ids=ids, w=w, logits_out=logits)
+    return ids, w, logits
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: f"H{w.H}E{w.E}k{w.k}I{w.I}s{w.n_shared}{w.expert_dtype}")
+def test_b1_small_shapes(wl):
+    L = _layer(wl)
+    hl = HostLayer(wl)
+    for tok in range(3):
+        a, x = pick_attempt(wl, tok, host_router=hl.router)
+        y_ref, ids_ref, w_ref = O.moe_layer_token(x, hl.router, hl.expert, wl.k, hl.shared)
+        ids, w, logits = _route(L, wl, x)
+        assert ids.cpu().numpy()[0].tolist() == ids_ref.tolist()
+        assert np.max(np.abs(w.cpu().numpy()[0] - w_ref)) < 1e-5
+        l_ref = O.router_logits(x, hl.router)[0]
+        assert np.max(np.abs(logits.cpu().numpy()[0] - l_ref)) <= 1e-4 * np.max(np.abs(l_ref)) + 1e-5
+        y = _run_token(L, wl, x)
+        assert rel_err(y, y_ref) <= TOL_BF16, (tok, rel_err(y, y_ref))
+        # routing supplied by the caller (from moe_route, whose router reduction is ordered
+        # differently) agrees with routing inside the launch to fp32 rounding
+        y2 = _run_token(L, wl, x, ids=ids, w=w)
+        assert rel_err(y2, y) < 1e-5
+
+
+def test_b1_tiny_f32_all_tokens():
+    wl = WORKLOADS["tiny_f32"]
+    L = _layer(wl)
+    hl = HostLayer(wl)
+    worst = 0.0
+    for tok in range(wl.tokens):
+        a, x = pick_attempt(wl, tok, host_router=hl.router)
+        y_ref, ids_ref, _ = O.moe_layer_token(x, hl.router, hl.expert, wl.k, hl.shared)
+        ids, _, _ = _route(L, wl, x)
+        assert ids.cpu().numpy()[0].tolist() == ids_ref.tolist()
+        y = _run_token(L, wl, x)
+        worst = max(worst, rel_err(y, y_ref))
+    assert worst <= TOL_BF16
+    print(f"tiny_f32: 64 tokens, worst max|dy|/||y||inf = {worst:.3e}")
+
+
+def test_b1_deterministic_and_repeatable():
+    wl = SMALL[2]
+    L = _layer(wl)
+    a, x = pick_attempt(wl, 0)
+    ys = [_run_token(L, wl, x) for _ in range(4)]
+    for y in ys[1:]:
+        assert np.array_equal(ys[0], y)
+
+
+def test_b1_full_size_stack_sampled():
+    """Full 40-layer-shape layers (H=2048, E=256, k=8, I=768, +1 shared, bf16) as timed."""
+    wl = WORKLOADS["qwen35_a3b_bf16"]
+    for layer in (0, 17):
+        L = _layer(wl, layer)
+        hl = HostLayer(wl, layer)
+        for tok in (0, 101):
+            a, x = pick_attempt(wl, tok, layer, host_router=hl.router)
+            y_ref, ids_ref, _ = O.moe_layer_token(x, hl.router, hl.expert, wl.k, hl.shared)
+            ids, _, _ = _route(L, wl, x)
+            assert ids.cpu().numpy()[0].tolist() == ids_ref.tolist()
+            y = _run_token(L, wl, x)
+            err = rel_err(y, y_ref)
+            print(f"layer {layer} token {tok}: max|dy|/||y||inf = {err:.3e}")
+            assert err <= TOL_BF16
+        L.close()
+        del L
+        import torch
+        torch.cuda.empty_cache()
