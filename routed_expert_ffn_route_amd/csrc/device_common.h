@@ -204,15 +204,36 @@ __device__ inline void wg_topk_keys(uint64_t* buf, uint64_t* tmp, int n, int k) 
 
 // ------------------------------------------------------------------------------------
 // Cross-workgroup signalling (device scope) with bounded waits.
+//
+// A release fence at device scope writes back the whole L2 of the issuing XCD, and those
+// write-backs serialise across the chip (measured: one fence per workgroup of a 256-WG
+// launch adds ~59 us).  So the kernels never issue one.  Data handed to other workgroups
+// is written with device-scope (L2 write-through) atomic stores; the writer waits for its
+// stores to complete (s_waitcnt) and then bumps a flag or counter with a relaxed atomic.
+// A reader spins with relaxed loads and then issues one acquire fence (an L2 invalidate,
+// which is cheap) before it reads the data.
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t atomic_load_dev(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t load_relaxed_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void atomic_store_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_relaxed_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t atomic_add_dev(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t add_relaxed_dev(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Device-coherent stores of values other workgroups will read.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this thread issued has completed.
+__device__ __forceinline__ void stores_complete() { __builtin_amdgcn_s_waitcnt(0); }
+// Make data that other workgroups completed before their flag visible to this one.
+__device__ __forceinline__ void acquire_dev() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz constant clock
@@ -222,8 +243,8 @@ constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz constant cl
 __device__ inline bool wait_geq(const uint32_t* p, uint32_t target, uint32_t* err,
                                 uint32_t errbit) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (atomic_load_dev(p) < target) {
-    __builtin_amdgcn_s_sleep(2);
+  while (load_relaxed_dev(p) < target) {
+    __builtin_amdgcn_s_sleep(1);
     if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
       __hip_atomic_fetch_or(err, errbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;

@@ -1,0 +1,347 @@
+// layer_common.h -- phases shared by the single-launch layer kernels (dense and
+// channel-sparse): the x vector in registers, router rows with the exact top-k, streamed
+// SwiGLU channels, and the deterministic cross-workgroup reduction of the output.
+//
+// Thread layout: a workgroup is `nteams` teams of 256 threads; a team covers one weight
+// row (lane i takes the 8-element chunks i, i+256, ...), so a wave's loads of a row are
+// contiguous 16-byte (bf16), 32-byte (fp32) or 4-byte (MXFP4) pieces.  Each thread keeps
+// the x values and the partial output of its chunks in registers (CPT chunks).
+#pragma once
+#include "kernels.h"
+
+namespace moe {
+namespace lc {
+
+constexpr int kWavesPerTeam = kTeam / kWave;
+
+template <int N> struct NextPow2 {
+  static constexpr int value = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16;
+};
+
+template <DT dt>
+__device__ __forceinline__ typename Fmt<dt>::Raw zero_raw() {
+  typename Fmt<dt>::Raw r;
+  __builtin_memset(&r, 0, sizeof(r));
+  return r;
+}
+
+template <DT dt, int CPT>
+__device__ __forceinline__ float chunk_dot(const typename Fmt<dt>::Raw (&r)[CPT],
+                                           const float (&xv)[CPT * 8]) {
+  float s = 0.0f;
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    float v[8];
+    Fmt<dt>::decode(r[m], v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = fmaf(v[i], xv[m * 8 + i], s);
+  }
+  return s;
+}
+
+// Per-thread view of the workgroup.
+struct Ctx {
+  int tid, nthreads, nteams, team, t, lane, wit, P, wg, H, nch;
+  float* red;     // [2][nteams][4][NP] team-reduction buffers (double buffered)
+  int red_stride; // floats per buffer
+  int parity;
+  __device__ float* next_red() {
+    float* r = red + parity * red_stride;
+    parity ^= 1;
+    return r;
+  }
+};
+
+template <int CPT>
+__device__ __forceinline__ void load_x(const float* x, const Ctx& c, float (&xv)[CPT * 8]) {
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const int ch = c.t + m * kTeam;
+    f32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+    if (ch < c.nch) {
+      lo = reinterpret_cast<const f32x4*>(x)[2 * ch];
+      hi = reinterpret_cast<const f32x4*>(x)[2 * ch + 1];
+    }
+    xv[m * 8 + 0] = lo.x; xv[m * 8 + 1] = lo.y; xv[m * 8 + 2] = lo.z; xv[m * 8 + 3] = lo.w;
+    xv[m * 8 + 4] = hi.x; xv[m * 8 + 5] = hi.y; xv[m * 8 + 6] = hi.z; xv[m * 8 + 7] = hi.w;
+  }
+}
+
+// Team dot products of C rows with x: returns, in every thread of the team, the C totals
+// (out[c]).  rows[c] < 0 marks an empty slot.  One barrier.  All threads must call.
+template <DT dt, int C, int CPT>
+__device__ __forceinline__ void team_dots(const void* base, const uint8_t* scales,
+                                          const long long (&rows)[C],
+                                          const float (&xv)[CPT * 8], Ctx& c,
+                                          float (&out)[C]) {
+  using F = Fmt<dt>;
+  typename F::Raw r[C][CPT];
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    const bool ok = rows[q] >= 0;
+    const size_t rr = ok ? (size_t)rows[q] : 0;
+    const void* p = row_ptr<dt>(base, rr, c.H);
+    const uint8_t* sp = scale_row_ptr(scales, rr, c.H);
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int ch = c.t + m * kTeam;
+      r[q][m] = (ok && ch < c.nch) ? F::load(p, sp, ch) : zero_raw<dt>();
+    }
+  }
+  constexpr int NP = NextPow2<C>::value;
+  float acc[NP];
+#pragma unroll
+  for (int q = 0; q < C; ++q) acc[q] = chunk_dot<dt, CPT>(r[q], xv);
+#pragma unroll
+  for (int q = C; q < NP; ++q) acc[q] = 0.0f;
+  const float tot = wave_multi_sum<NP>(acc, c.lane);
+  float* red = c.next_red();
+  if (c.lane < NP) red[(c.team * kWavesPerTeam + c.wit) * NP + c.lane] = tot;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerTeam; ++w) s += red[(c.team * kWavesPerTeam + w) * NP + q];
+    out[q] = s;
+  }
+}
+
+// One batch of C SwiGLU channels per team: gate and up dots, silu(g)*u*wt, and the
+// accumulation of that activation times the down row into yv.  All threads must call.
+// gate == nullptr: the gate values are given in gval[] (channel-sparse path).
+template <DT dt, int C, int CPT>
+__device__ __forceinline__ void swiglu_batch(
+    const void* G, const void* V, const void* D, const uint8_t* Gs, const uint8_t* Vs,
+    const uint8_t* Ds, const long long (&row)[C], const float (&wt)[C],
+    const float (&gval)[C], const float (&xv)[CPT * 8], float (&yv)[CPT * 8], Ctx& c) {
+  using F = Fmt<dt>;
+  const bool has_gate = G != nullptr;
+  typename F::Raw rg[C][CPT], rv[C][CPT], rd[C][CPT];
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    const bool ok = row[q] >= 0;
+    const size_t r = ok ? (size_t)row[q] : 0;
+    const void* gp = has_gate ? row_ptr<dt>(G, r, c.H) : nullptr;
+    const void* vp = row_ptr<dt>(V, r, c.H);
+    const void* dp = row_ptr<dt>(D, r, c.H);
+    const uint8_t* gsp = scale_row_ptr(Gs, r, c.H);
+    const uint8_t* vsp = scale_row_ptr(Vs, r, c.H);
+    const uint8_t* dsp = scale_row_ptr(Ds, r, c.H);
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int ch = c.t + m * kTeam;
+      const bool live = ok && ch < c.nch;
+      rg[q][m] = (live && has_gate) ? F::load(gp, gsp, ch) : zero_raw<dt>();
+      rv[q][m] = live ? F::load(vp, vsp, ch) : zero_raw<dt>();
+      rd[q][m] = live ? F::load(dp, dsp, ch) : zero_raw<dt>();
+    }
+  }
+  constexpr int NP = NextPow2<2 * C>::value;
+  float acc[NP];
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    acc[q] = has_gate ? chunk_dot<dt, CPT>(rg[q], xv) : 0.0f;
+    acc[C + q] = chunk_dot<dt, CPT>(rv[q], xv);
+  }
+#pragma unroll
+  for (int i = 2 * C; i < NP; ++i) acc[i] = 0.0f;
+  const float tot = wave_multi_sum<NP>(acc, c.lane);
+  float* red = c.next_red();
+  if (c.lane < NP) red[(c.team * kWavesPerTeam + c.wit) * NP + c.lane] = tot;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerTeam; ++w) {
+      g += red[(c.team * kWavesPerTeam + w) * NP + q];
+      u += red[(c.team * kWavesPerTeam + w) * NP + C + q];
+    }
+    if (!has_gate) g = gval[q];
+    const float act = silu(g) * u * wt[q];
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      float d[8];
+      F::decode(rd[q][m], d);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yv[m * 8 + i] = fmaf(act, d[i], yv[m * 8 + i]);
+    }
+  }
+}
+
+// Router rows of this workgroup (one row per team per round), published with
+// device-coherent stores.  Returns true in the workgroup that finished last: it then holds
+// every logit.  Workgroups with no router rows return false without touching the counter.
+template <DT RT, int CPT>
+__device__ inline bool router_rows(const void* router, int E, const float (&xv)[CPT * 8],
+                                   float* logits, uint32_t* router_done, int* s_flag, Ctx& c) {
+  const int n_router_wgs = min(c.P, (E + c.nteams - 1) / c.nteams);
+  if (c.wg >= n_router_wgs) return false;
+  for (int base = c.wg * c.nteams; base < E; base += c.P * c.nteams) {
+    const int e = base + c.team;
+    const long long rows[1] = {e < E ? (long long)e : -1};
+    float l[1];
+    team_dots<RT, 1, CPT>(router, nullptr, rows, xv, c, l);
+    if (c.t == 0 && e < E) st_dev(logits + e, l[0]);
+  }
+  stores_complete();
+  __syncthreads();
+  if (c.tid == 0) *s_flag = add_relaxed_dev(router_done, 1u) == (uint32_t)(n_router_wgs - 1);
+  __syncthreads();
+  const bool last = *s_flag != 0;
+  if (last) acquire_dev();
+  return last;
+}
+
+// Exact top-k of the E logits and the softmax over the k selected, by one workgroup;
+// publishes ids/w (device-coherent) and then sets *ready.  `keys` is LDS scratch of
+// ceil(E/64)*64 + ceil(E/64)*k + 64 entries.
+__device__ inline void topk_publish(const float* logits, int E, int k, uint64_t* keys,
+                                    int32_t* ids, float* w, uint32_t* ready, const Ctx& c) {
+  uint64_t* tmp = keys + ((E + 63) & ~63);
+  for (int e = c.tid; e < E; e += c.nthreads) keys[e] = make_key(logits[e], (uint32_t)e);
+  __syncthreads();
+  wg_topk_keys(keys, tmp, E, k);
+  if (c.tid < kWave) {
+    const float l0 = key_value(keys[0]);
+    const float ex = c.tid < k ? expf(key_value(keys[c.tid]) - l0) : 0.0f;
+    const float sum = wave_sum(ex);
+    if (c.tid < k) {
+      st_dev(ids + c.tid, (int32_t)key_index(keys[c.tid]));
+      st_dev(w + c.tid, ex / sum);
+    }
+  }
+  stores_complete();
+  __syncthreads();
+  if (c.tid == 0) store_relaxed_dev(ready, 1u);
+}
+
+// Wait for the routing (if computed inside the launch) and copy ids/w of the k slots to
+// LDS; ids out of range are reported and their slot skipped (-1).
+__device__ inline void fetch_routing(bool inside, const int32_t* ids_ws, const float* w_ws,
+                                     const int32_t* ids_in, const float* w_in, int E, int k,
+                                     Ctrl* ctrl, int* s_ids, float* s_w, const Ctx& c) {
+  const int32_t* src_ids = ids_in;
+  const float* src_w = w_in;
+  if (inside) {
+    if (c.tid == 0) wait_geq(&ctrl->route_ready, 1u, &ctrl->err, kErrRouteWait);
+    __syncthreads();
+    acquire_dev();
+    src_ids = ids_ws;
+    src_w = w_ws;
+  }
+  if (c.tid < k) {
+    int e = src_ids[c.tid];
+    if (e < 0 || e >= E) {
+      __hip_atomic_fetch_or(&ctrl->err, kErrBadId, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      e = -1;
+    }
+    s_ids[c.tid] = e;
+    s_w[c.tid] = src_w[c.tid];
+  }
+  __syncthreads();
+}
+
+// Stream channels [c0, c1) of a stacked [rows][H] expert set in batches of C per team.
+// chan(f, row, wt) maps a flat channel index to its weight row and weight (row < 0: skip).
+template <DT dt, int C, int CPT, typename Map>
+__device__ inline void stream_channels(const void* G, const void* V, const void* D,
+                                       const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
+                                       long long c0, long long c1, Map chan,
+                                       const float (&xv)[CPT * 8], float (&yv)[CPT * 8],
+                                       Ctx& c) {
+  for (long long base = c0; base < c1; base += (long long)c.nteams * C) {
+    long long row[C];
+    float wt[C], gv[C];
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+      const long long f = base + c.team * C + q;
+      row[q] = -1;
+      wt[q] = 0.0f;
+      gv[q] = 0.0f;
+      if (f < c1) chan(f, row[q], wt[q]);
+    }
+    swiglu_batch<dt, C, CPT>(G, V, D, Gs, Vs, Ds, row, wt, gv, xv, yv, c);
+  }
+}
+
+// Write this workgroup's partial output, then the last R workgroups to finish sum an
+// SW-column slice each over all P partials in a fixed order (p ascending in strided
+// groups, then a fixed tree), and the last reducer resets the control block.
+// `big` is LDS of at least max(nteams*H, nthreads) floats.
+template <int CPT>
+__device__ inline void reduce_output(const float (&yv)[CPT * 8], float* partials, float* y,
+                                     Ctrl* ctrl, int R, int SW, float* big, int* s_int,
+                                     const Ctx& c) {
+  const int H = c.H;
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const int ch = c.t + m * kTeam;
+    if (ch < c.nch) {
+      f32x4 lo = {yv[m * 8 + 0], yv[m * 8 + 1], yv[m * 8 + 2], yv[m * 8 + 3]};
+      f32x4 hi = {yv[m * 8 + 4], yv[m * 8 + 5], yv[m * 8 + 6], yv[m * 8 + 7]};
+      reinterpret_cast<f32x4*>(big + c.team * H)[2 * ch] = lo;
+      reinterpret_cast<f32x4*>(big + c.team * H)[2 * ch + 1] = hi;
+    }
+  }
+  __syncthreads();
+  for (int h = c.tid; h < H; h += c.nthreads) {
+    float s = big[h];
+    for (int tm = 1; tm < c.nteams; ++tm) s += big[tm * H + h];
+    st_dev(partials + (size_t)c.wg * H + h, s);
+  }
+  stores_complete();
+  __syncthreads();
+  if (c.tid == 0) s_int[1] = (int)add_relaxed_dev(&ctrl->done, 1u);
+  __syncthreads();
+  const int ticket = s_int[1];
+  if (ticket < c.P - R) return;
+  const int r = ticket - (c.P - R);
+  if (c.tid == 0) wait_geq(&ctrl->done, (uint32_t)c.P, &ctrl->err, kErrReduceWait);
+  __syncthreads();
+  acquire_dev();
+  const int h0 = r * SW;
+  const int wslice = min(SW, H - h0);
+  const int SWB = SW < c.nthreads ? SW : c.nthreads;  // columns per pass (power of two)
+  const int G = c.nthreads / SWB;
+  const int g = c.tid / SWB, col0 = c.tid % SWB;
+  for (int cb = 0; cb < wslice; cb += SWB) {
+    const int col = cb + col0;
+    float s = 0.0f;
+    if (col < wslice)
+      for (int p = g; p < c.P; p += G) s += partials[(size_t)p * H + h0 + col];
+    big[g * SWB + col0] = s;
+    __syncthreads();
+    for (int stride = G >> 1; stride >= 1; stride >>= 1) {
+      if (g < stride) big[g * SWB + col0] += big[(g + stride) * SWB + col0];
+      __syncthreads();
+    }
+    if (g == 0 && col < wslice) y[h0 + col] = big[col0];
+    __syncthreads();
+  }
+  if (c.tid == 0) {
+    const uint32_t old = add_relaxed_dev(&ctrl->exit, 1u);
+    if (old == (uint32_t)(R - 1)) {
+      store_relaxed_dev(&ctrl->router_done, 0u);
+      store_relaxed_dev(&ctrl->route_ready, 0u);
+      store_relaxed_dev(&ctrl->phase2_done, 0u);
+      store_relaxed_dev(&ctrl->select_ready, 0u);
+      store_relaxed_dev(&ctrl->done, 0u);
+      store_relaxed_dev(&ctrl->exit, 0u);
+    }
+  }
+}
+
+// Reducer count and slice width for H columns over P workgroups: power-of-two slices of at
+// least 32 columns, at most P/2 reducers.
+inline void reducer_split(int H, int P, int* R, int* SW) {
+  const int rmax = P / 2 > 0 ? P / 2 : 1;
+  int sw = 32;
+  while ((long long)sw * rmax < H) sw <<= 1;
+  *SW = sw;
+  *R = (H + sw - 1) / sw;
+}
+
+}  // namespace lc
+}  // namespace moe

@@ -266,9 +266,13 @@ hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touc
                         int32_t* touched, int32_t* offsets, int32_t* slots, Ctrl* ctrl,
                         hipStream_t s) {
   const int lds = union_lds_bytes(B, E);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(union_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
+  static int lds_set = 0;
+  if (lds > lds_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(union_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    if (e != hipSuccess) return e;
+    lds_set = 96 * 1024;
+  }
   hipLaunchKernelGGL(union_kernel, dim3(1), dim3(1024), lds, s, ids, B, k, E, n_touched,
                      touched, offsets, slots, ctrl);
   return hipGetLastError();
