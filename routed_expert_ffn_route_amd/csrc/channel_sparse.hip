@@ -9,7 +9,8 @@
 // the exact gate value (every gate row is read to score) and ||d_j|| precomputed at load.
 //
 // Phases inside the launch (one workgroup per CU):
-//  1. router rows + exact top-k (as in the dense kernel); shared experts stream meanwhile;
+//  1. router rows, then the exact top-k in every workgroup (as in the dense kernel);
+//     shared experts stream meanwhile;
 //  2. gate pass: each workgroup scores its contiguous share of the k*I candidates and
 //     stores g and s (device-coherent);
 //  3. grid barrier (every workgroup waits for all scores);
@@ -181,20 +182,16 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   for (int i = 0; i < CPT * 8; ++i) yv[i] = 0.0f;
 
   // 1. routing, and the shared experts while it is in flight
-  if (a.route_inside) {
-    if (router_rows<RT, CPT>(a.router, a.E, xv, a.logits_ws, &ctrl->router_done, s_int, c))
-      topk_publish(a.logits_ws, a.E, a.k, reinterpret_cast<uint64_t*>(big), a.ids_ws, a.w_ws,
-                   &ctrl->route_ready, c);
-  }
+  if (a.route_inside) router_rows<RT, CPT>(a.router, a.E, xv, a.logits_ws, &ctrl->router_done, c);
   if (a.NS > 0) {
     const long long nsc = (long long)a.NS * a.IS;
     stream_channels<ST, C, CPT>(
         a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, nsc * c.wg / c.P,
         nsc * (c.wg + 1) / c.P,
-        [](long long f, long long& row, float& wt) { row = f; wt = 1.0f; }, xv, yv, c);
+        [](long long f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
   }
-  fetch_routing(a.route_inside, a.ids_ws, a.w_ws, a.ids_in, a.w_in, a.E, a.k, ctrl, s_ids,
-                s_w, c);
+  fetch_routing(a.route_inside, a.logits_ws, a.ids_in, a.w_in, a.E, a.k, ctrl,
+                reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
 
   // 2. gate pass over this workgroup's share of the candidates
   {
@@ -240,12 +237,11 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
     wait_geq(&ctrl->phase2_done, (uint32_t)c.P, &ctrl->err, kErrPhaseWait);
   }
   __syncthreads();
-  acquire_dev();
 
   // 4. the same selection in every workgroup
   uint32_t* sbits = reinterpret_cast<uint32_t*>(big);
   int* kept = reinterpret_cast<int*>(sbits + n);
-  for (int f = c.tid; f < n; f += c.nthreads) sbits[f] = __float_as_uint(L.s_ws[f]);
+  for (int f = c.tid; f < n; f += c.nthreads) sbits[f] = __float_as_uint(ld_dev(L.s_ws + f));
   __syncthreads();
   const int K = select_topk_ascending(sbits, n, L.K, kept, hist, sh, c);
   if (c.wg == 0)
@@ -253,30 +249,21 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
 
   // 5. the kept channels: up row and down row only, gate value from the gate pass
   {
-    const int k0 = (int)((long long)K * c.wg / c.P), k1 = (int)((long long)K * (c.wg + 1) / c.P);
-    for (int base = k0; base < k1; base += c.nteams * C) {
-      long long row[C];
-      float wt[C], gv[C];
-#pragma unroll
-      for (int q = 0; q < C; ++q) {
-        const int i = base + c.team * C + q;
-        row[q] = -1;
-        wt[q] = 0.0f;
-        gv[q] = 0.0f;
-        if (i < k1) {
+    const float* g_ws = L.g_ws;
+    stream_channels<ET, C, CPT>(
+        nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, (long long)K * c.wg / c.P,
+        (long long)K * (c.wg + 1) / c.P,
+        [=](long long i, long long& row, float& wt, float& gv) {
           const int f = kept[i];
           const int slot = f / I;
           const int e = s_ids[slot];
           if (e >= 0) {
-            row[q] = (long long)e * I + (f % I);
-            wt[q] = s_w[slot];
-            gv[q] = L.g_ws[f];
+            row = (long long)e * I + (f % I);
+            wt = s_w[slot];
+            gv = ld_dev(g_ws + f);
           }
-        }
-      }
-      swiglu_batch<ET, C, CPT>(nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, row, wt,
-                               gv, xv, yv, c);
-    }
+        },
+        xv, yv, c);
   }
   __syncthreads();  // `big` is reused by the reduction below
 
@@ -301,8 +288,9 @@ hipError_t launch_t(const CSLaunch& L, int wgs, int threads, int lds, hipStream_
 template <DT ET, DT ST, DT RT>
 hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStream_t s) {
   const int cpt = (L.a.H / 8 + kTeam - 1) / kTeam;
-  if (cpt <= 1) return launch_t<ET, ST, RT, 2, 1>(L, wgs, threads, lds, s);
-  if (cpt <= 2) return launch_t<ET, ST, RT, 2, 2>(L, wgs, threads, lds, s);
+  if (cpt <= 1 && ET != DT::F32) return launch_t<ET, ST, RT, 2, 1>(L, wgs, threads, lds, s);
+  if (cpt <= 1) return launch_t<ET, ST, RT, 1, 1>(L, wgs, threads, lds, s);
+  if (cpt <= 2) return launch_t<ET, ST, RT, 1, 2>(L, wgs, threads, lds, s);
   return hipErrorInvalidValue;
 }
 

@@ -207,11 +207,13 @@ __device__ inline void wg_topk_keys(uint64_t* buf, uint64_t* tmp, int n, int k) 
 //
 // A release fence at device scope writes back the whole L2 of the issuing XCD, and those
 // write-backs serialise across the chip (measured: one fence per workgroup of a 256-WG
-// launch adds ~59 us).  So the kernels never issue one.  Data handed to other workgroups
-// is written with device-scope (L2 write-through) atomic stores; the writer waits for its
-// stores to complete (s_waitcnt) and then bumps a flag or counter with a relaxed atomic.
-// A reader spins with relaxed loads and then issues one acquire fence (an L2 invalidate,
-// which is cheap) before it reads the data.
+// launch adds ~59 us); acquire fences invalidate L2 and serialise too.  So the kernels issue
+// neither.  Data handed to other workgroups is written with device-scope atomic stores
+// (st_dev); the writer waits for its stores to complete (s_waitcnt) and then bumps a flag
+// or counter with a relaxed device-scope atomic.  A reader spins on the flag with relaxed
+// device-scope loads and, once it has seen it, reads the data with device-scope loads
+// (ld_dev), which do not hit stale cached copies; those loads are issued only after the
+// flag load has returned, and the data was complete in memory before the flag was written.
 // ------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t load_relaxed_dev(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -228,6 +230,10 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 }
 __device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Device-coherent loads of values other workgroups wrote with st_dev.
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until every memory operation this thread issued has completed.
 __device__ __forceinline__ void stores_complete() { __builtin_amdgcn_s_waitcnt(0); }

@@ -7,11 +7,11 @@
 // This kernel therefore does the whole layer in one launch of one workgroup per CU:
 //
 //  1. router rows are spread over the first workgroups (one team of 256 threads per
-//     row); the last router workgroup to finish sorts the logits (exact top-k on
-//     ordered 64-bit keys) and publishes ids and softmax weights;
+//     row) and published; once all are in, every workgroup selects the top-k itself
+//     (exact, on ordered 64-bit keys) with the softmax over the selected logits;
 //  2. meanwhile every workgroup streams its share of the shared experts' channels,
 //     which do not depend on routing;
-//  3. every workgroup waits for the routing, then streams its contiguous share of the
+//  3. with the routing known, every workgroup streams its contiguous share of the
 //     k*I routed channels.  For a channel j it reads row j of G_e and V_e and row j of
 //     D_e^T (the review of arXiv:2610.37386, "Background: channels and keep rules":
 //     channel j owns those rows/columns; D is stored transposed so d_j is contiguous),
@@ -67,12 +67,8 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
 #pragma unroll
   for (int i = 0; i < CPT * 8; ++i) yv[i] = 0.0f;
 
-  // 1. router rows; the last router workgroup does the top-k and publishes
-  if (a.route_inside) {
-    if (router_rows<RT, CPT>(a.router, a.E, xv, a.logits_ws, &ctrl->router_done, s_int, c))
-      topk_publish(a.logits_ws, a.E, a.k, reinterpret_cast<uint64_t*>(big), a.ids_ws, a.w_ws,
-                   &ctrl->route_ready, c);
-  }
+  // 1. router rows, spread over the first workgroups
+  if (a.route_inside) router_rows<RT, CPT>(a.router, a.E, xv, a.logits_ws, &ctrl->router_done, c);
 
   // 2. shared experts (independent of routing): flat channel f of [NS][IS] is row f
   if (a.NS > 0) {
@@ -80,19 +76,19 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
     stream_channels<ST, C, CPT>(
         a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, nsc * c.wg / c.P,
         nsc * (c.wg + 1) / c.P,
-        [](long long f, long long& row, float& wt) { row = f; wt = 1.0f; }, xv, yv, c);
+        [](long long f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
   }
 
   // 3. routed experts: flat channel f = slot * I + j
-  fetch_routing(a.route_inside, a.ids_ws, a.w_ws, a.ids_in, a.w_in, a.E, a.k, ctrl, s_ids,
-                s_w, c);
+  fetch_routing(a.route_inside, a.logits_ws, a.ids_in, a.w_in, a.E, a.k, ctrl,
+                reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
   {
     const long long nrc = (long long)a.k * a.I;
     const int I = a.I;
     stream_channels<ET, C, CPT>(
         a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s, nrc * c.wg / c.P,
         nrc * (c.wg + 1) / c.P,
-        [=](long long f, long long& row, float& wt) {
+        [=](long long f, long long& row, float& wt, float&) {
           const int slot = (int)(f / I), j = (int)(f - (long long)slot * I);
           const int e = s_ids[slot];
           if (e >= 0) {
@@ -127,9 +123,12 @@ template <DT ET, DT ST, DT RT>
 hipError_t launch_cpt(const B1Launch& L, int wgs, int threads, int lds, hipStream_t s) {
   const int nch = L.a.H / 8;
   const int cpt = (nch + kTeam - 1) / kTeam;
-  if (cpt <= 1) return launch_t<ET, ST, RT, 2, 1>(L, wgs, threads, lds, s);
-  if (cpt <= 2) return launch_t<ET, ST, RT, 2, 2>(L, wgs, threads, lds, s);
-  if (cpt <= 4) return launch_t<ET, ST, RT, 2, 4>(L, wgs, threads, lds, s);
+  // two channels per team and batch when a row is one chunk per thread, else one
+  // (keeps both pipeline stages in registers)
+  if (cpt <= 1 && ET != DT::F32) return launch_t<ET, ST, RT, 2, 1>(L, wgs, threads, lds, s);
+  if (cpt <= 1) return launch_t<ET, ST, RT, 1, 1>(L, wgs, threads, lds, s);
+  if (cpt <= 2) return launch_t<ET, ST, RT, 1, 2>(L, wgs, threads, lds, s);
+  if (cpt <= 4) return launch_t<ET, ST, RT, 1, 4>(L, wgs, threads, lds, s);
   return hipErrorInvalidValue;
 }
 

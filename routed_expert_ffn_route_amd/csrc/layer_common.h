@@ -107,22 +107,27 @@ __device__ __forceinline__ void team_dots(const void* base, const uint8_t* scale
   }
 }
 
-// One batch of C SwiGLU channels per team: gate and up dots, silu(g)*u*wt, and the
-// accumulation of that activation times the down row into yv.  All threads must call.
-// gate == nullptr: the gate values are given in gval[] (channel-sparse path).
+// Raw weight chunks of one batch of C SwiGLU channels per team (one pipeline stage).
 template <DT dt, int C, int CPT>
-__device__ __forceinline__ void swiglu_batch(
-    const void* G, const void* V, const void* D, const uint8_t* Gs, const uint8_t* Vs,
-    const uint8_t* Ds, const long long (&row)[C], const float (&wt)[C],
-    const float (&gval)[C], const float (&xv)[CPT * 8], float (&yv)[CPT * 8], Ctx& c) {
+struct Stage {
+  typename Fmt<dt>::Raw g[C][CPT], v[C][CPT], d[C][CPT];
+  float wt[C], gv[C];
+  bool live;
+};
+
+// Issue the loads of one batch (rows row[q] < 0 are empty slots; G == nullptr: no gate
+// rows, the gate values come in gv[]).
+template <DT dt, int C, int CPT>
+__device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G, const void* V,
+                                           const void* D, const uint8_t* Gs, const uint8_t* Vs,
+                                           const uint8_t* Ds, const long long (&row)[C],
+                                           const Ctx& c) {
   using F = Fmt<dt>;
-  const bool has_gate = G != nullptr;
-  typename F::Raw rg[C][CPT], rv[C][CPT], rd[C][CPT];
 #pragma unroll
   for (int q = 0; q < C; ++q) {
     const bool ok = row[q] >= 0;
     const size_t r = ok ? (size_t)row[q] : 0;
-    const void* gp = has_gate ? row_ptr<dt>(G, r, c.H) : nullptr;
+    const void* gp = G ? row_ptr<dt>(G, r, c.H) : nullptr;
     const void* vp = row_ptr<dt>(V, r, c.H);
     const void* dp = row_ptr<dt>(D, r, c.H);
     const uint8_t* gsp = scale_row_ptr(Gs, r, c.H);
@@ -132,17 +137,26 @@ __device__ __forceinline__ void swiglu_batch(
     for (int m = 0; m < CPT; ++m) {
       const int ch = c.t + m * kTeam;
       const bool live = ok && ch < c.nch;
-      rg[q][m] = (live && has_gate) ? F::load(gp, gsp, ch) : zero_raw<dt>();
-      rv[q][m] = live ? F::load(vp, vsp, ch) : zero_raw<dt>();
-      rd[q][m] = live ? F::load(dp, dsp, ch) : zero_raw<dt>();
+      st.g[q][m] = (live && G) ? F::load(gp, gsp, ch) : zero_raw<dt>();
+      st.v[q][m] = live ? F::load(vp, vsp, ch) : zero_raw<dt>();
+      st.d[q][m] = live ? F::load(dp, dsp, ch) : zero_raw<dt>();
     }
   }
+}
+
+// Gate and up dots of a loaded batch, team reduction through LDS (one barrier),
+// silu(g)*u*wt, and the accumulation of that activation times the down row into yv.
+// All threads of the workgroup must call.
+template <DT dt, int C, int CPT>
+__device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st, bool has_gate,
+                                              const float (&xv)[CPT * 8],
+                                              float (&yv)[CPT * 8], Ctx& c) {
   constexpr int NP = NextPow2<2 * C>::value;
   float acc[NP];
 #pragma unroll
   for (int q = 0; q < C; ++q) {
-    acc[q] = has_gate ? chunk_dot<dt, CPT>(rg[q], xv) : 0.0f;
-    acc[C + q] = chunk_dot<dt, CPT>(rv[q], xv);
+    acc[q] = has_gate ? chunk_dot<dt, CPT>(st.g[q], xv) : 0.0f;
+    acc[C + q] = chunk_dot<dt, CPT>(st.v[q], xv);
   }
 #pragma unroll
   for (int i = 2 * C; i < NP; ++i) acc[i] = 0.0f;
@@ -158,26 +172,61 @@ __device__ __forceinline__ void swiglu_batch(
       g += red[(c.team * kWavesPerTeam + w) * NP + q];
       u += red[(c.team * kWavesPerTeam + w) * NP + C + q];
     }
-    if (!has_gate) g = gval[q];
-    const float act = silu(g) * u * wt[q];
+    if (!has_gate) g = st.gv[q];
+    const float act = silu(g) * u * st.wt[q];
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
       float d[8];
-      F::decode(rd[q][m], d);
+      Fmt<dt>::decode(st.d[q][m], d);
 #pragma unroll
       for (int i = 0; i < 8; ++i) yv[m * 8 + i] = fmaf(act, d[i], yv[m * 8 + i]);
     }
   }
 }
 
+// Stream items [i0, i1) in batches of C per team, two batches in flight: the loads of
+// batch b+1 are issued before batch b is reduced.  map(i, row, wt, gv) gives the weight
+// row of item i (row < 0: skip), its weight and (gate-less path) its gate value.
+template <DT dt, int C, int CPT, typename Map>
+__device__ inline void stream_channels(const void* G, const void* V, const void* D,
+                                       const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
+                                       long long i0, long long i1, Map map,
+                                       const float (&xv)[CPT * 8], float (&yv)[CPT * 8],
+                                       Ctx& c) {
+  const long long per = (long long)c.nteams * C;
+  const long long nb = i1 > i0 ? (i1 - i0 + per - 1) / per : 0;
+  auto fill = [&](Stage<dt, C, CPT>& st, long long b) {
+    long long row[C];
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+      const long long i = i0 + b * per + c.team * C + q;
+      row[q] = -1;
+      st.wt[q] = 0.0f;
+      st.gv[q] = 0.0f;
+      if (i < i1) map(i, row[q], st.wt[q], st.gv[q]);
+    }
+    stage_load<dt, C, CPT>(st, G, V, D, Gs, Vs, Ds, row, c);
+  };
+  Stage<dt, C, CPT> A, B;
+  if (nb > 0) fill(A, 0);
+  for (long long b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) fill(B, b + 1);
+    stage_compute<dt, C, CPT>(A, G != nullptr, xv, yv, c);
+    if (b + 1 < nb) {
+      if (b + 2 < nb) fill(A, b + 2);
+      stage_compute<dt, C, CPT>(B, G != nullptr, xv, yv, c);
+    }
+  }
+}
+
 // Router rows of this workgroup (one row per team per round), published with
-// device-coherent stores.  Returns true in the workgroup that finished last: it then holds
-// every logit.  Workgroups with no router rows return false without touching the counter.
+// device-coherent stores, then counted in *router_done.  Workgroups with no router rows
+// return without touching the counter.
 template <DT RT, int CPT>
-__device__ inline bool router_rows(const void* router, int E, const float (&xv)[CPT * 8],
-                                   float* logits, uint32_t* router_done, int* s_flag, Ctx& c) {
+__device__ inline void router_rows(const void* router, int E, const float (&xv)[CPT * 8],
+                                   float* logits, uint32_t* router_done, Ctx& c) {
   const int n_router_wgs = min(c.P, (E + c.nteams - 1) / c.nteams);
-  if (c.wg >= n_router_wgs) return false;
+  if (c.wg >= n_router_wgs) return;
   for (int base = c.wg * c.nteams; base < E; base += c.P * c.nteams) {
     const int e = base + c.team;
     const long long rows[1] = {e < E ? (long long)e : -1};
@@ -187,20 +236,16 @@ __device__ inline bool router_rows(const void* router, int E, const float (&xv)[
   }
   stores_complete();
   __syncthreads();
-  if (c.tid == 0) *s_flag = add_relaxed_dev(router_done, 1u) == (uint32_t)(n_router_wgs - 1);
-  __syncthreads();
-  const bool last = *s_flag != 0;
-  if (last) acquire_dev();
-  return last;
+  if (c.tid == 0) add_relaxed_dev(router_done, 1u);
 }
 
-// Exact top-k of the E logits and the softmax over the k selected, by one workgroup;
-// publishes ids/w (device-coherent) and then sets *ready.  `keys` is LDS scratch of
-// ceil(E/64)*64 + ceil(E/64)*k + 64 entries.
-__device__ inline void topk_publish(const float* logits, int E, int k, uint64_t* keys,
-                                    int32_t* ids, float* w, uint32_t* ready, const Ctx& c) {
+// Exact top-k of the E logits and the softmax over the k selected, computed by the whole
+// workgroup into LDS (s_ids, s_w).  `keys` is LDS scratch of ceil(E/64)*64 + ceil(E/64)*k
+// + 64 entries.
+__device__ inline void topk_local(const float* logits, int E, int k, uint64_t* keys,
+                                  int* s_ids, float* s_w, const Ctx& c) {
   uint64_t* tmp = keys + ((E + 63) & ~63);
-  for (int e = c.tid; e < E; e += c.nthreads) keys[e] = make_key(logits[e], (uint32_t)e);
+  for (int e = c.tid; e < E; e += c.nthreads) keys[e] = make_key(ld_dev(logits + e), (uint32_t)e);
   __syncthreads();
   wg_topk_keys(keys, tmp, E, k);
   if (c.tid < kWave) {
@@ -208,62 +253,37 @@ __device__ inline void topk_publish(const float* logits, int E, int k, uint64_t*
     const float ex = c.tid < k ? expf(key_value(keys[c.tid]) - l0) : 0.0f;
     const float sum = wave_sum(ex);
     if (c.tid < k) {
-      st_dev(ids + c.tid, (int32_t)key_index(keys[c.tid]));
-      st_dev(w + c.tid, ex / sum);
+      s_ids[c.tid] = (int)key_index(keys[c.tid]);
+      s_w[c.tid] = ex / sum;
     }
   }
-  stores_complete();
   __syncthreads();
-  if (c.tid == 0) store_relaxed_dev(ready, 1u);
 }
 
-// Wait for the routing (if computed inside the launch) and copy ids/w of the k slots to
-// LDS; ids out of range are reported and their slot skipped (-1).
-__device__ inline void fetch_routing(bool inside, const int32_t* ids_ws, const float* w_ws,
-                                     const int32_t* ids_in, const float* w_in, int E, int k,
-                                     Ctrl* ctrl, int* s_ids, float* s_w, const Ctx& c) {
-  const int32_t* src_ids = ids_in;
-  const float* src_w = w_in;
+// The routing of this token in LDS (s_ids, s_w).  Inside the launch: wait until every
+// router workgroup has published its logits, then select the top-k in this workgroup (each
+// workgroup sorts the E logits itself, which costs less than one more cross-workgroup
+// hand-off).  Given routing: copy ids/w.  Out-of-range ids are reported and skipped (-1).
+__device__ inline void fetch_routing(bool inside, const float* logits, const int32_t* ids_in,
+                                     const float* w_in, int E, int k, Ctrl* ctrl,
+                                     uint64_t* keys, int* s_ids, float* s_w, const Ctx& c) {
   if (inside) {
-    if (c.tid == 0) wait_geq(&ctrl->route_ready, 1u, &ctrl->err, kErrRouteWait);
+    const uint32_t n_router_wgs = (uint32_t)min(c.P, (E + c.nteams - 1) / c.nteams);
+    if (c.tid == 0) wait_geq(&ctrl->router_done, n_router_wgs, &ctrl->err, kErrRouteWait);
     __syncthreads();
-    acquire_dev();
-    src_ids = ids_ws;
-    src_w = w_ws;
+    topk_local(logits, E, k, keys, s_ids, s_w, c);
+    return;
   }
   if (c.tid < k) {
-    int e = src_ids[c.tid];
+    int e = ids_in[c.tid];
     if (e < 0 || e >= E) {
       __hip_atomic_fetch_or(&ctrl->err, kErrBadId, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       e = -1;
     }
     s_ids[c.tid] = e;
-    s_w[c.tid] = src_w[c.tid];
+    s_w[c.tid] = w_in[c.tid];
   }
   __syncthreads();
-}
-
-// Stream channels [c0, c1) of a stacked [rows][H] expert set in batches of C per team.
-// chan(f, row, wt) maps a flat channel index to its weight row and weight (row < 0: skip).
-template <DT dt, int C, int CPT, typename Map>
-__device__ inline void stream_channels(const void* G, const void* V, const void* D,
-                                       const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
-                                       long long c0, long long c1, Map chan,
-                                       const float (&xv)[CPT * 8], float (&yv)[CPT * 8],
-                                       Ctx& c) {
-  for (long long base = c0; base < c1; base += (long long)c.nteams * C) {
-    long long row[C];
-    float wt[C], gv[C];
-#pragma unroll
-    for (int q = 0; q < C; ++q) {
-      const long long f = base + c.team * C + q;
-      row[q] = -1;
-      wt[q] = 0.0f;
-      gv[q] = 0.0f;
-      if (f < c1) chan(f, row[q], wt[q]);
-    }
-    swiglu_batch<dt, C, CPT>(G, V, D, Gs, Vs, Ds, row, wt, gv, xv, yv, c);
-  }
 }
 
 // Write this workgroup's partial output, then the last R workgroups to finish sum an
@@ -300,7 +320,6 @@ __device__ inline void reduce_output(const float (&yv)[CPT * 8], float* partials
   const int r = ticket - (c.P - R);
   if (c.tid == 0) wait_geq(&ctrl->done, (uint32_t)c.P, &ctrl->err, kErrReduceWait);
   __syncthreads();
-  acquire_dev();
   const int h0 = r * SW;
   const int wslice = min(SW, H - h0);
   const int SWB = SW < c.nthreads ? SW : c.nthreads;  // columns per pass (power of two)
@@ -309,8 +328,19 @@ __device__ inline void reduce_output(const float (&yv)[CPT * 8], float* partials
   for (int cb = 0; cb < wslice; cb += SWB) {
     const int col = cb + col0;
     float s = 0.0f;
-    if (col < wslice)
-      for (int p = g; p < c.P; p += G) s += partials[(size_t)p * H + h0 + col];
+    if (col < wslice) {
+      // eight loads in flight, summed in ascending p (a fixed order)
+      for (int p0 = g; p0 < c.P; p0 += 8 * G) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int p = p0 + u * G;
+          v[u] = p < c.P ? ld_dev(partials + (size_t)p * H + h0 + col) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+    }
     big[g * SWB + col0] = s;
     __syncthreads();
     for (int stride = G >> 1; stride >= 1; stride >>= 1) {

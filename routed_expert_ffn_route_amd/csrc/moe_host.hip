@@ -47,7 +47,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, total;
+      union_slots, cs_g, cs_s, cs_y, total;
 };
 
 bool desc_valid(const moe_layer_desc* d, std::string* why) {
@@ -106,6 +106,10 @@ Layout layout_of(const moe_layer_desc* d) {
   L.union_touched = take(E * 4);
   L.union_offsets = take((E + 1) * 4);
   L.union_slots = take(B * k * 4);
+  const size_t kI = d->kind == MOE_EXPERT_SWIGLU ? k * (size_t)d->inter : 0;
+  L.cs_g = take(kI * 4);
+  L.cs_s = take(kI * 4);
+  L.cs_y = take(d->kind == MOE_EXPERT_SWIGLU ? (size_t)d->hidden * 4 : 0);
   L.total = o;
   return L;
 }
@@ -132,6 +136,53 @@ static constexpr uint32_t kMagic = 0x4D6F4546u;
 static moe_status check_layer(moe_layer l) {
   if (!l || l->magic != kMagic) return fail(MOE_ERR_ARG, "invalid or destroyed layer handle");
   return MOE_OK;
+}
+
+static moe_status b1_types(moe_layer layer, DT* et, DT* st, DT* rt) {
+  const moe_layer_desc& d = layer->d;
+  *et = to_dt(d.expert_dtype);
+  *st = d.n_shared > 0 ? to_dt(d.shared_dtype) : (*et == DT::MXFP4 ? DT::BF16 : *et);
+  *rt = d.router_dtype == MOE_DTYPE_NONE ? *st : to_dt(d.router_dtype);
+  const bool combo_ok = (*et == DT::F32 && *st == DT::F32 && *rt == DT::F32) ||
+                        (*et == DT::BF16 && *st == DT::BF16 && *rt == DT::BF16) ||
+                        (*et == DT::BF16 && *st == DT::BF16 && *rt == DT::F32) ||
+                        (*et == DT::MXFP4 && *st == DT::BF16 && *rt == DT::BF16);
+  if (!combo_ok) return fail(MOE_ERR_UNSUPPORTED, "expert/shared/router dtype combination");
+  return MOE_OK;
+}
+
+static B1Args b1_args(moe_layer layer, const float* x, const int32_t* ids, const float* w,
+                      float* y) {
+  const moe_layer_desc& d = layer->d;
+  B1Args a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.router = layer->w.router;
+  a.gate = layer->w.gate;
+  a.up = layer->w.up;
+  a.down_t = layer->w.down_t;
+  a.gate_s = layer->w.gate_scale;
+  a.up_s = layer->w.up_scale;
+  a.down_s = layer->w.down_scale;
+  a.sh_gate = layer->w.sh_gate;
+  a.sh_up = layer->w.sh_up;
+  a.sh_down_t = layer->w.sh_down_t;
+  a.ids_in = ids;
+  a.w_in = w;
+  a.logits_ws = layer->at<float>(layer->L.logits);
+  a.ids_ws = layer->at<int32_t>(layer->L.ids);
+  a.w_ws = layer->at<float>(layer->L.w);
+  a.partials = layer->at<float>(layer->L.partials);
+  a.y = y;
+  a.ctrl = layer->ctrl();
+  a.H = d.hidden;
+  a.E = d.n_experts;
+  a.k = d.top_k;
+  a.I = d.inter;
+  a.NS = d.n_shared;
+  a.IS = d.shared_inter;
+  a.route_inside = ids == nullptr;
+  return a;
 }
 
 extern "C" {
@@ -287,45 +338,12 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     return fail(MOE_ERR_ARG, "routing inside the call needs a router");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d.kind == MOE_EXPERT_SWIGLU && B == 1) {
-    const DT et = to_dt(d.expert_dtype);
-    const DT st = d.n_shared > 0 ? to_dt(d.shared_dtype) : (et == DT::MXFP4 ? DT::BF16 : et);
-    const DT rt = d.router_dtype == MOE_DTYPE_NONE ? st : to_dt(d.router_dtype);
-    const bool combo_ok = (et == DT::F32 && st == DT::F32 && rt == DT::F32) ||
-                          (et == DT::BF16 && st == DT::BF16 && rt == DT::BF16) ||
-                          (et == DT::BF16 && st == DT::BF16 && rt == DT::F32) ||
-                          (et == DT::MXFP4 && st == DT::BF16 && rt == DT::BF16);
-    if (!combo_ok) return fail(MOE_ERR_UNSUPPORTED, "expert/shared/router dtype combination");
+    DT et, st, rt;
+    if (moe_status e = b1_types(layer, &et, &st, &rt)) return e;
     if (d.hidden > 8192) return fail(MOE_ERR_UNSUPPORTED, "batch-1 kernel needs hidden <= 8192");
     if (b1_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k) > 160 * 1024)
       return fail(MOE_ERR_UNSUPPORTED, "batch-1 kernel LDS exceeds 160 KiB");
-    B1Args a;
-    memset(&a, 0, sizeof(a));
-    a.x = x;
-    a.router = layer->w.router;
-    a.gate = layer->w.gate;
-    a.up = layer->w.up;
-    a.down_t = layer->w.down_t;
-    a.gate_s = layer->w.gate_scale;
-    a.up_s = layer->w.up_scale;
-    a.down_s = layer->w.down_scale;
-    a.sh_gate = layer->w.sh_gate;
-    a.sh_up = layer->w.sh_up;
-    a.sh_down_t = layer->w.sh_down_t;
-    a.ids_in = ids;
-    a.w_in = w;
-    a.logits_ws = layer->at<float>(layer->L.logits);
-    a.ids_ws = layer->at<int32_t>(layer->L.ids);
-    a.w_ws = layer->at<float>(layer->L.w);
-    a.partials = layer->at<float>(layer->L.partials);
-    a.y = y;
-    a.ctrl = layer->ctrl();
-    a.H = d.hidden;
-    a.E = d.n_experts;
-    a.k = d.top_k;
-    a.I = d.inter;
-    a.NS = d.n_shared;
-    a.IS = d.shared_inter;
-    a.route_inside = ids == nullptr;
+    B1Args a = b1_args(layer, x, ids, w, y);
     hipError_t e = launch_b1(a, et, st, rt, layer->workgroups, layer->threads, s);
     if (e != hipSuccess) return device_fail(e, "batch-1 layer launch");
     return ok();
@@ -337,8 +355,31 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
                               const float* w, int32_t keep, int32_t mode, int32_t* kept,
                               float* y, void* stream) {
   if (moe_status st = check_layer(layer)) return st;
-  (void)x; (void)ids; (void)w; (void)keep; (void)mode; (void)kept; (void)y; (void)stream;
-  return fail(MOE_ERR_UNSUPPORTED, "channel selection is not built yet");
+  const moe_layer_desc& d = layer->d;
+  if (d.kind != MOE_EXPERT_SWIGLU) return fail(MOE_ERR_ARG, "channel selection needs SWIGLU experts");
+  if (!x || !aligned16(x)) return fail(MOE_ERR_ARG, "x must be given and 16-byte aligned");
+  if (y && !aligned16(y)) return fail(MOE_ERR_ARG, "y must be 16-byte aligned");
+  const long long n = (long long)d.top_k * d.inter;
+  if (keep < 0 || keep > n) return fail(MOE_ERR_ARG, "keep=%d outside [0, k*I=%lld]", keep, n);
+  if (keep > 0 && !kept) return fail(MOE_ERR_ARG, "kept must be given when keep > 0");
+  if (mode != MOE_SCORE_GATE_DNORM && mode != MOE_SCORE_ROUTER_WEIGHTED)
+    return fail(MOE_ERR_ARG, "mode must be GATE_DNORM or ROUTER_WEIGHTED");
+  if ((ids == nullptr) != (w == nullptr))
+    return fail(MOE_ERR_ARG, "ids and w must both be given or both be null");
+  if (!ids && d.router_dtype == MOE_DTYPE_NONE)
+    return fail(MOE_ERR_ARG, "routing inside the call needs a router");
+  DT et, st, rt;
+  if (moe_status e = b1_types(layer, &et, &st, &rt)) return e;
+  if (et == DT::MXFP4) return fail(MOE_ERR_UNSUPPORTED, "channel selection for MXFP4 experts");
+  if (d.hidden > 4096) return fail(MOE_ERR_UNSUPPORTED, "channel selection needs hidden <= 4096");
+  if (cs_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k, d.inter) > 160 * 1024)
+    return fail(MOE_ERR_UNSUPPORTED, "k*I=%lld candidates exceed the selection LDS budget", n);
+  B1Args a = b1_args(layer, x, ids, w, y ? y : layer->at<float>(layer->L.cs_y));
+  hipError_t e = launch_cs(a, layer->at<float>(layer->L.dnorm), layer->at<float>(layer->L.cs_g),
+                           layer->at<float>(layer->L.cs_s), kept, keep, mode, et, st, rt,
+                           layer->workgroups, layer->threads, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "channel-sparse layer launch");
+  return ok();
 }
 
 moe_status moe_union_experts(const int32_t* ids, int32_t B, int32_t k, int32_t E,

@@ -7,7 +7,11 @@ import synth
 from synth import tensors as T
 from oracle import moe_oracle as O
 
-MARGIN = 1e-3       # minimum gap among the k+1 largest router logits (and channel scores)
+MARGIN = 1e-3       # minimum gap among the k+1 largest router logits
+# Channel scores are in output units (|silu(g)| * ||d||), not logit units; their K-th /
+# (K+1)-th gap must exceed this fraction of the largest score (fp32 score error is ~1e-6
+# of it).
+CH_MARGIN_REL = 1e-4
 TOL_BF16 = 2e-3     # max |dy| / ||y_ref||_inf for fp32 / bf16 weights, fp32 accumulation
 TOL_MXFP4 = 1e-2
 
