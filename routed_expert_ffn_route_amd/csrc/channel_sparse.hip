@@ -182,7 +182,8 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   for (int i = 0; i < CPT * 8; ++i) yv[i] = 0.0f;
 
   // 1. routing, and the shared experts while it is in flight
-  if (a.route_inside) router_rows<RT, CPT>(a.router, a.E, xv, a.logits_ws, &ctrl->router_done, c);
+  read_epoch(ctrl, c);
+  router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.logits_ws, ctrl, c);
   if (a.NS > 0) {
     const long long nsc = (long long)a.NS * a.IS;
     stream_channels<ST, C, CPT>(
@@ -233,8 +234,8 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   stores_complete();
   __syncthreads();
   if (c.tid == 0) {
-    add_relaxed_dev(&ctrl->phase2_done, 1u);
-    wait_geq(&ctrl->phase2_done, (uint32_t)c.P, &ctrl->err, kErrPhaseWait);
+    arrive(ctrl->phase2, c.wg);
+    wait_family(ctrl->phase2, c.P, c.epoch, &ctrl->err, kErrPhaseWait);
   }
   __syncthreads();
 
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   __syncthreads();  // `big` is reused by the reduction below
 
   // 6. deterministic cross-workgroup sum
-  reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, s_int, c);
+  reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, c);
 }
 
 template <DT ET, DT ST, DT RT, int C, int CPT>

@@ -244,37 +244,58 @@ __device__ __forceinline__ void acquire_dev() {
 
 constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz constant clock
 
-// Spin (one thread) until *p >= target or the time bound expires; on expiry set bit
-// `errbit` in *err and return false.  The caller's workgroup still runs to its end.
-__device__ inline bool wait_geq(const uint32_t* p, uint32_t target, uint32_t* err,
-                                uint32_t errbit) {
+
+// Control block at the start of every layer workspace (device memory, cleared at layer
+// creation).  Hand-offs between workgroups use arrival counters that only ever grow: launch
+// number n (= the epoch read at the start of the launch) is complete for a counter group
+// when the group reads (n + 1) * (its participant count).  Every launch increments every
+// counter family once per participating workgroup (also families its kernel does not
+// wait on), so the expected values stay in step across kernels sharing a workspace.  The
+// counters of one family are split over kGroups cache lines, so that arrivals contend in
+// groups of P/kGroups instead of all P on one address.
+constexpr int kGroups = 16;
+struct Ctrl {
+  uint32_t epoch;               // launches completed on this workspace
+  uint32_t err;                 // sticky error bits (read and cleared by moe_layer_check)
+  uint32_t pad0[30];
+  uint32_t router[kGroups][32]; // router workgroups that published their logits
+  uint32_t done[kGroups][32];   // workgroups that published their partial output
+  uint32_t phase2[kGroups][32]; // workgroups that published their channel scores
+};
+static_assert(sizeof(Ctrl) == 128 + 3 * kGroups * 128, "counter groups are 128-byte lines");
+
+enum : uint32_t {
+  kErrRouteWait = 1u, kErrReduceWait = 2u, kErrBadId = 4u, kErrPhaseWait = 8u,
+};
+
+__device__ __forceinline__ void arrive(uint32_t (*family)[32], int wg) {
+  add_relaxed_dev(&family[wg % kGroups][0], 1u);
+}
+
+// Participants of group g when workgroups 0..n-1 take part.
+__device__ __forceinline__ uint32_t group_count(int n, int g) {
+  return (uint32_t)(n / kGroups + (g < n % kGroups ? 1 : 0));
+}
+
+// One thread: wait until every group of `family` has seen all of launch `epoch`'s
+// arrivals from workgroups 0..n-1 (bounded; an expired wait sets `errbit`).
+__device__ inline bool wait_family(uint32_t (*family)[32], int n, uint32_t epoch,
+                                   uint32_t* err, uint32_t errbit) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (load_relaxed_dev(p) < target) {
+  while (true) {
+    bool all = true;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const uint32_t target = (epoch + 1u) * group_count(n, g);
+      all &= (int32_t)(load_relaxed_dev(&family[g][0]) - target) >= 0;
+    }
+    if (all) return true;
     __builtin_amdgcn_s_sleep(1);
     if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
       __hip_atomic_fetch_or(err, errbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
   }
-  return true;
 }
-
-// Control block at the start of every layer workspace (device memory, 256 bytes).
-struct Ctrl {
-  uint32_t router_done;   // router workgroups finished
-  uint32_t route_ready;   // top-k published
-  uint32_t done;          // workgroups that wrote their partial
-  uint32_t exit;          // reducers finished (the last one resets the block)
-  uint32_t phase2_done;   // channel-selection: scores written
-  uint32_t select_ready;  // channel-selection: kept list published
-  uint32_t err;           // sticky error bits (read and cleared by moe_layer_check)
-  uint32_t pad[57];
-};
-static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
-
-enum : uint32_t {
-  kErrRouteWait = 1u, kErrReduceWait = 2u, kErrBadId = 4u, kErrSelectWait = 8u,
-  kErrPhaseWait = 16u,
-};
 
 }  // namespace moe

@@ -16,9 +16,8 @@
 //     D_e^T (the review of arXiv:2610.37386, "Background: channels and keep rules":
 //     channel j owns those rows/columns; D is stored transposed so d_j is contiguous),
 //     forms a_j = silu(g_j.x)(v_j.x) w_e and accumulates a_j d_j into registers;
-//  4. each workgroup writes one partial H-vector; the last R workgroups to finish each
-//     sum an H/R slice over all partials in a fixed order (deterministic, no float
-//     atomics); the last reducer resets the control block for the next launch.
+//  4. each workgroup writes one partial H-vector; R fixed workgroups each sum an H/R
+//     slice over all partials in a fixed order (deterministic, no float atomics).
 //
 // All cross-workgroup waits are on work of workgroups that never wait before producing
 // it, and every wait is bounded in time (an expired wait sets an error bit).
@@ -67,8 +66,11 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
 #pragma unroll
   for (int i = 0; i < CPT * 8; ++i) yv[i] = 0.0f;
 
+  read_epoch(ctrl, c);
+  if (c.tid == 0) arrive(ctrl->phase2, c.wg);  // keeps that family in step (unused here)
+
   // 1. router rows, spread over the first workgroups
-  if (a.route_inside) router_rows<RT, CPT>(a.router, a.E, xv, a.logits_ws, &ctrl->router_done, c);
+  router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.logits_ws, ctrl, c);
 
   // 2. shared experts (independent of routing): flat channel f of [NS][IS] is row f
   if (a.NS > 0) {
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   }
 
   // 4. deterministic cross-workgroup sum of the partial outputs
-  reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, s_int, c);
+  reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, c);
 }
 
 template <DT ET, DT ST, DT RT, int C, int CPT>

@@ -60,6 +60,13 @@ hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touc
                         hipStream_t s);
 int union_lds_bytes(int B, int E);
 
+// Linear experts (one [I][H] bf16 matrix each) for a batch: x is split into bf16 hi/lo
+// (xh, xl workspace [B][H]) and the touched experts are applied with MFMA; y [B][I].
+hipError_t launch_linear(const void* M, const float* x, const float* w, const int32_t* n_touched,
+                         const int32_t* touched, const int32_t* offsets, const int32_t* slots,
+                         uint16_t* xh, uint16_t* xl, float* y, int H, int I, int E, int k,
+                         int B, hipStream_t s);
+
 // Load-time preparation: ||d_j||_2 of every row of a stacked [rows][H] tensor.
 hipError_t launch_row_norms(const void* rows_base, const uint8_t* scales, DT dt, size_t rows,
                             int H, float* out, hipStream_t s);

@@ -45,6 +45,7 @@ struct Ctx {
   float* red;     // [2][nteams][4][NP] team-reduction buffers (double buffered)
   int red_stride; // floats per buffer
   int parity;
+  uint32_t epoch; // launches completed on this workspace before this one
   __device__ float* next_red() {
     float* r = red + parity * red_stride;
     parity ^= 1;
@@ -220,23 +221,26 @@ __device__ inline void stream_channels(const void* G, const void* V, const void*
 }
 
 // Router rows of this workgroup (one row per team per round), published with
-// device-coherent stores, then counted in *router_done.  Workgroups with no router rows
-// return without touching the counter.
+// device-coherent stores; every router workgroup then arrives on the router counters
+// (also when the routing is given and no row is computed).
 template <DT RT, int CPT>
-__device__ inline void router_rows(const void* router, int E, const float (&xv)[CPT * 8],
-                                   float* logits, uint32_t* router_done, Ctx& c) {
+__device__ inline void router_rows(bool compute, const void* router, int E,
+                                   const float (&xv)[CPT * 8], float* logits, Ctrl* ctrl,
+                                   Ctx& c) {
   const int n_router_wgs = min(c.P, (E + c.nteams - 1) / c.nteams);
   if (c.wg >= n_router_wgs) return;
-  for (int base = c.wg * c.nteams; base < E; base += c.P * c.nteams) {
-    const int e = base + c.team;
-    const long long rows[1] = {e < E ? (long long)e : -1};
-    float l[1];
-    team_dots<RT, 1, CPT>(router, nullptr, rows, xv, c, l);
-    if (c.t == 0 && e < E) st_dev(logits + e, l[0]);
+  if (compute) {
+    for (int base = c.wg * c.nteams; base < E; base += c.P * c.nteams) {
+      const int e = base + c.team;
+      const long long rows[1] = {e < E ? (long long)e : -1};
+      float l[1];
+      team_dots<RT, 1, CPT>(router, nullptr, rows, xv, c, l);
+      if (c.t == 0 && e < E) st_dev(logits + e, l[0]);
+    }
+    stores_complete();
   }
-  stores_complete();
   __syncthreads();
-  if (c.tid == 0) add_relaxed_dev(router_done, 1u);
+  if (c.tid == 0) arrive(ctrl->router, c.wg);
 }
 
 // Exact top-k of the E logits and the softmax over the k selected, computed by the whole
@@ -268,8 +272,8 @@ __device__ inline void fetch_routing(bool inside, const float* logits, const int
                                      const float* w_in, int E, int k, Ctrl* ctrl,
                                      uint64_t* keys, int* s_ids, float* s_w, const Ctx& c) {
   if (inside) {
-    const uint32_t n_router_wgs = (uint32_t)min(c.P, (E + c.nteams - 1) / c.nteams);
-    if (c.tid == 0) wait_geq(&ctrl->router_done, n_router_wgs, &ctrl->err, kErrRouteWait);
+    const int n_router_wgs = min(c.P, (E + c.nteams - 1) / c.nteams);
+    if (c.tid == 0) wait_family(ctrl->router, n_router_wgs, c.epoch, &ctrl->err, kErrRouteWait);
     __syncthreads();
     topk_local(logits, E, k, keys, s_ids, s_w, c);
     return;
@@ -286,14 +290,14 @@ __device__ inline void fetch_routing(bool inside, const float* logits, const int
   __syncthreads();
 }
 
-// Write this workgroup's partial output, then the last R workgroups to finish sum an
-// SW-column slice each over all P partials in a fixed order (p ascending in strided
-// groups, then a fixed tree), and the last reducer resets the control block.
+// Write this workgroup's partial output and arrive on the done counters; R fixed
+// workgroups (every (P/R)-th) then each sum an SW-column slice over all P partials in a
+// fixed order (p ascending in strided groups, then a fixed tree).  The first reducer,
+// once every workgroup has arrived, advances the epoch for the next launch.
 // `big` is LDS of at least max(nteams*H, nthreads) floats.
 template <int CPT>
 __device__ inline void reduce_output(const float (&yv)[CPT * 8], float* partials, float* y,
-                                     Ctrl* ctrl, int R, int SW, float* big, int* s_int,
-                                     const Ctx& c) {
+                                     Ctrl* ctrl, int R, int SW, float* big, const Ctx& c) {
   const int H = c.H;
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
@@ -313,12 +317,14 @@ __device__ inline void reduce_output(const float (&yv)[CPT * 8], float* partials
   }
   stores_complete();
   __syncthreads();
-  if (c.tid == 0) s_int[1] = (int)add_relaxed_dev(&ctrl->done, 1u);
-  __syncthreads();
-  const int ticket = s_int[1];
-  if (ticket < c.P - R) return;
-  const int r = ticket - (c.P - R);
-  if (c.tid == 0) wait_geq(&ctrl->done, (uint32_t)c.P, &ctrl->err, kErrReduceWait);
+  if (c.tid == 0) arrive(ctrl->done, c.wg);
+  const int stride = c.P / R;
+  if (c.wg % stride != 0 || c.wg / stride >= R) return;
+  const int r = c.wg / stride;
+  if (c.tid == 0) {
+    wait_family(ctrl->done, c.P, c.epoch, &ctrl->err, kErrReduceWait);
+    if (r == 0) store_relaxed_dev(&ctrl->epoch, c.epoch + 1u);
+  }
   __syncthreads();
   const int h0 = r * SW;
   const int wslice = min(SW, H - h0);
@@ -343,24 +349,20 @@ __device__ inline void reduce_output(const float (&yv)[CPT * 8], float* partials
     }
     big[g * SWB + col0] = s;
     __syncthreads();
-    for (int stride = G >> 1; stride >= 1; stride >>= 1) {
-      if (g < stride) big[g * SWB + col0] += big[(g + stride) * SWB + col0];
+    for (int st = G >> 1; st >= 1; st >>= 1) {
+      if (g < st) big[g * SWB + col0] += big[(g + st) * SWB + col0];
       __syncthreads();
     }
     if (g == 0 && col < wslice) y[h0 + col] = big[col0];
     __syncthreads();
   }
-  if (c.tid == 0) {
-    const uint32_t old = add_relaxed_dev(&ctrl->exit, 1u);
-    if (old == (uint32_t)(R - 1)) {
-      store_relaxed_dev(&ctrl->router_done, 0u);
-      store_relaxed_dev(&ctrl->route_ready, 0u);
-      store_relaxed_dev(&ctrl->phase2_done, 0u);
-      store_relaxed_dev(&ctrl->select_ready, 0u);
-      store_relaxed_dev(&ctrl->done, 0u);
-      store_relaxed_dev(&ctrl->exit, 0u);
-    }
-  }
+}
+
+// Read the epoch (launches completed on this workspace) at the start of a launch.  Only
+// thread 0 waits on counters, so only it needs the value; no barrier, so the load's
+// latency overlaps the first weight loads.
+__device__ inline void read_epoch(Ctrl* ctrl, Ctx& c) {
+  c.epoch = c.tid == 0 ? load_relaxed_dev(&ctrl->epoch) : 0u;
 }
 
 // Reducer count and slice width for H columns over P workgroups: power-of-two slices of at

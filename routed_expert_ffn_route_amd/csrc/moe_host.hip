@@ -47,7 +47,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, cs_g, cs_s, cs_y, total;
+      union_slots, cs_g, cs_s, cs_y, xh, xl, total;
 };
 
 bool desc_valid(const moe_layer_desc* d, std::string* why) {
@@ -81,7 +81,8 @@ bool desc_valid(const moe_layer_desc* d, std::string* why) {
     }
   } else {
     if (d->n_shared != 0) return bad("LINEAR experts take no shared experts");
-    if (d->expert_dtype == MOE_MXFP4) return bad("LINEAR experts are F32 or BF16");
+    if (d->expert_dtype != MOE_BF16) return bad("LINEAR experts are BF16");
+    if (d->hidden % 1024 != 0) return bad("LINEAR experts need hidden to be a multiple of 1024");
   }
   (void)buf;
   return true;
@@ -110,6 +111,9 @@ Layout layout_of(const moe_layer_desc* d) {
   L.cs_g = take(kI * 4);
   L.cs_s = take(kI * 4);
   L.cs_y = take(d->kind == MOE_EXPERT_SWIGLU ? (size_t)d->hidden * 4 : 0);
+  const size_t xs = d->kind == MOE_EXPERT_LINEAR ? B * (size_t)d->hidden * 2 : 0;
+  L.xh = take(xs);
+  L.xl = take(xs);
   L.total = o;
   return L;
 }
@@ -348,7 +352,43 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     if (e != hipSuccess) return device_fail(e, "batch-1 layer launch");
     return ok();
   }
-  return fail(MOE_ERR_UNSUPPORTED, "this kind/batch combination is not built yet");
+  if (d.kind == MOE_EXPERT_LINEAR) {
+    if (union_lds_bytes(B, d.n_experts) > 96 * 1024)
+      return fail(MOE_ERR_UNSUPPORTED, "E*ceil(B/32)*4 + 8E exceeds the union LDS budget");
+    const int32_t* rid = ids;
+    const float* rw = w;
+    hipError_t e = hipSuccess;
+    if (!ids) {
+      RouteArgs r;
+      r.x = x;
+      r.logits_in = nullptr;
+      r.router = layer->w.router;
+      r.logits = layer->at<float>(layer->L.logits);
+      r.ids = layer->at<int32_t>(layer->L.ids);
+      r.w = layer->at<float>(layer->L.w);
+      r.H = d.hidden;
+      r.E = d.n_experts;
+      r.k = d.top_k;
+      r.B = B;
+      e = launch_route(r, to_dt(d.router_dtype), s);
+      rid = r.ids;
+      rw = r.w;
+    }
+    int32_t* n_t = layer->at<int32_t>(layer->L.union_n);
+    int32_t* touched = layer->at<int32_t>(layer->L.union_touched);
+    int32_t* offsets = layer->at<int32_t>(layer->L.union_offsets);
+    int32_t* slots = layer->at<int32_t>(layer->L.union_slots);
+    if (e == hipSuccess)
+      e = launch_union(rid, B, d.top_k, d.n_experts, n_t, touched, offsets, slots,
+                       layer->ctrl(), s);
+    if (e == hipSuccess)
+      e = launch_linear(layer->w.linear, x, rw, n_t, touched, offsets, slots,
+                        layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl), y,
+                        d.hidden, d.inter, d.n_experts, d.top_k, B, s);
+    if (e != hipSuccess) return device_fail(e, "linear-expert layer launch");
+    return ok();
+  }
+  return fail(MOE_ERR_UNSUPPORTED, "batched SwiGLU experts (B > 1) are not built yet");
 }
 
 moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* ids,
