@@ -37,7 +37,7 @@ struct CSLaunch {
   float* g_ws;         // [k*I]
   float* s_ws;         // [k*I]
   int32_t* kept_out;   // [K]
-  int K, mode, R, SW;
+  int K, mode, R, SW, tsz;
 };
 
 // Exclusive prefix sum over the workgroup (sh: LDS of nwaves+1 ints).  *total = sum.
@@ -154,9 +154,11 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   Ctx c;
   c.tid = threadIdx.x;
   c.nthreads = blockDim.x;
-  c.nteams = c.nthreads / kTeam;
-  c.team = c.tid / kTeam;
-  c.t = c.tid % kTeam;
+  c.tsz = L.tsz;
+  c.wpt = c.tsz / kWave;
+  c.nteams = c.nthreads / c.tsz;
+  c.team = c.tid / c.tsz;
+  c.t = c.tid % c.tsz;
   c.lane = c.tid & (kWave - 1);
   c.wit = c.t / kWave;
   c.P = gridDim.x;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   c.H = a.H;
   c.nch = a.H / 8;
   c.red = reinterpret_cast<float*>(smem);
-  c.red_stride = c.nteams * kWavesPerTeam * kMaxNP;
+  c.red_stride = (c.nthreads / kWave) * kMaxNP;
   c.parity = 0;
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
@@ -288,18 +290,17 @@ hipError_t launch_t(const CSLaunch& L, int wgs, int threads, int lds, hipStream_
 
 template <DT ET, DT ST, DT RT>
 hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStream_t s) {
-  const int cpt = (L.a.H / 8 + kTeam - 1) / kTeam;
+  const int cpt = (L.a.H / 8 + L.tsz - 1) / L.tsz;
   if (cpt <= 1 && ET != DT::F32) return launch_t<ET, ST, RT, 2, 1>(L, wgs, threads, lds, s);
   if (cpt <= 1) return launch_t<ET, ST, RT, 1, 1>(L, wgs, threads, lds, s);
-  if (cpt <= 2) return launch_t<ET, ST, RT, 1, 2>(L, wgs, threads, lds, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 int cs_lds_bytes(int H, int threads, int E, int k, int I) {
-  const int nteams = threads / kTeam;
-  const int fixed = 2 * nteams * lc::kWavesPerTeam * kMaxNP * 4 + (16 + 64 + 64 + 256 + 48) * 4;
+  const int nteams = threads / team_size(H);
+  const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + 256 + 48) * 4;
   const int n = k * I;
   const int sel = 2 * n * 4;
   const int ybuf = nteams * H * 4;
@@ -322,6 +323,7 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, float* g_ws, float* s_
   L.kept_out = kept;
   L.K = K;
   L.mode = mode;
+  L.tsz = team_size(a.H);
   lc::reducer_split(a.H, wgs, &L.R, &L.SW);
   const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)

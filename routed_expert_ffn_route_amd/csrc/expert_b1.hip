@@ -32,20 +32,23 @@ constexpr int kMaxNP = 16;
 
 struct B1Launch {
   B1Args a;
-  int R;   // reducers
-  int SW;  // slice width of each reducer (columns of y)
+  int R;    // reducers
+  int SW;   // slice width of each reducer (columns of y)
+  int tsz;  // threads per team (one weight row)
 };
 
-template <DT ET, DT ST, DT RT, int C, int CPT>
+template <DT ET, DT ST, DT RT, int CR, int CS, int CPT>
 __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   const B1Args& a = L.a;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   Ctx c;
   c.tid = threadIdx.x;
   c.nthreads = blockDim.x;
-  c.nteams = c.nthreads / kTeam;
-  c.team = c.tid / kTeam;
-  c.t = c.tid % kTeam;
+  c.tsz = L.tsz;
+  c.wpt = c.tsz / kWave;
+  c.nteams = c.nthreads / c.tsz;
+  c.team = c.tid / c.tsz;
+  c.t = c.tid % c.tsz;
   c.lane = c.tid & (kWave - 1);
   c.wit = c.t / kWave;
   c.P = gridDim.x;
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   c.H = a.H;
   c.nch = a.H / 8;
   c.red = reinterpret_cast<float*>(smem);
-  c.red_stride = c.nteams * kWavesPerTeam * kMaxNP;
+  c.red_stride = (c.nthreads / kWave) * kMaxNP;
   c.parity = 0;
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   // 2. shared experts (independent of routing): flat channel f of [NS][IS] is row f
   if (a.NS > 0) {
     const long long nsc = (long long)a.NS * a.IS;
-    stream_channels<ST, C, CPT>(
+    stream_channels<ST, CS, CPT>(
         a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, nsc * c.wg / c.P,
         nsc * (c.wg + 1) / c.P,
         [](long long f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   {
     const long long nrc = (long long)a.k * a.I;
     const int I = a.I;
-    stream_channels<ET, C, CPT>(
+    stream_channels<ET, CR, CPT>(
         a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s, nrc * c.wg / c.P,
         nrc * (c.wg + 1) / c.P,
         [=](long long f, long long& row, float& wt, float&) {
@@ -105,9 +108,9 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, c);
 }
 
-template <DT ET, DT ST, DT RT, int C, int CPT>
+template <DT ET, DT ST, DT RT, int CR, int CS, int CPT>
 hipError_t launch_t(const B1Launch& L, int wgs, int threads, int lds, hipStream_t s) {
-  auto fn = b1_kernel<ET, ST, RT, C, CPT>;
+  auto fn = b1_kernel<ET, ST, RT, CR, CS, CPT>;
   // Raise the dynamic-LDS limit once per instantiation (kept out of the per-launch path
   // so that graph capture records only the launch).
   static bool lds_set = false;
@@ -121,24 +124,32 @@ hipError_t launch_t(const B1Launch& L, int wgs, int threads, int lds, hipStream_
   return hipGetLastError();
 }
 
+// Channels per team and pipeline stage: enough bytes in flight without spilling the two
+// register stages (a bf16 or fp32 chunk holds 4 or 8 registers per row, an MXFP4 chunk 2).
+template <DT dt> constexpr int channels_per_batch() {
+  return dt == DT::MXFP4 ? 4 : dt == DT::BF16 ? 2 : 1;
+}
+
 template <DT ET, DT ST, DT RT>
 hipError_t launch_cpt(const B1Launch& L, int wgs, int threads, int lds, hipStream_t s) {
-  const int nch = L.a.H / 8;
-  const int cpt = (nch + kTeam - 1) / kTeam;
-  // two channels per team and batch when a row is one chunk per thread, else one
-  // (keeps both pipeline stages in registers)
-  if (cpt <= 1 && ET != DT::F32) return launch_t<ET, ST, RT, 2, 1>(L, wgs, threads, lds, s);
-  if (cpt <= 1) return launch_t<ET, ST, RT, 1, 1>(L, wgs, threads, lds, s);
-  if (cpt <= 2) return launch_t<ET, ST, RT, 1, 2>(L, wgs, threads, lds, s);
-  if (cpt <= 4) return launch_t<ET, ST, RT, 1, 4>(L, wgs, threads, lds, s);
+  constexpr int CR = channels_per_batch<ET>(), CS = channels_per_batch<ST>();
+  const int cpt = (L.a.H / 8 + L.tsz - 1) / L.tsz;
+  if (cpt <= 1) return launch_t<ET, ST, RT, CR, CS, 1>(L, wgs, threads, lds, s);
+  if (cpt <= 2) return launch_t<ET, ST, RT, 1, 1, 2>(L, wgs, threads, lds, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+// Threads per team: the smallest of 256/512/1024 that covers a row in one chunk per thread.
+int team_size(int H) {
+  const int nch = H / 8;
+  return nch <= 256 ? 256 : nch <= 512 ? 512 : 1024;
+}
+
 int b1_lds_bytes(int H, int threads, int E, int k) {
-  const int nteams = threads / kTeam;
-  const int red = 2 * nteams * kWavesPerTeam * kMaxNP * 4;
+  const int nteams = threads / team_size(H);
+  const int red = 2 * (threads / kWave) * kMaxNP * 4;
   const int small = (16 + 64 + 64) * 4;
   const int ybuf = nteams * H * 4;
   const int ek = (E + 63) & ~63;
@@ -153,6 +164,7 @@ hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int wgs, int threads,
                      hipStream_t s) {
   B1Launch L;
   L.a = a;
+  L.tsz = team_size(a.H);
   reducer_split(a.H, wgs, &L.R, &L.SW);
   const int lds = b1_lds_bytes(a.H, threads, a.E, a.k);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)

@@ -2,17 +2,17 @@
 // channel-sparse): the x vector in registers, router rows with the exact top-k, streamed
 // SwiGLU channels, and the deterministic cross-workgroup reduction of the output.
 //
-// Thread layout: a workgroup is `nteams` teams of 256 threads; a team covers one weight
-// row (lane i takes the 8-element chunks i, i+256, ...), so a wave's loads of a row are
-// contiguous 16-byte (bf16), 32-byte (fp32) or 4-byte (MXFP4) pieces.  Each thread keeps
-// the x values and the partial output of its chunks in registers (CPT chunks).
+// Thread layout: a workgroup is `nteams` teams of tsz (256, 512 or 1024) threads; a team
+// covers one weight row (lane i takes the 8-element chunks i, i+tsz, ...), so a wave's
+// loads of a row are contiguous 16-byte (bf16), 32-byte (fp32) or 4-byte (MXFP4) pieces.
+// Each thread keeps the x values and the partial output of its chunks in registers (CPT
+// chunks; the team width is chosen so that CPT is 1 up to H = 8192).
 #pragma once
 #include "kernels.h"
 
 namespace moe {
 namespace lc {
 
-constexpr int kWavesPerTeam = kTeam / kWave;
 
 template <int N> struct NextPow2 {
   static constexpr int value = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16;
@@ -42,6 +42,7 @@ __device__ __forceinline__ float chunk_dot(const typename Fmt<dt>::Raw (&r)[CPT]
 // Per-thread view of the workgroup.
 struct Ctx {
   int tid, nthreads, nteams, team, t, lane, wit, P, wg, H, nch;
+  int tsz, wpt;   // threads and waves per team (a team covers one weight row)
   float* red;     // [2][nteams][4][NP] team-reduction buffers (double buffered)
   int red_stride; // floats per buffer
   int parity;
@@ -57,7 +58,7 @@ template <int CPT>
 __device__ __forceinline__ void load_x(const float* x, const Ctx& c, float (&xv)[CPT * 8]) {
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
-    const int ch = c.t + m * kTeam;
+    const int ch = c.t + m * c.tsz;
     f32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
     if (ch < c.nch) {
       lo = reinterpret_cast<const f32x4*>(x)[2 * ch];
@@ -85,7 +86,7 @@ __device__ __forceinline__ void team_dots(const void* base, const uint8_t* scale
     const uint8_t* sp = scale_row_ptr(scales, rr, c.H);
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
-      const int ch = c.t + m * kTeam;
+      const int ch = c.t + m * c.tsz;
       r[q][m] = (ok && ch < c.nch) ? F::load(p, sp, ch) : zero_raw<dt>();
     }
   }
@@ -97,13 +98,13 @@ __device__ __forceinline__ void team_dots(const void* base, const uint8_t* scale
   for (int q = C; q < NP; ++q) acc[q] = 0.0f;
   const float tot = wave_multi_sum<NP>(acc, c.lane);
   float* red = c.next_red();
-  if (c.lane < NP) red[(c.team * kWavesPerTeam + c.wit) * NP + c.lane] = tot;
+  if (c.lane < NP) red[(c.team * c.wpt + c.wit) * NP + c.lane] = tot;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < C; ++q) {
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWavesPerTeam; ++w) s += red[(c.team * kWavesPerTeam + w) * NP + q];
+    for (int w = 0; w < c.wpt; ++w) s += red[(c.team * c.wpt + w) * NP + q];
     out[q] = s;
   }
 }
@@ -136,7 +137,7 @@ __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G,
     const uint8_t* dsp = scale_row_ptr(Ds, r, c.H);
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
-      const int ch = c.t + m * kTeam;
+      const int ch = c.t + m * c.tsz;
       const bool live = ok && ch < c.nch;
       st.g[q][m] = (live && G) ? F::load(gp, gsp, ch) : zero_raw<dt>();
       st.v[q][m] = live ? F::load(vp, vsp, ch) : zero_raw<dt>();
@@ -163,15 +164,15 @@ __device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st, bool 
   for (int i = 2 * C; i < NP; ++i) acc[i] = 0.0f;
   const float tot = wave_multi_sum<NP>(acc, c.lane);
   float* red = c.next_red();
-  if (c.lane < NP) red[(c.team * kWavesPerTeam + c.wit) * NP + c.lane] = tot;
+  if (c.lane < NP) red[(c.team * c.wpt + c.wit) * NP + c.lane] = tot;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < C; ++q) {
     float g = 0.0f, u = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWavesPerTeam; ++w) {
-      g += red[(c.team * kWavesPerTeam + w) * NP + q];
-      u += red[(c.team * kWavesPerTeam + w) * NP + C + q];
+    for (int w = 0; w < c.wpt; ++w) {
+      g += red[(c.team * c.wpt + w) * NP + q];
+      u += red[(c.team * c.wpt + w) * NP + C + q];
     }
     if (!has_gate) g = st.gv[q];
     const float act = silu(g) * u * st.wt[q];
@@ -301,7 +302,7 @@ __device__ inline void reduce_output(const float (&yv)[CPT * 8], float* partials
   const int H = c.H;
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
-    const int ch = c.t + m * kTeam;
+    const int ch = c.t + m * c.tsz;
     if (ch < c.nch) {
       f32x4 lo = {yv[m * 8 + 0], yv[m * 8 + 1], yv[m * 8 + 2], yv[m * 8 + 3]};
       f32x4 hi = {yv[m * 8 + 4], yv[m * 8 + 5], yv[m * 8 + 6], yv[m * 8 + 7]};
