@@ -30,9 +30,10 @@ def stream_id(wid: int, kind: str, layer: int = 0, sub: int = 0) -> int:
 
 
 def x_sub(token: int, attempt: int = 0, case: int = 0) -> int:
-    """Sub-index of the activation vector of one token (attempt = margin redraw count)."""
-    assert 0 <= attempt < 64 and 0 <= token < 2**20 and 0 <= case < 4
-    return (case << 30) | (token << 6) | attempt
+    """Sub-index of the activation vector of one token (attempt = margin redraw count,
+    case = an independent draw of the whole batch)."""
+    assert 0 <= attempt < 64 and 0 <= token < 2**20 and 0 <= case < 64
+    return (case << 26) | (token << 6) | attempt
 
 
 @dataclass(frozen=True)
