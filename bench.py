@@ -65,12 +65,17 @@ def layer_weight_bytes(wl, keep=None, n_read=None) -> float:
 
 
 def traffic_from_profiles(name: str, khash: str):
-    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled
+    by a copy kernel's readings), if they were taken on this kernel source: the last line of
+    profiles/traffic_<name>.txt is the JSON record."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        d = json.load(f)
+        recs = [ln for ln in f if ln.startswith("{")]
+    if not recs:
+        return None
+    d = json.loads(recs[-1])
     if d.get("kernel_hash") != khash:
         return None
     return d.get("hbm_bytes_per_launch")
@@ -255,13 +260,18 @@ def run_linear_sweep(args, wl):
             L.route(logits_in=logits[t % 4], ids=ids, w=w)
             L.forward(x[t % 4], y, ids=ids, w=w)
 
+        # touched-expert counts of the four routings, for the byte figure (untimed)
+        nt_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+        t_dev = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+        o_dev = torch.empty(wl.E + 1, dtype=torch.int32, device="cuda")
+        s_dev = torch.empty(B * wl.k, dtype=torch.int32, device="cuda")
+        for s in range(4):
+            L.route(logits_in=logits[s], ids=ids, w=w)
+            M.union_experts(ids, wl.E, nt_dev, t_dev, o_dev, s_dev)
+            n_touched.append(int(nt_dev.item()))
         for t in range(2):
             step(t)
         torch.cuda.synchronize()
-        from oracle import moe_oracle as O  # touched counts for the byte figure only
-        for s in range(4):
-            i, _ = O.route(logits[s].cpu().numpy(), wl.k)
-            n_touched.append(O.union_experts(i, wl.E)[0])
         # time the flush alone and subtract it
         fl_ms, _ = timed(lambda t: flush.fill_(float(t)), nsteps, graph_ok=not args.eager)
         gpu_ms, _ = timed(step, nsteps, graph_ok=not args.eager)
@@ -296,6 +306,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch without a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=40, help="layers in the oracle sample")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB ten times (the "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -308,6 +321,15 @@ def main():
     from synth import tensors as T
     from synth.workloads import WORKLOADS
     torch.cuda.set_device(0)
+    if args.copy_calibrate:
+        n = args.copy_calibrate * 2**20 // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibrate_bytes_each_way": n * 4, "copies": 10}), flush=True)
+        return
     wl = WORKLOADS[args.workload]
     if args.layers:
         wl = T.reduced(wl, layers=args.layers)

@@ -188,7 +188,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.logits_ws, ctrl, c);
   if (a.NS > 0) {
     const long long nsc = (long long)a.NS * a.IS;
-    stream_channels<ST, C, CPT>(
+    stream_channels<ST, C, CPT, true>(
         a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, nsc * c.wg / c.P,
         nsc * (c.wg + 1) / c.P,
         [](long long f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   // 5. the kept channels: up row and down row only, gate value from the gate pass
   {
     const float* g_ws = L.g_ws;
-    stream_channels<ET, C, CPT>(
+    stream_channels<ET, C, CPT, false>(
         nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, (long long)K * c.wg / c.P,
         (long long)K * (c.wg + 1) / c.P,
         [=](long long i, long long& row, float& wt, float& gv) {

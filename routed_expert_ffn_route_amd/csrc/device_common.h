@@ -83,6 +83,17 @@ template <> struct Fmt<DT::MXFP4> {
   static __host__ __device__ constexpr size_t scale_row_bytes(int H) { return (size_t)H / 32; }
 };
 
+// A pointer every lane of the wave holds the same value of, moved to scalar registers so
+// that loads use a scalar base plus a per-lane 32-bit offset (one offset register serves
+// every row of a batch instead of a 64-bit address register pair per row).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Address of row r of a stacked [rows][H] tensor, and of its MXFP4 scale row.
 template <DT dt>
 __device__ __forceinline__ const void* row_ptr(const void* base, size_t r, int H) {

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   // 2. shared experts (independent of routing): flat channel f of [NS][IS] is row f
   if (a.NS > 0) {
     const long long nsc = (long long)a.NS * a.IS;
-    stream_channels<ST, CS, CPT>(
+    stream_channels<ST, CS, CPT, true>(
         a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, nsc * c.wg / c.P,
         nsc * (c.wg + 1) / c.P,
         [](long long f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   {
     const long long nrc = (long long)a.k * a.I;
     const int I = a.I;
-    stream_channels<ET, CR, CPT>(
+    stream_channels<ET, CR, CPT, true>(
         a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s, nrc * c.wg / c.P,
         nrc * (c.wg + 1) / c.P,
         [=](long long f, long long& row, float& wt, float&) {
@@ -127,7 +127,7 @@ hipError_t launch_t(const B1Launch& L, int wgs, int threads, int lds, hipStream_
 // Channels per team and pipeline stage: enough bytes in flight without spilling the two
 // register stages (a bf16 or fp32 chunk holds 4 or 8 registers per row, an MXFP4 chunk 2).
 template <DT dt> constexpr int channels_per_batch() {
-  return dt == DT::MXFP4 ? 4 : dt == DT::BF16 ? 2 : 1;
+  return dt == DT::MXFP4 ? 2 : dt == DT::BF16 ? 2 : 1;
 }
 
 template <DT ET, DT ST, DT RT>

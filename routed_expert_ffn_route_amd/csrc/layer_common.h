@@ -25,6 +25,20 @@ __device__ __forceinline__ typename Fmt<dt>::Raw zero_raw() {
   return r;
 }
 
+// Keep a loaded chunk (live) or replace it by zeros.  Loads are always issued (from an
+// in-bounds address) and masked afterwards: a load under a branch makes the compiler wait for
+// every outstanding load at the join, which would serialise the two pipeline stages.
+template <DT dt>
+__device__ __forceinline__ typename Fmt<dt>::Raw mask_raw(typename Fmt<dt>::Raw r, bool live) {
+  const uint32_t m = live ? 0xFFFFFFFFu : 0u;
+  uint32_t w[sizeof(r) / 4];
+  __builtin_memcpy(w, &r, sizeof(r));
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(r) / 4); ++i) w[i] &= m;
+  __builtin_memcpy(&r, w, sizeof(r));
+  return r;
+}
+
 template <DT dt, int CPT>
 __device__ __forceinline__ float chunk_dot(const typename Fmt<dt>::Raw (&r)[CPT],
                                            const float (&xv)[CPT * 8]) {
@@ -82,12 +96,13 @@ __device__ __forceinline__ void team_dots(const void* base, const uint8_t* scale
   for (int q = 0; q < C; ++q) {
     const bool ok = rows[q] >= 0;
     const size_t rr = ok ? (size_t)rows[q] : 0;
-    const void* p = row_ptr<dt>(base, rr, c.H);
-    const uint8_t* sp = scale_row_ptr(scales, rr, c.H);
+    const void* p = uniform_ptr(row_ptr<dt>(base, rr, c.H));
+    const uint8_t* sp = scales ? uniform_ptr(scale_row_ptr(scales, rr, c.H)) : nullptr;
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
       const int ch = c.t + m * c.tsz;
-      r[q][m] = (ok && ch < c.nch) ? F::load(p, sp, ch) : zero_raw<dt>();
+      const int chc = ch < c.nch ? ch : c.nch - 1;
+      r[q][m] = mask_raw<dt>(F::load(p, sp, chc), ok && ch < c.nch);
     }
   }
   constexpr int NP = NextPow2<C>::value;
@@ -119,7 +134,7 @@ struct Stage {
 
 // Issue the loads of one batch (rows row[q] < 0 are empty slots; G == nullptr: no gate
 // rows, the gate values come in gv[]).
-template <DT dt, int C, int CPT>
+template <DT dt, int C, int CPT, bool HAS_G>
 __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G, const void* V,
                                            const void* D, const uint8_t* Gs, const uint8_t* Vs,
                                            const uint8_t* Ds, const long long (&row)[C],
@@ -129,19 +144,22 @@ __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G,
   for (int q = 0; q < C; ++q) {
     const bool ok = row[q] >= 0;
     const size_t r = ok ? (size_t)row[q] : 0;
-    const void* gp = G ? row_ptr<dt>(G, r, c.H) : nullptr;
-    const void* vp = row_ptr<dt>(V, r, c.H);
-    const void* dp = row_ptr<dt>(D, r, c.H);
-    const uint8_t* gsp = scale_row_ptr(Gs, r, c.H);
-    const uint8_t* vsp = scale_row_ptr(Vs, r, c.H);
-    const uint8_t* dsp = scale_row_ptr(Ds, r, c.H);
+    // the row is the same for every lane of the wave (one team = whole waves)
+    const void* vp = uniform_ptr(row_ptr<dt>(V, r, c.H));
+    const void* dp = uniform_ptr(row_ptr<dt>(D, r, c.H));
+    const uint8_t* vsp = Vs ? uniform_ptr(scale_row_ptr(Vs, r, c.H)) : nullptr;
+    const uint8_t* dsp = Ds ? uniform_ptr(scale_row_ptr(Ds, r, c.H)) : nullptr;
+    const void* gp = HAS_G ? uniform_ptr(row_ptr<dt>(G, r, c.H)) : nullptr;
+    const uint8_t* gsp = (HAS_G && Gs) ? uniform_ptr(scale_row_ptr(Gs, r, c.H)) : nullptr;
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
       const int ch = c.t + m * c.tsz;
+      const int chc = ch < c.nch ? ch : c.nch - 1;
       const bool live = ok && ch < c.nch;
-      st.g[q][m] = (live && G) ? F::load(gp, gsp, ch) : zero_raw<dt>();
-      st.v[q][m] = live ? F::load(vp, vsp, ch) : zero_raw<dt>();
-      st.d[q][m] = live ? F::load(dp, dsp, ch) : zero_raw<dt>();
+      if constexpr (HAS_G)
+        st.g[q][m] = mask_raw<dt>(F::load(gp, gsp, chc), live);
+      st.v[q][m] = mask_raw<dt>(F::load(vp, vsp, chc), live);
+      st.d[q][m] = mask_raw<dt>(F::load(dp, dsp, chc), live);
     }
   }
 }
@@ -149,15 +167,15 @@ __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G,
 // Gate and up dots of a loaded batch, team reduction through LDS (one barrier),
 // silu(g)*u*wt, and the accumulation of that activation times the down row into yv.
 // All threads of the workgroup must call.
-template <DT dt, int C, int CPT>
-__device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st, bool has_gate,
+template <DT dt, int C, int CPT, bool HAS_G>
+__device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st,
                                               const float (&xv)[CPT * 8],
                                               float (&yv)[CPT * 8], Ctx& c) {
   constexpr int NP = NextPow2<2 * C>::value;
   float acc[NP];
 #pragma unroll
   for (int q = 0; q < C; ++q) {
-    acc[q] = has_gate ? chunk_dot<dt, CPT>(st.g[q], xv) : 0.0f;
+    acc[q] = HAS_G ? chunk_dot<dt, CPT>(st.g[q], xv) : 0.0f;
     acc[C + q] = chunk_dot<dt, CPT>(st.v[q], xv);
   }
 #pragma unroll
@@ -174,7 +192,7 @@ __device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st, bool 
       g += red[(c.team * c.wpt + w) * NP + q];
       u += red[(c.team * c.wpt + w) * NP + C + q];
     }
-    if (!has_gate) g = st.gv[q];
+    if (!HAS_G) g = st.gv[q];
     const float act = silu(g) * u * st.wt[q];
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
@@ -188,8 +206,9 @@ __device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st, bool 
 
 // Stream items [i0, i1) in batches of C per team, two batches in flight: the loads of
 // batch b+1 are issued before batch b is reduced.  map(i, row, wt, gv) gives the weight
-// row of item i (row < 0: skip), its weight and (gate-less path) its gate value.
-template <DT dt, int C, int CPT, typename Map>
+// row of item i (row < 0: skip), its weight and (HAS_G false: no gate rows are read) its
+// gate value.
+template <DT dt, int C, int CPT, bool HAS_G, typename Map>
 __device__ inline void stream_channels(const void* G, const void* V, const void* D,
                                        const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
                                        long long i0, long long i1, Map map,
@@ -207,16 +226,16 @@ __device__ inline void stream_channels(const void* G, const void* V, const void*
       st.gv[q] = 0.0f;
       if (i < i1) map(i, row[q], st.wt[q], st.gv[q]);
     }
-    stage_load<dt, C, CPT>(st, G, V, D, Gs, Vs, Ds, row, c);
+    stage_load<dt, C, CPT, HAS_G>(st, G, V, D, Gs, Vs, Ds, row, c);
   };
   Stage<dt, C, CPT> A, B;
   if (nb > 0) fill(A, 0);
   for (long long b = 0; b < nb; b += 2) {
     if (b + 1 < nb) fill(B, b + 1);
-    stage_compute<dt, C, CPT>(A, G != nullptr, xv, yv, c);
+    stage_compute<dt, C, CPT, HAS_G>(A, xv, yv, c);
     if (b + 1 < nb) {
       if (b + 2 < nb) fill(A, b + 2);
-      stage_compute<dt, C, CPT>(B, G != nullptr, xv, yv, c);
+      stage_compute<dt, C, CPT, HAS_G>(B, xv, yv, c);
     }
   }
 }
