@@ -68,6 +68,36 @@ hipError_t launch_linear(const void* M, const float* x, const float* w, const in
                          uint16_t* xh, uint16_t* xl, float* y, int H, int I, int E, int k,
                          int B, hipStream_t s);
 
+// x [n] fp32 -> bf16 hi, lo with hi + lo ~= x (the MFMA paths' activation operand).
+hipError_t launch_split_x(const float* x, size_t n, uint16_t* xh, uint16_t* xl, hipStream_t s);
+
+// SwiGLU experts for a batch (B > 1): after routing and the touched-expert union, gate/up
+// on MFMA into act, down into per-(token, choice) partials, and the per-token combine.
+struct BsArgs {
+  const void* gate;                     // [E][I][H] (bf16 or MXFP4 codes)
+  const void* up;
+  const void* down_t;
+  const uint8_t* gate_s;                // MXFP4 scales [E][I][H/32] or null
+  const uint8_t* up_s;
+  const uint8_t* down_s;
+  const void* sh_gate;                  // [NS][IS][H] bf16
+  const void* sh_up;
+  const void* sh_down_t;
+  const uint16_t* xh;                   // [B][H] bf16 hi of x
+  const uint16_t* xl;                   // [B][H] bf16 lo of x
+  const float* w;                       // [B][k] router weights
+  const int32_t* n_touched;             // union: [1], [E], [E+1], [B*k]
+  const int32_t* touched;
+  const int32_t* offsets;
+  const int32_t* slots;
+  float* act;                           // [B*k + NS*B][IA] activations
+  float* part;                          // [B*k + NS*B][H] partial outputs
+  float* y;                             // [B][H]
+  int H, I, IS, IA, E, k, B, NS;
+  int slots_max;                        // min(E, B*k): routed expert slots launched
+};
+hipError_t launch_batched_swiglu(const BsArgs& a, DT et, DT st, hipStream_t s);
+
 // Load-time preparation: ||d_j||_2 of every row of a stacked [rows][H] tensor.
 hipError_t launch_row_norms(const void* rows_base, const uint8_t* scales, DT dt, size_t rows,
                             int H, float* out, hipStream_t s);

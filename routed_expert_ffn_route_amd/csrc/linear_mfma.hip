@@ -185,15 +185,18 @@ __global__ __launch_bounds__(1024) void linear_kernel(LinArgs a) {
 
 }  // namespace
 
+hipError_t launch_split_x(const float* x, size_t n, uint16_t* xh, uint16_t* xl, hipStream_t s) {
+  int g = (int)((n + 255) / 256);
+  g = g > 4096 ? 4096 : g;
+  hipLaunchKernelGGL(split_x_kernel, dim3(g), dim3(256), 0, s, x, n, xh, xl);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear(const void* M, const float* x, const float* w, const int32_t* n_touched,
                          const int32_t* touched, const int32_t* offsets, const int32_t* slots,
                          uint16_t* xh, uint16_t* xl, float* y, int H, int I, int E, int k,
                          int B, hipStream_t s) {
-  const size_t n = (size_t)B * H;
-  int g = (int)((n + 255) / 256);
-  g = g > 4096 ? 4096 : g;
-  hipLaunchKernelGGL(split_x_kernel, dim3(g), dim3(256), 0, s, x, n, xh, xl);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_split_x(x, (size_t)B * H, xh, xl, s);
   if (e != hipSuccess) return e;
   LinArgs a{M, xh, xl, w, n_touched, touched, offsets, slots, y, H, I, E, k, B};
   hipLaunchKernelGGL(linear_kernel, dim3((I + kRows - 1) / kRows), dim3(1024), 0, s, a);

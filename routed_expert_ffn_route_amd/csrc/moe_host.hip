@@ -47,7 +47,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, cs_g, cs_s, cs_y, xh, xl, total;
+      union_slots, cs_g, cs_s, cs_y, xh, xl, act, part, total;
 };
 
 bool desc_valid(const moe_layer_desc* d, std::string* why) {
@@ -111,9 +111,17 @@ Layout layout_of(const moe_layer_desc* d) {
   L.cs_g = take(kI * 4);
   L.cs_s = take(kI * 4);
   L.cs_y = take(d->kind == MOE_EXPERT_SWIGLU ? (size_t)d->hidden * 4 : 0);
-  const size_t xs = d->kind == MOE_EXPERT_LINEAR ? B * (size_t)d->hidden * 2 : 0;
+  const bool batched_swiglu = d->kind == MOE_EXPERT_SWIGLU && B > 1;
+  const size_t xs =
+      d->kind == MOE_EXPERT_LINEAR || batched_swiglu ? B * (size_t)d->hidden * 2 : 0;
   L.xh = take(xs);
   L.xl = take(xs);
+  // batched SwiGLU: activations and partial outputs of every (token, choice) and every
+  // (shared expert, token)
+  const size_t pairs = batched_swiglu ? B * k + (size_t)d->n_shared * B : 0;
+  const size_t ia = (size_t)(d->inter > d->shared_inter ? d->inter : d->shared_inter);
+  L.act = take(pairs * ia * 4);
+  L.part = take(pairs * (size_t)d->hidden * 4);
   L.total = o;
   return L;
 }
@@ -352,6 +360,75 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     if (e != hipSuccess) return device_fail(e, "batch-1 layer launch");
     return ok();
   }
+  if (d.kind == MOE_EXPERT_SWIGLU) {
+    DT et, st, rt;
+    if (moe_status e = b1_types(layer, &et, &st, &rt)) return e;
+    if (et == DT::F32 || st != DT::BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "batched SwiGLU needs BF16 or MXFP4 experts and BF16 "
+                                       "shared experts");
+    if (union_lds_bytes(B, d.n_experts) > 96 * 1024)
+      return fail(MOE_ERR_UNSUPPORTED, "E*ceil(B/32)*4 + 8E exceeds the union LDS budget");
+    const int32_t* rid = ids;
+    const float* rw = w;
+    hipError_t e = hipSuccess;
+    if (!ids) {
+      RouteArgs r;
+      r.x = x;
+      r.logits_in = nullptr;
+      r.router = layer->w.router;
+      r.logits = layer->at<float>(layer->L.logits);
+      r.ids = layer->at<int32_t>(layer->L.ids);
+      r.w = layer->at<float>(layer->L.w);
+      r.H = d.hidden;
+      r.E = d.n_experts;
+      r.k = d.top_k;
+      r.B = B;
+      e = launch_route(r, rt, s);
+      rid = r.ids;
+      rw = r.w;
+    }
+    BsArgs a;
+    memset(&a, 0, sizeof(a));
+    a.gate = layer->w.gate;
+    a.up = layer->w.up;
+    a.down_t = layer->w.down_t;
+    a.gate_s = layer->w.gate_scale;
+    a.up_s = layer->w.up_scale;
+    a.down_s = layer->w.down_scale;
+    a.sh_gate = layer->w.sh_gate;
+    a.sh_up = layer->w.sh_up;
+    a.sh_down_t = layer->w.sh_down_t;
+    a.xh = layer->at<uint16_t>(layer->L.xh);
+    a.xl = layer->at<uint16_t>(layer->L.xl);
+    a.w = rw;
+    a.n_touched = layer->at<int32_t>(layer->L.union_n);
+    a.touched = layer->at<int32_t>(layer->L.union_touched);
+    a.offsets = layer->at<int32_t>(layer->L.union_offsets);
+    a.slots = layer->at<int32_t>(layer->L.union_slots);
+    a.act = layer->at<float>(layer->L.act);
+    a.part = layer->at<float>(layer->L.part);
+    a.y = y;
+    a.H = d.hidden;
+    a.I = d.inter;
+    a.IS = d.n_shared > 0 ? d.shared_inter : 0;
+    a.IA = d.inter > a.IS ? d.inter : a.IS;
+    a.E = d.n_experts;
+    a.k = d.top_k;
+    a.B = B;
+    a.NS = d.n_shared;
+    a.slots_max = B * d.top_k < d.n_experts ? B * d.top_k : d.n_experts;
+    if (e == hipSuccess)
+      e = launch_union(rid, B, d.top_k, d.n_experts, layer->at<int32_t>(layer->L.union_n),
+                       layer->at<int32_t>(layer->L.union_touched),
+                       layer->at<int32_t>(layer->L.union_offsets),
+                       layer->at<int32_t>(layer->L.union_slots), layer->ctrl(), s);
+    if (e == hipSuccess)
+      e = launch_split_x(x, (size_t)B * d.hidden, layer->at<uint16_t>(layer->L.xh),
+                         layer->at<uint16_t>(layer->L.xl), s);
+    if (e == hipSuccess) e = launch_batched_swiglu(a, et, st, s);
+    if (e != hipSuccess) return device_fail(e, "batched SwiGLU layer launch");
+    return ok();
+  }
   if (d.kind == MOE_EXPERT_LINEAR) {
     if (union_lds_bytes(B, d.n_experts) > 96 * 1024)
       return fail(MOE_ERR_UNSUPPORTED, "E*ceil(B/32)*4 + 8E exceeds the union LDS budget");
@@ -388,7 +465,7 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     if (e != hipSuccess) return device_fail(e, "linear-expert layer launch");
     return ok();
   }
-  return fail(MOE_ERR_UNSUPPORTED, "batched SwiGLU experts (B > 1) are not built yet");
+  return fail(MOE_ERR_UNSUPPORTED, "unknown expert kind");
 }
 
 moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* ids,
