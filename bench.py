@@ -232,6 +232,88 @@ def run_stack(args, wl, keep=None):
     return out
 
 
+def run_batched_stack(args, wl, B):
+    """Batched decode (B tokens per step) through the SwiGLU stack: per layer, routing, the
+    touched-expert union and the batched expert kernels; each touched expert is read once
+    per step for all its tokens."""
+    import torch
+    import routed_expert_ffn_route_amd as M
+    from synth import tensors as T
+    nb = max(1, min(wl.tokens // B, max(args.steps, 1)))
+    t_gen = time.perf_counter()
+    desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, wl.n_shared, wl.I_shared,
+                       router_dtype=wl.router_dtype, expert_dtype=wl.expert_dtype,
+                       shared_dtype=wl.shared_dtype, max_batch=B)
+    layers, xs, ys = [], [], []
+    for l in range(wl.layers):
+        layers.append(M.Layer(desc, T.device_layer(wl, l)))
+        xs.append(T.device_x(wl, list(range(nb * B)), l))
+        ys.append(torch.empty_like(xs[-1]))
+    torch.cuda.synchronize()
+    print(f"# {wl.name}: generated {wl.layers} layers in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    # touched experts of every (layer, batch) for the byte figure (untimed)
+    ids = torch.empty((B, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((B, wl.k), dtype=torch.float32, device="cuda")
+    nt_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t_dev = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+    o_dev = torch.empty(wl.E + 1, dtype=torch.int32, device="cuda")
+    s_dev = torch.empty(B * wl.k, dtype=torch.int32, device="cuda")
+    touched = {}
+    for l in range(wl.layers):
+        for i in range(nb):
+            layers[l].route(x=xs[l][i * B:(i + 1) * B], ids=ids, w=w)
+            M.union_experts(ids, wl.E, nt_dev, t_dev, o_dev, s_dev)
+            touched[(l, i)] = int(nt_dev.item())
+
+    def step(t):
+        i = t % nb
+        for l in range(wl.layers):
+            layers[l].forward(xs[l][i * B:(i + 1) * B], ys[l][i * B:(i + 1) * B], B=B)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    for L in layers:
+        assert L.check() == 0, "device error word set"
+    K = args.steps
+    gpu_ms, wall_ms = timed(step, K, graph_ok=not args.eager)
+    for L in layers:
+        assert L.check() == 0, "device error word set"
+    step_bytes = sum(layer_weight_bytes(wl, n_read=touched[(l, t % nb)])
+                     for t in range(K) for l in range(wl.layers)) / K
+    mean_touched = sum(touched.values()) / len(touched)
+    achieved = step_bytes / (gpu_ms / 1e3 / K) / 1e9
+    return {
+        "metric": "MoE-stack batched decode tokens/s (aggregate over the batch)",
+        "value": round(K * B / (gpu_ms / 1e3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(gpu_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "hidden": wl.H, "experts": wl.E,
+                   "top_k": wl.k, "inter": wl.I, "shared": wl.n_shared,
+                   "weights": wl.expert_dtype, "batch": B, "graph": not args.eager},
+        "mean_touched_experts": round(mean_touched, 2),
+        "hbm_gb_s": round(achieved, 1),
+        "hbm_pct_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "wall_ms_per_step": round(wall_ms / K, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "route + union + gate/up + down + combine per layer",
+                     "bytes_per_step": step_bytes,
+                     "us_per_layer_step": round(gpu_ms * 1e3 / K / wl.layers, 3)},
+        "cpu_baseline": None,
+    }
+
+
 def run_linear_sweep(args, wl):
     """The linear-expert batch sweep: per batch, one step = route (given iid logits), union,
     and the MFMA grouped product; each step's touched experts are read once."""
@@ -303,6 +385,8 @@ def main():
                     help="channel-sparse workload: kept channels per token (-1: first of the "
                          "workload's keep counts)")
     ap.add_argument("--batches", default="", help="linear sweep: comma-separated batch sizes")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="SwiGLU stacks: tokens per step (B > 1 runs the batched layer)")
     ap.add_argument("--eager", action="store_true", help="launch without a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=40, help="layers in the oracle sample")
@@ -336,6 +420,9 @@ def main():
     if wl.kind == "linear":
         for line in run_linear_sweep(args, wl):
             print(json.dumps(line), flush=True)
+        return
+    if args.batch > 1:
+        print(json.dumps(run_batched_stack(args, wl, args.batch)), flush=True)
         return
     keep = None
     if wl.keep_fracs:
