@@ -185,7 +185,8 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
 
   // 1. routing, and the shared experts while it is in flight
   read_epoch(ctrl, c);
-  router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.logits_ws, ctrl, c);
+  router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.rlog, reinterpret_cast<float*>(big),
+                       reinterpret_cast<uint32_t*>(s_int), c);
   if (a.NS > 0) {
     const long long nsc = (long long)a.NS * a.IS;
     stream_channels<ST, C, CPT, true>(
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
         nsc * (c.wg + 1) / c.P,
         [](long long f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
   }
-  fetch_routing(a.route_inside, a.logits_ws, a.ids_in, a.w_in, a.E, a.k, ctrl,
+  fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
                 reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
 
   // 2. gate pass over this workgroup's share of the candidates
@@ -304,8 +305,7 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I) {
   const int n = k * I;
   const int sel = 2 * n * 4;
   const int ybuf = nteams * H * 4;
-  const int ek = (E + 63) & ~63;
-  const int topk = (ek + ((E + 63) / 64) * k + 64) * 8;
+  const int topk = topk_lds_bytes(E, k);
   int big = sel > ybuf ? sel : ybuf;
   big = big > topk ? big : topk;
   big = big > threads * 4 ? big : threads * 4;

@@ -159,58 +159,77 @@ __device__ __forceinline__ float key_value(uint64_t k) {
   return from_ordered_bits((uint32_t)(k >> 32));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((unsigned)(uint32_t)v, m, kWave);
-  const uint32_t hi = __shfl_xor((unsigned)(uint32_t)(v >> 32), m, kWave);
-  return ((uint64_t)hi << 32) | lo;
+// Rank of `me` among the keys [j0, j1) of `keys` (number of larger keys).  The lanes of a
+// wave read the same keys (LDS broadcasts, no cross-lane shuffles), 16 reads in flight per
+// batch; keys past `n` are clamped reads that count nothing.
+__device__ __forceinline__ int rank_in(const uint64_t* keys, int n, int j0, int j1,
+                                       uint64_t me) {
+  int r = 0;
+  for (int j = j0; j < j1; j += 16) {
+    uint64_t kk[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) kk[u] = keys[j + u < n ? j + u : n - 1];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) r += (j + u < j1 && kk[u] > me) ? 1 : 0;
+  }
+  return r;
 }
 
-// Bitonic sort of one key per lane across the 64 lanes, descending (lane 0 = largest).
-__device__ __forceinline__ uint64_t wave_bitonic_desc(uint64_t key, int lane) {
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t other = shfl_xor_u64(key, j);
-      const bool desc = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      const uint64_t mx = key > other ? key : other;
-      const uint64_t mn = key > other ? other : key;
-      key = (lower == desc) ? mx : mn;
-    }
+// Top-k of n distinct non-zero keys held in LDS (keys[n .. n rounded up to 64) must be 0).
+// Level 1: every group of 64 keys ranks its members among themselves (one wave per group)
+// and keeps its min(k, 64) best as candidates -- every key of the overall top k is among
+// its group's top k.  Level 2: the candidates are ranked among themselves (each rank split
+// over several threads, partial ranks summed with LDS atomics).  A key's rank is the
+// number of larger keys, so the keys of rank < k are the top k in descending order:
+// out[0..k).  LDS scratch `tmp` of topk_scratch_bytes(n, k).  The keys must be visible to
+// the whole workgroup before the call; all threads of the workgroup must call.
+__host__ __device__ constexpr int topk_candidates(int n, int k) {
+  return ((n + 63) / 64) * (k < 64 ? k : 64);
+}
+__host__ __device__ constexpr int topk_scratch_bytes(int n, int k) {
+  return topk_candidates(n, k) * 12;
+}
+__device__ inline void wg_topk_rank(const uint64_t* keys, void* tmp, int n, int k,
+                                    uint64_t* out) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nt / kWave;
+  const int kk = k < kWave ? k : kWave;
+  const int groups = (n + kWave - 1) / kWave;
+  const int C = groups * kk;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(tmp);
+  int* cnt = reinterpret_cast<int*>(cand + C);
+  for (int i = tid; i < C; i += nt) {
+    cand[i] = 0ull;
+    cnt[i] = 0;
   }
-  return key;
+  __syncthreads();
+  for (int g = wave; g < groups; g += nwaves) {
+    const uint64_t me = keys[g * kWave + lane];
+    const int r = rank_in(keys + g * kWave, kWave, 0, kWave, me);
+    if (me != 0ull && r < kk) cand[g * kk + r] = me;
+  }
+  __syncthreads();
+  int parts = nt / C;
+  parts = parts < 1 ? 1 : parts > 16 ? 16 : parts;
+  const int span = (C + parts - 1) / parts;
+  for (int i = tid; i < C * parts; i += nt) {
+    const int e = i % C, q = i / C;
+    const int j0 = q * span, j1 = j0 + span < C ? j0 + span : C;
+    const int r = rank_in(cand, C, j0, j1, cand[e]);
+    if (r) atomicAdd(&cnt[e], r);
+  }
+  __syncthreads();
+  for (int e = tid; e < C; e += nt) {
+    const int r = cnt[e];
+    if (r < k && cand[e] != 0ull) out[r] = cand[e];
+  }
+  __syncthreads();
 }
 
-// Top-k of n keys held in LDS `buf` (capacity >= n), by the whole workgroup.  Each level
-// sorts groups of 64 keys with one wave each and keeps the k best of every group, until at
-// most 64 remain.  Requires k <= 32 when n > 64 (each level then at least halves the
-// candidates).  On return buf[0..k) holds the k largest keys in descending order.
-// `tmp` must hold at least ceil(n/64)*k keys.  All threads of the workgroup must call.
-__device__ inline void wg_topk_keys(uint64_t* buf, uint64_t* tmp, int n, int k) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
-  uint64_t* src = buf;
-  uint64_t* dst = tmp;
-  while (true) {
-    const int groups = (n + kWave - 1) / kWave;
-    const int keep = k < kWave ? k : kWave;
-    for (int g = wave; g < groups; g += nwaves) {
-      const int i = g * kWave + lane;
-      uint64_t key = i < n ? src[i] : 0ull;
-      key = wave_bitonic_desc(key, lane);
-      if (lane < keep) dst[g * keep + lane] = key;
-    }
-    __syncthreads();
-    n = groups * keep;
-    uint64_t* t = src; src = dst; dst = t;
-    if (groups == 1) break;
-  }
-  if (src != buf) {
-    for (int i = threadIdx.x; i < k; i += blockDim.x) buf[i] = src[i];
-    __syncthreads();
-  }
+// LDS bytes the callers of wg_topk_rank set aside for n keys: keys (padded to 64), 64
+// selected keys, and the candidate scratch.
+__host__ __device__ constexpr int topk_lds_bytes(int n, int k) {
+  return ((n + 63) & ~63) * 8 + 64 * 8 + topk_scratch_bytes(n, k);
 }
 
 // ------------------------------------------------------------------------------------
@@ -246,6 +265,13 @@ __device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
 __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 64-bit device-coherent store / load (single-copy atomic): a value and its launch tag.
+__device__ __forceinline__ void st_dev64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Wait until every memory operation this thread issued has completed.
 __device__ __forceinline__ void stores_complete() { __builtin_amdgcn_s_waitcnt(0); }
 // Make data that other workgroups completed before their flag visible to this one.
@@ -254,6 +280,26 @@ __device__ __forceinline__ void acquire_dev() {
 }
 
 constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz constant clock
+
+// Spin until the 64-bit word at p carries `tag` in its upper half and return it: the data
+// and its arrival signal travel in one store, so a reader needs one round trip, not a flag
+// read followed by a data read (bounded; an expired wait sets `errbit` and returns the
+// stale word).
+__device__ inline uint64_t wait_tagged(const uint64_t* p, uint32_t tag, uint32_t* err,
+                                       uint32_t errbit) {
+  uint64_t v = ld_dev64(p);
+  if ((uint32_t)(v >> 32) == tag) return v;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    v = ld_dev64(p);
+    if ((uint32_t)(v >> 32) == tag) return v;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+      __hip_atomic_fetch_or(err, errbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return v;
+    }
+  }
+}
 
 
 // Control block at the start of every layer workspace (device memory, cleared at layer
@@ -269,7 +315,7 @@ struct Ctrl {
   uint32_t epoch;               // launches completed on this workspace
   uint32_t err;                 // sticky error bits (read and cleared by moe_layer_check)
   uint32_t pad0[30];
-  uint32_t router[kGroups][32]; // router workgroups that published their logits
+  uint32_t spare[kGroups][32];  // (unused: router logits carry their own launch tag)
   uint32_t done[kGroups][32];   // workgroups that published their partial output
   uint32_t phase2[kGroups][32]; // workgroups that published their channel scores
 };

@@ -73,7 +73,8 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   if (c.tid == 0) arrive(ctrl->phase2, c.wg);  // keeps that family in step (unused here)
 
   // 1. router rows, spread over the first workgroups
-  router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.logits_ws, ctrl, c);
+  router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.rlog, reinterpret_cast<float*>(big),
+                       reinterpret_cast<uint32_t*>(s_int), c);
 
   // 2. shared experts (independent of routing): flat channel f of [NS][IS] is row f
   if (a.NS > 0) {
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   }
 
   // 3. routed experts: flat channel f = slot * I + j
-  fetch_routing(a.route_inside, a.logits_ws, a.ids_in, a.w_in, a.E, a.k, ctrl,
+  fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
                 reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
   {
     const long long nrc = (long long)a.k * a.I;
@@ -152,8 +153,7 @@ int b1_lds_bytes(int H, int threads, int E, int k) {
   const int red = 2 * (threads / kWave) * kMaxNP * 4;
   const int small = (16 + 64 + 64) * 4;
   const int ybuf = nteams * H * 4;
-  const int ek = (E + 63) & ~63;
-  const int topk = (ek + ((E + 63) / 64) * k + 64) * 8;
+  const int topk = topk_lds_bytes(E, k);
   const int reduce = threads * 4;
   int big = ybuf > topk ? ybuf : topk;
   big = big > reduce ? big : reduce;

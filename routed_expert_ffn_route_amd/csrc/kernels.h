@@ -22,7 +22,7 @@ struct B1Args {
   const void* sh_down_t;
   const int32_t* ids_in;                // given routing [k] or null
   const float* w_in;
-  float* logits_ws;                     // [E]
+  uint64_t* rlog;                       // [E] router logits with their launch tag
   int32_t* ids_ws;                      // [k]
   float* w_ws;                          // [k]
   float* partials;                      // [P][H]

@@ -25,20 +25,6 @@ __device__ __forceinline__ typename Fmt<dt>::Raw zero_raw() {
   return r;
 }
 
-// Keep a loaded chunk (live) or replace it by zeros.  Loads are always issued (from an
-// in-bounds address) and masked afterwards: a load under a branch makes the compiler wait for
-// every outstanding load at the join, which would serialise the two pipeline stages.
-template <DT dt>
-__device__ __forceinline__ typename Fmt<dt>::Raw mask_raw(typename Fmt<dt>::Raw r, bool live) {
-  const uint32_t m = live ? 0xFFFFFFFFu : 0u;
-  uint32_t w[sizeof(r) / 4];
-  __builtin_memcpy(w, &r, sizeof(r));
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(r) / 4); ++i) w[i] &= m;
-  __builtin_memcpy(&r, w, sizeof(r));
-  return r;
-}
-
 template <DT dt, int CPT>
 __device__ __forceinline__ float chunk_dot(const typename Fmt<dt>::Raw (&r)[CPT],
                                            const float (&xv)[CPT * 8]) {
@@ -96,13 +82,12 @@ __device__ __forceinline__ void team_dots(const void* base, const uint8_t* scale
   for (int q = 0; q < C; ++q) {
     const bool ok = rows[q] >= 0;
     const size_t rr = ok ? (size_t)rows[q] : 0;
-    const void* p = uniform_ptr(row_ptr<dt>(base, rr, c.H));
-    const uint8_t* sp = scales ? uniform_ptr(scale_row_ptr(scales, rr, c.H)) : nullptr;
+    const void* p = row_ptr<dt>(base, rr, c.H);
+    const uint8_t* sp = scales ? scale_row_ptr(scales, rr, c.H) : nullptr;
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
       const int ch = c.t + m * c.tsz;
-      const int chc = ch < c.nch ? ch : c.nch - 1;
-      r[q][m] = mask_raw<dt>(F::load(p, sp, chc), ok && ch < c.nch);
+      r[q][m] = (ok && ch < c.nch) ? F::load(p, sp, ch) : zero_raw<dt>();
     }
   }
   constexpr int NP = NextPow2<C>::value;
@@ -145,21 +130,20 @@ __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G,
     const bool ok = row[q] >= 0;
     const size_t r = ok ? (size_t)row[q] : 0;
     // the row is the same for every lane of the wave (one team = whole waves)
-    const void* vp = uniform_ptr(row_ptr<dt>(V, r, c.H));
-    const void* dp = uniform_ptr(row_ptr<dt>(D, r, c.H));
-    const uint8_t* vsp = Vs ? uniform_ptr(scale_row_ptr(Vs, r, c.H)) : nullptr;
-    const uint8_t* dsp = Ds ? uniform_ptr(scale_row_ptr(Ds, r, c.H)) : nullptr;
-    const void* gp = HAS_G ? uniform_ptr(row_ptr<dt>(G, r, c.H)) : nullptr;
-    const uint8_t* gsp = (HAS_G && Gs) ? uniform_ptr(scale_row_ptr(Gs, r, c.H)) : nullptr;
+    const void* vp = row_ptr<dt>(V, r, c.H);
+    const void* dp = row_ptr<dt>(D, r, c.H);
+    const uint8_t* vsp = Vs ? scale_row_ptr(Vs, r, c.H) : nullptr;
+    const uint8_t* dsp = Ds ? scale_row_ptr(Ds, r, c.H) : nullptr;
+    const void* gp = HAS_G ? row_ptr<dt>(G, r, c.H) : nullptr;
+    const uint8_t* gsp = (HAS_G && Gs) ? scale_row_ptr(Gs, r, c.H) : nullptr;
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
       const int ch = c.t + m * c.tsz;
-      const int chc = ch < c.nch ? ch : c.nch - 1;
       const bool live = ok && ch < c.nch;
       if constexpr (HAS_G)
-        st.g[q][m] = mask_raw<dt>(F::load(gp, gsp, chc), live);
-      st.v[q][m] = mask_raw<dt>(F::load(vp, vsp, chc), live);
-      st.d[q][m] = mask_raw<dt>(F::load(dp, dsp, chc), live);
+        st.g[q][m] = live ? F::load(gp, gsp, ch) : zero_raw<dt>();
+      st.v[q][m] = live ? F::load(vp, vsp, ch) : zero_raw<dt>();
+      st.d[q][m] = live ? F::load(dp, dsp, ch) : zero_raw<dt>();
     }
   }
 }
@@ -240,44 +224,62 @@ __device__ inline void stream_channels(const void* G, const void* V, const void*
   }
 }
 
-// Router rows of this workgroup (one row per team per round), published with
-// device-coherent stores; every router workgroup then arrives on the router counters
-// (also when the routing is given and no row is computed).
+// Router logits, spread over the first workgroups (one team per row).  Each logit is
+// published as one 64-bit word: the launch tag (epoch + 1) in the upper half and the fp32
+// bits in the lower half, so readers wait on the data itself.  Every workgroup also learns
+// the launch epoch here (thread 0 loaded it at the start; the router rows hide the wait).
+// `buf` is LDS of at least ceil(E / P) + nteams floats; s_ep one LDS word.
 template <DT RT, int CPT>
 __device__ inline void router_rows(bool compute, const void* router, int E,
-                                   const float (&xv)[CPT * 8], float* logits, Ctrl* ctrl,
-                                   Ctx& c) {
+                                   const float (&xv)[CPT * 8], uint64_t* rlog, float* buf,
+                                   uint32_t* s_ep, Ctx& c) {
   const int n_router_wgs = min(c.P, (E + c.nteams - 1) / c.nteams);
-  if (c.wg >= n_router_wgs) return;
-  if (compute) {
-    for (int base = c.wg * c.nteams; base < E; base += c.P * c.nteams) {
+  const bool mine = compute && c.wg < n_router_wgs;
+  int nloc = 0;
+  if (mine) {
+    for (int base = c.wg * c.nteams; base < E; base += c.P * c.nteams, nloc += c.nteams) {
       const int e = base + c.team;
       const long long rows[1] = {e < E ? (long long)e : -1};
       float l[1];
       team_dots<RT, 1, CPT>(router, nullptr, rows, xv, c, l);
-      if (c.t == 0 && e < E) st_dev(logits + e, l[0]);
+      if (c.t == 0) buf[nloc + c.team] = l[0];
     }
-    stores_complete();
   }
+  if (c.tid == 0) *s_ep = c.epoch;
   __syncthreads();
-  if (c.tid == 0) arrive(ctrl->router, c.wg);
+  c.epoch = *s_ep;
+  if (mine) {
+    const uint64_t tag = (uint64_t)(c.epoch + 1u) << 32;
+    for (int i = c.tid; i < nloc; i += c.nthreads) {
+      const int e = c.wg * c.nteams + (i / c.nteams) * c.P * c.nteams + i % c.nteams;
+      if (e < E) st_dev64(rlog + e, tag | __float_as_uint(buf[i]));
+    }
+  }
 }
 
 // Exact top-k of the E logits and the softmax over the k selected, computed by the whole
-// workgroup into LDS (s_ids, s_w).  `keys` is LDS scratch of ceil(E/64)*64 + ceil(E/64)*k
-// + 64 entries.
-__device__ inline void topk_local(const float* logits, int E, int k, uint64_t* keys,
-                                  int* s_ids, float* s_w, const Ctx& c) {
-  uint64_t* tmp = keys + ((E + 63) & ~63);
-  for (int e = c.tid; e < E; e += c.nthreads) keys[e] = make_key(ld_dev(logits + e), (uint32_t)e);
+// workgroup into LDS (s_ids, s_w).  `keys` is LDS scratch of topk_lds_bytes(E) bytes.
+__device__ inline void topk_local(const uint64_t* rlog, int E, int k, uint64_t* keys,
+                                  int* s_ids, float* s_w, uint32_t* err, const Ctx& c) {
+  const int E64 = (E + 63) & ~63;
+  uint64_t* sel = keys + E64;
+  const uint32_t tag = c.epoch + 1u;
+  for (int e = c.tid; e < E64; e += c.nthreads) {
+    uint64_t key = 0ull;  // padding: below every real key
+    if (e < E) {
+      const uint64_t v = wait_tagged(rlog + e, tag, err, kErrRouteWait);
+      key = make_key(__uint_as_float((uint32_t)v), (uint32_t)e);
+    }
+    keys[e] = key;
+  }
   __syncthreads();
-  wg_topk_keys(keys, tmp, E, k);
+  wg_topk_rank(keys, sel + 64, E, k, sel);
   if (c.tid < kWave) {
-    const float l0 = key_value(keys[0]);
-    const float ex = c.tid < k ? expf(key_value(keys[c.tid]) - l0) : 0.0f;
+    const float l0 = key_value(sel[0]);
+    const float ex = c.tid < k ? expf(key_value(sel[c.tid]) - l0) : 0.0f;
     const float sum = wave_sum(ex);
     if (c.tid < k) {
-      s_ids[c.tid] = (int)key_index(keys[c.tid]);
+      s_ids[c.tid] = (int)key_index(sel[c.tid]);
       s_w[c.tid] = ex / sum;
     }
   }
@@ -288,14 +290,11 @@ __device__ inline void topk_local(const float* logits, int E, int k, uint64_t* k
 // router workgroup has published its logits, then select the top-k in this workgroup (each
 // workgroup sorts the E logits itself, which costs less than one more cross-workgroup
 // hand-off).  Given routing: copy ids/w.  Out-of-range ids are reported and skipped (-1).
-__device__ inline void fetch_routing(bool inside, const float* logits, const int32_t* ids_in,
+__device__ inline void fetch_routing(bool inside, const uint64_t* rlog, const int32_t* ids_in,
                                      const float* w_in, int E, int k, Ctrl* ctrl,
                                      uint64_t* keys, int* s_ids, float* s_w, const Ctx& c) {
   if (inside) {
-    const int n_router_wgs = min(c.P, (E + c.nteams - 1) / c.nteams);
-    if (c.tid == 0) wait_family(ctrl->router, n_router_wgs, c.epoch, &ctrl->err, kErrRouteWait);
-    __syncthreads();
-    topk_local(logits, E, k, keys, s_ids, s_w, c);
+    topk_local(rlog, E, k, keys, s_ids, s_w, &ctrl->err, c);
     return;
   }
   if (c.tid < k) {

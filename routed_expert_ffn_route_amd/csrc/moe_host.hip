@@ -46,7 +46,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
-  size_t ctrl, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
+  size_t ctrl, rlog, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
       union_slots, cs_g, cs_s, cs_y, xh, xl, act, part, total;
 };
 
@@ -98,6 +98,7 @@ Layout layout_of(const moe_layer_desc* d) {
   };
   const size_t B = (size_t)d->max_batch, E = (size_t)d->n_experts, k = (size_t)d->top_k;
   L.ctrl = take(sizeof(Ctrl));
+  L.rlog = take(E * 8);
   L.logits = take(B * E * 4);
   L.ids = take(B * k * 4);
   L.w = take(B * k * 4);
@@ -181,7 +182,7 @@ static B1Args b1_args(moe_layer layer, const float* x, const int32_t* ids, const
   a.sh_down_t = layer->w.sh_down_t;
   a.ids_in = ids;
   a.w_in = w;
-  a.logits_ws = layer->at<float>(layer->L.logits);
+  a.rlog = layer->at<uint64_t>(layer->L.rlog);
   a.ids_ws = layer->at<int32_t>(layer->L.ids);
   a.w_ws = layer->at<float>(layer->L.w);
   a.partials = layer->at<float>(layer->L.partials);
@@ -270,7 +271,8 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_weights* weigh
   l->threads = kThreads;
   l->magic = kMagic;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  e = hipMemsetAsync(l->ctrl(), 0, sizeof(Ctrl), s);
+  // control block and tagged router logits start at zero (tag 0 is never a launch's)
+  e = hipMemsetAsync(l->ctrl(), 0, L.rlog + (size_t)d.n_experts * 8, s);  // ctrl is at offset 0
   if (e == hipSuccess && d.kind == MOE_EXPERT_SWIGLU)
     e = launch_row_norms(w.down_t, w.down_scale, to_dt(d.expert_dtype),
                          (size_t)d.n_experts * d.inter, d.hidden, l->at<float>(L.dnorm), s);

@@ -78,23 +78,28 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* logits, float* l
                                                    float* w) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
-  uint64_t* tmp = keys + ((E + 63) & ~63);
+  const int E64 = (E + 63) & ~63;
+  uint64_t* sel = keys + E64;
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
     const float* lb = logits + (size_t)b * E;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      const float l = lb[e];
-      keys[e] = make_key(l, (uint32_t)e);
-      if (logits_copy) logits_copy[(size_t)b * E + e] = l;
+    for (int e = threadIdx.x; e < E64; e += blockDim.x) {
+      uint64_t key = 0ull;  // padding: below every real key
+      if (e < E) {
+        const float l = lb[e];
+        key = make_key(l, (uint32_t)e);
+        if (logits_copy) logits_copy[(size_t)b * E + e] = l;
+      }
+      keys[e] = key;
     }
     __syncthreads();
-    wg_topk_keys(keys, tmp, E, k);
+    wg_topk_rank(keys, sel + 64, E, k, sel);
     if (threadIdx.x < kWave) {
       const int i = threadIdx.x;
-      const float l0 = key_value(keys[0]);
-      const float ex = i < k ? expf(key_value(keys[i]) - l0) : 0.0f;
+      const float l0 = key_value(sel[0]);
+      const float ex = i < k ? expf(key_value(sel[i]) - l0) : 0.0f;
       const float sum = wave_sum(ex);
       if (i < k) {
-        ids[(size_t)b * k + i] = (int32_t)key_index(keys[i]);
+        ids[(size_t)b * k + i] = (int32_t)key_index(sel[i]);
         w[(size_t)b * k + i] = ex / sum;
       }
     }
@@ -250,7 +255,7 @@ hipError_t launch_route(const RouteArgs& a, DT rt, hipStream_t s) {
     if (e != hipSuccess) return e;
     lsrc = a.logits;
   }
-  const int lds = (((a.E + 63) & ~63) + ((a.E + 63) / 64) * a.k + 64) * 8;
+  const int lds = topk_lds_bytes(a.E, a.k);
   const int grid = a.B < 4096 ? a.B : 4096;
   float* copy = (a.logits_in && a.logits) ? a.logits : nullptr;
   hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(256), lds, s, lsrc, copy, a.E, a.k, a.B,
