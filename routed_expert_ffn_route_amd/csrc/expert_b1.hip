@@ -134,10 +134,9 @@ template <DT dt> constexpr int channels_per_batch() {
 template <DT ET, DT ST, DT RT>
 hipError_t launch_cpt(const B1Launch& L, int wgs, int threads, int lds, hipStream_t s) {
   constexpr int CR = channels_per_batch<ET>(), CS = channels_per_batch<ST>();
-  const int cpt = (L.a.H / 8 + L.tsz - 1) / L.tsz;
-  if (cpt <= 1) return launch_t<ET, ST, RT, CR, CS, 1>(L, wgs, threads, lds, s);
-  if (cpt <= 2) return launch_t<ET, ST, RT, 1, 1, 2>(L, wgs, threads, lds, s);
-  return hipErrorInvalidValue;
+  // team_size gives one chunk per thread for every H the host admits (H <= 8192)
+  if (L.a.H / 8 > L.tsz) return hipErrorInvalidValue;
+  return launch_t<ET, ST, RT, CR, CS, 1>(L, wgs, threads, lds, s);
 }
 
 }  // namespace
