@@ -29,13 +29,13 @@ namespace {
 using namespace lc;
 
 constexpr int kMaxNP = 16;
-constexpr int kGateBatch = 4;
+constexpr int kGateBatch = 8;  // gate rows per team per batch (one batch covers a share)
+constexpr int kPrefetch = 4;   // likeliest kept channels per share warmed in L2
 
 struct CSLaunch {
   B1Args a;
   const float* dnorm;  // [E*I]
-  float* g_ws;         // [k*I]
-  float* s_ws;         // [k*I]
+  uint64_t* s_ws;      // [k*I] launch-tagged scores
   int32_t* kept_out;   // [K]
   int K, mode, R, SW, tsz;
 };
@@ -43,22 +43,12 @@ struct CSLaunch {
 // Exclusive prefix sum over the workgroup (sh: LDS of nwaves+1 ints).  *total = sum.
 __device__ inline int block_excl_scan(int v, int* sh, const Ctx& c, int* total) {
   const int lane = c.lane, wave = c.tid >> 6, nw = c.nthreads >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == kWave - 1) sh[wave] = x;
   __syncthreads();
   if (wave == 0) {
     const int wv = lane < nw ? sh[lane] : 0;
-    int s = wv;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int y = __shfl_up(s, d, kWave);
-      if (lane >= d) s += y;
-    }
+    const int s = wave_incl_scan(wv);
     if (lane < nw) sh[lane] = s - wv;
     if (lane == nw - 1) sh[nw] = s;
   }
@@ -69,82 +59,74 @@ __device__ inline int block_excl_scan(int v, int* sh, const Ctx& c, int* total) 
   return res;
 }
 
-// Select the K largest of n non-negative scores (as uint32 bit patterns in `u`, which
-// order like the floats), ties to the lower index; write the kept indices ascending to
-// `kept`.  Returns the kept count.  `hist` is LDS of 256 ints, `sh` of 32 ints.
-__device__ inline int select_topk_ascending(const uint32_t* u, int n, int K, int* kept,
+// The K-th largest of n non-negative scores (as uint32 bit patterns in `u`, which order
+// like the floats), ties to the lower index: returns T (the K-th largest pattern) and, in
+// *need, how many of the values equal to T are kept (the lowest-indexed ones).  T is found
+// digit by digit, most significant first (11, 11 and 10 bits): a histogram of the digit
+// over the values that match the digits found so far, and the digit where the running
+// count from the top reaches the remaining need.  Requires 0 < K < n.  `hist` is LDS of
+// kSelBins ints, `sh` of 48 ints.
+constexpr int kSelBins = 2048;
+__device__ inline uint32_t select_threshold(const uint32_t* u, int n, int K, int* need_out,
                                             int* hist, int* sh, const Ctx& c) {
-  if (K <= 0) return 0;
-  const int seg = (n + c.nthreads - 1) / c.nthreads;
-  const int f0 = min(n, c.tid * seg), f1 = min(n, f0 + seg);
-  if (K >= n) {
-    for (int f = c.tid; f < n; f += c.nthreads) kept[f] = f;
-    __syncthreads();
-    return n;
-  }
   uint32_t prefix = 0, mask = 0;
   int need = K;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = c.tid; i < 256; i += c.nthreads) hist[i] = 0;
+  const int shifts[3] = {21, 10, 0};
+  const int widths[3] = {11, 11, 10};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = shifts[pass];
+    const uint32_t dmask = (1u << widths[pass]) - 1u;
+    const int nb = 1 << widths[pass];
+    for (int i = c.tid; i < nb; i += c.nthreads) hist[i] = 0;
     __syncthreads();
     for (int f = c.tid; f < n; f += c.nthreads) {
       const uint32_t v = u[f];
-      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255], 1);
+      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & dmask], 1);
     }
     __syncthreads();
-    if (c.tid < kWave) {
-      // lane l holds digits 255-4l .. 252-4l (descending); find where `need` falls
-      int cnt[4], s = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { cnt[q] = hist[255 - 4 * c.lane - q]; s += cnt[q]; }
-      int incl = s;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(incl, d, kWave);
-        if (c.lane >= d) incl += y;
-      }
-      int before = incl - s;  // count of larger digits
-      if (before < need && need <= incl) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (before < need && need <= before + cnt[q]) {
-            sh[0] = 255 - 4 * c.lane - q;
-            sh[1] = need - before;
-          }
-          before += cnt[q];
+    // thread t owns the bins nb-1-b for b in [t*per, (t+1)*per): counts from the top
+    const int per = (nb + c.nthreads - 1) / c.nthreads;
+    int local = 0;
+    for (int b = c.tid * per; b < (c.tid + 1) * per && b < nb; ++b) local += hist[nb - 1 - b];
+    int total;
+    const int before0 = block_excl_scan(local, sh + 2, c, &total);
+    if (before0 < need && need <= before0 + local) {
+      int before = before0;
+      for (int b = c.tid * per; b < (c.tid + 1) * per && b < nb; ++b) {
+        const int cnt = hist[nb - 1 - b];
+        if (before < need && need <= before + cnt) {
+          sh[0] = nb - 1 - b;
+          sh[1] = need - before;
         }
+        before += cnt;
       }
     }
     __syncthreads();
     const uint32_t digit = (uint32_t)sh[0];
     need = sh[1];
     prefix |= digit << shift;
-    mask |= 0xFFu << shift;
+    mask |= dmask << shift;
     __syncthreads();
   }
-  const uint32_t T = prefix;  // the K-th largest score; take `need` of the ties, lowest first
-  int eq = 0;
-  for (int f = f0; f < f1; ++f) eq += u[f] == T;
-  int tot;
-  int eq_base = block_excl_scan(eq, sh + 2, c, &tot);
-  int mine = 0;
-  for (int f = f0, r = eq_base; f < f1; ++f) {
+  *need_out = need;
+  return prefix;
+}
+
+// Counts, over u[0 .. m), of the values above T and of those equal to T (whole workgroup;
+// sh: LDS of 48 ints).
+__device__ inline void count_before(const uint32_t* u, int m, uint32_t T, int* gt, int* eq,
+                                    int* sh, const Ctx& c) {
+  int a = 0, b = 0;
+  for (int f = c.tid; f < m; f += c.nthreads) {
     const uint32_t v = u[f];
-    const bool take = v > T || (v == T && r < need);
-    r += v == T;
-    mine += take;
+    a += v > T ? 1 : 0;
+    b += v == T ? 1 : 0;
   }
-  int kept_total;
-  int base = block_excl_scan(mine, sh + 2, c, &kept_total);
-  for (int f = f0, r = eq_base; f < f1; ++f) {
-    const uint32_t v = u[f];
-    const bool take = v > T || (v == T && r < need);
-    r += v == T;
-    if (take) kept[base++] = f;
-  }
-  __syncthreads();
-  return kept_total;
+  int ta, tb;
+  block_excl_scan(a, sh + 2, c, &ta);
+  block_excl_scan(b, sh + 2, c, &tb);
+  *gt = ta;
+  *eq = tb;
 }
 
 template <DT ET, DT ST, DT RT, int C, int CPT>
@@ -171,8 +153,8 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
   float* s_w = reinterpret_cast<float*>(s_ids + 64);                // [64]
-  int* hist = reinterpret_cast<int*>(s_w + 64);                     // [256]
-  int* sh = hist + 256;                                             // [48]
+  int* hist = reinterpret_cast<int*>(s_w + 64);                     // [kSelBins]
+  int* sh = hist + kSelBins;                                        // [48]
   float* big = reinterpret_cast<float*>(sh + 48);
   Ctrl* ctrl = a.ctrl;
   const int I = a.I;
@@ -197,20 +179,29 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
                 reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
 
-  // 2. gate pass over this workgroup's share of the candidates
+  // 2. gate pass over this workgroup's share [g0, g1) of the candidates; g stays in LDS
+  const int g0 = (int)((long long)n * c.wg / c.P), g1 = (int)((long long)n * (c.wg + 1) / c.P);
+  uint32_t* sbits = reinterpret_cast<uint32_t*>(big);  // [n] all scores
+  float* s_g = reinterpret_cast<float*>(sbits + n);     // [g1 - g0] this share's gate values
+  int* loc = reinterpret_cast<int*>(s_g + (g1 - g0));   // [g1 - g0] this share's kept channels
+  float* s_loc = reinterpret_cast<float*>(loc + (g1 - g0));  // [g1 - g0] this share's scores
   {
-    const int f0 = (int)((long long)n * c.wg / c.P), f1 = (int)((long long)n * (c.wg + 1) / c.P);
-    for (int base = f0; base < f1; base += c.nteams * kGateBatch) {
+    for (int base = g0; base < g1; base += c.nteams * kGateBatch) {
       long long rows[kGateBatch];
 #pragma unroll
       for (int q = 0; q < kGateBatch; ++q) {
         const int f = base + c.team * kGateBatch + q;
         rows[q] = -1;
-        if (f < f1) {
+        if (f < g1) {
           const int e = s_ids[f / I];
           if (e >= 0) rows[q] = (long long)e * I + (f % I);
         }
       }
+      // the down-row norm of this thread's candidate is loaded with the gate rows
+      long long myrow = -1;
+#pragma unroll
+      for (int q = 0; q < kGateBatch; ++q) myrow = (q == c.t) ? rows[q] : myrow;
+      const float dn = (c.t < kGateBatch && myrow >= 0) ? L.dnorm[myrow] : 0.0f;
       float g[kGateBatch];
       team_dots<ET, kGateBatch, CPT>(a.gate, a.gate_s, rows, xv, c, g);
       if (c.t < kGateBatch) {
@@ -218,61 +209,115 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
 #pragma unroll
         for (int q = 0; q < kGateBatch; ++q) gq = (q == c.t) ? g[q] : gq;
         const int f = base + c.team * kGateBatch + c.t;
-        if (f < f1) {
+        if (f < g1) {
           const int slot = f / I;
-          const long long row = rows[c.t];
+          const long long row = myrow;
           float s = 0.0f;
           if (row >= 0) {
-            s = fabsf(silu(gq)) * L.dnorm[row];
+            s = fabsf(silu(gq)) * dn;
             if (L.mode == 1) s *= s_w[slot];
           }
-          st_dev(L.g_ws + f, gq);
-          st_dev(L.s_ws + f, s);
+          s_g[f - g0] = gq;
+          s_loc[f - g0] = s;
+          st_dev64(L.s_ws + f, ((uint64_t)(c.epoch + 1u) << 32) | __float_as_uint(s));
         }
       }
     }
   }
 
-  // 3. grid barrier: all scores written
-  stores_complete();
+  // 2b. warm L2 with the up and down rows of this share's likeliest kept channels (the
+  // kPrefetch highest local scores, one wave each, a load per 128-byte line): the kept
+  // stream reads them right after the selection, and these loads overlap the gathering of
+  // the other workgroups' scores.  Which rows are warmed affects only timing.
+  uint32_t warm[4] = {0, 0, 0, 0};
   __syncthreads();
-  if (c.tid == 0) {
-    arrive(ctrl->phase2, c.wg);
-    wait_family(ctrl->phase2, c.P, c.epoch, &ctrl->err, kErrPhaseWait);
-  }
-  __syncthreads();
-
-  // 4. the same selection in every workgroup
-  uint32_t* sbits = reinterpret_cast<uint32_t*>(big);
-  int* kept = reinterpret_cast<int*>(sbits + n);
-  for (int f = c.tid; f < n; f += c.nthreads) sbits[f] = __float_as_uint(ld_dev(L.s_ws + f));
-  __syncthreads();
-  const int K = select_topk_ascending(sbits, n, L.K, kept, hist, sh, c);
-  if (c.wg == 0)
-    for (int i = c.tid; i < K; i += c.nthreads) L.kept_out[i] = kept[i];
-
-  // 5. the kept channels: up row and down row only, gate value from the gate pass
   {
-    const float* g_ws = L.g_ws;
-    stream_channels<ET, C, CPT, false>(
-        nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, (long long)K * c.wg / c.P,
-        (long long)K * (c.wg + 1) / c.P,
-        [=](long long i, long long& row, float& wt, float& gv) {
-          const int f = kept[i];
-          const int slot = f / I;
-          const int e = s_ids[slot];
-          if (e >= 0) {
-            row = (long long)e * I + (f % I);
-            wt = s_w[slot];
-            gv = ld_dev(g_ws + f);
+    const int share = g1 - g0;
+    const int wave = c.tid >> 6;
+    if (wave < kPrefetch && wave < share) {
+      const int i = c.lane;
+      const float me = i < share ? s_loc[i] : -1.0f;
+      int rank = 0;
+      for (int j = 0; j < min(share, kWave); ++j) {
+        const float o = s_loc[j];
+        rank += (o > me || (o == me && j < i)) ? 1 : 0;
+      }
+      const unsigned long long hit = __ballot(i < share && rank == wave);
+      if (hit) {
+        const int src = __ffsll(hit) - 1;
+        const int f = g0 + src;
+        const int e = s_ids[f / I];
+        if (e >= 0 && s_loc[src] > 0.0f) {
+          const size_t row = (size_t)e * I + (f % I);
+          const size_t rb = Fmt<ET>::row_bytes(a.H);
+          const uint8_t* p = reinterpret_cast<const uint8_t*>(c.lane < 32 ? a.up : a.down_t) +
+                             row * rb;
+          // up to 4 lines per lane (rows of at most 16 KB); each value stays in its own
+          // register until the end of the kernel, so nothing waits for these loads
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const size_t off = (size_t)(c.lane & 31) * 128 + (size_t)q * 32 * 128;
+            warm[q] = *reinterpret_cast<const uint32_t*>(p + (off < rb ? off : rb - 4));
           }
-        },
-        xv, yv, c);
+        }
+      }
+    }
   }
+
+  // 3. every workgroup gathers all k*I scores (each published with its launch tag, so
+  // waiting on the scores themselves is the grid-wide hand-off)
+  for (int f = c.tid; f < n; f += c.nthreads)
+    sbits[f] = (uint32_t)wait_tagged(L.s_ws + f, c.epoch + 1u, &ctrl->err, kErrPhaseWait);
+  __syncthreads();
+
+  // 4. the same threshold in every workgroup; each keeps the channels of its own share:
+  // above T, or equal to T and among the first `need` ties in flat-id order
+  int nk = 0, kept_before = 0;
+  if (L.K >= n) {
+    for (int f = g0 + c.tid; f < g1; f += c.nthreads) loc[f - g0] = f;
+    nk = g1 - g0;
+    kept_before = g0;
+  } else if (L.K > 0) {
+    int need;
+    const uint32_t T = select_threshold(sbits, n, L.K, &need, hist, sh, c);
+    int gt, eq;
+    count_before(sbits, g0, T, &gt, &eq, sh, c);
+    kept_before = gt + min(eq, need);
+    if (c.tid == 0) {
+      int r = eq;
+      for (int f = g0; f < g1; ++f) {
+        const uint32_t v = sbits[f];
+        const bool take = v > T || (v == T && r < need);
+        r += v == T ? 1 : 0;
+        if (take) loc[nk++] = f;
+      }
+      sh[0] = nk;
+    }
+    __syncthreads();
+    nk = sh[0];
+  }
+  __syncthreads();
+  for (int i = c.tid; i < nk; i += c.nthreads) L.kept_out[kept_before + i] = loc[i];
+
+  // 5. the kept channels of this share: up row and down row only, gate value from LDS
+  stream_channels<ET, C, CPT, false>(
+      nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, 0, nk,
+      [=](long long i, long long& row, float& wt, float& gv) {
+        const int f = loc[i];
+        const int slot = f / I;
+        const int e = s_ids[slot];
+        if (e >= 0) {
+          row = (long long)e * I + (f % I);
+          wt = s_w[slot];
+          gv = s_g[f - g0];
+        }
+      },
+      xv, yv, c);
   __syncthreads();  // `big` is reused by the reduction below
 
   // 6. deterministic cross-workgroup sum
   reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, c);
+  s_int[15] = warm[0] ^ warm[1] ^ warm[2] ^ warm[3];  // keeps the warming loads
 }
 
 template <DT ET, DT ST, DT RT, int C, int CPT>
@@ -299,11 +344,12 @@ hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStrea
 
 }  // namespace
 
-int cs_lds_bytes(int H, int threads, int E, int k, int I) {
+int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs) {
   const int nteams = threads / team_size(H);
-  const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + 256 + 48) * 4;
+  const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + kSelBins + 48) * 4;
   const int n = k * I;
-  const int sel = 2 * n * 4;
+  const int share = (n + wgs - 1) / wgs;
+  const int sel = (n + 3 * share) * 4;  // all scores; this share's gate values, kept ids, scores
   const int ybuf = nteams * H * 4;
   const int topk = topk_lds_bytes(E, k);
   int big = sel > ybuf ? sel : ybuf;
@@ -312,20 +358,19 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I) {
   return fixed + big;
 }
 
-hipError_t launch_cs(const B1Args& a, const float* dnorm, float* g_ws, float* s_ws,
+hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* s_ws,
                      int32_t* kept, int K, int mode, DT et, DT st, DT rt, int wgs, int threads,
                      hipStream_t s) {
   CSLaunch L;
   L.a = a;
   L.dnorm = dnorm;
-  L.g_ws = g_ws;
   L.s_ws = s_ws;
   L.kept_out = kept;
   L.K = K;
   L.mode = mode;
   L.tsz = team_size(a.H);
   lc::reducer_split(a.H, wgs, &L.R, &L.SW);
-  const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I);
+  const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I, wgs);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)
     return launch_cpt<DT::F32, DT::F32, DT::F32>(L, wgs, threads, lds, s);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::BF16)

@@ -112,6 +112,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave: Hillis-Steele steps inside each row
+// of 16 lanes (DPP row shifts by 1, 2, 4, 8; lanes without a source add 0), then the last
+// lane of a row is broadcast into the rows above it (row_bcast:15 into rows 1 and 3,
+// row_bcast:31 into rows 2 and 3).  No LDS round trips, unlike a shuffle-based scan.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Reduce N values held by every lane of a wave.  On return, lane l holds the wave total of
 // value (l % N) in v[0] (N a power of two <= 64).  Uses N-1 + log2(64/N) exchanges
 // instead of N*6.
@@ -303,23 +317,21 @@ __device__ inline uint64_t wait_tagged(const uint64_t* p, uint32_t tag, uint32_t
 
 
 // Control block at the start of every layer workspace (device memory, cleared at layer
-// creation).  Hand-offs between workgroups use arrival counters that only ever grow: launch
-// number n (= the epoch read at the start of the launch) is complete for a counter group
-// when the group reads (n + 1) * (its participant count).  Every launch increments every
-// counter family once per participating workgroup (also families its kernel does not
-// wait on), so the expected values stay in step across kernels sharing a workspace.  The
-// counters of one family are split over kGroups cache lines, so that arrivals contend in
-// groups of P/kGroups instead of all P on one address.
+// creation).  `epoch` counts the batch-1 launches completed on this workspace; a launch
+// reads it at its start and tags the data it hands between workgroups (router logits,
+// channel scores) with epoch + 1, so readers wait on the data itself.  The partial outputs
+// are handed over with arrival counters that only ever grow: launch n is complete for a
+// counter group when the group reads (n + 1) * (its participant count); the counters are
+// split over kGroups cache lines, so that arrivals contend in groups of P/kGroups instead
+// of all P on one address.
 constexpr int kGroups = 16;
 struct Ctrl {
   uint32_t epoch;               // launches completed on this workspace
   uint32_t err;                 // sticky error bits (read and cleared by moe_layer_check)
   uint32_t pad0[30];
-  uint32_t spare[kGroups][32];  // (unused: router logits carry their own launch tag)
   uint32_t done[kGroups][32];   // workgroups that published their partial output
-  uint32_t phase2[kGroups][32]; // workgroups that published their channel scores
 };
-static_assert(sizeof(Ctrl) == 128 + 3 * kGroups * 128, "counter groups are 128-byte lines");
+static_assert(sizeof(Ctrl) == 128 + kGroups * 128, "counter groups are 128-byte lines");
 
 enum : uint32_t {
   kErrRouteWait = 1u, kErrReduceWait = 2u, kErrBadId = 4u, kErrPhaseWait = 8u,

@@ -70,7 +70,6 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   for (int i = 0; i < CPT * 8; ++i) yv[i] = 0.0f;
 
   read_epoch(ctrl, c);
-  if (c.tid == 0) arrive(ctrl->phase2, c.wg);  // keeps that family in step (unused here)
 
   // 1. router rows, spread over the first workgroups
   router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.rlog, reinterpret_cast<float*>(big),

@@ -38,10 +38,10 @@ int b1_lds_bytes(int H, int threads, int E, int k);
 int team_size(int H);
 
 // Channel-sparse batch-1 layer (fixed-count top-K keep rule over the k*I candidates).
-hipError_t launch_cs(const B1Args& a, const float* dnorm, float* g_ws, float* s_ws,
-                     int32_t* kept, int K, int mode, DT et, DT st, DT rt, int workgroups,
-                     int threads, hipStream_t s);
-int cs_lds_bytes(int H, int threads, int E, int k, int I);
+hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* s_ws, int32_t* kept,
+                     int K, int mode, DT et, DT st, DT rt, int workgroups, int threads,
+                     hipStream_t s);
+int cs_lds_bytes(int H, int threads, int E, int k, int I, int workgroups);
 
 // Routing: router GEMV for B tokens, then one workgroup per token for top-k + softmax.
 struct RouteArgs {

@@ -47,7 +47,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, rlog, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, cs_g, cs_s, cs_y, xh, xl, act, part, total;
+      union_slots, cs_s, cs_y, xh, xl, act, part, total;
 };
 
 bool desc_valid(const moe_layer_desc* d, std::string* why) {
@@ -109,8 +109,7 @@ Layout layout_of(const moe_layer_desc* d) {
   L.union_offsets = take((E + 1) * 4);
   L.union_slots = take(B * k * 4);
   const size_t kI = d->kind == MOE_EXPERT_SWIGLU ? k * (size_t)d->inter : 0;
-  L.cs_g = take(kI * 4);
-  L.cs_s = take(kI * 4);
+  L.cs_s = take(kI * 8);
   L.cs_y = take(d->kind == MOE_EXPERT_SWIGLU ? (size_t)d->hidden * 4 : 0);
   const bool batched_swiglu = d->kind == MOE_EXPERT_SWIGLU && B > 1;
   const size_t xs =
@@ -491,11 +490,12 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
   if (moe_status e = b1_types(layer, &et, &st, &rt)) return e;
   if (et == DT::MXFP4) return fail(MOE_ERR_UNSUPPORTED, "channel selection for MXFP4 experts");
   if (d.hidden > 4096) return fail(MOE_ERR_UNSUPPORTED, "channel selection needs hidden <= 4096");
-  if (cs_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k, d.inter) > 160 * 1024)
+  if (cs_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k, d.inter, layer->workgroups) >
+      160 * 1024)
     return fail(MOE_ERR_UNSUPPORTED, "k*I=%lld candidates exceed the selection LDS budget", n);
   B1Args a = b1_args(layer, x, ids, w, y ? y : layer->at<float>(layer->L.cs_y));
-  hipError_t e = launch_cs(a, layer->at<float>(layer->L.dnorm), layer->at<float>(layer->L.cs_g),
-                           layer->at<float>(layer->L.cs_s), kept, keep, mode, et, st, rt,
+  hipError_t e = launch_cs(a, layer->at<float>(layer->L.dnorm),
+                           layer->at<uint64_t>(layer->L.cs_s), kept, keep, mode, et, st, rt,
                            layer->workgroups, layer->threads, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "channel-sparse layer launch");
   return ok();
