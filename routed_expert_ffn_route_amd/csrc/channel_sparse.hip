@@ -161,7 +161,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   const int n = a.k * I;
 
   float xv[CPT * 8], yv[CPT * 8];
-  load_x<CPT>(a.x, c, xv);
+  load_x<8, CPT>(a.x, c, xv);
 #pragma unroll
   for (int i = 0; i < CPT * 8; ++i) yv[i] = 0.0f;
 

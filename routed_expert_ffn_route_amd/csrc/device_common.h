@@ -11,7 +11,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum class DT : int { F32 = 0, BF16 = 1, MXFP4 = 2 };
+// MXFP4W is MXFP4 read in 16-element chunks (8 bytes of codes + the block's scale byte per
+// thread and row) instead of 8-element ones: the same bytes, twice as many per load.
+enum class DT : int { F32 = 0, BF16 = 1, MXFP4 = 2, MXFP4W = 3 };
 
 constexpr int kWave = 64;
 constexpr int kTeam = 256;         // threads that cover one weight row together
@@ -27,6 +29,7 @@ constexpr int kChunkElems = 8;     // elements one thread takes from a row per c
 template <DT dt> struct Fmt;
 
 template <> struct Fmt<DT::F32> {
+  static constexpr int kE = 8;  // elements per chunk
   struct Raw { u32x4 a, b; };
   static __device__ __forceinline__ Raw load(const void* row, const uint8_t*, int c) {
     const u32x4* p = reinterpret_cast<const u32x4*>(row) + 2 * c;
@@ -45,6 +48,7 @@ template <> struct Fmt<DT::F32> {
 };
 
 template <> struct Fmt<DT::BF16> {
+  static constexpr int kE = 8;
   struct Raw { u32x4 a; };
   static __device__ __forceinline__ Raw load(const void* row, const uint8_t*, int c) {
     Raw r;
@@ -61,6 +65,7 @@ template <> struct Fmt<DT::BF16> {
 };
 
 template <> struct Fmt<DT::MXFP4> {
+  static constexpr int kE = 8;
   struct Raw { uint32_t q; uint32_t s; };
   static __device__ __forceinline__ Raw load(const void* row, const uint8_t* srow, int c) {
     Raw r;
@@ -78,6 +83,32 @@ template <> struct Fmt<DT::MXFP4> {
     f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.q, sc, 3);
     v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
     v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+  }
+  static __host__ __device__ constexpr size_t row_bytes(int H) { return (size_t)H / 2; }
+  static __host__ __device__ constexpr size_t scale_row_bytes(int H) { return (size_t)H / 32; }
+};
+
+template <> struct Fmt<DT::MXFP4W> {
+  static constexpr int kE = 16;
+  struct Raw { u32x2 q; uint32_t s; };
+  static __device__ __forceinline__ Raw load(const void* row, const uint8_t* srow, int c) {
+    Raw r;
+    r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row) + c);
+    r.s = __builtin_nontemporal_load(srow + (c >> 1));
+    return r;
+  }
+  static __device__ __forceinline__ void decode(const Raw& r, float v[16]) {
+    const float sc = __uint_as_float(r.s << 23);
+    const uint32_t w[2] = {r.q.x, r.q.y};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], sc, 0);
+      const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], sc, 1);
+      const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], sc, 2);
+      const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], sc, 3);
+      v[8 * k + 0] = p0.x; v[8 * k + 1] = p0.y; v[8 * k + 2] = p1.x; v[8 * k + 3] = p1.y;
+      v[8 * k + 4] = p2.x; v[8 * k + 5] = p2.y; v[8 * k + 6] = p3.x; v[8 * k + 7] = p3.y;
+    }
   }
   static __host__ __device__ constexpr size_t row_bytes(int H) { return (size_t)H / 2; }
   static __host__ __device__ constexpr size_t scale_row_bytes(int H) { return (size_t)H / 32; }

@@ -34,7 +34,10 @@ struct B1Launch {
   B1Args a;
   int R;    // reducers
   int SW;   // slice width of each reducer (columns of y)
-  int tsz;  // threads per team (one weight row)
+  int tsz;  // threads per team (one weight row) in 8-element chunks
+  int tsz_r;  // threads per team of the routed experts' layout
+  int big_floats;  // floats of the general LDS scratch (a second H-vector region follows
+                   // when the routed experts use their own layout)
 };
 
 template <DT ET, DT ST, DT RT, int CR, int CS, int CPT>
@@ -64,8 +67,12 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   float* big = s_w + 64;
   Ctrl* ctrl = a.ctrl;
 
+  // router and shared experts in 8-element chunks (layout c); the routed experts in the
+  // chunks of their format (layout cr: the same as c unless the chunks are wider)
+  constexpr int ER = kE<ET>;
+  constexpr bool kTwo = ER != 8;
   float xv[CPT * 8], yv[CPT * 8];
-  load_x<CPT>(a.x, c, xv);
+  load_x<8, CPT>(a.x, c, xv);
 #pragma unroll
   for (int i = 0; i < CPT * 8; ++i) yv[i] = 0.0f;
 
@@ -84,28 +91,59 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
         [](long long f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
   }
 
+  // with two layouts the shared experts' output moves to LDS now (ysh: nteams * H floats),
+  // freeing its registers for the routed stream
+  float* ysh = big + L.big_floats;
+  if constexpr (kTwo) teams_to_lds<8, CPT>(yv, ysh, c);
+
   // 3. routed experts: flat channel f = slot * I + j
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
                 reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
+  Ctx cr = c;
+  if constexpr (kTwo) {
+    cr.tsz = L.tsz_r;
+    cr.wpt = cr.tsz / kWave;
+    cr.nteams = cr.nthreads / cr.tsz;
+    cr.team = cr.tid / cr.tsz;
+    cr.t = cr.tid % cr.tsz;
+    cr.wit = cr.t / kWave;
+    cr.nch = a.H / ER;
+  }
+  float xr[kTwo ? CPT * ER : 1], yr[kTwo ? CPT * ER : 1];
+  if constexpr (kTwo) {
+    load_x<ER, CPT>(a.x, cr, xr);
+#pragma unroll
+    for (int i = 0; i < CPT * ER; ++i) yr[i] = 0.0f;
+  }
   {
     const long long nrc = (long long)a.k * a.I;
     const int I = a.I;
-    stream_channels<ET, CR, CPT, true>(
-        a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s, nrc * c.wg / c.P,
-        nrc * (c.wg + 1) / c.P,
-        [=](long long f, long long& row, float& wt, float&) {
-          const int slot = (int)(f / I), j = (int)(f - (long long)slot * I);
-          const int e = s_ids[slot];
-          if (e >= 0) {
-            row = (long long)e * I + j;
-            wt = s_w[slot];
-          }
-        },
-        xv, yv, c);
+    auto map = [=](long long f, long long& row, float& wt, float&) {
+      const int slot = (int)(f / I), j = (int)(f - (long long)slot * I);
+      const int e = s_ids[slot];
+      if (e >= 0) {
+        row = (long long)e * I + j;
+        wt = s_w[slot];
+      }
+    };
+    if constexpr (kTwo)
+      stream_channels<ET, CR, CPT, true>(a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s,
+                                         nrc * c.wg / c.P, nrc * (c.wg + 1) / c.P, map, xr, yr,
+                                         cr);
+    else
+      stream_channels<ET, CR, CPT, true>(a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s,
+                                         nrc * c.wg / c.P, nrc * (c.wg + 1) / c.P, map, xv, yv,
+                                         c);
   }
 
   // 4. deterministic cross-workgroup sum of the partial outputs
-  reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, c);
+  if constexpr (kTwo) {
+    add_teams_to_lds<ER, CPT>(yr, ysh, cr);
+    publish_and_reduce(a.partials, a.y, ctrl, L.R, L.SW, big, c, ysh);
+  } else {
+    teams_to_lds<8, CPT>(yv, big, c);
+    publish_and_reduce(a.partials, a.y, ctrl, L.R, L.SW, big, c);
+  }
 }
 
 template <DT ET, DT ST, DT RT, int CR, int CS, int CPT>
@@ -125,9 +163,10 @@ hipError_t launch_t(const B1Launch& L, int wgs, int threads, int lds, hipStream_
 }
 
 // Channels per team and pipeline stage: enough bytes in flight without spilling the two
-// register stages (a bf16 or fp32 chunk holds 4 or 8 registers per row, an MXFP4 chunk 2).
+// register stages (a bf16 or fp32 chunk holds 4 or 8 registers per row, an MXFP4 chunk 2,
+// a wide MXFP4 chunk 3, and its layout keeps 32 x and output values per thread).
 template <DT dt> constexpr int channels_per_batch() {
-  return dt == DT::MXFP4 ? 2 : dt == DT::BF16 ? 2 : 1;
+  return dt == DT::MXFP4W ? 2 : dt == DT::MXFP4 ? 2 : dt == DT::BF16 ? 2 : 1;
 }
 
 template <DT ET, DT ST, DT RT>
@@ -146,16 +185,28 @@ int team_size(int H) {
   return nch <= 256 ? 256 : nch <= 512 ? 512 : 1024;
 }
 
-int b1_lds_bytes(int H, int threads, int E, int k) {
+// Threads per team for rows of nch chunks: the smallest power of two of whole waves.
+static int team_threads(int nch) {
+  int t = 64;
+  while (t < nch && t < 1024) t <<= 1;
+  return t;
+}
+
+static int b1_big_floats(int H, int threads, int E, int k) {
   const int nteams = threads / team_size(H);
-  const int red = 2 * (threads / kWave) * kMaxNP * 4;
-  const int small = (16 + 64 + 64) * 4;
   const int ybuf = nteams * H * 4;
   const int topk = topk_lds_bytes(E, k);
   const int reduce = threads * 4;
   int big = ybuf > topk ? ybuf : topk;
   big = big > reduce ? big : reduce;
-  return red + small + big;
+  return (big + 15) / 16 * 4;
+}
+
+int b1_lds_bytes(int H, int threads, int E, int k, bool two_layouts) {
+  const int red = 2 * (threads / kWave) * kMaxNP * 4;
+  const int small = (16 + 64 + 64) * 4;
+  const int ysh = two_layouts ? (threads / team_size(H)) * H * 4 : 0;
+  return red + small + b1_big_floats(H, threads, E, k) * 4 + ysh;
 }
 
 hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int wgs, int threads,
@@ -163,16 +214,21 @@ hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int wgs, int threads,
   B1Launch L;
   L.a = a;
   L.tsz = team_size(a.H);
+  L.tsz_r = L.tsz;
   reducer_split(a.H, wgs, &L.R, &L.SW);
-  const int lds = b1_lds_bytes(a.H, threads, a.E, a.k);
+  const int lds = b1_lds_bytes(a.H, threads, a.E, a.k, et == DT::MXFP4);
+  L.big_floats = b1_big_floats(a.H, threads, a.E, a.k);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)
     return launch_cpt<DT::F32, DT::F32, DT::F32>(L, wgs, threads, lds, s);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::BF16)
     return launch_cpt<DT::BF16, DT::BF16, DT::BF16>(L, wgs, threads, lds, s);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::F32)
     return launch_cpt<DT::BF16, DT::BF16, DT::F32>(L, wgs, threads, lds, s);
-  if (et == DT::MXFP4 && st == DT::BF16 && rt == DT::BF16)
-    return launch_cpt<DT::MXFP4, DT::BF16, DT::BF16>(L, wgs, threads, lds, s);
+  if (et == DT::MXFP4 && st == DT::BF16 && rt == DT::BF16) {
+    // routed MXFP4 rows in 16-element chunks: 8 bytes of codes per thread and row
+    L.tsz_r = team_threads(a.H / kE<DT::MXFP4W>);
+    return launch_cpt<DT::MXFP4W, DT::BF16, DT::BF16>(L, wgs, threads, lds, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -34,7 +34,7 @@ struct B1Args {
 
 hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int workgroups, int threads,
                      hipStream_t s);
-int b1_lds_bytes(int H, int threads, int E, int k);
+int b1_lds_bytes(int H, int threads, int E, int k, bool two_layouts);
 int team_size(int H);
 
 // Channel-sparse batch-1 layer (fixed-count top-K keep rule over the k*I candidates).

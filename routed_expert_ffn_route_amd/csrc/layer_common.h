@@ -2,11 +2,13 @@
 // channel-sparse): the x vector in registers, router rows with the exact top-k, streamed
 // SwiGLU channels, and the deterministic cross-workgroup reduction of the output.
 //
-// Thread layout: a workgroup is `nteams` teams of tsz (256, 512 or 1024) threads; a team
-// covers one weight row (lane i takes the 8-element chunks i, i+tsz, ...), so a wave's
-// loads of a row are contiguous 16-byte (bf16), 32-byte (fp32) or 4-byte (MXFP4) pieces.
-// Each thread keeps the x values and the partial output of its chunks in registers (CPT
-// chunks; the team width is chosen so that CPT is 1 up to H = 8192).
+// Thread layout: a workgroup is `nteams` teams of tsz threads (whole waves); a team covers
+// one weight row (lane i takes the E-element chunks i, i+tsz, ...), so a wave's loads of a
+// row are contiguous 16-byte (bf16, E = 8), 32-byte (fp32, E = 8), 4-byte (MXFP4, E = 8)
+// or 8-byte (wide MXFP4, E = 16) pieces.  Each thread keeps the x values and the partial
+// output of its chunks in registers (CPT chunks; the team width is chosen so that CPT is
+// 1).  A kernel may use two layouts (two Ctx): the routed experts in wide MXFP4 chunks,
+// the router and shared experts in 8-element ones.
 #pragma once
 #include "kernels.h"
 
@@ -25,16 +27,19 @@ __device__ __forceinline__ typename Fmt<dt>::Raw zero_raw() {
   return r;
 }
 
+template <DT dt> constexpr int kE = Fmt<dt>::kE;
+
 template <DT dt, int CPT>
 __device__ __forceinline__ float chunk_dot(const typename Fmt<dt>::Raw (&r)[CPT],
-                                           const float (&xv)[CPT * 8]) {
+                                           const float (&xv)[CPT * kE<dt>]) {
+  constexpr int E = kE<dt>;
   float s = 0.0f;
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
-    float v[8];
+    float v[E];
     Fmt<dt>::decode(r[m], v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s = fmaf(v[i], xv[m * 8 + i], s);
+    for (int i = 0; i < E; ++i) s = fmaf(v[i], xv[m * E + i], s);
   }
   return s;
 }
@@ -54,18 +59,19 @@ struct Ctx {
   }
 };
 
-template <int CPT>
-__device__ __forceinline__ void load_x(const float* x, const Ctx& c, float (&xv)[CPT * 8]) {
+// x values of this thread's chunks (E elements each; zero past the row end).
+template <int E, int CPT>
+__device__ __forceinline__ void load_x(const float* x, const Ctx& c, float (&xv)[CPT * E]) {
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
     const int ch = c.t + m * c.tsz;
-    f32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-    if (ch < c.nch) {
-      lo = reinterpret_cast<const f32x4*>(x)[2 * ch];
-      hi = reinterpret_cast<const f32x4*>(x)[2 * ch + 1];
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+      f32x4 v = {0, 0, 0, 0};
+      if (ch < c.nch) v = reinterpret_cast<const f32x4*>(x)[(E / 4) * ch + q];
+      xv[m * E + 4 * q + 0] = v.x; xv[m * E + 4 * q + 1] = v.y;
+      xv[m * E + 4 * q + 2] = v.z; xv[m * E + 4 * q + 3] = v.w;
     }
-    xv[m * 8 + 0] = lo.x; xv[m * 8 + 1] = lo.y; xv[m * 8 + 2] = lo.z; xv[m * 8 + 3] = lo.w;
-    xv[m * 8 + 4] = hi.x; xv[m * 8 + 5] = hi.y; xv[m * 8 + 6] = hi.z; xv[m * 8 + 7] = hi.w;
   }
 }
 
@@ -74,7 +80,7 @@ __device__ __forceinline__ void load_x(const float* x, const Ctx& c, float (&xv)
 template <DT dt, int C, int CPT>
 __device__ __forceinline__ void team_dots(const void* base, const uint8_t* scales,
                                           const long long (&rows)[C],
-                                          const float (&xv)[CPT * 8], Ctx& c,
+                                          const float (&xv)[CPT * kE<dt>], Ctx& c,
                                           float (&out)[C]) {
   using F = Fmt<dt>;
   typename F::Raw r[C][CPT];
@@ -153,8 +159,9 @@ __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G,
 // All threads of the workgroup must call.
 template <DT dt, int C, int CPT, bool HAS_G>
 __device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st,
-                                              const float (&xv)[CPT * 8],
-                                              float (&yv)[CPT * 8], Ctx& c) {
+                                              const float (&xv)[CPT * kE<dt>],
+                                              float (&yv)[CPT * kE<dt>], Ctx& c) {
+  constexpr int E = kE<dt>;
   constexpr int NP = NextPow2<2 * C>::value;
   float acc[NP];
 #pragma unroll
@@ -180,10 +187,10 @@ __device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st,
     const float act = silu(g) * u * st.wt[q];
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
-      float d[8];
+      float d[E];
       Fmt<dt>::decode(st.d[q][m], d);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) yv[m * 8 + i] = fmaf(act, d[i], yv[m * 8 + i]);
+      for (int i = 0; i < E; ++i) yv[m * E + i] = fmaf(act, d[i], yv[m * E + i]);
     }
   }
 }
@@ -196,8 +203,8 @@ template <DT dt, int C, int CPT, bool HAS_G, typename Map>
 __device__ inline void stream_channels(const void* G, const void* V, const void* D,
                                        const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
                                        long long i0, long long i1, Map map,
-                                       const float (&xv)[CPT * 8], float (&yv)[CPT * 8],
-                                       Ctx& c) {
+                                       const float (&xv)[CPT * kE<dt>],
+                                       float (&yv)[CPT * kE<dt>], Ctx& c) {
   const long long per = (long long)c.nteams * C;
   const long long nb = i1 > i0 ? (i1 - i0 + per - 1) / per : 0;
   auto fill = [&](Stage<dt, C, CPT>& st, long long b) {
@@ -231,7 +238,7 @@ __device__ inline void stream_channels(const void* G, const void* V, const void*
 // `buf` is LDS of at least ceil(E / P) + nteams floats; s_ep one LDS word.
 template <DT RT, int CPT>
 __device__ inline void router_rows(bool compute, const void* router, int E,
-                                   const float (&xv)[CPT * 8], uint64_t* rlog, float* buf,
+                                   const float (&xv)[CPT * kE<RT>], uint64_t* rlog, float* buf,
                                    uint32_t* s_ep, Ctx& c) {
   const int n_router_wgs = min(c.P, (E + c.nteams - 1) / c.nteams);
   const bool mine = compute && c.wg < n_router_wgs;
@@ -309,31 +316,63 @@ __device__ inline void fetch_routing(bool inside, const uint64_t* rlog, const in
   __syncthreads();
 }
 
-// Write this workgroup's partial output and arrive on the done counters; R fixed
-// workgroups (every (P/R)-th) then each sum an SW-column slice over all P partials in a
-// fixed order (p ascending in strided groups, then a fixed tree).  The first reducer,
-// once every workgroup has arrived, advances the epoch for the next launch.
-// `big` is LDS of at least max(nteams*H, nthreads) floats.
-template <int CPT>
-__device__ inline void reduce_output(const float (&yv)[CPT * 8], float* partials, float* y,
-                                     Ctrl* ctrl, int R, int SW, float* big, const Ctx& c) {
+// This workgroup's output partial in LDS big[0 .. H): the teams' register vectors summed
+// in team order (big needs nteams * H floats).  E-element chunks.
+template <int E, int CPT>
+__device__ inline void teams_to_lds(const float (&yv)[CPT * E], float* big, const Ctx& c) {
   const int H = c.H;
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
     const int ch = c.t + m * c.tsz;
     if (ch < c.nch) {
-      f32x4 lo = {yv[m * 8 + 0], yv[m * 8 + 1], yv[m * 8 + 2], yv[m * 8 + 3]};
-      f32x4 hi = {yv[m * 8 + 4], yv[m * 8 + 5], yv[m * 8 + 6], yv[m * 8 + 7]};
-      reinterpret_cast<f32x4*>(big + c.team * H)[2 * ch] = lo;
-      reinterpret_cast<f32x4*>(big + c.team * H)[2 * ch + 1] = hi;
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q)
+        reinterpret_cast<f32x4*>(big + c.team * H)[(E / 4) * ch + q] =
+            f32x4{yv[m * E + 4 * q], yv[m * E + 4 * q + 1], yv[m * E + 4 * q + 2],
+                  yv[m * E + 4 * q + 3]};
     }
   }
   __syncthreads();
-  for (int h = c.tid; h < H; h += c.nthreads) {
-    float s = big[h];
-    for (int tm = 1; tm < c.nteams; ++tm) s += big[tm * H + h];
-    st_dev(partials + (size_t)c.wg * H + h, s);
+  if (c.nteams > 1) {
+    for (int h = c.tid; h < H; h += c.nthreads) {
+      float s = big[h];
+      for (int tm = 1; tm < c.nteams; ++tm) s += big[tm * H + h];
+      big[h] = s;
+    }
+    __syncthreads();
   }
+}
+
+// Add a second layout's register vectors to big[0 .. H), one team after the other (a fixed
+// order).
+template <int E, int CPT>
+__device__ inline void add_teams_to_lds(const float (&yv)[CPT * E], float* big, const Ctx& c) {
+  for (int tm = 0; tm < c.nteams; ++tm) {
+    if (c.team == tm) {
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        const int ch = c.t + m * c.tsz;
+        if (ch < c.nch) {
+#pragma unroll
+          for (int i = 0; i < E; ++i) big[E * ch + i] += yv[m * E + i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Publish src[0 .. H) (default: big) as this workgroup's partial output and arrive on the
+// done counters;
+// R fixed workgroups (every (P/R)-th) then each sum an SW-column slice over all P
+// partials in a fixed order (p ascending in strided groups, then a fixed tree).  The first
+// reducer, once every workgroup has arrived, advances the epoch for the next launch.
+// `big` is LDS of at least max(H, nthreads) floats.
+__device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl, int R, int SW,
+                                          float* big, const Ctx& c, const float* src = nullptr) {
+  const int H = c.H;
+  if (!src) src = big;
+  for (int h = c.tid; h < H; h += c.nthreads) st_dev(partials + (size_t)c.wg * H + h, src[h]);
   stores_complete();
   __syncthreads();
   if (c.tid == 0) arrive(ctrl->done, c.wg);
@@ -375,6 +414,14 @@ __device__ inline void reduce_output(const float (&yv)[CPT * 8], float* partials
     if (g == 0 && col < wslice) y[h0 + col] = big[col0];
     __syncthreads();
   }
+}
+
+// The whole output step for one register layout.
+template <int CPT, int E = 8>
+__device__ inline void reduce_output(const float (&yv)[CPT * E], float* partials, float* y,
+                                     Ctrl* ctrl, int R, int SW, float* big, const Ctx& c) {
+  teams_to_lds<E, CPT>(yv, big, c);
+  publish_and_reduce(partials, y, ctrl, R, SW, big, c);
 }
 
 // Read the epoch (launches completed on this workspace) at the start of a launch.  Only

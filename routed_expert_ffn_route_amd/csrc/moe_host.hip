@@ -354,7 +354,8 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     DT et, st, rt;
     if (moe_status e = b1_types(layer, &et, &st, &rt)) return e;
     if (d.hidden > 8192) return fail(MOE_ERR_UNSUPPORTED, "batch-1 kernel needs hidden <= 8192");
-    if (b1_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k) > 160 * 1024)
+    if (b1_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k, et == DT::MXFP4) >
+        160 * 1024)
       return fail(MOE_ERR_UNSUPPORTED, "batch-1 kernel LDS exceeds 160 KiB");
     B1Args a = b1_args(layer, x, ids, w, y);
     hipError_t e = launch_b1(a, et, st, rt, layer->workgroups, layer->threads, s);

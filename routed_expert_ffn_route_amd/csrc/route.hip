@@ -289,6 +289,7 @@ hipError_t launch_row_norms(const void* base, const uint8_t* sc, DT dt, size_t r
     case DT::F32: return launch_norms_t<DT::F32>(base, sc, rows, H, out, s);
     case DT::BF16: return launch_norms_t<DT::BF16>(base, sc, rows, H, out, s);
     case DT::MXFP4: return launch_norms_t<DT::MXFP4>(base, sc, rows, H, out, s);
+    default: break;
   }
   return hipErrorInvalidValue;
 }
