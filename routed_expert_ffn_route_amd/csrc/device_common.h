@@ -137,11 +137,7 @@ __device__ __forceinline__ const uint8_t* scale_row_ptr(const uint8_t* base, siz
 // ------------------------------------------------------------------------------------
 // Reductions
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
+
 
 // Inclusive prefix sum across the 64 lanes of a wave: Hillis-Steele steps inside each row
 // of 16 lanes (DPP row shifts by 1, 2, 4, 8; lanes without a source add 0), then the last
@@ -155,6 +151,40 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
   x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
+}
+
+// The value of lane (lane ^ M), without an LDS round trip where the hardware allows: DPP
+// quad permutes for M = 1, 2; DPP row shifts (left for lanes whose bit M is clear, right
+// for the others) for M = 4, 8; a swizzle (xor within 32 lanes) for M = 16; a permute for
+// M = 32.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+  const int xi = __float_as_int(x);
+  if constexpr (M == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xf, 0xf, false));
+  } else if constexpr (M == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xf, 0xf, false));
+  } else if constexpr (M == 4 || M == 8) {
+    const int up = __builtin_amdgcn_update_dpp(0, xi, 0x100 + M, 0xf, 0xf, false);  // lane+M
+    const int dn = __builtin_amdgcn_update_dpp(0, xi, 0x110 + M, 0xf, 0xf, false);  // lane-M
+    return __int_as_float((lane & M) ? dn : up);
+  } else if constexpr (M == 16) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(xi, 0x401F));  // and 0x1f, xor 0x10
+  } else {
+    return __shfl_xor(x, M, kWave);
+  }
+}
+
+// Sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  const int lane = (int)(threadIdx.x & (kWave - 1));
+  v += lane_xor<32>(v, lane);
+  v += lane_xor<16>(v, lane);
+  v += lane_xor<8>(v, lane);
+  v += lane_xor<4>(v, lane);
+  v += lane_xor<2>(v, lane);
+  v += lane_xor<1>(v, lane);
+  return v;
 }
 
 // Reduce N values held by every lane of a wave.  On return, lane l holds the wave total of
@@ -171,12 +201,23 @@ __device__ __forceinline__ float wave_multi_sum(float (&v)[N], int lane) {
     for (int i = 0; i < half; ++i) {
       const float send = upper ? v[i] : v[i + half];
       const float keep = upper ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, half, kWave);
+      float got;
+      if (half == 1) got = lane_xor<1>(send, lane);
+      else if (half == 2) got = lane_xor<2>(send, lane);
+      else if (half == 4) got = lane_xor<4>(send, lane);
+      else if (half == 8) got = lane_xor<8>(send, lane);
+      else if (half == 16) got = lane_xor<16>(send, lane);
+      else got = lane_xor<32>(send, lane);
+      v[i] = keep + got;
     }
   }
   float r = v[0];
-#pragma unroll
-  for (int m = N; m < kWave; m <<= 1) r += __shfl_xor(r, m, kWave);
+  if (N <= 1) r += lane_xor<1>(r, lane);
+  if (N <= 2) r += lane_xor<2>(r, lane);
+  if (N <= 4) r += lane_xor<4>(r, lane);
+  if (N <= 8) r += lane_xor<8>(r, lane);
+  if (N <= 16) r += lane_xor<16>(r, lane);
+  if (N <= 32) r += lane_xor<32>(r, lane);
   return r;  // lane l: total of value index (l & (N-1))
 }
 
