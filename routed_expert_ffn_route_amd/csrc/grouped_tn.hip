@@ -1,0 +1,265 @@
+// grouped_tn.hip -- linear experts for larger batches: a register-blocked MFMA tile per
+// (touched expert, block of 128 output rows) with the bucket's x staged in LDS.
+//
+// Same product as linear_mfma.hip (y_b = sum_i w_{b,i} M_{e_{b,i}} x_b, each touched expert
+// read once for all its tokens; "501B of which 23B are switched on", section 3[B]), laid out
+// for many tokens per expert: there, every wave loads its own copy of the tokens' x for its
+// 16 rows, so at ~100 tokens per expert the x traffic from L2 is ~12x the weight bytes.
+// Here a workgroup (4 waves x 32 rows) stages the x of up to 128 tokens for a 64-wide K
+// chunk in LDS once, and every wave reuses each x fragment across its two 16-row tiles.
+//
+// Pipeline per K chunk: the next chunk's weight fragments (from HBM) and x (from L2) are
+// loaded into registers while the current chunk's MFMAs run; x then goes to the other LDS
+// buffer.  Each workgroup writes one partial row per (token, choice) -- w times its
+// expert's output rows -- and a combine kernel sums a token's k partials in routing order:
+// every output element has one writer and a fixed order.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 (lane l: A[l%16][8(l/16)..+8], B[8(l/16)..+8][l%16],
+// D[4(l/16)..+4][l%16]); A = 16 weight rows, B = 16 tokens; x enters as bf16 hi + lo.
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWaves = 4;
+constexpr int kRowsW = 32;                 // rows per wave (2 MFMA row tiles)
+constexpr int kRows = kWaves * kRowsW;     // rows per workgroup
+constexpr int kKA = 64;                    // K per weight-fragment step (2 MFMA K-steps)
+constexpr int kTokMax = 128;               // tokens per pass (8 MFMA token tiles)
+constexpr int kXElems = 8192;              // staged x elements per buffer and array
+constexpr int kPad = 8;                    // bf16 padding per staged x row
+
+// K width of one staged x chunk for NT token tiles: a fixed LDS budget, so fewer tokens
+// give wider chunks (fewer barriers and x round trips per pass).
+template <int NT> constexpr int kx() { return kXElems / (16 * NT); }
+template <int NT> constexpr int ldx() { return kx<NT>() + kPad; }
+constexpr int kBufElems = kXElems + kTokMax * kPad;  // one staged array (max over NT)
+
+struct TnArgs {
+  const uint8_t* M;          // [E][I][H] bf16
+  const uint16_t* xh;        // [B][H]
+  const uint16_t* xl;
+  const float* w;            // [B][k]
+  const int32_t* n_touched;
+  const int32_t* touched;
+  const int32_t* offsets;
+  const int32_t* slots;
+  float* part;               // [B*k][I]
+  int H, I, k, slots_max;
+};
+
+// x of tokens tok_b[0..16NT) (padded with the first token), K [kc, kc + kx): 16NT tokens x
+// kx/8 pieces of 16 bytes = kXElems / 8 pieces, for hi and for lo; thread j holds pieces
+// j, j + 256, ... (4 of them).
+constexpr int kPP = kXElems / 8 / (kWaves * 64);
+struct XRegs {
+  u32x4 h[kPP], l[kPP];
+};
+
+template <int NT>
+__device__ __forceinline__ void x_load(XRegs& xr, const TnArgs& a, const int* tok_b, int np,
+                                       int kc) {
+  constexpr int PR = kx<NT>() / 8;  // pieces per token row
+#pragma unroll
+  for (int i = 0; i < kPP; ++i) {
+    const int p = threadIdx.x + i * kWaves * 64;
+    const int tok = p / PR, q = p % PR;
+    const int b = tok_b[tok < np ? tok : 0];
+    const size_t off = (size_t)b * a.H + kc + 8 * q;
+    xr.h[i] = *reinterpret_cast<const u32x4*>(a.xh + off);
+    xr.l[i] = *reinterpret_cast<const u32x4*>(a.xl + off);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void x_store(const XRegs& xr, uint16_t* xs_h, uint16_t* xs_l) {
+  constexpr int PR = kx<NT>() / 8;
+#pragma unroll
+  for (int i = 0; i < kPP; ++i) {
+    const int p = threadIdx.x + i * kWaves * 64;
+    const int tok = p / PR, q = p % PR;
+    *reinterpret_cast<u32x4*>(xs_h + tok * ldx<NT>() + 8 * q) = xr.h[i];
+    *reinterpret_cast<u32x4*>(xs_l + tok * ldx<NT>() + 8 * q) = xr.l[i];
+  }
+}
+
+// Weight fragments of one 64-wide K step: 2 row tiles x 2 MFMA K-steps, 16 bytes each.
+struct ARegs {
+  u32x4 f[2][2];
+};
+
+__device__ __forceinline__ void a_load(ARegs& ar, const uint8_t* const (&rp)[2], int kc, int g) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      ar.f[r][s] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(rp[r] + (size_t)(kc + 32 * s + 8 * g) * 2));
+}
+
+// MFMAs of one 64-wide K step against the staged x at column offset k0; the hi and lo
+// products of a tile go to different accumulators' turns so that consecutive MFMAs do not
+// depend on each other.
+template <int NT>
+__device__ __forceinline__ void step_mfma(const ARegs& ar, const uint16_t* xs_h,
+                                          const uint16_t* xs_l, int k0, int l16, int g,
+                                          f32x4 (&acc)[2][NT]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, ar.f[0][s]);
+    const bf16x8 a1 = __builtin_bit_cast(bf16x8, ar.f[1][s]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int o = (16 * t + l16) * ldx<NT>() + k0 + 32 * s + 8 * g;
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs_h + o));
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs_l + o));
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh, acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh, acc[1][t], 0, 0, 0);
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc[1][t], 0, 0, 0);
+    }
+  }
+}
+
+// One pass: tokens tok_*[0..np), np <= 16 NT, over all of K; writes the partial rows.
+// Weight fragments run one 64-wide step ahead in registers; the x chunk runs one chunk
+// ahead (registers, then the other LDS buffer).
+template <int NT>
+__device__ void tn_pass(const TnArgs& a, const uint8_t* Me, int rbase, const int* tok_b,
+                        const int* tok_slot, const float* tok_w, int np, uint16_t* xs) {
+  constexpr int KX = kx<NT>();
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const uint8_t* rp[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    int row = rbase + 16 * r + l16;
+    row = row < a.I ? row : a.I - 1;  // rows past the end compute values that are dropped
+    rp[r] = Me + (size_t)row * a.H * 2;
+  }
+  uint16_t* xs_h[2] = {xs, xs + 2 * kBufElems};
+  uint16_t* xs_l[2] = {xs + kBufElems, xs + 3 * kBufElems};
+  f32x4 acc[2][NT];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = f32x4{0, 0, 0, 0};
+  const int nxc = a.H / KX;  // x chunks (H is a multiple of 1024, KX divides 512)
+  ARegs cur, nxt;
+  XRegs xr;
+  a_load(cur, rp, 0, g);
+  x_load<NT>(xr, a, tok_b, np, 0);
+  x_store<NT>(xr, xs_h[0], xs_l[0]);
+  __syncthreads();
+  for (int c = 0; c < nxc; ++c) {
+    const bool more = c + 1 < nxc;
+    if (more) x_load<NT>(xr, a, tok_b, np, (c + 1) * KX);
+#pragma unroll 1
+    for (int k0 = 0; k0 < KX; k0 += kKA) {
+      const int kn = c * KX + k0 + kKA;
+      if (kn < a.H) a_load(nxt, rp, kn, g);
+      step_mfma<NT>(cur, xs_h[c & 1], xs_l[c & 1], k0, l16, g, acc);
+      cur = nxt;
+    }
+    if (more) x_store<NT>(xr, xs_h[(c + 1) & 1], xs_l[(c + 1) & 1]);
+    __syncthreads();
+  }
+  // partial rows: w times the expert's output, for each token of the pass
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tc = 16 * t + l16;
+    if (tc >= np) continue;
+    const float wt = tok_w[tc];
+    float* prow = a.part + (size_t)tok_slot[tc] * a.I;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = rbase + 16 * r + 4 * g;
+      const f32x4 v = acc[r][t] * wt;
+      if (row + 3 < a.I) {
+        *reinterpret_cast<f32x4*>(prow + row) = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (row + i < a.I) prow[row + i] = v[i];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [2 buffers][hi, lo][kBufElems]
+  __shared__ int tok_b[kTokMax];
+  __shared__ int tok_slot[kTokMax];
+  __shared__ float tok_w[kTokMax];
+  const int t = blockIdx.y;
+  if (t >= *a.n_touched || blockIdx.x * kRows >= a.I) return;  // whole workgroup leaves
+  const int e = a.touched[t];
+  const int s0 = a.offsets[e], ne = a.offsets[e + 1] - s0;
+  const uint8_t* Me = a.M + (size_t)e * a.I * a.H * 2;
+  const int rbase = blockIdx.x * kRows + (threadIdx.x >> 6) * kRowsW;
+  for (int p0 = 0; p0 < ne; p0 += kTokMax) {
+    const int np = min(kTokMax, ne - p0);
+    __syncthreads();  // the previous pass is done with the token list and x buffers
+    for (int i = threadIdx.x; i < np; i += blockDim.x) {
+      const int slot = a.slots[s0 + p0 + i];
+      tok_b[i] = slot / a.k;
+      tok_slot[i] = slot;
+      tok_w[i] = a.w[slot];
+    }
+    __syncthreads();
+    const int nt = (np + 15) / 16;
+    if (nt <= 1) tn_pass<1>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+    else if (nt <= 2) tn_pass<2>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+    else if (nt <= 4) tn_pass<4>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+    else tn_pass<8>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+  }
+}
+
+// y[b][r] = sum_i part[b*k + i][r], i in routing order.
+__global__ __launch_bounds__(256) void tn_combine_kernel(const float* part, float* y, int B,
+                                                         int k, int I) {
+  const int n4 = I / 4;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < (size_t)B * n4;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int b = (int)(idx / n4), c = (int)(idx % n4);
+    const f32x4* P = reinterpret_cast<const f32x4*>(part);
+    f32x4 s = {0, 0, 0, 0};
+    for (int i = 0; i < k; ++i) s += P[(size_t)(b * k + i) * n4 + c];
+    reinterpret_cast<f32x4*>(y)[(size_t)b * n4 + c] = s;
+  }
+}
+
+}  // namespace
+
+int tn_lds_bytes() { return 2 * 2 * kBufElems * 2; }
+
+hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
+                               const int32_t* n_touched, const int32_t* touched,
+                               const int32_t* offsets, const int32_t* slots, uint16_t* xh,
+                               uint16_t* xl, float* part, float* y, int H, int I, int E, int k,
+                               int B, hipStream_t s) {
+  hipError_t e = launch_split_x(x, (size_t)B * H, xh, xl, s);
+  if (e != hipSuccess) return e;
+  static bool lds_set = false;
+  if (!lds_set) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(tn_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, tn_lds_bytes());
+    if (e != hipSuccess) return e;
+    lds_set = true;
+  }
+  TnArgs a{reinterpret_cast<const uint8_t*>(M), xh, xl, w, n_touched, touched, offsets, slots,
+           part, H, I, k, B * k < E ? B * k : E};
+  hipLaunchKernelGGL(tn_kernel, dim3((I + kRows - 1) / kRows, a.slots_max), dim3(kWaves * 64),
+                     tn_lds_bytes(), s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)B * (I / 4);
+  int g = (int)((n + 255) / 256);
+  g = g > 4096 ? 4096 : g;
+  hipLaunchKernelGGL(tn_combine_kernel, dim3(g), dim3(256), 0, s, part, y, B, k, I);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -68,6 +68,15 @@ hipError_t launch_linear(const void* M, const float* x, const float* w, const in
                          uint16_t* xh, uint16_t* xl, float* y, int H, int I, int E, int k,
                          int B, hipStream_t s);
 
+// Linear experts for larger batches: one register-blocked MFMA tile per (touched expert,
+// 128 output rows) with the tokens' x staged in LDS, partial rows per (token, choice)
+// [B*k][I] in `part`, then a combine in routing order into y [B][I].
+hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
+                               const int32_t* n_touched, const int32_t* touched,
+                               const int32_t* offsets, const int32_t* slots, uint16_t* xh,
+                               uint16_t* xl, float* part, float* y, int H, int I, int E, int k,
+                               int B, hipStream_t s);
+
 // x [n] fp32 -> bf16 hi, lo with hi + lo ~= x (the MFMA paths' activation operand).
 hipError_t launch_split_x(const float* x, size_t n, uint16_t* xh, uint16_t* xl, hipStream_t s);
 

@@ -40,6 +40,9 @@ moe_status device_fail(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 constexpr int kMaxWorkgroups = 512;   // partial-sum rows reserved in the workspace
 constexpr int kThreads = 1024;
+// From this batch size on, linear experts use the tiled kernel (x staged in LDS, many tokens
+// per expert); below it the row-owner kernel, which needs no partial rows.
+constexpr int kLinearTiledMinBatch = 32;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -121,7 +124,12 @@ Layout layout_of(const moe_layer_desc* d) {
   const size_t pairs = batched_swiglu ? B * k + (size_t)d->n_shared * B : 0;
   const size_t ia = (size_t)(d->inter > d->shared_inter ? d->inter : d->shared_inter);
   L.act = take(pairs * ia * 4);
-  L.part = take(pairs * (size_t)d->hidden * 4);
+  // partial outputs: batched SwiGLU [pairs][H]; linear experts at larger batches [B*k][I]
+  const size_t lin_part = d->kind == MOE_EXPERT_LINEAR && B >= kLinearTiledMinBatch
+                              ? B * k * (size_t)d->inter * 4
+                              : 0;
+  const size_t sw_part = pairs * (size_t)d->hidden * 4;
+  L.part = take(lin_part > sw_part ? lin_part : sw_part);
   L.total = o;
   return L;
 }
@@ -460,7 +468,12 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     if (e == hipSuccess)
       e = launch_union(rid, B, d.top_k, d.n_experts, n_t, touched, offsets, slots,
                        layer->ctrl(), s);
-    if (e == hipSuccess)
+    if (e == hipSuccess && B >= kLinearTiledMinBatch)
+      e = launch_linear_tiled(layer->w.linear, x, rw, n_t, touched, offsets, slots,
+                              layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl),
+                              layer->at<float>(layer->L.part), y, d.hidden, d.inter,
+                              d.n_experts, d.top_k, B, s);
+    else if (e == hipSuccess)
       e = launch_linear(layer->w.linear, x, rw, n_t, touched, offsets, slots,
                         layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl), y,
                         d.hidden, d.inter, d.n_experts, d.top_k, B, s);
