@@ -99,9 +99,8 @@ __device__ __forceinline__ void a_load(ARegs& ar, const uint8_t* const (&rp)[2],
           reinterpret_cast<const u32x4*>(rp[r] + (size_t)(kc + 32 * s + 8 * g) * 2));
 }
 
-// MFMAs of one 64-wide K step against the staged x at column offset k0; the hi and lo
-// products of a tile go to different accumulators' turns so that consecutive MFMAs do not
-// depend on each other.
+// MFMAs of one 64-wide K step against the staged x at column offset k0: all hi products,
+// then all lo products, so that an accumulator's next MFMA is 2 NT issues away.
 template <int NT>
 __device__ __forceinline__ void step_mfma(const ARegs& ar, const uint16_t* xs_h,
                                           const uint16_t* xs_l, int k0, int l16, int g,
@@ -110,26 +109,37 @@ __device__ __forceinline__ void step_mfma(const ARegs& ar, const uint16_t* xs_h,
   for (int s = 0; s < 2; ++s) {
     const bf16x8 a0 = __builtin_bit_cast(bf16x8, ar.f[0][s]);
     const bf16x8 a1 = __builtin_bit_cast(bf16x8, ar.f[1][s]);
+    u32x4 bh[NT], bl[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int o = (16 * t + l16) * ldx<NT>() + k0 + 32 * s + 8 * g;
-      const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs_h + o));
-      const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs_l + o));
-      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh, acc[0][t], 0, 0, 0);
-      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh, acc[1][t], 0, 0, 0);
-      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc[0][t], 0, 0, 0);
-      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc[1][t], 0, 0, 0);
+      bh[t] = *reinterpret_cast<const u32x4*>(xs_h + o);
+      bl[t] = *reinterpret_cast<const u32x4*>(xs_l + o);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, bh[t]);
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, bl[t]);
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][t], 0, 0, 0);
     }
   }
 }
 
 // One pass: tokens tok_*[0..np), np <= 16 NT, over all of K; writes the partial rows.
-// Weight fragments run one 64-wide step ahead in registers; the x chunk runs one chunk
-// ahead (registers, then the other LDS buffer).
-template <int NT>
+// Weight fragments run DA 64-wide steps ahead in registers (a ring); the x chunk runs one
+// chunk ahead (registers, then the other LDS buffer).  nst is a multiple of the unrolled
+// group (H is a multiple of 1024).
+template <int NT, int DA>
 __device__ void tn_pass(const TnArgs& a, const uint8_t* Me, int rbase, const int* tok_b,
                         const int* tok_slot, const float* tok_w, int np, uint16_t* xs) {
   constexpr int KX = kx<NT>();
+  constexpr int SPC = KX / kKA;  // weight steps per x chunk
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const uint8_t* rp[2];
 #pragma unroll
@@ -145,25 +155,32 @@ __device__ void tn_pass(const TnArgs& a, const uint8_t* Me, int rbase, const int
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[r][t] = f32x4{0, 0, 0, 0};
-  const int nxc = a.H / KX;  // x chunks (H is a multiple of 1024, KX divides 512)
-  ARegs cur, nxt;
+  const int nst = a.H / kKA;  // weight steps (H is a multiple of 1024, KX divides 512)
+  constexpr int G = SPC > DA ? SPC : DA;  // steps per unrolled group (both powers of two)
+  ARegs ring[DA];
   XRegs xr;
-  a_load(cur, rp, 0, g);
   x_load<NT>(xr, a, tok_b, np, 0);
+#pragma unroll
+  for (int d = 0; d < DA; ++d) a_load(ring[d], rp, d * kKA, g);
   x_store<NT>(xr, xs_h[0], xs_l[0]);
   __syncthreads();
-  for (int c = 0; c < nxc; ++c) {
-    const bool more = c + 1 < nxc;
-    if (more) x_load<NT>(xr, a, tok_b, np, (c + 1) * KX);
-#pragma unroll 1
-    for (int k0 = 0; k0 < KX; k0 += kKA) {
-      const int kn = c * KX + k0 + kKA;
-      if (kn < a.H) a_load(nxt, rp, kn, g);
-      step_mfma<NT>(cur, xs_h[c & 1], xs_l[c & 1], k0, l16, g, acc);
-      cur = nxt;
+  for (int base = 0; base < nst; base += G) {
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int st = base + u;
+      const int c = st / SPC;          // x chunk of this step
+      const bool first = u % SPC == 0, last = u % SPC == SPC - 1;
+      const bool more = (c + 1) * SPC < nst;
+      if (first && more) x_load<NT>(xr, a, tok_b, np, (c + 1) * KX);
+      step_mfma<NT>(ring[u % DA], xs_h[c & 1], xs_l[c & 1], (u % SPC) * kKA, l16, g, acc);
+      // refill this ring slot DA steps ahead (refills past the end reread the last step)
+      const int sn = st + DA < nst ? st + DA : nst - 1;
+      a_load(ring[u % DA], rp, sn * kKA, g);
+      if (last) {
+        if (more) x_store<NT>(xr, xs_h[(c + 1) & 1], xs_l[(c + 1) & 1]);
+        __syncthreads();
+      }
     }
-    if (more) x_store<NT>(xr, xs_h[(c + 1) & 1], xs_l[(c + 1) & 1]);
-    __syncthreads();
   }
   // partial rows: w times the expert's output, for each token of the pass
 #pragma unroll
@@ -187,6 +204,10 @@ __device__ void tn_pass(const TnArgs& a, const uint8_t* Me, int rbase, const int
   }
 }
 
+// One kernel per range of token counts, so that the register allocation of the large
+// token tiles does not limit the weight prefetch depth of the small ones: SMALL takes the
+// experts with at most 32 tokens (deep prefetch), the other one the rest.
+template <bool SMALL>
 __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [2 buffers][hi, lo][kBufElems]
@@ -197,6 +218,7 @@ __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
   if (t >= *a.n_touched || blockIdx.x * kRows >= a.I) return;  // whole workgroup leaves
   const int e = a.touched[t];
   const int s0 = a.offsets[e], ne = a.offsets[e + 1] - s0;
+  if ((ne <= 32) != SMALL) return;  // the other kernel's expert
   const uint8_t* Me = a.M + (size_t)e * a.I * a.H * 2;
   const int rbase = blockIdx.x * kRows + (threadIdx.x >> 6) * kRowsW;
   for (int p0 = 0; p0 < ne; p0 += kTokMax) {
@@ -210,10 +232,13 @@ __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
     }
     __syncthreads();
     const int nt = (np + 15) / 16;
-    if (nt <= 1) tn_pass<1>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
-    else if (nt <= 2) tn_pass<2>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
-    else if (nt <= 4) tn_pass<4>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
-    else tn_pass<8>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+    if constexpr (SMALL) {
+      if (nt <= 1) tn_pass<1, 4>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+      else tn_pass<2, 4>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+    } else {
+      if (nt <= 4) tn_pass<4, 4>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+      else tn_pass<8, 4>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+    }
   }
 }
 
@@ -244,15 +269,21 @@ hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
   if (e != hipSuccess) return e;
   static bool lds_set = false;
   if (!lds_set) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(tn_kernel),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(tn_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, tn_lds_bytes());
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(tn_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, tn_lds_bytes());
     if (e != hipSuccess) return e;
     lds_set = true;
   }
   TnArgs a{reinterpret_cast<const uint8_t*>(M), xh, xl, w, n_touched, touched, offsets, slots,
            part, H, I, k, B * k < E ? B * k : E};
-  hipLaunchKernelGGL(tn_kernel, dim3((I + kRows - 1) / kRows, a.slots_max), dim3(kWaves * 64),
-                     tn_lds_bytes(), s, a);
+  const dim3 grid((I + kRows - 1) / kRows, a.slots_max);
+  hipLaunchKernelGGL(tn_kernel<true>, grid, dim3(kWaves * 64), tn_lds_bytes(), s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tn_kernel<false>, grid, dim3(kWaves * 64), tn_lds_bytes(), s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t n = (size_t)B * (I / 4);
