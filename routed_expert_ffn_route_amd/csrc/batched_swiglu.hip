@@ -35,42 +35,52 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Gate/up
 // ------------------------------------------------------------------------------------
 constexpr int kGuWaves = 4;
-constexpr int kGuRowsPerWave = 64;
-constexpr int kGuRows = kGuWaves * kGuRowsPerWave;  // channels per workgroup
-constexpr int kGuTok = 64;                          // tokens per pass (4 MFMA token tiles)
+constexpr int kGuRowsW = 32;                    // channels per wave (2 MFMA row tiles)
+constexpr int kGuRows = kGuWaves * kGuRowsW;    // channels per workgroup
+constexpr int kGuTok = 64;                      // tokens per pass (up to 4 token tiles)
+constexpr int kGuXElems = 8192;                 // staged x elements per buffer and array
+constexpr int kGuPad = 8;                       // bf16 padding per staged x row
+constexpr int kGuBuf = kGuXElems + kGuTok * kGuPad;
+constexpr int kGuDA = 2;                        // weight steps prefetched in registers
 
+// K width of one staged x chunk for NT token tiles (fixed LDS budget).
+template <int NT> constexpr int gu_kx() { return kGuXElems / (16 * NT); }
+template <int NT> constexpr int gu_ldx() { return gu_kx<NT>() + kGuPad; }
+
+// Weight fragments of one K step for one 16-row tile.  A step is STEP elements; MFMA
+// sub-step c of it takes A and B from the same K positions (boff).
 template <DT dt> struct Gu;
 
 template <> struct Gu<DT::BF16> {
-  static constexpr int LC = 8;  // elements per lane per step
-  struct Raw { u32x4 q; };
-  static __device__ __forceinline__ Raw load(const uint8_t* row, const uint8_t*, int k) {
+  static constexpr int STEP = 64, SUB = 2;  // lane: 16 bytes per sub-step
+  struct Raw { u32x4 f[2]; };
+  static __device__ __forceinline__ Raw load(const uint8_t* row, const uint8_t*, int k, int g) {
     Raw r;
-    r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + (size_t)k * 2));
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      r.f[c] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(row + (size_t)(k + 32 * c + 8 * g) * 2));
     return r;
   }
-  static __device__ __forceinline__ bf16x8 slice(const Raw& r, int) {
-    return __builtin_bit_cast(bf16x8, r.q);
+  static __device__ __forceinline__ bf16x8 frag(const Raw& r, int c) {
+    return __builtin_bit_cast(bf16x8, r.f[c]);
   }
-  static __device__ __forceinline__ Raw zero_if(Raw r, bool live) {
-    const uint32_t m = live ? 0xFFFFFFFFu : 0u;
-    r.q &= u32x4{m, m, m, m};
-    return r;
-  }
+  static __device__ __forceinline__ int boff(int c, int g) { return 32 * c + 8 * g; }
   static __host__ __device__ constexpr size_t row_bytes(int H) { return (size_t)H * 2; }
 };
 
 template <> struct Gu<DT::MXFP4> {
-  static constexpr int LC = 32;
+  static constexpr int STEP = 128, SUB = 4;  // lane: 32 codes (one scale block) per step
   struct Raw { u32x4 q; uint32_t s; };
-  static __device__ __forceinline__ Raw load(const uint8_t* row, const uint8_t* srow, int k) {
+  static __device__ __forceinline__ Raw load(const uint8_t* row, const uint8_t* srow, int k,
+                                             int g) {
     Raw r;
-    r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + k / 2));
-    r.s = __builtin_nontemporal_load(srow + k / 32);
+    r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + (k + 32 * g) / 2));
+    r.s = srow[(k + 32 * g) / 32];  // scale lines are reused by the next steps: cached
     return r;
   }
-  // slice c = elements 8c .. 8c+7 of the lane's 32: code dword c, low nibble first
-  static __device__ __forceinline__ bf16x8 slice(const Raw& r, int c) {
+  // sub-step c = elements 8c .. 8c+7 of the lane's 32: code dword c, low nibble first
+  static __device__ __forceinline__ bf16x8 frag(const Raw& r, int c) {
     const float sc = __uint_as_float(r.s << 23);
     const uint32_t w = c == 0 ? r.q.x : c == 1 ? r.q.y : c == 2 ? r.q.z : r.q.w;
     const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
@@ -79,105 +89,195 @@ template <> struct Gu<DT::MXFP4> {
     const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
     return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
   }
-  static __device__ __forceinline__ Raw zero_if(Raw r, bool live) {
-    const uint32_t m = live ? 0xFFFFFFFFu : 0u;
-    r.q &= u32x4{m, m, m, m};
-    return r;
-  }
+  static __device__ __forceinline__ int boff(int c, int g) { return 32 * g + 8 * c; }
   static __host__ __device__ constexpr size_t row_bytes(int H) { return (size_t)H / 2; }
 };
 
-// One pass of the gate/up products of R 16-row tiles of one wave (rows rbase + 16r + l%16)
-// for NT 16-token tiles, over all of K.  U steps are loaded before their MFMAs.
-template <DT dt, int R, int NT, int U>
-__device__ __forceinline__ void gu_tiles(const uint8_t* G, const uint8_t* V, const uint8_t* Gs,
-                                         const uint8_t* Vs, int H, int rows, int rbase,
-                                         const uint16_t* xh, const uint16_t* xl,
-                                         const int* tok_b, int np, f32x4 (&ag)[R][NT],
-                                         f32x4 (&au)[R][NT]) {
-  using F = Gu<dt>;
-  constexpr int LC = F::LC;
-  constexpr int SC = LC / 8;      // MFMAs per step and operand
-  constexpr int STEP = 4 * LC;    // elements of K per step
-  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
-  const size_t rb = F::row_bytes(H);
-  const uint8_t* gp[R];
-  const uint8_t* vp[R];
-  const uint8_t* gsp[R];
-  const uint8_t* vsp[R];
+// The staged x of tokens tok_b[0..16NT) (padded with the first token), K [kc, kc + kx):
+// 1024 pieces of 16 bytes per array, 4 per thread; K past H reads the last valid piece
+// and is never used.
+struct GuX {
+  u32x4 h[4], l[4];
+};
+
+template <int NT>
+__device__ __forceinline__ void gu_x_load(GuX& xr, const uint16_t* xh, const uint16_t* xl,
+                                          int H, const int* tok_b, int np, int kc) {
+  constexpr int PR = gu_kx<NT>() / 8;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    int row = rbase + 16 * r + l16;
-    row = row < rows ? row : rows - 1;  // rows past the end compute values that are dropped
-    gp[r] = G + (size_t)row * rb;
-    vp[r] = V + (size_t)row * rb;
-    gsp[r] = Gs ? Gs + (size_t)row * (H / 32) : nullptr;
-    vsp[r] = Vs ? Vs + (size_t)row * (H / 32) : nullptr;
-  }
-  const uint16_t* xhp[NT];
-  const uint16_t* xlp[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tc = 16 * t + l16;
-    const int b = tok_b[tc < np ? tc : 0];  // padded token columns repeat the first token
-    xhp[t] = xh + (size_t)b * H;
-    xlp[t] = xl + (size_t)b * H;
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      ag[r][t] = f32x4{0, 0, 0, 0};
-      au[r][t] = f32x4{0, 0, 0, 0};
-    }
-  for (int kb = 0; kb < H; kb += U * STEP) {
-    typename F::Raw A[U][2][R];
-    u32x4 Bh[U][NT][SC], Bl[U][NT][SC];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = kb + u * STEP + LC * g;
-      const bool live = k < H;  // H is a multiple of 32: a lane's piece is all in or all out
-      const int kc = live ? k : 0;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        A[u][0][r] = F::zero_if(F::load(gp[r], gsp[r], kc), live);
-        A[u][1][r] = F::zero_if(F::load(vp[r], vsp[r], kc), live);
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int c = 0; c < SC; ++c) {
-          Bh[u][t][c] = *reinterpret_cast<const u32x4*>(xhp[t] + kc + 8 * c);
-          Bl[u][t][c] = *reinterpret_cast<const u32x4*>(xlp[t] + kc + 8 * c);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < SC; ++c)
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const bf16x8 a0 = F::slice(A[u][0][r], c);
-          const bf16x8 a1 = F::slice(A[u][1][r], c);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const bf16x8 bh = __builtin_bit_cast(bf16x8, Bh[u][t][c]);
-            const bf16x8 bl = __builtin_bit_cast(bf16x8, Bl[u][t][c]);
-            ag[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh, ag[r][t], 0, 0, 0);
-            ag[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, ag[r][t], 0, 0, 0);
-            au[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh, au[r][t], 0, 0, 0);
-            au[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, au[r][t], 0, 0, 0);
-          }
-        }
+  for (int i = 0; i < 4; ++i) {
+    const int p = threadIdx.x + i * kGuWaves * 64;
+    const int tok = p / PR, q = p % PR;
+    const int b = tok_b[tok < np ? tok : 0];
+    int k = kc + 8 * q;
+    k = k < H ? k : H - 8;
+    const size_t off = (size_t)b * H + k;
+    xr.h[i] = *reinterpret_cast<const u32x4*>(xh + off);
+    xr.l[i] = *reinterpret_cast<const u32x4*>(xl + off);
   }
 }
 
-// a = w * silu(g) * u for the lane's 4 rows of each tile and its token column.
-template <int R, int NT>
-__device__ __forceinline__ void gu_store(const f32x4 (&ag)[R][NT], const f32x4 (&au)[R][NT],
-                                         int rows, int rbase, const int* tok_slot,
-                                         const float* tok_w, int np, float* act, int IA) {
+template <int NT>
+__device__ __forceinline__ void gu_x_store(const GuX& xr, uint16_t* xs_h, uint16_t* xs_l) {
+  constexpr int PR = gu_kx<NT>() / 8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = threadIdx.x + i * kGuWaves * 64;
+    const int tok = p / PR, q = p % PR;
+    *reinterpret_cast<u32x4*>(xs_h + tok * gu_ldx<NT>() + 8 * q) = xr.h[i];
+    *reinterpret_cast<u32x4*>(xs_l + tok * gu_ldx<NT>() + 8 * q) = xr.l[i];
+  }
+}
+
+template <DT dt>
+struct GuRing {
+  typename Gu<dt>::Raw r[2][2];  // [matrix: G, V][row tile]
+};
+
+template <DT dt>
+__device__ __forceinline__ void gu_a_load(GuRing<dt>& ar, const uint8_t* const (&rp)[2][2],
+                                          const uint8_t* const (&sp)[2][2], int k, int g) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) ar.r[m][r] = Gu<dt>::load(rp[m][r], sp[m][r], k, g);
+}
+
+// MFMAs of one K step (all its sub-steps) against the staged x at chunk offset k0.
+template <DT dt, int NT>
+__device__ __forceinline__ void gu_step(const GuRing<dt>& ar, const uint16_t* xs_h,
+                                        const uint16_t* xs_l, int k0, int l16, int g,
+                                        f32x4 (&acc)[2][2][NT]) {
+  using F = Gu<dt>;
+#pragma unroll
+  for (int c = 0; c < F::SUB; ++c) {
+    bf16x8 af[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) af[m][r] = F::frag(ar.r[m][r], c);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int o = (16 * t + l16) * gu_ldx<NT>() + k0 + F::boff(c, g);
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs_h + o));
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs_l + o));
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          acc[m][r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m][r], bh, acc[m][r][t], 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          acc[m][r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m][r], bl, acc[m][r][t], 0, 0, 0);
+    }
+  }
+}
+
+// One pass of one wave's 32 channels (rows rbase ..) for tokens tok_*[0..np), np <= 16 NT.
+// Weight fragments run kGuDA steps ahead in registers; the x chunk one chunk ahead.  The
+// full steps run pipelined; a K tail (H not a multiple of the step) runs after them with
+// masked fragments.
+template <DT dt, int NT>
+__device__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs, const uint8_t* Vs,
+                        int H, int rows, int rbase, const uint16_t* xh, const uint16_t* xl,
+                        const int* tok_b, const int* tok_slot, const float* tok_w, int np,
+                        uint16_t* xs, float* act, int IA) {
+  using F = Gu<dt>;
+  constexpr int KX = gu_kx<NT>();
+  constexpr int SPC = KX / F::STEP;
+  constexpr int GRP = SPC > kGuDA ? SPC : kGuDA;
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const uint8_t* rp[2][2];
+  const uint8_t* sp[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    int row = rbase + 16 * r + l16;
+    row = row < rows ? row : rows - 1;  // rows past the end compute values that are dropped
+    rp[0][r] = G + (size_t)row * F::row_bytes(H);
+    rp[1][r] = V + (size_t)row * F::row_bytes(H);
+    sp[0][r] = Gs ? Gs + (size_t)row * (H / 32) : nullptr;
+    sp[1][r] = Vs ? Vs + (size_t)row * (H / 32) : nullptr;
+  }
+  uint16_t* xs_h[2] = {xs, xs + 2 * kGuBuf};
+  uint16_t* xs_l[2] = {xs + kGuBuf, xs + 3 * kGuBuf};
+  f32x4 acc[2][2][NT];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[m][r][t] = f32x4{0, 0, 0, 0};
+  // full chunks, in groups of GRP steps
+  const int nfull = (H / KX) * SPC;                  // steps in full chunks
+  const int ngrp = nfull / GRP * GRP;                // steps run by the pipelined loop
+  GuRing<dt> ring[kGuDA];
+  GuX xr;
+  gu_x_load<NT>(xr, xh, xl, H, tok_b, np, 0);
+  if (ngrp > 0) {
+#pragma unroll
+    for (int d = 0; d < kGuDA; ++d) gu_a_load<dt>(ring[d], rp, sp, d * F::STEP, g);
+  }
+  gu_x_store<NT>(xr, xs_h[0], xs_l[0]);
+  __syncthreads();
+  for (int base = 0; base < ngrp; base += GRP) {
+#pragma unroll
+    for (int u = 0; u < GRP; ++u) {
+      const int st = base + u;
+      const int c = st / SPC;
+      const bool first = u % SPC == 0, last = u % SPC == SPC - 1;
+      const bool more = (c + 1) * KX < H;  // another (full or partial) chunk follows
+      if (first && more) gu_x_load<NT>(xr, xh, xl, H, tok_b, np, (c + 1) * KX);
+      gu_step<dt, NT>(ring[u % kGuDA], xs_h[c & 1], xs_l[c & 1], (u % SPC) * F::STEP, l16, g,
+                      acc);
+      const int sn = st + kGuDA < ngrp ? st + kGuDA : ngrp - 1;  // spare refills: reread
+      gu_a_load<dt>(ring[u % kGuDA], rp, sp, sn * F::STEP, g);
+      if (last) {
+        if (more) gu_x_store<NT>(xr, xs_h[(c + 1) & 1], xs_l[(c + 1) & 1]);
+        __syncthreads();
+      }
+    }
+  }
+  // the rest of K (ngrp steps are done; x of chunk ngrp/SPC is staged): masked steps,
+  // staging further chunks as they are reached
+  for (int st = ngrp; st * F::STEP < H; ++st) {
+    const int c = st / SPC;
+    const int k = st * F::STEP;
+    if (st > ngrp && st % SPC == 0) {
+      gu_x_load<NT>(xr, xh, xl, H, tok_b, np, c * KX);
+      gu_x_store<NT>(xr, xs_h[c & 1], xs_l[c & 1]);
+      __syncthreads();
+    }
+    GuRing<dt> ar;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        // pieces that start past H read the row's last piece and are zeroed
+        if constexpr (dt == DT::MXFP4) {
+          const int e0 = k + 32 * g;
+          const int ec = e0 < H ? e0 : H - 32;
+          typename F::Raw v;
+          v.q = *reinterpret_cast<const u32x4*>(rp[m][r] + ec / 2);
+          v.s = sp[m][r][ec / 32];
+          if (e0 >= H) v.q = u32x4{0, 0, 0, 0};
+          ar.r[m][r] = v;
+        } else {
+          typename F::Raw v;
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int e0 = k + 32 * cc + 8 * g;
+            const int ec = e0 < H ? e0 : H - 8;
+            v.f[cc] = *reinterpret_cast<const u32x4*>(rp[m][r] + (size_t)ec * 2);
+            if (e0 >= H) v.f[cc] = u32x4{0, 0, 0, 0};
+          }
+          ar.r[m][r] = v;
+        }
+      }
+    gu_step<dt, NT>(ar, xs_h[c & 1], xs_l[c & 1], k - c * KX, l16, g, acc);
+  }
+  // a = w * silu(g) * u for the lane's 4 rows of each tile and its token column
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int tc = 16 * t + l16;
@@ -185,48 +285,18 @@ __device__ __forceinline__ void gu_store(const f32x4 (&ag)[R][NT], const f32x4 (
     const float wt = tok_w[tc];
     float* arow = act + (size_t)tok_slot[tc] * IA;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < 2; ++r) {
       const int row = rbase + 16 * r + 4 * g;
-      f32x4 a;
+      f32x4 v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = wt * silu(ag[r][t][i]) * au[r][t][i];
+      for (int i = 0; i < 4; ++i) v[i] = wt * silu(acc[0][r][t][i]) * acc[1][r][t][i];
       if (row + 3 < rows) {
-        *reinterpret_cast<f32x4*>(arow + row) = a;
+        *reinterpret_cast<f32x4*>(arow + row) = v;
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (row + i < rows) arow[row + i] = a[i];
+          if (row + i < rows) arow[row + i] = v[i];
       }
-    }
-  }
-}
-
-// The wave's 64 rows for np <= 64 tokens: R*NT <= 4 keeps the accumulators in 32*R*NT
-// registers; fewer tiles per sweep when there are more token tiles.
-template <DT dt, int U>
-__device__ __forceinline__ void gu_wave(const uint8_t* G, const uint8_t* V, const uint8_t* Gs,
-                                        const uint8_t* Vs, int H, int rows, int rbase,
-                                        const uint16_t* xh, const uint16_t* xl, const int* tok_b,
-                                        const int* tok_slot, const float* tok_w, int np,
-                                        float* act, int IA) {
-  const int nt = (np + 15) / 16;
-  if (nt <= 1) {
-    f32x4 ag[4][1], au[4][1];
-    gu_tiles<dt, 4, 1, U>(G, V, Gs, Vs, H, rows, rbase, xh, xl, tok_b, np, ag, au);
-    gu_store<4, 1>(ag, au, rows, rbase, tok_slot, tok_w, np, act, IA);
-  } else if (nt <= 2) {
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-      f32x4 ag[2][2], au[2][2];
-      gu_tiles<dt, 2, 2, U>(G, V, Gs, Vs, H, rows, rbase + 32 * h, xh, xl, tok_b, np, ag, au);
-      gu_store<2, 2>(ag, au, rows, rbase + 32 * h, tok_slot, tok_w, np, act, IA);
-    }
-  } else {
-#pragma unroll 1
-    for (int h = 0; h < 4; ++h) {
-      f32x4 ag[1][4], au[1][4];
-      gu_tiles<dt, 1, 4, U>(G, V, Gs, Vs, H, rows, rbase + 16 * h, xh, xl, tok_b, np, ag, au);
-      gu_store<1, 4>(ag, au, rows, rbase + 16 * h, tok_slot, tok_w, np, act, IA);
     }
   }
 }
@@ -278,33 +348,53 @@ __device__ __forceinline__ void fill_tokens(const BsArgs& a, const Bucket& bk, i
 
 template <DT et, DT st>
 __global__ __launch_bounds__(kGuWaves * 64) void bs_gateup_kernel(BsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [2 buffers][hi, lo][kGuBuf]
   __shared__ int tok_b[kGuTok];
   __shared__ int tok_slot[kGuTok];
   __shared__ float tok_w[kGuTok];
   const Bucket bk = bucket_of(a, blockIdx.y);
   const int rows = bk.shared ? a.IS : a.I;
-  const int rbase = blockIdx.x * kGuRows + (threadIdx.x >> 6) * kGuRowsPerWave;
   if (bk.count == 0 || blockIdx.x * kGuRows >= rows) return;  // whole workgroup leaves
+  const int rbase = blockIdx.x * kGuRows + (threadIdx.x >> 6) * kGuRowsW;
+  const uint8_t *G, *V, *Gs = nullptr, *Vs = nullptr;
+  if (bk.shared) {
+    const size_t off = (size_t)bk.e * a.IS * Gu<st>::row_bytes(a.H);
+    G = reinterpret_cast<const uint8_t*>(a.sh_gate) + off;
+    V = reinterpret_cast<const uint8_t*>(a.sh_up) + off;
+  } else {
+    const size_t off = (size_t)bk.e * a.I;
+    G = reinterpret_cast<const uint8_t*>(a.gate) + off * Gu<et>::row_bytes(a.H);
+    V = reinterpret_cast<const uint8_t*>(a.up) + off * Gu<et>::row_bytes(a.H);
+    if (a.gate_s) Gs = a.gate_s + off * (a.H / 32);
+    if (a.up_s) Vs = a.up_s + off * (a.H / 32);
+  }
   for (int p0 = 0; p0 < bk.count; p0 += kGuTok) {
     const int np = min(kGuTok, bk.count - p0);
-    __syncthreads();  // the previous pass is done with the token list
+    __syncthreads();  // the previous pass is done with the token list and x buffers
     fill_tokens(a, bk, p0, np, tok_b, tok_slot, tok_w);
     __syncthreads();
-    if (rbase >= rows) continue;
+    const int nt = (np + 15) / 16;
     if (bk.shared) {
-      const size_t off = (size_t)bk.e * a.IS;
-      gu_wave<st, st == DT::MXFP4 ? 1 : 2>(
-          reinterpret_cast<const uint8_t*>(a.sh_gate) + off * Gu<st>::row_bytes(a.H),
-          reinterpret_cast<const uint8_t*>(a.sh_up) + off * Gu<st>::row_bytes(a.H), nullptr,
-          nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot, tok_w, np, a.act, a.IA);
+      if (nt <= 1)
+        gu_pass<st, 1>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
+                       tok_w, np, xs, a.act, a.IA);
+      else if (nt <= 2)
+        gu_pass<st, 2>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
+                       tok_w, np, xs, a.act, a.IA);
+      else
+        gu_pass<st, 4>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
+                       tok_w, np, xs, a.act, a.IA);
     } else {
-      const size_t off = (size_t)bk.e * a.I;
-      const uint8_t* gs = a.gate_s ? a.gate_s + off * (a.H / 32) : nullptr;
-      const uint8_t* vs = a.up_s ? a.up_s + off * (a.H / 32) : nullptr;
-      gu_wave<et, et == DT::MXFP4 ? 1 : 2>(
-          reinterpret_cast<const uint8_t*>(a.gate) + off * Gu<et>::row_bytes(a.H),
-          reinterpret_cast<const uint8_t*>(a.up) + off * Gu<et>::row_bytes(a.H), gs, vs, a.H,
-          rows, rbase, a.xh, a.xl, tok_b, tok_slot, tok_w, np, a.act, a.IA);
+      if (nt <= 1)
+        gu_pass<et, 1>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot, tok_w, np,
+                       xs, a.act, a.IA);
+      else if (nt <= 2)
+        gu_pass<et, 2>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot, tok_w, np,
+                       xs, a.act, a.IA);
+      else
+        gu_pass<et, 4>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot, tok_w, np,
+                       xs, a.act, a.IA);
     }
   }
 }
@@ -529,8 +619,16 @@ template <DT et, DT st>
 hipError_t launch_bs_typed(const BsArgs& a, hipStream_t s) {
   const int items = a.slots_max + a.NS;
   const int rows = a.I > a.IS ? a.I : a.IS;
+  constexpr int gu_lds = 2 * 2 * kGuBuf * 2;
+  static bool lds_set = false;
+  if (!lds_set) {
+    hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(bs_gateup_kernel<et, st>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, gu_lds);
+    if (e0 != hipSuccess) return e0;
+    lds_set = true;
+  }
   hipLaunchKernelGGL((bs_gateup_kernel<et, st>), dim3((rows + kGuRows - 1) / kGuRows, items),
-                     dim3(kGuWaves * 64), 0, s, a);
+                     dim3(kGuWaves * 64), gu_lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int cmin = dn_cols<et>() < dn_cols<st>() ? dn_cols<et>() : dn_cols<st>();
