@@ -41,11 +41,12 @@ constexpr int kGuTok = 64;                      // tokens per pass (up to 4 toke
 constexpr int kGuXElems = 8192;                 // staged x elements per buffer and array
 constexpr int kGuPad = 8;                       // bf16 padding per staged x row
 constexpr int kGuBuf = kGuXElems + kGuTok * kGuPad;
-constexpr int kGuDA = 2;                        // weight steps prefetched in registers
 
 // K width of one staged x chunk for NT token tiles (fixed LDS budget).
 template <int NT> constexpr int gu_kx() { return kGuXElems / (16 * NT); }
 template <int NT> constexpr int gu_ldx() { return gu_kx<NT>() + kGuPad; }
+constexpr int gu_gcd(int a, int b) { return b == 0 ? a : gu_gcd(b, a % b); }
+constexpr int gu_lcm(int a, int b) { return a / gu_gcd(a, b) * b; }
 
 // Weight fragments of one K step for one 16-row tile.  A step is STEP elements; MFMA
 // sub-step c of it takes A and B from the same K positions (boff).
@@ -70,30 +71,37 @@ template <> struct Gu<DT::BF16> {
 };
 
 template <> struct Gu<DT::MXFP4> {
-  static constexpr int STEP = 128, SUB = 4;  // lane: 32 codes (one scale block) per step
-  struct Raw { u32x4 q; uint32_t s; };
+  static constexpr int STEP = 256, SUB = 8;  // lane: 64 codes (two scale blocks) per step
+  struct Raw { u32x4 q[2]; uint32_t s[2]; };
   static __device__ __forceinline__ Raw load(const uint8_t* row, const uint8_t* srow, int k,
                                              int g) {
     Raw r;
-    r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + (k + 32 * g) / 2));
-    r.s = srow[(k + 32 * g) / 32];  // scale lines are reused by the next steps: cached
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = k + 64 * g + 32 * p;
+      r.q[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + e / 2));
+      r.s[p] = srow[e / 32];  // scale lines are reused by the next steps: cached
+    }
     return r;
   }
-  // sub-step c = elements 8c .. 8c+7 of the lane's 32: code dword c, low nibble first
+  // sub-step c = elements 8c .. 8c+7 of the lane's 64: code dword c of the two pieces, low
+  // nibble first
   static __device__ __forceinline__ bf16x8 frag(const Raw& r, int c) {
-    const float sc = __uint_as_float(r.s << 23);
-    const uint32_t w = c == 0 ? r.q.x : c == 1 ? r.q.y : c == 2 ? r.q.z : r.q.w;
+    const float sc = __uint_as_float(r.s[c >> 2] << 23);
+    const u32x4& q = r.q[c >> 2];
+    const uint32_t w = (c & 3) == 0 ? q.x : (c & 3) == 1 ? q.y : (c & 3) == 2 ? q.z : q.w;
     const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
     const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
     const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
     const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
     return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
   }
-  static __device__ __forceinline__ int boff(int c, int g) { return 32 * g + 8 * c; }
+  static __device__ __forceinline__ int boff(int c, int g) { return 64 * g + 8 * c; }
   static __host__ __device__ constexpr size_t row_bytes(int H) { return (size_t)H / 2; }
 };
 
-// The staged x of tokens tok_b[0..16NT) (padded with the first token), K [kc, kc + kx):
+// The staged x of tokens tok_b[0..np) (token columns past np repeat the first token, and
+// their results are dropped; unconditional loads keep the load counters exact), K [kc, kc + kx):
 // 1024 pieces of 16 bytes per array, 4 per thread; K past H reads the last valid piece
 // and is never used.
 struct GuX {
@@ -102,7 +110,7 @@ struct GuX {
 
 template <int NT>
 __device__ __forceinline__ void gu_x_load(GuX& xr, const uint16_t* xh, const uint16_t* xl,
-                                          int H, const int* tok_b, int np, int kc) {
+                                          int H, const lds_i32* tok_b, int np, int kc) {
   constexpr int PR = gu_kx<NT>() / 8;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -118,14 +126,14 @@ __device__ __forceinline__ void gu_x_load(GuX& xr, const uint16_t* xh, const uin
 }
 
 template <int NT>
-__device__ __forceinline__ void gu_x_store(const GuX& xr, uint16_t* xs_h, uint16_t* xs_l) {
+__device__ __forceinline__ void gu_x_store(const GuX& xr, lds_u16* xs_h, lds_u16* xs_l) {
   constexpr int PR = gu_kx<NT>() / 8;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = threadIdx.x + i * kGuWaves * 64;
     const int tok = p / PR, q = p % PR;
-    *reinterpret_cast<u32x4*>(xs_h + tok * gu_ldx<NT>() + 8 * q) = xr.h[i];
-    *reinterpret_cast<u32x4*>(xs_l + tok * gu_ldx<NT>() + 8 * q) = xr.l[i];
+    lds_st128(xs_h + tok * gu_ldx<NT>() + 8 * q, xr.h[i]);
+    lds_st128(xs_l + tok * gu_ldx<NT>() + 8 * q, xr.l[i]);
   }
 }
 
@@ -145,8 +153,8 @@ __device__ __forceinline__ void gu_a_load(GuRing<dt>& ar, const uint8_t* const (
 
 // MFMAs of one K step (all its sub-steps) against the staged x at chunk offset k0.
 template <DT dt, int NT>
-__device__ __forceinline__ void gu_step(const GuRing<dt>& ar, const uint16_t* xs_h,
-                                        const uint16_t* xs_l, int k0, int l16, int g,
+__device__ __forceinline__ void gu_step(const GuRing<dt>& ar, const lds_u16* xs_h,
+                                        const lds_u16* xs_l, int k0, int l16, int g,
                                         f32x4 (&acc)[2][2][NT]) {
   using F = Gu<dt>;
 #pragma unroll
@@ -159,8 +167,8 @@ __device__ __forceinline__ void gu_step(const GuRing<dt>& ar, const uint16_t* xs
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int o = (16 * t + l16) * gu_ldx<NT>() + k0 + F::boff(c, g);
-      const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs_h + o));
-      const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs_l + o));
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, lds_ld128(xs_h + o));
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, lds_ld128(xs_l + o));
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -176,18 +184,20 @@ __device__ __forceinline__ void gu_step(const GuRing<dt>& ar, const uint16_t* xs
 }
 
 // One pass of one wave's 32 channels (rows rbase ..) for tokens tok_*[0..np), np <= 16 NT.
-// Weight fragments run kGuDA steps ahead in registers; the x chunk one chunk ahead.  The
+// Weight fragments run DA steps ahead in registers; the x chunk one chunk ahead.  The
 // full steps run pipelined; a K tail (H not a multiple of the step) runs after them with
 // masked fragments.
-template <DT dt, int NT>
-__device__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs, const uint8_t* Vs,
-                        int H, int rows, int rbase, const uint16_t* xh, const uint16_t* xl,
-                        const int* tok_b, const int* tok_slot, const float* tok_w, int np,
-                        uint16_t* xs, float* act, int IA) {
+template <DT dt, int NT, int DA>
+__device__ __forceinline__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs,
+                                        const uint8_t* Vs, int H, int rows, int rbase,
+                                        const uint16_t* xh, const uint16_t* xl,
+                                        const lds_i32* tok_b, const lds_i32* tok_slot,
+                                        const lds_f32* tok_w, int np, lds_u16* xs, float* act,
+                                        int IA) {
   using F = Gu<dt>;
   constexpr int KX = gu_kx<NT>();
   constexpr int SPC = KX / F::STEP;
-  constexpr int GRP = SPC > kGuDA ? SPC : kGuDA;
+  constexpr int GRP = gu_lcm(SPC, DA);  // keeps both the ring slot and the chunk phase
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const uint8_t* rp[2][2];
   const uint8_t* sp[2][2];
@@ -200,8 +210,8 @@ __device__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs, c
     sp[0][r] = Gs ? Gs + (size_t)row * (H / 32) : nullptr;
     sp[1][r] = Vs ? Vs + (size_t)row * (H / 32) : nullptr;
   }
-  uint16_t* xs_h[2] = {xs, xs + 2 * kGuBuf};
-  uint16_t* xs_l[2] = {xs + kGuBuf, xs + 3 * kGuBuf};
+  lds_u16* xs_h[2] = {xs, xs + 2 * kGuBuf};
+  lds_u16* xs_l[2] = {xs + kGuBuf, xs + 3 * kGuBuf};
   f32x4 acc[2][2][NT];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -212,12 +222,12 @@ __device__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs, c
   // full chunks, in groups of GRP steps
   const int nfull = (H / KX) * SPC;                  // steps in full chunks
   const int ngrp = nfull / GRP * GRP;                // steps run by the pipelined loop
-  GuRing<dt> ring[kGuDA];
+  GuRing<dt> ring[DA];
   GuX xr;
   gu_x_load<NT>(xr, xh, xl, H, tok_b, np, 0);
   if (ngrp > 0) {
 #pragma unroll
-    for (int d = 0; d < kGuDA; ++d) gu_a_load<dt>(ring[d], rp, sp, d * F::STEP, g);
+    for (int d = 0; d < DA; ++d) gu_a_load<dt>(ring[d], rp, sp, d * F::STEP, g);
   }
   gu_x_store<NT>(xr, xs_h[0], xs_l[0]);
   __syncthreads();
@@ -229,10 +239,10 @@ __device__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs, c
       const bool first = u % SPC == 0, last = u % SPC == SPC - 1;
       const bool more = (c + 1) * KX < H;  // another (full or partial) chunk follows
       if (first && more) gu_x_load<NT>(xr, xh, xl, H, tok_b, np, (c + 1) * KX);
-      gu_step<dt, NT>(ring[u % kGuDA], xs_h[c & 1], xs_l[c & 1], (u % SPC) * F::STEP, l16, g,
+      gu_step<dt, NT>(ring[u % DA], xs_h[c & 1], xs_l[c & 1], (u % SPC) * F::STEP, l16, g,
                       acc);
-      const int sn = st + kGuDA < ngrp ? st + kGuDA : ngrp - 1;  // spare refills: reread
-      gu_a_load<dt>(ring[u % kGuDA], rp, sp, sn * F::STEP, g);
+      const int sn = st + DA < ngrp ? st + DA : ngrp - 1;  // spare refills: reread
+      gu_a_load<dt>(ring[u % DA], rp, sp, sn * F::STEP, g);
       if (last) {
         if (more) gu_x_store<NT>(xr, xs_h[(c + 1) & 1], xs_l[(c + 1) & 1]);
         __syncthreads();
@@ -256,12 +266,15 @@ __device__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs, c
       for (int r = 0; r < 2; ++r) {
         // pieces that start past H read the row's last piece and are zeroed
         if constexpr (dt == DT::MXFP4) {
-          const int e0 = k + 32 * g;
-          const int ec = e0 < H ? e0 : H - 32;
           typename F::Raw v;
-          v.q = *reinterpret_cast<const u32x4*>(rp[m][r] + ec / 2);
-          v.s = sp[m][r][ec / 32];
-          if (e0 >= H) v.q = u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int e0 = k + 64 * g + 32 * p;
+            const int ec = e0 < H ? e0 : H - 32;
+            v.q[p] = *reinterpret_cast<const u32x4*>(rp[m][r] + ec / 2);
+            v.s[p] = sp[m][r][ec / 32];
+            if (e0 >= H) v.q[p] = u32x4{0, 0, 0, 0};
+          }
           ar.r[m][r] = v;
         } else {
           typename F::Raw v;
@@ -301,8 +314,9 @@ __device__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs, c
   }
 }
 
-// Token bucket of expert slot t: routed (t < slots_max) -> the union's bucket, shared ->
-// every token of the batch.
+// Token bucket of work item t: the shared experts first (t < NS, every token of the batch;
+// their workgroups read the most and are dispatched first), then the routed expert slots
+// (the union's buckets; slots past n_touched are empty).
 struct Bucket {
   int count;
   bool shared;
@@ -311,26 +325,27 @@ struct Bucket {
 
 __device__ __forceinline__ Bucket bucket_of(const BsArgs& a, int t) {
   Bucket b;
-  if (t < a.slots_max) {
-    b.shared = false;
-    if (t >= *a.n_touched) {
-      b.count = 0;
-      b.e = 0;
-      return b;
-    }
-    b.e = a.touched[t];
-    b.count = a.offsets[b.e + 1] - a.offsets[b.e];
-  } else {
+  if (t < a.NS) {
     b.shared = true;
-    b.e = t - a.slots_max;
+    b.e = t;
     b.count = a.B;
+    return b;
   }
+  t -= a.NS;
+  b.shared = false;
+  if (t >= *a.n_touched) {
+    b.count = 0;
+    b.e = 0;
+    return b;
+  }
+  b.e = a.touched[t];
+  b.count = a.offsets[b.e + 1] - a.offsets[b.e];
   return b;
 }
 
 // Fill the pass's token list: token index, act/partial row, weight.
 __device__ __forceinline__ void fill_tokens(const BsArgs& a, const Bucket& bk, int p0, int np,
-                                            int* tok_b, int* tok_slot, float* tok_w) {
+                                            lds_i32* tok_b, lds_i32* tok_slot, lds_f32* tok_w) {
   for (int i = threadIdx.x; i < np; i += blockDim.x) {
     if (bk.shared) {
       const int b = p0 + i;
@@ -346,16 +361,21 @@ __device__ __forceinline__ void fill_tokens(const BsArgs& a, const Bucket& bk, i
   }
 }
 
-template <DT et, DT st>
-__global__ __launch_bounds__(kGuWaves * 64) void bs_gateup_kernel(BsArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [2 buffers][hi, lo][kGuBuf]
-  __shared__ int tok_b[kGuTok];
-  __shared__ int tok_slot[kGuTok];
-  __shared__ float tok_w[kGuTok];
+// Buckets of at most kGuSmall tokens (every bucket at small batches) run in a launch of
+// their own with one token tile: without the wider tiles' registers it keeps two
+// workgroups per CU and a deeper weight ring.  Larger buckets run in the other launch.
+constexpr int kGuSmall = 16;
+// weight bytes in flight per wave: 16 KB (MXFP4: 2 steps of 256), 24 KB (bf16: 3 steps of 64)
+template <DT dt> constexpr int gu_da_small() { return dt == DT::MXFP4 ? 2 : 3; }
+constexpr int kGuDALarge = 2;
+
+template <DT et, DT st, bool SMALL>
+__device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i32* tok_b,
+                                            lds_i32* tok_slot, lds_f32* tok_w) {
   const Bucket bk = bucket_of(a, blockIdx.y);
   const int rows = bk.shared ? a.IS : a.I;
-  if (bk.count == 0 || blockIdx.x * kGuRows >= rows) return;  // whole workgroup leaves
+  if (bk.count == 0 || (bk.count <= kGuSmall) != SMALL || blockIdx.x * kGuRows >= rows)
+    return;  // whole workgroup leaves
   const int rbase = blockIdx.x * kGuRows + (threadIdx.x >> 6) * kGuRowsW;
   const uint8_t *G, *V, *Gs = nullptr, *Vs = nullptr;
   if (bk.shared) {
@@ -369,34 +389,61 @@ __global__ __launch_bounds__(kGuWaves * 64) void bs_gateup_kernel(BsArgs a) {
     if (a.gate_s) Gs = a.gate_s + off * (a.H / 32);
     if (a.up_s) Vs = a.up_s + off * (a.H / 32);
   }
-  for (int p0 = 0; p0 < bk.count; p0 += kGuTok) {
-    const int np = min(kGuTok, bk.count - p0);
-    __syncthreads();  // the previous pass is done with the token list and x buffers
-    fill_tokens(a, bk, p0, np, tok_b, tok_slot, tok_w);
+  if constexpr (SMALL) {
+    fill_tokens(a, bk, 0, bk.count, tok_b, tok_slot, tok_w);
     __syncthreads();
-    const int nt = (np + 15) / 16;
-    if (bk.shared) {
-      if (nt <= 1)
-        gu_pass<st, 1>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
-                       tok_w, np, xs, a.act, a.IA);
-      else if (nt <= 2)
-        gu_pass<st, 2>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
-                       tok_w, np, xs, a.act, a.IA);
-      else
-        gu_pass<st, 4>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
-                       tok_w, np, xs, a.act, a.IA);
-    } else {
-      if (nt <= 1)
-        gu_pass<et, 1>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot, tok_w, np,
-                       xs, a.act, a.IA);
-      else if (nt <= 2)
-        gu_pass<et, 2>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot, tok_w, np,
-                       xs, a.act, a.IA);
-      else
-        gu_pass<et, 4>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot, tok_w, np,
-                       xs, a.act, a.IA);
+    if (bk.shared)
+      gu_pass<st, 1, gu_da_small<st>()>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b,
+                                 tok_slot, tok_w, bk.count, xs, a.act, a.IA);
+    else
+      gu_pass<et, 1, gu_da_small<et>()>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
+                                 tok_w, bk.count, xs, a.act, a.IA);
+  } else {
+    for (int p0 = 0; p0 < bk.count; p0 += kGuTok) {
+      const int np = min(kGuTok, bk.count - p0);
+      __syncthreads();  // the previous pass is done with the token list and x buffers
+      fill_tokens(a, bk, p0, np, tok_b, tok_slot, tok_w);
+      __syncthreads();
+      const bool two = np <= 32;
+      if (bk.shared) {
+        if (two)
+          gu_pass<st, 2, kGuDALarge>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl,
+                                     tok_b, tok_slot, tok_w, np, xs, a.act, a.IA);
+        else
+          gu_pass<st, 4, kGuDALarge>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl,
+                                     tok_b, tok_slot, tok_w, np, xs, a.act, a.IA);
+      } else {
+        if (two)
+          gu_pass<et, 2, kGuDALarge>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b,
+                                     tok_slot, tok_w, np, xs, a.act, a.IA);
+        else
+          gu_pass<et, 4, kGuDALarge>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b,
+                                     tok_slot, tok_w, np, xs, a.act, a.IA);
+      }
     }
   }
+}
+
+// x buffers in dynamic LDS: [2 buffers][hi, lo][kGuBuf]
+template <DT et, DT st>
+__global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bs_gateup_small_kernel(BsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int tok_b[kGuTok];
+  __shared__ int tok_slot[kGuTok];
+  __shared__ float tok_w[kGuTok];
+  gateup_body<et, st, true>(a, (lds_u16*)smem, (lds_i32*)tok_b, (lds_i32*)tok_slot,
+                            (lds_f32*)tok_w);
+}
+
+template <DT et, DT st>
+__global__ __launch_bounds__(kGuWaves * 64) void bs_gateup_large_kernel(BsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int tok_b[kGuTok];
+  __shared__ int tok_slot[kGuTok];
+  __shared__ float tok_w[kGuTok];
+  gateup_body<et, st, false>(a, (lds_u16*)smem, (lds_i32*)tok_b, (lds_i32*)tok_slot,
+                             (lds_f32*)tok_w);
 }
 
 // ------------------------------------------------------------------------------------
@@ -456,7 +503,7 @@ template <DT dt> constexpr int dn_cols() { return 64 * Dn<dt>::EPT; }
 // kDnU rows starting at j (TAIL: some of them past j1, which get weight 0).
 template <DT dt, int NT, bool TAIL>
 __device__ __forceinline__ void dn_rows(const uint8_t* D, const uint8_t* Ds, size_t rb, int H,
-                                        int hc, int j, int j1, const float* const (&ap)[NT],
+                                        int hc, int j, int j1, const gbl_f32* const (&ap)[NT],
                                         float (&acc)[NT][Dn<dt>::EPT]) {
   using F = Dn<dt>;
   constexpr int EPT = F::EPT;
@@ -492,7 +539,7 @@ __device__ __forceinline__ void dn_pass(const uint8_t* D, const uint8_t* Ds, int
   constexpr int EPT = F::EPT;
   const size_t rb = F::row_bytes(H);
   const int hc = live ? h : 0;  // dead lanes read column 0 and store nothing
-  const float* ap[NT];
+  const gbl_f32* ap[NT];
 #pragma unroll
   for (int p = 0; p < NT; ++p) {
     ap[p] = uniform_ptr(act + (size_t)pslot[p] * IA);
@@ -622,15 +669,26 @@ hipError_t launch_bs_typed(const BsArgs& a, hipStream_t s) {
   constexpr int gu_lds = 2 * 2 * kGuBuf * 2;
   static bool lds_set = false;
   if (!lds_set) {
-    hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(bs_gateup_kernel<et, st>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, gu_lds);
+    hipError_t e0 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(bs_gateup_small_kernel<et, st>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, gu_lds);
+    if (e0 == hipSuccess)
+      e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(bs_gateup_large_kernel<et, st>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, gu_lds);
     if (e0 != hipSuccess) return e0;
     lds_set = true;
   }
-  hipLaunchKernelGGL((bs_gateup_kernel<et, st>), dim3((rows + kGuRows - 1) / kGuRows, items),
-                     dim3(kGuWaves * 64), gu_lds, s, a);
+  const dim3 gu_grid((rows + kGuRows - 1) / kGuRows, items);
+  hipLaunchKernelGGL((bs_gateup_small_kernel<et, st>), gu_grid, dim3(kGuWaves * 64), gu_lds, s,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.B > kGuSmall) {  // no bucket holds more tokens than the batch
+    hipLaunchKernelGGL((bs_gateup_large_kernel<et, st>), gu_grid, dim3(kGuWaves * 64), gu_lds,
+                       s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int cmin = dn_cols<et>() < dn_cols<st>() ? dn_cols<et>() : dn_cols<st>();
   hipLaunchKernelGGL((bs_down_kernel<et, st>), dim3((a.H + cmin - 1) / cmin, items),
                      dim3(kDnWaves * 64), 0, s, a);

@@ -11,6 +11,21 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Pointers typed as LDS (address space 3).  Buffers chosen at run time among several LDS
+// arrays can otherwise reach the accesses as generic pointers, which compile to flat
+// memory operations that count against the global-load counter as well: waiting for one
+// of them then drains every global load in flight.
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) int lds_i32;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+__device__ __forceinline__ u32x4 lds_ld128(const lds_u16* p) {
+  return *reinterpret_cast<const lds_u32x4*>(p);
+}
+__device__ __forceinline__ void lds_st128(lds_u16* p, const u32x4& v) {
+  *reinterpret_cast<lds_u32x4*>(p) = v;
+}
+
 // MXFP4W is MXFP4 read in 16-element chunks (8 bytes of codes + the block's scale byte per
 // thread and row) instead of 8-element ones: the same bytes, twice as many per load.
 enum class DT : int { F32 = 0, BF16 = 1, MXFP4 = 2, MXFP4W = 3 };
@@ -116,14 +131,17 @@ template <> struct Fmt<DT::MXFP4W> {
 
 // A pointer every lane of the wave holds the same value of, moved to scalar registers so
 // that loads use a scalar base plus a per-lane 32-bit offset (one offset register serves
-// every row of a batch instead of a 64-bit address register pair per row).
+// every row of a batch instead of a 64-bit address register pair per row).  The result is
+// typed as global memory (address space 1): an address rebuilt from integers is otherwise
+// generic, and its loads become flat operations (see the LDS-typed pointers above).
 template <typename T>
-__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+__device__ __forceinline__ const __attribute__((address_space(1))) T* uniform_ptr(const T* p) {
   const uint64_t u = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+  return (const __attribute__((address_space(1))) T*)(((uint64_t)hi << 32) | lo);
 }
+typedef __attribute__((address_space(1))) float gbl_f32;
 
 // Address of row r of a stacked [rows][H] tensor, and of its MXFP4 scale row.
 template <DT dt>

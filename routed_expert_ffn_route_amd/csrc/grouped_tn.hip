@@ -59,7 +59,7 @@ struct XRegs {
 };
 
 template <int NT>
-__device__ __forceinline__ void x_load(XRegs& xr, const TnArgs& a, const int* tok_b, int np,
+__device__ __forceinline__ void x_load(XRegs& xr, const TnArgs& a, const lds_i32* tok_b, int np,
                                        int kc) {
   constexpr int PR = kx<NT>() / 8;  // pieces per token row
 #pragma unroll
@@ -74,14 +74,14 @@ __device__ __forceinline__ void x_load(XRegs& xr, const TnArgs& a, const int* to
 }
 
 template <int NT>
-__device__ __forceinline__ void x_store(const XRegs& xr, uint16_t* xs_h, uint16_t* xs_l) {
+__device__ __forceinline__ void x_store(const XRegs& xr, lds_u16* xs_h, lds_u16* xs_l) {
   constexpr int PR = kx<NT>() / 8;
 #pragma unroll
   for (int i = 0; i < kPP; ++i) {
     const int p = threadIdx.x + i * kWaves * 64;
     const int tok = p / PR, q = p % PR;
-    *reinterpret_cast<u32x4*>(xs_h + tok * ldx<NT>() + 8 * q) = xr.h[i];
-    *reinterpret_cast<u32x4*>(xs_l + tok * ldx<NT>() + 8 * q) = xr.l[i];
+    lds_st128(xs_h + tok * ldx<NT>() + 8 * q, xr.h[i]);
+    lds_st128(xs_l + tok * ldx<NT>() + 8 * q, xr.l[i]);
   }
 }
 
@@ -102,8 +102,8 @@ __device__ __forceinline__ void a_load(ARegs& ar, const uint8_t* const (&rp)[2],
 // MFMAs of one 64-wide K step against the staged x at column offset k0: all hi products,
 // then all lo products, so that an accumulator's next MFMA is 2 NT issues away.
 template <int NT>
-__device__ __forceinline__ void step_mfma(const ARegs& ar, const uint16_t* xs_h,
-                                          const uint16_t* xs_l, int k0, int l16, int g,
+__device__ __forceinline__ void step_mfma(const ARegs& ar, const lds_u16* xs_h,
+                                          const lds_u16* xs_l, int k0, int l16, int g,
                                           f32x4 (&acc)[2][NT]) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -113,8 +113,8 @@ __device__ __forceinline__ void step_mfma(const ARegs& ar, const uint16_t* xs_h,
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int o = (16 * t + l16) * ldx<NT>() + k0 + 32 * s + 8 * g;
-      bh[t] = *reinterpret_cast<const u32x4*>(xs_h + o);
-      bl[t] = *reinterpret_cast<const u32x4*>(xs_l + o);
+      bh[t] = lds_ld128(xs_h + o);
+      bl[t] = lds_ld128(xs_l + o);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -136,8 +136,9 @@ __device__ __forceinline__ void step_mfma(const ARegs& ar, const uint16_t* xs_h,
 // chunk ahead (registers, then the other LDS buffer).  nst is a multiple of the unrolled
 // group (H is a multiple of 1024).
 template <int NT, int DA>
-__device__ void tn_pass(const TnArgs& a, const uint8_t* Me, int rbase, const int* tok_b,
-                        const int* tok_slot, const float* tok_w, int np, uint16_t* xs) {
+__device__ __forceinline__ void tn_pass(const TnArgs& a, const uint8_t* Me, int rbase,
+                                        const lds_i32* tok_b, const lds_i32* tok_slot,
+                                        const lds_f32* tok_w, int np, lds_u16* xs) {
   constexpr int KX = kx<NT>();
   constexpr int SPC = KX / kKA;  // weight steps per x chunk
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
@@ -148,8 +149,8 @@ __device__ void tn_pass(const TnArgs& a, const uint8_t* Me, int rbase, const int
     row = row < a.I ? row : a.I - 1;  // rows past the end compute values that are dropped
     rp[r] = Me + (size_t)row * a.H * 2;
   }
-  uint16_t* xs_h[2] = {xs, xs + 2 * kBufElems};
-  uint16_t* xs_l[2] = {xs + kBufElems, xs + 3 * kBufElems};
+  lds_u16* xs_h[2] = {xs, xs + 2 * kBufElems};
+  lds_u16* xs_l[2] = {xs + kBufElems, xs + 3 * kBufElems};
   f32x4 acc[2][NT];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
@@ -210,10 +211,13 @@ __device__ void tn_pass(const TnArgs& a, const uint8_t* Me, int rbase, const int
 template <bool SMALL>
 __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [2 buffers][hi, lo][kBufElems]
-  __shared__ int tok_b[kTokMax];
-  __shared__ int tok_slot[kTokMax];
-  __shared__ float tok_w[kTokMax];
+  lds_u16* xs = (lds_u16*)smem;  // [2 buffers][hi, lo][kBufElems]
+  __shared__ int tok_b_[kTokMax];
+  __shared__ int tok_slot_[kTokMax];
+  __shared__ float tok_w_[kTokMax];
+  lds_i32* tok_b = (lds_i32*)tok_b_;
+  lds_i32* tok_slot = (lds_i32*)tok_slot_;
+  lds_f32* tok_w = (lds_f32*)tok_w_;
   const int t = blockIdx.y;
   if (t >= *a.n_touched || blockIdx.x * kRows >= a.I) return;  // whole workgroup leaves
   const int e = a.touched[t];
