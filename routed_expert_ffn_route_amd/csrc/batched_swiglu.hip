@@ -41,6 +41,7 @@ constexpr int kGuTok = 64;                      // tokens per pass (up to 4 toke
 constexpr int kGuXElems = 8192;                 // staged x elements per buffer and array
 constexpr int kGuPad = 8;                       // bf16 padding per staged x row
 constexpr int kGuBuf = kGuXElems + kGuTok * kGuPad;
+constexpr int kGuLds = 2 * 2 * kGuBuf * 2;      // dynamic LDS: [2 buffers][hi, lo][kGuBuf] bf16
 
 // K width of one staged x chunk for NT token tiles (fixed LDS budget).
 template <int NT> constexpr int gu_kx() { return kGuXElems / (16 * NT); }
@@ -54,8 +55,10 @@ template <DT dt> struct Gu;
 
 template <> struct Gu<DT::BF16> {
   static constexpr int STEP = 64, SUB = 2;  // lane: 16 bytes per sub-step
+  static constexpr bool kWideScales = false;
   struct Raw { u32x4 f[2]; };
-  static __device__ __forceinline__ Raw load(const uint8_t* row, const uint8_t*, int k, int g) {
+  static __device__ __forceinline__ Raw load(const uint8_t* row, const uint8_t*, int k, int g,
+                                             bool) {
     Raw r;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -63,31 +66,45 @@ template <> struct Gu<DT::BF16> {
           reinterpret_cast<const u32x4*>(row + (size_t)(k + 32 * c + 8 * g) * 2));
     return r;
   }
-  static __device__ __forceinline__ bf16x8 frag(const Raw& r, int c) {
+  static __device__ __forceinline__ void pass_on(const Raw&, Raw&) {}
+  static __device__ __forceinline__ bf16x8 frag(const Raw& r, int c, int) {
     return __builtin_bit_cast(bf16x8, r.f[c]);
   }
   static __device__ __forceinline__ int boff(int c, int g) { return 32 * c + 8 * g; }
   static __host__ __device__ constexpr size_t row_bytes(int H) { return (size_t)H * 2; }
 };
 
+// MXFP4 step of 256 elements: lane group g takes elements [32g, 32g + 32) and
+// [128 + 32g, 160 + 32g), so each load instruction reads 64 contiguous code bytes of each of
+// its 16 rows.  The scales of two steps are 16 bytes of the row (16-aligned when H is a
+// multiple of 512), read once with the even step by all four lanes of the row: lane g's
+// scale bytes are byte g of each dword (dwords 0, 1 for the even step's two pieces, 2, 3 for
+// the odd step's, handed to the odd step's fragments by pass_on).  Loading a scale per
+// piece and step instead doubled the cache lines each step touches, and line lookups, not
+// bytes, bound this stream.
 template <> struct Gu<DT::MXFP4> {
-  static constexpr int STEP = 256, SUB = 8;  // lane: 64 codes (two scale blocks) per step
-  struct Raw { u32x4 q[2]; uint32_t s[2]; };
+  static constexpr int STEP = 256, SUB = 8;
+  static constexpr bool kWideScales = true;
+  struct Raw { u32x4 q[2]; u32x4 s; };
   static __device__ __forceinline__ Raw load(const uint8_t* row, const uint8_t* srow, int k,
-                                             int g) {
+                                             int g, bool even) {
     Raw r;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int e = k + 64 * g + 32 * p;
-      r.q[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + e / 2));
-      r.s[p] = srow[e / 32];  // scale lines are reused by the next steps: cached
-    }
+    for (int p = 0; p < 2; ++p)
+      r.q[p] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(row + (k + 32 * g + 128 * p) / 2));
+    if (even)  // scale lines are reused by later steps: cached load
+      r.s = *(const __attribute__((address_space(1))) u32x4*)(srow + k / 32);
     return r;
   }
-  // sub-step c = elements 8c .. 8c+7 of the lane's 64: code dword c of the two pieces, low
-  // nibble first
-  static __device__ __forceinline__ bf16x8 frag(const Raw& r, int c) {
-    const float sc = __uint_as_float(r.s[c >> 2] << 23);
+  static __device__ __forceinline__ void pass_on(const Raw& even, Raw& odd) {
+    odd.s.x = even.s.z;
+    odd.s.y = even.s.w;
+  }
+  // sub-step c = elements 8(c & 3) .. +7 of piece c >> 2: code dword c & 3, low nibble first
+  static __device__ __forceinline__ bf16x8 frag(const Raw& r, int c, int g) {
+    const uint32_t sb = __builtin_amdgcn_ubfe((c >> 2) ? r.s.y : r.s.x, 8 * g, 8);
+    const float sc = __uint_as_float(sb << 23);
     const u32x4& q = r.q[c >> 2];
     const uint32_t w = (c & 3) == 0 ? q.x : (c & 3) == 1 ? q.y : (c & 3) == 2 ? q.z : q.w;
     const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
@@ -96,9 +113,17 @@ template <> struct Gu<DT::MXFP4> {
     const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
     return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
   }
-  static __device__ __forceinline__ int boff(int c, int g) { return 64 * g + 8 * c; }
+  static __device__ __forceinline__ int boff(int c, int g) {
+    return 32 * g + 128 * (c >> 2) + 8 * (c & 3);
+  }
   static __host__ __device__ constexpr size_t row_bytes(int H) { return (size_t)H / 2; }
 };
+
+// Steps the pipelined loops may run with the wide scale loads (all of them for bf16).
+template <DT dt>
+__device__ __forceinline__ bool gu_wide_ok(int H) {
+  return !Gu<dt>::kWideScales || H % 512 == 0;
+}
 
 // The staged x of tokens tok_b[0..np) (token columns past np repeat the first token, and
 // their results are dropped; unconditional loads keep the load counters exact), K [kc, kc + kx):
@@ -144,18 +169,31 @@ struct GuRing {
 
 template <DT dt>
 __device__ __forceinline__ void gu_a_load(GuRing<dt>& ar, const uint8_t* const (&rp)[2][2],
-                                          const uint8_t* const (&sp)[2][2], int k, int g) {
+                                          const uint8_t* const (&sp)[2][2], int k, int g,
+                                          bool even) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int r = 0; r < 2; ++r) ar.r[m][r] = Gu<dt>::load(rp[m][r], sp[m][r], k, g);
+    for (int r = 0; r < 2; ++r) ar.r[m][r] = Gu<dt>::load(rp[m][r], sp[m][r], k, g, even);
 }
 
-// MFMAs of one K step (all its sub-steps) against the staged x at chunk offset k0.
-template <DT dt, int NT>
+// The odd step's scales come from the even step's fragments (MXFP4).
+template <DT dt>
+__device__ __forceinline__ void gu_pass_on(const GuRing<dt>& even, GuRing<dt>& odd) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) Gu<dt>::pass_on(even.r[m][r], odd.r[m][r]);
+}
+
+// MFMAs of one K step (all its sub-steps) against the staged x: token tile t of the lane
+// starts at xo[t], the step at k0.  CLAMP (a K tail): x positions past kmax read the piece
+// at kmax, whose finite values meet zeroed weights.
+template <DT dt, int NT, bool CLAMP = false>
 __device__ __forceinline__ void gu_step(const GuRing<dt>& ar, const lds_u16* xs_h,
-                                        const lds_u16* xs_l, int k0, int l16, int g,
-                                        f32x4 (&acc)[2][2][NT]) {
+                                        const lds_u16* xs_l, const int (&xo)[NT], int k0,
+                                        int g, f32x4 (&acc)[2][2][NT],
+                                        int kmax = 0) {
   using F = Gu<dt>;
 #pragma unroll
   for (int c = 0; c < F::SUB; ++c) {
@@ -163,10 +201,12 @@ __device__ __forceinline__ void gu_step(const GuRing<dt>& ar, const lds_u16* xs_
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int r = 0; r < 2; ++r) af[m][r] = F::frag(ar.r[m][r], c);
+      for (int r = 0; r < 2; ++r) af[m][r] = F::frag(ar.r[m][r], c, g);
+    int kk = k0 + F::boff(c, g);
+    if (CLAMP) kk = kk < kmax ? kk : kmax;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int o = (16 * t + l16) * gu_ldx<NT>() + k0 + F::boff(c, g);
+      const int o = xo[t] + kk;
       const bf16x8 bh = __builtin_bit_cast(bf16x8, lds_ld128(xs_h + o));
       const bf16x8 bl = __builtin_bit_cast(bf16x8, lds_ld128(xs_l + o));
 #pragma unroll
@@ -183,114 +223,76 @@ __device__ __forceinline__ void gu_step(const GuRing<dt>& ar, const lds_u16* xs_
   }
 }
 
-// One pass of one wave's 32 channels (rows rbase ..) for tokens tok_*[0..np), np <= 16 NT.
-// Weight fragments run DA steps ahead in registers; the x chunk one chunk ahead.  The
-// full steps run pipelined; a K tail (H not a multiple of the step) runs after them with
-// masked fragments.
-template <DT dt, int NT, int DA>
-__device__ __forceinline__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs,
-                                        const uint8_t* Vs, int H, int rows, int rbase,
-                                        const uint16_t* xh, const uint16_t* xl,
-                                        const lds_i32* tok_b, const lds_i32* tok_slot,
-                                        const lds_f32* tok_w, int np, lds_u16* xs, float* act,
-                                        int IA) {
-  using F = Gu<dt>;
-  constexpr int KX = gu_kx<NT>();
-  constexpr int SPC = KX / F::STEP;
-  constexpr int GRP = gu_lcm(SPC, DA);  // keeps both the ring slot and the chunk phase
-  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
-  const uint8_t* rp[2][2];
+// Row pointers of the lane's two row tiles in G and V (and their scale rows).
+template <DT dt>
+struct GuRows {
+  const uint8_t* rp[2][2];  // [matrix][tile]
   const uint8_t* sp[2][2];
+};
+
+template <DT dt>
+__device__ __forceinline__ GuRows<dt> gu_rows(const uint8_t* G, const uint8_t* V,
+                                              const uint8_t* Gs, const uint8_t* Vs, int H,
+                                              int rows, int rbase, int l16, int g) {
+  using F = Gu<dt>;
+  GuRows<dt> R;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     int row = rbase + 16 * r + l16;
     row = row < rows ? row : rows - 1;  // rows past the end compute values that are dropped
-    rp[0][r] = G + (size_t)row * F::row_bytes(H);
-    rp[1][r] = V + (size_t)row * F::row_bytes(H);
-    sp[0][r] = Gs ? Gs + (size_t)row * (H / 32) : nullptr;
-    sp[1][r] = Vs ? Vs + (size_t)row * (H / 32) : nullptr;
+    R.rp[0][r] = G + (size_t)row * F::row_bytes(H);
+    R.rp[1][r] = V + (size_t)row * F::row_bytes(H);
+    R.sp[0][r] = Gs ? Gs + (size_t)row * (H / 32) : nullptr;
+    R.sp[1][r] = Vs ? Vs + (size_t)row * (H / 32) : nullptr;
   }
-  lds_u16* xs_h[2] = {xs, xs + 2 * kGuBuf};
-  lds_u16* xs_l[2] = {xs + kGuBuf, xs + 3 * kGuBuf};
-  f32x4 acc[2][2][NT];
+  return R;
+}
+
+// Weight fragments of a step that may reach past H: pieces that start past H read the
+// row's last piece and are zeroed.
+template <DT dt>
+__device__ __forceinline__ void gu_a_load_masked(GuRing<dt>& ar, const GuRows<dt>& R, int H,
+                                                 int k, int g) {
+  using F = Gu<dt>;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < 2; ++r) {
+      typename F::Raw v;
+      if constexpr (dt == DT::MXFP4) {
+        // any H that is a multiple of 32: the scale byte is read from the aligned dword
+        // holding it and placed where frag looks for it (byte g of s.x, s.y)
+        uint32_t sw[2];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[m][r][t] = f32x4{0, 0, 0, 0};
-  // full chunks, in groups of GRP steps
-  const int nfull = (H / KX) * SPC;                  // steps in full chunks
-  const int ngrp = nfull / GRP * GRP;                // steps run by the pipelined loop
-  GuRing<dt> ring[DA];
-  GuX xr;
-  gu_x_load<NT>(xr, xh, xl, H, tok_b, np, 0);
-  if (ngrp > 0) {
+        for (int p = 0; p < 2; ++p) {
+          const int e0 = k + 32 * g + 128 * p;
+          const int ec = e0 < H ? e0 : H - 32;
+          v.q[p] = *reinterpret_cast<const u32x4*>(R.rp[m][r] + ec / 2);
+          const uintptr_t a = reinterpret_cast<uintptr_t>(R.sp[m][r] + ec / 32);
+          const uint32_t w = *(const __attribute__((address_space(1))) uint32_t*)(
+              a & ~static_cast<uintptr_t>(3));
+          sw[p] = __builtin_amdgcn_ubfe(w, 8 * static_cast<uint32_t>(a & 3), 8) << (8 * g);
+          if (e0 >= H) v.q[p] = u32x4{0, 0, 0, 0};
+        }
+        v.s = u32x4{sw[0], sw[1], 0, 0};
+      } else {
 #pragma unroll
-    for (int d = 0; d < DA; ++d) gu_a_load<dt>(ring[d], rp, sp, d * F::STEP, g);
-  }
-  gu_x_store<NT>(xr, xs_h[0], xs_l[0]);
-  __syncthreads();
-  for (int base = 0; base < ngrp; base += GRP) {
-#pragma unroll
-    for (int u = 0; u < GRP; ++u) {
-      const int st = base + u;
-      const int c = st / SPC;
-      const bool first = u % SPC == 0, last = u % SPC == SPC - 1;
-      const bool more = (c + 1) * KX < H;  // another (full or partial) chunk follows
-      if (first && more) gu_x_load<NT>(xr, xh, xl, H, tok_b, np, (c + 1) * KX);
-      gu_step<dt, NT>(ring[u % DA], xs_h[c & 1], xs_l[c & 1], (u % SPC) * F::STEP, l16, g,
-                      acc);
-      const int sn = st + DA < ngrp ? st + DA : ngrp - 1;  // spare refills: reread
-      gu_a_load<dt>(ring[u % DA], rp, sp, sn * F::STEP, g);
-      if (last) {
-        if (more) gu_x_store<NT>(xr, xs_h[(c + 1) & 1], xs_l[(c + 1) & 1]);
-        __syncthreads();
-      }
-    }
-  }
-  // the rest of K (ngrp steps are done; x of chunk ngrp/SPC is staged): masked steps,
-  // staging further chunks as they are reached
-  for (int st = ngrp; st * F::STEP < H; ++st) {
-    const int c = st / SPC;
-    const int k = st * F::STEP;
-    if (st > ngrp && st % SPC == 0) {
-      gu_x_load<NT>(xr, xh, xl, H, tok_b, np, c * KX);
-      gu_x_store<NT>(xr, xs_h[c & 1], xs_l[c & 1]);
-      __syncthreads();
-    }
-    GuRing<dt> ar;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        // pieces that start past H read the row's last piece and are zeroed
-        if constexpr (dt == DT::MXFP4) {
-          typename F::Raw v;
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const int e0 = k + 64 * g + 32 * p;
-            const int ec = e0 < H ? e0 : H - 32;
-            v.q[p] = *reinterpret_cast<const u32x4*>(rp[m][r] + ec / 2);
-            v.s[p] = sp[m][r][ec / 32];
-            if (e0 >= H) v.q[p] = u32x4{0, 0, 0, 0};
-          }
-          ar.r[m][r] = v;
-        } else {
-          typename F::Raw v;
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const int e0 = k + 32 * cc + 8 * g;
-            const int ec = e0 < H ? e0 : H - 8;
-            v.f[cc] = *reinterpret_cast<const u32x4*>(rp[m][r] + (size_t)ec * 2);
-            if (e0 >= H) v.f[cc] = u32x4{0, 0, 0, 0};
-          }
-          ar.r[m][r] = v;
+        for (int cc = 0; cc < 2; ++cc) {
+          const int e0 = k + 32 * cc + 8 * g;
+          const int ec = e0 < H ? e0 : H - 8;
+          v.f[cc] = *reinterpret_cast<const u32x4*>(R.rp[m][r] + (size_t)ec * 2);
+          if (e0 >= H) v.f[cc] = u32x4{0, 0, 0, 0};
         }
       }
-    gu_step<dt, NT>(ar, xs_h[c & 1], xs_l[c & 1], k - c * KX, l16, g, acc);
-  }
-  // a = w * silu(g) * u for the lane's 4 rows of each tile and its token column
+      ar.r[m][r] = v;
+    }
+}
+
+// a = w * silu(g) * u for the lane's 4 rows of each tile and its token column.
+template <int NT>
+__device__ __forceinline__ void gu_epilogue(const f32x4 (&acc)[2][2][NT], int rows, int rbase,
+                                            int l16, int g, const lds_i32* tok_slot,
+                                            const lds_f32* tok_w, int np, float* act, int IA) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int tc = 16 * t + l16;
@@ -312,6 +314,162 @@ __device__ __forceinline__ void gu_pass(const uint8_t* G, const uint8_t* V, cons
       }
     }
   }
+}
+
+template <int NT>
+__device__ __forceinline__ void gu_acc_zero(f32x4 (&acc)[2][2][NT]) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[m][r][t] = f32x4{0, 0, 0, 0};
+}
+
+// One pass of one wave's 32 channels (rows rbase ..) for tokens tok_*[0..np), np <= 16 NT,
+// with x staged in chunks.  Weight fragments run DA steps ahead in registers; the x chunk
+// one chunk ahead.  The full steps run pipelined; a K tail (H not a multiple of the step)
+// runs after them with masked fragments.
+template <DT dt, int NT, int DA>
+__device__ __forceinline__ void gu_pass(const uint8_t* G, const uint8_t* V, const uint8_t* Gs,
+                                        const uint8_t* Vs, int H, int rows, int rbase,
+                                        const uint16_t* xh, const uint16_t* xl,
+                                        const lds_i32* tok_b, const lds_i32* tok_slot,
+                                        const lds_f32* tok_w, int np, lds_u16* xs, float* act,
+                                        int IA) {
+  using F = Gu<dt>;
+  constexpr int KX = gu_kx<NT>();
+  constexpr int SPC = KX / F::STEP;
+  static_assert(SPC >= 1 && KX % F::STEP == 0, "an x chunk holds whole steps");
+  constexpr int GRP = gu_lcm(SPC, DA);  // keeps both the ring slot and the chunk phase
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const GuRows<dt> R = gu_rows<dt>(G, V, Gs, Vs, H, rows, rbase, l16, g);
+  int xo[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) xo[t] = (16 * t + l16) * gu_ldx<NT>();
+  lds_u16* xs_h[2] = {xs, xs + 2 * kGuBuf};
+  lds_u16* xs_l[2] = {xs + kGuBuf, xs + 3 * kGuBuf};
+  f32x4 acc[2][2][NT];
+  gu_acc_zero<NT>(acc);
+  // full chunks, in groups of GRP steps
+  const int nfull = (H / KX) * SPC;                  // steps in full chunks
+  // steps run by the pipelined loop (none without the wide scale loads)
+  const int ngrp = gu_wide_ok<dt>(H) ? nfull / GRP * GRP : 0;
+  GuRing<dt> ring[DA];
+  GuX xr;
+  gu_x_load<NT>(xr, xh, xl, H, tok_b, np, 0);
+  if (ngrp > 0) {
+#pragma unroll
+    for (int d = 0; d < DA; ++d)
+      gu_a_load<dt>(ring[d], R.rp, R.sp, d * F::STEP, g, d % 2 == 0);
+  }
+  gu_x_store<NT>(xr, xs_h[0], xs_l[0]);
+  __syncthreads();
+  for (int base = 0; base < ngrp; base += GRP) {
+#pragma unroll
+    for (int u = 0; u < GRP; ++u) {
+      const int st = base + u;
+      const int c = st / SPC;
+      const bool first = u % SPC == 0, last = u % SPC == SPC - 1;
+      // x of the next chunk, also past the end of K (pieces clamp to H - 8; the buffer is
+      // not read again): a load under a run-time branch would leave the load counters
+      // unknown after it, and every later wait would drain all loads in flight
+      if (first) gu_x_load<NT>(xr, xh, xl, H, tok_b, np, (c + 1) * KX);
+      // Issue order is kept as written: the load counter completes in order, so a refill
+      // the scheduler sank below the x loads would be waited for at the x store.
+      __builtin_amdgcn_sched_barrier(0);
+      gu_step<dt, NT>(ring[u % DA], xs_h[c & 1], xs_l[c & 1], xo, (u % SPC) * F::STEP, g,
+                      acc);
+      if (u % 2 == 0) gu_pass_on<dt>(ring[u % DA], ring[(u + 1) % DA]);
+      const int sn = st + DA < ngrp ? st + DA : st;  // spare refills reread this step
+      gu_a_load<dt>(ring[u % DA], R.rp, R.sp, sn * F::STEP, g, u % 2 == 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (last) {
+        gu_x_store<NT>(xr, xs_h[(c + 1) & 1], xs_l[(c + 1) & 1]);
+        __syncthreads();
+      }
+    }
+  }
+  // the rest of K (ngrp steps are done; x of chunk ngrp/SPC is staged): masked steps,
+  // staging further chunks as they are reached
+  for (int st = ngrp; st * F::STEP < H; ++st) {
+    const int c = st / SPC;
+    const int k = st * F::STEP;
+    if (st > ngrp && st % SPC == 0) {
+      gu_x_load<NT>(xr, xh, xl, H, tok_b, np, c * KX);
+      gu_x_store<NT>(xr, xs_h[c & 1], xs_l[c & 1]);
+      __syncthreads();
+    }
+    GuRing<dt> ar;
+    gu_a_load_masked<dt>(ar, R, H, k, g);
+    gu_step<dt, NT>(ar, xs_h[c & 1], xs_l[c & 1], xo, k - c * KX, g, acc);
+  }
+  gu_epilogue<NT>(acc, rows, rbase, l16, g, tok_slot, tok_w, np, act, IA);
+}
+
+// LDS bytes of x held whole for np tokens (hi and lo rows of H + kGuPad bf16).
+__host__ __device__ constexpr int gu_res_bytes(int np, int H) { return np * (H + kGuPad) * 4; }
+template <DT dt>
+__device__ __forceinline__ bool gu_use_res(int np, int H) {
+  return dt == DT::MXFP4 && gu_res_bytes(np, H) <= kGuLds;
+}
+
+// One pass of one wave's 32 channels for np <= 16 tokens whose whole x is held in LDS
+// (staged once): the loop only streams weights, with no barrier and no x loads in it.
+// Token columns past np read the first token's x; their results are dropped.
+template <DT dt, int DA>
+__device__ __forceinline__ void gu_pass_res(const uint8_t* G, const uint8_t* V,
+                                            const uint8_t* Gs, const uint8_t* Vs, int H,
+                                            int rows, int rbase, const uint16_t* xh,
+                                            const uint16_t* xl, const lds_i32* tok_b,
+                                            const lds_i32* tok_slot, const lds_f32* tok_w,
+                                            int np, lds_u16* xs, float* act, int IA) {
+  using F = Gu<dt>;
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const GuRows<dt> R = gu_rows<dt>(G, V, Gs, Vs, H, rows, rbase, l16, g);
+  const int ldr = H + kGuPad;
+  lds_u16* xs_h = xs;
+  lds_u16* xs_l = xs + np * ldr;
+  const int nfull = H / F::STEP;
+  // steps run by the pipelined loop (none without the wide scale loads)
+  const int ngrp = gu_wide_ok<dt>(H) ? nfull / DA * DA : 0;
+  GuRing<dt> ring[DA];
+  if (ngrp > 0) {
+#pragma unroll
+    for (int d = 0; d < DA; ++d)
+      gu_a_load<dt>(ring[d], R.rp, R.sp, d * F::STEP, g, d % 2 == 0);
+  }
+  const int pr = H / 8;  // 16-byte pieces per x row
+  for (int p = threadIdx.x; p < np * pr; p += kGuWaves * 64) {
+    const int tok = p / pr, q = p - tok * pr;
+    const size_t off = (size_t)tok_b[tok] * H + 8 * q;
+    lds_st128(xs_h + tok * ldr + 8 * q, *reinterpret_cast<const u32x4*>(xh + off));
+    lds_st128(xs_l + tok * ldr + 8 * q, *reinterpret_cast<const u32x4*>(xl + off));
+  }
+  __syncthreads();
+  const int xo[1] = {(l16 < np ? l16 : 0) * ldr};
+  f32x4 acc[2][2][1];
+  gu_acc_zero<1>(acc);
+  for (int base = 0; base < ngrp; base += DA) {
+#pragma unroll
+    for (int u = 0; u < DA; ++u) {
+      const int st = base + u;
+      gu_step<dt, 1>(ring[u], xs_h, xs_l, xo, st * F::STEP, g, acc);
+      if (u % 2 == 0) gu_pass_on<dt>(ring[u], ring[(u + 1) % DA]);
+      const int sn = st + DA < ngrp ? st + DA : st;  // spare refills reread this step
+      gu_a_load<dt>(ring[u], R.rp, R.sp, sn * F::STEP, g, u % 2 == 0);
+      // each refill is issued right after its slot is consumed (left to itself the
+      // scheduler gathers them at the end of the group, and the next group then waits
+      // for all of them)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  for (int st = ngrp; st * F::STEP < H; ++st) {
+    GuRing<dt> ar;
+    gu_a_load_masked<dt>(ar, R, H, st * F::STEP, g);
+    gu_step<dt, 1, true>(ar, xs_h, xs_l, xo, st * F::STEP, g, acc, H - 8);
+  }
+  gu_epilogue<1>(acc, rows, rbase, l16, g, tok_slot, tok_w, np, act, IA);
 }
 
 // Token bucket of work item t: the shared experts first (t < NS, every token of the batch;
@@ -367,7 +525,12 @@ __device__ __forceinline__ void fill_tokens(const BsArgs& a, const Bucket& bk, i
 constexpr int kGuSmall = 16;
 // weight bytes in flight per wave: 16 KB (MXFP4: 2 steps of 256), 24 KB (bf16: 3 steps of 64)
 template <DT dt> constexpr int gu_da_small() { return dt == DT::MXFP4 ? 2 : 3; }
+template <DT dt> constexpr int gu_pass_tokens() {
+  return gu_kx<4>() >= Gu<dt>::STEP ? 64 : 32;
+}
 constexpr int kGuDALarge = 2;
+static_assert(gu_da_small<DT::MXFP4>() % 2 == 0 && kGuDALarge % 2 == 0,
+              "MXFP4 rings pair even and odd steps (their scales are read together)");
 
 template <DT et, DT st, bool SMALL>
 __device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i32* tok_b,
@@ -392,15 +555,30 @@ __device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i3
   if constexpr (SMALL) {
     fill_tokens(a, bk, 0, bk.count, tok_b, tok_slot, tok_w);
     __syncthreads();
-    if (bk.shared)
-      gu_pass<st, 1, gu_da_small<st>()>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b,
-                                 tok_slot, tok_w, bk.count, xs, a.act, a.IA);
-    else
-      gu_pass<et, 1, gu_da_small<et>()>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
-                                 tok_w, bk.count, xs, a.act, a.IA);
+    // MXFP4 buckets whose whole x fits in LDS skip the chunked staging (measured: faster for
+    // MXFP4 steps, slower for the short bf16 steps, which keep the chunks)
+    if (bk.shared) {
+      if (gu_use_res<st>(bk.count, a.H))
+        gu_pass_res<st, gu_da_small<st>()>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh,
+                                           a.xl, tok_b, tok_slot, tok_w, bk.count, xs, a.act,
+                                           a.IA);
+      else
+        gu_pass<st, 1, gu_da_small<st>()>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl,
+                                          tok_b, tok_slot, tok_w, bk.count, xs, a.act, a.IA);
+    } else {
+      if (gu_use_res<et>(bk.count, a.H))
+        gu_pass_res<et, gu_da_small<et>()>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b,
+                                           tok_slot, tok_w, bk.count, xs, a.act, a.IA);
+      else
+        gu_pass<et, 1, gu_da_small<et>()>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b,
+                                          tok_slot, tok_w, bk.count, xs, a.act, a.IA);
+    }
   } else {
-    for (int p0 = 0; p0 < bk.count; p0 += kGuTok) {
-      const int np = min(kGuTok, bk.count - p0);
+    // tokens per pass: 64 (four token tiles) where a four-tile x chunk holds a weight step,
+    // else 32 (the 256-element MXFP4 step)
+    const int ptok = bk.shared ? gu_pass_tokens<st>() : gu_pass_tokens<et>();
+    for (int p0 = 0; p0 < bk.count; p0 += ptok) {
+      const int np = min(ptok, bk.count - p0);
       __syncthreads();  // the previous pass is done with the token list and x buffers
       fill_tokens(a, bk, p0, np, tok_b, tok_slot, tok_w);
       __syncthreads();
@@ -409,14 +587,14 @@ __device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i3
         if (two)
           gu_pass<st, 2, kGuDALarge>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl,
                                      tok_b, tok_slot, tok_w, np, xs, a.act, a.IA);
-        else
+        else if constexpr (gu_pass_tokens<st>() == 64)
           gu_pass<st, 4, kGuDALarge>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl,
                                      tok_b, tok_slot, tok_w, np, xs, a.act, a.IA);
       } else {
         if (two)
           gu_pass<et, 2, kGuDALarge>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b,
                                      tok_slot, tok_w, np, xs, a.act, a.IA);
-        else
+        else if constexpr (gu_pass_tokens<et>() == 64)
           gu_pass<et, 4, kGuDALarge>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b,
                                      tok_slot, tok_w, np, xs, a.act, a.IA);
       }
@@ -666,7 +844,7 @@ template <DT et, DT st>
 hipError_t launch_bs_typed(const BsArgs& a, hipStream_t s) {
   const int items = a.slots_max + a.NS;
   const int rows = a.I > a.IS ? a.I : a.IS;
-  constexpr int gu_lds = 2 * 2 * kGuBuf * 2;
+  constexpr int gu_lds = kGuLds;
   static bool lds_set = false;
   if (!lds_set) {
     hipError_t e0 = hipFuncSetAttribute(

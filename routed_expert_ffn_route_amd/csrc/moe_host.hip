@@ -245,6 +245,8 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_weights* weigh
     if (mx != (w.gate_scale != nullptr) || mx != (w.up_scale != nullptr) ||
         mx != (w.down_scale != nullptr))
       return fail(MOE_ERR_ARG, "scales must be given iff expert_dtype is MXFP4");
+    if (mx && (!aligned16(w.gate_scale) || !aligned16(w.up_scale) || !aligned16(w.down_scale)))
+      return fail(MOE_ERR_ARG, "scale tensors must be 16-byte aligned");
     if (d.n_shared > 0) {
       if (!w.sh_gate || !w.sh_up || !w.sh_down_t)
         return fail(MOE_ERR_ARG, "shared expert tensors must be given");

@@ -59,8 +59,15 @@ SMALL = [
               I_shared=24, layers=1),
     T.reduced(WORKLOADS["mxfp4_e896_k16"], wid=156, H=2080, E=17, k=3, I=200, n_shared=0,
               I_shared=0, layers=1),
+    # MXFP4 buckets above 32 tokens (passes of 32), H a multiple of 512 (pipelined steps with
+    # the paired scale loads) and not (masked steps only); shared bf16 expert above 64
+    T.reduced(WORKLOADS["mxfp4_e896_k16"], wid=157, H=1024, E=4, k=2, I=72, n_shared=1,
+              I_shared=40, layers=1),
+    T.reduced(WORKLOADS["mxfp4_e896_k16"], wid=158, H=2080, E=3, k=2, I=48, n_shared=0,
+              I_shared=0, layers=1),
 ]
-BATCHES = {151: (2, 7, 40), 152: (70,), 153: (200,), 154: (3, 16), 155: (16,), 156: (9,)}
+BATCHES = {151: (2, 7, 40), 152: (70,), 153: (200,), 154: (3, 16), 155: (16,), 156: (9,),
+           157: (70,), 158: (50,)}
 CASES = [(wl, B) for wl in SMALL for B in BATCHES[wl.wid]]
 
 
