@@ -768,9 +768,16 @@ __device__ __forceinline__ void dn_item(const BsArgs& a, const Bucket& bk, const
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.x * dn_cols<dt>() + EPT * lane;
   const bool live = h < a.H;  // H is a multiple of 32 and EPT divides 32
-  const int per = (rows + kDnWaves - 1) / kDnWaves;
-  const int j0 = min(rows, wave * per), j1 = min(rows, j0 + per);
-  for (int p0 = 0; p0 < bk.count; p0 += NTM) {
+  // blockIdx.z = row slice + kDownRowSlices * pass group: the slice's channels, split in
+  // kDnWaves contiguous ranges, and every pass group-th pass of the bucket
+  const int rs = blockIdx.z % kDownRowSlices, pg = blockIdx.z / kDownRowSlices;
+  const int ngroups = gridDim.z / kDownRowSlices;
+  const int per_s = (rows + kDownRowSlices - 1) / kDownRowSlices;
+  const int s0 = min(rows, rs * per_s), s1 = min(rows, s0 + per_s);
+  const int per = (s1 - s0 + kDnWaves - 1) / kDnWaves;
+  const int j0 = min(s1, s0 + wave * per), j1 = min(s1, j0 + per);
+  float* part = a.part + (size_t)rs * a.pairs * a.H;  // this slice's partial rows
+  for (int p0 = pg * NTM; p0 < bk.count; p0 += ngroups * NTM) {
     const int np = min(NTM, bk.count - p0);
     __syncthreads();
     if (threadIdx.x < np) {
@@ -785,19 +792,19 @@ __device__ __forceinline__ void dn_item(const BsArgs& a, const Bucket& bk, const
     if (NTM >= 8 && np > 4) {
       float acc[8][EPT];
       dn_pass<dt, 8>(D, Ds, a.H, h, live, j0, j1, a.act, a.IA, ps, acc);
-      dn_reduce_store<dt, 8>(acc, red, ps, np, a.part, a.H, h, live);
+      dn_reduce_store<dt, 8>(acc, red, ps, np, part, a.H, h, live);
     } else if (NTM >= 4 && np > 2) {
       float acc[4][EPT];
       dn_pass<dt, 4>(D, Ds, a.H, h, live, j0, j1, a.act, a.IA, ps, acc);
-      dn_reduce_store<dt, 4>(acc, red, ps, np, a.part, a.H, h, live);
+      dn_reduce_store<dt, 4>(acc, red, ps, np, part, a.H, h, live);
     } else if (np > 1) {
       float acc[2][EPT];
       dn_pass<dt, 2>(D, Ds, a.H, h, live, j0, j1, a.act, a.IA, ps, acc);
-      dn_reduce_store<dt, 2>(acc, red, ps, np, a.part, a.H, h, live);
+      dn_reduce_store<dt, 2>(acc, red, ps, np, part, a.H, h, live);
     } else {
       float acc[1][EPT];
       dn_pass<dt, 1>(D, Ds, a.H, h, live, j0, j1, a.act, a.IA, ps, acc);
-      dn_reduce_store<dt, 1>(acc, red, ps, np, a.part, a.H, h, live);
+      dn_reduce_store<dt, 1>(acc, red, ps, np, part, a.H, h, live);
     }
   }
 }
@@ -825,17 +832,24 @@ __global__ __launch_bounds__(kDnWaves * 64) void bs_down_kernel(BsArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// Combine: y[b] = sum_i part[b*k + i] (routing order) + sum_s part[B*k + s*B + b]
+// Combine: y[b] = sum_i part[b*k + i] (routing order) + sum_s part[B*k + s*B + b], each
+// partial row the sum of its row slices in slice order
 // ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bs_combine_kernel(BsArgs a) {
   const int n4 = a.H / 4;
+  const size_t slice = (size_t)a.pairs * n4;  // f32x4 per row slice of the partials
   for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < (size_t)a.B * n4;
        idx += (size_t)gridDim.x * blockDim.x) {
     const int b = (int)(idx / n4), c = (int)(idx % n4);
     const f32x4* P = reinterpret_cast<const f32x4*>(a.part);
     f32x4 s = {0, 0, 0, 0};
-    for (int i = 0; i < a.k; ++i) s += P[(size_t)(b * a.k + i) * n4 + c];
-    for (int sh = 0; sh < a.NS; ++sh) s += P[(size_t)(a.B * a.k + sh * a.B + b) * n4 + c];
+    for (int i = 0; i < a.k; ++i)
+#pragma unroll
+      for (int r = 0; r < kDownRowSlices; ++r) s += P[r * slice + (size_t)(b * a.k + i) * n4 + c];
+    for (int sh = 0; sh < a.NS; ++sh)
+#pragma unroll
+      for (int r = 0; r < kDownRowSlices; ++r)
+        s += P[r * slice + (size_t)(a.B * a.k + sh * a.B + b) * n4 + c];
     reinterpret_cast<f32x4*>(a.y)[(size_t)b * n4 + c] = s;
   }
 }
@@ -868,7 +882,11 @@ hipError_t launch_bs_typed(const BsArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int cmin = dn_cols<et>() < dn_cols<st>() ? dn_cols<et>() : dn_cols<st>();
-  hipLaunchKernelGGL((bs_down_kernel<et, st>), dim3((a.H + cmin - 1) / cmin, items),
+  // pass groups: a bucket's passes (at most B pairs) spread over up to 8 workgroups
+  int groups = (a.B + 7) / 8;
+  groups = groups > 8 ? 8 : groups;
+  hipLaunchKernelGGL((bs_down_kernel<et, st>),
+                     dim3((a.H + cmin - 1) / cmin, items, kDownRowSlices * groups),
                      dim3(kDnWaves * 64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

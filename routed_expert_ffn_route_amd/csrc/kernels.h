@@ -100,11 +100,15 @@ struct BsArgs {
   const int32_t* offsets;
   const int32_t* slots;
   float* act;                           // [B*k + NS*B][IA] activations
-  float* part;                          // [B*k + NS*B][H] partial outputs
+  float* part;                          // [kDownRowSlices][pairs][H] partial outputs
   float* y;                             // [B][H]
   int H, I, IS, IA, E, k, B, NS;
+  int pairs;                            // B*k + NS*B
   int slots_max;                        // min(E, B*k): routed expert slots launched
 };
+// The down products of an expert are split in this many channel slices, each with its own
+// partial rows (more, shorter workgroups); the combine adds them in slice order.
+constexpr int kDownRowSlices = 2;
 hipError_t launch_batched_swiglu(const BsArgs& a, DT et, DT st, hipStream_t s);
 
 // Load-time preparation: ||d_j||_2 of every row of a stacked [rows][H] tensor.

@@ -124,11 +124,12 @@ Layout layout_of(const moe_layer_desc* d) {
   const size_t pairs = batched_swiglu ? B * k + (size_t)d->n_shared * B : 0;
   const size_t ia = (size_t)(d->inter > d->shared_inter ? d->inter : d->shared_inter);
   L.act = take(pairs * ia * 4);
-  // partial outputs: batched SwiGLU [pairs][H]; linear experts at larger batches [B*k][I]
+  // partial outputs: batched SwiGLU [kDownRowSlices][pairs][H]; linear experts at larger
+  // batches [B*k][I]
   const size_t lin_part = d->kind == MOE_EXPERT_LINEAR && B >= kLinearTiledMinBatch
                               ? B * k * (size_t)d->inter * 4
                               : 0;
-  const size_t sw_part = pairs * (size_t)d->hidden * 4;
+  const size_t sw_part = kDownRowSlices * pairs * (size_t)d->hidden * 4;
   L.part = take(lin_part > sw_part ? lin_part : sw_part);
   L.total = o;
   return L;
@@ -428,6 +429,7 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     a.k = d.top_k;
     a.B = B;
     a.NS = d.n_shared;
+    a.pairs = B * d.top_k + d.n_shared * B;
     a.slots_max = B * d.top_k < d.n_experts ? B * d.top_k : d.n_experts;
     if (e == hipSuccess)
       e = launch_union(rid, B, d.top_k, d.n_experts, layer->at<int32_t>(layer->L.union_n),
