@@ -472,6 +472,291 @@ __device__ __forceinline__ void gu_pass_res(const uint8_t* G, const uint8_t* V,
   gu_epilogue<1>(acc, rows, rbase, l16, g, tok_slot, tok_w, np, act, IA);
 }
 
+// ------------------------------------------------------------------------------------
+// Gate/up with the weights streamed into LDS (buckets of <= kGuSmall tokens)
+//
+// Loads in the MFMA operand layout touch 16 rows x 64 B per instruction, and the line
+// lookups, not the bytes, then bound the stream (about 5 TB/s on this part).  Here each wave
+// copies its 64 rows (32 of G, 32 of V) of a step straight into LDS with line-complete
+// 16-byte direct loads (8 rows x 128 B per instruction, about 6.3 TB/s), then reads the
+// MFMA fragments back from LDS.  A step is 128 bytes of every row for both formats (64 bf16
+// or 256 MXFP4 elements), so the same copy and read-back serve both.  The ring lives in LDS
+// (kGlDA steps per wave), not in registers; its waits are explicit load-counter waits whose
+// counts follow the issue order, which is pinned.
+// ------------------------------------------------------------------------------------
+constexpr int kGlDA = 2;                                  // steps in flight per wave
+constexpr int kGlSlot = 64 * 128;                         // one step of a wave's 64 rows
+constexpr int kGlScale = 64 * 16;                         // scale blocks of a step pair
+constexpr int kGlWave = kGlDA * kGlSlot;                  // a wave's weight ring
+constexpr int kGlRing = kGuWaves * kGlWave;               // static LDS of the rings
+constexpr int kGlScales = kGuWaves * 2 * kGlScale;        // static LDS of the scale slots
+
+// s_waitcnt with vmcnt = N (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left at their no-wait values).
+template <int N>
+__device__ __forceinline__ void gl_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+}
+
+// The same for a count known once the loop around it is unrolled.  n >= 63 needs no wait:
+// a wave holds at most 63 loads in flight (the counter's width), so a copy followed by 63
+// or more has landed.
+template <int N>
+__device__ __forceinline__ void gl_wait_upto(int n) {
+  if (n == N) {
+    gl_wait_vm<N>();
+  } else if constexpr (N > 0) {
+    gl_wait_upto<N - 1>(n);
+  }
+}
+__device__ __forceinline__ void gl_wait_n(int n) { gl_wait_upto<63>(n); }
+
+// Direct copies of step st into a ring slot: instruction i holds rows 8i .. 8i+7 of the
+// wave's 64 (matrix i / 4, tile (i / 2) % 2, half i % 2); lane l takes row l / 8 and the
+// 16-byte chunk (l % 8) ^ (l / 8), so that lane l of the instruction lands at 16 l and the
+// read-back of 16 rows at a 128-byte pitch spreads over all banks.
+//
+// The copies are issued from asm: the compiler then does not track them, and adds no wait
+// for all copies before every later LDS access (it cannot tell the ring, the scale slots and
+// the x buffers apart).  Their completion is awaited explicitly (gl_wait_vm); VMEM operations
+// it does not see only make its own load-counter waits stricter, as the counter completes
+// in order.  M0 carries the LDS address; nothing else in these kernels uses M0.
+__device__ __forceinline__ void gl_copy16(const lds_u8* dst, const uint8_t* src) {
+  const uint32_t la = (uint32_t)(uintptr_t)dst;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(la), "v"(src)
+               : "memory");
+}
+
+__device__ __forceinline__ void gl_issue(lds_u8* slot, const uint8_t* G, const uint8_t* V,
+                                         const uint32_t (&off)[2][2], int st) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    gl_copy16(slot + 1024 * i, (i >> 2 ? V : G) + off[(i >> 1) & 1][i & 1] + (size_t)st * 128);
+}
+
+// Scale blocks of an even step (MXFP4), copied like the codes: lane l takes row l of the
+// wave's 64 (matrix l / 32, tile (l / 16) % 2, row l % 16 of the tile) and its 16 scale
+// bytes of the step pair, landing at 16 l of the scale slot.
+__device__ __forceinline__ void gl_issue_scales(lds_u8* sslot, const uint8_t* src) {
+  gl_copy16(sslot, src);
+}
+
+// Fragments of a ring slot: tile (m, r) is rows 16 (2m + r) .. +15 of the slot; piece x of
+// lane (l16, g) is chunk 4x + g of row l16 (bf16: sub-step x; MXFP4: piece x), at ro[x].
+template <DT dt>
+__device__ __forceinline__ void gl_frags(GuRing<dt>& ar, const lds_u8* slot,
+                                         const uint32_t (&ro)[2]) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const lds_u8* tp = slot + 2048 * (2 * m + r);
+      if constexpr (dt == DT::MXFP4) {
+        ar.r[m][r].q[0] = lds_ld128(tp + ro[0]);
+        ar.r[m][r].q[1] = lds_ld128(tp + ro[1]);
+      } else {
+        ar.r[m][r].f[0] = lds_ld128(tp + ro[0]);
+        ar.r[m][r].f[1] = lds_ld128(tp + ro[1]);
+      }
+    }
+}
+
+// x chunk c of 16 token rows (hi and lo) copied into LDS buffer (xs_h, xs_l): each token
+// row of the chunk is 512 bf16 = one copy instruction; wave w copies tokens 4w .. 4w+3.
+// Pieces past H copy the row's last piece (never used); token rows past np copy token 0.
+__device__ __forceinline__ void gl_x_chunk(lds_u16* xs_h, lds_u16* xs_l, const uint16_t* const (&xrh)[4],
+                                           const uint16_t* const (&xrl)[4], int H, int kc,
+                                           int wv, int lane) {
+  int k = kc + 8 * lane;
+  k = k < H ? k : H - 8;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int tok = 4 * wv + t;
+    gl_copy16((const lds_u8*)(xs_h + tok * gu_ldx<1>()), (const uint8_t*)(xrh[t] + k));
+    gl_copy16((const lds_u8*)(xs_l + tok * gu_ldx<1>()), (const uint8_t*)(xrl[t] + k));
+  }
+}
+
+// One pass of one wave's 32 channels for np <= 16 tokens, weights through LDS.  RES: the
+// whole x of the tokens is in LDS (staged once); else x goes in 512-element chunks copied
+// into LDS one chunk ahead.  Per step, the wave issues (in this order) the x chunk copies
+// (8, first step of a chunk), then after using the step, the step pair's scale copy
+// (MXFP4, even steps) and the 8 weight copies of the step DA ahead.
+template <DT dt, bool RES>
+__device__ __forceinline__ void gu_pass_lds(const uint8_t* G, const uint8_t* V,
+                                            const uint8_t* Gs, const uint8_t* Vs, int H,
+                                            int rows, int rbase, const uint16_t* xh,
+                                            const uint16_t* xl, const lds_i32* tok_b,
+                                            const lds_i32* tok_slot, const lds_f32* tok_w,
+                                            int np, lds_u16* __restrict__ xs,
+                                            lds_u8* __restrict__ ring,
+                                            lds_u8* __restrict__ scl, float* act, int IA) {
+  using F = Gu<dt>;
+  constexpr bool MX = dt == DT::MXFP4;
+  constexpr int DA = kGlDA;
+  constexpr int KX = gu_kx<1>();
+  static_assert(KX == 512, "a chunk row is one 1 KB copy");
+  constexpr int SPC = RES ? 1 : KX / F::STEP;            // steps per x chunk
+  // steps per unrolled group: whole x chunks and ring turns, and for MXFP4 two step pairs,
+  // so that every slot index is a compile-time constant
+  constexpr int GRP = gu_lcm(gu_lcm(SPC, DA), MX ? 4 : 1);
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  lds_u8* wring = ring + wv * kGlWave;
+  const GuRows<dt> R = gu_rows<dt>(G, V, Gs, Vs, H, rows, rbase, l16, g);
+  const size_t rb = F::row_bytes(H);
+  uint32_t off[2][2];
+  {
+    const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int row = rbase + 16 * r + 8 * h + lr;
+        row = row < rows ? row : rows - 1;  // rows past the end give values that are dropped
+        off[r][h] = (uint32_t)(row * rb) + 16 * lc;
+      }
+  }
+  uint32_t ro[2];
+  {
+    const int r8 = l16 & 7, hi = l16 >> 3;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) ro[x] = 1024 * hi + 16 * (8 * r8 + ((4 * x + g) ^ r8));
+  }
+  // scale copy of this lane (MXFP4): row lane % 16 of tile (lane / 16) % 2 of matrix
+  // lane / 32; rows clamp like the codes'
+  const uint8_t* ssrc = nullptr;
+  if constexpr (MX) {
+    int row = rbase + 16 * ((lane >> 4) & 1) + (lane & 15);
+    row = row < rows ? row : rows - 1;
+    ssrc = (lane >> 5 ? Vs : Gs) + (size_t)row * (H / 32);
+  }
+  lds_u8* sring = scl + wv * 2 * kGlScale;  // two scale slots, by step pair parity
+  // x buffers
+  int xo[1];
+  lds_u16* xs_h[2];
+  lds_u16* xs_l[2];
+  const uint16_t* xrh[4];  // token rows this wave copies (chunked x)
+  const uint16_t* xrl[4];
+  if constexpr (RES) {
+    const int ldr = H + kGuPad;
+    xs_h[0] = xs_h[1] = xs;
+    xs_l[0] = xs_l[1] = xs + np * ldr;
+    xo[0] = (l16 < np ? l16 : 0) * ldr;
+  } else {
+    xs_h[0] = xs; xs_h[1] = xs + 2 * kGuBuf;
+    xs_l[0] = xs + kGuBuf; xs_l[1] = xs + 3 * kGuBuf;
+    xo[0] = l16 * gu_ldx<1>();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = 4 * wv + t;
+      const size_t b = (size_t)tok_b[tok < np ? tok : 0] * H;
+      xrh[t] = xh + b;
+      xrl[t] = xl + b;
+    }
+  }
+  f32x4 acc[2][2][1];
+  gu_acc_zero<1>(acc);
+  const int nfull = RES ? H / F::STEP : (H / KX) * SPC;
+  const int ngrp = gu_wide_ok<dt>(H) ? nfull / GRP * GRP : 0;
+  // x: staged whole (RES), or the first chunk copied
+  if constexpr (RES) {
+    const int pr = H / 8;  // 16-byte pieces per x row
+    for (int p = threadIdx.x; p < np * pr; p += kGuWaves * 64) {
+      const int tok = p / pr, q = p - tok * pr;
+      const size_t o = (size_t)tok_b[tok] * H + 8 * q;
+      lds_st128(xs_h[0] + tok * (H + kGuPad) + 8 * q, *reinterpret_cast<const u32x4*>(xh + o));
+      lds_st128(xs_l[0] + tok * (H + kGuPad) + 8 * q, *reinterpret_cast<const u32x4*>(xl + o));
+    }
+  } else {
+    gl_x_chunk(xs_h[0], xs_l[0], xrh, xrl, H, 0, wv, lane);
+  }
+  if (ngrp > 0) {
+    if constexpr (MX) gl_issue_scales(sring, ssrc);  // step pair 0
+#pragma unroll
+    for (int d = 0; d < DA; ++d) gl_issue(wring + d * kGlSlot, G, V, off, d);
+  }
+  gl_wait_vm<0>();  // x chunk 0 (and the first copies) landed
+  __syncthreads();
+  for (int base = 0; base < ngrp; base += GRP) {
+#pragma unroll
+    for (int u = 0; u < GRP; ++u) {
+      const int st = base + u;
+      const int c = RES ? 0 : st / SPC;
+      const bool first = !RES && u % SPC == 0;
+      const bool last = !RES && u % SPC == SPC - 1;
+      // the next chunk's x (past the end of K: the last pieces again, into the buffer that
+      // is not read any more)
+      if (first) gl_x_chunk(xs_h[(c + 1) & 1], xs_l[(c + 1) & 1], xrh, xrl, H, (c + 1) * KX, wv, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      // this step's copies have landed once at most this many later copies are in flight:
+      // the next step's weights (and its scales if it is even), and the x chunk copies of
+      // the previous step and of this one
+      {
+        const bool first_prev = !RES && (u + GRP - 1) % GRP % SPC == 0;
+        gl_wait_n(8 + (MX && u % 2 == 1 ? 1 : 0) + (first_prev ? 8 : 0) + (first ? 8 : 0));
+      }
+      GuRing<dt> ar;
+      gl_frags<dt>(ar, wring + (u % DA) * kGlSlot, ro);
+      if constexpr (MX) {
+        // the step pair's scale block of each of the lane's rows; the odd step takes dwords 2, 3
+        const lds_u8* sp = sring + ((u >> 1) & 1) * kGlScale + 16 * l16;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const u32x4 b = lds_ld128(sp + 16 * (32 * m + 16 * r));
+            ar.r[m][r].s = u % 2 == 0 ? b : u32x4{b.z, b.w, 0, 0};
+          }
+      }
+      gu_step<dt, 1>(ar, xs_h[c & 1], xs_l[c & 1], xo, RES ? st * F::STEP : (u % SPC) * F::STEP,
+                     g, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      const int sn = st + DA < ngrp ? st + DA : st;  // spare refills copy this step again
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's reads are done
+      if constexpr (MX)  // sn has the parity of st; its pair's slot is not the one in use
+        if (u % 2 == 0)
+          gl_issue_scales(sring + (((u + DA) >> 1) & 1) * kGlScale, ssrc + sn * F::STEP / 32);
+      gl_issue(wring + (u % DA) * kGlSlot, G, V, off, sn);
+      __builtin_amdgcn_sched_barrier(0);
+      if (last) {
+        // the next chunk's copies (issued at this chunk's first step) have landed once at
+        // most the copies issued after them are in flight: per step of the chunk, the
+        // weights (8) and the scales of its even steps
+        int after = 0;
+#pragma unroll
+        for (int v = u - SPC + 1; v <= u; ++v) after += 8 + (MX && v % 2 == 0 ? 1 : 0);
+        gl_wait_n(after);
+        __syncthreads();
+      }
+    }
+  }
+  gl_wait_vm<0>();  // every copy has landed (none may outlive the workgroup)
+  __syncthreads();
+  // the rest of K: masked steps with fragments in registers
+  for (int st = ngrp; st * F::STEP < H; ++st) {
+    const int c = RES ? 0 : st / SPC;
+    const int k = st * F::STEP;
+    if (!RES && st > ngrp && st % SPC == 0) {
+      __syncthreads();
+      GuX xr;
+      gu_x_load<1>(xr, xh, xl, H, tok_b, np, c * KX);
+      gu_x_store<1>(xr, xs_h[c & 1], xs_l[c & 1]);
+      __syncthreads();
+    }
+    GuRing<dt> ar;
+    gu_a_load_masked<dt>(ar, R, H, k, g);
+    if constexpr (RES)
+      gu_step<dt, 1, true>(ar, xs_h[0], xs_l[0], xo, k, g, acc, H - 8);
+    else
+      gu_step<dt, 1>(ar, xs_h[c & 1], xs_l[c & 1], xo, k - c * KX, g, acc);
+  }
+  gu_epilogue<1>(acc, rows, rbase, l16, g, tok_slot, tok_w, np, act, IA);
+}
+
 // Token bucket of work item t: the shared experts first (t < NS, every token of the batch;
 // their workgroups read the most and are dispatched first), then the routed expert slots
 // (the union's buckets; slots past n_touched are empty).
@@ -532,9 +817,10 @@ constexpr int kGuDALarge = 2;
 static_assert(gu_da_small<DT::MXFP4>() % 2 == 0 && kGuDALarge % 2 == 0,
               "MXFP4 rings pair even and odd steps (their scales are read together)");
 
-template <DT et, DT st, bool SMALL>
+template <DT et, DT st, bool SMALL, bool LDSW = false>
 __device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i32* tok_b,
-                                            lds_i32* tok_slot, lds_f32* tok_w) {
+                                            lds_i32* tok_slot, lds_f32* tok_w,
+                                            lds_u8* ring = nullptr, lds_u8* scl = nullptr) {
   const Bucket bk = bucket_of(a, blockIdx.y);
   const int rows = bk.shared ? a.IS : a.I;
   if (bk.count == 0 || (bk.count <= kGuSmall) != SMALL || blockIdx.x * kGuRows >= rows)
@@ -552,7 +838,25 @@ __device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i3
     if (a.gate_s) Gs = a.gate_s + off * (a.H / 32);
     if (a.up_s) Vs = a.up_s + off * (a.H / 32);
   }
-  if constexpr (SMALL) {
+  if constexpr (SMALL && LDSW) {
+    fill_tokens(a, bk, 0, bk.count, tok_b, tok_slot, tok_w);
+    __syncthreads();
+    if (bk.shared) {
+      if (gu_res_bytes(bk.count, a.H) <= kGuLds)
+        gu_pass_lds<st, true>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b,
+                              tok_slot, tok_w, bk.count, xs, ring, scl, a.act, a.IA);
+      else
+        gu_pass_lds<st, false>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl, tok_b,
+                               tok_slot, tok_w, bk.count, xs, ring, scl, a.act, a.IA);
+    } else {
+      if (gu_res_bytes(bk.count, a.H) <= kGuLds)
+        gu_pass_lds<et, true>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
+                              tok_w, bk.count, xs, ring, scl, a.act, a.IA);
+      else
+        gu_pass_lds<et, false>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
+                               tok_w, bk.count, xs, ring, scl, a.act, a.IA);
+    }
+  } else if constexpr (SMALL) {
     fill_tokens(a, bk, 0, bk.count, tok_b, tok_slot, tok_w);
     __syncthreads();
     // MXFP4 buckets whose whole x fits in LDS skip the chunked staging (measured: faster for
@@ -612,6 +916,20 @@ void bs_gateup_small_kernel(BsArgs a) {
   __shared__ float tok_w[kGuTok];
   gateup_body<et, st, true>(a, (lds_u16*)smem, (lds_i32*)tok_b, (lds_i32*)tok_slot,
                             (lds_f32*)tok_w);
+}
+
+// Buckets of <= kGuSmall tokens with the weights streamed through LDS (one workgroup per
+// CU: the x buffers in dynamic LDS and the weight ring in static LDS).
+template <DT et, DT st>
+__global__ __launch_bounds__(kGuWaves * 64) void bs_gateup_lds_kernel(BsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kGlRing];
+  __shared__ __attribute__((aligned(1024))) unsigned char scl[kGlScales];
+  __shared__ int tok_b[kGuTok];
+  __shared__ int tok_slot[kGuTok];
+  __shared__ float tok_w[kGuTok];
+  gateup_body<et, st, true, true>(a, (lds_u16*)smem, (lds_i32*)tok_b, (lds_i32*)tok_slot,
+                                  (lds_f32*)tok_w, (lds_u8*)ring, (lds_u8*)scl);
 }
 
 template <DT et, DT st>
@@ -862,7 +1180,7 @@ hipError_t launch_bs_typed(const BsArgs& a, hipStream_t s) {
   static bool lds_set = false;
   if (!lds_set) {
     hipError_t e0 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(bs_gateup_small_kernel<et, st>),
+        reinterpret_cast<const void*>(bs_gateup_lds_kernel<et, st>),
         hipFuncAttributeMaxDynamicSharedMemorySize, gu_lds);
     if (e0 == hipSuccess)
       e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(bs_gateup_large_kernel<et, st>),
@@ -871,7 +1189,7 @@ hipError_t launch_bs_typed(const BsArgs& a, hipStream_t s) {
     lds_set = true;
   }
   const dim3 gu_grid((rows + kGuRows - 1) / kGuRows, items);
-  hipLaunchKernelGGL((bs_gateup_small_kernel<et, st>), gu_grid, dim3(kGuWaves * 64), gu_lds, s,
+  hipLaunchKernelGGL((bs_gateup_lds_kernel<et, st>), gu_grid, dim3(kGuWaves * 64), gu_lds, s,
                      a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

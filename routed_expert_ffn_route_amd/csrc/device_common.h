@@ -19,11 +19,15 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) int lds_i32;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 __device__ __forceinline__ u32x4 lds_ld128(const lds_u16* p) {
   return *reinterpret_cast<const lds_u32x4*>(p);
 }
 __device__ __forceinline__ void lds_st128(lds_u16* p, const u32x4& v) {
   *reinterpret_cast<lds_u32x4*>(p) = v;
+}
+__device__ __forceinline__ u32x4 lds_ld128(const lds_u8* p) {
+  return *reinterpret_cast<const lds_u32x4*>(p);
 }
 
 // MXFP4W is MXFP4 read in 16-element chunks (8 bytes of codes + the block's scale byte per
