@@ -67,6 +67,11 @@ __device__ inline int block_excl_scan(int v, int* sh, const Ctx& c, int* total) 
 // count from the top reaches the remaining need.  Requires 0 < K < n.  `hist` is LDS of
 // kSelBins ints, `sh` of 48 ints.
 constexpr int kSelBins = 2048;
+// LDS of the histogram: the binned selection keeps one padding int after every 32 bins
+// (bin b at b + b / 32), so that a wave reading 32 consecutive bins per lane spreads over
+// the banks
+constexpr int kSelHist = kSelBins + kSelBins / 32;
+__device__ __forceinline__ int sel_slot(int b) { return b + (b >> 5); }
 __device__ inline uint32_t select_threshold(const uint32_t* u, int n, int K, int* need_out,
                                             int* hist, int* sh, const Ctx& c) {
   uint32_t prefix = 0, mask = 0;
@@ -112,6 +117,92 @@ __device__ inline uint32_t select_threshold(const uint32_t* u, int n, int K, int
   return prefix;
 }
 
+// The same threshold in one histogram pass where it can be done (returns false otherwise,
+// and the caller runs select_threshold).  The radix digits above pile most scores into a
+// few bins (the leading bits are sign and exponent), and LDS atomics on one bin serialize.
+// Here the bins split [lo, hi] of the patterns evenly instead: bin(v) =
+// floor((v - lo) * 2048 / (hi - lo + 1)) in float, which is monotone in v, so the K-th
+// largest lies in the bin where the count from the top reaches K.  The values of that bin
+// (at most kSelCand) are then ranked by brute force: T is the one with fewer than `need`
+// values above it and at least `need` at or above it.  Returns false when all values are
+// equal or that bin holds more than kSelCand values.  lo and hi come in per wave in
+// sh[4 + w] and sh[20 + w], and `hist` (kSelHist ints) comes in cleared (both done while
+// the scores arrive); wave 0 alone finds the bin, so the whole selection takes four
+// barriers.
+constexpr int kSelCand = 256;
+__device__ inline bool select_threshold_binned(const uint32_t* u, int n, int K, uint32_t* T_out,
+                                               int* need_out, int* hist, int* sh,
+                                               const Ctx& c) {
+  const int lane = c.lane, wave = c.tid >> 6, nw = c.nthreads >> 6;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int w = 0; w < nw; ++w) {
+    const uint32_t ol = (uint32_t)sh[4 + w], oh = (uint32_t)sh[20 + w];
+    lo = ol < lo ? ol : lo;
+    hi = oh > hi ? oh : hi;
+  }
+  if (hi == lo) return false;  // uniform: every thread read the same words
+  const float inv = (float)kSelBins / ((float)(hi - lo) + 1.0f);
+  auto bin = [&](uint32_t v) {
+    const int b = (int)((float)(v - lo) * inv);
+    return b < kSelBins - 1 ? b : kSelBins - 1;
+  };
+  for (int f = c.tid; f < n; f += c.nthreads) atomicAdd(&hist[sel_slot(bin(u[f]))], 1);
+  __syncthreads();
+  if (wave == 0) {
+    // lane l counts bins kSelBins - 1 - PB l - i, i < PB, from the top
+    // (the counts stay in registers: all reads are issued at once, none waits on another)
+    constexpr int PB = kSelBins / kWave;
+    int cnt[PB];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      cnt[i] = hist[sel_slot(kSelBins - 1 - PB * lane - i)];
+      local += cnt[i];
+    }
+    const int incl = wave_incl_scan(local);
+    int before = incl - local;
+    if (before < K && K <= incl) {
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        if (before < K && K <= before + cnt[i]) {
+          sh[40] = kSelBins - 1 - PB * lane - i;
+          sh[41] = K - before;  // the rank wanted within the bin
+          sh[42] = cnt[i];
+        }
+        before += cnt[i];
+      }
+    }
+    if (lane == 0) sh[44] = 0;
+  }
+  __syncthreads();
+  const int bstar = sh[40], needb = sh[41], m = sh[42];
+  if (m > kSelCand) return false;
+  // the bin's values (hist is free now; its counts were read before the barrier), then
+  // their ranks
+  for (int f = c.tid; f < n; f += c.nthreads) {
+    const uint32_t v = u[f];
+    if (bin(v) == bstar) hist[atomicAdd(&sh[44], 1)] = (int)v;
+  }
+  __syncthreads();
+  if (c.tid < m) {
+    const uint32_t key = (uint32_t)hist[c.tid];
+    int gt = 0, ge = 0;
+    for (int j = 0; j < m; ++j) {
+      const uint32_t o = (uint32_t)hist[j];
+      gt += o > key ? 1 : 0;
+      ge += o >= key ? 1 : 0;
+    }
+    if (gt < needb && needb <= ge) {  // the needb-th largest of the bin (equal keys agree)
+      sh[45] = (int)key;
+      sh[46] = needb - gt;
+    }
+  }
+  __syncthreads();
+  *T_out = (uint32_t)sh[45];
+  *need_out = sh[46];
+  return true;
+}
+
 // Counts, over u[0 .. m), of the values above T and of those equal to T (whole workgroup;
 // sh: LDS of 48 ints).
 __device__ inline void count_before(const uint32_t* u, int m, uint32_t T, int* gt, int* eq,
@@ -121,6 +212,13 @@ __device__ inline void count_before(const uint32_t* u, int m, uint32_t T, int* g
     const uint32_t v = u[f];
     a += v > T ? 1 : 0;
     b += v == T ? 1 : 0;
+  }
+  if (m < 32768) {  // both counts in one scan: a in the upper, b in the lower 16 bits
+    int t;
+    block_excl_scan(a * 65536 + b, sh + 2, c, &t);
+    *gt = t >> 16;
+    *eq = t & 0xFFFF;
+    return;
   }
   int ta, tb;
   block_excl_scan(a, sh + 2, c, &ta);
@@ -153,8 +251,8 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
   float* s_w = reinterpret_cast<float*>(s_ids + 64);                // [64]
-  int* hist = reinterpret_cast<int*>(s_w + 64);                     // [kSelBins]
-  int* sh = hist + kSelBins;                                        // [48]
+  int* hist = reinterpret_cast<int*>(s_w + 64);                     // [kSelHist]
+  int* sh = hist + kSelHist;                                        // [48]
   float* big = reinterpret_cast<float*>(sh + 48);
   Ctrl* ctrl = a.ctrl;
   const int I = a.I;
@@ -266,8 +364,29 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
 
   // 3. every workgroup gathers all k*I scores (each published with its launch tag, so
   // waiting on the scores themselves is the grid-wide hand-off)
-  for (int f = c.tid; f < n; f += c.nthreads)
-    sbits[f] = (uint32_t)wait_tagged(L.s_ws + f, c.epoch + 1u, &ctrl->err, kErrPhaseWait);
+  // (meanwhile the range of the scores per wave and a cleared histogram for the selection)
+  {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int f = c.tid; f < n; f += c.nthreads) {
+      const uint32_t v =
+          (uint32_t)wait_tagged(L.s_ws + f, c.epoch + 1u, &ctrl->err, kErrPhaseWait);
+      sbits[f] = v;
+      lo = v < lo ? v : lo;
+      hi = v > hi ? v : hi;
+    }
+    for (int i = c.tid; i < kSelHist; i += c.nthreads) hist[i] = 0;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const uint32_t ol = (uint32_t)__shfl_xor((int)lo, m);
+      const uint32_t oh = (uint32_t)__shfl_xor((int)hi, m);
+      lo = ol < lo ? ol : lo;
+      hi = oh > hi ? oh : hi;
+    }
+    if (c.lane == 0) {
+      sh[4 + (c.tid >> 6)] = (int)lo;
+      sh[20 + (c.tid >> 6)] = (int)hi;
+    }
+  }
   __syncthreads();
 
   // 4. the same threshold in every workgroup; each keeps the channels of its own share:
@@ -279,19 +398,28 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
     kept_before = g0;
   } else if (L.K > 0) {
     int need;
-    const uint32_t T = select_threshold(sbits, n, L.K, &need, hist, sh, c);
+    uint32_t T;
+    if (!select_threshold_binned(sbits, n, L.K, &T, &need, hist, sh, c))
+      T = select_threshold(sbits, n, L.K, &need, hist, sh, c);
     int gt, eq;
     count_before(sbits, g0, T, &gt, &eq, sh, c);
     kept_before = gt + min(eq, need);
-    if (c.tid == 0) {
-      int r = eq;
-      for (int f = g0; f < g1; ++f) {
-        const uint32_t v = sbits[f];
-        const bool take = v > T || (v == T && r < need);
-        r += v == T ? 1 : 0;
-        if (take) loc[nk++] = f;
+    if ((c.tid >> 6) == 0) {  // wave 0: 64 candidates of the share at a time
+      const uint64_t below = (1ull << c.lane) - 1ull;
+      int r = eq, pos = 0;  // T-valued candidates before, kept so far
+      for (int base = g0; base < g1; base += kWave) {
+        const int f = base + c.lane;
+        const bool in = f < g1;
+        const uint32_t v = in ? sbits[f] : 0u;
+        const bool isT = in && v == T;
+        const uint64_t mT = __ballot(isT);
+        const bool take = in && (v > T || (isT && r + __popcll(mT & below) < need));
+        const uint64_t mk = __ballot(take);
+        if (take) loc[pos + __popcll(mk & below)] = f;
+        pos += __popcll(mk);
+        r += __popcll(mT);
       }
-      sh[0] = nk;
+      if (c.lane == 0) sh[0] = pos;
     }
     __syncthreads();
     nk = sh[0];
@@ -346,7 +474,7 @@ hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStrea
 
 int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs) {
   const int nteams = threads / team_size(H);
-  const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + kSelBins + 48) * 4;
+  const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + kSelHist + 48) * 4;
   const int n = k * I;
   const int share = (n + wgs - 1) / wgs;
   const int sel = (n + 3 * share) * 4;  // all scores; this share's gate values, kept ids, scores
