@@ -24,6 +24,7 @@
 // MXFP4 rows: LC = 32 (one 16-byte load of codes = exactly one scale block), decoded to
 // bf16 in registers (e2m1 times a power of two is exact in bf16).
 #include "kernels.h"
+#include "lds_copy.h"
 
 namespace moe {
 namespace {
@@ -491,45 +492,10 @@ constexpr int kGlWave = kGlDA * kGlSlot;                  // a wave's weight rin
 constexpr int kGlRing = kGuWaves * kGlWave;               // static LDS of the rings
 constexpr int kGlScales = kGuWaves * 2 * kGlScale;        // static LDS of the scale slots
 
-// s_waitcnt with vmcnt = N (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
-// lgkmcnt left at their no-wait values).
-template <int N>
-__device__ __forceinline__ void gl_wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
-}
-
-// The same for a count known once the loop around it is unrolled.  n >= 63 needs no wait:
-// a wave holds at most 63 loads in flight (the counter's width), so a copy followed by 63
-// or more has landed.
-template <int N>
-__device__ __forceinline__ void gl_wait_upto(int n) {
-  if (n == N) {
-    gl_wait_vm<N>();
-  } else if constexpr (N > 0) {
-    gl_wait_upto<N - 1>(n);
-  }
-}
-__device__ __forceinline__ void gl_wait_n(int n) { gl_wait_upto<63>(n); }
-
 // Direct copies of step st into a ring slot: instruction i holds rows 8i .. 8i+7 of the
 // wave's 64 (matrix i / 4, tile (i / 2) % 2, half i % 2); lane l takes row l / 8 and the
 // 16-byte chunk (l % 8) ^ (l / 8), so that lane l of the instruction lands at 16 l and the
 // read-back of 16 rows at a 128-byte pitch spreads over all banks.
-//
-// The copies are issued from asm: the compiler then does not track them, and adds no wait
-// for all copies before every later LDS access (it cannot tell the ring, the scale slots and
-// the x buffers apart).  Their completion is awaited explicitly (gl_wait_vm); VMEM operations
-// it does not see only make its own load-counter waits stricter, as the counter completes
-// in order.  M0 carries the LDS address; nothing else in these kernels uses M0.
-__device__ __forceinline__ void gl_copy16(const lds_u8* dst, const uint8_t* src) {
-  const uint32_t la = (uint32_t)(uintptr_t)dst;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(la), "v"(src)
-               : "memory");
-}
-
 __device__ __forceinline__ void gl_issue(lds_u8* slot, const uint8_t* G, const uint8_t* V,
                                          const uint32_t (&off)[2][2], int st) {
 #pragma unroll
@@ -716,7 +682,7 @@ __device__ __forceinline__ void gu_pass_lds(const uint8_t* G, const uint8_t* V,
                      g, acc);
       __builtin_amdgcn_sched_barrier(0);
       const int sn = st + DA < ngrp ? st + DA : st;  // spare refills copy this step again
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's reads are done
+      gl_wait_lds();  // the slot's reads are done
       if constexpr (MX)  // sn has the parity of st; its pair's slot is not the one in use
         if (u % 2 == 0)
           gl_issue_scales(sring + (((u + DA) >> 1) & 1) * kGlScale, ssrc + sn * F::STEP / 32);
