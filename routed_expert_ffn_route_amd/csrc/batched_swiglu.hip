@@ -5,7 +5,7 @@
 // reads are shared, not skipped ("501B of which 23B are switched on", section 3[B]); the
 // expert FFN itself is the gated one of the "Routed experts" section of the arXiv
 // 2610.37386 review.  After routing and the union, three launches:
-//   1. gate/up  (MFMA): for every (touched or shared expert, block of 256 channels), the
+//   1. gate/up  (MFMA): for every (touched or shared expert, block of 128 channels), the
 //      products g = G x and u = V x for the expert's tokens, then a = w * silu(g) * u with
 //      w the router weight of that token's choice (1 for a shared expert);
 //   2. down (VALU): for every (expert, block of output columns), one partial output
@@ -17,12 +17,13 @@
 // Gate/up on MFMA (v_mfma_f32_16x16x32_bf16; lane l holds A[l%16][8*(l/16)..+8],
 // B[8*(l/16)..+8][l%16], D[4*(l/16)..+4][l%16]).  A is 16 channel rows, B is 16 tokens.
 // x enters as bf16 hi + lo (two MFMAs per product, ~16 significant bits).  The K order
-// inside a step is permuted so each lane loads one contiguous piece of its row: a step
-// spans 4*LC elements and lane group g = l/16 owns [kb + LC*g, kb + LC*g + LC); MFMA number
-// c of the step takes its 8-element slice c from A and B alike (a permutation of K applied
-// to both operands leaves the product unchanged).  bf16 rows: LC = 8 (one 16-byte load);
-// MXFP4 rows: LC = 32 (one 16-byte load of codes = exactly one scale block), decoded to
-// bf16 in registers (e2m1 times a power of two is exact in bf16).
+// inside a step is permuted (the same permutation for A and B leaves the product
+// unchanged) so that each lane's operand pieces are whole 16-byte pieces of its row: bf16
+// steps of 64 elements (lane group g: elements 32c + 8g .. +8 of sub-step c), MXFP4 steps of
+// 256 elements (lane group g: elements 32g .. +32 and 128 + 32g .. +32, one scale block
+// each), decoded to bf16 in registers (e2m1 times a power of two is exact in bf16).
+// Buckets of up to 16 tokens stream the weights into LDS with line-complete direct copies
+// and read the fragments back from there; larger buckets load them into a register ring.
 #include "kernels.h"
 #include "lds_copy.h"
 
@@ -410,69 +411,6 @@ __device__ __forceinline__ void gu_pass(const uint8_t* G, const uint8_t* V, cons
 
 // LDS bytes of x held whole for np tokens (hi and lo rows of H + kGuPad bf16).
 __host__ __device__ constexpr int gu_res_bytes(int np, int H) { return np * (H + kGuPad) * 4; }
-template <DT dt>
-__device__ __forceinline__ bool gu_use_res(int np, int H) {
-  return dt == DT::MXFP4 && gu_res_bytes(np, H) <= kGuLds;
-}
-
-// One pass of one wave's 32 channels for np <= 16 tokens whose whole x is held in LDS
-// (staged once): the loop only streams weights, with no barrier and no x loads in it.
-// Token columns past np read the first token's x; their results are dropped.
-template <DT dt, int DA>
-__device__ __forceinline__ void gu_pass_res(const uint8_t* G, const uint8_t* V,
-                                            const uint8_t* Gs, const uint8_t* Vs, int H,
-                                            int rows, int rbase, const uint16_t* xh,
-                                            const uint16_t* xl, const lds_i32* tok_b,
-                                            const lds_i32* tok_slot, const lds_f32* tok_w,
-                                            int np, lds_u16* xs, float* act, int IA) {
-  using F = Gu<dt>;
-  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
-  const GuRows<dt> R = gu_rows<dt>(G, V, Gs, Vs, H, rows, rbase, l16, g);
-  const int ldr = H + kGuPad;
-  lds_u16* xs_h = xs;
-  lds_u16* xs_l = xs + np * ldr;
-  const int nfull = H / F::STEP;
-  // steps run by the pipelined loop (none without the wide scale loads)
-  const int ngrp = gu_wide_ok<dt>(H) ? nfull / DA * DA : 0;
-  GuRing<dt> ring[DA];
-  if (ngrp > 0) {
-#pragma unroll
-    for (int d = 0; d < DA; ++d)
-      gu_a_load<dt>(ring[d], R.rp, R.sp, d * F::STEP, g, d % 2 == 0);
-  }
-  const int pr = H / 8;  // 16-byte pieces per x row
-  for (int p = threadIdx.x; p < np * pr; p += kGuWaves * 64) {
-    const int tok = p / pr, q = p - tok * pr;
-    const size_t off = (size_t)tok_b[tok] * H + 8 * q;
-    lds_st128(xs_h + tok * ldr + 8 * q, *reinterpret_cast<const u32x4*>(xh + off));
-    lds_st128(xs_l + tok * ldr + 8 * q, *reinterpret_cast<const u32x4*>(xl + off));
-  }
-  __syncthreads();
-  const int xo[1] = {(l16 < np ? l16 : 0) * ldr};
-  f32x4 acc[2][2][1];
-  gu_acc_zero<1>(acc);
-  for (int base = 0; base < ngrp; base += DA) {
-#pragma unroll
-    for (int u = 0; u < DA; ++u) {
-      const int st = base + u;
-      gu_step<dt, 1>(ring[u], xs_h, xs_l, xo, st * F::STEP, g, acc);
-      if (u % 2 == 0) gu_pass_on<dt>(ring[u], ring[(u + 1) % DA]);
-      const int sn = st + DA < ngrp ? st + DA : st;  // spare refills reread this step
-      gu_a_load<dt>(ring[u], R.rp, R.sp, sn * F::STEP, g, u % 2 == 0);
-      // each refill is issued right after its slot is consumed (left to itself the
-      // scheduler gathers them at the end of the group, and the next group then waits
-      // for all of them)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  for (int st = ngrp; st * F::STEP < H; ++st) {
-    GuRing<dt> ar;
-    gu_a_load_masked<dt>(ar, R, H, st * F::STEP, g);
-    gu_step<dt, 1, true>(ar, xs_h, xs_l, xo, st * F::STEP, g, acc, H - 8);
-  }
-  gu_epilogue<1>(acc, rows, rbase, l16, g, tok_slot, tok_w, np, act, IA);
-}
-
 // ------------------------------------------------------------------------------------
 // Gate/up with the weights streamed into LDS (buckets of <= kGuSmall tokens)
 //
@@ -771,19 +709,17 @@ __device__ __forceinline__ void fill_tokens(const BsArgs& a, const Bucket& bk, i
 }
 
 // Buckets of at most kGuSmall tokens (every bucket at small batches) run in a launch of
-// their own with one token tile: without the wider tiles' registers it keeps two
-// workgroups per CU and a deeper weight ring.  Larger buckets run in the other launch.
+// their own with one token tile and the weights streamed through LDS; larger buckets run
+// in the other launch with 2 or 4 token tiles and a register ring.
 constexpr int kGuSmall = 16;
-// weight bytes in flight per wave: 16 KB (MXFP4: 2 steps of 256), 24 KB (bf16: 3 steps of 64)
-template <DT dt> constexpr int gu_da_small() { return dt == DT::MXFP4 ? 2 : 3; }
 template <DT dt> constexpr int gu_pass_tokens() {
   return gu_kx<4>() >= Gu<dt>::STEP ? 64 : 32;
 }
 constexpr int kGuDALarge = 2;
-static_assert(gu_da_small<DT::MXFP4>() % 2 == 0 && kGuDALarge % 2 == 0,
+static_assert(kGuDALarge % 2 == 0,
               "MXFP4 rings pair even and odd steps (their scales are read together)");
 
-template <DT et, DT st, bool SMALL, bool LDSW = false>
+template <DT et, DT st, bool SMALL>
 __device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i32* tok_b,
                                             lds_i32* tok_slot, lds_f32* tok_w,
                                             lds_u8* ring = nullptr, lds_u8* scl = nullptr) {
@@ -804,7 +740,7 @@ __device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i3
     if (a.gate_s) Gs = a.gate_s + off * (a.H / 32);
     if (a.up_s) Vs = a.up_s + off * (a.H / 32);
   }
-  if constexpr (SMALL && LDSW) {
+  if constexpr (SMALL) {
     fill_tokens(a, bk, 0, bk.count, tok_b, tok_slot, tok_w);
     __syncthreads();
     if (bk.shared) {
@@ -821,27 +757,6 @@ __device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i3
       else
         gu_pass_lds<et, false>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b, tok_slot,
                                tok_w, bk.count, xs, ring, scl, a.act, a.IA);
-    }
-  } else if constexpr (SMALL) {
-    fill_tokens(a, bk, 0, bk.count, tok_b, tok_slot, tok_w);
-    __syncthreads();
-    // MXFP4 buckets whose whole x fits in LDS skip the chunked staging (measured: faster for
-    // MXFP4 steps, slower for the short bf16 steps, which keep the chunks)
-    if (bk.shared) {
-      if (gu_use_res<st>(bk.count, a.H))
-        gu_pass_res<st, gu_da_small<st>()>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh,
-                                           a.xl, tok_b, tok_slot, tok_w, bk.count, xs, a.act,
-                                           a.IA);
-      else
-        gu_pass<st, 1, gu_da_small<st>()>(G, V, nullptr, nullptr, a.H, rows, rbase, a.xh, a.xl,
-                                          tok_b, tok_slot, tok_w, bk.count, xs, a.act, a.IA);
-    } else {
-      if (gu_use_res<et>(bk.count, a.H))
-        gu_pass_res<et, gu_da_small<et>()>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b,
-                                           tok_slot, tok_w, bk.count, xs, a.act, a.IA);
-      else
-        gu_pass<et, 1, gu_da_small<et>()>(G, V, Gs, Vs, a.H, rows, rbase, a.xh, a.xl, tok_b,
-                                          tok_slot, tok_w, bk.count, xs, a.act, a.IA);
     }
   } else {
     // tokens per pass: 64 (four token tiles) where a four-tile x chunk holds a weight step,
@@ -872,18 +787,6 @@ __device__ __forceinline__ void gateup_body(const BsArgs& a, lds_u16* xs, lds_i3
   }
 }
 
-// x buffers in dynamic LDS: [2 buffers][hi, lo][kGuBuf]
-template <DT et, DT st>
-__global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bs_gateup_small_kernel(BsArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int tok_b[kGuTok];
-  __shared__ int tok_slot[kGuTok];
-  __shared__ float tok_w[kGuTok];
-  gateup_body<et, st, true>(a, (lds_u16*)smem, (lds_i32*)tok_b, (lds_i32*)tok_slot,
-                            (lds_f32*)tok_w);
-}
-
 // Buckets of <= kGuSmall tokens with the weights streamed through LDS (one workgroup per
 // CU: the x buffers in dynamic LDS and the weight ring in static LDS).
 template <DT et, DT st>
@@ -894,7 +797,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void bs_gateup_lds_kernel(BsArgs a) 
   __shared__ int tok_b[kGuTok];
   __shared__ int tok_slot[kGuTok];
   __shared__ float tok_w[kGuTok];
-  gateup_body<et, st, true, true>(a, (lds_u16*)smem, (lds_i32*)tok_b, (lds_i32*)tok_slot,
+  gateup_body<et, st, true>(a, (lds_u16*)smem, (lds_i32*)tok_b, (lds_i32*)tok_slot,
                                   (lds_f32*)tok_w, (lds_u8*)ring, (lds_u8*)scl);
 }
 
