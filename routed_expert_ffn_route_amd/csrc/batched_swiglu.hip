@@ -848,7 +848,7 @@ template <> struct Dn<DT::MXFP4> {
     return r;
   }
   static __device__ __forceinline__ void decode(const Raw& r, float (&v)[EPT]) {
-    const float sc = __uint_as_float(r.s << 23);
+    const float sc = __uint_as_float((uint32_t)r.s << 23);
     const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {

@@ -234,13 +234,8 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   Ctx c;
   c.tid = threadIdx.x;
   c.nthreads = blockDim.x;
-  c.tsz = L.tsz;
-  c.wpt = c.tsz / kWave;
-  c.nteams = c.nthreads / c.tsz;
-  c.team = c.tid / c.tsz;
-  c.t = c.tid % c.tsz;
+  set_teams(c, L.tsz);
   c.lane = c.tid & (kWave - 1);
-  c.wit = c.t / kWave;
   c.P = gridDim.x;
   c.wg = blockIdx.x;
   c.H = a.H;
@@ -248,6 +243,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   c.red = reinterpret_cast<float*>(smem);
   c.red_stride = (c.nthreads / kWave) * kMaxNP;
   c.parity = 0;
+  c.zrow = a.zrow;
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
   float* s_w = reinterpret_cast<float*>(s_ids + 64);                // [64]
@@ -269,10 +265,10 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
                        reinterpret_cast<uint32_t*>(s_int), c);
   if (a.NS > 0) {
     const long long nsc = (long long)a.NS * a.IS;
-    stream_channels<ST, C, CPT, true>(
-        a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, nsc * c.wg / c.P,
-        nsc * (c.wg + 1) / c.P,
-        [](long long f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
+    stream_channels<ST, C, CPT, true, true>(
+        a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, (int)(nsc * c.wg / c.P),
+        (int)(nsc * (c.wg + 1) / c.P),
+        [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
   }
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
                 reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
@@ -428,9 +424,9 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   for (int i = c.tid; i < nk; i += c.nthreads) L.kept_out[kept_before + i] = loc[i];
 
   // 5. the kept channels of this share: up row and down row only, gate value from LDS
-  stream_channels<ET, C, CPT, false>(
+  stream_channels<ET, C, CPT, false, false>(
       nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, 0, nk,
-      [=](long long i, long long& row, float& wt, float& gv) {
+      [=](int i, long long& row, float& wt, float& gv) {
         const int f = loc[i];
         const int slot = f / I;
         const int e = s_ids[slot];

@@ -10,6 +10,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Pointers typed as LDS (address space 3).  Buffers chosen at run time among several LDS
 // arrays can otherwise reach the accesses as generic pointers, which compile to flat
@@ -19,6 +20,20 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) int lds_i32;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+// Buffer resource over `bytes` bytes from the wave-uniform address p.  Loads through it at
+// byte offsets at or past `bytes` return zeros without a memory access, so a resource of
+// 0 bytes serves an empty slot and the lanes past a row's end need no bounds test.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // third word: 32-bit data format, the raw-buffer setting on this architecture
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+constexpr int kNT = 2;  // cache policy of the weight streams: non-temporal
+// global-memory (address space 1) views: loads through them are global_load_* (never flat)
+typedef __attribute__((address_space(1))) uint8_t gbl_u8;
+typedef __attribute__((address_space(1))) uint32_t gbl_u32;
+typedef __attribute__((address_space(1))) u32x2 gbl_u32x2;
+typedef __attribute__((address_space(1))) u32x4 gbl_u32x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 __device__ __forceinline__ u32x4 lds_ld128(const lds_u16* p) {
   return *reinterpret_cast<const lds_u32x4*>(p);
@@ -57,6 +72,21 @@ template <> struct Fmt<DT::F32> {
     r.b = __builtin_nontemporal_load(p + 1);
     return r;
   }
+  // the same through buffer resources (w: the row, s: its scales; zeros out of range) or
+  // from global-memory pointers
+  static __device__ __forceinline__ Raw load_b(rsrc_t w, rsrc_t, int c) {
+    Raw r;
+    r.a = __builtin_amdgcn_raw_buffer_load_b128(w, 32 * c, 0, kNT);
+    r.b = __builtin_amdgcn_raw_buffer_load_b128(w, 32 * c + 16, 0, kNT);
+    return r;
+  }
+  static __device__ __forceinline__ Raw load_g(const gbl_u8* row, const gbl_u8*, int c) {
+    const gbl_u32x4* p = reinterpret_cast<const gbl_u32x4*>(row) + 2 * c;
+    Raw r;
+    r.a = __builtin_nontemporal_load(p);
+    r.b = __builtin_nontemporal_load(p + 1);
+    return r;
+  }
   static __device__ __forceinline__ void decode(const Raw& r, float v[8]) {
     v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
     v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
@@ -74,6 +104,16 @@ template <> struct Fmt<DT::BF16> {
     r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + c);
     return r;
   }
+  static __device__ __forceinline__ Raw load_b(rsrc_t w, rsrc_t, int c) {
+    Raw r;
+    r.a = __builtin_amdgcn_raw_buffer_load_b128(w, 16 * c, 0, kNT);
+    return r;
+  }
+  static __device__ __forceinline__ Raw load_g(const gbl_u8* row, const gbl_u8*, int c) {
+    Raw r;
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32x4*>(row) + c);
+    return r;
+  }
   static __device__ __forceinline__ void decode(const Raw& r, float v[8]) {
     v[0] = __uint_as_float(r.a.x << 16); v[1] = __uint_as_float(r.a.x & 0xFFFF0000u);
     v[2] = __uint_as_float(r.a.y << 16); v[3] = __uint_as_float(r.a.y & 0xFFFF0000u);
@@ -85,17 +125,29 @@ template <> struct Fmt<DT::BF16> {
 
 template <> struct Fmt<DT::MXFP4> {
   static constexpr int kE = 8;
-  struct Raw { uint32_t q; uint32_t s; };
+  struct Raw { uint32_t q; uint8_t s; };  // s: kept a byte until decode (no early zero-extension)
   static __device__ __forceinline__ Raw load(const void* row, const uint8_t* srow, int c) {
     Raw r;
     r.q = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row) + c);
     r.s = __builtin_nontemporal_load(srow + (c >> 2));
     return r;
   }
+  static __device__ __forceinline__ Raw load_b(rsrc_t w, rsrc_t s, int c) {
+    Raw r;
+    r.q = __builtin_amdgcn_raw_buffer_load_b32(w, 4 * c, 0, kNT);
+    r.s = __builtin_amdgcn_raw_buffer_load_b8(s, c >> 2, 0, kNT);
+    return r;
+  }
+  static __device__ __forceinline__ Raw load_g(const gbl_u8* row, const gbl_u8* srow, int c) {
+    Raw r;
+    r.q = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32*>(row) + c);
+    r.s = __builtin_nontemporal_load(srow + (c >> 2));
+    return r;
+  }
   // value = e2m1(code) * 2^(scale - 127): the hardware conversion applies the fp32
   // scale 2^(scale-127), built from the e8m0 byte (a zero byte gives 0, not 2^-127).
   static __device__ __forceinline__ void decode(const Raw& r, float v[8]) {
-    const float sc = __uint_as_float(r.s << 23);
+    const float sc = __uint_as_float((uint32_t)r.s << 23);
     f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.q, sc, 0);
     f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.q, sc, 1);
     f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.q, sc, 2);
@@ -109,15 +161,27 @@ template <> struct Fmt<DT::MXFP4> {
 
 template <> struct Fmt<DT::MXFP4W> {
   static constexpr int kE = 16;
-  struct Raw { u32x2 q; uint32_t s; };
+  struct Raw { u32x2 q; uint8_t s; };
   static __device__ __forceinline__ Raw load(const void* row, const uint8_t* srow, int c) {
     Raw r;
     r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row) + c);
     r.s = __builtin_nontemporal_load(srow + (c >> 1));
     return r;
   }
+  static __device__ __forceinline__ Raw load_b(rsrc_t w, rsrc_t s, int c) {
+    Raw r;
+    r.q = __builtin_amdgcn_raw_buffer_load_b64(w, 8 * c, 0, kNT);
+    r.s = __builtin_amdgcn_raw_buffer_load_b8(s, c >> 1, 0, kNT);
+    return r;
+  }
+  static __device__ __forceinline__ Raw load_g(const gbl_u8* row, const gbl_u8* srow, int c) {
+    Raw r;
+    r.q = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32x2*>(row) + c);
+    r.s = __builtin_nontemporal_load(srow + (c >> 1));
+    return r;
+  }
   static __device__ __forceinline__ void decode(const Raw& r, float v[16]) {
-    const float sc = __uint_as_float(r.s << 23);
+    const float sc = __uint_as_float((uint32_t)r.s << 23);
     const uint32_t w[2] = {r.q.x, r.q.y};
 #pragma unroll
     for (int k = 0; k < 2; ++k) {

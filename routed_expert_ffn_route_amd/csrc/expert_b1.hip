@@ -47,13 +47,8 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   Ctx c;
   c.tid = threadIdx.x;
   c.nthreads = blockDim.x;
-  c.tsz = L.tsz;
-  c.wpt = c.tsz / kWave;
-  c.nteams = c.nthreads / c.tsz;
-  c.team = c.tid / c.tsz;
-  c.t = c.tid % c.tsz;
+  set_teams(c, L.tsz);
   c.lane = c.tid & (kWave - 1);
-  c.wit = c.t / kWave;
   c.P = gridDim.x;
   c.wg = blockIdx.x;
   c.H = a.H;
@@ -61,6 +56,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   c.red = reinterpret_cast<float*>(smem);
   c.red_stride = (c.nthreads / kWave) * kMaxNP;
   c.parity = 0;
+  c.zrow = a.zrow;
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
   float* s_w = reinterpret_cast<float*>(s_ids + 64);                // [64]
@@ -85,10 +81,10 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   // 2. shared experts (independent of routing): flat channel f of [NS][IS] is row f
   if (a.NS > 0) {
     const long long nsc = (long long)a.NS * a.IS;
-    stream_channels<ST, CS, CPT, true>(
-        a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, nsc * c.wg / c.P,
-        nsc * (c.wg + 1) / c.P,
-        [](long long f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
+    stream_channels<ST, CS, CPT, true, true>(
+        a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, (int)(nsc * c.wg / c.P),
+        (int)(nsc * (c.wg + 1) / c.P),
+        [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
   }
 
   // with two layouts the shared experts' output moves to LDS now (ysh: nteams * H floats),
@@ -101,25 +97,23 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
                 reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
   Ctx cr = c;
   if constexpr (kTwo) {
-    cr.tsz = L.tsz_r;
-    cr.wpt = cr.tsz / kWave;
-    cr.nteams = cr.nthreads / cr.tsz;
-    cr.team = cr.tid / cr.tsz;
-    cr.t = cr.tid % cr.tsz;
-    cr.wit = cr.t / kWave;
+    set_teams(cr, L.tsz_r);
     cr.nch = a.H / ER;
   }
-  float xr[kTwo ? CPT * ER : 1], yr[kTwo ? CPT * ER : 1];
+  // the routed layout's x as f16 pairs (MXFP4 dot products), its outputs in fp32
+  XHalf<CPT> xr;
+  float yr[kTwo ? CPT * ER : 1];
   if constexpr (kTwo) {
-    load_x<ER, CPT>(a.x, cr, xr);
+    load_x_half<CPT>(a.x, cr, xr);
 #pragma unroll
     for (int i = 0; i < CPT * ER; ++i) yr[i] = 0.0f;
   }
   {
-    const long long nrc = (long long)a.k * a.I;
+    const long long nrc = (long long)a.k * a.I;  // below 2^31 (checked at layer creation)
+    const int i0 = (int)(nrc * c.wg / c.P), i1 = (int)(nrc * (c.wg + 1) / c.P);
     const int I = a.I;
-    auto map = [=](long long f, long long& row, float& wt, float&) {
-      const int slot = (int)(f / I), j = (int)(f - (long long)slot * I);
+    auto map = [=](int f, long long& row, float& wt, float&) {
+      const int slot = f / I, j = f - slot * I;
       const int e = s_ids[slot];
       if (e >= 0) {
         row = (long long)e * I + j;
@@ -127,13 +121,11 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
       }
     };
     if constexpr (kTwo)
-      stream_channels<ET, CR, CPT, true>(a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s,
-                                         nrc * c.wg / c.P, nrc * (c.wg + 1) / c.P, map, xr, yr,
-                                         cr);
+      stream_channels<ET, CR, CPT, true, false>(a.gate, a.up, a.down_t, a.gate_s, a.up_s,
+                                                a.down_s, i0, i1, map, xr, yr, cr);
     else
-      stream_channels<ET, CR, CPT, true>(a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s,
-                                         nrc * c.wg / c.P, nrc * (c.wg + 1) / c.P, map, xv, yv,
-                                         c);
+      stream_channels<ET, CR, CPT, true, false>(a.gate, a.up, a.down_t, a.gate_s, a.up_s,
+                                                a.down_s, i0, i1, map, xv, yv, c);
   }
 
   // 4. deterministic cross-workgroup sum of the partial outputs

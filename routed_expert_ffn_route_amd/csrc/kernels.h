@@ -23,6 +23,7 @@ struct B1Args {
   const int32_t* ids_in;                // given routing [k] or null
   const float* w_in;
   uint64_t* rlog;                       // [E] router logits with their launch tag
+  const uint8_t* zrow;                  // zeroed bytes, at least H * 4: read by empty slots
   int32_t* ids_ws;                      // [k]
   float* w_ws;                          // [k]
   float* partials;                      // [P][H]

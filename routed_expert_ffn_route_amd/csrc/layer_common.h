@@ -52,12 +52,25 @@ struct Ctx {
   int red_stride; // floats per buffer
   int parity;
   uint32_t epoch; // launches completed on this workspace before this one
+  const uint8_t* zrow;  // zeroed global memory of at least one weight row and scale row
   __device__ float* next_red() {
     float* r = red + parity * red_stride;
     parity ^= 1;
     return r;
   }
 };
+
+// Team layout of a context: teams of tsz threads (whole waves).  The team and the wave
+// within it are wave-uniform, so they live in scalar registers: item indices and weight-row
+// addresses derived from them are then scalar arithmetic.
+__device__ __forceinline__ void set_teams(Ctx& c, int tsz) {
+  c.tsz = tsz;
+  c.wpt = tsz / kWave;
+  c.nteams = c.nthreads / tsz;
+  c.team = __builtin_amdgcn_readfirstlane(c.tid / tsz);
+  c.t = c.tid % tsz;
+  c.wit = __builtin_amdgcn_readfirstlane(c.t / kWave);
+}
 
 // x values of this thread's chunks (E elements each; zero past the row end).
 template <int E, int CPT>
@@ -75,6 +88,141 @@ __device__ __forceinline__ void load_x(const float* x, const Ctx& c, float (&xv)
   }
 }
 
+// x of a thread's 16-element chunks as f16 pairs for the MXFP4 dot products: per chunk,
+// x * 2^-e with e chosen from the chunk's largest |x| so that the values sit well inside
+// the f16 range (largest magnitude in [2^14, 2^15)), and 2^e to scale the dot back.
+template <int CPT>
+struct XHalf {
+  f16x2 p[CPT][8];
+  float sc[CPT];
+};
+
+template <int CPT>
+__device__ __forceinline__ void load_x_half(const float* x, const Ctx& c, XHalf<CPT>& xh) {
+  float v[CPT * 16];
+  load_x<16, CPT>(x, c, v);
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[16 * m + i]));
+    // binary exponent of mx (subnormal or zero: -127; the scale then stays finite)
+    const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 127;
+    const int e = ex - 14;
+    xh.sc[m] = ldexpf(1.0f, e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xh.p[m][j].x = (_Float16)ldexpf(v[16 * m + 2 * j], -e);
+      xh.p[m][j].y = (_Float16)ldexpf(v[16 * m + 2 * j + 1], -e);
+    }
+  }
+}
+
+// This thread's share of the dot product of a weight row with x (before the sum over the
+// team): fp32 fused multiply-adds for float x, or, for MXFP4 chunks with x as f16 pairs,
+// the hardware fp4 -> f16 conversion and two-element f16 dot products accumulated in fp32,
+// scaled by the block scale and 2^e afterwards.
+template <DT dt, int CPT, int N>
+__device__ __forceinline__ float xdot(const typename Fmt<dt>::Raw (&r)[CPT],
+                                      const float (&xv)[N]) {
+  return chunk_dot<dt, CPT>(r, xv);
+}
+template <DT dt, int CPT>
+__device__ __forceinline__ float xdot(const typename Fmt<dt>::Raw (&r)[CPT],
+                                      const XHalf<CPT>& xh) {
+  static_assert(dt == DT::MXFP4W, "f16 x pairs serve the 16-element MXFP4 chunks");
+  float s = 0.0f;
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const uint32_t w[2] = {r[m].q.x, r[m].q.y};
+    float d = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const f16x2* xp = &xh.p[m][4 * k];
+      d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[k], 1.0f, 0),
+                                 xp[0], d, false);
+      d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[k], 1.0f, 1),
+                                 xp[1], d, false);
+      d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[k], 1.0f, 2),
+                                 xp[2], d, false);
+      d = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[k], 1.0f, 3),
+                                 xp[3], d, false);
+    }
+    // e8m0 scale 2^(s-127) (a zero byte gives 0, as in the fp32 decode)
+    s = fmaf(d * __uint_as_float((uint32_t)r[m].s << 23), xh.sc[m], s);
+  }
+  return s;
+}
+
+// Where the chunks of one slot (weight row `row`, row < 0 for an empty slot) are loaded
+// from.  Every slot is loaded unconditionally: a load under a branch makes the compiler wait
+// for all loads in flight before the next use of any of them.
+//   BUF: buffer resources over the row and its scale row.  An empty slot gets resources of
+//     0 bytes, whose loads return zeros without a memory access, and the lanes past the row
+//     end read zeros: for streams with many empty slots.
+//   otherwise: global loads from wave-uniform pointers, slightly cheaper per load.  An empty
+//     slot reads the zeroed row; lanes past the row end re-read its last chunk (their x
+//     values are zero and their outputs are never stored).
+template <DT dt, bool BUF> struct RowSrc;
+template <DT dt> struct RowSrc<dt, true> {
+  rsrc_t w, s;
+  __device__ __forceinline__ void set(const void* base, const uint8_t* scales, size_t r,
+                                      bool ok, const Ctx& c) {
+    w = make_rsrc(row_ptr<dt>(base, r, c.H), ok ? (uint32_t)Fmt<dt>::row_bytes(c.H) : 0u);
+    s = make_rsrc(scales ? scale_row_ptr(scales, r, c.H) : base,
+                  ok && scales ? (uint32_t)(c.H / 32) : 0u);
+  }
+  __device__ __forceinline__ typename Fmt<dt>::Raw load(int ch, const Ctx&) const {
+    return Fmt<dt>::load_b(w, s, ch);
+  }
+};
+template <DT dt> struct RowSrc<dt, false> {
+  const gbl_u8 *w, *s;
+  __device__ __forceinline__ void set(const void* base, const uint8_t* scales, size_t r,
+                                      bool ok, const Ctx& c) {
+    w = uniform_ptr(ok ? reinterpret_cast<const uint8_t*>(row_ptr<dt>(base, r, c.H)) : c.zrow);
+    s = uniform_ptr(ok && scales ? scale_row_ptr(scales, r, c.H) : c.zrow);
+  }
+  __device__ __forceinline__ typename Fmt<dt>::Raw load(int ch, const Ctx& c) const {
+    return Fmt<dt>::load_g(w, s, ch < c.nch ? ch : c.nch - 1);
+  }
+};
+
+template <DT dt, bool BUF>
+__device__ __forceinline__ RowSrc<dt, BUF> slot_rows(const void* base, const uint8_t* scales,
+                                                     long long row, const Ctx& c) {
+  // the row index is wave-uniform: in scalar registers, the address arithmetic is scalar too
+  const uint64_t ru = (uint64_t)row;
+  const long long rs = (long long)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ru >> 32))
+                                    << 32) |
+                                   __builtin_amdgcn_readfirstlane((uint32_t)ru));
+  RowSrc<dt, BUF> src;
+  src.set(base, scales, rs >= 0 ? (size_t)rs : 0, rs >= 0, c);
+  return src;
+}
+
+// After the barrier that follows the waves' writes of their NP partial totals to
+// red[(team * wpt + wave) * NP + p]: the team totals, lane l holding total l % NP.  Lane l
+// sums the partials l, l + 64, ... of the team's wpt * NP, then lanes of equal l % NP are
+// summed by exchanges across the higher lane bits.  Total p is then readlane(v, p).
+template <int NP>
+__device__ __forceinline__ float team_totals(const float* red, const Ctx& c) {
+  const float* tr = red + c.team * c.wpt * NP;
+  const int n = c.wpt * NP;
+  float v = c.lane < n ? tr[c.lane] : 0.0f;
+  for (int o = c.lane + kWave; o < n; o += kWave) v += tr[o];
+  if constexpr (NP <= 1) v += lane_xor<1>(v, c.lane);
+  if constexpr (NP <= 2) v += lane_xor<2>(v, c.lane);
+  if constexpr (NP <= 4) v += lane_xor<4>(v, c.lane);
+  if constexpr (NP <= 8) v += lane_xor<8>(v, c.lane);
+  if constexpr (NP <= 16) v += lane_xor<16>(v, c.lane);
+  if constexpr (NP <= 32) v += lane_xor<32>(v, c.lane);
+  return v;
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Team dot products of C rows with x: returns, in every thread of the team, the C totals
 // (out[c]).  rows[c] < 0 marks an empty slot.  One barrier.  All threads must call.
 template <DT dt, int C, int CPT>
@@ -86,15 +234,9 @@ __device__ __forceinline__ void team_dots(const void* base, const uint8_t* scale
   typename F::Raw r[C][CPT];
 #pragma unroll
   for (int q = 0; q < C; ++q) {
-    const bool ok = rows[q] >= 0;
-    const size_t rr = ok ? (size_t)rows[q] : 0;
-    const void* p = row_ptr<dt>(base, rr, c.H);
-    const uint8_t* sp = scales ? scale_row_ptr(scales, rr, c.H) : nullptr;
+    const RowSrc<dt, true> src = slot_rows<dt, true>(base, scales, rows[q], c);
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) {
-      const int ch = c.t + m * c.tsz;
-      r[q][m] = (ok && ch < c.nch) ? F::load(p, sp, ch) : zero_raw<dt>();
-    }
+    for (int m = 0; m < CPT; ++m) r[q][m] = src.load(c.t + m * c.tsz, c);
   }
   constexpr int NP = NextPow2<C>::value;
   float acc[NP];
@@ -106,13 +248,9 @@ __device__ __forceinline__ void team_dots(const void* base, const uint8_t* scale
   float* red = c.next_red();
   if (c.lane < NP) red[(c.team * c.wpt + c.wit) * NP + c.lane] = tot;
   __syncthreads();
+  const float v = team_totals<NP>(red, c);
 #pragma unroll
-  for (int q = 0; q < C; ++q) {
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < c.wpt; ++w) s += red[(c.team * c.wpt + w) * NP + q];
-    out[q] = s;
-  }
+  for (int q = 0; q < C; ++q) out[q] = lane_value(v, q);
 }
 
 // Raw weight chunks of one batch of C SwiGLU channels per team (one pipeline stage).
@@ -125,7 +263,7 @@ struct Stage {
 
 // Issue the loads of one batch (rows row[q] < 0 are empty slots; G == nullptr: no gate
 // rows, the gate values come in gv[]).
-template <DT dt, int C, int CPT, bool HAS_G>
+template <DT dt, int C, int CPT, bool HAS_G, bool BUF>
 __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G, const void* V,
                                            const void* D, const uint8_t* Gs, const uint8_t* Vs,
                                            const uint8_t* Ds, const long long (&row)[C],
@@ -133,23 +271,17 @@ __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G,
   using F = Fmt<dt>;
 #pragma unroll
   for (int q = 0; q < C; ++q) {
-    const bool ok = row[q] >= 0;
-    const size_t r = ok ? (size_t)row[q] : 0;
     // the row is the same for every lane of the wave (one team = whole waves)
-    const void* vp = row_ptr<dt>(V, r, c.H);
-    const void* dp = row_ptr<dt>(D, r, c.H);
-    const uint8_t* vsp = Vs ? scale_row_ptr(Vs, r, c.H) : nullptr;
-    const uint8_t* dsp = Ds ? scale_row_ptr(Ds, r, c.H) : nullptr;
-    const void* gp = HAS_G ? row_ptr<dt>(G, r, c.H) : nullptr;
-    const uint8_t* gsp = (HAS_G && Gs) ? scale_row_ptr(Gs, r, c.H) : nullptr;
+    RowSrc<dt, BUF> gs;
+    if constexpr (HAS_G) gs = slot_rows<dt, BUF>(G, Gs, row[q], c);
+    const RowSrc<dt, BUF> vs = slot_rows<dt, BUF>(V, Vs, row[q], c);
+    const RowSrc<dt, BUF> ds = slot_rows<dt, BUF>(D, Ds, row[q], c);
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
       const int ch = c.t + m * c.tsz;
-      const bool live = ok && ch < c.nch;
-      if constexpr (HAS_G)
-        st.g[q][m] = live ? F::load(gp, gsp, ch) : zero_raw<dt>();
-      st.v[q][m] = live ? F::load(vp, vsp, ch) : zero_raw<dt>();
-      st.d[q][m] = live ? F::load(dp, dsp, ch) : zero_raw<dt>();
+      if constexpr (HAS_G) st.g[q][m] = gs.load(ch, c);
+      st.v[q][m] = vs.load(ch, c);
+      st.d[q][m] = ds.load(ch, c);
     }
   }
 }
@@ -157,17 +289,16 @@ __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G,
 // Gate and up dots of a loaded batch, team reduction through LDS (one barrier),
 // silu(g)*u*wt, and the accumulation of that activation times the down row into yv.
 // All threads of the workgroup must call.
-template <DT dt, int C, int CPT, bool HAS_G>
-__device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st,
-                                              const float (&xv)[CPT * kE<dt>],
+template <DT dt, int C, int CPT, bool HAS_G, typename X>
+__device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st, const X& xv,
                                               float (&yv)[CPT * kE<dt>], Ctx& c) {
   constexpr int E = kE<dt>;
   constexpr int NP = NextPow2<2 * C>::value;
   float acc[NP];
 #pragma unroll
   for (int q = 0; q < C; ++q) {
-    acc[q] = HAS_G ? chunk_dot<dt, CPT>(st.g[q], xv) : 0.0f;
-    acc[C + q] = chunk_dot<dt, CPT>(st.v[q], xv);
+    acc[q] = HAS_G ? xdot<dt, CPT>(st.g[q], xv) : 0.0f;
+    acc[C + q] = xdot<dt, CPT>(st.v[q], xv);
   }
 #pragma unroll
   for (int i = 2 * C; i < NP; ++i) acc[i] = 0.0f;
@@ -175,14 +306,11 @@ __device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st,
   float* red = c.next_red();
   if (c.lane < NP) red[(c.team * c.wpt + c.wit) * NP + c.lane] = tot;
   __syncthreads();
+  const float v = team_totals<NP>(red, c);
 #pragma unroll
   for (int q = 0; q < C; ++q) {
-    float g = 0.0f, u = 0.0f;
-#pragma unroll
-    for (int w = 0; w < c.wpt; ++w) {
-      g += red[(c.team * c.wpt + w) * NP + q];
-      u += red[(c.team * c.wpt + w) * NP + C + q];
-    }
+    float g = lane_value(v, q);
+    const float u = lane_value(v, C + q);
     if (!HAS_G) g = st.gv[q];
     const float act = silu(g) * u * st.wt[q];
 #pragma unroll
@@ -198,37 +326,40 @@ __device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st,
 // Stream items [i0, i1) in batches of C per team, two batches in flight: the loads of
 // batch b+1 are issued before batch b is reduced.  map(i, row, wt, gv) gives the weight
 // row of item i (row < 0: skip), its weight and (HAS_G false: no gate rows are read) its
-// gate value.
-template <DT dt, int C, int CPT, bool HAS_G, typename Map>
+// gate value  BUF: the load path (RowSrc).
+template <DT dt, int C, int CPT, bool HAS_G, bool BUF, typename Map, typename X>
 __device__ inline void stream_channels(const void* G, const void* V, const void* D,
                                        const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
-                                       long long i0, long long i1, Map map,
-                                       const float (&xv)[CPT * kE<dt>],
+                                       int i0, int i1, Map map, const X& xv,
                                        float (&yv)[CPT * kE<dt>], Ctx& c) {
-  const long long per = (long long)c.nteams * C;
-  const long long nb = i1 > i0 ? (i1 - i0 + per - 1) / per : 0;
-  auto fill = [&](Stage<dt, C, CPT>& st, long long b) {
+  const int per = c.nteams * C;
+  const int nb = i1 > i0 ? (i1 - i0 + per - 1) / per : 0;
+  auto fill = [&](Stage<dt, C, CPT>& st, int b) {
     long long row[C];
 #pragma unroll
     for (int q = 0; q < C; ++q) {
-      const long long i = i0 + b * per + c.team * C + q;
+      const int i = i0 + b * per + c.team * C + q;
       row[q] = -1;
       st.wt[q] = 0.0f;
       st.gv[q] = 0.0f;
       if (i < i1) map(i, row[q], st.wt[q], st.gv[q]);
     }
-    stage_load<dt, C, CPT, HAS_G>(st, G, V, D, Gs, Vs, Ds, row, c);
+    stage_load<dt, C, CPT, HAS_G, BUF>(st, G, V, D, Gs, Vs, Ds, row, c);
   };
+  // Pairs of batches, then an odd last one.  The loads of every stage are issued without
+  // a condition (a batch past the end reads the zero row), so that the compiler's wait
+  // before each compute covers exactly that stage's loads: after a conditional load it
+  // would also wait for the other stage.
   Stage<dt, C, CPT> A, B;
-  if (nb > 0) fill(A, 0);
-  for (long long b = 0; b < nb; b += 2) {
-    if (b + 1 < nb) fill(B, b + 1);
+  fill(A, 0);
+  int b = 0;
+  for (; b + 1 < nb; b += 2) {
+    fill(B, b + 1);
     stage_compute<dt, C, CPT, HAS_G>(A, xv, yv, c);
-    if (b + 1 < nb) {
-      if (b + 2 < nb) fill(A, b + 2);
-      stage_compute<dt, C, CPT, HAS_G>(B, xv, yv, c);
-    }
+    fill(A, b + 2);
+    stage_compute<dt, C, CPT, HAS_G>(B, xv, yv, c);
   }
+  if (b < nb) stage_compute<dt, C, CPT, HAS_G>(A, xv, yv, c);
 }
 
 // Router logits, spread over the first workgroups (one team per row).  Each logit is

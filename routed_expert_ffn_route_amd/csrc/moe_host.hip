@@ -49,7 +49,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
-  size_t ctrl, rlog, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
+  size_t ctrl, rlog, zrow, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
       union_slots, cs_s, cs_y, xh, xl, act, part, total;
 };
 
@@ -67,6 +67,9 @@ bool desc_valid(const moe_layer_desc* d, std::string* why) {
   if (d->top_k > 32 && d->n_experts > 64)
     return bad("top_k above 32 needs n_experts <= 64");
   if (d->inter < 8 || d->inter % 8 != 0) return bad("inter must be a positive multiple of 8");
+  // channel indices of the batch-1 kernels are 32-bit
+  if ((long long)d->n_experts * d->inter > 0x7FFFFFFFll)
+    return bad("n_experts * inter must be below 2^31");
   if (d->kind != MOE_EXPERT_SWIGLU && d->kind != MOE_EXPERT_LINEAR) return bad("bad kind");
   if (d->max_batch < 1 || d->max_batch > 4096) return bad("max_batch must be in [1, 4096]");
   if (d->router_dtype != MOE_DTYPE_NONE && d->router_dtype != MOE_F32 &&
@@ -79,6 +82,8 @@ bool desc_valid(const moe_layer_desc* d, std::string* why) {
     if (d->n_shared > 0) {
       if (d->shared_inter < 8 || d->shared_inter % 8 != 0)
         return bad("shared_inter must be a positive multiple of 8");
+      if ((long long)d->n_shared * d->shared_inter > 0x7FFFFFFFll)
+        return bad("n_shared * shared_inter must be below 2^31");
       if (d->shared_dtype != MOE_F32 && d->shared_dtype != MOE_BF16)
         return bad("shared_dtype must be F32 or BF16");
     }
@@ -102,6 +107,8 @@ Layout layout_of(const moe_layer_desc* d) {
   const size_t B = (size_t)d->max_batch, E = (size_t)d->n_experts, k = (size_t)d->top_k;
   L.ctrl = take(sizeof(Ctrl));
   L.rlog = take(E * 8);
+  // zeros that empty slots of the batch-1 streams read in place of a weight row
+  L.zrow = take((size_t)d->hidden * 4);
   L.logits = take(B * E * 4);
   L.ids = take(B * k * 4);
   L.w = take(B * k * 4);
@@ -191,6 +198,7 @@ static B1Args b1_args(moe_layer layer, const float* x, const int32_t* ids, const
   a.ids_in = ids;
   a.w_in = w;
   a.rlog = layer->at<uint64_t>(layer->L.rlog);
+  a.zrow = layer->at<uint8_t>(layer->L.zrow);
   a.ids_ws = layer->at<int32_t>(layer->L.ids);
   a.w_ws = layer->at<float>(layer->L.w);
   a.partials = layer->at<float>(layer->L.partials);
@@ -281,8 +289,9 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_weights* weigh
   l->threads = kThreads;
   l->magic = kMagic;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // control block and tagged router logits start at zero (tag 0 is never a launch's)
-  e = hipMemsetAsync(l->ctrl(), 0, L.rlog + (size_t)d.n_experts * 8, s);  // ctrl is at offset 0
+  // control block, tagged router logits (tag 0 is never a launch's) and the zero row start
+  // at zero; ctrl is at offset 0 and the zero row follows the logits
+  e = hipMemsetAsync(l->ctrl(), 0, L.zrow + (size_t)d.hidden * 4, s);
   if (e == hipSuccess && d.kind == MOE_EXPERT_SWIGLU)
     e = launch_row_norms(w.down_t, w.down_scale, to_dt(d.expert_dtype),
                          (size_t)d.n_experts * d.inter, d.hidden, l->at<float>(L.dnorm), s);

@@ -35,6 +35,10 @@ SMALL = [
               I_shared=24, layers=1),
     T.reduced(WORKLOADS["mxfp4_e896_k16"], wid=143, H=2048, E=17, k=3, I=200, n_shared=0,
               I_shared=0, layers=1),
+    # long expert rows (I = 32800) and a share of more than 512 routed channels per
+    # workgroup
+    T.reduced(WORKLOADS["mxfp4_e896_k16"], wid=144, H=256, E=4, k=4, I=32800, n_shared=1,
+              I_shared=64, layers=1),
 ]
 
 
