@@ -80,11 +80,13 @@ template <> struct Fmt<DT::F32> {
     r.b = __builtin_amdgcn_raw_buffer_load_b128(w, 32 * c + 16, 0, kNT);
     return r;
   }
+  // (offsets as unsigned 32-bit byte counts: the loads take a scalar base plus a 32-bit
+  // lane offset, with no 64-bit address arithmetic per lane)
   static __device__ __forceinline__ Raw load_g(const gbl_u8* row, const gbl_u8*, int c) {
-    const gbl_u32x4* p = reinterpret_cast<const gbl_u32x4*>(row) + 2 * c;
+    const uint32_t o = 32u * (uint32_t)c;
     Raw r;
-    r.a = __builtin_nontemporal_load(p);
-    r.b = __builtin_nontemporal_load(p + 1);
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32x4*>(row + o));
+    r.b = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32x4*>(row + o + 16u));
     return r;
   }
   static __device__ __forceinline__ void decode(const Raw& r, float v[8]) {
@@ -111,7 +113,7 @@ template <> struct Fmt<DT::BF16> {
   }
   static __device__ __forceinline__ Raw load_g(const gbl_u8* row, const gbl_u8*, int c) {
     Raw r;
-    r.a = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32x4*>(row) + c);
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32x4*>(row + 16u * (uint32_t)c));
     return r;
   }
   static __device__ __forceinline__ void decode(const Raw& r, float v[8]) {
@@ -140,8 +142,8 @@ template <> struct Fmt<DT::MXFP4> {
   }
   static __device__ __forceinline__ Raw load_g(const gbl_u8* row, const gbl_u8* srow, int c) {
     Raw r;
-    r.q = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32*>(row) + c);
-    r.s = __builtin_nontemporal_load(srow + (c >> 2));
+    r.q = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32*>(row + 4u * (uint32_t)c));
+    r.s = __builtin_nontemporal_load(srow + ((uint32_t)c >> 2));
     return r;
   }
   // value = e2m1(code) * 2^(scale - 127): the hardware conversion applies the fp32
@@ -176,8 +178,8 @@ template <> struct Fmt<DT::MXFP4W> {
   }
   static __device__ __forceinline__ Raw load_g(const gbl_u8* row, const gbl_u8* srow, int c) {
     Raw r;
-    r.q = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32x2*>(row) + c);
-    r.s = __builtin_nontemporal_load(srow + (c >> 1));
+    r.q = __builtin_nontemporal_load(reinterpret_cast<const gbl_u32x2*>(row + 8u * (uint32_t)c));
+    r.s = __builtin_nontemporal_load(srow + ((uint32_t)c >> 1));
     return r;
   }
   static __device__ __forceinline__ void decode(const Raw& r, float v[16]) {
@@ -261,53 +263,68 @@ __device__ __forceinline__ float lane_xor(float x, int lane) {
   }
 }
 
-// Sum over the 64 lanes of a wave, in every lane.
-__device__ __forceinline__ float wave_sum(float v) {
-  const int lane = (int)(threadIdx.x & (kWave - 1));
-  v += lane_xor<32>(v, lane);
-  v += lane_xor<16>(v, lane);
-  v += lane_xor<8>(v, lane);
-  v += lane_xor<4>(v, lane);
-  v += lane_xor<2>(v, lane);
-  v += lane_xor<1>(v, lane);
-  return v;
+// Sum over the lanes that agree with this one in the low log2(B) lane bits (B a power of
+// two <= 64), in every lane: quad permutes (DPP) for lane bits 0-1, rotations within a row
+// of 16 (DPP) for bits 2-3 (x + ror4(x), then + ror8: the four lanes of a residue mod 4),
+// and swaps of rows (permlane16) and of wave halves (permlane32) for bits 4-5.  Each step
+// is one exchange-and-add, none of them through LDS.
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int B>
+__device__ __forceinline__ float sum_lanes_above(float x) {
+  if constexpr (B <= 1) x = add_dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (B <= 2) x = add_dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (B <= 4) x = add_dpp<0x124>(x);  // row_ror:4
+  if constexpr (B <= 8) x = add_dpp<0x128>(x);  // row_ror:8
+  if constexpr (B <= 16) {
+    // one of the two results is this lane's value, the other its partner's in the row pair
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (B <= 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
 }
 
+// Sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_sum(float v) { return sum_lanes_above<1>(v); }
+
 // Reduce N values held by every lane of a wave.  On return, lane l holds the wave total of
-// value (l % N) in v[0] (N a power of two <= 64).  Uses N-1 + log2(64/N) exchanges
-// instead of N*6.
+// value (l % N) (N a power of two <= 16).  Halving steps first: at width w, a lane with bit
+// w/2 set keeps the upper half of its values and adds its partner's (lane ^ w/2) upper
+// half, the other lane the lower halves; N-1 exchanges instead of N*6.
 template <int N>
 __device__ __forceinline__ float wave_multi_sum(float (&v)[N], int lane) {
-  // halving steps: at width w, lanes with bit set keep the upper half of the values
 #pragma unroll
   for (int w = N; w > 1; w >>= 1) {
     const int half = w >> 1;
-    const bool upper = (lane & half) != 0;   // which half this lane keeps
+    const bool upper = (lane & half) != 0;
 #pragma unroll
     for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[i + half];
-      const float keep = upper ? v[i + half] : v[i];
+      const float lo = v[i], hi = v[i + half];  // values, so that the selects stay selects
+      const float send = upper ? lo : hi;
+      const float keep = upper ? hi : lo;
       float got;
       if (half == 1) got = lane_xor<1>(send, lane);
       else if (half == 2) got = lane_xor<2>(send, lane);
       else if (half == 4) got = lane_xor<4>(send, lane);
-      else if (half == 8) got = lane_xor<8>(send, lane);
-      else if (half == 16) got = lane_xor<16>(send, lane);
-      else got = lane_xor<32>(send, lane);
+      else got = lane_xor<8>(send, lane);
       v[i] = keep + got;
     }
   }
-  float r = v[0];
-  if (N <= 1) r += lane_xor<1>(r, lane);
-  if (N <= 2) r += lane_xor<2>(r, lane);
-  if (N <= 4) r += lane_xor<4>(r, lane);
-  if (N <= 8) r += lane_xor<8>(r, lane);
-  if (N <= 16) r += lane_xor<16>(r, lane);
-  if (N <= 32) r += lane_xor<32>(r, lane);
-  return r;  // lane l: total of value index (l & (N-1))
+  return sum_lanes_above<N>(v[0]);  // lane l: total of value index (l & (N-1))
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// z * sigmoid(z) with the hardware exponential and reciprocal (about 1 ulp each)
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // ------------------------------------------------------------------------------------
 // Exact top-k keys: descending float, ties to the lower index.

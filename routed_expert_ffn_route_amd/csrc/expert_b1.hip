@@ -114,7 +114,8 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
     const int I = a.I;
     auto map = [=](int f, long long& row, float& wt, float&) {
       const int slot = f / I, j = f - slot * I;
-      const int e = s_ids[slot];
+      // the expert id is wave-uniform (f is): scalar, so the row arithmetic is too
+      const int e = __builtin_amdgcn_readfirstlane(s_ids[slot]);
       if (e >= 0) {
         row = (long long)e * I + j;
         wt = s_w[slot];

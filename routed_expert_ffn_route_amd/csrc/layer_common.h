@@ -211,13 +211,7 @@ __device__ __forceinline__ float team_totals(const float* red, const Ctx& c) {
   const int n = c.wpt * NP;
   float v = c.lane < n ? tr[c.lane] : 0.0f;
   for (int o = c.lane + kWave; o < n; o += kWave) v += tr[o];
-  if constexpr (NP <= 1) v += lane_xor<1>(v, c.lane);
-  if constexpr (NP <= 2) v += lane_xor<2>(v, c.lane);
-  if constexpr (NP <= 4) v += lane_xor<4>(v, c.lane);
-  if constexpr (NP <= 8) v += lane_xor<8>(v, c.lane);
-  if constexpr (NP <= 16) v += lane_xor<16>(v, c.lane);
-  if constexpr (NP <= 32) v += lane_xor<32>(v, c.lane);
-  return v;
+  return sum_lanes_above<NP>(v);
 }
 __device__ __forceinline__ float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
