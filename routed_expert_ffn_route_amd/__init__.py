@@ -116,17 +116,22 @@ class Layer:
 
     ``tensors`` maps weight names (router, gate, up, down_t, gate_scale, up_scale,
     down_scale, linear, sh_gate, sh_up, sh_down_t) to device tensors laid out as in
-    include/moe_ffn.h.  The workspace is a uint8 device tensor owned by this object.
+    include/moe_ffn.h.  The workspace is a uint8 device tensor owned by this object, or the
+    caller's ``workspace`` (at least workspace_bytes(desc) + 256 bytes), kept alive here.
     """
 
-    def __init__(self, desc: LayerDesc, tensors: dict, stream=None):
+    def __init__(self, desc: LayerDesc, tensors: dict, stream=None, workspace=None):
         import torch
         self.desc = desc
         self.tensors = dict(tensors)  # keep the weights alive
         nbytes = workspace_bytes(desc)
         if nbytes == 0:
             raise MoeError(MOE_ERR_ARG, "invalid layer descriptor")
-        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
+        if workspace is None:
+            workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
+        elif workspace.numel() * workspace.element_size() < nbytes + 256:
+            raise MoeError(MOE_ERR_ARG, "workspace too small")
+        self.workspace = workspace
         off = (-self.workspace.data_ptr()) % 256
         self._ws_ptr = self.workspace.data_ptr() + off
         self._ws_bytes = nbytes

@@ -289,9 +289,12 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_weights* weigh
   l->threads = kThreads;
   l->magic = kMagic;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // control block, tagged router logits (tag 0 is never a launch's) and the zero row start
-  // at zero; ctrl is at offset 0 and the zero row follows the logits
-  e = hipMemsetAsync(l->ctrl(), 0, L.zrow + (size_t)d.hidden * 4, s);
+  // Everything from the control block (offset 0) through the tagged channel scores starts
+  // at zero: the epoch and arrival counters, the zero row, and every word that carries a
+  // launch tag (router logits, channel scores; tag 0 is never a launch's).  Memory reused
+  // from an earlier layer could otherwise hold words with the tag of this layer's first
+  // launch.
+  e = hipMemsetAsync(l->ctrl(), 0, L.cs_y, s);
   if (e == hipSuccess && d.kind == MOE_EXPERT_SWIGLU)
     e = launch_row_norms(w.down_t, w.down_scale, to_dt(d.expert_dtype),
                          (size_t)d.n_experts * d.inter, d.hidden, l->at<float>(L.dnorm), s);

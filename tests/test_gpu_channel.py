@@ -138,3 +138,28 @@ def test_channel_select_full_size(frac_i):
         err = rel_err(y, y_ref)
         print(f"keep {keep} token {tok} attempt {a}: max|dy|/||y||inf = {err:.3e}")
         assert err <= TOL_BF16
+
+
+def test_channel_select_poisoned_workspace():
+    """A workspace whose every 8-byte word carries the first launch's tag (as memory reused
+    from an earlier layer can) must not be mistaken for this launch's data: layer creation
+    clears every tagged word."""
+    import torch
+    import routed_expert_ffn_route_amd as M
+    wl = SMALL[2]
+    desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, wl.n_shared, wl.I_shared,
+                       router_dtype=wl.router_dtype, expert_dtype=wl.expert_dtype,
+                       shared_dtype=wl.shared_dtype, max_batch=1)
+    nbytes = (M.workspace_bytes(desc) + 256 + 7) // 8 * 8
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws.view(torch.int64).fill_((1 << 32) | 0x3F800000)  # tag 1, value 1.0
+    L = M.Layer(desc, T.device_layer(wl, 0), workspace=ws)
+    hl = HostLayer(wl)
+    keep = 100
+    a, x, dnorm_of = pick_attempt_cs(wl, hl, 5, keep, "gate_dnorm")
+    ids, w = O.route(O.router_logits(x, hl.router), wl.k)
+    kept_ref, y_ref = O.channel_select_token(x, ids[0], w[0], hl.expert, dnorm_of, keep,
+                                             hl.shared)
+    kept, y = _run(L, wl, x, keep, 0)
+    assert kept.tolist() == kept_ref.tolist()
+    assert rel_err(y, y_ref) <= TOL_BF16
