@@ -151,12 +151,16 @@ __device__ inline bool select_threshold_binned(const uint32_t* u, int n, int K, 
   if (wave == 0) {
     // lane l counts bins kSelBins - 1 - PB l - i, i < PB, from the top
     // (the counts stay in registers: all reads are issued at once, none waits on another)
+    // Those PB bins share (b >> 5) = kWave - 1 - lane, so their padded slots are the PB
+    // consecutive words from 33 * (kWave - 1 - lane): one base address and constant offsets.
     constexpr int PB = kSelBins / kWave;
+    static_assert(PB == 32, "the padded histogram layout puts 32 bins per 33 words");
+    const lds_i32* hb = (const lds_i32*)hist + 33 * (kWave - 1 - lane);
     int cnt[PB];
     int local = 0;
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      cnt[i] = hist[sel_slot(kSelBins - 1 - PB * lane - i)];
+      cnt[i] = hb[PB - 1 - i];
       local += cnt[i];
     }
     const int incl = wave_incl_scan(local);
