@@ -366,13 +366,30 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   // waiting on the scores themselves is the grid-wide hand-off)
   // (meanwhile the range of the scores per wave and a cleared histogram for the selection)
   {
+    // eight scores per thread in flight at once (the loads are unconditional, so none
+    // waits for another); only a score not yet tagged with this launch is polled again
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int f = c.tid; f < n; f += c.nthreads) {
-      const uint32_t v =
-          (uint32_t)wait_tagged(L.s_ws + f, c.epoch + 1u, &ctrl->err, kErrPhaseWait);
-      sbits[f] = v;
-      lo = v < lo ? v : lo;
-      hi = v > hi ? v : hi;
+    const uint32_t tag = c.epoch + 1u;
+    constexpr int kG = 8;
+    for (int f0 = c.tid; f0 < n; f0 += kG * c.nthreads) {
+      uint64_t w[kG];
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const int f = f0 + u * c.nthreads;
+        w[u] = ld_dev64(L.s_ws + (f < n ? f : n - 1));
+      }
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const int f = f0 + u * c.nthreads;
+        if (f < n) {
+          if ((uint32_t)(w[u] >> 32) != tag)
+            w[u] = wait_tagged(L.s_ws + f, tag, &ctrl->err, kErrPhaseWait);
+          const uint32_t v = (uint32_t)w[u];
+          sbits[f] = v;
+          lo = v < lo ? v : lo;
+          hi = v > hi ? v : hi;
+        }
+      }
     }
     for (int i = c.tid; i < kSelHist; i += c.nthreads) hist[i] = 0;
 #pragma unroll
@@ -431,9 +448,10 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   stream_channels<ET, C, CPT, false, false>(
       nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, 0, nk,
       [=](int i, long long& row, float& wt, float& gv) {
-        const int f = loc[i];
+        // i is wave-uniform, so are f and e: scalar, and so is the row arithmetic
+        const int f = __builtin_amdgcn_readfirstlane(loc[i]);
         const int slot = f / I;
-        const int e = s_ids[slot];
+        const int e = __builtin_amdgcn_readfirstlane(s_ids[slot]);
         if (e >= 0) {
           row = (long long)e * I + (f % I);
           wt = s_w[slot];
