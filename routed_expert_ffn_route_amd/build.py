@@ -8,7 +8,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
 SOURCES = ["moe_host.hip", "expert_b1.hip", "channel_sparse.hip", "route.hip",
-           "batched_swiglu.hip", "linear_mfma.hip", "grouped_tn.hip"]
+           "batched_swiglu.hip", "linear_mfma.hip", "linear_gemv.hip", "grouped_tn.hip"]
 
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -69,6 +69,18 @@ hipError_t launch_linear(const void* M, const float* x, const float* w, const in
                          uint16_t* xh, uint16_t* xl, float* y, int H, int I, int E, int k,
                          int B, hipStream_t s);
 
+// Linear experts at batches of up to kGemvMaxBatch tokens on VALU (whole-line weight
+// loads; workgroup r owns RW output rows of every touched expert): y [B][I].  `zrow` is
+// zeroed memory of at least H * 2 bytes (empty slots read it).  `workgroups` bounds the
+// grid.  Returns hipErrorInvalidValue outside linear_gemv_fits.
+constexpr int kGemvMaxBatch = 4;
+bool linear_gemv_fits(int H, int I, int B);
+hipError_t launch_linear_gemv(const void* M, const float* x, const float* w,
+                              const int32_t* n_touched, const int32_t* touched,
+                              const int32_t* offsets, const int32_t* slots,
+                              const uint8_t* zrow, float* y, int H, int I, int k, int B,
+                              int workgroups, hipStream_t s);
+
 // Linear experts for larger batches: one register-blocked MFMA tile per (touched expert,
 // 128 output rows) with the tokens' x staged in LDS, partial rows per (token, choice)
 // [B*k][I] in `part`, then a combine in routing order into y [B][I].

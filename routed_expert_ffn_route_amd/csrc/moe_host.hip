@@ -489,6 +489,10 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
                               layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl),
                               layer->at<float>(layer->L.part), y, d.hidden, d.inter,
                               d.n_experts, d.top_k, B, s);
+    else if (e == hipSuccess && linear_gemv_fits(d.hidden, d.inter, B))
+      e = launch_linear_gemv(layer->w.linear, x, rw, n_t, touched, offsets, slots,
+                             layer->at<uint8_t>(layer->L.zrow), y, d.hidden, d.inter,
+                             d.top_k, B, layer->workgroups, s);
     else if (e == hipSuccess)
       e = launch_linear(layer->w.linear, x, rw, n_t, touched, offsets, slots,
                         layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl), y,
