@@ -112,21 +112,12 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
     const long long nrc = (long long)a.k * a.I;  // below 2^31 (checked at layer creation)
     const int i0 = (int)(nrc * c.wg / c.P), i1 = (int)(nrc * (c.wg + 1) / c.P);
     const int I = a.I;
-    auto map = [=](int f, long long& row, float& wt, float&) {
-      const int slot = f / I, j = f - slot * I;
-      // the expert id is wave-uniform (f is): scalar, so the row arithmetic is too
-      const int e = __builtin_amdgcn_readfirstlane(s_ids[slot]);
-      if (e >= 0) {
-        row = (long long)e * I + j;
-        wt = s_w[slot];
-      }
-    };
     if constexpr (kTwo)
-      stream_channels<ET, CR, CPT, true, false>(a.gate, a.up, a.down_t, a.gate_s, a.up_s,
-                                                a.down_s, i0, i1, map, xr, yr, cr);
+      stream_routed<ET, CR, CPT>(a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s, i0, i1, I,
+                                 a.k, s_ids, s_w, xr, yr, cr);
     else
-      stream_channels<ET, CR, CPT, true, false>(a.gate, a.up, a.down_t, a.gate_s, a.up_s,
-                                                a.down_s, i0, i1, map, xv, yv, c);
+      stream_routed<ET, CR, CPT>(a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s, i0, i1, I,
+                                 a.k, s_ids, s_w, xv, yv, c);
   }
 
   // 4. deterministic cross-workgroup sum of the partial outputs

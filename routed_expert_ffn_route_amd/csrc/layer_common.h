@@ -356,6 +356,96 @@ __device__ inline void stream_channels(const void* G, const void* V, const void*
   if (b < nb) stage_compute<dt, C, CPT, HAS_G>(A, xv, yv, c);
 }
 
+// The routed experts' channels [i0, i1): flat channel f = slot * I + j is row j of expert
+// s_ids[slot] (negative: an empty slot), weighted by s_w[slot].  The same two-stage stream
+// as stream_channels, but the team's items are walked incrementally: (slot, j) of its next
+// first item advances by a batch per fill, and the current and next slot's expert offsets
+// stay in scalar registers, so an item's three row addresses are a 32-bit multiply and
+// 64-bit adds (the host admits E * I < 2^31; a row offset within one expert, I * row bytes,
+// stays below 2^32).  Every wave of the compute unit issues this scalar code, and scalar
+// instructions issue at the rate of vector ones, so the per-item divisions and 64-bit
+// multiplications of the generic map made the stream scalar-bound.
+template <DT dt, int C, int CPT, typename X>
+__device__ inline void stream_routed(const void* G, const void* V, const void* D,
+                                     const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
+                                     int i0, int i1, int I, int k, const int* s_ids,
+                                     const float* s_w, const X& xv,
+                                     float (&yv)[CPT * kE<dt>], Ctx& c) {
+  using F = Fmt<dt>;
+  const int per = c.nteams * C;
+  const int nb = i1 > i0 ? (i1 - i0 + per - 1) / per : 0;
+  const uint32_t rb = (uint32_t)F::row_bytes(c.H);
+  const uint32_t sb = (uint32_t)(c.H / 32);
+  const uint8_t* const gb = reinterpret_cast<const uint8_t*>(G);
+  const uint8_t* const vb = reinterpret_cast<const uint8_t*>(V);
+  const uint8_t* const db = reinterpret_cast<const uint8_t*>(D);
+  struct SlotState {
+    uint64_t od, os;  // byte offsets of the expert's rows and scale rows
+    float wt;
+    bool ok;
+  };
+  auto slot_state = [&](int sl) {
+    SlotState st;
+    const int sc = sl < k ? sl : 0;
+    const int e = __builtin_amdgcn_readfirstlane(s_ids[sc]);
+    st.ok = sl < k && e >= 0;
+    const uint64_t r = (uint64_t)(st.ok ? e : 0) * (uint64_t)I;
+    st.od = r * rb;
+    st.os = r * sb;
+    st.wt = s_w[sc];
+    return st;
+  };
+  int f = i0 + c.team * C;  // the team's first item of the next batch
+  int slot = f / I, j = f - slot * I;
+  SlotState cur = slot_state(slot), nxt = slot_state(slot + 1);
+  const int ch0 = c.t;
+  auto fill = [&](Stage<dt, C, CPT>& st) {
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+      const bool wrap = j + q >= I;
+      const int jq = wrap ? j + q - I : j + q;
+      const SlotState& ss = wrap ? nxt : cur;
+      const bool live = f + q < i1 && ss.ok;
+      const uint64_t od = ss.od + (uint64_t)((uint32_t)jq * rb);
+      const uint64_t os = ss.os + (uint64_t)((uint32_t)jq * sb);
+      RowSrc<dt, false> gs, vs, ds;
+      gs.w = uniform_ptr(live ? gb + od : c.zrow);
+      vs.w = uniform_ptr(live ? vb + od : c.zrow);
+      ds.w = uniform_ptr(live ? db + od : c.zrow);
+      gs.s = uniform_ptr(live && Gs ? Gs + os : c.zrow);
+      vs.s = uniform_ptr(live && Vs ? Vs + os : c.zrow);
+      ds.s = uniform_ptr(live && Ds ? Ds + os : c.zrow);
+      st.wt[q] = live ? ss.wt : 0.0f;
+      st.gv[q] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        const int ch = ch0 + m * c.tsz;
+        st.g[q][m] = gs.load(ch, c);
+        st.v[q][m] = vs.load(ch, c);
+        st.d[q][m] = ds.load(ch, c);
+      }
+    }
+    f += per;
+    j += per;
+    while (j >= I) {
+      j -= I;
+      ++slot;
+      cur = nxt;
+      nxt = slot_state(slot + 1);
+    }
+  };
+  Stage<dt, C, CPT> A, B;
+  fill(A);
+  int b = 0;
+  for (; b + 1 < nb; b += 2) {
+    fill(B);
+    stage_compute<dt, C, CPT, true>(A, xv, yv, c);
+    fill(A);
+    stage_compute<dt, C, CPT, true>(B, xv, yv, c);
+  }
+  if (b < nb) stage_compute<dt, C, CPT, true>(A, xv, yv, c);
+}
+
 // Router logits, spread over the first workgroups (one team per row).  Each logit is
 // published as one 64-bit word: the launch tag (epoch + 1) in the upper half and the fp32
 // bits in the lower half, so readers wait on the data itself.  Every workgroup also learns

@@ -70,6 +70,9 @@ bool desc_valid(const moe_layer_desc* d, std::string* why) {
   // channel indices of the batch-1 kernels are 32-bit
   if ((long long)d->n_experts * d->inter > 0x7FFFFFFFll)
     return bad("n_experts * inter must be below 2^31");
+  // one expert's rows are addressed with 32-bit byte offsets
+  if ((long long)d->inter * d->hidden * 4 >= (1ll << 32))
+    return bad("inter * hidden must be below 2^30");
   if (d->kind != MOE_EXPERT_SWIGLU && d->kind != MOE_EXPERT_LINEAR) return bad("bad kind");
   if (d->max_batch < 1 || d->max_batch > 4096) return bad("max_batch must be in [1, 4096]");
   if (d->router_dtype != MOE_DTYPE_NONE && d->router_dtype != MOE_F32 &&
