@@ -32,7 +32,8 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {
     "b1": ["expert_b1.hip", "layer_common.h", "device_common.h"],
     "cs": ["channel_sparse.hip", "layer_common.h", "device_common.h"],
-    "linear": ["linear_mfma.hip", "route.hip"],
+    "linear": ["linear_mfma.hip", "linear_gemv.hip", "grouped_tn.hip", "route.hip",
+               "layer_common.h", "device_common.h"],
 }
 BYTES_PER_ELEM = {"f32": 4.0, "bf16": 2.0, "mxfp4": 0.5 + 1.0 / 32.0}
 
@@ -325,7 +326,16 @@ def run_linear_sweep(args, wl):
     desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, kind=M.LINEAR, router_dtype=None,
                        expert_dtype="bf16", max_batch=bmax)
     L = M.Layer(desc, T.device_layer(wl, 0))
-    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    flush = torch.zeros(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(512 * 2**20 // 64, dtype=torch.float32, device="cuda")
+
+    def evict(t):
+        # evict the previous step's experts from the 256 MB MALL and the L2s
+        if args.flush == "fill":
+            flush.fill_(float(t))  # 512 MB of writes (their write-back can overlap the step)
+        else:
+            sink.copy_(flush.view(-1, 16)[:, 0])  # one 4-byte read per 64-byte piece: 512 MB
+                                                  # of lines read, 32 MB written
     lines = []
     for B in batches:
         nsteps = max(2, min(args.steps, 64 if B <= 64 else 16))
@@ -338,7 +348,7 @@ def run_linear_sweep(args, wl):
         n_touched = []
 
         def step(t):
-            flush.fill_(float(t))  # evict the previous step's experts from the 256 MB MALL
+            evict(t)
             L.route(logits_in=logits[t % 4], ids=ids, w=w)
             L.forward(x[t % 4], y, ids=ids, w=w)
 
@@ -355,7 +365,7 @@ def run_linear_sweep(args, wl):
             step(t)
         torch.cuda.synchronize()
         # time the flush alone and subtract it
-        fl_ms, _ = timed(lambda t: flush.fill_(float(t)), nsteps, graph_ok=not args.eager)
+        fl_ms, _ = timed(evict, nsteps, graph_ok=not args.eager)
         gpu_ms, _ = timed(step, nsteps, graph_ok=not args.eager)
         assert L.check() == 0
         step_s = (gpu_ms - fl_ms) / 1e3 / nsteps
@@ -369,7 +379,7 @@ def run_linear_sweep(args, wl):
             "touched_experts": touched, "hbm_gb_s": round(achieved, 1),
             "hbm_pct_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
             "tflop_s": round(flops / step_s / 1e12, 2), "steps": nsteps,
-            "note": "MALL flushed before each step (512 MB fill, timed separately and "
+            "note": f"MALL flushed before each step (512 MB {args.flush}, timed separately and "
                     "subtracted)", "kernel_hash": kernel_hash("linear")})
     return lines
 
@@ -384,6 +394,9 @@ def main():
     ap.add_argument("--keep", type=int, default=-1,
                     help="channel-sparse workload: kept channels per token (-1: first of the "
                          "workload's keep counts)")
+    ap.add_argument("--flush", choices=["read", "fill"], default="read",
+                    help="linear sweep: how the MALL is flushed between steps (a strided read "
+                         "of 512 MB, or a 512 MB fill)")
     ap.add_argument("--batches", default="", help="linear sweep: comma-separated batch sizes")
     ap.add_argument("--batch", type=int, default=1,
                     help="SwiGLU stacks: tokens per step (B > 1 runs the batched layer)")

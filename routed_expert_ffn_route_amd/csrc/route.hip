@@ -119,8 +119,8 @@ __global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, 
   uint32_t* bits = reinterpret_cast<uint32_t*>(smem);          // [E][W]
   int32_t* cnt = reinterpret_cast<int32_t*>(bits + (size_t)E * W);  // [E]
   int32_t* off = cnt + E;                                      // [E+1]
-  __shared__ int32_t part[1024];
-  __shared__ int32_t tpart[1024];
+  __shared__ int32_t part[1024 / kWave];
+  __shared__ int32_t tpart[1024 / kWave];
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int i = tid; i < E * W; i += nt) bits[i] = 0u;
   __syncthreads();
@@ -146,17 +146,24 @@ __global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, 
     cnt[e] = c;
   }
   __syncthreads();
-  // Exclusive scan of counts (and of touched flags): contiguous segments per thread.
+  // Exclusive scan of counts (and of touched flags): contiguous segments per thread, an
+  // inclusive scan of the segment sums within each wave (shuffles), then the wave totals
+  // in order.
   const int seg = (E + nt - 1) / nt;
   const int e0 = tid * seg, e1 = min(E, e0 + seg);
   int s = 0, ts = 0;
   for (int e = e0; e < e1; ++e) { s += cnt[e]; ts += cnt[e] > 0; }
-  part[tid] = s;
-  tpart[tid] = ts;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  int is = s, its = ts;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int a = __shfl_up(is, d, kWave), b = __shfl_up(its, d, kWave);
+    if (lane >= d) { is += a; its += b; }
+  }
+  if (lane == kWave - 1) { part[wave] = is; tpart[wave] = its; }
   __syncthreads();
   if (tid == 0) {
     int run = 0, trun = 0;
-    for (int i = 0; i < nt; ++i) {
+    for (int i = 0; i < nt / kWave; ++i) {
       const int v = part[i], tv = tpart[i];
       part[i] = run; tpart[i] = trun;
       run += v; trun += tv;
@@ -166,8 +173,8 @@ __global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, 
     *n_touched = trun;
   }
   __syncthreads();
-  s = part[tid];
-  ts = tpart[tid];
+  s = part[wave] + is - s;
+  ts = tpart[wave] + its - ts;
   for (int e = e0; e < e1; ++e) {
     off[e] = s;
     offsets[e] = s;

@@ -29,7 +29,7 @@ def _route_given_logits(L, wl, tokens, case):
 
 
 @pytest.mark.parametrize("E,k,B", [(16, 3, 1), (64, 3, 16), (64, 3, 256), (8, 2, 4096),
-                                   (896, 16, 16), (5, 5, 7)])
+                                   (896, 16, 16), (5, 5, 7), (3000, 8, 33)])
 def test_union_matches_oracle(E, k, B):
     import torch
     import routed_expert_ffn_route_amd as M
