@@ -292,6 +292,12 @@ hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
   hipLaunchKernelGGL(tn_kernel<false>, grid, dim3(kWaves * 64), tn_lds_bytes(), s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_part_combine(part, y, B, k, I, s);
+}
+
+hipError_t launch_part_combine(const float* part, float* y, int B, int k, int I,
+                               hipStream_t s) {
+  if (I % 4 != 0) return hipErrorInvalidValue;
   const size_t n = (size_t)B * (I / 4);
   int g = (int)((n + 255) / 256);
   g = g > 4096 ? 4096 : g;

@@ -81,8 +81,23 @@ hipError_t launch_linear_gemv(const void* M, const float* x, const float* w,
                               const uint8_t* zrow, float* y, int H, int I, int k, int B,
                               int workgroups, hipStream_t s);
 
+// Linear experts at batches of up to 256 / k tokens on VALU, each touched expert against
+// its own tokens only (passes of up to four tokens): partial rows per (token, choice)
+// [B*k][I] in `part`, then launch_part_combine into y [B][I].  `zrow` is zeroed memory of
+// at least H * 4 bytes.  Returns hipErrorInvalidValue outside linear_pass_fits.
+bool linear_pass_fits(int H, int I, int B, int k);
+hipError_t launch_linear_pass(const void* M, const float* x, const float* w,
+                              const int32_t* n_touched, const int32_t* touched,
+                              const int32_t* offsets, const int32_t* slots,
+                              const uint8_t* zrow, float* part, float* y, int H, int I, int k,
+                              int B, int workgroups, hipStream_t s);
+
+// y[b] = sum over i < k, in order, of part[b*k + i] (rows of I floats; I % 4 == 0).
+hipError_t launch_part_combine(const float* part, float* y, int B, int k, int I,
+                               hipStream_t s);
+
 // Linear experts for larger batches: one register-blocked MFMA tile per (touched expert,
-// 128 output rows) with the tokens' x staged in LDS, partial rows per (token, choice)
+// 256 output rows) with the tokens' x staged in LDS, partial rows per (token, choice)
 // [B*k][I] in `part`, then a combine in routing order into y [B][I].
 hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
                                const int32_t* n_touched, const int32_t* touched,

@@ -184,6 +184,187 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
   }
 }
 
+// Batches of five to 31 tokens.  Computing every token against every touched row (as above)
+// would cost B multiply-adds per weight for about B * k / n_touched tokens that use it, so
+// here each touched expert is paired with its own tokens only: a *pass* is (expert, up to
+// four of its tokens), and an expert with more tokens takes several passes (rare at these
+// batches: 1.4 tokens per touched expert at B = 16, k = 3, E = 64).  The (pass, row) items
+// are laid out pass-major and cut into contiguous ranges, one per workgroup, so a team
+// changes pass once or twice per launch and keeps its passes' x in registers in between.
+// A workgroup no longer owns whole output rows, so each item writes w * dot into the partial
+// row of its (token, choice) -- each written exactly once -- and a second kernel adds a
+// token's k partials in routing order.
+constexpr int kPassTok = 4;     // tokens per pass
+constexpr int kMaxPass = 256;   // passes per launch (B * k <= 256)
+constexpr int kPassRows = 4;    // rows per team and batch (I % kPassRows == 0)
+
+struct PassArgs {
+  const void* M;             // [E][I][H] bf16
+  const float* x;            // [B][H]
+  const float* w;            // [B][k]
+  const int32_t* n_touched;  // [1]
+  const int32_t* touched;    // [E]
+  const int32_t* offsets;    // [E+1]
+  const int32_t* slots;      // [B*k]
+  const uint8_t* zrow;       // zeroed bytes, at least H * 4
+  float* part;               // [B*k][I]
+  int H, I, k, B;
+  int tsz;                   // threads per team
+};
+
+__global__ __launch_bounds__(1024) void gemv_pass_kernel(PassArgs a) {
+  using F = Fmt<DT::BF16>;
+  constexpr int C = kPassRows;
+  constexpr int NT = kPassTok;
+  constexpr int NP = C * NT;
+  static_assert(NP <= kMaxNP, "reduction width");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  Ctx c;
+  c.tid = threadIdx.x;
+  c.nthreads = blockDim.x;
+  set_teams(c, a.tsz);
+  c.lane = c.tid & (kWave - 1);
+  c.P = gridDim.x;
+  c.wg = blockIdx.x;
+  c.H = a.H;
+  c.nch = a.H / 8;
+  c.red = reinterpret_cast<float*>(smem);
+  c.red_stride = (c.nthreads / kWave) * kMaxNP;
+  c.parity = 0;
+  c.epoch = 0;
+  c.zrow = a.zrow;
+  int* s_pe = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [kMaxPass] expert of pass
+  int* s_ps = s_pe + kMaxPass;                                   // [kMaxPass][NT] slot or -1
+  int* s_np = s_ps + kMaxPass * NT;                              // [1] pass count
+
+  // The passes, in touched-expert order: wave 0 scans the per-expert pass counts
+  // (ceil(tokens / NT)) 64 experts at a time.
+  if (c.tid < kWave) {
+    const int nt = *a.n_touched;
+    int carry = 0;
+    for (int i0 = 0; i0 < nt; i0 += kWave) {
+      const int i = i0 + c.lane;
+      int e = 0, o = 0, n = 0;
+      if (i < nt) {
+        e = a.touched[i];
+        o = a.offsets[e];
+        n = a.offsets[e + 1] - o;
+      }
+      const int np = (n + NT - 1) / NT;
+      int inc = np;
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_up(inc, d, kWave);
+        if (c.lane >= d) inc += t;
+      }
+      const int p0 = carry + inc - np;
+      for (int q = 0; q < np; ++q) {
+        const int p = p0 + q;
+        if (p < kMaxPass) {
+          s_pe[p] = e;
+#pragma unroll
+          for (int u = 0; u < NT; ++u) s_ps[p * NT + u] = q * NT + u < n ? a.slots[o + q * NT + u] : -1;
+        }
+      }
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+    if (c.lane == 0) *s_np = min(carry, kMaxPass);
+  }
+  __syncthreads();
+  const int npass = *s_np;
+
+  // Items are chunks of C consecutive rows of one pass: chunk q = pass * IC + row / C.
+  // Workgroup r takes chunks [q0, q1); in batch b, team t takes chunk q0 + b * nteams + t.
+  const int IC = a.I / C;
+  const long long nchunks = (long long)npass * IC;
+  const int q0 = (int)(nchunks * c.wg / c.P), q1 = (int)(nchunks * (c.wg + 1) / c.P);
+  const int nb = (q1 - q0 + c.nteams - 1) / c.nteams;
+  const uint32_t row_bytes = (uint32_t)a.H * 2u;
+  const int ch = c.t < c.nch ? c.t : c.nch - 1;
+  // walk state of this team's next chunk (incremental: no division per batch)
+  int f_q = q0 + c.team;
+  int f_p = f_q / IC, f_j = f_q - f_p * IC;
+  auto pass_base = [&](int p) -> const uint8_t* {
+    const int e = __builtin_amdgcn_readfirstlane(s_pe[p < npass ? p : 0]);
+    return reinterpret_cast<const uint8_t*>(a.M) + (size_t)e * a.I * row_bytes;
+  };
+  const uint8_t* base = pass_base(f_p);
+  struct Stage {
+    F::Raw r[C];
+    int p;    // pass, -1 past the range
+    int row;  // first row
+  };
+  auto fill = [&](Stage& st) {
+    const bool live = f_q < q1;
+    const uint8_t* rp = base + (uint32_t)(f_j * C) * row_bytes;
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+      st.r[q] = F::load_g(uniform_ptr(live ? rp : c.zrow), nullptr, ch);
+      rp += row_bytes;
+    }
+    st.p = live ? f_p : -1;
+    st.row = f_j * C;
+    f_q += c.nteams;
+    f_j += c.nteams;
+    bool moved = false;
+    while (f_j >= IC) {
+      f_j -= IC;
+      ++f_p;
+      moved = true;
+    }
+    if (moved) base = pass_base(f_p);
+  };
+  // x of the pass in registers (zero for the empty token places)
+  float xv[NT][8];
+  int x_pass = -1;
+  auto compute = [&](const Stage& st) {
+    if (st.p >= 0 && st.p != x_pass) {
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const int slot = s_ps[st.p * NT + u];
+        const float* xp = slot >= 0 ? a.x + (size_t)(slot / a.k) * a.H
+                                    : reinterpret_cast<const float*>(c.zrow);
+        load_x<8, 1>(xp, c, xv[u]);
+      }
+      x_pass = st.p;
+    }
+    float acc[NP];
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+      float v[8];
+      F::decode(st.r[q], v);
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(v[i], xv[u][i], s);
+        acc[q * NT + u] = s;
+      }
+    }
+    const float tot = wave_multi_sum<NP>(acc, c.lane);
+    float* red = c.next_red();
+    if (c.lane < NP) red[(c.team * c.wpt + c.wit) * NP + c.lane] = tot;
+    __syncthreads();
+    // lane l of the team holds the team total of value l: thread q*NT + u finishes
+    // (row q, token place u)
+    const float v = team_totals<NP>(red, c);
+    if (c.t < NP && st.p >= 0) {
+      const int q = c.t / NT, u = c.t - q * NT;
+      const int slot = s_ps[st.p * NT + u];
+      if (slot >= 0) a.part[(size_t)slot * a.I + st.row + q] = a.w[slot] * v;
+    }
+  };
+  Stage A, B;
+  fill(A);
+  int b = 0;
+  for (; b + 1 < nb; b += 2) {
+    fill(B);
+    compute(A);
+    fill(A);
+    compute(B);
+  }
+  if (b < nb) compute(A);
+}
+
 int gemv_team(int H) {
   const int nch = H / 8;
   int t = 64;
@@ -196,6 +377,27 @@ int gemv_team(int H) {
 bool linear_gemv_fits(int H, int I, int B) {
   return B >= 1 && B <= kGemvMaxBatch && H % 8 == 0 && H / 8 <= 1024 &&
          (unsigned long long)I * H * 2 < (1ull << 32);
+}
+
+bool linear_pass_fits(int H, int I, int B, int k) {
+  return B >= 1 && (long long)B * k <= kMaxPass && H % 8 == 0 && H / 8 <= 1024 &&
+         I % kPassRows == 0 && (unsigned long long)I * H * 2 < (1ull << 32);
+}
+
+hipError_t launch_linear_pass(const void* M, const float* x, const float* w,
+                              const int32_t* n_touched, const int32_t* touched,
+                              const int32_t* offsets, const int32_t* slots,
+                              const uint8_t* zrow, float* part, float* y, int H, int I, int k,
+                              int B, int workgroups, hipStream_t s) {
+  if (!linear_pass_fits(H, I, B, k) || workgroups < 1) return hipErrorInvalidValue;
+  PassArgs a{M, x, w, n_touched, touched, offsets, slots, zrow, part, H, I, k, B, 0};
+  a.tsz = gemv_team(H);
+  const int threads = 1024;
+  const int lds = 2 * (threads / kWave) * kMaxNP * 4 + kMaxPass * 4 + kMaxPass * kPassTok * 4 + 16;
+  hipLaunchKernelGGL(gemv_pass_kernel, dim3(workgroups), dim3(threads), lds, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_part_combine(part, y, B, k, I, s);
 }
 
 hipError_t launch_linear_gemv(const void* M, const float* x, const float* w,

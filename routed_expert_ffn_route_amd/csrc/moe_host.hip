@@ -134,9 +134,9 @@ Layout layout_of(const moe_layer_desc* d) {
   const size_t pairs = batched_swiglu ? B * k + (size_t)d->n_shared * B : 0;
   const size_t ia = (size_t)(d->inter > d->shared_inter ? d->inter : d->shared_inter);
   L.act = take(pairs * ia * 4);
-  // partial outputs: batched SwiGLU [kDownRowSlices][pairs][H]; linear experts at larger
-  // batches [B*k][I]
-  const size_t lin_part = d->kind == MOE_EXPERT_LINEAR && B >= kLinearTiledMinBatch
+  // partial outputs: batched SwiGLU [kDownRowSlices][pairs][H]; linear experts above
+  // kGemvMaxBatch tokens [B*k][I]
+  const size_t lin_part = d->kind == MOE_EXPERT_LINEAR && B > kGemvMaxBatch
                               ? B * k * (size_t)d->inter * 4
                               : 0;
   const size_t sw_part = kDownRowSlices * pairs * (size_t)d->hidden * 4;
@@ -496,6 +496,10 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
       e = launch_linear_gemv(layer->w.linear, x, rw, n_t, touched, offsets, slots,
                              layer->at<uint8_t>(layer->L.zrow), y, d.hidden, d.inter,
                              d.top_k, B, layer->workgroups, s);
+    else if (e == hipSuccess && linear_pass_fits(d.hidden, d.inter, B, d.top_k))
+      e = launch_linear_pass(layer->w.linear, x, rw, n_t, touched, offsets, slots,
+                             layer->at<uint8_t>(layer->L.zrow), layer->at<float>(layer->L.part),
+                             y, d.hidden, d.inter, d.top_k, B, layer->workgroups, s);
     else if (e == hipSuccess)
       e = launch_linear(layer->w.linear, x, rw, n_t, touched, offsets, slots,
                         layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl), y,

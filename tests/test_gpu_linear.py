@@ -54,7 +54,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 40, 300, 600])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 16, 31, 40, 300, 600])
 @pytest.mark.parametrize("wl", SMALL, ids=lambda w: f"H{w.H}E{w.E}k{w.k}I{w.I}")
 def test_linear_small(wl, B):
     import torch
