@@ -139,7 +139,8 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
  * 501B/23B post, section 2).  ids [B][k] with distinct experts per token, 0 <= id < E.
  * Writes n_touched [1], touched [E] (ascending; first n_touched valid), offsets [E+1]
  * (prefix sum of per-expert counts) and slots [B*k] (flat b*k+i grouped by expert,
- * ascending within an expert).  One workgroup; needs E*ceil(B/32)*4 + 8*E <= 96 KiB. */
+ * ascending within an expert).  One workgroup; needs E*(ceil(B/32) | 1)*8 + 8*E bytes of
+ * LDS, at most 144 KiB (else MOE_ERR_UNSUPPORTED). */
 moe_status moe_union_experts(const int32_t* ids, int32_t B, int32_t k, int32_t E,
                              int32_t* n_touched, int32_t* touched, int32_t* offsets,
                              int32_t* slots, void* stream);

@@ -61,6 +61,7 @@ hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touc
                         int32_t* touched, int32_t* offsets, int32_t* slots, Ctrl* ctrl,
                         hipStream_t s);
 int union_lds_bytes(int B, int E);
+constexpr int kUnionMaxLds = 144 * 1024;  // dynamic LDS the union kernel may use
 
 // Linear experts (one [I][H] bf16 matrix each) for a batch: x is split into bf16 hi/lo
 // (xh, xl workspace [B][H]) and the touched experts are applied with MFMA; y [B][I].

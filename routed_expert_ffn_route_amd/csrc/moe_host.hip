@@ -394,8 +394,8 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     if (et == DT::F32 || st != DT::BF16)
       return fail(MOE_ERR_UNSUPPORTED, "batched SwiGLU needs BF16 or MXFP4 experts and BF16 "
                                        "shared experts");
-    if (union_lds_bytes(B, d.n_experts) > 96 * 1024)
-      return fail(MOE_ERR_UNSUPPORTED, "E*ceil(B/32)*4 + 8E exceeds the union LDS budget");
+    if (union_lds_bytes(B, d.n_experts) > kUnionMaxLds)
+      return fail(MOE_ERR_UNSUPPORTED, "E*(ceil(B/32)|1)*8 + 8E bytes exceed the union LDS budget (144 KiB)");
     const int32_t* rid = ids;
     const float* rw = w;
     hipError_t e = hipSuccess;
@@ -459,8 +459,8 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     return ok();
   }
   if (d.kind == MOE_EXPERT_LINEAR) {
-    if (union_lds_bytes(B, d.n_experts) > 96 * 1024)
-      return fail(MOE_ERR_UNSUPPORTED, "E*ceil(B/32)*4 + 8E exceeds the union LDS budget");
+    if (union_lds_bytes(B, d.n_experts) > kUnionMaxLds)
+      return fail(MOE_ERR_UNSUPPORTED, "E*(ceil(B/32)|1)*8 + 8E bytes exceed the union LDS budget (144 KiB)");
     const int32_t* rid = ids;
     const float* rw = w;
     hipError_t e = hipSuccess;
@@ -549,8 +549,8 @@ moe_status moe_union_experts(const int32_t* ids, int32_t B, int32_t k, int32_t E
     return fail(MOE_ERR_ARG, "null pointer");
   if (E < 1 || E > 4096 || k < 1 || k > E || B < 1 || B > 4096)
     return fail(MOE_ERR_ARG, "sizes out of range");
-  if (union_lds_bytes(B, E) > 96 * 1024)
-    return fail(MOE_ERR_UNSUPPORTED, "E*ceil(B/32)*4 + 8E exceeds the 96 KiB LDS budget");
+  if (union_lds_bytes(B, E) > kUnionMaxLds)
+    return fail(MOE_ERR_UNSUPPORTED, "E*(ceil(B/32)|1)*8 + 8E bytes exceed the union LDS budget (144 KiB)");
   hipError_t e = launch_union(ids, B, k, E, n_touched, touched, offsets, slots, nullptr,
                               reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "union launch");

@@ -109,20 +109,24 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* logits, float* l
 
 // Union of the batch's experts in one workgroup: a bitmap of tokens per expert in LDS
 // (LDS atomics give a schedule-independent result), per-expert counts, a prefix sum, and
-// each (token, slot) placed by the rank of its token among the expert's tokens.
+// each (token, slot) placed by the rank of its token among the expert's tokens.  The
+// bitmap rows are padded to an odd word count, so that threads reading the same word of
+// different experts hit different banks, and the count pass also keeps each row's running
+// popcount per word, so a rank is two reads however large the batch.
 __global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, int k, int E,
                                                      int32_t* n_touched, int32_t* touched,
                                                      int32_t* offsets, int32_t* slots,
                                                      Ctrl* ctrl) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int W = (B + 31) / 32;
-  uint32_t* bits = reinterpret_cast<uint32_t*>(smem);          // [E][W]
-  int32_t* cnt = reinterpret_cast<int32_t*>(bits + (size_t)E * W);  // [E]
+  const int W = (B + 31) / 32, Wp = W | 1;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(smem);                // [E][Wp]
+  int32_t* pre = reinterpret_cast<int32_t*>(bits + (size_t)E * Wp);  // [E][Wp] set bits before word q
+  int32_t* cnt = pre + (size_t)E * Wp;                               // [E]
   int32_t* off = cnt + E;                                      // [E+1]
   __shared__ int32_t part[1024 / kWave];
   __shared__ int32_t tpart[1024 / kWave];
   const int tid = threadIdx.x, nt = blockDim.x;
-  for (int i = tid; i < E * W; i += nt) bits[i] = 0u;
+  for (int i = tid; i < E * Wp; i += nt) bits[i] = 0u;
   __syncthreads();
   for (int f = tid; f < B * k; f += nt) {
     const int e = ids[f], b = f / k;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, 
                               __HIP_MEMORY_SCOPE_AGENT);
       continue;
     }
-    const uint32_t old = atomicOr(&bits[e * W + b / 32], 1u << (b % 32));
+    const uint32_t old = atomicOr(&bits[e * Wp + b / 32], 1u << (b % 32));
     if ((old >> (b % 32)) & 1u) {
       if (ctrl)
         __hip_atomic_fetch_or(&ctrl->err, kErrBadId, __ATOMIC_RELAXED,
@@ -142,7 +146,10 @@ __global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, 
   __syncthreads();
   for (int e = tid; e < E; e += nt) {
     int c = 0;
-    for (int q = 0; q < W; ++q) c += __popc(bits[e * W + q]);
+    for (int q = 0; q < W; ++q) {
+      pre[e * Wp + q] = c;
+      c += __popc(bits[e * Wp + q]);
+    }
     cnt[e] = c;
   }
   __syncthreads();
@@ -185,9 +192,8 @@ __global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, 
   for (int f = tid; f < B * k; f += nt) {
     const int e = ids[f], b = f / k;
     if (e < 0 || e >= E) continue;
-    const uint32_t* be = bits + e * W;
-    int rank = __popc(be[b / 32] & ((1u << (b % 32)) - 1u));
-    for (int q = 0; q < b / 32; ++q) rank += __popc(be[q]);
+    const int q = e * Wp + b / 32;
+    const int rank = pre[q] + __popc(bits[q] & ((1u << (b % 32)) - 1u));
     slots[off[e] + rank] = f;
   }
 }
@@ -271,7 +277,7 @@ hipError_t launch_route(const RouteArgs& a, DT rt, hipStream_t s) {
 }
 
 int union_lds_bytes(int B, int E) {
-  return E * ((B + 31) / 32) * 4 + (2 * E + 1) * 4;
+  return E * (((B + 31) / 32) | 1) * 8 + (2 * E + 1) * 4;
 }
 
 hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touched,
@@ -281,9 +287,9 @@ hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touc
   static int lds_set = 0;
   if (lds > lds_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(union_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kUnionMaxLds);
     if (e != hipSuccess) return e;
-    lds_set = 96 * 1024;
+    lds_set = kUnionMaxLds;
   }
   hipLaunchKernelGGL(union_kernel, dim3(1), dim3(1024), lds, s, ids, B, k, E, n_touched,
                      touched, offsets, slots, ctrl);
