@@ -220,13 +220,21 @@ __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
   lds_i32* tok_b = (lds_i32*)tok_b_;
   lds_i32* tok_slot = (lds_i32*)tok_slot_;
   lds_f32* tok_w = (lds_f32*)tok_w_;
-  const int t = blockIdx.y;
-  if (t >= *a.n_touched || blockIdx.x * kRows >= a.I) return;  // whole workgroup leaves
+  // XCD-aware order: consecutive workgroups are dealt round-robin to the 8 XCDs, so
+  // workgroup L runs on XCD L % 8.  Numbered this way, XCD x takes touched experts x, x + 8,
+  // ... one at a time with all of an expert's row blocks together: the blocks share the
+  // expert's x chunks, which then come from that XCD's L2 (the grid's y is a multiple of 8).
+  const int L = blockIdx.y * gridDim.x + blockIdx.x;
+  const int sq = L / 8;
+  const int bx = sq % gridDim.x;
+  const int t = (sq / gridDim.x) * 8 + L % 8;
+  // (a whole workgroup leaves)
+  if (t >= a.slots_max || t >= *a.n_touched || bx * kRows >= a.I) return;
   const int e = a.touched[t];
   const int s0 = a.offsets[e], ne = a.offsets[e + 1] - s0;
   if ((ne <= 32) != SMALL) return;  // the other kernel's expert
   const uint8_t* Me = a.M + (size_t)e * a.I * a.H * 2;
-  const int rbase = blockIdx.x * kRows + (threadIdx.x >> 6) * kRowsW;
+  const int rbase = bx * kRows + (threadIdx.x >> 6) * kRowsW;
   for (int p0 = 0; p0 < ne; p0 += kTokMax) {
     const int np = min(kTokMax, ne - p0);
     __syncthreads();  // the previous pass is done with the token list and x buffers
@@ -285,7 +293,7 @@ hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
   }
   TnArgs a{reinterpret_cast<const uint8_t*>(M), xh, xl, w, n_touched, touched, offsets, slots,
            part, H, I, k, B * k < E ? B * k : E};
-  const dim3 grid((I + kRows - 1) / kRows, a.slots_max);
+  const dim3 grid((I + kRows - 1) / kRows, (a.slots_max + 7) / 8 * 8);
   hipLaunchKernelGGL(tn_kernel<true>, grid, dim3(kWaves * 64), tn_lds_bytes(), s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
