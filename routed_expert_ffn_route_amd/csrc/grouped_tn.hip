@@ -16,14 +16,24 @@
 // expert's output rows -- and a combine kernel sums a token's k partials in routing order:
 // every output element has one writer and a fixed order.
 //
-// MFMA v_mfma_f32_16x16x32_bf16 (lane l: A[l%16][8(l/16)..+8], B[8(l/16)..+8][l%16],
-// D[4(l/16)..+4][l%16]); A = 16 weight rows, B = 16 tokens; x enters as bf16 hi + lo.
+// MFMA 16x16x32 (lane l: A[l%16][8(l/16)..+8], B[8(l/16)..+8][l%16], D[4(l/16)..+4][l%16]);
+// A = 16 weight rows, B = 16 tokens.  Two operand forms:
+// * up to 32 tokens per expert (a weight stream): bf16, x entering as bf16 hi + lo (two
+//   MFMAs per product, ~16 significant bits of x);
+// * more tokens (where the MFMAs and the staged x bound the kernel): f16, one MFMA per
+//   product.  x is f16 scaled per token by a power of two chosen from the token's largest
+//   |x| (largest magnitude in [2^14, 2^15)), so its rounding is 2^-11 relative to that
+//   magnitude, and the scale is undone on the fp32 result.  A bf16 weight is exactly an f16
+//   when 2^-14 <= |w| < 65504 (8 significant bits fit in 11); smaller ones keep their f16
+//   subnormal bits (an absolute error below 2^-24).  This halves the MFMAs and the staged
+//   x bytes: the 2048-token step went from 2.61 to 2.04 ms.
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 8;
 constexpr int kRowsW = 32;                 // rows per wave (2 MFMA row tiles)
@@ -41,8 +51,10 @@ constexpr int kBufElems = kXElems + kTokMax * kPad;  // one staged array (max ov
 
 struct TnArgs {
   const uint8_t* M;          // [E][I][H] bf16
-  const uint16_t* xh;        // [B][H]
-  const uint16_t* xl;
+  const uint16_t* xh;        // [B][H] bf16 hi of x
+  const uint16_t* xl;        // [B][H] bf16 lo of x
+  const uint16_t* x16;       // [B][H] f16 bits of x * 2^-e_b
+  const float* xsc;          // [B] 2^e_b
   const float* w;            // [B][k]
   const int32_t* n_touched;
   const int32_t* touched;
@@ -52,9 +64,12 @@ struct TnArgs {
   int H, I, k, slots_max;
 };
 
+// The operand form for NT token tiles (see the header).
+template <int NT> constexpr bool use_f16() { return NT >= 4; }
+
 // x of tokens tok_b[0..16NT) (padded with the first token), K [kc, kc + kx): 16NT tokens x
-// kx/8 pieces of 16 bytes = kXElems / 8 pieces, for hi and for lo; thread j holds pieces
-// j, j + 256, ... (4 of them).
+// kx/8 pieces of 16 bytes = kXElems / 8 pieces, per staged array (hi and lo, or the f16
+// x); thread j holds pieces j, j + 512, ...
 constexpr int kPP = kXElems / 8 / (kWaves * 64);
 struct XRegs {
   u32x4 h[kPP], l[kPP];
@@ -70,8 +85,12 @@ __device__ __forceinline__ void x_load(XRegs& xr, const TnArgs& a, const lds_i32
     const int tok = p / PR, q = p % PR;
     const int b = tok_b[tok < np ? tok : 0];
     const size_t off = (size_t)b * a.H + kc + 8 * q;
-    xr.h[i] = *reinterpret_cast<const u32x4*>(a.xh + off);
-    xr.l[i] = *reinterpret_cast<const u32x4*>(a.xl + off);
+    if constexpr (use_f16<NT>()) {
+      xr.h[i] = *reinterpret_cast<const u32x4*>(a.x16 + off);
+    } else {
+      xr.h[i] = *reinterpret_cast<const u32x4*>(a.xh + off);
+      xr.l[i] = *reinterpret_cast<const u32x4*>(a.xl + off);
+    }
   }
 }
 
@@ -83,7 +102,7 @@ __device__ __forceinline__ void x_store(const XRegs& xr, lds_u16* xs_h, lds_u16*
     const int p = threadIdx.x + i * kWaves * 64;
     const int tok = p / PR, q = p % PR;
     lds_st128(xs_h + tok * ldx<NT>() + 8 * q, xr.h[i]);
-    lds_st128(xs_l + tok * ldx<NT>() + 8 * q, xr.l[i]);
+    if constexpr (!use_f16<NT>()) lds_st128(xs_l + tok * ldx<NT>() + 8 * q, xr.l[i]);
   }
 }
 
@@ -101,34 +120,60 @@ __device__ __forceinline__ void a_load(ARegs& ar, const uint8_t* const (&rp)[2],
           reinterpret_cast<const u32x4*>(rp[r] + (size_t)(kc + 32 * s + 8 * g) * 2));
 }
 
-// MFMAs of one 64-wide K step against the staged x at column offset k0: all hi products,
-// then all lo products, so that an accumulator's next MFMA is 2 NT issues away.
+// bf16 weight pairs (one dword) -> f16 pairs: exact for normal f16 magnitudes.
+// (The conversion's rounding mode is immaterial where it is exact; v_cvt_pkrtz packs the
+// pair in one instruction.)
+__device__ __forceinline__ f16x8 w_f16(const u32x4& v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[i] << 16),
+                                                         __uint_as_float(v[i] & 0xFFFF0000u)));
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// MFMAs of one 64-wide K step against the staged x at column offset k0.  bf16 form: all
+// hi products, then all lo products, so that an accumulator's next MFMA is 2 NT issues
+// away; f16 form: NT >= 4, so they are 2 NT apart anyway.
 template <int NT>
 __device__ __forceinline__ void step_mfma(const ARegs& ar, const lds_u16* xs_h,
                                           const lds_u16* xs_l, int k0, int l16, int g,
                                           f32x4 (&acc)[2][NT]) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const bf16x8 a0 = __builtin_bit_cast(bf16x8, ar.f[0][s]);
-    const bf16x8 a1 = __builtin_bit_cast(bf16x8, ar.f[1][s]);
-    u32x4 bh[NT], bl[NT];
+    u32x4 bh[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int o = (16 * t + l16) * ldx<NT>() + k0 + 32 * s + 8 * g;
-      bh[t] = lds_ld128(xs_h + o);
-      bl[t] = lds_ld128(xs_l + o);
-    }
+    for (int t = 0; t < NT; ++t)
+      bh[t] = lds_ld128(xs_h + (16 * t + l16) * ldx<NT>() + k0 + 32 * s + 8 * g);
+    if constexpr (use_f16<NT>()) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, bh[t]);
-      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][t], 0, 0, 0);
-      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][t], 0, 0, 0);
-    }
+      for (int r = 0; r < 2; ++r) {
+        const f16x8 ar16 = w_f16(ar.f[r][s]);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, bl[t]);
-      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][t], 0, 0, 0);
-      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][t], 0, 0, 0);
+        for (int t = 0; t < NT; ++t)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              ar16, __builtin_bit_cast(f16x8, bh[t]), acc[r][t], 0, 0, 0);
+      }
+    } else {
+      u32x4 bl[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        bl[t] = lds_ld128(xs_l + (16 * t + l16) * ldx<NT>() + k0 + 32 * s + 8 * g);
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, ar.f[0][s]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, ar.f[1][s]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, bh[t]);
+        acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][t], 0, 0, 0);
+        acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, bl[t]);
+        acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][t], 0, 0, 0);
+        acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][t], 0, 0, 0);
+      }
     }
   }
 }
@@ -185,7 +230,7 @@ __device__ __forceinline__ void tn_pass(const TnArgs& a, const uint8_t* Me, int 
       }
     }
   }
-  // partial rows: w times the expert's output, for each token of the pass
+  // partial rows: w (times the token's x scale) times the expert's output, per token
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int tc = 16 * t + l16;
@@ -213,7 +258,7 @@ __device__ __forceinline__ void tn_pass(const TnArgs& a, const uint8_t* Me, int 
 template <bool SMALL>
 __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  lds_u16* xs = (lds_u16*)smem;  // [2 buffers][hi, lo][kBufElems]
+  lds_u16* xs = (lds_u16*)smem;  // [2 buffers][hi, lo][kBufElems] (f16 form: hi only)
   __shared__ int tok_b_[kTokMax];
   __shared__ int tok_slot_[kTokMax];
   __shared__ float tok_w_[kTokMax];
@@ -242,7 +287,7 @@ __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
       const int slot = a.slots[s0 + p0 + i];
       tok_b[i] = slot / a.k;
       tok_slot[i] = slot;
-      tok_w[i] = a.w[slot];
+      tok_w[i] = SMALL ? a.w[slot] : a.w[slot] * a.xsc[slot / a.k];
     }
     __syncthreads();
     const int nt = (np + 15) / 16;
@@ -251,7 +296,7 @@ __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
       else tn_pass<2, 4>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
     } else {
       if (nt <= 4) tn_pass<4, 4>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
-      else tn_pass<8, 4>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
+      else tn_pass<8, 2>(a, Me, rbase, tok_b, tok_slot, tok_w, np, xs);
     }
   }
 }
@@ -270,6 +315,39 @@ __global__ __launch_bounds__(256) void tn_combine_kernel(const float* part, floa
   }
 }
 
+// Both operand forms of x, one workgroup per token: bf16 hi = RNE(x), lo = RNE(x - hi);
+// and f16 of x * 2^-e_b, e_b chosen from the token's largest |x| (largest magnitude in
+// [2^14, 2^15); e_b = 0 for an all-zero token, clamped to +-100), with 2^e_b.
+__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__global__ __launch_bounds__(256) void x_prep_kernel(const float* x, int H, uint16_t* xh,
+                                                     uint16_t* xl, uint16_t* x16, float* xsc) {
+  __shared__ float red[4];
+  const float* xb = x + (size_t)blockIdx.x * H;
+  float mx = 0.0f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) mx = fmaxf(mx, fabsf(xb[i]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int e = mx > 0.0f ? (int)((__float_as_uint(mx) >> 23) & 0xFF) - 127 - 14 : 0;
+  e = e < -100 ? -100 : e > 100 ? 100 : e;
+  const float inv = ldexpf(1.0f, -e);
+  const size_t o = (size_t)blockIdx.x * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    const float f = xb[i];
+    const uint16_t h = bf16_bits_rne(f);
+    xh[o + i] = h;
+    xl[o + i] = bf16_bits_rne(f - __uint_as_float((uint32_t)h << 16));
+    x16[o + i] = __builtin_bit_cast(uint16_t, (_Float16)(f * inv));
+  }
+  if (threadIdx.x == 0) xsc[blockIdx.x] = ldexpf(1.0f, e);
+}
+
 }  // namespace
 
 int tn_lds_bytes() { return 2 * 2 * kBufElems * 2; }
@@ -277,9 +355,10 @@ int tn_lds_bytes() { return 2 * 2 * kBufElems * 2; }
 hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
                                const int32_t* n_touched, const int32_t* touched,
                                const int32_t* offsets, const int32_t* slots, uint16_t* xh,
-                               uint16_t* xl, float* part, float* y, int H, int I, int E, int k,
-                               int B, hipStream_t s) {
-  hipError_t e = launch_split_x(x, (size_t)B * H, xh, xl, s);
+                               uint16_t* xl, uint16_t* x16, float* xsc, float* part, float* y,
+                               int H, int I, int E, int k, int B, hipStream_t s) {
+  hipLaunchKernelGGL(x_prep_kernel, dim3(B), dim3(256), 0, s, x, H, xh, xl, x16, xsc);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static bool lds_set = false;
   if (!lds_set) {
@@ -291,8 +370,8 @@ hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
     if (e != hipSuccess) return e;
     lds_set = true;
   }
-  TnArgs a{reinterpret_cast<const uint8_t*>(M), xh, xl, w, n_touched, touched, offsets, slots,
-           part, H, I, k, B * k < E ? B * k : E};
+  TnArgs a{reinterpret_cast<const uint8_t*>(M), xh, xl, x16, xsc, w, n_touched, touched,
+           offsets, slots, part, H, I, k, B * k < E ? B * k : E};
   const dim3 grid((I + kRows - 1) / kRows, (a.slots_max + 7) / 8 * 8);
   hipLaunchKernelGGL(tn_kernel<true>, grid, dim3(kWaves * 64), tn_lds_bytes(), s, a);
   e = hipGetLastError();

@@ -97,14 +97,15 @@ hipError_t launch_linear_pass(const void* M, const float* x, const float* w,
 hipError_t launch_part_combine(const float* part, float* y, int B, int k, int I,
                                hipStream_t s);
 
-// Linear experts for larger batches: one register-blocked MFMA tile per (touched expert,
-// 256 output rows) with the tokens' x staged in LDS, partial rows per (token, choice)
+// Linear experts for larger batches: x in both MFMA operand forms (bf16 hi/lo in xh, xl;
+// scaled f16 in x16 with per-token scales xsc, workspace [B][H] each and [B]), then one
+// register-blocked MFMA tile per (touched expert, 256 output rows) with the tokens' x staged in LDS, partial rows per (token, choice)
 // [B*k][I] in `part`, then a combine in routing order into y [B][I].
 hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
                                const int32_t* n_touched, const int32_t* touched,
                                const int32_t* offsets, const int32_t* slots, uint16_t* xh,
-                               uint16_t* xl, float* part, float* y, int H, int I, int E, int k,
-                               int B, hipStream_t s);
+                               uint16_t* xl, uint16_t* x16, float* xsc, float* part, float* y,
+                               int H, int I, int E, int k, int B, hipStream_t s);
 
 // x [n] fp32 -> bf16 hi, lo with hi + lo ~= x (the MFMA paths' activation operand).
 hipError_t launch_split_x(const float* x, size_t n, uint16_t* xh, uint16_t* xl, hipStream_t s);

@@ -50,7 +50,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, rlog, zrow, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, cs_s, cs_y, xh, xl, act, part, total;
+      union_slots, cs_s, cs_y, xh, xl, x16, xsc, act, part, total;
 };
 
 bool desc_valid(const moe_layer_desc* d, std::string* why) {
@@ -129,6 +129,10 @@ Layout layout_of(const moe_layer_desc* d) {
       d->kind == MOE_EXPERT_LINEAR || batched_swiglu ? B * (size_t)d->hidden * 2 : 0;
   L.xh = take(xs);
   L.xl = take(xs);
+  // linear experts at larger batches: x as scaled f16 and the per-token scales
+  const bool lin_tiled = d->kind == MOE_EXPERT_LINEAR && B >= kLinearTiledMinBatch;
+  L.x16 = take(lin_tiled ? B * (size_t)d->hidden * 2 : 0);
+  L.xsc = take(lin_tiled ? B * (size_t)4 : 0);
   // batched SwiGLU: activations and partial outputs of every (token, choice) and every
   // (shared expert, token)
   const size_t pairs = batched_swiglu ? B * k + (size_t)d->n_shared * B : 0;
@@ -490,6 +494,7 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     if (e == hipSuccess && B >= kLinearTiledMinBatch)
       e = launch_linear_tiled(layer->w.linear, x, rw, n_t, touched, offsets, slots,
                               layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl),
+                              layer->at<uint16_t>(layer->L.x16), layer->at<float>(layer->L.xsc),
                               layer->at<float>(layer->L.part), y, d.hidden, d.inter,
                               d.n_experts, d.top_k, B, s);
     else if (e == hipSuccess && linear_gemv_fits(d.hidden, d.inter, B))
