@@ -15,57 +15,65 @@
 namespace moe {
 namespace {
 
-// Router GEMV for B tokens: one team (256 threads) per router row, the row held in
-// registers and dotted with every token's x; 8 tokens reduced per LDS round.
+// Router GEMV for B tokens: one team (256 threads) per R router rows, held in registers;
+// each x chunk load serves the R rows (x is read from L2 once per R rows, not per row), and
+// R rows x TB tokens are reduced per LDS round.
 template <DT RT, int CPT>
 __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
-  __shared__ float red[2][4][8];
+  constexpr int R = 4, TB = 4, NP = R * TB;
+  __shared__ float red[2][4][NP];
   const int t = threadIdx.x, lane = t & 63, wit = t >> 6;
   const int nch = a.H / 8;
-  for (int e = blockIdx.x; e < a.E; e += gridDim.x) {
-    typename Fmt<RT>::Raw r[CPT];
-    const void* rp = row_ptr<RT>(a.router, (size_t)e, a.H);
+  for (int e0 = blockIdx.x * R; e0 < a.E; e0 += gridDim.x * R) {
+    typename Fmt<RT>::Raw r[R][CPT];
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) {
-      const int ch = t + m * kTeam;
-      if (ch < nch) r[m] = Fmt<RT>::load(rp, nullptr, ch);
-      else __builtin_memset(&r[m], 0, sizeof(r[m]));
+    for (int rr = 0; rr < R; ++rr) {
+      const int e = e0 + rr < a.E ? e0 + rr : a.E - 1;  // rows past E: computed, dropped
+      const void* rp = row_ptr<RT>(a.router, (size_t)e, a.H);
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        const int ch = t + m * kTeam;
+        if (ch < nch) r[rr][m] = Fmt<RT>::load(rp, nullptr, ch);
+        else __builtin_memset(&r[rr][m], 0, sizeof(r[rr][m]));
+      }
     }
-    float w[CPT * 8];
-#pragma unroll
-    for (int m = 0; m < CPT; ++m) Fmt<RT>::decode(r[m], &w[m * 8]);
     int parity = 0;
-    for (int b0 = 0; b0 < a.B; b0 += 8) {
-      float acc[8];
+    for (int b0 = 0; b0 < a.B; b0 += TB) {
+      float acc[NP];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        acc[q] = 0.0f;
+      for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int q = 0; q < TB; ++q) {
         const int b = b0 + q;
-        if (b < a.B) {
-          const float* xb = a.x + (size_t)b * a.H;
+        if (b >= a.B) continue;
+        const float* xb = a.x + (size_t)b * a.H;
 #pragma unroll
-          for (int m = 0; m < CPT; ++m) {
-            const int ch = t + m * kTeam;
-            if (ch < nch) {
-              const f32x4 lo = reinterpret_cast<const f32x4*>(xb)[2 * ch];
-              const f32x4 hi = reinterpret_cast<const f32x4*>(xb)[2 * ch + 1];
-              float s = acc[q];
-              s = fmaf(w[m * 8 + 0], lo.x, s); s = fmaf(w[m * 8 + 1], lo.y, s);
-              s = fmaf(w[m * 8 + 2], lo.z, s); s = fmaf(w[m * 8 + 3], lo.w, s);
-              s = fmaf(w[m * 8 + 4], hi.x, s); s = fmaf(w[m * 8 + 5], hi.y, s);
-              s = fmaf(w[m * 8 + 6], hi.z, s); s = fmaf(w[m * 8 + 7], hi.w, s);
-              acc[q] = s;
-            }
+        for (int m = 0; m < CPT; ++m) {
+          const int ch = t + m * kTeam;
+          if (ch >= nch) continue;
+          const f32x4 lo = reinterpret_cast<const f32x4*>(xb)[2 * ch];
+          const f32x4 hi = reinterpret_cast<const f32x4*>(xb)[2 * ch + 1];
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) {
+            float w[8];
+            Fmt<RT>::decode(r[rr][m], w);
+            float s = acc[rr * TB + q];
+            s = fmaf(w[0], lo.x, s); s = fmaf(w[1], lo.y, s);
+            s = fmaf(w[2], lo.z, s); s = fmaf(w[3], lo.w, s);
+            s = fmaf(w[4], hi.x, s); s = fmaf(w[5], hi.y, s);
+            s = fmaf(w[6], hi.z, s); s = fmaf(w[7], hi.w, s);
+            acc[rr * TB + q] = s;
           }
         }
       }
-      const float tot = wave_multi_sum<8>(acc, lane);
-      if (lane < 8) red[parity][wit][lane] = tot;
+      const float tot = wave_multi_sum<NP>(acc, lane);
+      if (lane < NP) red[parity][wit][lane] = tot;
       __syncthreads();
-      if (t < 8 && b0 + t < a.B) {
-        const float l = red[parity][0][t] + red[parity][1][t] + red[parity][2][t] +
-                        red[parity][3][t];
-        a.logits[(size_t)(b0 + t) * a.E + e] = l;
+      if (t < NP) {
+        const int rr = t / TB, q = t % TB, b = b0 + q, e = e0 + rr;
+        if (b < a.B && e < a.E)
+          a.logits[(size_t)b * a.E + e] =
+              red[parity][0][t] + red[parity][1][t] + red[parity][2][t] + red[parity][3][t];
       }
       parity ^= 1;
     }
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
 }
 
 // Top-k + softmax: one workgroup per token.
-__global__ __launch_bounds__(256) void topk_kernel(const float* logits, float* logits_copy,
+__global__ __launch_bounds__(1024) void topk_kernel(const float* logits, float* logits_copy,
                                                    int E, int k, int B, int32_t* ids,
                                                    float* w) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -234,7 +242,8 @@ int cpt_for(int H) {
 
 template <DT RT>
 hipError_t launch_gemv(const RouteArgs& a, hipStream_t s) {
-  const int grid = a.E < 2048 ? a.E : 2048;
+  const int rows = (a.E + 3) / 4;  // four router rows per workgroup pass
+  const int grid = rows < 2048 ? rows : 2048;
   switch (cpt_for(a.H)) {
     case 1: hipLaunchKernelGGL((router_gemv_kernel<RT, 1>), dim3(grid), dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((router_gemv_kernel<RT, 2>), dim3(grid), dim3(256), 0, s, a); break;
@@ -271,7 +280,7 @@ hipError_t launch_route(const RouteArgs& a, DT rt, hipStream_t s) {
   const int lds = topk_lds_bytes(a.E, a.k);
   const int grid = a.B < 4096 ? a.B : 4096;
   float* copy = (a.logits_in && a.logits) ? a.logits : nullptr;
-  hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(256), lds, s, lsrc, copy, a.E, a.k, a.B,
+  hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(1024), lds, s, lsrc, copy, a.E, a.k, a.B,
                      a.ids, a.w);
   return hipGetLastError();
 }
