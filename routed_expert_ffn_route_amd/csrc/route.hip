@@ -42,26 +42,30 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
       float acc[NP];
 #pragma unroll
       for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
+      // x loads without conditions (tokens past B re-read token B-1 and are dropped;
+      // chunks past the row end re-read the last chunk against zero weights), so that all
+      // of a chunk's token loads are in flight together
 #pragma unroll
-      for (int q = 0; q < TB; ++q) {
-        const int b = b0 + q;
-        if (b >= a.B) continue;
-        const float* xb = a.x + (size_t)b * a.H;
+      for (int m = 0; m < CPT; ++m) {
+        const int ch = min(t + m * kTeam, nch - 1);
+        f32x4 lo[TB], hi[TB];
 #pragma unroll
-        for (int m = 0; m < CPT; ++m) {
-          const int ch = t + m * kTeam;
-          if (ch >= nch) continue;
-          const f32x4 lo = reinterpret_cast<const f32x4*>(xb)[2 * ch];
-          const f32x4 hi = reinterpret_cast<const f32x4*>(xb)[2 * ch + 1];
+        for (int q = 0; q < TB; ++q) {
+          const float* xb = a.x + (size_t)min(b0 + q, a.B - 1) * a.H;
+          lo[q] = reinterpret_cast<const f32x4*>(xb)[2 * ch];
+          hi[q] = reinterpret_cast<const f32x4*>(xb)[2 * ch + 1];
+        }
+#pragma unroll
+        for (int q = 0; q < TB; ++q) {
 #pragma unroll
           for (int rr = 0; rr < R; ++rr) {
             float w[8];
             Fmt<RT>::decode(r[rr][m], w);
             float s = acc[rr * TB + q];
-            s = fmaf(w[0], lo.x, s); s = fmaf(w[1], lo.y, s);
-            s = fmaf(w[2], lo.z, s); s = fmaf(w[3], lo.w, s);
-            s = fmaf(w[4], hi.x, s); s = fmaf(w[5], hi.y, s);
-            s = fmaf(w[6], hi.z, s); s = fmaf(w[7], hi.w, s);
+            s = fmaf(w[0], lo[q].x, s); s = fmaf(w[1], lo[q].y, s);
+            s = fmaf(w[2], lo[q].z, s); s = fmaf(w[3], lo[q].w, s);
+            s = fmaf(w[4], hi[q].x, s); s = fmaf(w[5], hi[q].y, s);
+            s = fmaf(w[6], hi[q].z, s); s = fmaf(w[7], hi[q].w, s);
             acc[rr * TB + q] = s;
           }
         }
