@@ -71,16 +71,16 @@ hipError_t launch_linear(const void* M, const float* x, const float* w, const in
                          int B, hipStream_t s);
 
 // Linear experts at batches of up to kGemvMaxBatch tokens on VALU (whole-line weight
-// loads; workgroup r owns RW output rows of every touched expert): y [B][I].  `zrow` is
-// zeroed memory of at least H * 2 bytes (empty slots read it).  `workgroups` bounds the
-// grid.  Returns hipErrorInvalidValue outside linear_gemv_fits.
+// loads; workgroup r owns RW output rows of every touched expert): y [B][I], from the
+// routing ids [B][k] and weights directly (no union launch; an id outside [0, E) or
+// repeated within a token sets kErrBadId in *err and is skipped).  `zrow` is zeroed memory
+// of at least H * 2 bytes (empty slots read it).  `workgroups` bounds the grid.  Returns
+// hipErrorInvalidValue outside linear_gemv_fits, for E > 4096 or B * k > 256.
 constexpr int kGemvMaxBatch = 4;
 bool linear_gemv_fits(int H, int I, int B);
-hipError_t launch_linear_gemv(const void* M, const float* x, const float* w,
-                              const int32_t* n_touched, const int32_t* touched,
-                              const int32_t* offsets, const int32_t* slots,
-                              const uint8_t* zrow, float* y, int H, int I, int k, int B,
-                              int workgroups, hipStream_t s);
+hipError_t launch_linear_gemv(const void* M, const float* x, const int32_t* ids, const float* w,
+                              uint32_t* err, const uint8_t* zrow, float* y, int H, int I, int E,
+                              int k, int B, int workgroups, hipStream_t s);
 
 // Linear experts at batches of up to 256 / k tokens on VALU, each touched expert against
 // its own tokens only (passes of up to four tokens): partial rows per (token, choice)

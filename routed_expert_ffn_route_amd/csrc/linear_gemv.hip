@@ -33,14 +33,12 @@ constexpr int kGemvMaxT = 256;  // touched experts (B * k <= 4 * 64)
 struct GemvArgs {
   const void* M;             // [E][I][H] bf16
   const float* x;            // [B][H]
+  const int32_t* ids;        // [B][k]
   const float* w;            // [B][k]
-  const int32_t* n_touched;  // [1]
-  const int32_t* touched;    // [E]
-  const int32_t* offsets;    // [E+1]
-  const int32_t* slots;      // [B*k]
+  uint32_t* err;             // sticky error bits (bad or repeated ids)
   const uint8_t* zrow;       // zeroed bytes, at least H * 2
   float* y;                  // [B][I]
-  int H, I, k, B;
+  int H, I, E, k, B;
   int tsz;                   // threads per team
   int rw;                    // output rows per workgroup
 };
@@ -70,24 +68,45 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
   float* ys = c.red + 2 * c.red_stride;               // [rw][NB] this workgroup's rows of y
   int* s_t = reinterpret_cast<int*>(ys + rw * NB);    // [kGemvMaxT] touched experts
   float* s_w = reinterpret_cast<float*>(s_t + kGemvMaxT);  // [kGemvMaxT][NB] token weights
+  uint32_t* bm = reinterpret_cast<uint32_t*>(s_w + kGemvMaxT * NB);  // [EW] experts routed to
+  int* s_nt = reinterpret_cast<int*>(bm + (a.E + 31) / 32);          // [1] touched count
 
-  // touched experts and, per expert, each token's routing weight (0 if not routed to it)
-  const int nt = min(*a.n_touched, kGemvMaxT);
-  for (int i = c.tid; i < nt; i += c.nthreads) {
-    const int e = a.touched[i];
-    s_t[i] = e;
-    float wt[NB];
-#pragma unroll
-    for (int t = 0; t < NB; ++t) wt[t] = 0.0f;
-    for (int s = a.offsets[e]; s < a.offsets[e + 1]; ++s) {
-      const int slot = a.slots[s];
-      const int t = slot / a.k;
-#pragma unroll
-      for (int tt = 0; tt < NB; ++tt)
-        if (tt == t) wt[tt] = a.w[slot];
+  // The touched experts in ascending order and, per expert, each token's routing weight (0
+  // if not routed to it), from the ids directly (B * k <= 256 entries; every workgroup
+  // builds the same table): a bitmap of the routed experts, then an expert's place is the
+  // number of set bits below it.
+  const int EW = (a.E + 31) / 32, nf = a.B * a.k;
+  for (int i = c.tid; i < EW; i += c.nthreads) bm[i] = 0u;
+  for (int i = c.tid; i < kGemvMaxT * NB; i += c.nthreads) s_w[i] = 0.0f;
+  for (int i = c.tid; i < kGemvMaxT; i += c.nthreads) s_t[i] = 0;  // (no ids valid: expert 0)
+  __syncthreads();
+  for (int f = c.tid; f < nf; f += c.nthreads) {
+    const int e = a.ids[f];
+    bool bad = e < 0 || e >= a.E;
+    for (int j = f - f % a.k; j < f && !bad; ++j) bad = a.ids[j] == e;  // repeated in a token
+    if (bad) {
+      if (c.wg == 0) __hip_atomic_fetch_or(a.err, kErrBadId, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      continue;
     }
-#pragma unroll
-    for (int t = 0; t < NB; ++t) s_w[i * NB + t] = wt[t];
+    atomicOr(&bm[e / 32], 1u << (e % 32));
+  }
+  __syncthreads();
+  for (int f = c.tid; f < nf; f += c.nthreads) {
+    const int e = a.ids[f];
+    if (e < 0 || e >= a.E) continue;
+    bool dup = false;
+    for (int j = f - f % a.k; j < f && !dup; ++j) dup = a.ids[j] == e;
+    if (dup) continue;
+    int r = __popc(bm[e / 32] & ((1u << (e % 32)) - 1u));
+    for (int q = 0; q < e / 32; ++q) r += __popc(bm[q]);
+    s_t[r] = e;
+    s_w[r * NB + f / a.k] = a.w[f];
+  }
+  if (c.tid == 0) {
+    int n = 0;
+    for (int q = 0; q < EW; ++q) n += __popc(bm[q]);
+    *s_nt = n;
   }
   for (int i = c.tid; i < rw * NB; i += c.nthreads) ys[i] = 0.0f;
   // x of the tokens (zero for the padding tokens past B)
@@ -102,6 +121,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
     }
   }
   __syncthreads();
+  const int nt = *s_nt;
 
   const int r0 = c.wg * rw;
   const int nitems = nt * rw;
@@ -400,13 +420,13 @@ hipError_t launch_linear_pass(const void* M, const float* x, const float* w,
   return launch_part_combine(part, y, B, k, I, s);
 }
 
-hipError_t launch_linear_gemv(const void* M, const float* x, const float* w,
-                              const int32_t* n_touched, const int32_t* touched,
-                              const int32_t* offsets, const int32_t* slots,
-                              const uint8_t* zrow, float* y, int H, int I, int k, int B,
-                              int workgroups, hipStream_t s) {
-  if (!linear_gemv_fits(H, I, B) || workgroups < 1) return hipErrorInvalidValue;
-  GemvArgs a{M, x, w, n_touched, touched, offsets, slots, zrow, y, H, I, k, B, 0, 0};
+hipError_t launch_linear_gemv(const void* M, const float* x, const int32_t* ids, const float* w,
+                              uint32_t* err, const uint8_t* zrow, float* y, int H, int I, int E,
+                              int k, int B, int workgroups, hipStream_t s) {
+  if (!linear_gemv_fits(H, I, B) || workgroups < 1 || E < 1 || E > 4096 ||
+      B * k > kGemvMaxT)
+    return hipErrorInvalidValue;
+  GemvArgs a{M, x, ids, w, err, zrow, y, H, I, E, k, B, 0, 0};
   a.tsz = gemv_team(H);
   const int threads = 1024;
   const int nb = B <= 1 ? 1 : B <= 2 ? 2 : 4;
@@ -417,7 +437,7 @@ hipError_t launch_linear_gemv(const void* M, const float* x, const float* w,
   a.rw = rw;
   const int wgs = (I + rw - 1) / rw;
   const int lds = 2 * (threads / kWave) * kMaxNP * 4 + rw * nb * 4 + kGemvMaxT * 4 +
-                  kGemvMaxT * nb * 4;
+                  kGemvMaxT * nb * 4 + ((E + 31) / 32) * 4 + 16;
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   if (nb == 1)
     hipLaunchKernelGGL(gemv_kernel<1>, dim3(wgs), dim3(threads), lds, s, a);

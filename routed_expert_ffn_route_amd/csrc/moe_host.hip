@@ -488,27 +488,33 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     int32_t* touched = layer->at<int32_t>(layer->L.union_touched);
     int32_t* offsets = layer->at<int32_t>(layer->L.union_offsets);
     int32_t* slots = layer->at<int32_t>(layer->L.union_slots);
-    if (e == hipSuccess)
+    // up to kGemvMaxBatch tokens: the VALU kernel builds the touched list from the ids itself
+    const bool gemv = B < kLinearTiledMinBatch && linear_gemv_fits(d.hidden, d.inter, B) &&
+                      B * d.top_k <= 256;
+    if (e == hipSuccess && gemv) {
+      e = launch_linear_gemv(layer->w.linear, x, rid, rw, &layer->ctrl()->err,
+                             layer->at<uint8_t>(layer->L.zrow), y, d.hidden, d.inter,
+                             d.n_experts, d.top_k, B, layer->workgroups, s);
+    } else if (e == hipSuccess) {
       e = launch_union(rid, B, d.top_k, d.n_experts, n_t, touched, offsets, slots,
                        layer->ctrl(), s);
-    if (e == hipSuccess && B >= kLinearTiledMinBatch)
-      e = launch_linear_tiled(layer->w.linear, x, rw, n_t, touched, offsets, slots,
-                              layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl),
-                              layer->at<uint16_t>(layer->L.x16), layer->at<float>(layer->L.xsc),
-                              layer->at<float>(layer->L.part), y, d.hidden, d.inter,
-                              d.n_experts, d.top_k, B, s);
-    else if (e == hipSuccess && linear_gemv_fits(d.hidden, d.inter, B))
-      e = launch_linear_gemv(layer->w.linear, x, rw, n_t, touched, offsets, slots,
-                             layer->at<uint8_t>(layer->L.zrow), y, d.hidden, d.inter,
-                             d.top_k, B, layer->workgroups, s);
-    else if (e == hipSuccess && linear_pass_fits(d.hidden, d.inter, B, d.top_k))
-      e = launch_linear_pass(layer->w.linear, x, rw, n_t, touched, offsets, slots,
-                             layer->at<uint8_t>(layer->L.zrow), layer->at<float>(layer->L.part),
-                             y, d.hidden, d.inter, d.top_k, B, layer->workgroups, s);
-    else if (e == hipSuccess)
-      e = launch_linear(layer->w.linear, x, rw, n_t, touched, offsets, slots,
-                        layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl), y,
-                        d.hidden, d.inter, d.n_experts, d.top_k, B, s);
+      if (e == hipSuccess && B >= kLinearTiledMinBatch)
+        e = launch_linear_tiled(layer->w.linear, x, rw, n_t, touched, offsets, slots,
+                                layer->at<uint16_t>(layer->L.xh),
+                                layer->at<uint16_t>(layer->L.xl),
+                                layer->at<uint16_t>(layer->L.x16),
+                                layer->at<float>(layer->L.xsc), layer->at<float>(layer->L.part),
+                                y, d.hidden, d.inter, d.n_experts, d.top_k, B, s);
+      else if (e == hipSuccess && linear_pass_fits(d.hidden, d.inter, B, d.top_k))
+        e = launch_linear_pass(layer->w.linear, x, rw, n_t, touched, offsets, slots,
+                               layer->at<uint8_t>(layer->L.zrow),
+                               layer->at<float>(layer->L.part), y, d.hidden, d.inter,
+                               d.top_k, B, layer->workgroups, s);
+      else if (e == hipSuccess)
+        e = launch_linear(layer->w.linear, x, rw, n_t, touched, offsets, slots,
+                          layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl),
+                          y, d.hidden, d.inter, d.n_experts, d.top_k, B, s);
+    }
     if (e != hipSuccess) return device_fail(e, "linear-expert layer launch");
     return ok();
   }

@@ -114,3 +114,23 @@ def test_linear_full_size_sampled(B):
     L.close()
     del L
     torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+def test_linear_small_batch_flags_bad_ids():
+    """At B <= 4 the VALU kernel reads the ids itself: an id repeated within a token or
+    outside [0, E) is skipped and reported through the layer's error bits; a clean call
+    afterwards reports nothing."""
+    import torch
+    wl = SMALL[1]
+    L = _layer(wl, max_batch=4)
+    x = T.device_x(wl, [0, 1], case=1)
+    y = torch.empty((2, wl.I), dtype=torch.float32, device="cuda")
+    w = torch.full((2, wl.k), 1.0 / wl.k, dtype=torch.float32, device="cuda")
+    for bad in ([[1, 1, 2], [3, 4, 5]], [[1, 2, wl.E], [3, 4, 5]]):
+        ids = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        L.forward(x, y, ids=ids, w=w)
+        assert L.check() != 0
+    ids = torch.tensor([[1, 2, 3], [3, 4, 5]], dtype=torch.int32, device="cuda")
+    L.forward(x, y, ids=ids, w=w)
+    assert L.check() == 0
