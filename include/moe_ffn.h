@@ -146,7 +146,8 @@ moe_status moe_union_experts(const int32_t* ids, int32_t B, int32_t k, int32_t E
                              int32_t* slots, void* stream);
 
 /* Synchronise `stream` and read the layer's device error word (0 = none; nonzero means a
- * bounded in-kernel wait expired or an id was out of range); clears it. */
+ * bounded in-kernel wait expired, or a given id was outside [0, E) or repeated within a
+ * token -- such ids are skipped); clears it. */
 moe_status moe_layer_check(moe_layer layer, void* stream, int32_t* device_error);
 
 /* Launch geometry of the persistent kernels (workgroups, threads per workgroup). */
