@@ -233,6 +233,105 @@ def run_stack(args, wl, keep=None):
     return out
 
 
+PHASES = {
+    "b1": {0: "start", 1: "router rows published", 2: "shared experts streamed",
+           3: "routing known (top-k + softmax)", 4: "routed stream done",
+           13: "partial output published", 14: "reducer: all partials arrived",
+           15: "reducer: y written"},
+    "cs": {0: "start", 1: "router rows published", 2: "shared experts streamed",
+           3: "routing known (top-k + softmax)", 4: "gate pass done (g published)",
+           5: "all gate values gathered", 6: "threshold and kept list known",
+           7: "kept rows streamed", 13: "partial output published",
+           14: "reducer: all partials arrived", 15: "reducer: y written"},
+}
+
+
+def run_timeline(args, wl, keep=None):
+    """Phase timeline of the single-launch layer kernel: the library's timeline build records,
+    per workgroup, the 100 MHz constant clock at the end of each phase.  The launches of
+    `steps` tokens through the stack are captured in one HIP graph (each launch with its own
+    stamp rows) and replayed once; per launch, times are taken from the earliest workgroup
+    start, then the median over launches of the median and the maximum over workgroups."""
+    import numpy as np
+    import torch
+    import routed_expert_ffn_route_amd as M
+    from synth import tensors as T
+    L = M.use_timeline_library()
+    ntok = min(wl.tokens, max(args.steps, 1))
+    desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, wl.n_shared, wl.I_shared,
+                       router_dtype=wl.router_dtype, expert_dtype=wl.expert_dtype,
+                       shared_dtype=wl.shared_dtype, max_batch=1)
+    layers, xs, ys, kepts = [], [], [], []
+    for l in range(wl.layers):
+        layers.append(M.Layer(desc, T.device_layer(wl, l)))
+        xs.append(T.device_x(wl, list(range(ntok)), l))
+        ys.append(torch.empty_like(xs[-1]))
+        if keep is not None:
+            kepts.append(torch.empty((ntok, max(keep, 1)), dtype=torch.int32, device="cuda"))
+    P = layers[0].geometry()[0]
+    K = args.steps
+    nl = K * wl.layers
+    per = 512 * 16
+    stamps = torch.zeros(nl * per, dtype=torch.int64, device="cuda")
+
+    def launch(t, l, rec):
+        L.moe_debug_set_stamps(ctypes_ptr(stamps, rec * per) if rec is not None else None)
+        tt = t % ntok
+        if keep is None:
+            layers[l].forward(xs[l][tt:tt + 1], ys[l][tt:tt + 1], B=1)
+        else:
+            layers[l].channel_select(xs[l][tt:tt + 1], keep, kepts[l][tt], y=ys[l][tt:tt + 1])
+
+    for t in range(args.warmup):
+        for l in range(wl.layers):
+            launch(t, l, None)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(K):
+            for l in range(wl.layers):
+                launch(t, l, t * wl.layers + l)
+    L.moe_debug_set_stamps(None)
+    torch.cuda.synchronize()
+    stamps.zero_()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    for lay in layers:
+        assert lay.check() == 0, "device error word set"
+    st = stamps.view(nl, 512, 16).cpu().numpy()[:, :P, :].astype(np.int64)
+    kind = "b1" if keep is None else "cs"
+    names = PHASES[kind]
+    rows = []
+    t0 = st[:, :, 0].min(axis=1)  # earliest workgroup start per launch
+    for i, name in sorted(names.items()):
+        med, mx = [], []
+        for n in range(nl):
+            v = st[n, :, i]
+            v = v[v > 0]
+            if v.size:
+                med.append(np.median(v - t0[n]) * 0.01)
+                mx.append(np.max(v - t0[n]) * 0.01)
+        if med:
+            rows.append({"phase": i, "name": name, "median_us": round(float(np.median(med)), 2),
+                         "max_us": round(float(np.median(mx)), 2)})
+    # start of launch n+1 (earliest workgroup) after the last stamp of launch n
+    last = st.max(axis=(1, 2))
+    gaps = [(t0[n + 1] - last[n]) * 0.01 for n in range(nl - 1)]
+    span = [(last[n] - t0[n]) * 0.01 for n in range(nl)]
+    return {"timeline": kind, "workload": wl.name, "keep": keep, "launches": nl,
+            "workgroups": P, "phases": rows,
+            "first_start_to_last_stamp_us": round(float(np.median(span)), 2),
+            "last_stamp_to_next_start_us": round(float(np.median(gaps)), 2) if gaps else None,
+            "note": "100 MHz constant clock (10 ns); median over launches of the per-launch "
+                    "median / max over workgroups, from the earliest workgroup start"}
+
+
+def ctypes_ptr(t, offset_elems=0):
+    import ctypes
+    return ctypes.c_void_p(t.data_ptr() + offset_elems * t.element_size())
+
+
 def run_batched_stack(args, wl, B):
     """Batched decode (B tokens per step) through the SwiGLU stack: per layer, routing, the
     touched-expert union and the batched expert kernels; each touched expert is read once
@@ -401,6 +500,9 @@ def main():
     ap.add_argument("--batch", type=int, default=1,
                     help="SwiGLU stacks: tokens per step (B > 1 runs the batched layer)")
     ap.add_argument("--eager", action="store_true", help="launch without a HIP graph")
+    ap.add_argument("--timeline", action="store_true",
+                    help="batch-1 stacks: per-phase timeline from the timeline build of the "
+                         "library (libmoe_ffn_timeline.so) instead of the throughput line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=40, help="layers in the oracle sample")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
@@ -440,6 +542,9 @@ def main():
     keep = None
     if wl.keep_fracs:
         keep = args.keep if args.keep >= 0 else wl.keep_counts()[0]
+    if args.timeline:
+        print(json.dumps(run_timeline(args, wl, keep)), flush=True)
+        return
     print(json.dumps(run_stack(args, wl, keep)), flush=True)
 
 

@@ -145,6 +145,17 @@ moe_status moe_union_experts(const int32_t* ids, int32_t B, int32_t k, int32_t E
                              int32_t* n_touched, int32_t* touched, int32_t* offsets,
                              int32_t* slots, void* stream);
 
+/* The routing a layer call last used, read back for checking: enqueues on `stream` a copy
+ * of B rows of ids [B][k] (int32, routing order) and w [B][k] (fp32) from the workspace
+ * into the caller's device buffers.  Valid after a moe_ffn_forward or moe_channel_select
+ * call that routed inside the call (ids == NULL): at B = 1 the top-k chosen inside the
+ * single launch, for B > 1 that of the routing step in front of the batched kernels.  At
+ * B = 1 with given ids it holds the ids the launch used (-1 for a skipped id).  Other
+ * rows, and rows past the last call's B, are unspecified.  Routing k of E experts per
+ * token, re-chosen in every layer: "Mixture of Experts Changes the Arithmetic", section
+ * "Two Numbers Instead of One".  1 <= B <= max_batch; ids and w must be given. */
+moe_status moe_layer_routing(moe_layer layer, int32_t B, int32_t* ids, float* w, void* stream);
+
 /* Synchronise `stream` and read the layer's device error word (0 = none; nonzero means a
  * bounded in-kernel wait expired, or a given id was outside [0, E) or repeated within a
  * token -- such ids are skipped); clears it. */

@@ -173,6 +173,19 @@ def moe_layer_token(x, w_router, get_expert, k, shared=(), logits=None):
     return y, ids, w
 
 
+def moe_layer_given(x, ids, w, get_expert, shared=()):
+    """The same layer output for a routing given as ids [k'] and weights w [k']: the
+    router-weighted sum of the listed experts' outputs plus the shared experts
+    [Reader, "Background"; MoE-arith, "Two Numbers"]."""
+    x = np.asarray(x, dtype=np.float64).reshape(-1)
+    y = np.zeros_like(x)
+    for e, we in zip(ids, w):
+        y += float(we) * expert_output(x, *get_expert(int(e)))
+    for (g, u, d) in shared:
+        y += expert_output(x, g, u, d)
+    return y
+
+
 # ----------------------------------------------------------------------------------------
 # Channel-sparse variant: fixed-count top-K keep rule across all routed experts
 # ----------------------------------------------------------------------------------------

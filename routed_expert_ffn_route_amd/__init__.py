@@ -22,9 +22,11 @@ DTYPES = {None: DTYPE_NONE, "f32": F32, "bf16": BF16, "mxfp4": MXFP4}
 # Every symbol include/moe_ffn.h declares.
 EXPORTS = (
     "moe_layer_workspace_bytes", "moe_layer_create", "moe_layer_destroy", "moe_route",
-    "moe_ffn_forward", "moe_channel_select", "moe_union_experts", "moe_layer_check",
-    "moe_layer_geometry", "moe_status_string", "moe_last_error",
+    "moe_ffn_forward", "moe_channel_select", "moe_union_experts", "moe_layer_routing",
+    "moe_layer_check", "moe_layer_geometry", "moe_status_string", "moe_last_error",
 )
+# The phase-timeline build (libmoe_ffn_timeline.so) exports one more, for measurement only.
+TIMELINE_LIB_PATH = os.path.join(_HERE, "libmoe_ffn_timeline.so")
 
 
 class LayerDesc(ctypes.Structure):
@@ -46,6 +48,19 @@ class MoeError(RuntimeError):
 
 
 _lib = None
+
+
+def use_timeline_library():
+    """Load the phase-timeline build instead of libmoe_ffn.so (before any other call):
+    the same kernels with per-workgroup phase stamps compiled in (bench.py --timeline)."""
+    global LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("a library is already loaded")
+    LIB_PATH = TIMELINE_LIB_PATH
+    L = lib()
+    L.moe_debug_set_stamps.restype = ctypes.c_int32
+    L.moe_debug_set_stamps.argtypes = [ctypes.c_void_p]
+    return L
 
 
 def lib():
@@ -72,6 +87,8 @@ def lib():
         L.moe_channel_select.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp]
         L.moe_union_experts.restype = i32
         L.moe_union_experts.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.moe_layer_routing.restype = i32
+        L.moe_layer_routing.argtypes = [vp, i32, vp, vp, vp]
         L.moe_layer_check.restype = i32
         L.moe_layer_check.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.moe_layer_geometry.restype = i32
@@ -91,6 +108,26 @@ def _check(status):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None, min_numel=None):
+    """Reject a tensor the kernels would misread or overrun: it must be a contiguous CUDA
+    tensor of `dtype`, with `shape` (None entries match any size) or at least `min_numel`
+    elements.  Raises MoeError(MOE_ERR_ARG) before any native call."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise MoeError(MOE_ERR_ARG, f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise MoeError(MOE_ERR_ARG, f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise MoeError(MOE_ERR_ARG, f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoeError(MOE_ERR_ARG, f"{name} must be contiguous")
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and s != d for s, d in zip(shape, t.shape)):
+            raise MoeError(MOE_ERR_ARG, f"{name} has shape {tuple(t.shape)}, needs {shape}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise MoeError(MOE_ERR_ARG, f"{name} has {t.numel()} elements, needs {min_numel}")
 
 
 def _stream(stream):
@@ -156,20 +193,59 @@ class Layer:
 
     def route(self, x=None, logits_in=None, B=None, ids=None, w=None, logits_out=None,
               stream=None):
+        import torch
+        d = self.desc
         src = x if x is not None else logits_in
+        if src is None:
+            raise MoeError(MOE_ERR_ARG, "one of x and logits_in must be given")
         B = src.shape[0] if B is None else B
+        if x is not None:
+            _need(x, "x", torch.float32, min_numel=B * d.hidden)
+        if logits_in is not None:
+            _need(logits_in, "logits_in", torch.float32, min_numel=B * d.n_experts)
+        _need(ids, "ids", torch.int32, min_numel=B * d.top_k)
+        _need(w, "w", torch.float32, min_numel=B * d.top_k)
+        if logits_out is not None:
+            _need(logits_out, "logits_out", torch.float32, min_numel=B * d.n_experts)
         _check(lib().moe_route(self.handle, _ptr(x), _ptr(logits_in), B, _ptr(ids), _ptr(w),
                                _ptr(logits_out), _stream(stream)))
 
     def forward(self, x, y, ids=None, w=None, B=None, stream=None):
+        import torch
+        d = self.desc
         B = x.shape[0] if B is None else B
+        out_dim = d.inter if d.kind == LINEAR else d.hidden
+        _need(x, "x", torch.float32, min_numel=B * d.hidden)
+        _need(y, "y", torch.float32, min_numel=B * out_dim)
+        if ids is not None:
+            _need(ids, "ids", torch.int32, min_numel=B * d.top_k)
+        if w is not None:
+            _need(w, "w", torch.float32, min_numel=B * d.top_k)
         _check(lib().moe_ffn_forward(self.handle, _ptr(x), B, _ptr(ids), _ptr(w), _ptr(y),
                                      _stream(stream)))
 
     def channel_select(self, x, keep, kept, y=None, ids=None, w=None,
                        mode=SCORE_GATE_DNORM, stream=None):
+        import torch
+        d = self.desc
+        _need(x, "x", torch.float32, min_numel=d.hidden)
+        if kept is not None or keep > 0:
+            _need(kept, "kept", torch.int32, min_numel=keep)
+        if y is not None:
+            _need(y, "y", torch.float32, min_numel=d.hidden)
+        if ids is not None:
+            _need(ids, "ids", torch.int32, min_numel=d.top_k)
+        if w is not None:
+            _need(w, "w", torch.float32, min_numel=d.top_k)
         _check(lib().moe_channel_select(self.handle, _ptr(x), _ptr(ids), _ptr(w), keep, mode,
                                         _ptr(kept), _ptr(y), _stream(stream)))
+
+    def routing(self, ids, w, B=1, stream=None):
+        """Copy the routing the last call used into ids, w [B][k] (moe_layer_routing)."""
+        import torch
+        _need(ids, "ids", torch.int32, min_numel=B * self.desc.top_k)
+        _need(w, "w", torch.float32, min_numel=B * self.desc.top_k)
+        _check(lib().moe_layer_routing(self.handle, B, _ptr(ids), _ptr(w), _stream(stream)))
 
     def check(self, stream=None) -> int:
         err = ctypes.c_int32(0)
@@ -183,6 +259,12 @@ class Layer:
 
 
 def union_experts(ids, E, n_touched, touched, offsets, slots, stream=None):
+    import torch
+    _need(ids, "ids", torch.int32, shape=(None, None))
     B, k = ids.shape
+    _need(n_touched, "n_touched", torch.int32, min_numel=1)
+    _need(touched, "touched", torch.int32, min_numel=E)
+    _need(offsets, "offsets", torch.int32, min_numel=E + 1)
+    _need(slots, "slots", torch.int32, min_numel=B * k)
     _check(lib().moe_union_experts(_ptr(ids), B, k, E, _ptr(n_touched), _ptr(touched),
                                    _ptr(offsets), _ptr(slots), _stream(stream)))

@@ -1,12 +1,17 @@
-"""Compile the gfx950 kernels and the C ABI into routed_expert_ffn_route_amd/libmoe_ffn.so."""
+"""Compile the gfx950 kernels and the C ABI into routed_expert_ffn_route_amd/libmoe_ffn.so.
+
+``build(timeline=True)`` compiles a second library, libmoe_ffn_timeline.so, with the phase
+stamps of the single-launch kernels compiled in (MOE_TIMELINE) and the extra export
+``moe_debug_set_stamps``; it serves ``bench.py --timeline`` only.
+"""
 import os
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
+LIB_TIMELINE = os.path.join(HERE, "libmoe_ffn_timeline.so")
 SOURCES = ["moe_host.hip", "expert_b1.hip", "channel_sparse.hip", "route.hip",
            "batched_swiglu.hip", "linear_mfma.hip", "linear_gemv.hip", "grouped_tn.hip"]
 
@@ -15,9 +20,9 @@ HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
                "-Wall", "-Wno-unused-function", "-Wno-unused-result"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str, defines, verbose: bool) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = ["hipcc", *HIPCC_FLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -30,17 +35,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    build_dir = os.path.join(HERE, "_build_timeline" if timeline else "_build")
+    lib = LIB_TIMELINE if timeline else LIB
+    defines = ["-DMOE_TIMELINE"] if timeline else []
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = ["hipcc", "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", LIB + ".tmp"]
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines, verbose), SOURCES))
+    cmd = ["hipcc", "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, timeline="--timeline" in sys.argv))

@@ -1019,8 +1019,8 @@ __global__ __launch_bounds__(kDnWaves * 64) void bs_down_kernel(BsArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// Combine: y[b] = sum_i part[b*k + i] (routing order) + sum_s part[B*k + s*B + b], each
-// partial row the sum of its row slices in slice order
+// Combine: y[b] = sum_i part[b*k + i] (routing order, the choices that were used) +
+// sum_s part[B*k + s*B + b], each partial row the sum of its row slices in slice order
 // ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bs_combine_kernel(BsArgs a) {
   const int n4 = a.H / 4;
@@ -1030,9 +1030,11 @@ __global__ __launch_bounds__(256) void bs_combine_kernel(BsArgs a) {
     const int b = (int)(idx / n4), c = (int)(idx % n4);
     const f32x4* P = reinterpret_cast<const f32x4*>(a.part);
     f32x4 s = {0, 0, 0, 0};
-    for (int i = 0; i < a.k; ++i)
+    for (int i = 0; i < a.k; ++i) {
+      if (!choice_used(a.ids + (size_t)b * a.k, i, a.E)) continue;  // partial not written
 #pragma unroll
       for (int r = 0; r < kDownRowSlices; ++r) s += P[r * slice + (size_t)(b * a.k + i) * n4 + c];
+    }
     for (int sh = 0; sh < a.NS; ++sh)
 #pragma unroll
       for (int r = 0; r < kDownRowSlices; ++r)

@@ -248,6 +248,8 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   c.red_stride = (c.nthreads / kWave) * kMaxNP;
   c.parity = 0;
   c.zrow = a.zrow;
+  c.stamps = a.stamps;
+  MOE_STAMP(c.stamps, kStampStart);
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
   float* s_w = reinterpret_cast<float*>(s_ids + 64);                // [64]
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
         [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
   }
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
-                reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
+                reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c);
 
   // 2. gate pass over this workgroup's share [g0, g1) of the candidates; g stays in LDS
   const int g0 = (int)((long long)n * c.wg / c.P), g1 = (int)((long long)n * (c.wg + 1) / c.P);

@@ -468,6 +468,17 @@ __device__ __forceinline__ void acquire_dev() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
+// Whether choice i of a token's routing row (k ids) is used: 0 <= id < E and not equal to
+// an earlier choice of the same token (a repeated expert counts once, at its first choice).
+// Every path applies this rule; the ones that see a bad id also set kErrBadId.
+__device__ __forceinline__ bool choice_used(const int32_t* row, int i, int E) {
+  const int e = row[i];
+  if (e < 0 || e >= E) return false;
+  for (int j = 0; j < i; ++j)
+    if (row[j] == e) return false;
+  return true;
+}
+
 constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz constant clock
 
 // Spin until the 64-bit word at p carries `tag` in its upper half and return it: the data
@@ -511,6 +522,27 @@ static_assert(sizeof(Ctrl) == 128 + kGroups * 128, "counter groups are 128-byte 
 enum : uint32_t {
   kErrRouteWait = 1u, kErrReduceWait = 2u, kErrBadId = 4u, kErrPhaseWait = 8u,
 };
+
+// Phase timeline (a separate build of the library with MOE_TIMELINE defined; the product
+// build compiles these to nothing): thread 0 of every workgroup records the 100 MHz
+// constant clock when it passes phase i of a single-launch layer kernel, into
+// stamps[workgroup][kStamps].  Recording is one scalar clock read and one store; it adds no
+// barrier, so the phases keep their order and overlap.
+constexpr int kStamps = 16;
+// stamp slots common to the single-launch kernels (each kernel numbers its other phases
+// from 1): start, partial output published, all partials arrived (reducers), y written
+enum : int { kStampStart = 0, kStampPublished = 13, kStampArrived = 14, kStampReduced = 15 };
+#ifdef MOE_TIMELINE
+#define MOE_STAMP(buf, i)                                                              \
+  do {                                                                                 \
+    if (threadIdx.x == 0 && (buf) != nullptr)                                          \
+      (buf)[blockIdx.x * ::moe::kStamps + (i)] = __builtin_amdgcn_s_memrealtime();     \
+  } while (0)
+#else
+#define MOE_STAMP(buf, i) \
+  do {                    \
+  } while (0)
+#endif
 
 __device__ __forceinline__ void arrive(uint32_t (*family)[32], int wg) {
   add_relaxed_dev(&family[wg % kGroups][0], 1u);

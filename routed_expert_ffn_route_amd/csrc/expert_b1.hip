@@ -57,6 +57,8 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   c.red_stride = (c.nthreads / kWave) * kMaxNP;
   c.parity = 0;
   c.zrow = a.zrow;
+  c.stamps = a.stamps;
+  MOE_STAMP(c.stamps, kStampStart);
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
   float* s_w = reinterpret_cast<float*>(s_ids + 64);                // [64]
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   // 1. router rows, spread over the first workgroups
   router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.rlog, reinterpret_cast<float*>(big),
                        reinterpret_cast<uint32_t*>(s_int), c);
+  MOE_STAMP(c.stamps, 1);
 
   // 2. shared experts (independent of routing): flat channel f of [NS][IS] is row f
   if (a.NS > 0) {
@@ -91,10 +94,12 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   // freeing its registers for the routed stream
   float* ysh = big + L.big_floats;
   if constexpr (kTwo) teams_to_lds<8, CPT>(yv, ysh, c);
+  MOE_STAMP(c.stamps, 2);
 
   // 3. routed experts: flat channel f = slot * I + j
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
-                reinterpret_cast<uint64_t*>(big), s_ids, s_w, c);
+                reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c);
+  MOE_STAMP(c.stamps, 3);
   Ctx cr = c;
   if constexpr (kTwo) {
     set_teams(cr, L.tsz_r);
@@ -121,6 +126,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   }
 
   // 4. deterministic cross-workgroup sum of the partial outputs
+  MOE_STAMP(c.stamps, 4);
   if constexpr (kTwo) {
     add_teams_to_lds<ER, CPT>(yr, ysh, cr);
     publish_and_reduce(a.partials, a.y, ctrl, L.R, L.SW, big, c, ysh);

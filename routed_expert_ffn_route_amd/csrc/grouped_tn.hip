@@ -301,16 +301,19 @@ __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
   }
 }
 
-// y[b][r] = sum_i part[b*k + i][r], i in routing order.
-__global__ __launch_bounds__(256) void tn_combine_kernel(const float* part, float* y, int B,
-                                                         int k, int I) {
+// y[b][r] = sum_i part[b*k + i][r], i in routing order, over the choices that were used
+// (choice_used: a skipped id's partial row was not written by this call).
+__global__ __launch_bounds__(256) void tn_combine_kernel(const float* part, const int32_t* ids,
+                                                         float* y, int B, int k, int I,
+                                                         int E) {
   const int n4 = I / 4;
   for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < (size_t)B * n4;
        idx += (size_t)gridDim.x * blockDim.x) {
     const int b = (int)(idx / n4), c = (int)(idx % n4);
     const f32x4* P = reinterpret_cast<const f32x4*>(part);
     f32x4 s = {0, 0, 0, 0};
-    for (int i = 0; i < k; ++i) s += P[(size_t)(b * k + i) * n4 + c];
+    for (int i = 0; i < k; ++i)
+      if (choice_used(ids + (size_t)b * k, i, E)) s += P[(size_t)(b * k + i) * n4 + c];
     reinterpret_cast<f32x4*>(y)[(size_t)b * n4 + c] = s;
   }
 }
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(256) void x_prep_kernel(const float* x, int H, uint
 int tn_lds_bytes() { return 2 * 2 * kBufElems * 2; }
 
 hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
-                               const int32_t* n_touched, const int32_t* touched,
+                               const int32_t* ids, const int32_t* n_touched, const int32_t* touched,
                                const int32_t* offsets, const int32_t* slots, uint16_t* xh,
                                uint16_t* xl, uint16_t* x16, float* xsc, float* part, float* y,
                                int H, int I, int E, int k, int B, hipStream_t s) {
@@ -379,16 +382,17 @@ hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
   hipLaunchKernelGGL(tn_kernel<false>, grid, dim3(kWaves * 64), tn_lds_bytes(), s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_part_combine(part, y, B, k, I, s);
+  return launch_part_combine(part, ids, y, B, k, I, E, s);
 }
 
-hipError_t launch_part_combine(const float* part, float* y, int B, int k, int I,
-                               hipStream_t s) {
+hipError_t launch_part_combine(const float* part, const int32_t* ids, float* y, int B, int k,
+                               int I, int E, hipStream_t s) {
   if (I % 4 != 0) return hipErrorInvalidValue;
   const size_t n = (size_t)B * (I / 4);
   int g = (int)((n + 255) / 256);
   g = g > 4096 ? 4096 : g;
-  hipLaunchKernelGGL(tn_combine_kernel, dim3(g), dim3(256), 0, s, part, y, B, k, I);
+  hipLaunchKernelGGL(tn_combine_kernel, dim3(g), dim3(256), 0, s, part, ids, y, B, k, I,
+                     E);
   return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct B1Args {
   Ctrl* ctrl;
   int H, E, k, I, NS, IS;
   int route_inside;
+  uint64_t* stamps;                     // [P][kStamps] phase clock (timeline build) or null
 };
 
 hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int workgroups, int threads,
@@ -88,21 +89,24 @@ hipError_t launch_linear_gemv(const void* M, const float* x, const int32_t* ids,
 // at least H * 4 bytes.  Returns hipErrorInvalidValue outside linear_pass_fits.
 bool linear_pass_fits(int H, int I, int B, int k);
 hipError_t launch_linear_pass(const void* M, const float* x, const float* w,
-                              const int32_t* n_touched, const int32_t* touched,
-                              const int32_t* offsets, const int32_t* slots,
-                              const uint8_t* zrow, float* part, float* y, int H, int I, int k,
-                              int B, int workgroups, hipStream_t s);
+                              const int32_t* ids, const int32_t* n_touched,
+                              const int32_t* touched, const int32_t* offsets,
+                              const int32_t* slots, const uint8_t* zrow, float* part, float* y,
+                              int H, int I, int E, int k, int B, int workgroups,
+                              hipStream_t s);
 
-// y[b] = sum over i < k, in order, of part[b*k + i] (rows of I floats; I % 4 == 0).
-hipError_t launch_part_combine(const float* part, float* y, int B, int k, int I,
-                               hipStream_t s);
+// y[b] = sum over i < k, in order, of part[b*k + i] (rows of I floats; I % 4 == 0), over
+// the choices of ids [B][k] that were used (choice_used).
+hipError_t launch_part_combine(const float* part, const int32_t* ids, float* y, int B, int k,
+                               int I, int E, hipStream_t s);
 
 // Linear experts for larger batches: x in both MFMA operand forms (bf16 hi/lo in xh, xl;
 // scaled f16 in x16 with per-token scales xsc, workspace [B][H] each and [B]), then one
 // register-blocked MFMA tile per (touched expert, 256 output rows) with the tokens' x staged in LDS, partial rows per (token, choice)
 // [B*k][I] in `part`, then a combine in routing order into y [B][I].
 hipError_t launch_linear_tiled(const void* M, const float* x, const float* w,
-                               const int32_t* n_touched, const int32_t* touched,
+                               const int32_t* ids, const int32_t* n_touched,
+                               const int32_t* touched,
                                const int32_t* offsets, const int32_t* slots, uint16_t* xh,
                                uint16_t* xl, uint16_t* x16, float* xsc, float* part, float* y,
                                int H, int I, int E, int k, int B, hipStream_t s);
@@ -125,6 +129,7 @@ struct BsArgs {
   const uint16_t* xh;                   // [B][H] bf16 hi of x
   const uint16_t* xl;                   // [B][H] bf16 lo of x
   const float* w;                       // [B][k] router weights
+  const int32_t* ids;                   // [B][k] routing ids (the combine skips unused ones)
   const int32_t* n_touched;             // union: [1], [E], [E+1], [B*k]
   const int32_t* touched;
   const int32_t* offsets;

@@ -53,6 +53,7 @@ struct Ctx {
   int parity;
   uint32_t epoch; // launches completed on this workspace before this one
   const uint8_t* zrow;  // zeroed global memory of at least one weight row and scale row
+  uint64_t* stamps = nullptr;  // phase timeline (MOE_STAMP) or null
   __device__ float* next_red() {
     float* r = red + parity * red_stride;
     parity ^= 1;
@@ -262,7 +263,6 @@ __device__ __forceinline__ void stage_load(Stage<dt, C, CPT>& st, const void* G,
                                            const void* D, const uint8_t* Gs, const uint8_t* Vs,
                                            const uint8_t* Ds, const long long (&row)[C],
                                            const Ctx& c) {
-  using F = Fmt<dt>;
 #pragma unroll
   for (int q = 0; q < C; ++q) {
     // the row is the same for every lane of the wave (one team = whole waves)
@@ -511,24 +511,36 @@ __device__ inline void topk_local(const uint64_t* rlog, int E, int k, uint64_t* 
 // The routing of this token in LDS (s_ids, s_w).  Inside the launch: wait until every
 // router workgroup has published its logits, then select the top-k in this workgroup (each
 // workgroup sorts the E logits itself, which costs less than one more cross-workgroup
-// hand-off).  Given routing: copy ids/w.  Out-of-range ids are reported and skipped (-1).
+// hand-off).  Given routing: copy ids/w; an id outside [0, E), or equal to an earlier id of
+// the token, is reported and skipped (-1), so a repeated expert counts once (its first
+// choice).  Workgroup 0 also stores the routing it used into ids_ws / w_ws [k], where the
+// host can read back what the launch chose.
 __device__ inline void fetch_routing(bool inside, const uint64_t* rlog, const int32_t* ids_in,
                                      const float* w_in, int E, int k, Ctrl* ctrl,
-                                     uint64_t* keys, int* s_ids, float* s_w, const Ctx& c) {
+                                     uint64_t* keys, int* s_ids, float* s_w, int32_t* ids_ws,
+                                     float* w_ws, const Ctx& c) {
   if (inside) {
     topk_local(rlog, E, k, keys, s_ids, s_w, &ctrl->err, c);
-    return;
-  }
-  if (c.tid < k) {
-    int e = ids_in[c.tid];
-    if (e < 0 || e >= E) {
-      __hip_atomic_fetch_or(&ctrl->err, kErrBadId, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      e = -1;
+  } else {
+    if (c.tid < k) {
+      int e = ids_in[c.tid];
+      bool bad = e < 0 || e >= E;
+      for (int j = 0; j < c.tid && !bad; ++j) bad = ids_in[j] == e;
+      if (bad) {
+        if (c.wg == 0)
+          __hip_atomic_fetch_or(&ctrl->err, kErrBadId, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+        e = -1;
+      }
+      s_ids[c.tid] = e;
+      s_w[c.tid] = w_in[c.tid];
     }
-    s_ids[c.tid] = e;
-    s_w[c.tid] = w_in[c.tid];
+    __syncthreads();
   }
-  __syncthreads();
+  if (c.wg == 0 && c.tid < k) {
+    ids_ws[c.tid] = s_ids[c.tid];
+    w_ws[c.tid] = s_w[c.tid];
+  }
 }
 
 // This workgroup's output partial in LDS big[0 .. H): the teams' register vectors summed
@@ -590,6 +602,7 @@ __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl,
   for (int h = c.tid; h < H; h += c.nthreads) st_dev(partials + (size_t)c.wg * H + h, src[h]);
   stores_complete();
   __syncthreads();
+  MOE_STAMP(c.stamps, kStampPublished);
   if (c.tid == 0) arrive(ctrl->done, c.wg);
   const int stride = c.P / R;
   if (c.wg % stride != 0 || c.wg / stride >= R) return;
@@ -599,6 +612,7 @@ __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl,
     if (r == 0) store_relaxed_dev(&ctrl->epoch, c.epoch + 1u);
   }
   __syncthreads();
+  MOE_STAMP(c.stamps, kStampArrived);
   const int h0 = r * SW;
   const int wslice = min(SW, H - h0);
   const int SWB = SW < c.nthreads ? SW : c.nthreads;  // columns per pass (power of two)
@@ -629,6 +643,7 @@ __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl,
     if (g == 0 && col < wslice) y[h0 + col] = big[col0];
     __syncthreads();
   }
+  MOE_STAMP(c.stamps, kStampReduced);
 }
 
 // The whole output step for one register layout.

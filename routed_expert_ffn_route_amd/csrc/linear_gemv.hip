@@ -405,10 +405,10 @@ bool linear_pass_fits(int H, int I, int B, int k) {
 }
 
 hipError_t launch_linear_pass(const void* M, const float* x, const float* w,
-                              const int32_t* n_touched, const int32_t* touched,
+                              const int32_t* ids, const int32_t* n_touched, const int32_t* touched,
                               const int32_t* offsets, const int32_t* slots,
-                              const uint8_t* zrow, float* part, float* y, int H, int I, int k,
-                              int B, int workgroups, hipStream_t s) {
+                              const uint8_t* zrow, float* part, float* y, int H, int I, int E,
+                              int k, int B, int workgroups, hipStream_t s) {
   if (!linear_pass_fits(H, I, B, k) || workgroups < 1) return hipErrorInvalidValue;
   PassArgs a{M, x, w, n_touched, touched, offsets, slots, zrow, part, H, I, k, B, 0};
   a.tsz = gemv_team(H);
@@ -417,7 +417,7 @@ hipError_t launch_linear_pass(const void* M, const float* x, const float* w,
   hipLaunchKernelGGL(gemv_pass_kernel, dim3(workgroups), dim3(threads), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_part_combine(part, y, B, k, I, s);
+  return launch_part_combine(part, ids, y, B, k, I, E, s);
 }
 
 hipError_t launch_linear_gemv(const void* M, const float* x, const int32_t* ids, const float* w,

@@ -168,6 +168,10 @@ struct moe_layer_s {
 
 static constexpr uint32_t kMagic = 0x4D6F4546u;
 
+// Phase-timeline buffer of the single-launch kernels ([workgroups][kStamps] uint64 device
+// memory), set by moe_debug_set_stamps in the timeline build only.
+static uint64_t* g_stamps = nullptr;
+
 static moe_status check_layer(moe_layer l) {
   if (!l || l->magic != kMagic) return fail(MOE_ERR_ARG, "invalid or destroyed layer handle");
   return MOE_OK;
@@ -218,6 +222,7 @@ static B1Args b1_args(moe_layer layer, const float* x, const int32_t* ids, const
   a.NS = d.n_shared;
   a.IS = d.shared_inter;
   a.route_inside = ids == nullptr;
+  a.stamps = g_stamps;
   return a;
 }
 
@@ -235,6 +240,16 @@ const char* moe_status_string(moe_status s) {
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+#ifdef MOE_TIMELINE
+// Timeline build only (not part of the product ABI): every later batch-1 launch records its
+// phase clock into `stamps` (device memory of at least 512 * kStamps uint64), or stops
+// recording when it is null.
+int moe_debug_set_stamps(void* stamps) {
+  g_stamps = reinterpret_cast<uint64_t*>(stamps);
+  return (int)kStamps;
+}
+#endif
 
 size_t moe_layer_workspace_bytes(const moe_layer_desc* desc) {
   if (!desc_valid(desc, nullptr)) return 0;
@@ -340,6 +355,22 @@ moe_status moe_layer_check(moe_layer layer, void* stream, int32_t* device_error)
   return ok();
 }
 
+moe_status moe_layer_routing(moe_layer layer, int32_t B, int32_t* ids, float* w,
+                             void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const moe_layer_desc& d = layer->d;
+  if (B < 1 || B > d.max_batch) return fail(MOE_ERR_ARG, "B=%d outside [1, max_batch]", B);
+  if (!ids || !w) return fail(MOE_ERR_ARG, "ids and w must be given");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t n = (size_t)B * d.top_k * 4;
+  hipError_t e = hipMemcpyAsync(ids, layer->at<int32_t>(layer->L.ids), n,
+                                hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(w, layer->at<float>(layer->L.w), n, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return device_fail(e, "moe_layer_routing copy");
+  return ok();
+}
+
 moe_status moe_route(moe_layer layer, const float* x, const float* logits_in, int32_t B,
                      int32_t* ids, float* w, float* logits_out, void* stream) {
   if (moe_status st = check_layer(layer)) return st;
@@ -433,6 +464,7 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     a.xh = layer->at<uint16_t>(layer->L.xh);
     a.xl = layer->at<uint16_t>(layer->L.xl);
     a.w = rw;
+    a.ids = rid;
     a.n_touched = layer->at<int32_t>(layer->L.union_n);
     a.touched = layer->at<int32_t>(layer->L.union_touched);
     a.offsets = layer->at<int32_t>(layer->L.union_offsets);
@@ -499,17 +531,17 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
       e = launch_union(rid, B, d.top_k, d.n_experts, n_t, touched, offsets, slots,
                        layer->ctrl(), s);
       if (e == hipSuccess && B >= kLinearTiledMinBatch)
-        e = launch_linear_tiled(layer->w.linear, x, rw, n_t, touched, offsets, slots,
+        e = launch_linear_tiled(layer->w.linear, x, rw, rid, n_t, touched, offsets, slots,
                                 layer->at<uint16_t>(layer->L.xh),
                                 layer->at<uint16_t>(layer->L.xl),
                                 layer->at<uint16_t>(layer->L.x16),
                                 layer->at<float>(layer->L.xsc), layer->at<float>(layer->L.part),
                                 y, d.hidden, d.inter, d.n_experts, d.top_k, B, s);
       else if (e == hipSuccess && linear_pass_fits(d.hidden, d.inter, B, d.top_k))
-        e = launch_linear_pass(layer->w.linear, x, rw, n_t, touched, offsets, slots,
+        e = launch_linear_pass(layer->w.linear, x, rw, rid, n_t, touched, offsets, slots,
                                layer->at<uint8_t>(layer->L.zrow),
                                layer->at<float>(layer->L.part), y, d.hidden, d.inter,
-                               d.top_k, B, layer->workgroups, s);
+                               d.n_experts, d.top_k, B, layer->workgroups, s);
       else if (e == hipSuccess)
         e = launch_linear(layer->w.linear, x, rw, n_t, touched, offsets, slots,
                           layer->at<uint16_t>(layer->L.xh), layer->at<uint16_t>(layer->L.xl),

@@ -204,6 +204,11 @@ __global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, 
   for (int f = tid; f < B * k; f += nt) {
     const int e = ids[f], b = f / k;
     if (e < 0 || e >= E) continue;
+    // a repeated expert within a token keeps its first choice only (the token is counted
+    // once above); the later choice gets no slot
+    bool dup = false;
+    for (int j = b * k; j < f && !dup; ++j) dup = ids[j] == e;
+    if (dup) continue;
     const int q = e * Wp + b / 32;
     const int rank = pre[q] + __popc(bits[q] & ((1u << (b % 32)) - 1u));
     slots[off[e] + rank] = f;

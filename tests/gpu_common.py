@@ -54,3 +54,23 @@ def rel_err(y, y_ref):
     y = np.asarray(y, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     return float(np.max(np.abs(y - y_ref)) / np.max(np.abs(y_ref)))
+
+
+def used_choices(ids_row, E):
+    """Choices a token's routing row contributes: ids in [0, E), a repeated expert counted
+    once at its first choice (the rule every path of the library applies)."""
+    out = []
+    for i, e in enumerate(ids_row):
+        if 0 <= e < E and e not in ids_row[:i]:
+            out.append(i)
+    return out
+
+
+def corrupt(ids_np, E):
+    """Copy of a routing with a repeated id in token 0, ids past E in token 1 and below 0 in
+    token 2 (tokens past those untouched)."""
+    bad = ids_np.copy()
+    bad[0, 2] = bad[0, 0]
+    bad[1, 1] = E + 3
+    bad[2, 0] = -1
+    return bad

@@ -48,6 +48,20 @@ def _run_token(L, wl, x_np, ids=None, w=None):
     return y.cpu().numpy()[0]
 
 
+def _routing(L, k, B=1):
+    """The routing the last call used (moe_layer_routing), as numpy ids [B][k], w [B][k]."""
+    import torch
+    ids = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((B, k), dtype=torch.float32, device="cuda")
+    L.routing(ids, w, B=B)
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+# the router weights of the timed launch against the oracle's fp64 softmax: fp32 logits
+# (error ~1e-7 of their size) and the hardware exponential move w by well under this
+W_TOL = 1e-6
+
+
 def _route(L, wl, x_np):
     import torch
     x = torch.from_numpy(x_np).cuda().reshape(1, -1)
@@ -72,6 +86,10 @@ def test_b1_small_shapes(wl):
         assert np.max(np.abs(logits.cpu().numpy()[0] - l_ref)) <= 1e-4 * np.max(np.abs(l_ref)) + 1e-5
         y = _run_token(L, wl, x)
         assert rel_err(y, y_ref) <= TOL_BF16, (tok, rel_err(y, y_ref))
+        # the top-k the single launch chose itself: same experts in the same order
+        rid, rw = _routing(L, wl.k)
+        assert rid[0].tolist() == ids_ref.tolist(), (tok, rid[0], ids_ref)
+        assert np.max(np.abs(rw[0] - w_ref)) <= W_TOL
         # routing supplied by the caller (from moe_route, whose router reduction is ordered
         # differently) agrees with routing inside the launch to fp32 rounding
         y2 = _run_token(L, wl, x, ids=ids, w=w)
@@ -90,6 +108,9 @@ def test_b1_tiny_f32_all_tokens():
         assert ids.cpu().numpy()[0].tolist() == ids_ref.tolist()
         y = _run_token(L, wl, x)
         worst = max(worst, rel_err(y, y_ref))
+        rid, rw = _routing(L, wl.k)
+        assert rid[0].tolist() == ids_ref.tolist(), tok
+        assert np.max(np.abs(rw[0] - O.route(O.router_logits(x, hl.router), wl.k)[1][0])) <= W_TOL
     assert worst <= TOL_BF16
     print(f"tiny_f32: 64 tokens, worst max|dy|/||y||inf = {worst:.3e}")
 
@@ -111,10 +132,13 @@ def test_b1_full_size_stack_sampled():
         hl = HostLayer(wl, layer)
         for tok in (0, 101):
             a, x = pick_attempt(wl, tok, layer, host_router=hl.router)
-            y_ref, ids_ref, _ = O.moe_layer_token(x, hl.router, hl.expert, wl.k, hl.shared)
+            y_ref, ids_ref, w_ref = O.moe_layer_token(x, hl.router, hl.expert, wl.k, hl.shared)
             ids, _, _ = _route(L, wl, x)
             assert ids.cpu().numpy()[0].tolist() == ids_ref.tolist()
             y = _run_token(L, wl, x)
+            rid, rw = _routing(L, wl.k)
+            assert rid[0].tolist() == ids_ref.tolist()
+            assert np.max(np.abs(rw[0] - w_ref)) <= W_TOL
             err = rel_err(y, y_ref)
             print(f"layer {layer} token {tok}: max|dy|/||y||inf = {err:.3e}")
             assert err <= TOL_BF16
@@ -122,3 +146,48 @@ def test_b1_full_size_stack_sampled():
         del L
         import torch
         torch.cuda.empty_cache()
+
+
+def test_b1_routing_full_size_many_tokens():
+    """The timed launch's own top-k at the full 40-layer stack shapes (E=256, k=8): ids in
+    routing order and weights for 16 margin-checked tokens over four layers."""
+    wl = WORKLOADS["qwen35_a3b_bf16"]
+    import torch
+    for layer in (0, 13, 26, 39):
+        L = _layer(wl, layer)
+        Wr = T.router(wl, layer)
+        for tok in range(4):
+            a, x = pick_attempt(wl, tok, layer, host_router=Wr)
+            ids_ref, w_ref = O.route(O.router_logits(x, Wr), wl.k)
+            _run_token(L, wl, x)
+            rid, rw = _routing(L, wl.k)
+            assert rid[0].tolist() == ids_ref[0].tolist(), (layer, tok)
+            assert np.max(np.abs(rw[0] - w_ref[0])) <= W_TOL
+        L.close()
+        del L
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bad", ["repeat", "range"])
+def test_b1_given_bad_ids_skipped(bad):
+    """A given id outside [0, E) or repeated within the token is skipped (its first choice
+    kept), reported in the error word, and y is the oracle's with that choice removed."""
+    import torch
+    wl = SMALL[2]
+    L = _layer(wl)
+    hl = HostLayer(wl)
+    a, x = pick_attempt(wl, 0, host_router=hl.router)
+    _, ids_ref, w_ref = O.moe_layer_token(x, hl.router, hl.expert, wl.k, hl.shared)
+    ids = ids_ref.astype(np.int64).copy()
+    w = w_ref.copy()
+    ids[3] = ids[1] if bad == "repeat" else wl.E + 5
+    keep = [i for i in range(wl.k) if i != 3]
+    y_ref = O.moe_layer_given(x, ids[keep], w[keep], hl.expert, hl.shared)
+    xd = torch.from_numpy(x).cuda().reshape(1, -1)
+    yd = torch.empty_like(xd)
+    L.forward(xd, yd, ids=torch.from_numpy(ids.astype(np.int32)).cuda().reshape(1, -1),
+              w=torch.from_numpy(w.astype(np.float32)).cuda().reshape(1, -1))
+    assert L.check() != 0
+    assert rel_err(yd.cpu().numpy()[0], y_ref) <= TOL_BF16
+    rid, _ = _routing(L, wl.k)
+    assert rid[0][3] == -1 and rid[0][1] == ids[1]

@@ -3,7 +3,8 @@ gate/up, down partials, per-token combine) against the oracle, token by token.""
 import numpy as np
 import pytest
 
-from gpu_common import HostLayer, TOL_BF16, TOL_MXFP4, cuda_ok, pick_attempt, rel_err
+from gpu_common import (HostLayer, TOL_BF16, TOL_MXFP4, corrupt, cuda_ok, pick_attempt,
+                        rel_err, used_choices as _used)
 from synth import tensors as T
 from synth.workloads import WORKLOADS
 from oracle import moe_oracle as O
@@ -161,6 +162,13 @@ def test_batched_full_size_sampled(name, B, sample):
     assert L.check() == 0
     yc = y.cpu().numpy()
     xc = x.cpu().numpy()
+    # the routing step of the batched call, every token of the batch against the oracle
+    rid = torch.empty((B, wl.k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((B, wl.k), dtype=torch.float32, device="cuda")
+    L.routing(rid, rw, B=B)
+    ids_ref, w_ref = O.route(O.router_logits(xc, hl.router), wl.k)
+    assert np.array_equal(rid.cpu().numpy(), ids_ref)
+    assert np.max(np.abs(rw.cpu().numpy() - w_ref)) <= 1e-6
     worst = 0.0
     for b in sample:
         y_ref, _, _ = O.moe_layer_token(xc[b], hl.router, hl.expert, wl.k, hl.shared)
@@ -171,3 +179,30 @@ def test_batched_full_size_sampled(name, B, sample):
     L.close()
     del L
     torch.cuda.empty_cache()
+
+
+def test_batched_bad_ids_skipped():
+    """Given ids with a repeat, an id past E and a negative id (tokens 0-2) at B=16: skipped,
+    reported, and y equals the oracle with those choices removed, after a clean call."""
+    import torch
+    wl = SMALL[0]
+    B = 16
+    L = _layer(wl, max_batch=B)
+    hl = HostLayer(wl)
+    attempts, X = _batch(wl, hl, B, case=6)
+    ys, ids, ws = _oracle(wl, hl, X)
+    x = T.device_x(wl, list(range(B)), attempts=attempts, case=6)
+    ids_np = np.stack([ids[b] for b in range(B)]).astype(np.int32)
+    w_np = np.stack([ws[b] for b in range(B)]).astype(np.float32)
+    w_t = torch.from_numpy(w_np).cuda()
+    y = torch.empty((B, wl.H), dtype=torch.float32, device="cuda")
+    L.forward(x, y, ids=torch.from_numpy(ids_np).cuda(), w=w_t)
+    assert L.check() == 0
+    bad = corrupt(ids_np, wl.E)
+    L.forward(x, y, ids=torch.from_numpy(bad).cuda(), w=w_t)
+    assert L.check() != 0
+    yc = y.cpu().numpy()
+    for b in range(B):
+        use = _used(bad[b].tolist(), wl.E)
+        y_ref = O.moe_layer_given(X[b], bad[b, use], w_np[b, use], hl.expert, hl.shared)
+        assert rel_err(yc[b], y_ref) <= TOL_BF16, b

@@ -3,7 +3,7 @@
 import numpy as np
 import pytest
 
-from gpu_common import TOL_BF16, cuda_ok, rel_err
+from gpu_common import TOL_BF16, corrupt, cuda_ok, rel_err, used_choices as _used
 from synth import tensors as T
 from synth.workloads import WORKLOADS
 from oracle import moe_oracle as O
@@ -134,3 +134,34 @@ def test_linear_small_batch_flags_bad_ids():
     ids = torch.tensor([[1, 2, 3], [3, 4, 5]], dtype=torch.int32, device="cuda")
     L.forward(x, y, ids=ids, w=w)
     assert L.check() == 0
+
+
+@pytest.mark.parametrize("B", [3, 16, 40])
+def test_linear_bad_ids_skipped_every_path(B):
+    """Bad given ids at B=3 (VALU row-owner kernel), B=16 (VALU passes) and B=40 (MFMA
+    tiles): the bad choices are skipped, the error word is set, and y equals the oracle with
+    those choices removed -- also after a clean call has left other partial rows behind."""
+    import torch
+    wl = SMALL[1]
+    L = _layer(wl, max_batch=64)
+    tokens = list(range(B))
+    logits, ids, w = _route_given_logits(L, wl, tokens, case=5)
+    x = T.device_x(wl, tokens, case=5)
+    y = torch.empty((B, wl.I), dtype=torch.float32, device="cuda")
+    L.forward(x, y, ids=ids, w=w)  # a clean call first: partial rows of every choice written
+    assert L.check() == 0
+    bad = corrupt(ids.cpu().numpy(), wl.E)
+    L.forward(x, y, ids=torch.from_numpy(bad).cuda(), w=w)
+    assert L.check() != 0
+    mats = {}
+
+    def get(e):
+        if e not in mats:
+            mats[e] = T.linear(wl, e)
+        return mats[e]
+
+    xs, ys, wn = x.cpu().numpy(), y.cpu().numpy(), w.cpu().numpy()
+    for b in range(B):
+        use = _used(bad[b].tolist(), wl.E)
+        yref = O.linear_moe(xs[b:b + 1], bad[b:b + 1, use], wn[b:b + 1, use], get)[0]
+        assert rel_err(ys[b], yref) <= TOL_BF16, b

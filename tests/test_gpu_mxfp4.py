@@ -19,6 +19,17 @@ def _layer(wl, layer=0, max_batch=1):
     return M.Layer(desc, T.device_layer(wl, layer))
 
 
+W_TOL = 1e-6  # router weights of the launch vs the oracle's fp64 softmax
+
+
+def _routing(L, k, B=1):
+    import torch
+    ids = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((B, k), dtype=torch.float32, device="cuda")
+    L.routing(ids, w, B=B)
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
 def _run(L, x_np):
     import torch
     x = torch.from_numpy(x_np).cuda().reshape(1, -1)
@@ -62,12 +73,42 @@ def test_mxfp4_b1_full_size_sampled():
     hl = HostLayer(wl, 0)
     for tok in (0, 5):
         a, x = pick_attempt(wl, tok, 0, host_router=hl.router)
-        y_ref, _, _ = O.moe_layer_token(x, hl.router, hl.expert, wl.k, hl.shared)
+        y_ref, ids_ref, w_ref = O.moe_layer_token(x, hl.router, hl.expert, wl.k, hl.shared)
         hl._experts.clear()
         y = _run(L, x)
+        rid, rw = _routing(L, wl.k)
+        assert rid[0].tolist() == ids_ref.tolist()
+        assert np.max(np.abs(rw[0] - w_ref)) <= W_TOL
         err = rel_err(y, y_ref)
         print(f"mxfp4 token {tok}: max|dy|/||y||inf = {err:.3e}")
         assert err <= TOL_MXFP4
     L.close()
     del L
     torch.cuda.empty_cache()
+
+
+def test_mxfp4_routing_full_size_tokens():
+    """E=896, k=16 routing at the full shapes for 10 margin-checked tokens over two layers:
+    the top-k the single launch chose (moe_layer_routing after moe_ffn_forward) and that of
+    moe_route, both against the oracle's ids in routing order and its weights."""
+    import torch
+    wl = WORKLOADS["mxfp4_e896_k16"]
+    for layer in (0, 5):
+        L = _layer(wl, layer)
+        Wr = T.router(wl, layer)
+        for tok in range(5):
+            a, x = pick_attempt(wl, tok, layer, host_router=Wr)
+            ids_ref, w_ref = O.route(O.router_logits(x, Wr), wl.k)
+            xd = torch.from_numpy(x).cuda().reshape(1, -1)
+            ids = torch.empty((1, wl.k), dtype=torch.int32, device="cuda")
+            w = torch.empty((1, wl.k), dtype=torch.float32, device="cuda")
+            L.route(x=xd, ids=ids, w=w)
+            assert ids.cpu().numpy()[0].tolist() == ids_ref[0].tolist(), (layer, tok)
+            assert np.max(np.abs(w.cpu().numpy()[0] - w_ref[0])) <= W_TOL
+            _run(L, x)
+            rid, rw = _routing(L, wl.k)
+            assert rid[0].tolist() == ids_ref[0].tolist(), (layer, tok)
+            assert np.max(np.abs(rw[0] - w_ref[0])) <= W_TOL
+        L.close()
+        del L
+        torch.cuda.empty_cache()
