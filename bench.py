@@ -236,12 +236,17 @@ def run_stack(args, wl, keep=None):
 PHASES = {
     "b1": {0: "start", 1: "router rows published", 2: "shared experts streamed",
            3: "routing known (top-k + softmax)", 4: "routed stream done",
+           5: "partial output summed in LDS", 6: "shared rows prefetched (wave 4)",
+           7: "reducer: every thread's partials seen", 8: "top-k: wave 0 keys sorted in runs", 9: "top-k: wave 0 top of its keys",
+           10: "top-k: wave 0 keys polled", 11: "top-k: ranked", 12: "router rows computed",
            13: "partial output published", 14: "reducer: all partials arrived",
            15: "reducer: y written"},
     "cs": {0: "start", 1: "router rows published", 2: "shared experts streamed",
            3: "routing known (top-k + softmax)", 4: "gate pass done (g published)",
            5: "all gate values gathered", 6: "threshold and kept list known",
-           7: "kept rows streamed", 13: "partial output published",
+           7: "kept rows streamed", 8: "top-k: wave 0 keys sorted in runs",
+           9: "top-k: wave 0 top of its keys", 10: "top-k: wave 0 keys polled", 11: "top-k: ranked",
+           12: "router rows computed", 13: "partial output published",
            14: "reducer: all partials arrived", 15: "reducer: y written"},
 }
 
@@ -315,12 +320,23 @@ def run_timeline(args, wl, keep=None):
         if med:
             rows.append({"phase": i, "name": name, "median_us": round(float(np.median(med)), 2),
                          "max_us": round(float(np.median(mx)), 2)})
+    # per XCD (workgroup w runs on XCD w % 8): median over launches of the median over the
+    # XCD's workgroups, for the end of the stream and the publish
+    per_xcd = {}
+    for i in (4, 13):
+        if i in names:
+            vals = []
+            for x in range(8):
+                med = [np.median(st[n, x::8, i][st[n, x::8, i] > 0] - t0[n]) * 0.01
+                       for n in range(nl) if (st[n, x::8, i] > 0).any()]
+                vals.append(round(float(np.median(med)), 2) if med else None)
+            per_xcd[names[i]] = vals
     # start of launch n+1 (earliest workgroup) after the last stamp of launch n
     last = st.max(axis=(1, 2))
     gaps = [(t0[n + 1] - last[n]) * 0.01 for n in range(nl - 1)]
     span = [(last[n] - t0[n]) * 0.01 for n in range(nl)]
     return {"timeline": kind, "workload": wl.name, "keep": keep, "launches": nl,
-            "workgroups": P, "phases": rows,
+            "workgroups": P, "phases": rows, "per_xcd_median_us": per_xcd,
             "first_start_to_last_stamp_us": round(float(np.median(span)), 2),
             "last_stamp_to_next_start_us": round(float(np.median(gaps)), 2) if gaps else None,
             "note": "100 MHz constant clock (10 ns); median over launches of the per-launch "

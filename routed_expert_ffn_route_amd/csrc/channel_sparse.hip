@@ -267,14 +267,21 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
 
   // 1. routing, and the shared experts while it is in flight
   read_epoch(ctrl, c);
-  router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.rlog, reinterpret_cast<float*>(big),
-                       reinterpret_cast<uint32_t*>(s_int), c);
+  RouterRound<RT, CPT> rr;
+  router_issue<RT, CPT>(a.route_inside, a.router, a.E, c, rr);
+  auto finish_router = [&] {
+    router_finish<RT, CPT>(rr, a.router, a.E, xv, a.rlog, reinterpret_cast<float*>(big),
+                           reinterpret_cast<uint32_t*>(s_int), c);
+  };
   if (a.NS > 0) {
     const long long nsc = (long long)a.NS * a.IS;
     stream_channels<ST, C, CPT, true, true>(
         a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, (int)(nsc * c.wg / c.P),
         (int)(nsc * (c.wg + 1) / c.P),
-        [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
+        [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c,
+        finish_router);
+  } else {
+    finish_router();
   }
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
                 reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c);
@@ -502,7 +509,7 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs) {
   const int topk = topk_lds_bytes(E, k);
   int big = sel > ybuf ? sel : ybuf;
   big = big > topk ? big : topk;
-  big = big > threads * 4 ? big : threads * 4;
+  big = big > threads * 8 ? big : threads * 8;
   return fixed + big;
 }
 

@@ -45,6 +45,32 @@ __device__ __forceinline__ u32x4 lds_ld128(const lds_u8* p) {
   return *reinterpret_cast<const lds_u32x4*>(p);
 }
 
+// Phase timeline (a separate build of the library with MOE_TIMELINE defined; the product
+// build compiles these to nothing): thread 0 of every workgroup records the 100 MHz
+// constant clock when it passes phase i of a single-launch layer kernel, into
+// stamps[workgroup][kStamps].  Recording is one scalar clock read and one store; it adds no
+// barrier, so the phases keep their order and overlap.
+constexpr int kStamps = 16;
+// stamp slots common to the single-launch kernels (each kernel numbers its other phases
+// from 1): start, partial output published, all partials arrived (reducers), y written
+enum : int {
+  kStampStart = 0, kStampAllPolled = 7, kStampSorted = 8, kStampWaveTop = 9, kStampKeys = 10,
+  kStampRanked = 11,
+  kStampRouterDots = 12,
+  kStampPublished = 13, kStampArrived = 14, kStampReduced = 15
+};
+#ifdef MOE_TIMELINE
+#define MOE_STAMP(buf, i)                                                              \
+  do {                                                                                 \
+    if (threadIdx.x == 0 && (buf) != nullptr)                                          \
+      (buf)[blockIdx.x * ::moe::kStamps + (i)] = __builtin_amdgcn_s_memrealtime();     \
+  } while (0)
+#else
+#define MOE_STAMP(buf, i) \
+  do {                    \
+  } while (0)
+#endif
+
 // MXFP4W is MXFP4 read in 16-element chunks (8 bytes of codes + the block's scale byte per
 // thread and row) instead of 8-element ones: the same bytes, twice as many per load.
 enum class DT : int { F32 = 0, BF16 = 1, MXFP4 = 2, MXFP4W = 3 };
@@ -348,77 +374,166 @@ __device__ __forceinline__ float key_value(uint64_t k) {
   return from_ordered_bits((uint32_t)(k >> 32));
 }
 
-// Rank of `me` among the keys [j0, j1) of `keys` (number of larger keys).  The lanes of a
-// wave read the same keys (LDS broadcasts, no cross-lane shuffles), 16 reads in flight per
-// batch; keys past `n` are clamped reads that count nothing.
-__device__ __forceinline__ int rank_in(const uint64_t* keys, int n, int j0, int j1,
-                                       uint64_t me) {
-  int r = 0;
-  for (int j = j0; j < j1; j += 16) {
-    uint64_t kk[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) kk[u] = keys[j + u < n ? j + u : n - 1];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) r += (j + u < j1 && kk[u] > me) ? 1 : 0;
+// ------------------------------------------------------------------------------------
+// Top-k in registers: bitonic networks on 64-bit keys held one per lane, with the partner
+// lane's key fetched by DPP moves (within rows of 16) and row swaps (permlane16/32), never
+// through LDS.  A "run" is KP consecutive lanes (KP a power of two <= 64) holding keys in
+// descending order.
+// ------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  // every lane has a source lane in the patterns used here (bound_ctrl: no old value)
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// Value of lane ^ 16 (SW = 16) or lane ^ 32 (SW = 32).  The swap returns this lane's own
+// word in one result and the partner's in the other; the one that differs from the own word
+// is the partner's (if both equal it, so does the partner's).
+template <int SW>
+__device__ __forceinline__ uint32_t swap_rows32(uint32_t v) {
+  const auto r = SW == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                          : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return r[0] == v ? r[1] : r[0];
+}
+template <int SW>
+__device__ __forceinline__ uint64_t swap_rows64(uint64_t v) {
+  return ((uint64_t)swap_rows32<SW>((uint32_t)(v >> 32)) << 32) | swap_rows32<SW>((uint32_t)v);
+}
+// Key of lane ^ J (J = 1 ... 32).
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
+  if constexpr (J == 1) return dpp64<0xB1>(v);               // quad_perm [1,0,3,2]
+  else if constexpr (J == 2) return dpp64<0x4E>(v);          // quad_perm [2,3,0,1]
+  else if constexpr (J == 4) return dpp64<0x141>(dpp64<0x1B>(v));  // half_mirror(quad_mirror)
+  else if constexpr (J == 8) return dpp64<0x128>(v);         // row_ror:8
+  else return swap_rows64<J>(v);                             // 16, 32
+}
+// Key of the lane mirrored within its aligned block of M lanes (lane -> M - 1 - lane).
+template <int M>
+__device__ __forceinline__ uint64_t mirror_lane64(uint64_t v) {
+  if constexpr (M == 1) return v;
+  else if constexpr (M == 2) return dpp64<0xB1>(v);
+  else if constexpr (M == 4) return dpp64<0x1B>(v);          // quad_perm [3,2,1,0]
+  else if constexpr (M == 8) return dpp64<0x141>(v);         // row_half_mirror
+  else if constexpr (M == 16) return dpp64<0x140>(v);        // row_mirror
+  else if constexpr (M == 32) return swap_rows64<16>(dpp64<0x140>(v));
+  else return swap_rows64<32>(swap_rows64<16>(dpp64<0x140>(v)));
+}
+// Compare-exchange with the partner: the lane with `lower` set keeps the larger key, the
+// other the smaller.  Written as one comparison and a select, so that it compiles to
+// v_cmp + mask logic + v_cndmask (a conditional choice between two comparisons compiles to
+// branches around each exchange).
+__device__ __forceinline__ uint64_t cmpx(uint64_t x, uint64_t p, bool lower) {
+  const bool gt = p > x;
+  return (gt == lower) ? p : x;  // equal keys: either choice holds the same key
+}
+// Sort every run of KP lanes descending (bitonic, mirror form: merging two sorted halves
+// starts with mirrored partners, then half-cleaners with lane ^ j partners).
+template <int KP>
+__device__ __forceinline__ uint64_t sort_runs(uint64_t x, int lane) {
+  if constexpr (KP >= 2) {
+    x = sort_runs<KP / 2>(x, lane);
+    x = cmpx(x, mirror_lane64<KP>(x), (lane & (KP - 1)) < KP / 2);
+    if constexpr (KP >= 8) x = cmpx(x, xor_lane64<KP / 4>(x), (lane & (KP / 4)) == 0);
+    if constexpr (KP >= 16) x = cmpx(x, xor_lane64<KP / 8>(x), (lane & (KP / 8)) == 0);
+    if constexpr (KP >= 32) x = cmpx(x, xor_lane64<KP / 16>(x), (lane & (KP / 16)) == 0);
+    if constexpr (KP >= 64) x = cmpx(x, xor_lane64<KP / 32>(x), (lane & (KP / 32)) == 0);
+    if constexpr (KP >= 4) x = cmpx(x, xor_lane64<1>(x), (lane & 1) == 0);
   }
-  return r;
+  return x;
+}
+// Half-cleaners of a bitonic run of KP lanes: sorts it descending.
+template <int KP>
+__device__ __forceinline__ uint64_t clean_run(uint64_t x, int lane) {
+  if constexpr (KP >= 64) x = cmpx(x, xor_lane64<32>(x), (lane & 32) == 0);
+  if constexpr (KP >= 32) x = cmpx(x, xor_lane64<16>(x), (lane & 16) == 0);
+  if constexpr (KP >= 16) x = cmpx(x, xor_lane64<8>(x), (lane & 8) == 0);
+  if constexpr (KP >= 8) x = cmpx(x, xor_lane64<4>(x), (lane & 4) == 0);
+  if constexpr (KP >= 4) x = cmpx(x, xor_lane64<2>(x), (lane & 2) == 0);
+  if constexpr (KP >= 2) x = cmpx(x, xor_lane64<1>(x), (lane & 1) == 0);
+  return x;
+}
+// Sorted runs of KP lanes, each copied in every KP-block of a block of M / 2 lanes (M >=
+// 2 KP) -> the top KP of each block of M lanes, sorted, in every KP-block of it: the larger
+// of each key and its mirror across the block forms a bitonic run, then half-cleaners.
+template <int KP, int M>
+__device__ __forceinline__ uint64_t merge_runs(uint64_t x, int lane) {
+  const uint64_t p = mirror_lane64<M>(x);
+  x = p > x ? p : x;
+  return clean_run<KP>(x, lane);
+}
+// Sorted runs of KP lanes -> the top KP of all 64 lanes, sorted, in lanes [0, KP) (and in
+// every other KP-block).  `used` lanes from 0 hold keys (the rest hold zero keys): rounds
+// that would only merge zeros are skipped.
+template <int KP>
+__device__ __forceinline__ uint64_t merge_wave(uint64_t x, int lane, int used) {
+  if constexpr (KP < 64) {
+    if (used > KP) x = merge_runs<KP, 2 * KP>(x, lane);
+    if constexpr (4 * KP <= 64) if (used > 2 * KP) x = merge_runs<KP, 4 * KP>(x, lane);
+    if constexpr (8 * KP <= 64) if (used > 4 * KP) x = merge_runs<KP, 8 * KP>(x, lane);
+    if constexpr (16 * KP <= 64) if (used > 8 * KP) x = merge_runs<KP, 16 * KP>(x, lane);
+    if constexpr (32 * KP <= 64) if (used > 16 * KP) x = merge_runs<KP, 32 * KP>(x, lane);
+    if constexpr (64 * KP <= 64) if (used > 32 * KP) x = merge_runs<KP, 64 * KP>(x, lane);
+  }
+  return x;
+}
+// Merge two sorted top-KP runs (lanes [0, KP) of each, copies in every KP-block): the top
+// KP of both, sorted.
+template <int KP>
+__device__ __forceinline__ uint64_t merge_two(uint64_t r, uint64_t s, int lane) {
+  const uint64_t p = mirror_lane64<KP>(s);
+  r = p > r ? p : r;
+  return clean_run<KP>(r, lane);
 }
 
-// Top-k of n distinct non-zero keys held in LDS (keys[n .. n rounded up to 64) must be 0).
-// Level 1: every group of 64 keys ranks its members among themselves (one wave per group)
-// and keeps its min(k, 64) best as candidates -- every key of the overall top k is among
-// its group's top k.  Level 2: the candidates are ranked among themselves (each rank split
-// over several threads, partial ranks summed with LDS atomics).  A key's rank is the
-// number of larger keys, so the keys of rank < k are the top k in descending order:
-// out[0..k).  LDS scratch `tmp` of topk_scratch_bytes(n, k).  The keys must be visible to
-// the whole workgroup before the call; all threads of the workgroup must call.
-__host__ __device__ constexpr int topk_candidates(int n, int k) {
-  return ((n + 63) / 64) * (k < 64 ? k : 64);
-}
-__host__ __device__ constexpr int topk_scratch_bytes(int n, int k) {
-  return topk_candidates(n, k) * 12;
-}
-__device__ inline void wg_topk_rank(const uint64_t* keys, void* tmp, int n, int k,
-                                    uint64_t* out) {
-  const int nt = blockDim.x, tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nt / kWave;
-  const int kk = k < kWave ? k : kWave;
-  const int groups = (n + kWave - 1) / kWave;
-  const int C = groups * kk;
-  uint64_t* cand = reinterpret_cast<uint64_t*>(tmp);
-  int* cnt = reinterpret_cast<int*>(cand + C);
-  for (int i = tid; i < C; i += nt) {
-    cand[i] = 0ull;
-    cnt[i] = 0;
+// Top-k of n keys, descending, computed by a whole workgroup: key(i) for i < n is
+// fetched by the lanes themselves (wave w takes the 64-key chunks w, w + nwaves, ...), each
+// wave keeps the top KP of its chunks in registers (bitonic), the waves' runs meet in LDS
+// and wave 0 merges them.  Returns in wave 0, lane i < k, the i-th largest key (0 past n).
+// `cand` is LDS of nwaves * KP keys.  KP = the smallest power of two >= k (<= 64).  All
+// threads of the workgroup must call; one barrier.
+template <int KP, typename KeyOf>
+__device__ inline uint64_t wg_topk_bitonic(int n, KeyOf key_of, uint64_t* cand,
+                                           uint64_t* stamps = nullptr) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int chunks = (n + kWave - 1) / kWave;
+  uint64_t top = 0ull;
+  for (int ch = wave; ch < chunks; ch += nwaves) {
+    const int i = ch * kWave + lane;
+    uint64_t x = i < n ? key_of(i) : 0ull;
+    if (ch == wave) MOE_STAMP(stamps, kStampKeys);
+    x = sort_runs<KP>(x, lane);
+    if (ch == wave) MOE_STAMP(stamps, kStampSorted);
+    const int used = min(kWave, n - ch * kWave);
+    x = merge_wave<KP>(x, lane, used);
+    top = ch == wave ? x : merge_two<KP>(top, x, lane);
   }
+  if (wave == 0) MOE_STAMP(stamps, kStampWaveTop);
+  const int runs = min(nwaves, chunks);
+  if (wave < runs && lane < KP) cand[wave * KP + lane] = top;
   __syncthreads();
-  for (int g = wave; g < groups; g += nwaves) {
-    const uint64_t me = keys[g * kWave + lane];
-    const int r = rank_in(keys + g * kWave, kWave, 0, kWave, me);
-    if (me != 0ull && r < kk) cand[g * kk + r] = me;
+  uint64_t res = 0ull;
+  if (wave == 0) {
+    const int total = runs * KP;
+    for (int g = 0; g * kWave < total; ++g) {
+      const int i = g * kWave + lane;
+      uint64_t x = i < total ? cand[i] : 0ull;
+      x = merge_wave<KP>(x, lane, min(kWave, total - g * kWave));
+      res = g == 0 ? x : merge_two<KP>(res, x, lane);
+    }
   }
-  __syncthreads();
-  int parts = nt / C;
-  parts = parts < 1 ? 1 : parts > 16 ? 16 : parts;
-  const int span = (C + parts - 1) / parts;
-  for (int i = tid; i < C * parts; i += nt) {
-    const int e = i % C, q = i / C;
-    const int j0 = q * span, j1 = j0 + span < C ? j0 + span : C;
-    const int r = rank_in(cand, C, j0, j1, cand[e]);
-    if (r) atomicAdd(&cnt[e], r);
-  }
-  __syncthreads();
-  for (int e = tid; e < C; e += nt) {
-    const int r = cnt[e];
-    if (r < k && cand[e] != 0ull) out[r] = cand[e];
-  }
-  __syncthreads();
+  return res;
 }
 
-// LDS bytes the callers of wg_topk_rank set aside for n keys: keys (padded to 64), 64
-// selected keys, and the candidate scratch.
+// LDS bytes the callers of wg_topk_bitonic set aside: one run of KP keys per wave (up to
+// 16 waves).
+__host__ __device__ constexpr int topk_kp(int k) {
+  return k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64;
+}
 __host__ __device__ constexpr int topk_lds_bytes(int n, int k) {
-  return ((n + 63) & ~63) * 8 + 64 * 8 + topk_scratch_bytes(n, k);
+  return (void)n, 16 * topk_kp(k) * 8;
 }
 
 // ------------------------------------------------------------------------------------
@@ -485,18 +600,31 @@ constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz constant cl
 // and its arrival signal travel in one store, so a reader needs one round trip, not a flag
 // read followed by a data read (bounded; an expired wait sets `errbit` and returns the
 // stale word).
+// While waiting, three polls stay in flight, one issued about every 100 ns, so the word is
+// seen about 100 ns after it lands rather than up to a full load round trip later.
 __device__ inline uint64_t wait_tagged(const uint64_t* p, uint32_t tag, uint32_t* err,
                                        uint32_t errbit) {
   uint64_t v = ld_dev64(p);
   if ((uint32_t)(v >> 32) == tag) return v;
+  uint64_t r0 = ld_dev64(p);
+  __builtin_amdgcn_s_sleep(2);
+  uint64_t r1 = ld_dev64(p);
+  __builtin_amdgcn_s_sleep(2);
+  uint64_t r2 = ld_dev64(p);
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   while (true) {
-    __builtin_amdgcn_s_sleep(1);
-    v = ld_dev64(p);
-    if ((uint32_t)(v >> 32) == tag) return v;
+    if ((uint32_t)(r0 >> 32) == tag) return r0;
+    __builtin_amdgcn_s_sleep(2);
+    r0 = ld_dev64(p);
+    if ((uint32_t)(r1 >> 32) == tag) return r1;
+    __builtin_amdgcn_s_sleep(2);
+    r1 = ld_dev64(p);
+    if ((uint32_t)(r2 >> 32) == tag) return r2;
+    __builtin_amdgcn_s_sleep(2);
+    r2 = ld_dev64(p);
     if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
       __hip_atomic_fetch_or(err, errbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return v;
+      return r2;
     }
   }
 }
@@ -504,74 +632,20 @@ __device__ inline uint64_t wait_tagged(const uint64_t* p, uint32_t tag, uint32_t
 
 // Control block at the start of every layer workspace (device memory, cleared at layer
 // creation).  `epoch` counts the batch-1 launches completed on this workspace; a launch
-// reads it at its start and tags the data it hands between workgroups (router logits,
-// channel scores) with epoch + 1, so readers wait on the data itself.  The partial outputs
-// are handed over with arrival counters that only ever grow: launch n is complete for a
-// counter group when the group reads (n + 1) * (its participant count); the counters are
-// split over kGroups cache lines, so that arrivals contend in groups of P/kGroups instead
-// of all P on one address.
-constexpr int kGroups = 16;
+// reads it at its start and tags the data it hands between workgroups with it: router
+// logits and channel gate values carry epoch + 1 in the upper half of a 64-bit word, the
+// partial outputs carry (epoch + 1) & 1 in the lowest bit of every value.  Readers wait on
+// the data itself, so there are no arrival counters.
 struct Ctrl {
   uint32_t epoch;               // launches completed on this workspace
   uint32_t err;                 // sticky error bits (read and cleared by moe_layer_check)
-  uint32_t pad0[30];
-  uint32_t done[kGroups][32];   // workgroups that published their partial output
+  uint32_t pad0[62];
 };
-static_assert(sizeof(Ctrl) == 128 + kGroups * 128, "counter groups are 128-byte lines");
+static_assert(sizeof(Ctrl) == 256, "one 256-byte block");
 
 enum : uint32_t {
   kErrRouteWait = 1u, kErrReduceWait = 2u, kErrBadId = 4u, kErrPhaseWait = 8u,
 };
 
-// Phase timeline (a separate build of the library with MOE_TIMELINE defined; the product
-// build compiles these to nothing): thread 0 of every workgroup records the 100 MHz
-// constant clock when it passes phase i of a single-launch layer kernel, into
-// stamps[workgroup][kStamps].  Recording is one scalar clock read and one store; it adds no
-// barrier, so the phases keep their order and overlap.
-constexpr int kStamps = 16;
-// stamp slots common to the single-launch kernels (each kernel numbers its other phases
-// from 1): start, partial output published, all partials arrived (reducers), y written
-enum : int { kStampStart = 0, kStampPublished = 13, kStampArrived = 14, kStampReduced = 15 };
-#ifdef MOE_TIMELINE
-#define MOE_STAMP(buf, i)                                                              \
-  do {                                                                                 \
-    if (threadIdx.x == 0 && (buf) != nullptr)                                          \
-      (buf)[blockIdx.x * ::moe::kStamps + (i)] = __builtin_amdgcn_s_memrealtime();     \
-  } while (0)
-#else
-#define MOE_STAMP(buf, i) \
-  do {                    \
-  } while (0)
-#endif
-
-__device__ __forceinline__ void arrive(uint32_t (*family)[32], int wg) {
-  add_relaxed_dev(&family[wg % kGroups][0], 1u);
-}
-
-// Participants of group g when workgroups 0..n-1 take part.
-__device__ __forceinline__ uint32_t group_count(int n, int g) {
-  return (uint32_t)(n / kGroups + (g < n % kGroups ? 1 : 0));
-}
-
-// One thread: wait until every group of `family` has seen all of launch `epoch`'s
-// arrivals from workgroups 0..n-1 (bounded; an expired wait sets `errbit`).
-__device__ inline bool wait_family(uint32_t (*family)[32], int n, uint32_t epoch,
-                                   uint32_t* err, uint32_t errbit) {
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (true) {
-    bool all = true;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      const uint32_t target = (epoch + 1u) * group_count(n, g);
-      all &= (int32_t)(load_relaxed_dev(&family[g][0]) - target) >= 0;
-    }
-    if (all) return true;
-    __builtin_amdgcn_s_sleep(1);
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-      __hip_atomic_fetch_or(err, errbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
-  }
-}
 
 }  // namespace moe

@@ -29,6 +29,9 @@ namespace {
 using namespace lc;
 
 constexpr int kMaxNP = 16;
+#ifndef MOE_B1_BF16_C
+#define MOE_B1_BF16_C 1
+#endif
 
 struct B1Launch {
   B1Args a;
@@ -76,30 +79,70 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
 
   read_epoch(ctrl, c);
 
-  // 1. router rows, spread over the first workgroups
-  router_rows<RT, CPT>(a.route_inside, a.router, a.E, xv, a.rlog, reinterpret_cast<float*>(big),
-                       reinterpret_cast<uint32_t*>(s_int), c);
-  MOE_STAMP(c.stamps, 1);
+  // 1. router rows, spread over all workgroups (one row each at E <= P)
+  RouterRound<RT, CPT> rr;
+  router_issue<RT, CPT>(a.route_inside, a.router, a.E, c, rr);
+  auto finish_router = [&] {
+    router_finish<RT, CPT>(rr, a.router, a.E, xv, a.rlog, reinterpret_cast<float*>(big),
+                           reinterpret_cast<uint32_t*>(s_int), c);
+    MOE_STAMP(c.stamps, 1);
+  };
 
-  // 2. shared experts (independent of routing): flat channel f of [NS][IS] is row f
-  if (a.NS > 0) {
-    const long long nsc = (long long)a.NS * a.IS;
-    stream_channels<ST, CS, CPT, true, true>(
-        a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, (int)(nsc * c.wg / c.P),
-        (int)(nsc * (c.wg + 1) / c.P),
-        [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
+  // The shared experts do not depend on routing.  With one row format for every expert they
+  // are the leading slots of the routed stream below, read after the routing is known: the
+  // router's loads then have the memory to themselves, and the stream has no gap between
+  // shared and routed rows.  With two formats (MXFP4 routed experts, bf16 shared ones) they
+  // stream before the routing, their first loads queued right behind the router rows', and
+  // their output moves to LDS (ysh: nteams * H floats), freeing its registers.
+  float* ysh = big + L.big_floats;
+  if constexpr (kTwo) {
+    if (a.NS > 0) {
+      const long long nsc = (long long)a.NS * a.IS;  // flat channel f of [NS][IS] is row f
+      stream_channels<ST, CS, CPT, true, true>(
+          a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, (int)(nsc * c.wg / c.P),
+          (int)(nsc * (c.wg + 1) / c.P),
+          [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c,
+          finish_router);
+    } else {
+      finish_router();
+    }
+    teams_to_lds<8, CPT>(yv, ysh, c);
+    MOE_STAMP(c.stamps, 2);
+  } else {
+    finish_router();
   }
 
-  // with two layouts the shared experts' output moves to LDS now (ysh: nteams * H floats),
-  // freeing its registers for the routed stream
-  float* ysh = big + L.big_floats;
-  if constexpr (kTwo) teams_to_lds<8, CPT>(yv, ysh, c);
-  MOE_STAMP(c.stamps, 2);
+  SlotSet ss;
+  ss.G = reinterpret_cast<const uint8_t*>(a.gate);
+  ss.V = reinterpret_cast<const uint8_t*>(a.up);
+  ss.D = reinterpret_cast<const uint8_t*>(a.down_t);
+  ss.Gs = a.gate_s;
+  ss.Vs = a.up_s;
+  ss.Ds = a.down_s;
+  ss.SG = reinterpret_cast<const uint8_t*>(a.sh_gate);
+  ss.SV = reinterpret_cast<const uint8_t*>(a.sh_up);
+  ss.SD = reinterpret_cast<const uint8_t*>(a.sh_down_t);
+  ss.I = a.I;
+  ss.IS = a.IS > 0 ? a.IS : 1;
+  ss.NS = kTwo ? 0 : a.NS;
+  ss.k = a.k;
+  ss.s_ids = s_ids;
+  ss.s_w = s_w;
+  const SlotShare share = slot_share(ss, c);
 
-  // 3. routed experts: flat channel f = slot * I + j
+  // 2. the routing (top-k of the published logits, or the given ids) in LDS.  While the
+  // waves that poll the logits wait, the other waves warm L2 with this workgroup's
+  // shared-expert rows, so the stream reads them from there and the memory's bandwidth goes
+  // to the routed rows.
+  uint32_t warm[kWarmLoads] = {0, 0};
+  if (!kTwo && a.route_inside)
+    warm_rows(ss.SG, ss.SV, ss.SD, share.s0, share.s1, (uint32_t)Fmt<ST>::row_bytes(a.H),
+              min(c.nthreads, (a.E + kWave - 1) / kWave * kWave), c, warm);
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
                 reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c);
   MOE_STAMP(c.stamps, 3);
+
+  // 3. the slot stream: [shared slots,] routed slots; flat channel f, contiguous shares
   Ctx cr = c;
   if constexpr (kTwo) {
     set_teams(cr, L.tsz_r);
@@ -113,17 +156,10 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
 #pragma unroll
     for (int i = 0; i < CPT * ER; ++i) yr[i] = 0.0f;
   }
-  {
-    const long long nrc = (long long)a.k * a.I;  // below 2^31 (checked at layer creation)
-    const int i0 = (int)(nrc * c.wg / c.P), i1 = (int)(nrc * (c.wg + 1) / c.P);
-    const int I = a.I;
-    if constexpr (kTwo)
-      stream_routed<ET, CR, CPT>(a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s, i0, i1, I,
-                                 a.k, s_ids, s_w, xr, yr, cr);
-    else
-      stream_routed<ET, CR, CPT>(a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s, i0, i1, I,
-                                 a.k, s_ids, s_w, xv, yv, c);
-  }
+  if constexpr (kTwo)
+    stream_routed<ET, CR, CPT>(ss, share, xr, yr, cr);
+  else
+    stream_routed<ET, CR, CPT>(ss, share, xv, yv, c);
 
   // 4. deterministic cross-workgroup sum of the partial outputs
   MOE_STAMP(c.stamps, 4);
@@ -132,8 +168,10 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
     publish_and_reduce(a.partials, a.y, ctrl, L.R, L.SW, big, c, ysh);
   } else {
     teams_to_lds<8, CPT>(yv, big, c);
+    MOE_STAMP(c.stamps, 5);
     publish_and_reduce(a.partials, a.y, ctrl, L.R, L.SW, big, c);
   }
+  s_int[15] = (int)(warm[0] ^ warm[1]);  // keeps the warming loads (see warm_rows)
 }
 
 template <DT ET, DT ST, DT RT, int CR, int CS, int CPT>
@@ -156,7 +194,7 @@ hipError_t launch_t(const B1Launch& L, int wgs, int threads, int lds, hipStream_
 // register stages (a bf16 or fp32 chunk holds 4 or 8 registers per row, an MXFP4 chunk 2,
 // a wide MXFP4 chunk 3, and its layout keeps 32 x and output values per thread).
 template <DT dt> constexpr int channels_per_batch() {
-  return dt == DT::MXFP4W ? 2 : dt == DT::MXFP4 ? 2 : dt == DT::BF16 ? 2 : 1;
+  return dt == DT::MXFP4W ? 2 : dt == DT::MXFP4 ? 2 : dt == DT::BF16 ? MOE_B1_BF16_C : 1;
 }
 
 template <DT ET, DT ST, DT RT>
@@ -186,7 +224,7 @@ static int b1_big_floats(int H, int threads, int E, int k) {
   const int nteams = threads / team_size(H);
   const int ybuf = nteams * H * 4;
   const int topk = topk_lds_bytes(E, k);
-  const int reduce = threads * 4;
+  const int reduce = threads * 8;  // the reducers' two floats per thread
   int big = ybuf > topk ? ybuf : topk;
   big = big > reduce ? big : reduce;
   return (big + 15) / 16 * 4;

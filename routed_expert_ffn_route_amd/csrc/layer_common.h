@@ -218,25 +218,33 @@ __device__ __forceinline__ float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Team dot products of C rows with x: returns, in every thread of the team, the C totals
-// (out[c]).  rows[c] < 0 marks an empty slot.  One barrier.  All threads must call.
+// Team dot products of C rows with x, in two halves so that the loads can be issued early
+// and other loads queued behind them: team_dots_load issues the loads of rows[] (rows[c] < 0
+// marks an empty slot), team_dots_compute returns, in every thread of the team, the C totals
+// (out[c]) -- one barrier; all threads must call.  team_dots does both.
 template <DT dt, int C, int CPT>
-__device__ __forceinline__ void team_dots(const void* base, const uint8_t* scales,
-                                          const long long (&rows)[C],
-                                          const float (&xv)[CPT * kE<dt>], Ctx& c,
-                                          float (&out)[C]) {
-  using F = Fmt<dt>;
-  typename F::Raw r[C][CPT];
+struct TeamRows {
+  typename Fmt<dt>::Raw r[C][CPT];
+};
+template <DT dt, int C, int CPT>
+__device__ __forceinline__ void team_dots_load(const void* base, const uint8_t* scales,
+                                               const long long (&rows)[C], const Ctx& c,
+                                               TeamRows<dt, C, CPT>& tr) {
 #pragma unroll
   for (int q = 0; q < C; ++q) {
     const RowSrc<dt, true> src = slot_rows<dt, true>(base, scales, rows[q], c);
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) r[q][m] = src.load(c.t + m * c.tsz, c);
+    for (int m = 0; m < CPT; ++m) tr.r[q][m] = src.load(c.t + m * c.tsz, c);
   }
+}
+template <DT dt, int C, int CPT>
+__device__ __forceinline__ void team_dots_compute(const TeamRows<dt, C, CPT>& tr,
+                                                  const float (&xv)[CPT * kE<dt>], Ctx& c,
+                                                  float (&out)[C]) {
   constexpr int NP = NextPow2<C>::value;
   float acc[NP];
 #pragma unroll
-  for (int q = 0; q < C; ++q) acc[q] = chunk_dot<dt, CPT>(r[q], xv);
+  for (int q = 0; q < C; ++q) acc[q] = chunk_dot<dt, CPT>(tr.r[q], xv);
 #pragma unroll
   for (int q = C; q < NP; ++q) acc[q] = 0.0f;
   const float tot = wave_multi_sum<NP>(acc, c.lane);
@@ -246,6 +254,15 @@ __device__ __forceinline__ void team_dots(const void* base, const uint8_t* scale
   const float v = team_totals<NP>(red, c);
 #pragma unroll
   for (int q = 0; q < C; ++q) out[q] = lane_value(v, q);
+}
+template <DT dt, int C, int CPT>
+__device__ __forceinline__ void team_dots(const void* base, const uint8_t* scales,
+                                          const long long (&rows)[C],
+                                          const float (&xv)[CPT * kE<dt>], Ctx& c,
+                                          float (&out)[C]) {
+  TeamRows<dt, C, CPT> tr;
+  team_dots_load<dt, C, CPT>(base, scales, rows, c, tr);
+  team_dots_compute<dt, C, CPT>(tr, xv, c, out);
 }
 
 // Raw weight chunks of one batch of C SwiGLU channels per team (one pipeline stage).
@@ -321,11 +338,12 @@ __device__ __forceinline__ void stage_compute(const Stage<dt, C, CPT>& st, const
 // batch b+1 are issued before batch b is reduced.  map(i, row, wt, gv) gives the weight
 // row of item i (row < 0: skip), its weight and (HAS_G false: no gate rows are read) its
 // gate value  BUF: the load path (RowSrc).
-template <DT dt, int C, int CPT, bool HAS_G, bool BUF, typename Map, typename X>
+template <DT dt, int C, int CPT, bool HAS_G, bool BUF, typename Map, typename X,
+          typename Between>
 __device__ inline void stream_channels(const void* G, const void* V, const void* D,
                                        const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
                                        int i0, int i1, Map map, const X& xv,
-                                       float (&yv)[CPT * kE<dt>], Ctx& c) {
+                                       float (&yv)[CPT * kE<dt>], Ctx& c, Between between) {
   const int per = c.nteams * C;
   const int nb = i1 > i0 ? (i1 - i0 + per - 1) / per : 0;
   auto fill = [&](Stage<dt, C, CPT>& st, int b) {
@@ -346,6 +364,7 @@ __device__ inline void stream_channels(const void* G, const void* V, const void*
   // would also wait for the other stage.
   Stage<dt, C, CPT> A, B;
   fill(A, 0);
+  between();  // work that waits on loads issued before this stream's first ones
   int b = 0;
   for (; b + 1 < nb; b += 2) {
     fill(B, b + 1);
@@ -355,83 +374,165 @@ __device__ inline void stream_channels(const void* G, const void* V, const void*
   }
   if (b < nb) stage_compute<dt, C, CPT, HAS_G>(A, xv, yv, c);
 }
+template <DT dt, int C, int CPT, bool HAS_G, bool BUF, typename Map, typename X>
+__device__ inline void stream_channels(const void* G, const void* V, const void* D,
+                                       const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
+                                       int i0, int i1, Map map, const X& xv,
+                                       float (&yv)[CPT * kE<dt>], Ctx& c) {
+  stream_channels<dt, C, CPT, HAS_G, BUF>(G, V, D, Gs, Vs, Ds, i0, i1, map, xv, yv, c, [] {});
+}
 
-// The routed experts' channels [i0, i1): flat channel f = slot * I + j is row j of expert
-// s_ids[slot] (negative: an empty slot), weighted by s_w[slot].  The same two-stage stream
-// as stream_channels, but the team's items are walked incrementally: (slot, j) of its next
-// first item advances by a batch per fill, and the current and next slot's expert offsets
-// stay in scalar registers, so an item's three row addresses are a 32-bit multiply and
-// 64-bit adds (the host admits E * I < 2^31; a row offset within one expert, I * row bytes,
-// stays below 2^32).  Every wave of the compute unit issues this scalar code, and scalar
-// instructions issue at the rate of vector ones, so the per-item divisions and 64-bit
-// multiplications of the generic map made the stream scalar-bound.
+// Expert rows of a slot stream: NS shared slots first (slot s < NS: the I_s rows of shared
+// expert s, weight 1), then the k routed slots (slot NS + r: the I rows of expert s_ids[r],
+// weight s_w[r]; an id < 0 is an empty slot).  All slots share one row format.
+struct SlotSet {
+  const uint8_t *G, *V, *D;        // routed [E][I][H]
+  const uint8_t *Gs, *Vs, *Ds;     // routed MXFP4 scales or null
+  const uint8_t *SG, *SV, *SD;     // shared [NS][IS][H] (NS > 0)
+  int I, IS, NS, k;
+  const int* s_ids;
+  const float* s_w;
+};
+
+// A workgroup's share of the slot stream: shared channels [s0, s1) (flat shared channel f is
+// row f % IS of shared expert f / IS) followed by routed channels [r0, r1) (flat routed
+// channel f is row f % I of routed slot f / I), walked as one sequence of items.  Giving
+// every workgroup a slice of both keeps the shared rows spread over the whole chip.
+struct SlotShare {
+  int s0, s1, r0, r1;
+};
+__device__ __forceinline__ SlotShare slot_share(const SlotSet& ss, const Ctx& c) {
+  const long long nsh = (long long)ss.NS * ss.IS, nrt = (long long)ss.k * ss.I;
+  SlotShare sh;
+  sh.s0 = (int)(nsh * c.wg / c.P);
+  sh.s1 = (int)(nsh * (c.wg + 1) / c.P);
+  sh.r0 = (int)(nrt * c.wg / c.P);
+  sh.r1 = (int)(nrt * (c.wg + 1) / c.P);
+  return sh;
+}
+
+// The share's items, in batches of C per team, two batches in flight, as stream_channels.
+// The team's items are walked incrementally: (slot, j) of its next first item advances by a
+// batch per fill, and the current and next slot's row bases stay in scalar registers, so an
+// item's three row addresses are a 32-bit multiply and pointer adds (a row offset within one
+// expert, I * row bytes, stays below 2^32).  Every wave of the compute unit issues this
+// scalar code, and scalar instructions issue at the rate of vector ones, so per-item
+// divisions and 64-bit multiplications made the stream scalar-bound.  Only the step from the
+// shared items to the routed ones (once per team) divides again.
 template <DT dt, int C, int CPT, typename X>
-__device__ inline void stream_routed(const void* G, const void* V, const void* D,
-                                     const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
-                                     int i0, int i1, int I, int k, const int* s_ids,
-                                     const float* s_w, const X& xv,
+__device__ inline void stream_routed(const SlotSet& ss, const SlotShare& sh, const X& xv,
                                      float (&yv)[CPT * kE<dt>], Ctx& c) {
   using F = Fmt<dt>;
   const int per = c.nteams * C;
-  const int nb = i1 > i0 ? (i1 - i0 + per - 1) / per : 0;
+  const int ns = sh.s1 - sh.s0, n = ns + (sh.r1 - sh.r0);
+  const int nb = (n + per - 1) / per;
   const uint32_t rb = (uint32_t)F::row_bytes(c.H);
   const uint32_t sb = (uint32_t)(c.H / 32);
-  const uint8_t* const gb = reinterpret_cast<const uint8_t*>(G);
-  const uint8_t* const vb = reinterpret_cast<const uint8_t*>(V);
-  const uint8_t* const db = reinterpret_cast<const uint8_t*>(D);
+  const int nsl = ss.NS + ss.k;
   struct SlotState {
-    uint64_t od, os;  // byte offsets of the expert's rows and scale rows
+    const uint8_t *g, *v, *d;     // first row of the slot's expert
+    const uint8_t *gs, *vs, *ds;  // its scale rows (or null)
     float wt;
+    int width;                    // channels of the slot
     bool ok;
   };
   auto slot_state = [&](int sl) {
     SlotState st;
-    const int sc = sl < k ? sl : 0;
-    const int e = __builtin_amdgcn_readfirstlane(s_ids[sc]);
-    st.ok = sl < k && e >= 0;
-    const uint64_t r = (uint64_t)(st.ok ? e : 0) * (uint64_t)I;
-    st.od = r * rb;
-    st.os = r * sb;
-    st.wt = s_w[sc];
+    st.gs = st.vs = st.ds = nullptr;
+    if (sl < ss.NS) {
+      const uint64_t o = (uint64_t)(uint32_t)sl * (uint32_t)ss.IS * rb;
+      st.g = ss.SG + o;
+      st.v = ss.SV + o;
+      st.d = ss.SD + o;
+      st.wt = 1.0f;
+      st.width = ss.IS;
+      st.ok = true;
+    } else {
+      const int r = sl - ss.NS;
+      const int rc = r < ss.k ? r : 0;
+      const int e = __builtin_amdgcn_readfirstlane(ss.s_ids[rc]);
+      st.ok = r < ss.k && e >= 0;
+      const uint64_t row = (uint64_t)(st.ok ? e : 0) * (uint64_t)ss.I;
+      st.g = ss.G + row * rb;
+      st.v = ss.V + row * rb;
+      st.d = ss.D + row * rb;
+      if (ss.Gs) {
+        st.gs = ss.Gs + row * sb;
+        st.vs = ss.Vs + row * sb;
+        st.ds = ss.Ds + row * sb;
+      }
+      st.wt = ss.s_w[rc];
+      st.width = ss.I;
+    }
     return st;
   };
-  int f = i0 + c.team * C;  // the team's first item of the next batch
-  int slot = f / I, j = f - slot * I;
-  SlotState cur = slot_state(slot), nxt = slot_state(slot + 1);
+  // (slot, j) of the share's item v (divisions)
+  auto pos_of = [&](int v, int& slot, int& j) {
+    if (v < ns) {
+      const int f = sh.s0 + v;
+      slot = f / ss.IS;
+      j = f - slot * ss.IS;
+    } else {
+      const int f = sh.r0 + (v - ns);
+      slot = ss.NS + f / ss.I;
+      j = f - (slot - ss.NS) * ss.I;
+    }
+    if (slot > nsl) slot = nsl;
+  };
+  int v = c.team * C;  // the team's first item of the next batch
+  int slot, j;
+  pos_of(v, slot, j);
+  SlotState cur = slot_state(slot), nxt = slot_state(slot + 1 < nsl ? slot + 1 : nsl);
   const int ch0 = c.t;
   auto fill = [&](Stage<dt, C, CPT>& st) {
+    const bool straddle = v < ns && v + C > ns;  // the batch holds both kinds of items
 #pragma unroll
     for (int q = 0; q < C; ++q) {
-      const bool wrap = j + q >= I;
-      const int jq = wrap ? j + q - I : j + q;
-      const SlotState& ss = wrap ? nxt : cur;
-      const bool live = f + q < i1 && ss.ok;
-      const uint64_t od = ss.od + (uint64_t)((uint32_t)jq * rb);
-      const uint64_t os = ss.os + (uint64_t)((uint32_t)jq * sb);
-      RowSrc<dt, false> gs, vs, ds;
-      gs.w = uniform_ptr(live ? gb + od : c.zrow);
-      vs.w = uniform_ptr(live ? vb + od : c.zrow);
-      ds.w = uniform_ptr(live ? db + od : c.zrow);
-      gs.s = uniform_ptr(live && Gs ? Gs + os : c.zrow);
-      vs.s = uniform_ptr(live && Vs ? Vs + os : c.zrow);
-      ds.s = uniform_ptr(live && Ds ? Ds + os : c.zrow);
-      st.wt[q] = live ? ss.wt : 0.0f;
+      int jq;
+      SlotState sq;
+      if (C > 1 && straddle) {
+        int sl;
+        pos_of(v + q, sl, jq);
+        sq = slot_state(sl);
+      } else {
+        const bool wrap = j + q >= cur.width;
+        jq = wrap ? j + q - cur.width : j + q;
+        sq = wrap ? nxt : cur;
+      }
+      const bool live = v + q < n && sq.ok;
+      const uint32_t od = (uint32_t)jq * rb;
+      const uint32_t os = (uint32_t)jq * sb;
+      RowSrc<dt, false> gsrc, vsrc, dsrc;
+      gsrc.w = uniform_ptr(live ? sq.g + od : c.zrow);
+      vsrc.w = uniform_ptr(live ? sq.v + od : c.zrow);
+      dsrc.w = uniform_ptr(live ? sq.d + od : c.zrow);
+      gsrc.s = uniform_ptr(live && sq.gs ? sq.gs + os : c.zrow);
+      vsrc.s = uniform_ptr(live && sq.vs ? sq.vs + os : c.zrow);
+      dsrc.s = uniform_ptr(live && sq.ds ? sq.ds + os : c.zrow);
+      st.wt[q] = live ? sq.wt : 0.0f;
       st.gv[q] = 0.0f;
 #pragma unroll
       for (int m = 0; m < CPT; ++m) {
         const int ch = ch0 + m * c.tsz;
-        st.g[q][m] = gs.load(ch, c);
-        st.v[q][m] = vs.load(ch, c);
-        st.d[q][m] = ds.load(ch, c);
+        st.g[q][m] = gsrc.load(ch, c);
+        st.v[q][m] = vsrc.load(ch, c);
+        st.d[q][m] = dsrc.load(ch, c);
       }
     }
-    f += per;
-    j += per;
-    while (j >= I) {
-      j -= I;
-      ++slot;
-      cur = nxt;
-      nxt = slot_state(slot + 1);
+    const int v0 = v;
+    v += per;
+    if (v0 < ns && v >= ns) {  // from the shared items to the routed ones
+      pos_of(v, slot, j);
+      cur = slot_state(slot);
+      nxt = slot_state(slot + 1 < nsl ? slot + 1 : nsl);
+    } else {
+      j += per;
+      while (j >= cur.width && slot < nsl) {
+        j -= cur.width;
+        ++slot;
+        cur = nxt;
+        nxt = slot_state(slot + 1 < nsl ? slot + 1 : nsl);
+      }
     }
   };
   Stage<dt, C, CPT> A, B;
@@ -446,66 +547,117 @@ __device__ inline void stream_routed(const void* G, const void* V, const void* D
   if (b < nb) stage_compute<dt, C, CPT, true>(A, xv, yv, c);
 }
 
-// Router logits, spread over the first workgroups (one team per row).  Each logit is
-// published as one 64-bit word: the launch tag (epoch + 1) in the upper half and the fp32
-// bits in the lower half, so readers wait on the data itself.  Every workgroup also learns
-// the launch epoch here (thread 0 loaded it at the start; the router rows hide the wait).
-// `buf` is LDS of at least ceil(E / P) + nteams floats; s_ep one LDS word.
-template <DT RT, int CPT>
-__device__ inline void router_rows(bool compute, const void* router, int E,
-                                   const float (&xv)[CPT * kE<RT>], uint64_t* rlog, float* buf,
-                                   uint32_t* s_ep, Ctx& c) {
-  const int n_router_wgs = min(c.P, (E + c.nteams - 1) / c.nteams);
-  const bool mine = compute && c.wg < n_router_wgs;
-  int nloc = 0;
-  if (mine) {
-    for (int base = c.wg * c.nteams; base < E; base += c.P * c.nteams, nloc += c.nteams) {
-      const int e = base + c.team;
-      const long long rows[1] = {e < E ? (long long)e : -1};
-      float l[1];
-      team_dots<RT, 1, CPT>(router, nullptr, rows, xv, c, l);
-      if (c.t == 0) buf[nloc + c.team] = l[0];
-    }
-  }
-  if (c.tid == 0) *s_ep = c.epoch;
-  __syncthreads();
-  c.epoch = *s_ep;
-  if (mine) {
-    const uint64_t tag = (uint64_t)(c.epoch + 1u) << 32;
-    for (int i = c.tid; i < nloc; i += c.nthreads) {
-      const int e = c.wg * c.nteams + (i / c.nteams) * c.P * c.nteams + i % c.nteams;
-      if (e < E) st_dev64(rlog + e, tag | __float_as_uint(buf[i]));
+// Warm L2 with rows [s0, s1) of three stacked [rows][H] tensors (a share's shared-expert
+// rows, which do not depend on routing), using the threads from `first` on (whose waves have
+// nothing else in flight): one 4-byte load per 128-byte line, plain loads so that the lines
+// are allocated in L2 and the stream's later reads of them hit there, at most kWarmLoads per
+// thread.  The values go to w[], which the caller keeps alive to the end of the kernel, so
+// the loads are neither removed nor waited for before then.
+constexpr int kWarmLoads = 2;
+__device__ inline void warm_rows(const uint8_t* G, const uint8_t* V, const uint8_t* D, int s0,
+                                 int s1, uint32_t rb, int first, const Ctx& c,
+                                 uint32_t (&w)[kWarmLoads]) {
+  const uint32_t lines = s1 > s0 ? (uint32_t)(s1 - s0) * (rb / 128) : 0u;  // per tensor
+  const uint32_t nthr = c.nthreads > first ? (uint32_t)(c.nthreads - first) : 1u;
+  const uint32_t me = c.tid >= first ? (uint32_t)(c.tid - first) : 3u * lines;
+#pragma unroll
+  for (int u = 0; u < kWarmLoads; ++u) {
+    const uint32_t i = me + (uint32_t)u * nthr;
+    w[u] = 0;
+    if (i < 3 * lines) {
+      const uint32_t t = i / lines, r = i - t * lines;
+      const uint8_t* base = t == 0 ? G : t == 1 ? V : D;
+      w[u] = *reinterpret_cast<const uint32_t*>(base + (size_t)s0 * rb + 128ull * r);
     }
   }
 }
 
-// Exact top-k of the E logits and the softmax over the k selected, computed by the whole
-// workgroup into LDS (s_ids, s_w).  `keys` is LDS scratch of topk_lds_bytes(E) bytes.
-__device__ inline void topk_local(const uint64_t* rlog, int E, int k, uint64_t* keys,
-                                  int* s_ids, float* s_w, uint32_t* err, const Ctx& c) {
-  const int E64 = (E + 63) & ~63;
-  uint64_t* sel = keys + E64;
-  const uint32_t tag = c.epoch + 1u;
-  for (int e = c.tid; e < E64; e += c.nthreads) {
-    uint64_t key = 0ull;  // padding: below every real key
-    if (e < E) {
-      const uint64_t v = wait_tagged(rlog + e, tag, err, kErrRouteWait);
-      key = make_key(__uint_as_float((uint32_t)v), (uint32_t)e);
-    }
-    keys[e] = key;
+// Router logits, spread over all workgroups: workgroup wg computes rows wg, wg + P, ...
+// (one team per row), so every router row is done at about the same time and no workgroup
+// carries more than ceil(E / P) rows.  In two halves: router_issue issues the loads of the
+// first round of rows (one row per team) so that the shared experts' first loads can be
+// queued right behind them; router_finish computes those dots (then any further rounds),
+// and publishes each logit as one 64-bit word: the launch tag (epoch + 1) in the upper half
+// and the fp32 bits in the lower half, so readers wait on the data itself.  Every workgroup
+// also learns the launch epoch here (thread 0 loaded it at the start).  `buf` is LDS of at
+// least ceil(E / P) floats; s_ep one LDS word.
+template <DT RT, int CPT>
+struct RouterRound {
+  int nrows;  // this workgroup's rows (wave-uniform)
+  TeamRows<RT, 1, CPT> tr;
+};
+template <DT RT, int CPT>
+__device__ inline void router_issue(bool compute, const void* router, int E, const Ctx& c,
+                                    RouterRound<RT, CPT>& rr) {
+  rr.nrows = compute && c.wg < E ? (E - 1 - c.wg) / c.P + 1 : 0;
+  if (rr.nrows > 0) {
+    const long long rows[1] = {c.team < rr.nrows ? (long long)c.wg + (long long)c.P * c.team
+                                                 : -1ll};
+    team_dots_load<RT, 1, CPT>(router, nullptr, rows, c, rr.tr);
   }
+}
+template <DT RT, int CPT>
+__device__ inline void router_finish(const RouterRound<RT, CPT>& rr, const void* router, int E,
+                                     const float (&xv)[CPT * kE<RT>], uint64_t* rlog,
+                                     float* buf, uint32_t* s_ep, Ctx& c) {
+  const int nrows = rr.nrows;
+  if (nrows > 0) {
+    float l[1];
+    team_dots_compute<RT, 1, CPT>(rr.tr, xv, c, l);
+    if (c.t == 0 && c.team < nrows) buf[c.team] = l[0];
+    for (int m0 = c.nteams; m0 < nrows; m0 += c.nteams) {
+      const int m = m0 + c.team;
+      const long long rows[1] = {m < nrows ? (long long)c.wg + (long long)c.P * m : -1ll};
+      team_dots<RT, 1, CPT>(router, nullptr, rows, xv, c, l);
+      if (c.t == 0 && m < nrows) buf[m] = l[0];
+    }
+    MOE_STAMP(c.stamps, kStampRouterDots);
+  }
+  if (c.tid == 0) *s_ep = c.epoch;
   __syncthreads();
-  wg_topk_rank(keys, sel + 64, E, k, sel);
+  c.epoch = *s_ep;
+  const uint64_t tag = (uint64_t)(c.epoch + 1u) << 32;
+  for (int m = c.tid; m < nrows; m += c.nthreads)
+    st_dev64(rlog + c.wg + (size_t)c.P * m, tag | __float_as_uint(buf[m]));
+}
+
+// Exact top-k of the E logits and the softmax over the k selected, computed by the whole
+// workgroup into LDS (s_ids, s_w): the waves poll the tagged logits themselves and select in
+// registers (wg_topk_bitonic); wave 0 then forms the weights.  `keys` is LDS scratch of
+// topk_lds_bytes(E, k) bytes.
+template <int KP>
+__device__ inline void topk_local_kp(const uint64_t* rlog, int E, int k, uint64_t* keys,
+                                     int* s_ids, float* s_w, uint32_t* err, const Ctx& c) {
+  const uint32_t tag = c.epoch + 1u;
+  const uint64_t top = wg_topk_bitonic<KP>(
+      E,
+      [&](int e) {
+        const uint64_t v = wait_tagged(rlog + e, tag, err, kErrRouteWait);
+        return make_key(__uint_as_float((uint32_t)v), (uint32_t)e);
+      },
+      keys, c.stamps);
+  MOE_STAMP(c.stamps, kStampRanked);
   if (c.tid < kWave) {
-    const float l0 = key_value(sel[0]);
-    const float ex = c.tid < k ? expf(key_value(sel[c.tid]) - l0) : 0.0f;
+    // the largest selected logit (lane 0's key) for a max-subtracted softmax
+    const float l0 = from_ordered_bits(__builtin_amdgcn_readfirstlane((uint32_t)(top >> 32)));
+    const float ex = c.tid < k ? expf(key_value(top) - l0) : 0.0f;
     const float sum = wave_sum(ex);
     if (c.tid < k) {
-      s_ids[c.tid] = (int)key_index(sel[c.tid]);
+      s_ids[c.tid] = (int)key_index(top);
       s_w[c.tid] = ex / sum;
     }
   }
   __syncthreads();
+}
+__device__ inline void topk_local(const uint64_t* rlog, int E, int k, uint64_t* keys,
+                                  int* s_ids, float* s_w, uint32_t* err, const Ctx& c) {
+  if (k <= 1) topk_local_kp<1>(rlog, E, k, keys, s_ids, s_w, err, c);
+  else if (k <= 2) topk_local_kp<2>(rlog, E, k, keys, s_ids, s_w, err, c);
+  else if (k <= 4) topk_local_kp<4>(rlog, E, k, keys, s_ids, s_w, err, c);
+  else if (k <= 8) topk_local_kp<8>(rlog, E, k, keys, s_ids, s_w, err, c);
+  else if (k <= 16) topk_local_kp<16>(rlog, E, k, keys, s_ids, s_w, err, c);
+  else if (k <= 32) topk_local_kp<32>(rlog, E, k, keys, s_ids, s_w, err, c);
+  else topk_local_kp<64>(rlog, E, k, keys, s_ids, s_w, err, c);
 }
 
 // The routing of this token in LDS (s_ids, s_w).  Inside the launch: wait until every
@@ -589,59 +741,133 @@ __device__ inline void add_teams_to_lds(const float (&yv)[CPT * E], float* big, 
   }
 }
 
-// Publish src[0 .. H) (default: big) as this workgroup's partial output and arrive on the
-// done counters;
-// R fixed workgroups (every (P/R)-th) then each sum an SW-column slice over all P
-// partials in a fixed order (p ascending in strided groups, then a fixed tree).  The first
-// reducer, once every workgroup has arrived, advances the epoch for the next launch.
-// `big` is LDS of at least max(H, nthreads) floats.
+// Publish src[0 .. H) (default: big) as this workgroup's partial output row, then (R fixed
+// workgroups, every (P/R)-th) sum an SW-column slice of y over all P partial rows in a
+// fixed order.  Deterministic: no float atomics, the same order in every launch.
+//
+// Hand-off without counters or fences: every value of a partial row carries the launch's
+// parity ((epoch + 1) & 1) in its lowest mantissa bit, and is written with device-scope
+// 64-bit stores; the reducer clears that bit again before adding, so the sum sees the value
+// with its last mantissa bit cleared in every launch (a change of at most one unit in the
+// last place, the same in every launch: results stay bit-identical).  Every launch writes every
+// partial row in full, so before this launch's store a word holds the previous launch's
+// value, whose parity differs (or the zeros of layer creation, parity 0, before the first
+// launch, whose parity is 1).  A reducer therefore polls the partial values themselves:
+// it is done with a word once both of its floats show this launch's parity, so the sum
+// starts as the partials arrive and ends one round trip after the last one lands.  The
+// first reducer, once it has seen every workgroup's partial (so every workgroup has read the
+// epoch), advances the epoch for the next launch.  `big` is LDS of at least
+// max(H, nthreads) floats.
+__device__ __forceinline__ float with_parity(float v, uint32_t par) {
+  return __uint_as_float((__float_as_uint(v) & ~1u) | par);
+}
+__device__ inline bool parity_ok(uint64_t v, uint32_t par) {
+  return (((uint32_t)v & 1u) == par) && (((uint32_t)(v >> 32) & 1u) == par);
+}
 __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl, int R, int SW,
                                           float* big, const Ctx& c, const float* src = nullptr) {
   const int H = c.H;
   if (!src) src = big;
-  for (int h = c.tid; h < H; h += c.nthreads) st_dev(partials + (size_t)c.wg * H + h, src[h]);
-  stores_complete();
-  __syncthreads();
+  const uint32_t par = (c.epoch + 1u) & 1u;
+  uint64_t* prow = reinterpret_cast<uint64_t*>(partials + (size_t)c.wg * H);
+  for (int h2 = c.tid; h2 < H / 2; h2 += c.nthreads) {
+    const uint32_t lo = __float_as_uint(with_parity(src[2 * h2], par));
+    const uint32_t hi = __float_as_uint(with_parity(src[2 * h2 + 1], par));
+    st_dev64(prow + h2, ((uint64_t)hi << 32) | lo);
+  }
   MOE_STAMP(c.stamps, kStampPublished);
-  if (c.tid == 0) arrive(ctrl->done, c.wg);
   const int stride = c.P / R;
   if (c.wg % stride != 0 || c.wg / stride >= R) return;
   const int r = c.wg / stride;
-  if (c.tid == 0) {
-    wait_family(ctrl->done, c.P, c.epoch, &ctrl->err, kErrReduceWait);
-    if (r == 0) store_relaxed_dev(&ctrl->epoch, c.epoch + 1u);
-  }
-  __syncthreads();
-  MOE_STAMP(c.stamps, kStampArrived);
+  __syncthreads();  // src may alias big, which the reduction below reuses
+  // Thread layout of a reducer: word q = tid % NW of the slice (two columns), partial rows
+  // p = g, g + G, ... with g = tid / NW; each thread sums its rows in ascending p, then the
+  // G groups are summed in a fixed tree (across the lanes of a wave, then across waves).
   const int h0 = r * SW;
   const int wslice = min(SW, H - h0);
-  const int SWB = SW < c.nthreads ? SW : c.nthreads;  // columns per pass (power of two)
-  const int G = c.nthreads / SWB;
-  const int g = c.tid / SWB, col0 = c.tid % SWB;
-  for (int cb = 0; cb < wslice; cb += SWB) {
-    const int col = cb + col0;
-    float s = 0.0f;
-    if (col < wslice) {
-      // eight loads in flight, summed in ascending p (a fixed order)
-      for (int p0 = g; p0 < c.P; p0 += 8 * G) {
-        float v[8];
+  const int NW = SW / 2;                       // words per slice row (SW is a power of two)
+  const int G = c.nthreads / NW;               // row groups (NW <= 64 keeps G >= 16)
+  const int q = c.tid % NW, g = c.tid / NW;
+  const bool live = 2 * q < wslice;
+  float s0 = 0.0f, s1 = 0.0f;
+  if (live) {
+    constexpr int kBatch = 8;  // loads in flight per thread
+    for (int p0 = g; p0 < c.P; p0 += kBatch * G) {
+      const uint64_t* src[kBatch];
+      uint64_t v[kBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int p = p0 + u * G;
-          v[u] = p < c.P ? ld_dev(partials + (size_t)p * H + h0 + col) : 0.0f;
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = min(p0 + u * G, c.P - 1);  // rows past P re-read the last (not summed)
+        src[u] = reinterpret_cast<const uint64_t*>(partials + (size_t)p * H + h0) + q;
+        v[u] = ld_dev64(src[u]);
+      }
+      // the words not yet of this launch are polled again together, so the batch costs one
+      // round trip after its last word lands (bounded like wait_tagged)
+      uint32_t late = 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) late |= parity_ok(v[u], par) ? 0u : 1u << u;
+      if (late) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (late) {
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (late & (1u << u)) v[u] = ld_dev64(src[u]);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (parity_ok(v[u], par)) late &= ~(1u << u);
+          if (late && __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            __hip_atomic_fetch_or(&ctrl->err, kErrReduceWait, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
         }
+      }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < kBatch; ++u) {
+        if (p0 + u * G < c.P) {
+          s0 += __uint_as_float((uint32_t)v[u] & ~1u);
+          s1 += __uint_as_float((uint32_t)(v[u] >> 32) & ~1u);
+        }
       }
     }
-    big[g * SWB + col0] = s;
-    __syncthreads();
-    for (int st = G >> 1; st >= 1; st >>= 1) {
-      if (g < st) big[g * SWB + col0] += big[(g + st) * SWB + col0];
-      __syncthreads();
+  }
+  MOE_STAMP(c.stamps, kStampArrived);
+  // groups within a wave: lanes that share q (lane % NW), summed over the higher lane bits
+  if (NW < kWave) {
+    if (NW == 16) { s0 = sum_lanes_above<16>(s0); s1 = sum_lanes_above<16>(s1); }
+    else if (NW == 32) { s0 = sum_lanes_above<32>(s0); s1 = sum_lanes_above<32>(s1); }
+    else if (NW == 8) { s0 = sum_lanes_above<8>(s0); s1 = sum_lanes_above<8>(s1); }
+    else if (NW == 4) { s0 = sum_lanes_above<4>(s0); s1 = sum_lanes_above<4>(s1); }
+    else if (NW == 2) { s0 = sum_lanes_above<2>(s0); s1 = sum_lanes_above<2>(s1); }
+    else { s0 = sum_lanes_above<1>(s0); s1 = sum_lanes_above<1>(s1); }
+  }
+  // then the waves (each holds every word of the slice once when NW <= 64), in wave order
+  const int wave = c.tid / kWave, nw = c.nthreads / kWave;
+  const int lane = c.tid % kWave;
+  const int NWw = NW < kWave ? NW : kWave;     // words per wave
+  const int wpr = NW / NWw;                    // waves per group row (NW > 64: several)
+  if (lane < NWw) {
+    big[2 * (wave * NWw + lane)] = s0;
+    big[2 * (wave * NWw + lane) + 1] = s1;
+  }
+  __syncthreads();
+  MOE_STAMP(c.stamps, kStampAllPolled);
+  if (r == 0 && c.tid == 0) store_relaxed_dev(&ctrl->epoch, c.epoch + 1u);
+  for (int col = c.tid; col < wslice; col += c.nthreads) {
+    const int qq = col / 2, par2 = col % 2;
+    const int wq = qq / NWw, lq = qq % NWw;    // wave within a group row, lane
+    // the (at most 16) values are read together, then added in wave order
+    constexpr int kMaxWaves = 1024 / kWave;
+    float v[kMaxWaves];
+#pragma unroll
+    for (int u = 0; u < kMaxWaves; ++u) {
+      const int w0 = wq + u * wpr;
+      v[u] = w0 < nw ? big[2 * (w0 * NWw + lq) + par2] : 0.0f;
     }
-    if (g == 0 && col < wslice) y[h0 + col] = big[col0];
-    __syncthreads();
+    float t = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kMaxWaves; ++u) t += v[u];
+    y[h0 + col] = t;
   }
   MOE_STAMP(c.stamps, kStampReduced);
 }

@@ -85,8 +85,11 @@ bool desc_valid(const moe_layer_desc* d, std::string* why) {
     if (d->n_shared > 0) {
       if (d->shared_inter < 8 || d->shared_inter % 8 != 0)
         return bad("shared_inter must be a positive multiple of 8");
-      if ((long long)d->n_shared * d->shared_inter > 0x7FFFFFFFll)
-        return bad("n_shared * shared_inter must be below 2^31");
+      if ((long long)d->n_shared * d->shared_inter + (long long)d->top_k * d->inter >
+          0x7FFFFFFFll)
+        return bad("n_shared * shared_inter + top_k * inter must be below 2^31");
+      if ((long long)d->shared_inter * d->hidden * 4 >= (1ll << 32))
+        return bad("shared_inter * hidden must be below 2^30");
       if (d->shared_dtype != MOE_F32 && d->shared_dtype != MOE_BF16)
         return bad("shared_dtype must be F32 or BF16");
     }

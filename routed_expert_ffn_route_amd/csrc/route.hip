@@ -84,38 +84,31 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
   }
 }
 
-// Top-k + softmax: one workgroup per token.
+// Top-k + softmax: one workgroup per token (wg_topk_bitonic: the waves read the logits and
+// select in registers; wave 0 forms the weights).
+template <int KP>
 __global__ __launch_bounds__(1024) void topk_kernel(const float* logits, float* logits_copy,
                                                    int E, int k, int B, int32_t* ids,
                                                    float* w) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
-  const int E64 = (E + 63) & ~63;
-  uint64_t* sel = keys + E64;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem);
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
     const float* lb = logits + (size_t)b * E;
-    for (int e = threadIdx.x; e < E64; e += blockDim.x) {
-      uint64_t key = 0ull;  // padding: below every real key
-      if (e < E) {
-        const float l = lb[e];
-        key = make_key(l, (uint32_t)e);
-        if (logits_copy) logits_copy[(size_t)b * E + e] = l;
-      }
-      keys[e] = key;
-    }
-    __syncthreads();
-    wg_topk_rank(keys, sel + 64, E, k, sel);
+    if (logits_copy)
+      for (int e = threadIdx.x; e < E; e += blockDim.x) logits_copy[(size_t)b * E + e] = lb[e];
+    const uint64_t top = wg_topk_bitonic<KP>(
+        E, [&](int e) { return make_key(lb[e], (uint32_t)e); }, cand);
     if (threadIdx.x < kWave) {
       const int i = threadIdx.x;
-      const float l0 = key_value(sel[0]);
-      const float ex = i < k ? expf(key_value(sel[i]) - l0) : 0.0f;
+      const float l0 = from_ordered_bits(__builtin_amdgcn_readfirstlane((uint32_t)(top >> 32)));
+      const float ex = i < k ? expf(key_value(top) - l0) : 0.0f;
       const float sum = wave_sum(ex);
       if (i < k) {
-        ids[(size_t)b * k + i] = (int32_t)key_index(sel[i]);
+        ids[(size_t)b * k + i] = (int32_t)key_index(top);
         w[(size_t)b * k + i] = ex / sum;
       }
     }
-    __syncthreads();
+    __syncthreads();  // cand is reused by the next token
   }
 }
 
@@ -286,11 +279,20 @@ hipError_t launch_route(const RouteArgs& a, DT rt, hipStream_t s) {
     if (e != hipSuccess) return e;
     lsrc = a.logits;
   }
-  const int lds = topk_lds_bytes(a.E, a.k);
+  const int lds = 16 * topk_kp(a.k) * 8;
   const int grid = a.B < 4096 ? a.B : 4096;
   float* copy = (a.logits_in && a.logits) ? a.logits : nullptr;
-  hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(1024), lds, s, lsrc, copy, a.E, a.k, a.B,
-                     a.ids, a.w);
+  switch (topk_kp(a.k)) {
+#define MOE_TOPK_CASE(KP)                                                                   \
+  case KP:                                                                                  \
+    hipLaunchKernelGGL(topk_kernel<KP>, dim3(grid), dim3(1024), lds, s, lsrc, copy, a.E, a.k, \
+                       a.B, a.ids, a.w);                                                    \
+    break;
+    MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(4) MOE_TOPK_CASE(8) MOE_TOPK_CASE(16)
+    MOE_TOPK_CASE(32) MOE_TOPK_CASE(64)
+#undef MOE_TOPK_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
