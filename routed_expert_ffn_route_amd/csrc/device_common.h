@@ -65,9 +65,19 @@ enum : int {
     if (threadIdx.x == 0 && (buf) != nullptr)                                          \
       (buf)[blockIdx.x * ::moe::kStamps + (i)] = __builtin_amdgcn_s_memrealtime();     \
   } while (0)
+// the same once `val` (a register value) has been computed: the clock read is otherwise
+// free to move ahead of arithmetic it does not depend on
+#define MOE_STAMP_AFTER(buf, i, val)     \
+  do {                                   \
+    asm volatile("" ::"v"(val));         \
+    MOE_STAMP(buf, i);                   \
+  } while (0)
 #else
 #define MOE_STAMP(buf, i) \
   do {                    \
+  } while (0)
+#define MOE_STAMP_AFTER(buf, i, val) \
+  do {                               \
   } while (0)
 #endif
 

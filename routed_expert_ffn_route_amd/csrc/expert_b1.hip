@@ -128,7 +128,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   ss.k = a.k;
   ss.s_ids = s_ids;
   ss.s_w = s_w;
-  const SlotShare share = slot_share(ss, c);
+  const SlotShare share = slot_share(ss, c, L.R);
 
   // 2. the routing (top-k of the published logits, or the given ids) in LDS.  While the
   // waves that poll the logits wait, the other waves warm L2 with this workgroup's
@@ -157,12 +157,14 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
     for (int i = 0; i < CPT * ER; ++i) yr[i] = 0.0f;
   }
   if constexpr (kTwo)
-    stream_routed<ET, CR, CPT>(ss, share, xr, yr, cr);
+    stream_routed_flat<ET, CR, CPT>(a.gate, a.up, a.down_t, a.gate_s, a.up_s, a.down_s,
+                                    share.r0, share.r1, a.I, a.k, s_ids, s_w, xr, yr, cr);
   else
     stream_routed<ET, CR, CPT>(ss, share, xv, yv, c);
 
   // 4. deterministic cross-workgroup sum of the partial outputs
-  MOE_STAMP(c.stamps, 4);
+  if constexpr (kTwo) MOE_STAMP_AFTER(c.stamps, 4, yr[0]);
+  else MOE_STAMP_AFTER(c.stamps, 4, yv[0]);
   if constexpr (kTwo) {
     add_teams_to_lds<ER, CPT>(yr, ysh, cr);
     publish_and_reduce(a.partials, a.y, ctrl, L.R, L.SW, big, c, ysh);
@@ -199,7 +201,10 @@ template <DT dt> constexpr int channels_per_batch() {
 
 template <DT ET, DT ST, DT RT>
 hipError_t launch_cpt(const B1Launch& L, int wgs, int threads, int lds, hipStream_t s) {
-  constexpr int CR = channels_per_batch<ET>(), CS = channels_per_batch<ST>();
+  // the shared experts stream on their own before the routing when the formats differ (two
+  // channels per team there, as the routed MXFP4 rows); otherwise they are slots of the
+  // routed stream and CS is unused
+  constexpr int CR = channels_per_batch<ET>(), CS = ET == DT::MXFP4W ? 2 : CR;
   // team_size gives one chunk per thread for every H the host admits (H <= 8192)
   if (L.a.H / 8 > L.tsz) return hipErrorInvalidValue;
   return launch_t<ET, ST, RT, CR, CS, 1>(L, wgs, threads, lds, s);

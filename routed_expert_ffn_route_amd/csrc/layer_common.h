@@ -401,13 +401,24 @@ struct SlotSet {
 struct SlotShare {
   int s0, s1, r0, r1;
 };
-__device__ __forceinline__ SlotShare slot_share(const SlotSet& ss, const Ctx& c) {
+// Reducer workgroups have the reduction to do after their stream, so they take a smaller
+// share of it: kReducerShare / kShareUnit of a plain workgroup's.  share_prefix(w) is the
+// stream position (in units) where workgroup w's share starts.
+constexpr int kShareUnit = 16, kReducerShare = 16;
+__host__ __device__ __forceinline__ long long share_prefix(int w, int P, int R) {
+  // reducers below w: the odd w' < w with (w' >> 1) < R (all w' < w when P < 2)
+  const int red = P < 2 ? (w < R ? w : R) : (w / 2 < R ? w / 2 : R);
+  return (long long)w * kShareUnit - (long long)red * (kShareUnit - kReducerShare);
+}
+__device__ __forceinline__ SlotShare slot_share(const SlotSet& ss, const Ctx& c, int R) {
   const long long nsh = (long long)ss.NS * ss.IS, nrt = (long long)ss.k * ss.I;
+  const long long tot = share_prefix(c.P, c.P, R);
+  const long long a = share_prefix(c.wg, c.P, R), b = share_prefix(c.wg + 1, c.P, R);
   SlotShare sh;
-  sh.s0 = (int)(nsh * c.wg / c.P);
-  sh.s1 = (int)(nsh * (c.wg + 1) / c.P);
-  sh.r0 = (int)(nrt * c.wg / c.P);
-  sh.r1 = (int)(nrt * (c.wg + 1) / c.P);
+  sh.s0 = (int)(nsh * a / tot);
+  sh.s1 = (int)(nsh * b / tot);
+  sh.r0 = (int)(nrt * a / tot);
+  sh.r1 = (int)(nrt * b / tot);
   return sh;
 }
 
@@ -533,6 +544,97 @@ __device__ inline void stream_routed(const SlotSet& ss, const SlotShare& sh, con
         cur = nxt;
         nxt = slot_state(slot + 1 < nsl ? slot + 1 : nsl);
       }
+    }
+  };
+  Stage<dt, C, CPT> A, B;
+  fill(A);
+  int b = 0;
+  for (; b + 1 < nb; b += 2) {
+    fill(B);
+    stage_compute<dt, C, CPT, true>(A, xv, yv, c);
+    fill(A);
+    stage_compute<dt, C, CPT, true>(B, xv, yv, c);
+  }
+  if (b < nb) stage_compute<dt, C, CPT, true>(A, xv, yv, c);
+}
+
+// The routed experts only (no shared slots; the MXFP4 layer), channels [i0, i1): flat
+// channel f = slot * I + j is row j of expert
+// s_ids[slot] (negative: an empty slot), weighted by s_w[slot].  The same two-stage stream
+// as stream_channels, but the team's items are walked incrementally: (slot, j) of its next
+// first item advances by a batch per fill, and the current and next slot's expert offsets
+// stay in scalar registers, so an item's three row addresses are a 32-bit multiply and
+// 64-bit adds (the host admits E * I < 2^31; a row offset within one expert, I * row bytes,
+// stays below 2^32).  Every wave of the compute unit issues this scalar code, and scalar
+// instructions issue at the rate of vector ones, so the per-item divisions and 64-bit
+// multiplications of the generic map made the stream scalar-bound.
+template <DT dt, int C, int CPT, typename X>
+__device__ inline void stream_routed_flat(const void* G, const void* V, const void* D,
+                                     const uint8_t* Gs, const uint8_t* Vs, const uint8_t* Ds,
+                                     int i0, int i1, int I, int k, const int* s_ids,
+                                     const float* s_w, const X& xv,
+                                     float (&yv)[CPT * kE<dt>], Ctx& c) {
+  using F = Fmt<dt>;
+  const int per = c.nteams * C;
+  const int nb = i1 > i0 ? (i1 - i0 + per - 1) / per : 0;
+  const uint32_t rb = (uint32_t)F::row_bytes(c.H);
+  const uint32_t sb = (uint32_t)(c.H / 32);
+  const uint8_t* const gb = reinterpret_cast<const uint8_t*>(G);
+  const uint8_t* const vb = reinterpret_cast<const uint8_t*>(V);
+  const uint8_t* const db = reinterpret_cast<const uint8_t*>(D);
+  struct SlotState {
+    uint64_t od, os;  // byte offsets of the expert's rows and scale rows
+    float wt;
+    bool ok;
+  };
+  auto slot_state = [&](int sl) {
+    SlotState st;
+    const int sc = sl < k ? sl : 0;
+    const int e = __builtin_amdgcn_readfirstlane(s_ids[sc]);
+    st.ok = sl < k && e >= 0;
+    const uint64_t r = (uint64_t)(st.ok ? e : 0) * (uint64_t)I;
+    st.od = r * rb;
+    st.os = r * sb;
+    st.wt = s_w[sc];
+    return st;
+  };
+  int f = i0 + c.team * C;  // the team's first item of the next batch
+  int slot = f / I, j = f - slot * I;
+  SlotState cur = slot_state(slot), nxt = slot_state(slot + 1);
+  const int ch0 = c.t;
+  auto fill = [&](Stage<dt, C, CPT>& st) {
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+      const bool wrap = j + q >= I;
+      const int jq = wrap ? j + q - I : j + q;
+      const SlotState& ss = wrap ? nxt : cur;
+      const bool live = f + q < i1 && ss.ok;
+      const uint64_t od = ss.od + (uint64_t)((uint32_t)jq * rb);
+      const uint64_t os = ss.os + (uint64_t)((uint32_t)jq * sb);
+      RowSrc<dt, false> gs, vs, ds;
+      gs.w = uniform_ptr(live ? gb + od : c.zrow);
+      vs.w = uniform_ptr(live ? vb + od : c.zrow);
+      ds.w = uniform_ptr(live ? db + od : c.zrow);
+      gs.s = uniform_ptr(live && Gs ? Gs + os : c.zrow);
+      vs.s = uniform_ptr(live && Vs ? Vs + os : c.zrow);
+      ds.s = uniform_ptr(live && Ds ? Ds + os : c.zrow);
+      st.wt[q] = live ? ss.wt : 0.0f;
+      st.gv[q] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        const int ch = ch0 + m * c.tsz;
+        st.g[q][m] = gs.load(ch, c);
+        st.v[q][m] = vs.load(ch, c);
+        st.d[q][m] = ds.load(ch, c);
+      }
+    }
+    f += per;
+    j += per;
+    while (j >= I) {
+      j -= I;
+      ++slot;
+      cur = nxt;
+      nxt = slot_state(slot + 1);
     }
   };
   Stage<dt, C, CPT> A, B;
@@ -758,6 +860,14 @@ __device__ inline void add_teams_to_lds(const float (&yv)[CPT * E], float* big, 
 // first reducer, once it has seen every workgroup's partial (so every workgroup has read the
 // epoch), advances the epoch for the next launch.  `big` is LDS of at least
 // max(H, nthreads) floats.
+// Which workgroups reduce: the odd ones, 1, 3, ..., 2R - 1 (R <= P / 2), so that the reducers
+// are spread over the XCDs of odd index (workgroup w runs on XCD w % 8) rather than stacked on
+// two of them.  Returns the reducer index, or -1.
+__host__ __device__ __forceinline__ int reducer_index(int wg, int P, int R) {
+  if (P < 2) return wg < R ? wg : -1;
+  return (wg & 1) && (wg >> 1) < R ? wg >> 1 : -1;
+}
+
 __device__ __forceinline__ float with_parity(float v, uint32_t par) {
   return __uint_as_float((__float_as_uint(v) & ~1u) | par);
 }
@@ -776,9 +886,8 @@ __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl,
     st_dev64(prow + h2, ((uint64_t)hi << 32) | lo);
   }
   MOE_STAMP(c.stamps, kStampPublished);
-  const int stride = c.P / R;
-  if (c.wg % stride != 0 || c.wg / stride >= R) return;
-  const int r = c.wg / stride;
+  const int r = reducer_index(c.wg, c.P, R);
+  if (r < 0) return;
   __syncthreads();  // src may alias big, which the reduction below reuses
   // Thread layout of a reducer: word q = tid % NW of the slice (two columns), partial rows
   // p = g, g + G, ... with g = tid / NW; each thread sums its rows in ascending p, then the
