@@ -123,6 +123,22 @@ moe_status moe_route(moe_layer layer, const float* x, const float* logits_in, in
 moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int32_t* ids,
                            const float* w, float* y, void* stream);
 
+/* moe_ffn_forward without a layer handle or a caller workspace, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid it).  It validates desc and weights as moe_layer_create does and runs the same
+ * kernels as moe_ffn_forward, with the layer's workspace (less the down-norm table, which
+ * only moe_channel_select reads) in a static scratch array of the library: 32 MiB per GPU,
+ * held from the first call on that GPU until the process ends.  A descriptor whose
+ * workspace exceeds it returns MOE_ERR_UNSUPPORTED (moe_layer_workspace_bytes gives an upper
+ * bound).  Calls no allocator.  Every call on a GPU shares that GPU's scratch: each call first
+ * clears what must start at zero (a fill kernel on `stream`), and calls that overlap on one
+ * GPU (concurrent streams or threads) race and give undefined results.  The device error
+ * word (bad ids, expired waits) is not reported: it lives in the scratch and the next call
+ * clears it. */
+moe_status moe_ffn_forward_noalloc(const moe_layer_desc* desc, const moe_weights* weights,
+                                   const float* x, int32_t B, const int32_t* ids,
+                                   const float* w, float* y, void* stream);
+
 /* Channel-sparse layer for one token (B = 1, SWIGLU; the fixed-count top-K keep rule of
  * the review's section "Background: channels and keep rules" with the output-unit score
  * of "The weights-only reader" stage 2).  Candidates are the k*I channels of the routed

@@ -22,7 +22,8 @@ DTYPES = {None: DTYPE_NONE, "f32": F32, "bf16": BF16, "mxfp4": MXFP4}
 # Every symbol include/moe_ffn.h declares.
 EXPORTS = (
     "moe_layer_workspace_bytes", "moe_layer_create", "moe_layer_destroy", "moe_route",
-    "moe_ffn_forward", "moe_channel_select", "moe_union_experts", "moe_layer_routing",
+    "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_channel_select", "moe_union_experts",
+    "moe_layer_routing",
     "moe_layer_check", "moe_layer_geometry", "moe_status_string", "moe_last_error",
 )
 # The phase-timeline build (libmoe_ffn_timeline.so) exports one more, for measurement only.
@@ -83,6 +84,9 @@ def lib():
         L.moe_route.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp]
         L.moe_ffn_forward.restype = i32
         L.moe_ffn_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.moe_ffn_forward_noalloc.restype = i32
+        L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(Weights),
+                                              vp, i32, vp, vp, vp, vp]
         L.moe_channel_select.restype = i32
         L.moe_channel_select.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp]
         L.moe_union_experts.restype = i32
@@ -256,6 +260,25 @@ class Layer:
         wg, th = ctypes.c_int32(), ctypes.c_int32()
         _check(lib().moe_layer_geometry(self.handle, ctypes.byref(wg), ctypes.byref(th)))
         return wg.value, th.value
+
+
+def forward_noalloc(desc: LayerDesc, tensors: dict, x, y, ids=None, w=None, B=None,
+                    stream=None):
+    """moe_ffn_forward_noalloc: the layer without a handle or workspace (the library's static
+    scratch); `tensors` as for Layer."""
+    import torch
+    B = x.shape[0] if B is None else B
+    out_dim = desc.inter if desc.kind == LINEAR else desc.hidden
+    _need(x, "x", torch.float32, min_numel=B * desc.hidden)
+    _need(y, "y", torch.float32, min_numel=B * out_dim)
+    if ids is not None:
+        _need(ids, "ids", torch.int32, min_numel=B * desc.top_k)
+    if w is not None:
+        _need(w, "w", torch.float32, min_numel=B * desc.top_k)
+    wts = Weights(*[None if tensors.get(n) is None else tensors[n].data_ptr()
+                    for n, _ in Weights._fields_])
+    _check(lib().moe_ffn_forward_noalloc(ctypes.byref(desc), ctypes.byref(wts), _ptr(x), B,
+                                         _ptr(ids), _ptr(w), _ptr(y), _stream(stream)))
 
 
 def union_experts(ids, E, n_touched, touched, offsets, slots, stream=None):

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -102,7 +103,7 @@ bool desc_valid(const moe_layer_desc* d, std::string* why) {
   return true;
 }
 
-Layout layout_of(const moe_layer_desc* d) {
+Layout layout_of(const moe_layer_desc* d, bool with_dnorm = true) {
   Layout L;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -118,7 +119,7 @@ Layout layout_of(const moe_layer_desc* d) {
   L.logits = take(B * E * 4);
   L.ids = take(B * k * 4);
   L.w = take(B * k * 4);
-  L.dnorm = take(d->kind == MOE_EXPERT_SWIGLU ? E * (size_t)d->inter * 4 : 0);
+  L.dnorm = take(d->kind == MOE_EXPERT_SWIGLU && with_dnorm ? E * (size_t)d->inter * 4 : 0);
   L.partials = take((size_t)kMaxWorkgroups * (size_t)d->hidden * 4);
   L.union_n = take(4);
   L.union_touched = take(E * 4);
@@ -229,45 +230,8 @@ static B1Args b1_args(moe_layer layer, const float* x, const int32_t* ids, const
   return a;
 }
 
-extern "C" {
-
-const char* moe_status_string(moe_status s) {
-  switch (s) {
-    case MOE_OK: return "ok";
-    case MOE_ERR_ARG: return "invalid argument";
-    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
-    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
-    case MOE_ERR_DEVICE: return "device error";
-  }
-  return "unknown status";
-}
-
-const char* moe_last_error(void) { return g_last_error.c_str(); }
-
-#ifdef MOE_TIMELINE
-// Timeline build only (not part of the product ABI): every later batch-1 launch records its
-// phase clock into `stamps` (device memory of at least 512 * kStamps uint64), or stops
-// recording when it is null.
-int moe_debug_set_stamps(void* stamps) {
-  g_stamps = reinterpret_cast<uint64_t*>(stamps);
-  return (int)kStamps;
-}
-#endif
-
-size_t moe_layer_workspace_bytes(const moe_layer_desc* desc) {
-  if (!desc_valid(desc, nullptr)) return 0;
-  return layout_of(desc).total;
-}
-
-moe_status moe_layer_create(const moe_layer_desc* desc, const moe_weights* weights,
-                            void* workspace, size_t workspace_bytes, void* stream,
-                            moe_layer* out) {
-  std::string why;
-  if (!out) return fail(MOE_ERR_ARG, "out is null");
-  if (!desc_valid(desc, &why)) return fail(MOE_ERR_ARG, "descriptor: %s", why.c_str());
-  if (!weights) return fail(MOE_ERR_ARG, "weights is null");
-  const moe_layer_desc& d = *desc;
-  const moe_weights& w = *weights;
+// Host-side checks of the weight pointers against a valid descriptor.
+static moe_status validate_weights(const moe_layer_desc& d, const moe_weights& w) {
   if ((d.router_dtype == MOE_DTYPE_NONE) != (w.router == nullptr))
     return fail(MOE_ERR_ARG, "router pointer must be given iff router_dtype is not NONE");
   if (w.router && !aligned16(w.router)) return fail(MOE_ERR_ARG, "router is not 16-byte aligned");
@@ -291,120 +255,54 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_weights* weigh
     if (!w.linear || !aligned16(w.linear))
       return fail(MOE_ERR_ARG, "linear must be given and 16-byte aligned");
   }
-  const Layout L = layout_of(&d);
-  if (!workspace || ((uintptr_t)workspace % kAlign) != 0)
-    return fail(MOE_ERR_WORKSPACE, "workspace must be non-null and 256-byte aligned");
-  if (workspace_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
-                L.total);
+  return MOE_OK;
+}
 
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
-  moe_layer l = new (std::nothrow) moe_layer_s;
-  if (!l) return fail(MOE_ERR_ARG, "out of host memory");
-  l->d = d;
-  l->w = w;
-  l->ws = reinterpret_cast<unsigned char*>(workspace);
-  l->L = L;
-  l->device = dev;
-  l->workgroups = cus < kMaxWorkgroups ? cus : kMaxWorkgroups;
-  l->threads = kThreads;
-  l->magic = kMagic;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // Everything from the control block (offset 0) through the tagged channel scores starts
-  // at zero: the epoch and arrival counters, the zero row, and every word that carries a
-  // launch tag (router logits, channel scores; tag 0 is never a launch's).  Memory reused
-  // from an earlier layer could otherwise hold words with the tag of this layer's first
-  // launch.
-  e = hipMemsetAsync(l->ctrl(), 0, L.cs_y, s);
-  if (e == hipSuccess && d.kind == MOE_EXPERT_SWIGLU)
-    e = launch_row_norms(w.down_t, w.down_scale, to_dt(d.expert_dtype),
-                         (size_t)d.n_experts * d.inter, d.hidden, l->at<float>(L.dnorm), s);
-  if (e != hipSuccess) {
-    l->magic = 0;
-    delete l;
-    return device_fail(e, "layer preparation");
+// ------------------------------------------------------------------------------------
+// Static scratch for moe_ffn_forward_noalloc: the workspace of one call at a time per GPU,
+// in the code object's own device memory (every GPU the library runs on holds its copy until
+// the process ends).  Host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device; the array's name in host code is a stand-in, not a device
+// address.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+static int g_scratch_cus[kMaxDevices];
+
+// The scratch's device address and the compute-unit count of device `dev`, looked up once per
+// device (with that device current).
+static moe_status scratch_for(int dev, void** ptr, int* cus) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_fail(e, "hipGetSymbolAddress(scratch)");
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
+    g_scratch_cus[dev] = n;
+    g_scratch_ptr[dev] = p;
   }
-  *out = l;
-  return ok();
+  *ptr = g_scratch_ptr[dev];
+  *cus = g_scratch_cus[dev];
+  return MOE_OK;
 }
 
-moe_status moe_layer_destroy(moe_layer layer) {
-  if (moe_status st = check_layer(layer)) return st;
-  layer->magic = 0;
-  delete layer;
-  return ok();
+// Zero `words` 32-bit words (a fill kernel, so that the clearing can be captured in a graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t words) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
 }
 
-moe_status moe_layer_geometry(moe_layer layer, int32_t* workgroups, int32_t* threads) {
-  if (moe_status st = check_layer(layer)) return st;
-  if (workgroups) *workgroups = layer->workgroups;
-  if (threads) *threads = layer->threads;
-  return ok();
-}
-
-moe_status moe_layer_check(moe_layer layer, void* stream, int32_t* device_error) {
-  if (moe_status st = check_layer(layer)) return st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint32_t err = 0;
-  hipError_t e = hipStreamSynchronize(s);
-  if (e == hipSuccess) e = hipMemcpy(&err, &layer->ctrl()->err, 4, hipMemcpyDeviceToHost);
-  if (e == hipSuccess && err) e = hipMemset(&layer->ctrl()->err, 0, 4);
-  if (e != hipSuccess) return device_fail(e, "moe_layer_check");
-  if (device_error) *device_error = (int32_t)err;
-  return ok();
-}
-
-moe_status moe_layer_routing(moe_layer layer, int32_t B, int32_t* ids, float* w,
-                             void* stream) {
-  if (moe_status st = check_layer(layer)) return st;
-  const moe_layer_desc& d = layer->d;
-  if (B < 1 || B > d.max_batch) return fail(MOE_ERR_ARG, "B=%d outside [1, max_batch]", B);
-  if (!ids || !w) return fail(MOE_ERR_ARG, "ids and w must be given");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const size_t n = (size_t)B * d.top_k * 4;
-  hipError_t e = hipMemcpyAsync(ids, layer->at<int32_t>(layer->L.ids), n,
-                                hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(w, layer->at<float>(layer->L.w), n, hipMemcpyDeviceToDevice, s);
-  if (e != hipSuccess) return device_fail(e, "moe_layer_routing copy");
-  return ok();
-}
-
-moe_status moe_route(moe_layer layer, const float* x, const float* logits_in, int32_t B,
-                     int32_t* ids, float* w, float* logits_out, void* stream) {
-  if (moe_status st = check_layer(layer)) return st;
-  const moe_layer_desc& d = layer->d;
-  if (B < 1 || B > d.max_batch) return fail(MOE_ERR_ARG, "B=%d outside [1, max_batch]", B);
-  if ((x == nullptr) == (logits_in == nullptr))
-    return fail(MOE_ERR_ARG, "exactly one of x and logits_in must be given");
-  if (x && d.router_dtype == MOE_DTYPE_NONE)
-    return fail(MOE_ERR_ARG, "routing from x needs a router");
-  if (!ids || !w) return fail(MOE_ERR_ARG, "ids and w must be given");
-  if ((x && !aligned16(x)) || (logits_in && !aligned16(logits_in)))
-    return fail(MOE_ERR_ARG, "x and logits_in must be 16-byte aligned");
-  RouteArgs a;
-  a.x = x;
-  a.logits_in = logits_in;
-  a.router = layer->w.router;
-  a.logits = logits_out ? logits_out : layer->at<float>(layer->L.logits);
-  a.ids = ids;
-  a.w = w;
-  a.H = d.hidden;
-  a.E = d.n_experts;
-  a.k = d.top_k;
-  a.B = B;
-  hipError_t e = launch_route(a, to_dt(d.router_dtype), reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return device_fail(e, "moe_route launch");
-  return ok();
-}
-
-moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int32_t* ids,
-                           const float* w, float* y, void* stream) {
-  if (moe_status st = check_layer(layer)) return st;
+// moe_ffn_forward on a checked handle (also serves moe_ffn_forward_noalloc, whose handle
+// lives on the stack and binds the library's static scratch).
+static moe_status forward_impl(moe_layer layer, const float* x, int32_t B, const int32_t* ids,
+                               const float* w, float* y, void* stream) {
   const moe_layer_desc& d = layer->d;
   if (!x || !y) return fail(MOE_ERR_ARG, "x and y must be given");
   if (!aligned16(x) || !aligned16(y)) return fail(MOE_ERR_ARG, "x and y must be 16-byte aligned");
@@ -554,6 +452,202 @@ moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int
     return ok();
   }
   return fail(MOE_ERR_UNSUPPORTED, "unknown expert kind");
+}
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+#ifdef MOE_TIMELINE
+// Timeline build only (not part of the product ABI): every later batch-1 launch records its
+// phase clock into `stamps` (device memory of at least 512 * kStamps uint64), or stops
+// recording when it is null.
+int moe_debug_set_stamps(void* stamps) {
+  g_stamps = reinterpret_cast<uint64_t*>(stamps);
+  return (int)kStamps;
+}
+#endif
+
+size_t moe_layer_workspace_bytes(const moe_layer_desc* desc) {
+  if (!desc_valid(desc, nullptr)) return 0;
+  return layout_of(desc).total;
+}
+
+moe_status moe_layer_create(const moe_layer_desc* desc, const moe_weights* weights,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            moe_layer* out) {
+  std::string why;
+  if (!out) return fail(MOE_ERR_ARG, "out is null");
+  if (!desc_valid(desc, &why)) return fail(MOE_ERR_ARG, "descriptor: %s", why.c_str());
+  if (!weights) return fail(MOE_ERR_ARG, "weights is null");
+  const moe_layer_desc& d = *desc;
+  const moe_weights& w = *weights;
+  if (moe_status st = validate_weights(d, w)) return st;
+  const Layout L = layout_of(&d);
+  if (!workspace || ((uintptr_t)workspace % kAlign) != 0)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be non-null and 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                L.total);
+
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
+  moe_layer l = new (std::nothrow) moe_layer_s;
+  if (!l) return fail(MOE_ERR_ARG, "out of host memory");
+  l->d = d;
+  l->w = w;
+  l->ws = reinterpret_cast<unsigned char*>(workspace);
+  l->L = L;
+  l->device = dev;
+  l->workgroups = cus < kMaxWorkgroups ? cus : kMaxWorkgroups;
+  l->threads = kThreads;
+  l->magic = kMagic;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // Everything from the control block (offset 0) through the tagged channel scores starts
+  // at zero: the epoch and arrival counters, the zero row, and every word that carries a
+  // launch tag (router logits, channel scores; tag 0 is never a launch's).  Memory reused
+  // from an earlier layer could otherwise hold words with the tag of this layer's first
+  // launch.
+  e = hipMemsetAsync(l->ctrl(), 0, L.cs_y, s);
+  if (e == hipSuccess && d.kind == MOE_EXPERT_SWIGLU)
+    e = launch_row_norms(w.down_t, w.down_scale, to_dt(d.expert_dtype),
+                         (size_t)d.n_experts * d.inter, d.hidden, l->at<float>(L.dnorm), s);
+  if (e != hipSuccess) {
+    l->magic = 0;
+    delete l;
+    return device_fail(e, "layer preparation");
+  }
+  *out = l;
+  return ok();
+}
+
+moe_status moe_layer_destroy(moe_layer layer) {
+  if (moe_status st = check_layer(layer)) return st;
+  layer->magic = 0;
+  delete layer;
+  return ok();
+}
+
+moe_status moe_layer_geometry(moe_layer layer, int32_t* workgroups, int32_t* threads) {
+  if (moe_status st = check_layer(layer)) return st;
+  if (workgroups) *workgroups = layer->workgroups;
+  if (threads) *threads = layer->threads;
+  return ok();
+}
+
+moe_status moe_layer_check(moe_layer layer, void* stream, int32_t* device_error) {
+  if (moe_status st = check_layer(layer)) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t err = 0;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(&err, &layer->ctrl()->err, 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && err) e = hipMemset(&layer->ctrl()->err, 0, 4);
+  if (e != hipSuccess) return device_fail(e, "moe_layer_check");
+  if (device_error) *device_error = (int32_t)err;
+  return ok();
+}
+
+moe_status moe_layer_routing(moe_layer layer, int32_t B, int32_t* ids, float* w,
+                             void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const moe_layer_desc& d = layer->d;
+  if (B < 1 || B > d.max_batch) return fail(MOE_ERR_ARG, "B=%d outside [1, max_batch]", B);
+  if (!ids || !w) return fail(MOE_ERR_ARG, "ids and w must be given");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t n = (size_t)B * d.top_k * 4;
+  hipError_t e = hipMemcpyAsync(ids, layer->at<int32_t>(layer->L.ids), n,
+                                hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(w, layer->at<float>(layer->L.w), n, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return device_fail(e, "moe_layer_routing copy");
+  return ok();
+}
+
+moe_status moe_route(moe_layer layer, const float* x, const float* logits_in, int32_t B,
+                     int32_t* ids, float* w, float* logits_out, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const moe_layer_desc& d = layer->d;
+  if (B < 1 || B > d.max_batch) return fail(MOE_ERR_ARG, "B=%d outside [1, max_batch]", B);
+  if ((x == nullptr) == (logits_in == nullptr))
+    return fail(MOE_ERR_ARG, "exactly one of x and logits_in must be given");
+  if (x && d.router_dtype == MOE_DTYPE_NONE)
+    return fail(MOE_ERR_ARG, "routing from x needs a router");
+  if (!ids || !w) return fail(MOE_ERR_ARG, "ids and w must be given");
+  if ((x && !aligned16(x)) || (logits_in && !aligned16(logits_in)))
+    return fail(MOE_ERR_ARG, "x and logits_in must be 16-byte aligned");
+  RouteArgs a;
+  a.x = x;
+  a.logits_in = logits_in;
+  a.router = layer->w.router;
+  a.logits = logits_out ? logits_out : layer->at<float>(layer->L.logits);
+  a.ids = ids;
+  a.w = w;
+  a.H = d.hidden;
+  a.E = d.n_experts;
+  a.k = d.top_k;
+  a.B = B;
+  hipError_t e = launch_route(a, to_dt(d.router_dtype), reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "moe_route launch");
+  return ok();
+}
+
+moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int32_t* ids,
+                           const float* w, float* y, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  return forward_impl(layer, x, B, ids, w, y, stream);
+}
+
+moe_status moe_ffn_forward_noalloc(const moe_layer_desc* desc, const moe_weights* weights,
+                                   const float* x, int32_t B, const int32_t* ids,
+                                   const float* w, float* y, void* stream) {
+  std::string why;
+  if (!desc_valid(desc, &why)) return fail(MOE_ERR_ARG, "descriptor: %s", why.c_str());
+  if (!weights) return fail(MOE_ERR_ARG, "weights is null");
+  if (moe_status st = validate_weights(*desc, *weights)) return st;
+  // the layer's workspace without the down-norm table (only channel selection reads it)
+  const Layout L = layout_of(desc, /*with_dnorm=*/false);
+  if (L.total > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "needs %zu bytes of scratch; the static scratch holds %zu",
+                L.total, kScratchBytes);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  void* ptr = nullptr;
+  if (moe_status st = scratch_for(dev, &ptr, &cus)) return st;
+  moe_layer_s l;
+  l.d = *desc;
+  l.w = *weights;
+  l.ws = reinterpret_cast<unsigned char*>(ptr);
+  l.L = L;
+  l.device = dev;
+  l.workgroups = cus < kMaxWorkgroups ? cus : kMaxWorkgroups;
+  l.threads = kThreads;
+  l.magic = kMagic;
+  // Everything that must start at zero, as at layer creation: the control block (epoch,
+  // error word), the tagged words, the zero row and the partial rows, through the channel
+  // scores.  The previous call on this GPU left its own contents there.
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t words = L.cs_y / 4;
+  const int grid = (int)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, s,
+                     reinterpret_cast<uint32_t*>(ptr), words);
+  e = hipGetLastError();
+  if (e != hipSuccess) return device_fail(e, "scratch clear");
+  return forward_impl(&l, x, B, ids, w, y, stream);
 }
 
 moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* ids,
