@@ -237,17 +237,21 @@ PHASES = {
     "b1": {0: "start", 1: "router rows published", 2: "shared experts streamed",
            3: "routing known (top-k + softmax)", 4: "routed stream done",
            5: "partial output summed in LDS", 6: "shared rows prefetched (wave 4)",
-           7: "reducer: every thread's partials seen", 8: "top-k: wave 0 keys sorted in runs", 9: "top-k: wave 0 top of its keys",
+           7: "reducer: every thread's partials seen", 8: "top-k: wave 0 keys sorted in runs",
+           9: "top-k: wave 0 top of its keys",
            10: "top-k: wave 0 keys polled", 11: "top-k: ranked", 12: "router rows computed",
            13: "partial output published", 14: "reducer: all partials arrived",
            15: "reducer: y written"},
-    "cs": {0: "start", 1: "router rows published", 2: "shared experts streamed",
-           3: "routing known (top-k + softmax)", 4: "gate pass done (g published)",
-           5: "all gate values gathered", 6: "threshold and kept list known",
+    "cs": {0: "start", 1: "router rows published", 3: "routing known (top-k + softmax)",
+           4: "gate values published", 2: "shared experts streamed",
+           5: "all gate values gathered and scored", 6: "threshold known",
            7: "kept rows streamed", 8: "top-k: wave 0 keys sorted in runs",
-           9: "top-k: wave 0 top of its keys", 10: "top-k: wave 0 keys polled", 11: "top-k: ranked",
-           12: "router rows computed", 13: "partial output published",
-           14: "reducer: all partials arrived", 15: "reducer: y written"},
+           9: "top-k: wave 0 top of its keys", 10: "top-k: wave 0 keys polled",
+           11: "top-k: ranked", 12: "router rows computed", 13: "partial output published",
+           14: "reducer: all partials arrived", 15: "reducer: y written",
+           16: "gather: gate words in (wave 0)", 17: "select: histogram done",
+           18: "select: bin found", 19: "select: bin members listed",
+           21: "kept counts scanned", 22: "slot tables ready", 23: "kept list ready"},
 }
 
 
@@ -276,7 +280,7 @@ def run_timeline(args, wl, keep=None):
     P = layers[0].geometry()[0]
     K = args.steps
     nl = K * wl.layers
-    per = 512 * 16
+    per = 512 * 32
     stamps = torch.zeros(nl * per, dtype=torch.int64, device="cuda")
 
     def launch(t, l, rec):
@@ -304,7 +308,7 @@ def run_timeline(args, wl, keep=None):
     torch.cuda.synchronize()
     for lay in layers:
         assert lay.check() == 0, "device error word set"
-    st = stamps.view(nl, 512, 16).cpu().numpy()[:, :P, :].astype(np.int64)
+    st = stamps.view(nl, 512, 32).cpu().numpy()[:, :P, :].astype(np.int64)
     kind = "b1" if keep is None else "cs"
     names = PHASES[kind]
     rows = []
@@ -331,12 +335,20 @@ def run_timeline(args, wl, keep=None):
                        for n in range(nl) if (st[n, x::8, i] > 0).any()]
                 vals.append(round(float(np.median(med)), 2) if med else None)
             per_xcd[names[i]] = vals
+    # shader clock: s_memtime ticks between the start and the publish of the partial output,
+    # over the 100 MHz clock between the same two points
+    ticks = (st[:, :, 31] - st[:, :, 30]).astype(np.float64)
+    real = (st[:, :, 13] - st[:, :, 0]).astype(np.float64) * 10.0  # ns
+    ok = (ticks > 0) & (real > 0)
+    clock_ghz = round(float(np.median(ticks[ok] / real[ok])), 3) if ok.any() else None
+    st = st[:, :, :30]
     # start of launch n+1 (earliest workgroup) after the last stamp of launch n
     last = st.max(axis=(1, 2))
     gaps = [(t0[n + 1] - last[n]) * 0.01 for n in range(nl - 1)]
     span = [(last[n] - t0[n]) * 0.01 for n in range(nl)]
     return {"timeline": kind, "workload": wl.name, "keep": keep, "launches": nl,
             "workgroups": P, "phases": rows, "per_xcd_median_us": per_xcd,
+            "shader_clock_ghz": clock_ghz,
             "first_start_to_last_stamp_us": round(float(np.median(span)), 2),
             "last_stamp_to_next_start_us": round(float(np.median(gaps)), 2) if gaps else None,
             "note": "100 MHz constant clock (10 ns); median over launches of the per-launch "

@@ -145,8 +145,9 @@ moe_status moe_ffn_forward_noalloc(const moe_layer_desc* desc, const moe_weights
  * experts (shared experts are always read in full and never candidates).  Every gate row
  * is read to score; only the kept channels' up rows and down rows are read.
  * ids/w: both NULL to route inside the call, or both given [k].  keep: 0..k*I.
- * kept [keep] receives the kept candidates as ascending flat ids slot*I + j (slot in
- * routing order); ties in the score go to the lower flat id.  y [H] (may be NULL). */
+ * kept [keep] receives the kept channels as ascending ids e*I + j (channel j of expert e;
+ * -1 for a channel of a skipped given id); ties in the score go to the lower e*I + j.  The
+ * kept rows are split evenly over the workgroups.  y [H] (may be NULL). */
 moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* ids,
                               const float* w, int32_t keep, int32_t mode, int32_t* kept,
                               float* y, void* stream);

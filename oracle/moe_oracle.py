@@ -226,16 +226,19 @@ def channel_select_token(x, ids, w, get_expert, dnorm_of, keep, shared=(),
     """Fixed-count top-K keep rule over the k*I candidates of one token.
 
     Kept channels are computed exactly from their full rows; dropped channels contribute
-    nothing and their up rows and down columns are never read [Reader, "Background"].
-    Candidate (slot i, channel j) has flat id i*I + j, slot i in routing order.  Ties in the
-    score go to the lower flat id.  Returns (kept flat ids ascending [K], y [H]).
+    nothing and their up rows and down columns are never read [Reader, "Background"].  A
+    channel is row j of expert e, identified by e*I + j [Reader, "Background": channel j owns
+    row j of G_e and V_e and column j of D_e].  Candidates are ranked by score, ties to the
+    lower e*I + j; the first `keep` are kept.  Returns (kept channel ids e*I + j ascending
+    [K], y [H]).
     """
     x = np.asarray(x, dtype=np.float64).reshape(-1)
     s, g = channel_scores(x, ids, w, get_expert, dnorm_of, mode)
     k, I = s.shape
-    kept = np.sort(topk_order(s.reshape(-1), keep))
+    cid = (np.asarray(ids, dtype=np.int64)[:, None] * I + np.arange(I)[None, :]).reshape(-1)
+    order = np.lexsort((cid, -s.reshape(-1)))[:keep]  # score descending, then channel id
     y = np.zeros_like(x)
-    for f in kept:
+    for f in order:
         i, j = divmod(int(f), I)
         _, V, Dt = get_expert(int(ids[i]))
         vj = to_f64(_row(V, j))
@@ -244,7 +247,7 @@ def channel_select_token(x, ids, w, get_expert, dnorm_of, keep, shared=(),
         y += w[i] * a * dj.reshape(-1)
     for (gs, us, ds) in shared:
         y += expert_output(x, gs, us, ds)
-    return kept, y
+    return np.sort(cid[order]), y
 
 
 def _row(t, j):

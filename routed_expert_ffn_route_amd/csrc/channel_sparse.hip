@@ -9,17 +9,20 @@
 // the exact gate value (every gate row is read to score) and ||d_j|| precomputed at load.
 //
 // Phases inside the launch (one workgroup per CU):
-//  1. router rows, then the exact top-k in every workgroup (as in the dense kernel);
-//     shared experts stream meanwhile;
-//  2. gate pass: each workgroup scores its contiguous share of the k*I candidates and
-//     stores g and s (device-coherent);
-//  3. grid barrier (every workgroup waits for all scores);
-//  4. every workgroup selects the same K kept channels from the k*I scores: a 4-pass
-//     radix select on the score bits finds the K-th largest score T, the candidates above
-//     T and the lowest-indexed ones equal to T are kept (ties to the lower flat id), and a
-//     block scan compacts them in ascending flat-id order;
-//  5. each workgroup streams its share of the kept channels: the up row and the down row
-//     only, with the stored gate value;
+//  1. router rows and the exact top-k in every workgroup, as in the dense kernel; the
+//     workgroup's shared-expert rows are warmed into L2 while the logits are awaited;
+//  2. gate pass: each workgroup computes g for its contiguous share of the k*I candidates
+//     and publishes each value with the launch tag (a 64-bit word, as the router logits);
+//  3. the workgroup's share of the shared experts, whose reads cover the gate hand-off;
+//  4. every workgroup gathers all k*I gate values (waiting on the tags), scores every
+//     candidate itself (||d_j|| from the load-time table) and finds the same K-th largest
+//     score T and how many candidates tied at T are kept: a 2048-bin histogram over the
+//     score range, a scan for the bin holding the K-th, and a rank count of that bin's few
+//     members (a radix search on the score bits when the bin is crowded);
+//  5. a scan over the candidates gives every kept channel its place in the output order
+//     (ascending e*I + j: experts in id order, channels in order; ties at T go to the lower
+//     e*I + j), and each workgroup takes an equal slice of the K kept channels in that
+//     order, writes their ids, and streams their up row and down row only, with g from LDS;
 //  6. the deterministic cross-workgroup sum of the partial outputs.
 #include "layer_common.h"
 
@@ -29,13 +32,17 @@ namespace {
 using namespace lc;
 
 constexpr int kMaxNP = 16;
-constexpr int kGateBatch = 8;  // gate rows per team per batch (one batch covers a share)
-constexpr int kPrefetch = 4;   // likeliest kept channels per share warmed in L2
+constexpr int kGateBatch = 8;  // gate rows per team per batch
+constexpr int kSelBins = 2048; // histogram bins of the selection
+constexpr int kSelCand = 512;  // bin members ranked by brute force (else the radix search)
+constexpr int kMaxSlots = 64;  // k
+constexpr int kSlotPad = kMaxSlots + 4;  // slot tables of kMaxSlots + 1 ints, padded so
+                                          // that the arrays after them are 16-byte aligned
 
 struct CSLaunch {
   B1Args a;
   const float* dnorm;  // [E*I]
-  uint64_t* s_ws;      // [k*I] launch-tagged scores
+  uint64_t* g_ws;      // [k*I] launch-tagged gate values
   int32_t* kept_out;   // [K]
   int K, mode, R, SW, tsz;
 };
@@ -66,12 +73,6 @@ __device__ inline int block_excl_scan(int v, int* sh, const Ctx& c, int* total) 
 // over the values that match the digits found so far, and the digit where the running
 // count from the top reaches the remaining need.  Requires 0 < K < n.  `hist` is LDS of
 // kSelBins ints, `sh` of 48 ints.
-constexpr int kSelBins = 2048;
-// LDS of the histogram: the binned selection keeps one padding int after every 32 bins
-// (bin b at b + b / 32), so that a wave reading 32 consecutive bins per lane spreads over
-// the banks
-constexpr int kSelHist = kSelBins + kSelBins / 32;
-__device__ __forceinline__ int sel_slot(int b) { return b + (b >> 5); }
 __device__ inline uint32_t select_threshold(const uint32_t* u, int n, int K, int* need_out,
                                             int* hist, int* sh, const Ctx& c) {
   uint32_t prefix = 0, mask = 0;
@@ -117,119 +118,125 @@ __device__ inline uint32_t select_threshold(const uint32_t* u, int n, int K, int
   return prefix;
 }
 
-// The same threshold in one histogram pass where it can be done (returns false otherwise,
-// and the caller runs select_threshold).  The radix digits above pile most scores into a
-// few bins (the leading bits are sign and exponent), and LDS atomics on one bin serialize.
-// Here the bins split [lo, hi] of the patterns evenly instead: bin(v) =
-// floor((v - lo) * 2048 / (hi - lo + 1)) in float, which is monotone in v, so the K-th
-// largest lies in the bin where the count from the top reaches K.  The values of that bin
-// (at most kSelCand) are then ranked by brute force: T is the one with fewer than `need`
-// values above it and at least `need` at or above it.  Returns false when all values are
-// equal or that bin holds more than kSelCand values.  lo and hi come in per wave in
-// sh[4 + w] and sh[20 + w], and `hist` (kSelHist ints) comes in cleared (both done while
-// the scores arrive); wave 0 alone finds the bin, so the whole selection takes four
-// barriers.
-constexpr int kSelCand = 256;
-__device__ inline bool select_threshold_binned(const uint32_t* u, int n, int K, uint32_t* T_out,
-                                               int* need_out, int* hist, int* sh,
-                                               const Ctx& c) {
-  const int lane = c.lane, wave = c.tid >> 6, nw = c.nthreads >> 6;
+
+// Wave-wide minimum / maximum of an unsigned value, in every lane (DPP within rows of 16,
+// then row and half swaps).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, true));
+  x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, true));
+  x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xf, 0xf, true));
+  x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, true));
+  x = min(x, swap_rows32<16>(x));
+  return min(x, swap_rows32<32>(x));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xf, 0xf, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, true));
+  x = max(x, swap_rows32<16>(x));
+  return max(x, swap_rows32<32>(x));
+}
+
+// The K-th largest of the n score patterns (0 < K < n; non-negative floats, whose bit
+// patterns order like the values; each thread holds eight of them in sb, all of them are in sv
+// for the radix fallback) and how many of the values equal to it are kept (*need;
+// the ties kept are decided later, in channel order).  One histogram pass bins the patterns
+// linearly over [lo, hi] (a monotone binning: bin order is score order); a scan over the bins
+// finds the bin holding the K-th largest and its rank there; that bin's members (few for a
+// spread of scores) are ranked by brute force.  A crowded bin (more than kSelCand members)
+// falls back to the radix search.  lo, hi come in per wave in sh[4 + w] and sh[20 + w];
+// hist (kSelBins ints) and sh[44] come in cleared; mem is LDS of kSelCand words.
+__device__ inline uint32_t select_kth(const uint32_t* sv, const uint32_t (&sb)[8], bool mine,
+                                      int n, int K, int* need_out, int* hist, uint32_t* mem,
+                                      int* sh, const Ctx& c) {
+  const int nw = c.nthreads >> 6;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
   for (int w = 0; w < nw; ++w) {
-    const uint32_t ol = (uint32_t)sh[4 + w], oh = (uint32_t)sh[20 + w];
-    lo = ol < lo ? ol : lo;
-    hi = oh > hi ? oh : hi;
+    lo = min(lo, (uint32_t)sh[4 + w]);
+    hi = max(hi, (uint32_t)sh[20 + w]);
   }
-  if (hi == lo) return false;  // uniform: every thread read the same words
-  const float inv = (float)kSelBins / ((float)(hi - lo) + 1.0f);
-  auto bin = [&](uint32_t v) {
-    const int b = (int)((float)(v - lo) * inv);
-    return b < kSelBins - 1 ? b : kSelBins - 1;
-  };
-  for (int f = c.tid; f < n; f += c.nthreads) atomicAdd(&hist[sel_slot(bin(u[f]))], 1);
-  __syncthreads();
-  if (wave == 0) {
-    // lane l counts bins kSelBins - 1 - PB l - i, i < PB, from the top
-    // (the counts stay in registers: all reads are issued at once, none waits on another)
-    // Those PB bins share (b >> 5) = kWave - 1 - lane, so their padded slots are the PB
-    // consecutive words from 33 * (kWave - 1 - lane): one base address and constant offsets.
-    constexpr int PB = kSelBins / kWave;
-    static_assert(PB == 32, "the padded histogram layout puts 32 bins per 33 words");
-    const lds_i32* hb = (const lds_i32*)hist + 33 * (kWave - 1 - lane);
-    int cnt[PB];
-    int local = 0;
+  if (hi > lo) {
+    const float inv = (float)kSelBins / ((float)(hi - lo) + 1.0f);
+    auto bin = [&](uint32_t v) {
+      const int b = (int)((float)(v - lo) * inv);
+      return b < kSelBins - 1 ? b : kSelBins - 1;
+    };
+    if (mine) {
 #pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      cnt[i] = hb[PB - 1 - i];
+      for (int i = 0; i < 8; ++i) atomicAdd(&hist[bin(sb[i])], 1);
+    }
+    __syncthreads();
+    MOE_STAMP(c.stamps, 17);
+    // thread t holds bins 2047 - 2t and 2046 - 2t (counts from the top); an inclusive scan of
+    // those pair counts over the workgroup finds the bin where the count from the top reaches K
+    const int bpt = kSelBins / c.nthreads;  // 2 for 1024 threads
+    int cnt[4] = {0, 0, 0, 0};
+    int local = 0;
+    for (int i = 0; i < bpt; ++i) {
+      cnt[i] = hist[kSelBins - 1 - bpt * c.tid - i];
       local += cnt[i];
     }
-    const int incl = wave_incl_scan(local);
-    int before = incl - local;
-    if (before < K && K <= incl) {
-#pragma unroll
-      for (int i = 0; i < PB; ++i) {
+    int total;
+    const int before0 = block_excl_scan(local, sh + 48, c, &total);
+    if (before0 < K && K <= before0 + local) {
+      int before = before0;
+      for (int i = 0; i < bpt; ++i) {
         if (before < K && K <= before + cnt[i]) {
-          sh[40] = kSelBins - 1 - PB * lane - i;
+          sh[40] = kSelBins - 1 - bpt * c.tid - i;
           sh[41] = K - before;  // the rank wanted within the bin
           sh[42] = cnt[i];
         }
         before += cnt[i];
       }
     }
-    if (lane == 0) sh[44] = 0;
-  }
-  __syncthreads();
-  const int bstar = sh[40], needb = sh[41], m = sh[42];
-  if (m > kSelCand) return false;
-  // the bin's values (hist is free now; its counts were read before the barrier), then
-  // their ranks
-  for (int f = c.tid; f < n; f += c.nthreads) {
-    const uint32_t v = u[f];
-    if (bin(v) == bstar) hist[atomicAdd(&sh[44], 1)] = (int)v;
-  }
-  __syncthreads();
-  if (c.tid < m) {
-    const uint32_t key = (uint32_t)hist[c.tid];
-    int gt = 0, ge = 0;
-    for (int j = 0; j < m; ++j) {
-      const uint32_t o = (uint32_t)hist[j];
-      gt += o > key ? 1 : 0;
-      ge += o >= key ? 1 : 0;
+    __syncthreads();
+    MOE_STAMP(c.stamps, 18);
+    const int bstar = sh[40], needb = sh[41], m = sh[42];
+    if (m <= kSelCand) {
+      if (mine) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (bin(sb[i]) == bstar) mem[atomicAdd(&sh[44], 1)] = sb[i];
+      }
+      __syncthreads();
+      MOE_STAMP(c.stamps, 19);
+      if (c.tid < m) {
+        const uint32_t key = mem[c.tid];
+        int gt = 0, ge = 0;
+        int j = 0;
+        for (; j + 8 <= m; j += 8) {  // eight reads in flight
+          uint32_t o[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) o[u] = mem[j + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            gt += o[u] > key ? 1 : 0;
+            ge += o[u] >= key ? 1 : 0;
+          }
+        }
+        for (; j < m; ++j) {
+          const uint32_t o = mem[j];
+          gt += o > key ? 1 : 0;
+          ge += o >= key ? 1 : 0;
+        }
+        if (gt < needb && needb <= ge) {  // the needb-th largest of the bin (equal keys agree)
+          sh[45] = (int)key;
+          sh[46] = needb - gt;
+        }
+      }
+      __syncthreads();
+      *need_out = sh[46];
+      return (uint32_t)sh[45];
     }
-    if (gt < needb && needb <= ge) {  // the needb-th largest of the bin (equal keys agree)
-      sh[45] = (int)key;
-      sh[46] = needb - gt;
-    }
   }
-  __syncthreads();
-  *T_out = (uint32_t)sh[45];
-  *need_out = sh[46];
-  return true;
+  // all scores equal, or a crowded bin: the exact radix search over the bit patterns
+  return select_threshold(sv, n, K, need_out, hist, sh, c);
 }
 
-// Counts, over u[0 .. m), of the values above T and of those equal to T (whole workgroup;
-// sh: LDS of 48 ints).
-__device__ inline void count_before(const uint32_t* u, int m, uint32_t T, int* gt, int* eq,
-                                    int* sh, const Ctx& c) {
-  int a = 0, b = 0;
-  for (int f = c.tid; f < m; f += c.nthreads) {
-    const uint32_t v = u[f];
-    a += v > T ? 1 : 0;
-    b += v == T ? 1 : 0;
-  }
-  if (m < 32768) {  // both counts in one scan: a in the upper, b in the lower 16 bits
-    int t;
-    block_excl_scan(a * 65536 + b, sh + 2, c, &t);
-    *gt = t >> 16;
-    *eq = t & 0xFFFF;
-    return;
-  }
-  int ta, tb;
-  block_excl_scan(a, sh + 2, c, &ta);
-  block_excl_scan(b, sh + 2, c, &tb);
-  *gt = ta;
-  *eq = tb;
-}
+// Candidates per thread in the selection: eight consecutive ones, which lie in one slot (I
+// is a multiple of 8), so their gate values, norms and scores stay in registers.
+constexpr int kCh = 8;
 
 template <DT ET, DT ST, DT RT, int C, int CPT>
 __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
@@ -250,229 +257,299 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   c.zrow = a.zrow;
   c.stamps = a.stamps;
   MOE_STAMP(c.stamps, kStampStart);
+  MOE_CLOCK(c.stamps, kStampClk0);
+  const int I = a.I, k = a.k;
+  const int n = k * I;                                 // <= kCh * nthreads (host checks)
+  const DivI divI(I);
+  const int kl = (L.K + c.P - 1) / c.P + 1;            // kept channels per workgroup, at most
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
   float* s_w = reinterpret_cast<float*>(s_ids + 64);                // [64]
-  int* hist = reinterpret_cast<int*>(s_w + 64);                     // [kSelHist]
-  int* sh = hist + kSelHist;                                        // [48]
-  float* big = reinterpret_cast<float*>(sh + 48);
+  int* sh = reinterpret_cast<int*>(s_w + 64);                       // [96]
+  int* slot_gt = sh + 96;                                           // [kMaxSlots + 1]
+  int* slot_eq = slot_gt + kSlotPad;                                // [kMaxSlots + 1]
+  int* hist = slot_eq + kSlotPad;                                   // [kSelBins]
+  uint32_t* mem = reinterpret_cast<uint32_t*>(hist + kSelBins);     // [kSelCand]
+  int* klist = reinterpret_cast<int*>(mem + kSelCand);              // [kl]
+  float* gl = reinterpret_cast<float*>(klist + ((kl + 3) & ~3));    // [n] gate values
+  uint32_t* sv = reinterpret_cast<uint32_t*>(gl + n);               // [n] score patterns
+  float* big = reinterpret_cast<float*>(sv + n);
   Ctrl* ctrl = a.ctrl;
-  const int I = a.I;
-  const int n = a.k * I;
+  // channel-selection launches on this workspace so far: its gate values carry the parity
+  const uint32_t cs_ep = load_relaxed_dev(&ctrl->cs_epoch);
+  const uint32_t gpar = (cs_ep + 1u) & 1u;
 
   float xv[CPT * 8], yv[CPT * 8];
   load_x<8, CPT>(a.x, c, xv);
 #pragma unroll
   for (int i = 0; i < CPT * 8; ++i) yv[i] = 0.0f;
-
-  // 1. routing, and the shared experts while it is in flight
   read_epoch(ctrl, c);
+
+  // 1. router rows, then the routing; the shared-expert rows are warmed meanwhile
   RouterRound<RT, CPT> rr;
   router_issue<RT, CPT>(a.route_inside, a.router, a.E, c, rr);
-  auto finish_router = [&] {
-    router_finish<RT, CPT>(rr, a.router, a.E, xv, a.rlog, reinterpret_cast<float*>(big),
-                           reinterpret_cast<uint32_t*>(s_int), c);
-  };
-  if (a.NS > 0) {
-    const long long nsc = (long long)a.NS * a.IS;
-    stream_channels<ST, C, CPT, true, true>(
-        a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, (int)(nsc * c.wg / c.P),
-        (int)(nsc * (c.wg + 1) / c.P),
-        [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c,
-        finish_router);
-  } else {
-    finish_router();
-  }
-  fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
+  router_finish<RT, CPT>(rr, a.router, a.E, xv, a.rlog, big, reinterpret_cast<uint32_t*>(s_int),
+                         c);
+  MOE_STAMP(c.stamps, 1);
+  const long long nsc = (long long)a.NS * a.IS;  // flat shared channel f of [NS][IS] is row f
+  const int s0 = (int)(nsc * c.wg / c.P), s1 = (int)(nsc * (c.wg + 1) / c.P);
+  uint32_t warm[kWarmLoads] = {0, 0};
+  if (a.route_inside && a.NS > 0)
+    warm_rows(reinterpret_cast<const uint8_t*>(a.sh_gate),
+              reinterpret_cast<const uint8_t*>(a.sh_up),
+              reinterpret_cast<const uint8_t*>(a.sh_down_t), s0, s1,
+              (uint32_t)Fmt<ST>::row_bytes(a.H),
+              min(c.nthreads, (a.E + kWave - 1) / kWave * kWave), c, warm);
+  fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, k, ctrl,
                 reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c);
+  MOE_STAMP(c.stamps, 3);
 
-  // 2. gate pass over this workgroup's share [g0, g1) of the candidates; g stays in LDS
+  // This thread's eight candidates [c0, c0 + 8) of slot sl0 (threads past n / 8 have none):
+  // their down-row norms, in flight through the gate pass
+  const int c0 = c.tid * kCh;
+  const bool mine = c0 < n;
+  const int sl0 = mine ? divI.div(c0) : 0, j0 = c0 - sl0 * I;
+  const int e0 = s_ids[sl0];
+  f32x4 dn4[2];
+  {
+    const float* dp = L.dnorm + (size_t)(e0 >= 0 ? e0 : 0) * I + (mine ? j0 : 0);
+    dn4[0] = reinterpret_cast<const f32x4*>(dp)[0];
+    dn4[1] = reinterpret_cast<const f32x4*>(dp)[1];
+  }
+  const float wsl = L.mode == 1 ? s_w[sl0] : 1.0f;
+
+  // 2. gate pass over this workgroup's share [g0, g1) of the candidates: the rows' loads go
+  // out first, the shared experts' right behind them; the gate dot products are computed and
+  // published (a 32-bit word each, the launch parity in its lowest bit) while the shared rows
+  // arrive; 3. then this workgroup's share of the shared experts (weight 1), whose reads cover
+  // the hand-off of the gate values
   const int g0 = (int)((long long)n * c.wg / c.P), g1 = (int)((long long)n * (c.wg + 1) / c.P);
-  uint32_t* sbits = reinterpret_cast<uint32_t*>(big);  // [n] all scores
-  float* s_g = reinterpret_cast<float*>(sbits + n);     // [g1 - g0] this share's gate values
-  int* loc = reinterpret_cast<int*>(s_g + (g1 - g0));   // [g1 - g0] this share's kept channels
-  float* s_loc = reinterpret_cast<float*>(loc + (g1 - g0));  // [g1 - g0] this share's scores
+  auto gate_rows = [&](int base, long long (&rows)[kGateBatch]) {
+#pragma unroll
+    for (int q = 0; q < kGateBatch; ++q) {
+      const int f = base + c.team * kGateBatch + q;
+      rows[q] = -1;
+      if (f < g1) {
+        const int sl = divI.div(f);
+        const int e = s_ids[sl];
+        if (e >= 0) rows[q] = (long long)e * I + (f - sl * I);
+      }
+    }
+  };
+  auto publish_gate = [&](int base, const float (&g)[kGateBatch]) {
+    if (c.t < kGateBatch) {
+      float gq = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kGateBatch; ++q) gq = (q == c.t) ? g[q] : gq;
+      const int f = base + c.team * kGateBatch + c.t;
+      if (f < g1)
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(L.g_ws) + f,
+                           (__float_as_uint(gq) & ~1u) | gpar, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  TeamRows<ET, kGateBatch, CPT> gr;
   {
-    for (int base = g0; base < g1; base += c.nteams * kGateBatch) {
+    long long rows[kGateBatch];
+    gate_rows(g0, rows);
+    team_dots_load<ET, kGateBatch, CPT>(a.gate, a.gate_s, rows, c, gr);
+  }
+  auto finish_gates = [&] {
+    float g[kGateBatch];
+    team_dots_compute<ET, kGateBatch, CPT>(gr, xv, c, g);
+    publish_gate(g0, g);
+    for (int base = g0 + c.nteams * kGateBatch; base < g1; base += c.nteams * kGateBatch) {
       long long rows[kGateBatch];
-#pragma unroll
-      for (int q = 0; q < kGateBatch; ++q) {
-        const int f = base + c.team * kGateBatch + q;
-        rows[q] = -1;
-        if (f < g1) {
-          const int e = s_ids[f / I];
-          if (e >= 0) rows[q] = (long long)e * I + (f % I);
-        }
-      }
-      // the down-row norm of this thread's candidate is loaded with the gate rows
-      long long myrow = -1;
-#pragma unroll
-      for (int q = 0; q < kGateBatch; ++q) myrow = (q == c.t) ? rows[q] : myrow;
-      const float dn = (c.t < kGateBatch && myrow >= 0) ? L.dnorm[myrow] : 0.0f;
-      float g[kGateBatch];
+      gate_rows(base, rows);
       team_dots<ET, kGateBatch, CPT>(a.gate, a.gate_s, rows, xv, c, g);
-      if (c.t < kGateBatch) {
-        float gq = 0.0f;
+      publish_gate(base, g);
+    }
+    MOE_STAMP(c.stamps, 4);
+  };
+  if (a.NS > 0)
+    stream_channels<ST, C, CPT, true, true>(
+        a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, s0, s1,
+        [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c,
+        finish_gates);
+  else
+    finish_gates();
+  MOE_STAMP(c.stamps, 2);
+
+  // 4. every gate value: this thread's eight as two 16-byte device-coherent loads, polled
+  // again while any of them lacks the launch parity; scores in registers, the gate values
+  // and score patterns to LDS, the range of the scores per wave; the histogram and the
+  // selection words cleared meanwhile
+  float gv[kCh];
+  uint32_t sb[kCh];
+  {
+    const rsrc_t gsrc = make_rsrc(L.g_ws, (uint32_t)n * 4u);
+    u32x4 w4[2];
 #pragma unroll
-        for (int q = 0; q < kGateBatch; ++q) gq = (q == c.t) ? g[q] : gq;
-        const int f = base + c.team * kGateBatch + c.t;
-        if (f < g1) {
-          const int slot = f / I;
-          const long long row = myrow;
-          float s = 0.0f;
-          if (row >= 0) {
-            s = fabsf(silu(gq)) * dn;
-            if (L.mode == 1) s *= s_w[slot];
-          }
-          s_g[f - g0] = gq;
-          s_loc[f - g0] = s;
-          st_dev64(L.s_ws + f, ((uint64_t)(c.epoch + 1u) << 32) | __float_as_uint(s));
+    for (int h = 0; h < 2; ++h)
+      w4[h] = __builtin_amdgcn_raw_buffer_load_b128(gsrc, (mine ? c0 : 0) * 4 + 16 * h, 0,
+                                                     kSc1);
+    auto ready = [&](const u32x4& v) {
+      return ((v.x & 1u) == gpar) & ((v.y & 1u) == gpar) & ((v.z & 1u) == gpar) &
+             ((v.w & 1u) == gpar);
+    };
+    if (mine && !(ready(w4[0]) && ready(w4[1]))) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (!(ready(w4[0]) && ready(w4[1]))) {
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          w4[h] = __builtin_amdgcn_raw_buffer_load_b128(gsrc, c0 * 4 + 16 * h, 0, kSc1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+          __hip_atomic_fetch_or(&ctrl->err, kErrPhaseWait, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+          break;
         }
       }
     }
-  }
-
-  // 2b. warm L2 with the up and down rows of this share's likeliest kept channels (the
-  // kPrefetch highest local scores, one wave each, a load per 128-byte line): the kept
-  // stream reads them right after the selection, and these loads overlap the gathering of
-  // the other workgroups' scores.  Which rows are warmed affects only timing.
-  uint32_t warm[4] = {0, 0, 0, 0};
-  __syncthreads();
-  {
-    const int share = g1 - g0;
-    const int wave = c.tid >> 6;
-    if (wave < kPrefetch && wave < share) {
-      const int i = c.lane;
-      const float me = i < share ? s_loc[i] : -1.0f;
-      int rank = 0;
-      for (int j = 0; j < min(share, kWave); ++j) {
-        const float o = s_loc[j];
-        rank += (o > me || (o == me && j < i)) ? 1 : 0;
-      }
-      const unsigned long long hit = __ballot(i < share && rank == wave);
-      if (hit) {
-        const int src = __ffsll(hit) - 1;
-        const int f = g0 + src;
-        const int e = s_ids[f / I];
-        if (e >= 0 && s_loc[src] > 0.0f) {
-          const size_t row = (size_t)e * I + (f % I);
-          const size_t rb = Fmt<ET>::row_bytes(a.H);
-          const uint8_t* p = reinterpret_cast<const uint8_t*>(c.lane < 32 ? a.up : a.down_t) +
-                             row * rb;
-          // up to 4 lines per lane (rows of at most 16 KB); each value stays in its own
-          // register until the end of the kernel, so nothing waits for these loads
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const size_t off = (size_t)(c.lane & 31) * 128 + (size_t)q * 32 * 128;
-            warm[q] = *reinterpret_cast<const uint32_t*>(p + (off < rb ? off : rb - 4));
-          }
-        }
-      }
-    }
-  }
-
-  // 3. every workgroup gathers all k*I scores (each published with its launch tag, so
-  // waiting on the scores themselves is the grid-wide hand-off)
-  // (meanwhile the range of the scores per wave and a cleared histogram for the selection)
-  {
-    // eight scores per thread in flight at once (the loads are unconditional, so none
-    // waits for another); only a score not yet tagged with this launch is polled again
+    const uint32_t wr[kCh] = {w4[0].x, w4[0].y, w4[0].z, w4[0].w,
+                              w4[1].x, w4[1].y, w4[1].z, w4[1].w};
+    const float dn[kCh] = {dn4[0].x, dn4[0].y, dn4[0].z, dn4[0].w,
+                           dn4[1].x, dn4[1].y, dn4[1].z, dn4[1].w};
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    const uint32_t tag = c.epoch + 1u;
-    constexpr int kG = 8;
-    for (int f0 = c.tid; f0 < n; f0 += kG * c.nthreads) {
-      uint64_t w[kG];
 #pragma unroll
-      for (int u = 0; u < kG; ++u) {
-        const int f = f0 + u * c.nthreads;
-        w[u] = ld_dev64(L.s_ws + (f < n ? f : n - 1));
-      }
+    for (int i = 0; i < kCh; ++i) {
+      gv[i] = __uint_as_float(wr[i] & ~1u);  // the value every workgroup sees
+      const float sc = mine && e0 >= 0 ? fabsf(silu(gv[i])) * dn[i] * wsl : 0.0f;
+      sb[i] = __float_as_uint(sc);
+      lo = mine ? min(lo, sb[i]) : lo;
+      hi = mine ? max(hi, sb[i]) : hi;
+    }
+    MOE_STAMP_AFTER(c.stamps, 16, lo);
+    if (mine) {
 #pragma unroll
-      for (int u = 0; u < kG; ++u) {
-        const int f = f0 + u * c.nthreads;
-        if (f < n) {
-          if ((uint32_t)(w[u] >> 32) != tag)
-            w[u] = wait_tagged(L.s_ws + f, tag, &ctrl->err, kErrPhaseWait);
-          const uint32_t v = (uint32_t)w[u];
-          sbits[f] = v;
-          lo = v < lo ? v : lo;
-          hi = v > hi ? v : hi;
-        }
+      for (int h = 0; h < 2; ++h) {
+        reinterpret_cast<f32x4*>(gl + c0)[h] = f32x4{gv[4 * h], gv[4 * h + 1], gv[4 * h + 2],
+                                                     gv[4 * h + 3]};
+        reinterpret_cast<u32x4*>(sv + c0)[h] = u32x4{sb[4 * h], sb[4 * h + 1], sb[4 * h + 2],
+                                                     sb[4 * h + 3]};
       }
     }
-    for (int i = c.tid; i < kSelHist; i += c.nthreads) hist[i] = 0;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      const uint32_t ol = (uint32_t)__shfl_xor((int)lo, m);
-      const uint32_t oh = (uint32_t)__shfl_xor((int)hi, m);
-      lo = ol < lo ? ol : lo;
-      hi = oh > hi ? oh : hi;
-    }
+    for (int i = c.tid; i < kSelBins; i += c.nthreads) hist[i] = 0;
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
     if (c.lane == 0) {
       sh[4 + (c.tid >> 6)] = (int)lo;
       sh[20 + (c.tid >> 6)] = (int)hi;
     }
+    if (c.tid == 0) sh[44] = 0;
   }
   __syncthreads();
+  MOE_STAMP(c.stamps, 5);
 
-  // 4. the same threshold in every workgroup; each keeps the channels of its own share:
-  // above T, or equal to T and among the first `need` ties in flat-id order
-  int nk = 0, kept_before = 0;
-  if (L.K >= n) {
-    for (int f = g0 + c.tid; f < g1; f += c.nthreads) loc[f - g0] = f;
-    nk = g1 - g0;
-    kept_before = g0;
-  } else if (L.K > 0) {
-    int need;
-    uint32_t T;
-    if (!select_threshold_binned(sbits, n, L.K, &T, &need, hist, sh, c))
-      T = select_threshold(sbits, n, L.K, &need, hist, sh, c);
-    int gt, eq;
-    count_before(sbits, g0, T, &gt, &eq, sh, c);
-    kept_before = gt + min(eq, need);
-    if ((c.tid >> 6) == 0) {  // wave 0: 64 candidates of the share at a time
-      const uint64_t below = (1ull << c.lane) - 1ull;
-      int r = eq, pos = 0;  // T-valued candidates before, kept so far
-      for (int base = g0; base < g1; base += kWave) {
-        const int f = base + c.lane;
-        const bool in = f < g1;
-        const uint32_t v = in ? sbits[f] : 0u;
-        const bool isT = in && v == T;
-        const uint64_t mT = __ballot(isT);
-        const bool take = in && (v > T || (isT && r + __popcll(mT & below) < need));
-        const uint64_t mk = __ballot(take);
-        if (take) loc[pos + __popcll(mk & below)] = f;
-        pos += __popcll(mk);
-        r += __popcll(mT);
-      }
-      if (c.lane == 0) sh[0] = pos;
+  // 5. the threshold: T = the K-th largest score (all kept when K >= n, none when K = 0)
+  uint32_t T = 0u;
+  int need = 0;
+  if (L.K > 0 && L.K < n) T = select_kth(sv, sb, mine, n, L.K, &need, hist, mem, sh, c);
+  const bool all = L.K >= n, none = L.K == 0;
+  MOE_STAMP(c.stamps, 6);
+  // counts of this thread's candidates above T and equal to T (kept outright / tied),
+  // prefix-summed over the workgroup in candidate order (one scan: above in the upper 16 bits)
+  int ngt = 0, neq = 0;
+  bool ab[kCh], ti[kCh];
+#pragma unroll
+  for (int i = 0; i < kCh; ++i) {
+    ab[i] = mine && !none && (all || sb[i] > T);
+    ti[i] = mine && !none && !all && sb[i] == T;
+    ngt += ab[i] ? 1 : 0;
+    neq += ti[i] ? 1 : 0;
+  }
+  int tot;
+  const int ex = block_excl_scan(ngt * 65536 + neq, sh + 48, c, &tot);
+  MOE_STAMP(c.stamps, 21);
+  const int gtp = ex >> 16, eqp = ex & 0xFFFF;  // counts before c0
+  // the prefixes at the slot boundaries (slot s = candidates [s * I, (s + 1) * I)): written by
+  // the thread whose eight candidates start the slot
+  if (mine && j0 == 0) {
+    slot_gt[sl0] = gtp;
+    slot_eq[sl0] = eqp;
+  }
+  if (c.tid == 0) {
+    slot_gt[k] = tot >> 16;
+    slot_eq[k] = tot & 0xFFFF;
+  }
+  __syncthreads();
+  // Output order: slots by expert id (a slot without an expert after every expert, in slot
+  // order), channels within a slot in order; the candidates tied at T that are kept are the
+  // first `need` in that order.  Wave 0, lane s < k: the slot's rank in that order (ranks are
+  // distinct), its counts moved to lane rank, exclusive scans over the ranks give the ties
+  // kept before it and its output base, moved back to lane s.
+  int* slot_tk = hist;                // [k] ties kept in the slot (hist is free now)
+  int* slot_base = hist + kMaxSlots;  // [k] first output position of the slot's kept channels
+  if (c.tid < kWave) {
+    const int sl = c.lane;
+    const int key = sl < k ? (s_ids[sl] >= 0 ? s_ids[sl] : a.E + sl) : 0x7FFFFFFF;
+    int rank = 0;
+    for (int o = 0; o < k; ++o) {
+      const int ko = __builtin_amdgcn_readlane(key, o);
+      rank += ko < key ? 1 : 0;
     }
-    __syncthreads();
-    nk = sh[0];
+    const int dst = sl < k ? rank : sl;  // lanes past k keep their place (zero counts)
+    const int eq_s = sl < k ? slot_eq[sl + 1] - slot_eq[sl] : 0;
+    const int gt_s = sl < k ? slot_gt[sl + 1] - slot_gt[sl] : 0;
+    const int req = __builtin_amdgcn_ds_permute(dst * 4, eq_s);
+    const int rgt = __builtin_amdgcn_ds_permute(dst * 4, gt_s);
+    const int eqb = wave_incl_scan(req) - req;
+    const int tk = min(max(need - eqb, 0), req);
+    const int kept = rgt + tk;
+    const int base = wave_incl_scan(kept) - kept;
+    const int tk_s = __shfl(tk, dst, kWave);
+    const int base_s = __shfl(base, dst, kWave);
+    if (sl < k) {
+      slot_tk[sl] = tk_s;
+      slot_base[sl] = base_s;
+    }
   }
   __syncthreads();
-  for (int i = c.tid; i < nk; i += c.nthreads) L.kept_out[kept_before + i] = loc[i];
+  MOE_STAMP(c.stamps, 22);
+  // each kept candidate's output position; this workgroup takes positions [ks0, ks1)
+  const int ks0 = (int)((long long)L.K * c.wg / c.P), ks1 = (int)((long long)L.K * (c.wg + 1) / c.P);
+  if (mine) {
+    const int gin0 = gtp - slot_gt[sl0], qin0 = eqp - slot_eq[sl0];
+    const int tk = slot_tk[sl0], sbase = slot_base[sl0];
+    int gin = gin0, qin = qin0;
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      if (ab[i] || (ti[i] && qin < tk)) {
+        const int pos = sbase + gin + min(qin, tk);
+        if (pos >= ks0 && pos < ks1) {
+          klist[pos - ks0] = c0 + i;
+          L.kept_out[pos] = e0 >= 0 ? e0 * I + j0 + i : -1;
+        }
+      }
+      gin += ab[i] ? 1 : 0;
+      qin += ti[i] ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  MOE_STAMP(c.stamps, 23);
 
-  // 5. the kept channels of this share: up row and down row only, gate value from LDS
+  // 6. this workgroup's slice of the kept channels: up row and down row only, g from LDS
   stream_channels<ET, C, CPT, false, false>(
-      nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, 0, nk,
-      [=](int i, long long& row, float& wt, float& gv) {
-        // i is wave-uniform, so are f and e: scalar, and so is the row arithmetic
-        const int f = __builtin_amdgcn_readfirstlane(loc[i]);
-        const int slot = f / I;
-        const int e = __builtin_amdgcn_readfirstlane(s_ids[slot]);
+      nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, 0, ks1 - ks0,
+      [=](int i, long long& row, float& wt, float& gvv) {
+        // i is wave-uniform, so are f, the slot and the expert: scalar row arithmetic
+        const int f = __builtin_amdgcn_readfirstlane(klist[i]);
+        const int sl = divI.div(f);
+        const int e = __builtin_amdgcn_readfirstlane(s_ids[sl]);
         if (e >= 0) {
-          row = (long long)e * I + (f % I);
-          wt = s_w[slot];
-          gv = s_g[f - g0];
+          row = (long long)e * I + (f - sl * I);
+          wt = s_w[sl];
+          gvv = gl[f];
         }
       },
       xv, yv, c);
+  MOE_STAMP_AFTER(c.stamps, 7, yv[0]);
   __syncthreads();  // `big` is reused by the reduction below
 
-  // 6. deterministic cross-workgroup sum
-  reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, c);
-  s_int[15] = warm[0] ^ warm[1] ^ warm[2] ^ warm[3];  // keeps the warming loads
+  // 7. deterministic cross-workgroup sum; its first reducer also advances the count of
+  // channel-selection launches
+  reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, c, &ctrl->cs_epoch, cs_ep + 1u);
+  s_int[15] = (int)(warm[0] ^ warm[1]);  // keeps the warming loads (see warm_rows)
 }
 
 template <DT ET, DT ST, DT RT, int C, int CPT>
@@ -499,33 +576,41 @@ hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStrea
 
 }  // namespace
 
-int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs) {
+// LDS of the channel-sparse kernel: team-reduction buffers, routing, selection words, slot
+// tables, histogram, bin members, this workgroup's kept list, the gate values and score
+// patterns of all k*I candidates, and the larger of the router / top-k / output scratch.
+int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K) {
   const int nteams = threads / team_size(H);
-  const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + kSelHist + 48) * 4;
   const int n = k * I;
-  const int share = (n + wgs - 1) / wgs;
-  const int sel = (n + 3 * share) * 4;  // all scores; this share's gate values, kept ids, scores
+  const int kl = (K + wgs - 1) / wgs + 1;
+  const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + 96) * 4 +
+                    2 * kSlotPad * 4 + kSelBins * 4 + kSelCand * 4 +
+                    ((kl + 3) & ~3) * 4 + 2 * n * 4;
   const int ybuf = nteams * H * 4;
   const int topk = topk_lds_bytes(E, k);
-  int big = sel > ybuf ? sel : ybuf;
-  big = big > topk ? big : topk;
+  const int router = ((E + wgs - 1) / wgs) * 4;
+  int big = ybuf > topk ? ybuf : topk;
   big = big > threads * 8 ? big : threads * 8;
-  return fixed + big;
+  big = big > router ? big : router;
+  return fixed + (big + 15) / 16 * 16;
 }
 
-hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* s_ws,
-                     int32_t* kept, int K, int mode, DT et, DT st, DT rt, int wgs, int threads,
-                     hipStream_t s) {
+hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_t* kept, int K,
+                     int mode, DT et, DT st, DT rt, int wgs, int threads, hipStream_t s) {
+  // the selection's bin scan holds at most four bins per thread
+  if (a.k > kMaxSlots || (long long)a.k * a.I > (long long)kCh * threads || a.I % kCh != 0 ||
+      threads * 4 < kSelBins || threads > 1024)
+    return hipErrorInvalidValue;
   CSLaunch L;
   L.a = a;
   L.dnorm = dnorm;
-  L.s_ws = s_ws;
+  L.g_ws = g_ws;
   L.kept_out = kept;
   L.K = K;
   L.mode = mode;
   L.tsz = team_size(a.H);
   lc::reducer_split(a.H, wgs, &L.R, &L.SW);
-  const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I, wgs);
+  const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I, wgs, K);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)
     return launch_cpt<DT::F32, DT::F32, DT::F32>(L, wgs, threads, lds, s);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::BF16)

@@ -29,6 +29,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 constexpr int kNT = 2;  // cache policy of the weight streams: non-temporal
+constexpr int kSc1 = 16;  // cache policy of device-coherent buffer loads (sc1)
 // global-memory (address space 1) views: loads through them are global_load_* (never flat)
 typedef __attribute__((address_space(1))) uint8_t gbl_u8;
 typedef __attribute__((address_space(1))) uint32_t gbl_u32;
@@ -50,7 +51,7 @@ __device__ __forceinline__ u32x4 lds_ld128(const lds_u8* p) {
 // constant clock when it passes phase i of a single-launch layer kernel, into
 // stamps[workgroup][kStamps].  Recording is one scalar clock read and one store; it adds no
 // barrier, so the phases keep their order and overlap.
-constexpr int kStamps = 16;
+constexpr int kStamps = 32;
 // stamp slots common to the single-launch kernels (each kernel numbers its other phases
 // from 1): start, partial output published, all partials arrived (reducers), y written
 enum : int {
@@ -59,7 +60,15 @@ enum : int {
   kStampRouterDots = 12,
   kStampPublished = 13, kStampArrived = 14, kStampReduced = 15
 };
+// Slots 30 and 31 hold the shader clock (s_memtime) at the start and at the publish of the
+// partial output, for the clock frequency the kernel ran at.
+enum : int { kStampClk0 = 30, kStampClk1 = 31 };
 #ifdef MOE_TIMELINE
+#define MOE_CLOCK(buf, i)                                                              \
+  do {                                                                                 \
+    if (threadIdx.x == 0 && (buf) != nullptr)                                          \
+      (buf)[blockIdx.x * ::moe::kStamps + (i)] = __builtin_amdgcn_s_memtime();         \
+  } while (0)
 #define MOE_STAMP(buf, i)                                                              \
   do {                                                                                 \
     if (threadIdx.x == 0 && (buf) != nullptr)                                          \
@@ -73,6 +82,9 @@ enum : int {
     MOE_STAMP(buf, i);                   \
   } while (0)
 #else
+#define MOE_CLOCK(buf, i) \
+  do {                    \
+  } while (0)
 #define MOE_STAMP(buf, i) \
   do {                    \
   } while (0)
@@ -356,6 +368,20 @@ __device__ __forceinline__ float wave_multi_sum(float (&v)[N], int lane) {
   }
   return sum_lanes_above<N>(v[0]);  // lane l: total of value index (l & (N-1))
 }
+
+// Quotient by a fixed positive divisor d of 0 <= n < 2^24: a float multiply by 1/d (off by at
+// most one) and one correction step, instead of the long integer division sequence.
+struct DivI {
+  int d;
+  float inv;
+  __device__ explicit DivI(int d_) : d(d_), inv(1.0f / (float)d_) {}
+  __device__ __forceinline__ int div(int n) const {
+    int q = (int)((float)n * inv);
+    if (q * d > n) --q;
+    else if ((q + 1) * d <= n) ++q;
+    return q;
+  }
+};
 
 // z * sigmoid(z) with the hardware exponential and reciprocal (about 1 ulp each)
 __device__ __forceinline__ float silu(float z) {
@@ -649,7 +675,9 @@ __device__ inline uint64_t wait_tagged(const uint64_t* p, uint32_t tag, uint32_t
 struct Ctrl {
   uint32_t epoch;               // launches completed on this workspace
   uint32_t err;                 // sticky error bits (read and cleared by moe_layer_check)
-  uint32_t pad0[62];
+  uint32_t cs_epoch;            // channel-selection launches completed (their gate values
+                                // carry (cs_epoch + 1) & 1 in the lowest bit)
+  uint32_t pad0[61];
 };
 static_assert(sizeof(Ctrl) == 256, "one 256-byte block");
 

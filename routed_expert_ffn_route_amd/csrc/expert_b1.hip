@@ -62,6 +62,7 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   c.zrow = a.zrow;
   c.stamps = a.stamps;
   MOE_STAMP(c.stamps, kStampStart);
+  MOE_CLOCK(c.stamps, kStampClk0);
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
   float* s_w = reinterpret_cast<float*>(s_ids + 64);                // [64]

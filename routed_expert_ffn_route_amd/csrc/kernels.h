@@ -40,10 +40,13 @@ int b1_lds_bytes(int H, int threads, int E, int k, bool two_layouts);
 int team_size(int H);
 
 // Channel-sparse batch-1 layer (fixed-count top-K keep rule over the k*I candidates).
-hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* s_ws, int32_t* kept,
+// kept [K] receives the kept channels as ascending ids e*I + j (-1 for a channel of a
+// skipped given id); g_ws [k*I] (32-bit words) holds the gate values with the launch parity.
+hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_t* kept,
                      int K, int mode, DT et, DT st, DT rt, int workgroups, int threads,
                      hipStream_t s);
-int cs_lds_bytes(int H, int threads, int E, int k, int I, int workgroups);
+int cs_lds_bytes(int H, int threads, int E, int k, int I, int workgroups, int K);
+constexpr int kCsMaxPerThread = 8;  // k*I <= 8 * threads
 
 // Routing: router GEMV for B tokens, then one workgroup per token for top-k + softmax.
 struct RouteArgs {

@@ -875,7 +875,8 @@ __device__ inline bool parity_ok(uint64_t v, uint32_t par) {
   return (((uint32_t)v & 1u) == par) && (((uint32_t)(v >> 32) & 1u) == par);
 }
 __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl, int R, int SW,
-                                          float* big, const Ctx& c, const float* src = nullptr) {
+                                          float* big, const Ctx& c, const float* src = nullptr,
+                                          uint32_t* ctr2 = nullptr, uint32_t ctr2_next = 0) {
   const int H = c.H;
   if (!src) src = big;
   const uint32_t par = (c.epoch + 1u) & 1u;
@@ -886,6 +887,7 @@ __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl,
     st_dev64(prow + h2, ((uint64_t)hi << 32) | lo);
   }
   MOE_STAMP(c.stamps, kStampPublished);
+  MOE_CLOCK(c.stamps, kStampClk1);
   const int r = reducer_index(c.wg, c.P, R);
   if (r < 0) return;
   __syncthreads();  // src may alias big, which the reduction below reuses
@@ -961,7 +963,10 @@ __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl,
   }
   __syncthreads();
   MOE_STAMP(c.stamps, kStampAllPolled);
-  if (r == 0 && c.tid == 0) store_relaxed_dev(&ctrl->epoch, c.epoch + 1u);
+  if (r == 0 && c.tid == 0) {
+    store_relaxed_dev(&ctrl->epoch, c.epoch + 1u);
+    if (ctr2) store_relaxed_dev(ctr2, ctr2_next);
+  }
   for (int col = c.tid; col < wslice; col += c.nthreads) {
     const int qq = col / 2, par2 = col % 2;
     const int wq = qq / NWw, lq = qq % NWw;    // wave within a group row, lane
@@ -984,9 +989,10 @@ __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl,
 // The whole output step for one register layout.
 template <int CPT, int E = 8>
 __device__ inline void reduce_output(const float (&yv)[CPT * E], float* partials, float* y,
-                                     Ctrl* ctrl, int R, int SW, float* big, const Ctx& c) {
+                                     Ctrl* ctrl, int R, int SW, float* big, const Ctx& c,
+                                     uint32_t* ctr2 = nullptr, uint32_t ctr2_next = 0) {
   teams_to_lds<E, CPT>(yv, big, c);
-  publish_and_reduce(partials, y, ctrl, R, SW, big, c);
+  publish_and_reduce(partials, y, ctrl, R, SW, big, c, nullptr, ctr2, ctr2_next);
 }
 
 // Read the epoch (launches completed on this workspace) at the start of a launch.  Only

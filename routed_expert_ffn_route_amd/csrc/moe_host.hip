@@ -472,7 +472,7 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 #ifdef MOE_TIMELINE
 // Timeline build only (not part of the product ABI): every later batch-1 launch records its
 // phase clock into `stamps` (device memory of at least 512 * kStamps uint64), or stops
-// recording when it is null.
+// recording when it is null.  Returns kStamps.
 int moe_debug_set_stamps(void* stamps) {
   g_stamps = reinterpret_cast<uint64_t*>(stamps);
   return (int)kStamps;
@@ -671,8 +671,11 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
   if (moe_status e = b1_types(layer, &et, &st, &rt)) return e;
   if (et == DT::MXFP4) return fail(MOE_ERR_UNSUPPORTED, "channel selection for MXFP4 experts");
   if (d.hidden > 4096) return fail(MOE_ERR_UNSUPPORTED, "channel selection needs hidden <= 4096");
-  if (cs_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k, d.inter, layer->workgroups) >
-      160 * 1024)
+  if (d.top_k > 64 || n > (long long)kCsMaxPerThread * layer->threads)
+    return fail(MOE_ERR_UNSUPPORTED, "channel selection needs k <= 64 and k*I <= %d",
+                kCsMaxPerThread * layer->threads);
+  if (cs_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k, d.inter, layer->workgroups,
+                   keep) > 160 * 1024)
     return fail(MOE_ERR_UNSUPPORTED, "k*I=%lld candidates exceed the selection LDS budget", n);
   B1Args a = b1_args(layer, x, ids, w, y ? y : layer->at<float>(layer->L.cs_y));
   hipError_t e = launch_cs(a, layer->at<float>(layer->L.dnorm),

@@ -92,7 +92,8 @@ def test_channel_select_degenerate_keeps():
     assert rel_err(y0, y_shared) <= TOL_BF16
     n = wl.k * wl.I
     kept, yn = _run(L, wl, x, n, 0)
-    assert kept.tolist() == list(range(n))
+    ids, _ = O.route(O.router_logits(x, hl.router), wl.k)
+    assert kept.tolist() == sorted(int(e) * wl.I + j for e in ids[0] for j in range(wl.I))
     assert rel_err(yn, y_dense) <= TOL_BF16
     # and the dense kernel agrees with keep-everything to fp32 rounding
     xd = torch.from_numpy(x).cuda().reshape(1, -1)
@@ -123,6 +124,7 @@ def test_channel_select_given_routing_and_repeatable():
 @pytest.mark.parametrize("frac_i", [0, 1])
 def test_channel_select_full_size(frac_i):
     """The 40-layer stack's shapes (H=2048, E=256, k=8, I=768, +1 shared) at 13% / 18%."""
+    import torch
     wl = WORKLOADS["qwen35_a3b_sparse"]
     keep = wl.keep_counts()[frac_i]
     assert keep == (799, 1106)[frac_i]
@@ -135,6 +137,12 @@ def test_channel_select_full_size(frac_i):
                                                  hl.shared)
         kept, y = _run(L, wl, x, keep, 0)
         assert kept.tolist() == kept_ref.tolist()
+        # the top-k the launch chose itself, in routing order
+        rid = torch.empty((1, wl.k), dtype=torch.int32, device="cuda")
+        rw = torch.empty((1, wl.k), dtype=torch.float32, device="cuda")
+        L.routing(rid, rw)
+        assert rid.cpu().numpy()[0].tolist() == ids[0].tolist()
+        assert np.max(np.abs(rw.cpu().numpy()[0] - w[0])) <= 1e-6
         err = rel_err(y, y_ref)
         print(f"keep {keep} token {tok} attempt {a}: max|dy|/||y||inf = {err:.3e}")
         assert err <= TOL_BF16

@@ -218,7 +218,7 @@ def test_keep_all_channels_equals_dense():
                                      lambda e: O.down_norms(experts[e][2]), k * I, shared=[sh])
     dense = sum(we * O.expert_output(x, *experts[e]) for e, we in zip(ids, w))
     dense = dense + O.expert_output(x, *sh)
-    assert kept.tolist() == list(range(k * I))
+    assert kept.tolist() == sorted(int(e) * I + j for e in ids for j in range(I))
     assert np.max(np.abs(y - dense)) < 1e-12
 
 
@@ -247,7 +247,7 @@ def test_channel_select_bruteforce(mode, keep):
                key=lambda sub: sum(score(*cands[c]) for c in sub))
     kept, y = O.channel_select_token(x, ids, w, lambda e: experts[e],
                                      lambda e: O.down_norms(experts[e][2]), keep, mode=mode)
-    assert kept.tolist() == sorted(best)
+    assert kept.tolist() == sorted(int(ids[cands[c][0]]) * I + cands[c][1] for c in best)
     ref = [0.0] * len(x)
     for c in best:
         i, j = cands[c]
@@ -272,15 +272,19 @@ def test_equal_down_norms_rank_by_gate():
     kept, _ = O.channel_select_token(x, ids, w, lambda e: experts[e],
                                      lambda e: O.down_norms(experts[e][2]), 5)
     act = np.concatenate([np.abs(O.silu(experts[e][0] @ x)) for e in ids])
-    assert kept.tolist() == sorted(np.argsort(-act, kind="stable")[:5].tolist())
+    cid = np.concatenate([e * I + np.arange(I) for e in ids])
+    assert kept.tolist() == sorted(cid[np.argsort(-act, kind="stable")[:5]].tolist())
 
 
-def test_channel_ties_go_to_lower_flat_id():
+def test_channel_ties_go_to_lower_channel_id():
+    """Equal scores are kept in channel-id order e*I + j, not in routing-slot order: with the
+    routing (1, 0) the four tied channels are, in slot order, ids 3, 4, 0, 1; the lowest
+    three ids are 0, 1, 3."""
     H, I = 2, 3
     x = np.array([1.0, 0.0])
     G = np.array([[1.0, 0.0], [1.0, 0.0], [0.5, 0.0]])
     ex = (G, np.ones((I, H)), np.ones((I, H)))
-    kept, _ = O.channel_select_token(x, np.array([0, 1]), np.array([0.5, 0.5]),
+    kept, _ = O.channel_select_token(x, np.array([1, 0]), np.array([0.5, 0.5]),
                                      lambda e: ex, lambda e: O.down_norms(ex[2]), 3)
     assert kept.tolist() == [0, 1, 3]
 
