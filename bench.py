@@ -82,41 +82,146 @@ def traffic_from_profiles(name: str, khash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def blas_threads() -> int:
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
-    except Exception:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """Host threads this process may run on (its CPU affinity set)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
         return os.cpu_count() or 1
 
 
 def cpu_baseline(wl, sample_layers: int, token: int = 0, keep=None):
-    """The oracle, as written, on the host cores: one token through `sample_layers` layers
-    (weight generation excluded from the timing).  Returns the record and the outputs."""
+    """The C++ oracle (oracle/cpp/moe_oracle.cpp: plain loops, double accumulation), as
+    written, on the host: one token through `sample_layers` layers, timed at 1 thread and at
+    every host thread of this process (independent outputs split over threads).  Host weight
+    generation is outside the timing.  Returns the record and the layer outputs."""
     from synth import tensors as T
-    from oracle import moe_oracle as O
-    total = 0.0
+    from oracle import cpp_oracle as C
+    nthr = host_threads()
+    totals = {1: 0.0, nthr: 0.0}
     outs = []
     for layer in range(sample_layers):
         Wr = T.router(wl, layer)
         x = T.x(wl, token, layer, 0)
-        ids, w = O.route(O.router_logits(x, Wr), wl.k)
+        ids, w = C.route(C.router_logits(x, Wr), wl.k)
         experts = {int(e): T.expert(wl, layer, int(e)) for e in ids[0]}
         shared = [T.shared(wl, layer, s) for s in range(wl.n_shared)]
-        t0 = time.perf_counter()
-        if keep is None:
-            y, _, _ = O.moe_layer_token(x, Wr, lambda e: experts[e], wl.k, shared)
-        else:
-            _, y = O.channel_select_token(x, ids[0], w[0], lambda e: experts[e],
-                                          lambda e: O.down_norms(experts[e][2]), keep, shared)
-        total += time.perf_counter() - t0
+        dn = {}
+        if keep is not None:
+            dn = {e: C.down_norms(experts[e][2]) for e in experts}
+        for th in totals:
+            C.set_threads(th)
+            t0 = time.perf_counter()
+            if keep is None:
+                y, _, _ = C.moe_layer_token(x, Wr, lambda e: experts[e], wl.k, shared)
+            else:
+                _, y = C.channel_select_token(x, ids[0], w[0], lambda e: experts[e],
+                                              dn.__getitem__, keep, shared)
+            totals[th] += time.perf_counter() - t0
+        C.set_threads(1)
         outs.append(y)
-    rec = {"value": (sample_layers / wl.layers) / total, "unit": "tokens/s",
-           "cores": blas_threads(), "kind": "oracle",
-           "sample": f"token {token} through layers 0..{sample_layers - 1} of {wl.layers} "
-                     f"(fp64 numpy oracle, weight generation excluded): {total:.2f} s of CPU "
-                     f"time, scaled to a full {wl.layers}-layer token"}
+    scale = sample_layers / wl.layers
+    rec = {"value": round(scale / totals[nthr], 4), "unit": "tokens/s", "cores": nthr,
+           "kind": "oracle", "value_1_thread": round(scale / totals[1], 4),
+           "cpu_model": cpu_model(),
+           "sample": f"token {token} through layers 0..{sample_layers - 1} of {wl.layers} (C++ "
+                     f"fp64 oracle, host weight generation excluded): {totals[1]:.2f} s wall "
+                     f"at 1 thread, {totals[nthr]:.2f} s at {nthr} threads, scaled to a full "
+                     f"{wl.layers}-layer token"}
     return rec, outs
+
+
+_PROBE = None
+
+
+def probe_lib():
+    global _PROBE
+    if _PROBE is None:
+        import ctypes
+        path = os.path.join(ROOT, "routed_expert_ffn_route_amd", "libmoe_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python routed_expert_ffn_route_amd/build.py`")
+        L = ctypes.CDLL(path)
+        L.probe_stream_read.restype = ctypes.c_int
+        L.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        L.probe_empty.restype = ctypes.c_int
+        L.probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        _PROBE = L
+    return _PROBE
+
+
+def stream_probe(gib: int = 4, reps: int = 5) -> float:
+    """Achieved HBM read bandwidth (GB/s): a read-only stream over `gib` GiB (16 times the
+    256 MB MALL, so nothing is served from it) with non-temporal 16-byte loads, 4096
+    workgroups of 256 threads, timed over `reps` launches with HIP events on the launching
+    stream."""
+    import torch
+    L = probe_lib()
+    nbytes = gib * 2**30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        assert L.probe_stream_read(buf.data_ptr(), nbytes, 4096, sink.data_ptr(), st) == 0
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        assert L.probe_stream_read(buf.data_ptr(), nbytes, 4096, sink.data_ptr(), st) == 0
+    end.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (start.elapsed_time(end) / 1e3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def launch_floor(workgroups: int, threads: int, nodes: int = 40, reps: int = 50) -> float:
+    """Microseconds per launch of an empty kernel with the layer kernel's geometry, `nodes`
+    launches captured in one HIP graph and replayed `reps` times: the per-layer floor that
+    dispatch alone sets."""
+    import torch
+    L = probe_lib()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(nodes):
+                assert L.probe_empty(workgroups, threads,
+                                     torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / (reps * nodes)
+
+
+def platform_figures(achieved_gbs: float, workgroups: int, threads: int) -> dict:
+    """The probe bandwidth, the achieved rate as a share of it, and the launch floor."""
+    probe = stream_probe()
+    return {"probe_gb_s": round(probe, 1), "pct_of_probe": round(100 * achieved_gbs / probe, 2),
+            "launch_floor_us": round(launch_floor(workgroups, threads), 3)}
 
 
 def timed(fn, steps, graph_ok=True):
@@ -222,6 +327,8 @@ def run_stack(args, wl, keep=None):
                      "us_per_launch": round(per_launch_s * 1e6, 3), "kernel_hash": khash},
         "cpu_baseline": None,
     }
+    wgs, thr = layers[0].geometry()
+    out.update(platform_figures(achieved, wgs, thr))
     if not args.no_cpu_baseline:
         cb, outs = cpu_baseline(wl, min(args.cpu_layers, wl.layers), token=0, keep=keep)
         worst = 0.0
@@ -412,7 +519,9 @@ def run_batched_stack(args, wl, B):
                      for t in range(K) for l in range(wl.layers)) / K
     mean_touched = sum(touched.values()) / len(touched)
     achieved = step_bytes / (gpu_ms / 1e3 / K) / 1e9
-    return {
+    wgs, thr = layers[0].geometry()
+    plat = platform_figures(achieved, wgs, thr)
+    return {**plat, 
         "metric": "MoE-stack batched decode tokens/s (aggregate over the batch)",
         "value": round(K * B / (gpu_ms / 1e3), 2),
         "unit": "tokens/s",
@@ -464,6 +573,9 @@ def run_linear_sweep(args, wl):
             sink.copy_(flush.view(-1, 16)[:, 0])  # one 4-byte read per 64-byte piece: 512 MB
                                                   # of lines read, 32 MB written
     lines = []
+    probe = stream_probe()
+    wgs, thr = L.geometry()
+    floor = launch_floor(wgs, thr)
     for B in batches:
         nsteps = max(2, min(args.steps, 64 if B <= 64 else 16))
         tokens = list(range(B))
@@ -506,6 +618,8 @@ def run_linear_sweep(args, wl):
             "touched_experts": touched, "hbm_gb_s": round(achieved, 1),
             "hbm_pct_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
             "tflop_s": round(flops / step_s / 1e12, 2), "steps": nsteps,
+            "probe_gb_s": round(probe, 1), "pct_of_probe": round(100 * achieved / probe, 2),
+            "launch_floor_us": round(floor, 3),
             "note": f"MALL flushed before each step (512 MB {args.flush}, timed separately and "
                     "subtracted)", "kernel_hash": kernel_hash("linear")})
     return lines

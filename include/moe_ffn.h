@@ -181,7 +181,9 @@ moe_status moe_layer_check(moe_layer layer, void* stream, int32_t* device_error)
 /* Launch geometry of the persistent kernels (workgroups, threads per workgroup). */
 moe_status moe_layer_geometry(moe_layer layer, int32_t* workgroups, int32_t* threads);
 
-const char* moe_status_string(moe_status status);
+/* Text of a status code: `status` is a moe_status value passed as its integer (any other
+ * value gives "unknown status"; taking an int keeps out-of-range codes well defined in C++). */
+const char* moe_status_string(int32_t status);
 const char* moe_last_error(void);
 
 #ifdef __cplusplus

@@ -10,7 +10,10 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_ffn.so")
+# MOE_FFN_LIBRARY names another build of the same library (the sanitizer build of the host
+# code, libmoe_ffn_san.so, is loaded this way by the host-validation tests)
+LIB_PATH = os.environ.get("MOE_FFN_LIBRARY") or os.path.join(_HERE, "libmoe_ffn.so")
+SAN_LIB_PATH = os.path.join(_HERE, "libmoe_ffn_san.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 DTYPE_NONE, F32, BF16, MXFP4 = -1, 0, 1, 2

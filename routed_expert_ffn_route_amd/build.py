@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
 LIB_TIMELINE = os.path.join(HERE, "libmoe_ffn_timeline.so")
+LIB_PROBE = os.path.join(HERE, "libmoe_probe.so")  # the benchmark's measurement kernels
 SOURCES = ["moe_host.hip", "expert_b1.hip", "channel_sparse.hip", "route.hip",
            "batched_swiglu.hip", "linear_mfma.hip", "linear_gemv.hip", "grouped_tn.hip"]
 
@@ -35,6 +36,19 @@ def _compile(src: str, build_dir: str, defines, verbose: bool) -> str:
     return obj
 
 
+def build_probe(verbose: bool = False) -> str:
+    """libmoe_probe.so: the read-only stream probe and the empty kernel of bench.py."""
+    cmd = ["hipcc", *HIPCC_FLAGS, "-shared", os.path.join(CSRC, "probe.hip"),
+           "-o", LIB_PROBE + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for probe.hip:\n" + r.stderr)
+    os.replace(LIB_PROBE + ".tmp", LIB_PROBE)
+    return LIB_PROBE
+
+
 def build(verbose: bool = False, timeline: bool = False) -> str:
     build_dir = os.path.join(HERE, "_build_timeline" if timeline else "_build")
     lib = LIB_TIMELINE if timeline else LIB
@@ -53,3 +67,4 @@ def build(verbose: bool = False, timeline: bool = False) -> str:
 if __name__ == "__main__":
     import sys
     print(build(verbose=True, timeline="--timeline" in sys.argv))
+    print(build_probe(verbose=True))

@@ -553,7 +553,8 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
 }
 
 template <DT ET, DT ST, DT RT, int C, int CPT>
-hipError_t launch_t(const CSLaunch& L, int wgs, int threads, int lds, hipStream_t s) {
+hipError_t launch_t(const CSLaunch& L, int wgs, int threads, int lds, hipStream_t s,
+                    int* occ) {
   auto fn = cs_kernel<ET, ST, RT, C, CPT>;
   static bool lds_set = false;
   if (!lds_set) {
@@ -562,15 +563,19 @@ hipError_t launch_t(const CSLaunch& L, int wgs, int threads, int lds, hipStream_
     if (e != hipSuccess) return e;
     lds_set = true;
   }
+  if (occ)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, reinterpret_cast<const void*>(fn),
+                                                        threads, lds);
   hipLaunchKernelGGL(fn, dim3(wgs), dim3(threads), lds, s, L);
   return hipGetLastError();
 }
 
 template <DT ET, DT ST, DT RT>
-hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStream_t s) {
+hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStream_t s,
+                      int* occ) {
   const int cpt = (L.a.H / 8 + L.tsz - 1) / L.tsz;
-  if (cpt <= 1 && ET != DT::F32) return launch_t<ET, ST, RT, 2, 1>(L, wgs, threads, lds, s);
-  if (cpt <= 1) return launch_t<ET, ST, RT, 1, 1>(L, wgs, threads, lds, s);
+  if (cpt <= 1 && ET != DT::F32) return launch_t<ET, ST, RT, 2, 1>(L, wgs, threads, lds, s, occ);
+  if (cpt <= 1) return launch_t<ET, ST, RT, 1, 1>(L, wgs, threads, lds, s, occ);
   return hipErrorInvalidValue;
 }
 
@@ -596,7 +601,8 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K) {
 }
 
 hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_t* kept, int K,
-                     int mode, DT et, DT st, DT rt, int wgs, int threads, hipStream_t s) {
+                     int mode, DT et, DT st, DT rt, int wgs, int threads, hipStream_t s,
+                     int* occ) {
   // the selection's bin scan holds at most four bins per thread
   if (a.k > kMaxSlots || (long long)a.k * a.I > (long long)kCh * threads || a.I % kCh != 0 ||
       threads * 4 < kSelBins || threads > 1024)
@@ -612,11 +618,11 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_
   lc::reducer_split(a.H, wgs, &L.R, &L.SW);
   const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I, wgs, K);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)
-    return launch_cpt<DT::F32, DT::F32, DT::F32>(L, wgs, threads, lds, s);
+    return launch_cpt<DT::F32, DT::F32, DT::F32>(L, wgs, threads, lds, s, occ);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::BF16)
-    return launch_cpt<DT::BF16, DT::BF16, DT::BF16>(L, wgs, threads, lds, s);
+    return launch_cpt<DT::BF16, DT::BF16, DT::BF16>(L, wgs, threads, lds, s, occ);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::F32)
-    return launch_cpt<DT::BF16, DT::BF16, DT::F32>(L, wgs, threads, lds, s);
+    return launch_cpt<DT::BF16, DT::BF16, DT::F32>(L, wgs, threads, lds, s, occ);
   return hipErrorInvalidValue;
 }
 

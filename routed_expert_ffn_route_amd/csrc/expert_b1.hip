@@ -178,7 +178,8 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
 }
 
 template <DT ET, DT ST, DT RT, int CR, int CS, int CPT>
-hipError_t launch_t(const B1Launch& L, int wgs, int threads, int lds, hipStream_t s) {
+hipError_t launch_t(const B1Launch& L, int wgs, int threads, int lds, hipStream_t s,
+                    int* occ) {
   auto fn = b1_kernel<ET, ST, RT, CR, CS, CPT>;
   // Raise the dynamic-LDS limit once per instantiation (kept out of the per-launch path
   // so that graph capture records only the launch).
@@ -189,6 +190,9 @@ hipError_t launch_t(const B1Launch& L, int wgs, int threads, int lds, hipStream_
     if (e != hipSuccess) return e;
     lds_set = true;
   }
+  if (occ)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, reinterpret_cast<const void*>(fn),
+                                                        threads, lds);
   hipLaunchKernelGGL(fn, dim3(wgs), dim3(threads), lds, s, L);
   return hipGetLastError();
 }
@@ -201,14 +205,15 @@ template <DT dt> constexpr int channels_per_batch() {
 }
 
 template <DT ET, DT ST, DT RT>
-hipError_t launch_cpt(const B1Launch& L, int wgs, int threads, int lds, hipStream_t s) {
+hipError_t launch_cpt(const B1Launch& L, int wgs, int threads, int lds, hipStream_t s,
+                      int* occ) {
   // the shared experts stream on their own before the routing when the formats differ (two
   // channels per team there, as the routed MXFP4 rows); otherwise they are slots of the
   // routed stream and CS is unused
   constexpr int CR = channels_per_batch<ET>(), CS = ET == DT::MXFP4W ? 2 : CR;
   // team_size gives one chunk per thread for every H the host admits (H <= 8192)
   if (L.a.H / 8 > L.tsz) return hipErrorInvalidValue;
-  return launch_t<ET, ST, RT, CR, CS, 1>(L, wgs, threads, lds, s);
+  return launch_t<ET, ST, RT, CR, CS, 1>(L, wgs, threads, lds, s, occ);
 }
 
 }  // namespace
@@ -244,7 +249,7 @@ int b1_lds_bytes(int H, int threads, int E, int k, bool two_layouts) {
 }
 
 hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int wgs, int threads,
-                     hipStream_t s) {
+                     hipStream_t s, int* occ) {
   B1Launch L;
   L.a = a;
   L.tsz = team_size(a.H);
@@ -253,15 +258,15 @@ hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int wgs, int threads,
   const int lds = b1_lds_bytes(a.H, threads, a.E, a.k, et == DT::MXFP4);
   L.big_floats = b1_big_floats(a.H, threads, a.E, a.k);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)
-    return launch_cpt<DT::F32, DT::F32, DT::F32>(L, wgs, threads, lds, s);
+    return launch_cpt<DT::F32, DT::F32, DT::F32>(L, wgs, threads, lds, s, occ);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::BF16)
-    return launch_cpt<DT::BF16, DT::BF16, DT::BF16>(L, wgs, threads, lds, s);
+    return launch_cpt<DT::BF16, DT::BF16, DT::BF16>(L, wgs, threads, lds, s, occ);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::F32)
-    return launch_cpt<DT::BF16, DT::BF16, DT::F32>(L, wgs, threads, lds, s);
+    return launch_cpt<DT::BF16, DT::BF16, DT::F32>(L, wgs, threads, lds, s, occ);
   if (et == DT::MXFP4 && st == DT::BF16 && rt == DT::BF16) {
     // routed MXFP4 rows in 16-element chunks: 8 bytes of codes per thread and row
     L.tsz_r = team_threads(a.H / kE<DT::MXFP4W>);
-    return launch_cpt<DT::MXFP4W, DT::BF16, DT::BF16>(L, wgs, threads, lds, s);
+    return launch_cpt<DT::MXFP4W, DT::BF16, DT::BF16>(L, wgs, threads, lds, s, occ);
   }
   return hipErrorInvalidValue;
 }

@@ -34,8 +34,10 @@ struct B1Args {
   uint64_t* stamps;                     // [P][kStamps] phase clock (timeline build) or null
 };
 
+// occupancy != null: launch nothing; *occupancy = workgroups of this kernel and LDS size that
+// fit on one CU at once (the persistent kernels need at least 1)
 hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int workgroups, int threads,
-                     hipStream_t s);
+                     hipStream_t s, int* occupancy = nullptr);
 int b1_lds_bytes(int H, int threads, int E, int k, bool two_layouts);
 int team_size(int H);
 
@@ -44,7 +46,7 @@ int team_size(int H);
 // skipped given id); g_ws [k*I] (32-bit words) holds the gate values with the launch parity.
 hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_t* kept,
                      int K, int mode, DT et, DT st, DT rt, int workgroups, int threads,
-                     hipStream_t s);
+                     hipStream_t s, int* occupancy = nullptr);
 int cs_lds_bytes(int H, int threads, int E, int k, int I, int workgroups, int K);
 constexpr int kCsMaxPerThread = 8;  // k*I <= 8 * threads
 

@@ -299,6 +299,39 @@ __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t wor
     p[i] = 0u;
 }
 
+// The batch-1 kernels are persistent: their workgroups wait on one another's results (router
+// logits, gate values, partial outputs), so all of them -- one per CU -- must be resident at
+// once.  The occupancy the runtime computes from the kernel's registers and this layer's LDS
+// must allow one workgroup of `threads` per CU; a kernel that needs more would hang on its own
+// bounded waits instead.  Shapes or types the kernels do not take are left to the calls, which
+// reject them.
+static moe_status check_residency(moe_layer l) {
+  const moe_layer_desc& d = l->d;
+  if (d.kind != MOE_EXPERT_SWIGLU) return ok();
+  DT et = to_dt(d.expert_dtype), st, rt;
+  st = d.n_shared > 0 ? to_dt(d.shared_dtype) : (et == DT::MXFP4 ? DT::BF16 : et);
+  rt = d.router_dtype == MOE_DTYPE_NONE ? st : to_dt(d.router_dtype);
+  B1Args a = b1_args(l, nullptr, nullptr, nullptr, nullptr);
+  if (d.hidden <= 8192 && b1_lds_bytes(d.hidden, l->threads, d.n_experts, d.top_k,
+                                       et == DT::MXFP4) <= 160 * 1024) {
+    int occ = 0;
+    const hipError_t e = launch_b1(a, et, st, rt, l->workgroups, l->threads, nullptr, &occ);
+    if (e == hipSuccess && occ < 1)
+      return fail(MOE_ERR_UNSUPPORTED, "the batch-1 kernel cannot keep a workgroup of %d "
+                  "threads resident on every CU (occupancy %d)", l->threads, occ);
+  }
+  if (et != DT::MXFP4 && d.hidden <= 4096 && d.top_k <= 64 &&
+      (long long)d.top_k * d.inter <= (long long)kCsMaxPerThread * l->threads) {
+    int occ = 0;
+    const hipError_t e = launch_cs(a, nullptr, nullptr, nullptr, 0, 0, et, st, rt,
+                                   l->workgroups, l->threads, nullptr, &occ);
+    if (e == hipSuccess && occ < 1)
+      return fail(MOE_ERR_UNSUPPORTED, "the channel-sparse kernel cannot keep a workgroup of "
+                  "%d threads resident on every CU (occupancy %d)", l->threads, occ);
+  }
+  return ok();
+}
+
 // moe_ffn_forward on a checked handle (also serves moe_ffn_forward_noalloc, whose handle
 // lives on the stack and binds the library's static scratch).
 static moe_status forward_impl(moe_layer layer, const float* x, int32_t B, const int32_t* ids,
@@ -456,7 +489,7 @@ static moe_status forward_impl(moe_layer layer, const float* x, int32_t B, const
 
 extern "C" {
 
-const char* moe_status_string(moe_status s) {
+const char* moe_status_string(int32_t s) {
   switch (s) {
     case MOE_OK: return "ok";
     case MOE_ERR_ARG: return "invalid argument";
@@ -516,6 +549,11 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_weights* weigh
   l->workgroups = cus < kMaxWorkgroups ? cus : kMaxWorkgroups;
   l->threads = kThreads;
   l->magic = kMagic;
+  if (moe_status st = check_residency(l)) {
+    l->magic = 0;
+    delete l;
+    return st;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // Everything from the control block (offset 0) through the tagged channel scores starts
   // at zero: the epoch and arrival counters, the zero row, and every word that carries a
@@ -637,6 +675,7 @@ moe_status moe_ffn_forward_noalloc(const moe_layer_desc* desc, const moe_weights
   l.workgroups = cus < kMaxWorkgroups ? cus : kMaxWorkgroups;
   l.threads = kThreads;
   l.magic = kMagic;
+  if (moe_status st = check_residency(&l)) return st;
   // Everything that must start at zero, as at layer creation: the control block (epoch,
   // error word), the tagged words, the zero row and the partial rows, through the channel
   // scores.  The previous call on this GPU left its own contents there.

@@ -116,3 +116,32 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(M, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         M.lib()
+
+
+def test_host_validation_under_asan_ubsan():
+    """The tests above, run again in a child process against libmoe_ffn_san.so: the host
+    code built with AddressSanitizer and UndefinedBehaviorSanitizer (any report aborts the
+    child with a nonzero status).  The child also confirms that it mapped that library and
+    the ASan runtime."""
+    import subprocess
+    import sys
+    from routed_expert_ffn_route_amd import build_sanitize as BS
+    if not BS.ASAN_RUNTIME:
+        pytest.skip("no clang ASan runtime in this image")
+    if not os.path.exists(BS.SAN_LIB):
+        BS.build_sanitized()
+    env = dict(os.environ, MOE_FFN_LIBRARY=BS.SAN_LIB, LD_PRELOAD=BS.ASAN_RUNTIME,
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_abi_host.py", "-q",
+                        "-p", "no:cacheprovider", "-k", "not asan_ubsan"],
+                       cwd=root, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    assert "7 passed" in r.stdout, r.stdout[-2000:]
+    probe = ("import routed_expert_ffn_route_amd as M; M.lib(); "
+             "m = open('/proc/self/maps').read(); "
+             "assert 'libmoe_ffn_san.so' in m and 'libclang_rt.asan' in m; print('mapped')")
+    r = subprocess.run([sys.executable, "-c", probe], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0 and "mapped" in r.stdout, r.stderr[-2000:]

@@ -13,7 +13,12 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
+from oracle import cpp_oracle as CPP
 from oracle import moe_oracle as O
+
+# The pins below that take an `O` argument run against both oracles: the numpy one and the
+# plain C++17 one (oracle/cpp/moe_oracle.cpp through oracle/cpp_oracle.py).
+both = pytest.mark.parametrize("O", [O, CPP], ids=["numpy", "cpp"])
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -43,13 +48,15 @@ def rand_expert(rng, I, H, scale=0.5):
 
 
 # ---------------------------------------------------------------- storage decoding
-def test_bf16_widening_known_patterns():
+@both
+def test_bf16_widening_known_patterns(O):
     pats = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x4049, 0x3C23], dtype=np.uint16)
     want = [1.0, -2.0, 1.0078125, 0.0, -0.0, 3.140625, 0.009948730468750]
     assert O.bf16_to_f64(pats).tolist() == want
 
 
-def test_mxfp4_e2m1_table_and_scale():
+@both
+def test_mxfp4_e2m1_table_and_scale(O):
     # OCP MX v1.0 FP4 E2M1: codes 0..7 = 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 is the sign.
     codes = np.array([[0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE] * 2], dtype=np.uint8)
     vals = O.mxfp4_to_f64(codes, np.array([[127]], dtype=np.uint8))[0]
@@ -61,7 +68,8 @@ def test_mxfp4_e2m1_table_and_scale():
     assert tiny[2] == 2.0 ** -127
 
 
-def test_mxfp4_generator_roundtrip_bound():
+@both
+def test_mxfp4_generator_roundtrip_bound(O):
     import synth
     codes, scales = synth.mxfp4(0, 123, 0, 4, 256, 0.02)
     w = synth.normal_f32(0, 123, 0, 4 * 256, 0.02).reshape(4, 256).astype(np.float64)
@@ -80,14 +88,16 @@ def test_mxfp4_generator_roundtrip_bound():
 
 
 # ---------------------------------------------------------------- routing
-def test_router_identity_rows_give_x():
+@both
+def test_router_identity_rows_give_x(O):
     rng = np.random.default_rng(1)
     x = rng.normal(size=8)
     assert np.array_equal(O.router_logits(x, np.eye(8))[0], x)
 
 
+@both
 @pytest.mark.parametrize("E,k", [(5, 1), (6, 2), (8, 3), (10, 4), (7, 7)])
-def test_topk_bruteforce_subsets(E, k):
+def test_topk_bruteforce_subsets(E, k, O):
     rng = np.random.default_rng(E * 10 + k)
     for _ in range(20):
         l = rng.normal(size=E)
@@ -97,14 +107,16 @@ def test_topk_bruteforce_subsets(E, k):
         assert all(l[ids[0][i]] > l[ids[0][i + 1]] for i in range(k - 1))
 
 
-def test_topk_exact_ties_go_to_lower_index():
+@both
+def test_topk_exact_ties_go_to_lower_index(O):
     l = np.array([1.0, 3.0, 3.0, 2.0, 3.0, -1.0])
     assert O.route(l[None], 2)[0][0].tolist() == [1, 2]
     assert O.route(l[None], 4)[0][0].tolist() == [1, 2, 4, 3]
     assert O.route(np.zeros((1, 5)), 3)[0][0].tolist() == [0, 1, 2]
 
 
-def test_softmax_weights_closed_forms():
+@both
+def test_softmax_weights_closed_forms(O):
     l = np.array([[2.0, 1.0, 0.0, -3.0]])
     ids, w = O.route(l, 2)
     assert ids[0].tolist() == [0, 1]
@@ -127,7 +139,8 @@ def test_topk_margin():
 
 
 # ---------------------------------------------------------------- experts and mixture
-def test_swiglu_hand_example():
+@both
+def test_swiglu_hand_example(O):
     g = golden("swiglu_hand_example.json")
     x = np.array(g["x"])
     ex = [(np.array(e["G"]), np.array(e["V"]), np.array(e["Dt"])) for e in g["experts"]]
@@ -137,7 +150,8 @@ def test_swiglu_hand_example():
     assert y.tolist() == pytest.approx(g["y"], rel=1e-15)
 
 
-def test_expert_output_matches_loops_nonsquare():
+@both
+def test_expert_output_matches_loops_nonsquare(O):
     rng = np.random.default_rng(4)
     H, I = 7, 5                       # non-square so a transposed operand cannot pass
     x = rng.normal(size=H)
@@ -146,7 +160,8 @@ def test_expert_output_matches_loops_nonsquare():
     assert np.max(np.abs(O.expert_output(x, G, V, Dt) - ref)) < 1e-12
 
 
-def test_k_equals_E_is_dense_softmax_mixture():
+@both
+def test_k_equals_E_is_dense_softmax_mixture(O):
     rng = np.random.default_rng(5)
     H, I, E = 6, 4, 5
     x = rng.normal(size=H)
@@ -164,7 +179,8 @@ def test_k_equals_E_is_dense_softmax_mixture():
     assert np.max(np.abs(y - ref)) < 1e-12
 
 
-def test_top1_of_one_expert_is_textbook_swiglu():
+@both
+def test_top1_of_one_expert_is_textbook_swiglu(O):
     rng = np.random.default_rng(6)
     H, I = 5, 3
     x = rng.normal(size=H)
@@ -174,7 +190,8 @@ def test_top1_of_one_expert_is_textbook_swiglu():
     assert np.max(np.abs(y - loop_expert(x.tolist(), *[m.tolist() for m in ex]))) < 1e-12
 
 
-def test_zero_gate_leaves_shared_only():
+@both
+def test_zero_gate_leaves_shared_only(O):
     rng = np.random.default_rng(7)
     H, I, E, k = 6, 4, 6, 2
     x = rng.normal(size=H)
@@ -186,7 +203,8 @@ def test_zero_gate_leaves_shared_only():
     assert np.max(np.abs(y - loop_expert(x.tolist(), *[m.tolist() for m in sh]))) < 1e-12
 
 
-def test_expert_permutation_only_permutes_ids():
+@both
+def test_expert_permutation_only_permutes_ids(O):
     rng = np.random.default_rng(8)
     H, I, E, k = 6, 3, 7, 3
     x = rng.normal(size=H)
@@ -211,7 +229,8 @@ def _sparse_setup(seed, H=5, I=3, E=5, k=2):
     return x, experts, sh, ids[0], w[0]
 
 
-def test_keep_all_channels_equals_dense():
+@both
+def test_keep_all_channels_equals_dense(O):
     x, experts, sh, ids, w = _sparse_setup(9)
     k, I = len(ids), experts[0][0].shape[0]
     kept, y = O.channel_select_token(x, ids, w, lambda e: experts[e],
@@ -222,7 +241,8 @@ def test_keep_all_channels_equals_dense():
     assert np.max(np.abs(y - dense)) < 1e-12
 
 
-def test_keep_zero_channels_is_shared_only():
+@both
+def test_keep_zero_channels_is_shared_only(O):
     x, experts, sh, ids, w = _sparse_setup(10)
     kept, y = O.channel_select_token(x, ids, w, lambda e: experts[e],
                                      lambda e: O.down_norms(experts[e][2]), 0, shared=[sh])
@@ -230,9 +250,10 @@ def test_keep_zero_channels_is_shared_only():
     assert np.max(np.abs(y - O.expert_output(x, *sh))) < 1e-15
 
 
+@both
 @pytest.mark.parametrize("mode", ["gate_dnorm", "router_weighted"])
 @pytest.mark.parametrize("keep", [1, 2, 3, 4])
-def test_channel_select_bruteforce(mode, keep):
+def test_channel_select_bruteforce(mode, keep, O):
     x, experts, sh, ids, w = _sparse_setup(11 + keep)
     I = experts[0][0].shape[0]
     cands = [(i, j) for i in range(len(ids)) for j in range(I)]
@@ -259,7 +280,8 @@ def test_channel_select_bruteforce(mode, keep):
     assert np.max(np.abs(y - ref)) < 1e-12
 
 
-def test_equal_down_norms_rank_by_gate():
+@both
+def test_equal_down_norms_rank_by_gate(O):
     rng = np.random.default_rng(12)
     H, I, E, k = 6, 8, 4, 2
     x = rng.normal(size=H)
@@ -276,7 +298,8 @@ def test_equal_down_norms_rank_by_gate():
     assert kept.tolist() == sorted(cid[np.argsort(-act, kind="stable")[:5]].tolist())
 
 
-def test_channel_ties_go_to_lower_channel_id():
+@both
+def test_channel_ties_go_to_lower_channel_id(O):
     """Equal scores are kept in channel-id order e*I + j, not in routing-slot order: with the
     routing (1, 0) the four tied channels are, in slot order, ids 3, 4, 0, 1; the lowest
     three ids are 0, 1, 3."""
@@ -290,7 +313,8 @@ def test_channel_ties_go_to_lower_channel_id():
 
 
 # ---------------------------------------------------------------- union and touched counts
-def test_union_matches_sets():
+@both
+def test_union_matches_sets(O):
     rng = np.random.default_rng(13)
     E, k, B = 12, 3, 9
     ids = np.stack([rng.choice(E, k, replace=False) for _ in range(B)])
