@@ -350,15 +350,14 @@ PHASES = {
            13: "partial output published", 14: "reducer: all partials arrived",
            15: "reducer: y written"},
     "cs": {0: "start", 1: "router rows published", 3: "routing known (top-k + softmax)",
-           4: "gate values published", 2: "shared experts streamed",
-           5: "all gate values gathered and scored", 6: "threshold known",
+           4: "own scores published", 2: "shared experts streamed",
+           5: "all scores gathered", 6: "threshold known", 23: "own kept list ready",
            7: "kept rows streamed", 8: "top-k: wave 0 keys sorted in runs",
            9: "top-k: wave 0 top of its keys", 10: "top-k: wave 0 keys polled",
            11: "top-k: ranked", 12: "router rows computed", 13: "partial output published",
            14: "reducer: all partials arrived", 15: "reducer: y written",
-           16: "gather: gate words in (wave 0)", 17: "select: histogram done",
-           18: "select: bin found", 19: "select: bin members listed",
-           21: "kept counts scanned", 22: "slot tables ready", 23: "kept list ready"},
+           16: "gather: scores in (wave 0)", 17: "select: histogram done",
+           18: "select: bin found", 19: "select: bin members listed"},
 }
 
 

@@ -9,21 +9,23 @@
 // the exact gate value (every gate row is read to score) and ||d_j|| precomputed at load.
 //
 // Phases inside the launch (one workgroup per CU):
-//  1. router rows and the exact top-k in every workgroup, as in the dense kernel; the
-//     workgroup's shared-expert rows are warmed into L2 while the logits are awaited;
-//  2. gate pass: each workgroup computes g for its contiguous share of the k*I candidates
-//     and publishes each value with the launch tag (a 64-bit word, as the router logits);
-//  3. the workgroup's share of the shared experts, whose reads cover the gate hand-off;
-//  4. every workgroup gathers all k*I gate values (waiting on the tags), scores every
-//     candidate itself (||d_j|| from the load-time table) and finds the same K-th largest
-//     score T and how many candidates tied at T are kept: a 2048-bin histogram over the
-//     score range, a scan for the bin holding the K-th, and a rank count of that bin's few
-//     members (a radix search on the score bits when the bin is crowded);
-//  5. a scan over the candidates gives every kept channel its place in the output order
-//     (ascending e*I + j: experts in id order, channels in order; ties at T go to the lower
-//     e*I + j), and each workgroup takes an equal slice of the K kept channels in that
-//     order, writes their ids, and streams their up row and down row only, with g from LDS;
-//  6. the deterministic cross-workgroup sum of the partial outputs.
+//  1. router rows and the exact top-k in every workgroup, as in the dense kernel; once the
+//     logits arrive, the workgroup's shared-expert rows are warmed into L2;
+//  2. gate pass: each workgroup owns a contiguous share of the k*I candidates, reads their
+//     gate rows, and publishes each score as a 32-bit word carrying the launch parity in its
+//     lowest bit; the gate values and scores of its own candidates stay in LDS;
+//  3. its share of the shared experts, which covers the scores' hand-off;
+//  4. every workgroup gathers all k*I scores and finds the same K-th largest T, how many
+//     scores equal T and how many of those are kept: a 2048-bin histogram over the score
+//     range, a scan for the bin holding the K-th, and a rank count of that bin's few members
+//     (a radix search on the score bits when the bin is crowded); meanwhile the up and down
+//     rows of its own candidates that scored at least 0.85 of the previous launch's threshold
+//     are prefetched into L2 (a hint only; it decides nothing);
+//  5. each workgroup streams the up and down rows of its own kept candidates (those above T,
+//     and the ties at T when all are kept; otherwise the lowest e*I + j of them, found by a
+//     scan over all candidates in that order), with g from LDS;
+//  6. the deterministic cross-workgroup sum of the partial outputs; after its partial is out,
+//     workgroup 0 writes the kept list in ascending e*I + j and the threshold hint.
 #include "layer_common.h"
 
 namespace moe {
@@ -42,7 +44,7 @@ constexpr int kSlotPad = kMaxSlots + 4;  // slot tables of kMaxSlots + 1 ints, p
 struct CSLaunch {
   B1Args a;
   const float* dnorm;  // [E*I]
-  uint64_t* g_ws;      // [k*I] launch-tagged gate values
+  uint64_t* g_ws;      // channel scores with the launch parity, one copy per XCD
   int32_t* kept_out;   // [K]
   int K, mode, R, SW, tsz;
 };
@@ -74,7 +76,7 @@ __device__ inline int block_excl_scan(int v, int* sh, const Ctx& c, int* total) 
 // count from the top reaches the remaining need.  Requires 0 < K < n.  `hist` is LDS of
 // kSelBins ints, `sh` of 48 ints.
 __device__ inline uint32_t select_threshold(const uint32_t* u, int n, int K, int* need_out,
-                                            int* hist, int* sh, const Ctx& c) {
+                                            int* ties_out, int* hist, int* sh, const Ctx& c) {
   uint32_t prefix = 0, mask = 0;
   int need = K;
   const int shifts[3] = {21, 10, 0};
@@ -103,6 +105,7 @@ __device__ inline uint32_t select_threshold(const uint32_t* u, int n, int K, int
         if (before < need && need <= before + cnt) {
           sh[0] = nb - 1 - b;
           sh[1] = need - before;
+          sh[47] = cnt;  // after the last digit: how many values equal T
         }
         before += cnt;
       }
@@ -115,6 +118,7 @@ __device__ inline uint32_t select_threshold(const uint32_t* u, int n, int K, int
     __syncthreads();
   }
   *need_out = need;
+  *ties_out = sh[47];
   return prefix;
 }
 
@@ -140,54 +144,64 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 
 // The K-th largest of the n score patterns (0 < K < n; non-negative floats, whose bit
 // patterns order like the values; each thread holds eight of them in sb, all of them are in sv
-// for the radix fallback) and how many of the values equal to it are kept (*need;
-// the ties kept are decided later, in channel order).  One histogram pass bins the patterns
+// for the radix fallback), how many of the values equal to it are kept (*need; which ones is
+// decided later, in channel order) and how many there are (*ties).  One histogram pass bins the patterns
 // linearly over [lo, hi] (a monotone binning: bin order is score order); a scan over the bins
 // finds the bin holding the K-th largest and its rank there; that bin's members (few for a
 // spread of scores) are ranked by brute force.  A crowded bin (more than kSelCand members)
 // falls back to the radix search.  lo, hi come in per wave in sh[4 + w] and sh[20 + w];
 // hist (kSelBins ints) and sh[44] come in cleared; mem is LDS of kSelCand words.
 __device__ inline uint32_t select_kth(const uint32_t* sv, const uint32_t (&sb)[8], bool mine,
-                                      int n, int K, int* need_out, int* hist, uint32_t* mem,
-                                      int* sh, const Ctx& c) {
+                                      int n, int K, int* need_out, int* ties_out, int* hist,
+                                      uint32_t* mem, int* sh, const Ctx& c) {
   const int nw = c.nthreads >> 6;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int w = 0; w < nw; ++w) {
-    lo = min(lo, (uint32_t)sh[4 + w]);
-    hi = max(hi, (uint32_t)sh[20 + w]);
-  }
+  // the range over all waves: lane w reads wave w's bounds, then a wave reduction
+  uint32_t lo = c.lane < nw ? (uint32_t)sh[4 + c.lane] : 0xFFFFFFFFu;
+  uint32_t hi = c.lane < nw ? (uint32_t)sh[20 + c.lane] : 0u;
+  lo = __builtin_amdgcn_readfirstlane(wave_min_u32(lo));
+  hi = __builtin_amdgcn_readfirstlane(wave_max_u32(hi));
   if (hi > lo) {
     const float inv = (float)kSelBins / ((float)(hi - lo) + 1.0f);
     auto bin = [&](uint32_t v) {
       const int b = (int)((float)(v - lo) * inv);
       return b < kSelBins - 1 ? b : kSelBins - 1;
     };
+    int bins[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bins[i] = bin(sb[i]);
     if (mine) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) atomicAdd(&hist[bin(sb[i])], 1);
+      for (int i = 0; i < 8; ++i) atomicAdd(&hist[bins[i]], 1);
     }
     __syncthreads();
     MOE_STAMP(c.stamps, 17);
-    // thread t holds bins 2047 - 2t and 2046 - 2t (counts from the top); an inclusive scan of
-    // those pair counts over the workgroup finds the bin where the count from the top reaches K
-    const int bpt = kSelBins / c.nthreads;  // 2 for 1024 threads
-    int cnt[4] = {0, 0, 0, 0};
-    int local = 0;
-    for (int i = 0; i < bpt; ++i) {
-      cnt[i] = hist[kSelBins - 1 - bpt * c.tid - i];
-      local += cnt[i];
-    }
-    int total;
-    const int before0 = block_excl_scan(local, sh + 48, c, &total);
-    if (before0 < K && K <= before0 + local) {
-      int before = before0;
-      for (int i = 0; i < bpt; ++i) {
-        if (before < K && K <= before + cnt[i]) {
-          sh[40] = kSelBins - 1 - bpt * c.tid - i;
-          sh[41] = K - before;  // the rank wanted within the bin
-          sh[42] = cnt[i];
-        }
-        before += cnt[i];
+    // Wave 0 finds the bin where the count from the top reaches K: lane l sums super-bin l
+    // (the 32 bins [2048 - 32 (l + 1), 2048 - 32 l), counted from the top), a scan over the
+    // lanes finds the super-bin, and a scan over its 32 bins (lane l: the l-th from its top)
+    // the bin
+    if (c.tid < kWave) {
+      constexpr int kSuper = kSelBins / kWave;  // 32 bins per lane
+      const int4* hb = reinterpret_cast<const int4*>(hist + kSelBins - kSuper * (c.lane + 1));
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < kSuper / 4; ++u) {
+        const int4 q = hb[u];
+        cnt += q.x + q.y + q.z + q.w;
+      }
+      const int incl = wave_incl_scan(cnt);
+      const int excl = incl - cnt;
+      const uint64_t bal = __ballot(excl < K && K <= incl);
+      const int L = (int)__builtin_ctzll(bal);
+      const int before = __builtin_amdgcn_readlane(excl, L);
+      const int b = kSelBins - kSuper * L - 1 - c.lane;
+      const int v = c.lane < kSuper ? hist[b] : 0;
+      const int incl2 = wave_incl_scan(v) + before;
+      const int excl2 = incl2 - v;
+      const bool here = c.lane < kSuper && excl2 < K && K <= incl2;
+      if (here) {
+        sh[40] = b;
+        sh[41] = K - excl2;  // the rank wanted within the bin
+        sh[42] = v;
       }
     }
     __syncthreads();
@@ -197,11 +211,27 @@ __device__ inline uint32_t select_kth(const uint32_t* sv, const uint32_t (&sb)[8
       if (mine) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (bin(sb[i]) == bstar) mem[atomicAdd(&sh[44], 1)] = sb[i];
+          if (bins[i] == bstar) mem[atomicAdd(&sh[44], 1)] = sb[i];
       }
       __syncthreads();
       MOE_STAMP(c.stamps, 19);
-      if (c.tid < m) {
+      if (m <= kWave) {
+        // wave 0: lane l holds member l; each counts the members above and at least it
+        if (c.tid < kWave) {
+          const uint32_t key = c.lane < m ? mem[c.lane] : 0u;
+          int gt = 0, ge = 0;
+          for (int j = 0; j < m; ++j) {
+            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+            gt += o > key ? 1 : 0;
+            ge += o >= key ? 1 : 0;
+          }
+          if (c.lane < m && gt < needb && needb <= ge) {  // equal keys agree
+            sh[45] = (int)key;
+            sh[46] = needb - gt;
+            sh[47] = ge - gt;  // how many values equal it (all lie in this bin)
+          }
+        }
+      } else if (c.tid < m) {
         const uint32_t key = mem[c.tid];
         int gt = 0, ge = 0;
         int j = 0;
@@ -223,20 +253,101 @@ __device__ inline uint32_t select_kth(const uint32_t* sv, const uint32_t (&sb)[8
         if (gt < needb && needb <= ge) {  // the needb-th largest of the bin (equal keys agree)
           sh[45] = (int)key;
           sh[46] = needb - gt;
+          sh[47] = ge - gt;
         }
       }
       __syncthreads();
       *need_out = sh[46];
+      *ties_out = sh[47];
       return (uint32_t)sh[45];
     }
   }
   // all scores equal, or a crowded bin: the exact radix search over the bit patterns
-  return select_threshold(sv, n, K, need_out, hist, sh, c);
+  return select_threshold(sv, n, K, need_out, ties_out, hist, sh, c);
 }
 
 // Candidates per thread in the selection: eight consecutive ones, which lie in one slot (I
-// is a multiple of 8), so their gate values, norms and scores stay in registers.
+// is a multiple of 8), so their scores stay in registers.
 constexpr int kCh = 8;
+// Own candidates per workgroup at most (ceil(k*I / P); the host checks)
+constexpr int kOwnMax = kCsOwnMax;
+
+// The kept candidates in the output order (ascending e*I + j: slots by expert id, a slot
+// without an expert after every expert, channels within a slot in order).  Candidate f of this
+// thread's eight [c0, c0 + 8) (slot sl0, first channel j0) is kept if its score pattern sb is
+// above T, or equals T and is among the first `need` such in that order.  Returns the kept
+// mask (bit i: candidate c0 + i) and, in pos[i], each kept candidate's output position.  Runs
+// a packed workgroup scan in candidate order, per-slot counts and (wave 0) the slots' ranks;
+// every thread must call.  slot_* are LDS of kSlotPad ints each, sh of 96 ints.
+__device__ inline uint32_t kept_in_order(const uint32_t (&sb)[kCh], bool mine, int sl0, int j0,
+                                         uint32_t T, int need, bool all, bool none, int k,
+                                         int E, const int* s_ids, int* sh, int* slot_gt,
+                                         int* slot_eq, int* slot_tk, int* slot_base,
+                                         const Ctx& c, int (&pos)[kCh]) {
+  int ngt = 0, neq = 0;
+  bool ab[kCh], ti[kCh];
+#pragma unroll
+  for (int i = 0; i < kCh; ++i) {
+    ab[i] = mine && !none && (all || sb[i] > T);
+    ti[i] = mine && !none && !all && sb[i] == T;
+    ngt += ab[i] ? 1 : 0;
+    neq += ti[i] ? 1 : 0;
+  }
+  int tot;
+  const int ex = block_excl_scan(ngt * 65536 + neq, sh + 48, c, &tot);
+  const int gtp = ex >> 16, eqp = ex & 0xFFFF;  // counts before this thread's candidates
+  // the prefixes at the slot boundaries, written by the thread whose candidates start a slot
+  if (mine && j0 == 0) {
+    slot_gt[sl0] = gtp;
+    slot_eq[sl0] = eqp;
+  }
+  if (c.tid == 0) {
+    slot_gt[k] = tot >> 16;
+    slot_eq[k] = tot & 0xFFFF;
+  }
+  __syncthreads();
+  // Wave 0, lane s < k: the slot's rank in the output order (ranks are distinct), its counts
+  // moved to lane rank, exclusive scans over the ranks give the ties kept before it and its
+  // output base, moved back to lane s.
+  if (c.tid < kWave) {
+    const int sl = c.lane;
+    const int key = sl < k ? (s_ids[sl] >= 0 ? s_ids[sl] : E + sl) : 0x7FFFFFFF;
+    int rank = 0;
+    for (int o = 0; o < k; ++o) {
+      const int ko = __builtin_amdgcn_readlane(key, o);
+      rank += ko < key ? 1 : 0;
+    }
+    const int dst = sl < k ? rank : sl;  // lanes past k keep their place (zero counts)
+    const int eq_s = sl < k ? slot_eq[sl + 1] - slot_eq[sl] : 0;
+    const int gt_s = sl < k ? slot_gt[sl + 1] - slot_gt[sl] : 0;
+    const int req = __builtin_amdgcn_ds_permute(dst * 4, eq_s);
+    const int rgt = __builtin_amdgcn_ds_permute(dst * 4, gt_s);
+    const int eqb = wave_incl_scan(req) - req;
+    const int tk = min(max(need - eqb, 0), req);
+    const int kept = rgt + tk;
+    const int base = wave_incl_scan(kept) - kept;
+    const int tk_s = __shfl(tk, dst, kWave);
+    const int base_s = __shfl(base, dst, kWave);
+    if (sl < k) {
+      slot_tk[sl] = tk_s;
+      slot_base[sl] = base_s;
+    }
+  }
+  __syncthreads();
+  uint32_t mask = 0;
+  if (mine) {
+    const int tk = slot_tk[sl0], sbase = slot_base[sl0];
+    int gin = gtp - slot_gt[sl0], qin = eqp - slot_eq[sl0];
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      pos[i] = sbase + gin + min(qin, tk);
+      if (ab[i] || (ti[i] && qin < tk)) mask |= 1u << i;
+      gin += ab[i] ? 1 : 0;
+      qin += ti[i] ? 1 : 0;
+    }
+  }
+  return mask;
+}
 
 template <DT ET, DT ST, DT RT, int C, int CPT>
 __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
@@ -261,7 +372,6 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   const int I = a.I, k = a.k;
   const int n = k * I;                                 // <= kCh * nthreads (host checks)
   const DivI divI(I);
-  const int kl = (L.K + c.P - 1) / c.P + 1;            // kept channels per workgroup, at most
   int* s_int = reinterpret_cast<int*>(c.red + 2 * c.red_stride);  // [16]
   int* s_ids = s_int + 16;                                          // [64]
   float* s_w = reinterpret_cast<float*>(s_ids + 64);                // [64]
@@ -270,14 +380,21 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   int* slot_eq = slot_gt + kSlotPad;                                // [kMaxSlots + 1]
   int* hist = slot_eq + kSlotPad;                                   // [kSelBins]
   uint32_t* mem = reinterpret_cast<uint32_t*>(hist + kSelBins);     // [kSelCand]
-  int* klist = reinterpret_cast<int*>(mem + kSelCand);              // [kl]
-  float* gl = reinterpret_cast<float*>(klist + ((kl + 3) & ~3));    // [n] gate values
-  uint32_t* sv = reinterpret_cast<uint32_t*>(gl + n);               // [n] score patterns
-  float* big = reinterpret_cast<float*>(sv + n);
+  float* own_g = reinterpret_cast<float*>(mem + kSelCand);          // [kOwnMax] gate values
+  uint32_t* own_s = reinterpret_cast<uint32_t*>(own_g + kOwnMax);   // [kOwnMax] score patterns
+  float* own_dn = reinterpret_cast<float*>(own_s + kOwnMax);        // [kOwnMax] ||d_j||
+  int* own_keep = reinterpret_cast<int*>(own_dn + kOwnMax);         // [kOwnMax] kept flags
+  int* klist = own_keep + kOwnMax;                                  // [kOwnMax] kept, in order
+  uint32_t* sv = reinterpret_cast<uint32_t*>(klist + kOwnMax);      // [n] score patterns
+  float* big = reinterpret_cast<float*>(sv + ((n + 3) & ~3));
   Ctrl* ctrl = a.ctrl;
-  // channel-selection launches on this workspace so far: its gate values carry the parity
+  // channel-selection launches on this workspace so far: its scores carry the parity
   const uint32_t cs_ep = load_relaxed_dev(&ctrl->cs_epoch);
   const uint32_t gpar = (cs_ep + 1u) & 1u;
+  const float t_prev = __uint_as_float(load_relaxed_dev(&ctrl->cs_tprev));
+  // the scores, one copy per XCD (npad words each); this workgroup polls copy wg % 8
+  const int npad = (n + 63) & ~63;
+  uint32_t* scores = reinterpret_cast<uint32_t*>(L.g_ws);
 
   float xv[CPT * 8], yv[CPT * 8];
   load_x<8, CPT>(a.x, c, xv);
@@ -291,39 +408,33 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   router_finish<RT, CPT>(rr, a.router, a.E, xv, a.rlog, big, reinterpret_cast<uint32_t*>(s_int),
                          c);
   MOE_STAMP(c.stamps, 1);
+  // this workgroup's shared-expert rows are warmed into L2 by waves 1.. once every logit has
+  // been read, while wave 0 finishes the top-k (earlier, the warm loads delay the polls)
   const long long nsc = (long long)a.NS * a.IS;  // flat shared channel f of [NS][IS] is row f
   const int s0 = (int)(nsc * c.wg / c.P), s1 = (int)(nsc * (c.wg + 1) / c.P);
   uint32_t warm[kWarmLoads] = {0, 0};
-  if (a.route_inside && a.NS > 0)
-    warm_rows(reinterpret_cast<const uint8_t*>(a.sh_gate),
-              reinterpret_cast<const uint8_t*>(a.sh_up),
-              reinterpret_cast<const uint8_t*>(a.sh_down_t), s0, s1,
-              (uint32_t)Fmt<ST>::row_bytes(a.H),
-              min(c.nthreads, (a.E + kWave - 1) / kWave * kWave), c, warm);
+  auto warm_shared = [&] {
+    if (a.NS > 0)
+      warm_rows(reinterpret_cast<const uint8_t*>(a.sh_gate),
+                reinterpret_cast<const uint8_t*>(a.sh_up),
+                reinterpret_cast<const uint8_t*>(a.sh_down_t), s0, s1,
+                (uint32_t)Fmt<ST>::row_bytes(a.H), kWave, c, warm);
+  };
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, k, ctrl,
-                reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c);
+                reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c, warm_shared);
   MOE_STAMP(c.stamps, 3);
 
-  // This thread's eight candidates [c0, c0 + 8) of slot sl0 (threads past n / 8 have none):
-  // their down-row norms, in flight through the gate pass
-  const int c0 = c.tid * kCh;
-  const bool mine = c0 < n;
-  const int sl0 = mine ? divI.div(c0) : 0, j0 = c0 - sl0 * I;
-  const int e0 = s_ids[sl0];
-  f32x4 dn4[2];
-  {
-    const float* dp = L.dnorm + (size_t)(e0 >= 0 ? e0 : 0) * I + (mine ? j0 : 0);
-    dn4[0] = reinterpret_cast<const f32x4*>(dp)[0];
-    dn4[1] = reinterpret_cast<const f32x4*>(dp)[1];
-  }
-  const float wsl = L.mode == 1 ? s_w[sl0] : 1.0f;
-
-  // 2. gate pass over this workgroup's share [g0, g1) of the candidates: the rows' loads go
-  // out first, the shared experts' right behind them; the gate dot products are computed and
-  // published (a 32-bit word each, the launch parity in its lowest bit) while the shared rows
-  // arrive; 3. then this workgroup's share of the shared experts (weight 1), whose reads cover
-  // the hand-off of the gate values
+  // 2. gate pass over this workgroup's own candidates [g0, g1) (flat f = slot * I + j): the
+  // down-row norms and the gate rows are loaded, each score s = |silu(g)| ||d|| (times w_e)
+  // is published as a 32-bit word with the launch parity in its lowest bit, and g and s stay
+  // in LDS for this workgroup's own kept channels
   const int g0 = (int)((long long)n * c.wg / c.P), g1 = (int)((long long)n * (c.wg + 1) / c.P);
+  const int nown = g1 - g0;
+  float dnv = 0.0f;
+  if (c.tid < nown) {
+    const int f = g0 + c.tid, sl = divI.div(f), e = s_ids[sl];
+    dnv = e >= 0 ? L.dnorm[(size_t)e * I + (f - sl * I)] : 0.0f;
+  }
   auto gate_rows = [&](int base, long long (&rows)[kGateBatch]) {
 #pragma unroll
     for (int q = 0; q < kGateBatch; ++q) {
@@ -336,53 +447,96 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
       }
     }
   };
-  auto publish_gate = [&](int base, const float (&g)[kGateBatch]) {
+  auto publish = [&](int base, const float (&g)[kGateBatch]) {
     if (c.t < kGateBatch) {
       float gq = 0.0f;
 #pragma unroll
       for (int q = 0; q < kGateBatch; ++q) gq = (q == c.t) ? g[q] : gq;
       const int f = base + c.team * kGateBatch + c.t;
-      if (f < g1)
-        __hip_atomic_store(reinterpret_cast<uint32_t*>(L.g_ws) + f,
-                           (__float_as_uint(gq) & ~1u) | gpar, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      if (f < g1) {
+        const int o = f - g0;
+        const float wsl = L.mode == 1 ? s_w[divI.div(f)] : 1.0f;
+        const uint32_t sp = __float_as_uint(fabsf(silu(gq)) * own_dn[o] * wsl) & ~1u;
+#pragma unroll
+        for (int x = 0; x < kPollCopies; ++x)
+          __hip_atomic_store(scores + (size_t)x * npad + f, sp | gpar, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        own_g[o] = gq;
+        own_s[o] = sp;  // the value every workgroup will see
+      }
     }
   };
-  TeamRows<ET, kGateBatch, CPT> gr;
   {
+    TeamRows<ET, kGateBatch, CPT> gr;
     long long rows[kGateBatch];
     gate_rows(g0, rows);
     team_dots_load<ET, kGateBatch, CPT>(a.gate, a.gate_s, rows, c, gr);
-  }
-  auto finish_gates = [&] {
+    if (c.tid < nown) own_dn[c.tid] = dnv;  // visible after the barrier of the dots below
     float g[kGateBatch];
     team_dots_compute<ET, kGateBatch, CPT>(gr, xv, c, g);
-    publish_gate(g0, g);
+    publish(g0, g);
     for (int base = g0 + c.nteams * kGateBatch; base < g1; base += c.nteams * kGateBatch) {
-      long long rows[kGateBatch];
       gate_rows(base, rows);
       team_dots<ET, kGateBatch, CPT>(a.gate, a.gate_s, rows, xv, c, g);
-      publish_gate(base, g);
+      publish(base, g);
     }
-    MOE_STAMP(c.stamps, 4);
+  }
+  __syncthreads();
+  MOE_STAMP(c.stamps, 4);
+
+  // 3. (issued after the gather below) prefetch into L2 the up and down rows of the own
+  // candidates likely to be kept: scores at least 0.85 of the previous launch's threshold (a
+  // hint: the keep decision does not use it).  One 4-byte load per 128-byte line; a wave per
+  // candidate.
+  // Up to two candidates per wave and two loads per lane and candidate (rows up to 8 KB); the
+  // loaded words are kept in registers and consumed only at the end of the kernel, so no wait
+  // before then covers them.
+  uint32_t warm2[2][2] = {{0, 0}, {0, 0}};
+  auto warm_kept = [&] {
+    if (t_prev > 0.0f && L.K > 0 && L.K < n) {
+      const uint32_t rb = (uint32_t)Fmt<ET>::row_bytes(a.H), lines = (rb + 127) / 128;
+      const int nw = c.nthreads / kWave;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int o = c.tid / kWave + nw * u;
+        if (o < nown && __uint_as_float(own_s[o]) >= 0.85f * t_prev) {
+          const int f = g0 + o, sl = divI.div(f), e = s_ids[sl];
+          if (e >= 0) {
+            const size_t row = (size_t)e * I + (f - sl * I);
+            const uint8_t* vr = reinterpret_cast<const uint8_t*>(a.up) + row * rb;
+            const uint8_t* dr = reinterpret_cast<const uint8_t*>(a.down_t) + row * rb;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t l = c.lane + kWave * h;
+              if (l < 2 * lines) {
+                const uint8_t* p = l < lines ? vr + 128ull * l : dr + 128ull * (l - lines);
+                warm2[u][h] = *reinterpret_cast<const uint32_t*>(p);
+              }
+            }
+          }
+        }
+      }
+    }
   };
+
+  // this workgroup's share of the shared experts (weight 1, warm in L2): covers the hand-off
+  // of the scores
   if (a.NS > 0)
     stream_channels<ST, C, CPT, true, true>(
         a.sh_gate, a.sh_up, a.sh_down_t, nullptr, nullptr, nullptr, s0, s1,
-        [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c,
-        finish_gates);
-  else
-    finish_gates();
+        [](int f, long long& row, float& wt, float&) { row = f; wt = 1.0f; }, xv, yv, c);
   MOE_STAMP(c.stamps, 2);
 
-  // 4. every gate value: this thread's eight as two 16-byte device-coherent loads, polled
-  // again while any of them lacks the launch parity; scores in registers, the gate values
-  // and score patterns to LDS, the range of the scores per wave; the histogram and the
-  // selection words cleared meanwhile
-  float gv[kCh];
+  // 4. every score: this thread's eight as two 16-byte device-coherent loads from this XCD's
+  // copy, polled again while any lacks the launch parity; the patterns to LDS (for the radix
+  // fallback and the output list), the range per wave; the histogram and the selection words
+  // cleared meanwhile
+  const int c0 = c.tid * kCh;
+  const bool mine = c0 < n;
+  const int sl0 = mine ? divI.div(c0) : 0, j0 = c0 - sl0 * I;
   uint32_t sb[kCh];
   {
-    const rsrc_t gsrc = make_rsrc(L.g_ws, (uint32_t)n * 4u);
+    const rsrc_t gsrc = make_rsrc(scores + (size_t)(c.wg % kPollCopies) * npad, (uint32_t)n * 4u);
     u32x4 w4[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -408,26 +562,19 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
     }
     const uint32_t wr[kCh] = {w4[0].x, w4[0].y, w4[0].z, w4[0].w,
                               w4[1].x, w4[1].y, w4[1].z, w4[1].w};
-    const float dn[kCh] = {dn4[0].x, dn4[0].y, dn4[0].z, dn4[0].w,
-                           dn4[1].x, dn4[1].y, dn4[1].z, dn4[1].w};
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
     for (int i = 0; i < kCh; ++i) {
-      gv[i] = __uint_as_float(wr[i] & ~1u);  // the value every workgroup sees
-      const float sc = mine && e0 >= 0 ? fabsf(silu(gv[i])) * dn[i] * wsl : 0.0f;
-      sb[i] = __float_as_uint(sc);
+      sb[i] = mine ? wr[i] & ~1u : 0u;
       lo = mine ? min(lo, sb[i]) : lo;
       hi = mine ? max(hi, sb[i]) : hi;
     }
     MOE_STAMP_AFTER(c.stamps, 16, lo);
     if (mine) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        reinterpret_cast<f32x4*>(gl + c0)[h] = f32x4{gv[4 * h], gv[4 * h + 1], gv[4 * h + 2],
-                                                     gv[4 * h + 3]};
+      for (int h = 0; h < 2; ++h)
         reinterpret_cast<u32x4*>(sv + c0)[h] = u32x4{sb[4 * h], sb[4 * h + 1], sb[4 * h + 2],
                                                      sb[4 * h + 3]};
-      }
     }
     for (int i = c.tid; i < kSelBins; i += c.nthreads) hist[i] = 0;
     lo = wave_min_u32(lo);
@@ -440,116 +587,94 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   }
   __syncthreads();
   MOE_STAMP(c.stamps, 5);
+  warm_kept();  // its loads land in L2 during the selection, which issues no memory loads
 
-  // 5. the threshold: T = the K-th largest score (all kept when K >= n, none when K = 0)
+  // 6. the threshold: T = the K-th largest score (all kept when K >= n, none when K = 0), how
+  // many of the scores equal to T are kept (need) and how many there are (ties)
   uint32_t T = 0u;
-  int need = 0;
-  if (L.K > 0 && L.K < n) T = select_kth(sv, sb, mine, n, L.K, &need, hist, mem, sh, c);
+  int need = 0, ties = 0;
+  if (L.K > 0 && L.K < n) T = select_kth(sv, sb, mine, n, L.K, &need, &ties, hist, mem, sh, c);
   const bool all = L.K >= n, none = L.K == 0;
   MOE_STAMP(c.stamps, 6);
-  // counts of this thread's candidates above T and equal to T (kept outright / tied),
-  // prefix-summed over the workgroup in candidate order (one scan: above in the upper 16 bits)
-  int ngt = 0, neq = 0;
-  bool ab[kCh], ti[kCh];
-#pragma unroll
-  for (int i = 0; i < kCh; ++i) {
-    ab[i] = mine && !none && (all || sb[i] > T);
-    ti[i] = mine && !none && !all && sb[i] == T;
-    ngt += ab[i] ? 1 : 0;
-    neq += ti[i] ? 1 : 0;
-  }
-  int tot;
-  const int ex = block_excl_scan(ngt * 65536 + neq, sh + 48, c, &tot);
-  MOE_STAMP(c.stamps, 21);
-  const int gtp = ex >> 16, eqp = ex & 0xFFFF;  // counts before c0
-  // the prefixes at the slot boundaries (slot s = candidates [s * I, (s + 1) * I)): written by
-  // the thread whose eight candidates start the slot
-  if (mine && j0 == 0) {
-    slot_gt[sl0] = gtp;
-    slot_eq[sl0] = eqp;
-  }
-  if (c.tid == 0) {
-    slot_gt[k] = tot >> 16;
-    slot_eq[k] = tot & 0xFFFF;
-  }
-  __syncthreads();
-  // Output order: slots by expert id (a slot without an expert after every expert, in slot
-  // order), channels within a slot in order; the candidates tied at T that are kept are the
-  // first `need` in that order.  Wave 0, lane s < k: the slot's rank in that order (ranks are
-  // distinct), its counts moved to lane rank, exclusive scans over the ranks give the ties
-  // kept before it and its output base, moved back to lane s.
-  int* slot_tk = hist;                // [k] ties kept in the slot (hist is free now)
-  int* slot_base = hist + kMaxSlots;  // [k] first output position of the slot's kept channels
-  if (c.tid < kWave) {
-    const int sl = c.lane;
-    const int key = sl < k ? (s_ids[sl] >= 0 ? s_ids[sl] : a.E + sl) : 0x7FFFFFFF;
-    int rank = 0;
-    for (int o = 0; o < k; ++o) {
-      const int ko = __builtin_amdgcn_readlane(key, o);
-      rank += ko < key ? 1 : 0;
-    }
-    const int dst = sl < k ? rank : sl;  // lanes past k keep their place (zero counts)
-    const int eq_s = sl < k ? slot_eq[sl + 1] - slot_eq[sl] : 0;
-    const int gt_s = sl < k ? slot_gt[sl + 1] - slot_gt[sl] : 0;
-    const int req = __builtin_amdgcn_ds_permute(dst * 4, eq_s);
-    const int rgt = __builtin_amdgcn_ds_permute(dst * 4, gt_s);
-    const int eqb = wave_incl_scan(req) - req;
-    const int tk = min(max(need - eqb, 0), req);
-    const int kept = rgt + tk;
-    const int base = wave_incl_scan(kept) - kept;
-    const int tk_s = __shfl(tk, dst, kWave);
-    const int base_s = __shfl(base, dst, kWave);
-    if (sl < k) {
-      slot_tk[sl] = tk_s;
-      slot_base[sl] = base_s;
-    }
-  }
-  __syncthreads();
-  MOE_STAMP(c.stamps, 22);
-  // each kept candidate's output position; this workgroup takes positions [ks0, ks1)
-  const int ks0 = (int)((long long)L.K * c.wg / c.P), ks1 = (int)((long long)L.K * (c.wg + 1) / c.P);
-  if (mine) {
-    const int gin0 = gtp - slot_gt[sl0], qin0 = eqp - slot_eq[sl0];
-    const int tk = slot_tk[sl0], sbase = slot_base[sl0];
-    int gin = gin0, qin = qin0;
+  // this workgroup's own kept candidates: above T, or at T when every tie is kept; when only
+  // some ties are (equal scores straddling the K-th place), the lowest e*I + j of them, which
+  // takes the output-order scan over all candidates
+  int* slot_tk = hist;                // [k] (hist is free now)
+  int* slot_base = hist + kMaxSlots;  // [k]
+  if (!all && !none && need < ties) {
+    int pos[kCh];
+    const uint32_t m = kept_in_order(sb, mine, sl0, j0, T, need, all, none, k, a.E, s_ids, sh,
+                                     slot_gt, slot_eq, slot_tk, slot_base, c, pos);
 #pragma unroll
     for (int i = 0; i < kCh; ++i) {
-      if (ab[i] || (ti[i] && qin < tk)) {
-        const int pos = sbase + gin + min(qin, tk);
-        if (pos >= ks0 && pos < ks1) {
-          klist[pos - ks0] = c0 + i;
-          L.kept_out[pos] = e0 >= 0 ? e0 * I + j0 + i : -1;
-        }
-      }
-      gin += ab[i] ? 1 : 0;
-      qin += ti[i] ? 1 : 0;
+      const int f = c0 + i;
+      if (mine && f >= g0 && f < g1) own_keep[f - g0] = (m >> i) & 1u;
     }
+  } else if (c.tid < nown) {
+    const uint32_t v = own_s[c.tid];
+    own_keep[c.tid] = !none && (all || v > T || (v == T && need == ties));
   }
   __syncthreads();
+  // wave 0 lists them in candidate order
+  if (c.tid < kWave) {
+    int nk = 0;
+    for (int o0 = 0; o0 < nown; o0 += kWave) {
+      const int o = o0 + c.lane;
+      const bool kk = o < nown && own_keep[o];
+      const uint64_t bal = __ballot(kk);
+      const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (kk) klist[nk + before] = o;
+      nk += __popcll(bal);
+    }
+    if (c.lane == 0) s_int[14] = nk;
+  }
+  __syncthreads();
+  const int nkept = s_int[14];
   MOE_STAMP(c.stamps, 23);
 
-  // 6. this workgroup's slice of the kept channels: up row and down row only, g from LDS
+  // 7. the own kept channels: up row and down row only, g from LDS
   stream_channels<ET, C, CPT, false, false>(
-      nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, 0, ks1 - ks0,
+      nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, 0, nkept,
       [=](int i, long long& row, float& wt, float& gvv) {
-        // i is wave-uniform, so are f, the slot and the expert: scalar row arithmetic
-        const int f = __builtin_amdgcn_readfirstlane(klist[i]);
+        // i is wave-uniform, so are the candidate, its slot and expert: scalar arithmetic
+        const int o = __builtin_amdgcn_readfirstlane(klist[i]);
+        const int f = g0 + o;
         const int sl = divI.div(f);
         const int e = __builtin_amdgcn_readfirstlane(s_ids[sl]);
         if (e >= 0) {
           row = (long long)e * I + (f - sl * I);
           wt = s_w[sl];
-          gvv = gl[f];
+          gvv = own_g[o];
         }
       },
       xv, yv, c);
   MOE_STAMP_AFTER(c.stamps, 7, yv[0]);
   __syncthreads();  // `big` is reused by the reduction below
 
-  // 7. deterministic cross-workgroup sum; its first reducer also advances the count of
+  // 8. deterministic cross-workgroup sum; its first reducer also advances the count of
   // channel-selection launches
   reduce_output<CPT>(yv, a.partials, a.y, ctrl, L.R, L.SW, big, c, &ctrl->cs_epoch, cs_ep + 1u);
-  s_int[15] = (int)(warm[0] ^ warm[1]);  // keeps the warming loads (see warm_rows)
+
+  // 9. workgroup 0 (not a reducer) writes the kept list after its partial output is out: every
+  // kept candidate's id e*I + j at its place in ascending order (-1 for a skipped given id),
+  // and the threshold as the next launch's prefetch hint
+  if (c.wg == 0 && !none && L.K > 0) {
+    __syncthreads();
+    uint32_t sb2[kCh];
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) sb2[i] = mine ? sv[c0 + i] : 0u;
+    int pos[kCh];
+    const uint32_t m = kept_in_order(sb2, mine, sl0, j0, T, need, all, none, k, a.E, s_ids, sh,
+                                     slot_gt, slot_eq, slot_tk, slot_base, c, pos);
+    const int e0 = mine ? s_ids[sl0] : -1;
+#pragma unroll
+    for (int i = 0; i < kCh; ++i)
+      if ((m >> i) & 1u) L.kept_out[pos[i]] = e0 >= 0 ? e0 * I + j0 + i : -1;
+    if (c.tid == 0 && !all) store_relaxed_dev(&ctrl->cs_tprev, T);
+  }
+  s_int[15] = (int)(warm[0] ^ warm[1] ^ warm2[0][0] ^ warm2[0][1] ^ warm2[1][0] ^
+                    warm2[1][1]);  // keeps the warming loads
 }
 
 template <DT ET, DT ST, DT RT, int C, int CPT>
@@ -585,12 +710,12 @@ hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStrea
 // tables, histogram, bin members, this workgroup's kept list, the gate values and score
 // patterns of all k*I candidates, and the larger of the router / top-k / output scratch.
 int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K) {
+  (void)K;
   const int nteams = threads / team_size(H);
   const int n = k * I;
-  const int kl = (K + wgs - 1) / wgs + 1;
   const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + 96) * 4 +
-                    2 * kSlotPad * 4 + kSelBins * 4 + kSelCand * 4 +
-                    ((kl + 3) & ~3) * 4 + 2 * n * 4;
+                    2 * kSlotPad * 4 + kSelBins * 4 + kSelCand * 4 + 5 * kOwnMax * 4 +
+                    ((n + 3) & ~3) * 4;
   const int ybuf = nteams * H * 4;
   const int topk = topk_lds_bytes(E, k);
   const int router = ((E + wgs - 1) / wgs) * 4;
@@ -604,8 +729,9 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_
                      int mode, DT et, DT st, DT rt, int wgs, int threads, hipStream_t s,
                      int* occ) {
   // the selection's bin scan holds at most four bins per thread
-  if (a.k > kMaxSlots || (long long)a.k * a.I > (long long)kCh * threads || a.I % kCh != 0 ||
-      threads * 4 < kSelBins || threads > 1024)
+  const long long n = (long long)a.k * a.I;
+  if (a.k > kMaxSlots || n > (long long)kCh * threads || a.I % kCh != 0 ||
+      threads * 4 < kSelBins || threads > 1024 || (n + wgs - 1) / wgs > kOwnMax)
     return hipErrorInvalidValue;
   CSLaunch L;
   L.a = a;

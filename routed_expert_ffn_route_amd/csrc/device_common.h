@@ -29,6 +29,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 constexpr int kNT = 2;  // cache policy of the weight streams: non-temporal
+// Words that every workgroup polls (router logits, channel scores) are written in one copy
+// per XCD (workgroup w runs on XCD w % 8, reads copy w % 8): a line polled by all 256
+// workgroups queues their requests at one memory channel; a copy is polled by 32.  Any copy
+// holds the same data, so a different workgroup-to-XCD mapping only costs locality.
+constexpr int kPollCopies = 8;
 constexpr int kSc1 = 16;  // cache policy of device-coherent buffer loads (sc1)
 // global-memory (address space 1) views: loads through them are global_load_* (never flat)
 typedef __attribute__((address_space(1))) uint8_t gbl_u8;
@@ -529,9 +534,15 @@ __device__ __forceinline__ uint64_t merge_two(uint64_t r, uint64_t s, int lane) 
 // and wave 0 merges them.  Returns in wave 0, lane i < k, the i-th largest key (0 past n).
 // `cand` is LDS of nwaves * KP keys.  KP = the smallest power of two >= k (<= 64).  All
 // threads of the workgroup must call; one barrier.
-template <int KP, typename KeyOf>
+struct NoHook {
+  __device__ void operator()() const {}
+};
+// after_keys() runs in every wave but wave 0 once all keys have been read (after the barrier
+// that follows the per-wave runs), while wave 0 merges the runs.
+template <int KP, typename KeyOf, typename AfterKeys = NoHook>
 __device__ inline uint64_t wg_topk_bitonic(int n, KeyOf key_of, uint64_t* cand,
-                                           uint64_t* stamps = nullptr) {
+                                           uint64_t* stamps = nullptr,
+                                           AfterKeys after_keys = AfterKeys()) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nwaves = blockDim.x / kWave;
   const int chunks = (n + kWave - 1) / kWave;
@@ -551,6 +562,7 @@ __device__ inline uint64_t wg_topk_bitonic(int n, KeyOf key_of, uint64_t* cand,
   if (wave < runs && lane < KP) cand[wave * KP + lane] = top;
   __syncthreads();
   uint64_t res = 0ull;
+  if (wave != 0) after_keys();
   if (wave == 0) {
     const int total = runs * KP;
     for (int g = 0; g * kWave < total; ++g) {
@@ -675,9 +687,11 @@ __device__ inline uint64_t wait_tagged(const uint64_t* p, uint32_t tag, uint32_t
 struct Ctrl {
   uint32_t epoch;               // launches completed on this workspace
   uint32_t err;                 // sticky error bits (read and cleared by moe_layer_check)
-  uint32_t cs_epoch;            // channel-selection launches completed (their gate values
-                                // carry (cs_epoch + 1) & 1 in the lowest bit)
-  uint32_t pad0[61];
+  uint32_t cs_epoch;            // channel-selection launches completed (their channel
+                                // scores carry (cs_epoch + 1) & 1 in the lowest bit)
+  uint32_t cs_tprev;            // the last channel-selection launch's threshold score (fp32
+                                // bits; a prefetch hint only, never a result)
+  uint32_t pad0[60];
 };
 static_assert(sizeof(Ctrl) == 256, "one 256-byte block");
 

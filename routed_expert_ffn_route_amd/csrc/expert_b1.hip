@@ -131,16 +131,19 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   ss.s_w = s_w;
   const SlotShare share = slot_share(ss, c, L.R);
 
-  // 2. the routing (top-k of the published logits, or the given ids) in LDS.  While the
-  // waves that poll the logits wait, the other waves warm L2 with this workgroup's
-  // shared-expert rows, so the stream reads them from there and the memory's bandwidth goes
-  // to the routed rows.
+  // 2. the routing (top-k of the published logits, or the given ids) in LDS.  Once every logit
+  // has been read, waves 1.. warm L2 with this workgroup's shared-expert rows while wave 0
+  // finishes the top-k, so the stream reads those from there and the memory's bandwidth goes
+  // to the routed rows.  (Issued together with the logit polls, the 9 MB of warm loads of a
+  // layer queued ahead of them and stretched the router hand-off from 0.9 to 2.3 us.)
   uint32_t warm[kWarmLoads] = {0, 0};
-  if (!kTwo && a.route_inside)
-    warm_rows(ss.SG, ss.SV, ss.SD, share.s0, share.s1, (uint32_t)Fmt<ST>::row_bytes(a.H),
-              min(c.nthreads, (a.E + kWave - 1) / kWave * kWave), c, warm);
+  auto warm_shared = [&] {
+    if (!kTwo)
+      warm_rows(ss.SG, ss.SV, ss.SD, share.s0, share.s1, (uint32_t)Fmt<ST>::row_bytes(a.H),
+                kWave, c, warm);
+  };
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, a.k, ctrl,
-                reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c);
+                reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c, warm_shared);
   MOE_STAMP(c.stamps, 3);
 
   // 3. the slot stream: [shared slots,] routed slots; flat channel f, contiguous shares

@@ -49,6 +49,7 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_
                      hipStream_t s, int* occupancy = nullptr);
 int cs_lds_bytes(int H, int threads, int E, int k, int I, int workgroups, int K);
 constexpr int kCsMaxPerThread = 8;  // k*I <= 8 * threads
+constexpr int kCsOwnMax = 64;       // ceil(k*I / workgroups) <= 64 (own candidates)
 
 // Routing: router GEMV for B tokens, then one workgroup per token for top-k + softmax.
 struct RouteArgs {

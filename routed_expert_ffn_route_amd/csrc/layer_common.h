@@ -719,25 +719,31 @@ __device__ inline void router_finish(const RouterRound<RT, CPT>& rr, const void*
   __syncthreads();
   c.epoch = *s_ep;
   const uint64_t tag = (uint64_t)(c.epoch + 1u) << 32;
-  for (int m = c.tid; m < nrows; m += c.nthreads)
-    st_dev64(rlog + c.wg + (size_t)c.P * m, tag | __float_as_uint(buf[m]));
+  // one copy per XCD (E rounded up to whole 128-byte lines per copy)
+  const int Ep = (E + 15) & ~15;
+  for (int i = c.tid; i < nrows * kPollCopies; i += c.nthreads) {
+    const int m = i % nrows, x = i / nrows;
+    st_dev64(rlog + (size_t)x * Ep + c.wg + (size_t)c.P * m, tag | __float_as_uint(buf[m]));
+  }
 }
 
 // Exact top-k of the E logits and the softmax over the k selected, computed by the whole
 // workgroup into LDS (s_ids, s_w): the waves poll the tagged logits themselves and select in
 // registers (wg_topk_bitonic); wave 0 then forms the weights.  `keys` is LDS scratch of
 // topk_lds_bytes(E, k) bytes.
-template <int KP>
+template <int KP, typename AfterKeys>
 __device__ inline void topk_local_kp(const uint64_t* rlog, int E, int k, uint64_t* keys,
-                                     int* s_ids, float* s_w, uint32_t* err, const Ctx& c) {
+                                     int* s_ids, float* s_w, uint32_t* err, const Ctx& c,
+                                     AfterKeys after_keys) {
   const uint32_t tag = c.epoch + 1u;
+  const uint64_t* copy = rlog + (size_t)(c.wg % kPollCopies) * ((E + 15) & ~15);
   const uint64_t top = wg_topk_bitonic<KP>(
       E,
       [&](int e) {
-        const uint64_t v = wait_tagged(rlog + e, tag, err, kErrRouteWait);
+        const uint64_t v = wait_tagged(copy + e, tag, err, kErrRouteWait);
         return make_key(__uint_as_float((uint32_t)v), (uint32_t)e);
       },
-      keys, c.stamps);
+      keys, c.stamps, after_keys);
   MOE_STAMP(c.stamps, kStampRanked);
   if (c.tid < kWave) {
     // the largest selected logit (lane 0's key) for a max-subtracted softmax
@@ -751,15 +757,17 @@ __device__ inline void topk_local_kp(const uint64_t* rlog, int E, int k, uint64_
   }
   __syncthreads();
 }
+template <typename AfterKeys>
 __device__ inline void topk_local(const uint64_t* rlog, int E, int k, uint64_t* keys,
-                                  int* s_ids, float* s_w, uint32_t* err, const Ctx& c) {
-  if (k <= 1) topk_local_kp<1>(rlog, E, k, keys, s_ids, s_w, err, c);
-  else if (k <= 2) topk_local_kp<2>(rlog, E, k, keys, s_ids, s_w, err, c);
-  else if (k <= 4) topk_local_kp<4>(rlog, E, k, keys, s_ids, s_w, err, c);
-  else if (k <= 8) topk_local_kp<8>(rlog, E, k, keys, s_ids, s_w, err, c);
-  else if (k <= 16) topk_local_kp<16>(rlog, E, k, keys, s_ids, s_w, err, c);
-  else if (k <= 32) topk_local_kp<32>(rlog, E, k, keys, s_ids, s_w, err, c);
-  else topk_local_kp<64>(rlog, E, k, keys, s_ids, s_w, err, c);
+                                  int* s_ids, float* s_w, uint32_t* err, const Ctx& c,
+                                  AfterKeys after_keys) {
+  if (k <= 1) topk_local_kp<1>(rlog, E, k, keys, s_ids, s_w, err, c, after_keys);
+  else if (k <= 2) topk_local_kp<2>(rlog, E, k, keys, s_ids, s_w, err, c, after_keys);
+  else if (k <= 4) topk_local_kp<4>(rlog, E, k, keys, s_ids, s_w, err, c, after_keys);
+  else if (k <= 8) topk_local_kp<8>(rlog, E, k, keys, s_ids, s_w, err, c, after_keys);
+  else if (k <= 16) topk_local_kp<16>(rlog, E, k, keys, s_ids, s_w, err, c, after_keys);
+  else if (k <= 32) topk_local_kp<32>(rlog, E, k, keys, s_ids, s_w, err, c, after_keys);
+  else topk_local_kp<64>(rlog, E, k, keys, s_ids, s_w, err, c, after_keys);
 }
 
 // The routing of this token in LDS (s_ids, s_w).  Inside the launch: wait until every
@@ -769,12 +777,14 @@ __device__ inline void topk_local(const uint64_t* rlog, int E, int k, uint64_t* 
 // the token, is reported and skipped (-1), so a repeated expert counts once (its first
 // choice).  Workgroup 0 also stores the routing it used into ids_ws / w_ws [k], where the
 // host can read back what the launch chose.
+template <typename AfterKeys = NoHook>
 __device__ inline void fetch_routing(bool inside, const uint64_t* rlog, const int32_t* ids_in,
                                      const float* w_in, int E, int k, Ctrl* ctrl,
                                      uint64_t* keys, int* s_ids, float* s_w, int32_t* ids_ws,
-                                     float* w_ws, const Ctx& c) {
+                                     float* w_ws, const Ctx& c,
+                                     AfterKeys after_keys = AfterKeys()) {
   if (inside) {
-    topk_local(rlog, E, k, keys, s_ids, s_w, &ctrl->err, c);
+    topk_local(rlog, E, k, keys, s_ids, s_w, &ctrl->err, c, after_keys);
   } else {
     if (c.tid < k) {
       int e = ids_in[c.tid];

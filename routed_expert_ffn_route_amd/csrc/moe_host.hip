@@ -113,7 +113,7 @@ Layout layout_of(const moe_layer_desc* d, bool with_dnorm = true) {
   };
   const size_t B = (size_t)d->max_batch, E = (size_t)d->n_experts, k = (size_t)d->top_k;
   L.ctrl = take(sizeof(Ctrl));
-  L.rlog = take(E * 8);
+  L.rlog = take((size_t)kPollCopies * ((E + 15) & ~(size_t)15) * 8);  // a copy per XCD
   // zeros that empty slots of the batch-1 streams read in place of a weight row
   L.zrow = take((size_t)d->hidden * 4);
   L.logits = take(B * E * 4);
@@ -126,7 +126,9 @@ Layout layout_of(const moe_layer_desc* d, bool with_dnorm = true) {
   L.union_offsets = take((E + 1) * 4);
   L.union_slots = take(B * k * 4);
   const size_t kI = d->kind == MOE_EXPERT_SWIGLU ? k * (size_t)d->inter : 0;
-  L.cs_s = take(kI * 8);
+  // channel selection: the launch-tagged scores [k*I] (32-bit), one copy per XCD, each padded
+  // to 64 words
+  L.cs_s = take(kI ? (size_t)kPollCopies * ((kI + 63) / 64) * 64 * 4 : 0);
   L.cs_y = take(d->kind == MOE_EXPERT_SWIGLU ? (size_t)d->hidden * 4 : 0);
   const bool batched_swiglu = d->kind == MOE_EXPERT_SWIGLU && B > 1;
   const size_t xs =
@@ -710,9 +712,10 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
   if (moe_status e = b1_types(layer, &et, &st, &rt)) return e;
   if (et == DT::MXFP4) return fail(MOE_ERR_UNSUPPORTED, "channel selection for MXFP4 experts");
   if (d.hidden > 4096) return fail(MOE_ERR_UNSUPPORTED, "channel selection needs hidden <= 4096");
-  if (d.top_k > 64 || n > (long long)kCsMaxPerThread * layer->threads)
-    return fail(MOE_ERR_UNSUPPORTED, "channel selection needs k <= 64 and k*I <= %d",
-                kCsMaxPerThread * layer->threads);
+  if (d.top_k > 64 || n > (long long)kCsMaxPerThread * layer->threads ||
+      (n + layer->workgroups - 1) / layer->workgroups > kCsOwnMax)
+    return fail(MOE_ERR_UNSUPPORTED, "channel selection needs k <= 64, k*I <= %d and at most "
+                "%d candidates per workgroup", kCsMaxPerThread * layer->threads, kCsOwnMax);
   if (cs_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k, d.inter, layer->workgroups,
                    keep) > 160 * 1024)
     return fail(MOE_ERR_UNSUPPORTED, "k*I=%lld candidates exceed the selection LDS budget", n);
