@@ -165,29 +165,31 @@ def probe_lib():
 
 def stream_probe(gib: int = 4, reps: int = 5) -> float:
     """Achieved HBM read bandwidth (GB/s): a read-only stream over `gib` GiB (16 times the
-    256 MB MALL, so nothing is served from it) with non-temporal 16-byte loads, 4096
-    workgroups of 256 threads, timed over `reps` launches with HIP events on the launching
-    stream."""
+    256 MB MALL, so nothing is served from it) with non-temporal 16-byte loads (each wave's
+    load one contiguous KiB), timed over `reps` launches with HIP events on the launching
+    stream; the best of four grid sizes (1024 to 8192 workgroups of 256 threads)."""
     import torch
     L = probe_lib()
     nbytes = gib * 2**30
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
-    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
-    for _ in range(2):
-        assert L.probe_stream_read(buf.data_ptr(), nbytes, 4096, sink.data_ptr(), st) == 0
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
-        assert L.probe_stream_read(buf.data_ptr(), nbytes, 4096, sink.data_ptr(), st) == 0
-    end.record()
-    torch.cuda.synchronize()
-    gbs = nbytes * reps / (start.elapsed_time(end) / 1e3) / 1e9
+    best = 0.0
+    for blocks in (1024, 2048, 4096, 8192):
+        for _ in range(2):
+            assert L.probe_stream_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), st) == 0
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            assert L.probe_stream_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), st) == 0
+        end.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes * reps / (start.elapsed_time(end) / 1e3) / 1e9)
     del buf
     torch.cuda.empty_cache()
-    return gbs
+    return best
 
 
 def launch_floor(workgroups: int, threads: int, nodes: int = 40, reps: int = 50) -> float:
