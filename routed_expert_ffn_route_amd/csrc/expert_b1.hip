@@ -170,8 +170,11 @@ __global__ __launch_bounds__(1024) void b1_kernel(B1Launch L) {
   if constexpr (kTwo) MOE_STAMP_AFTER(c.stamps, 4, yr[0]);
   else MOE_STAMP_AFTER(c.stamps, 4, yv[0]);
   if constexpr (kTwo) {
-    add_teams_to_lds<ER, CPT>(yr, ysh, cr);
-    publish_and_reduce(a.partials, a.y, ctrl, L.R, L.SW, big, c, ysh);
+    // the routed teams' vectors to big (one H-vector each); the publish adds them to the
+    // shared output in ysh, in team order
+    teams_to_lds_split<ER, CPT>(yr, big, cr);
+    publish_and_reduce(a.partials, a.y, ctrl, L.R, L.SW, big, c, ysh, nullptr, 0, big,
+                       cr.nteams);
   } else {
     teams_to_lds<8, CPT>(yv, big, c);
     MOE_STAMP(c.stamps, 5);
@@ -234,13 +237,16 @@ static int team_threads(int nch) {
   return t;
 }
 
-static int b1_big_floats(int H, int threads, int E, int k) {
+static int b1_big_floats(int H, int threads, int E, int k, bool two_layouts) {
   const int nteams = threads / team_size(H);
   const int ybuf = nteams * H * 4;
   const int topk = topk_lds_bytes(E, k);
   const int reduce = threads * 8;  // the reducers' two floats per thread
+  // MXFP4: the routed layout's teams, one H-vector each (16 values per thread at most)
+  const int routed = two_layouts ? threads * 16 * 4 : 0;
   int big = ybuf > topk ? ybuf : topk;
   big = big > reduce ? big : reduce;
+  big = big > routed ? big : routed;
   return (big + 15) / 16 * 4;
 }
 
@@ -248,7 +254,7 @@ int b1_lds_bytes(int H, int threads, int E, int k, bool two_layouts) {
   const int red = 2 * (threads / kWave) * kMaxNP * 4;
   const int small = (16 + 64 + 64) * 4;
   const int ysh = two_layouts ? (threads / team_size(H)) * H * 4 : 0;
-  return red + small + b1_big_floats(H, threads, E, k) * 4 + ysh;
+  return red + small + b1_big_floats(H, threads, E, k, two_layouts) * 4 + ysh;
 }
 
 hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int wgs, int threads,
@@ -259,7 +265,7 @@ hipError_t launch_b1(const B1Args& a, DT et, DT st, DT rt, int wgs, int threads,
   L.tsz_r = L.tsz;
   reducer_split(a.H, wgs, &L.R, &L.SW);
   const int lds = b1_lds_bytes(a.H, threads, a.E, a.k, et == DT::MXFP4);
-  L.big_floats = b1_big_floats(a.H, threads, a.E, a.k);
+  L.big_floats = b1_big_floats(a.H, threads, a.E, a.k, et == DT::MXFP4);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)
     return launch_cpt<DT::F32, DT::F32, DT::F32>(L, wgs, threads, lds, s, occ);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::BF16)

@@ -834,26 +834,28 @@ __device__ inline void teams_to_lds(const float (&yv)[CPT * E], float* big, cons
   }
 }
 
-// Add a second layout's register vectors to big[0 .. H), one team after the other (a fixed
-// order).
+// Each team's register vector to its own H-vector of LDS, buf[team * H .. + H) (16-byte
+// stores, no read-modify-write: a team's lanes hold E consecutive values each, so E-float
+// read-modify-writes at that stride serialised on a few LDS banks, ~3 us per team at
+// H = 7168).  The sum over teams is taken by the reader, in team order.
 template <int E, int CPT>
-__device__ inline void add_teams_to_lds(const float (&yv)[CPT * E], float* big, const Ctx& c) {
-  for (int tm = 0; tm < c.nteams; ++tm) {
-    if (c.team == tm) {
+__device__ inline void teams_to_lds_split(const float (&yv)[CPT * E], float* buf, const Ctx& c) {
 #pragma unroll
-      for (int m = 0; m < CPT; ++m) {
-        const int ch = c.t + m * c.tsz;
-        if (ch < c.nch) {
+  for (int m = 0; m < CPT; ++m) {
+    const int ch = c.t + m * c.tsz;
+    if (ch < c.nch) {
 #pragma unroll
-          for (int i = 0; i < E; ++i) big[E * ch + i] += yv[m * E + i];
-        }
-      }
+      for (int q = 0; q < E / 4; ++q)
+        reinterpret_cast<f32x4*>(buf + c.team * c.H)[(E / 4) * ch + q] =
+            f32x4{yv[m * E + 4 * q], yv[m * E + 4 * q + 1], yv[m * E + 4 * q + 2],
+                  yv[m * E + 4 * q + 3]};
     }
-    __syncthreads();
   }
+  __syncthreads();
 }
 
-// Publish src[0 .. H) (default: big) as this workgroup's partial output row, then (R fixed
+// Publish src[0 .. H) (default: big), plus nadds more H-vectors at adds, as this workgroup's
+// partial output row, then (R fixed
 // workgroups, every (P/R)-th) sum an SW-column slice of y over all P partial rows in a
 // fixed order.  Deterministic: no float atomics, the same order in every launch.
 //
@@ -886,14 +888,21 @@ __device__ inline bool parity_ok(uint64_t v, uint32_t par) {
 }
 __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl, int R, int SW,
                                           float* big, const Ctx& c, const float* src = nullptr,
-                                          uint32_t* ctr2 = nullptr, uint32_t ctr2_next = 0) {
+                                          uint32_t* ctr2 = nullptr, uint32_t ctr2_next = 0,
+                                          const float* adds = nullptr, int nadds = 0) {
   const int H = c.H;
   if (!src) src = big;
   const uint32_t par = (c.epoch + 1u) & 1u;
   uint64_t* prow = reinterpret_cast<uint64_t*>(partials + (size_t)c.wg * H);
   for (int h2 = c.tid; h2 < H / 2; h2 += c.nthreads) {
-    const uint32_t lo = __float_as_uint(with_parity(src[2 * h2], par));
-    const uint32_t hi = __float_as_uint(with_parity(src[2 * h2 + 1], par));
+    // src plus the nadds H-vectors at adds (in order)
+    float a = src[2 * h2], b = src[2 * h2 + 1];
+    for (int t = 0; t < nadds; ++t) {
+      a += adds[t * H + 2 * h2];
+      b += adds[t * H + 2 * h2 + 1];
+    }
+    const uint32_t lo = __float_as_uint(with_parity(a, par));
+    const uint32_t hi = __float_as_uint(with_parity(b, par));
     st_dev64(prow + h2, ((uint64_t)hi << 32) | lo);
   }
   MOE_STAMP(c.stamps, kStampPublished);
@@ -916,11 +925,13 @@ __device__ inline void publish_and_reduce(float* partials, float* y, Ctrl* ctrl,
     for (int p0 = g; p0 < c.P; p0 += kBatch * G) {
       const uint64_t* src[kBatch];
       uint64_t v[kBatch];
+      // rows past P are not read: a word that passes the parity check and is not summed
+      const uint64_t none = (uint64_t)par | ((uint64_t)par << 32);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int p = min(p0 + u * G, c.P - 1);  // rows past P re-read the last (not summed)
+        const int p = min(p0 + u * G, c.P - 1);
         src[u] = reinterpret_cast<const uint64_t*>(partials + (size_t)p * H + h0) + q;
-        v[u] = ld_dev64(src[u]);
+        v[u] = p0 + u * G < c.P ? ld_dev64(src[u]) : none;
       }
       // the words not yet of this launch are polled again together, so the batch costs one
       // round trip after its last word lands (bounded like wait_tagged)
