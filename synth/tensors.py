@@ -58,6 +58,13 @@ def linear(wl: Workload, e: int):
                       wl.I, wl.H, wl.sigma_gate)
 
 
+def rotation_signs(wl: Workload, layer: int) -> np.ndarray:
+    """The random signs of a layer's block Hadamard rotation: H values in {-1, +1} (int8), the
+    sign of the generator's draw (a draw of exactly 0 counts as +1)."""
+    v = normal_f32(wl.seed, stream_id(wl.wwid, "signs", layer), 0, wl.H, 1.0)
+    return np.where(v < 0, -1, 1).astype(np.int8)
+
+
 def x(wl: Workload, token: int, layer: int = 0, attempt: int = 0, case: int = 0):
     return normal_f32(wl.seed, stream_id(wl.wid, "x", layer, x_sub(token, attempt, case)), 0,
                       wl.H, wl.sigma_x)
@@ -156,5 +163,6 @@ def reduced(wl: Workload, **changes) -> Workload:
     return dataclasses.replace(wl, **changes)
 
 
-__all__ = ["router", "expert", "shared", "linear", "x", "logits", "device_layer", "device_x",
+__all__ = ["router", "expert", "shared", "linear", "x", "logits", "rotation_signs",
+           "device_layer", "device_x",
            "device_logits", "reduced", "np"]

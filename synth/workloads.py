@@ -20,7 +20,7 @@ from dataclasses import dataclass, field
 KIND = {
     "router": 1, "gate": 2, "up": 3, "down_t": 4,
     "sh_gate": 5, "sh_up": 6, "sh_down_t": 7,
-    "x": 8, "logits": 9, "linear": 10,
+    "x": 8, "logits": 9, "linear": 10, "signs": 11,
 }
 
 
