@@ -152,6 +152,39 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
                               const float* w, int32_t keep, int32_t mode, int32_t* kept,
                               float* y, void* stream);
 
+/* The ternary-sketch channel screen (the review of arXiv:2610.37386, "The weights-only
+ * reader", stages 1 and 2).  Load time, once: every routed channel's gate row and up row is
+ * rotated in blocks of 128 coordinates by a randomized Hadamard transform (unnormalized:
+ * u = H_128 (s * w) per block, s the layer's random signs, H_128 the Sylvester-ordered
+ * Walsh-Hadamard matrix; g.x = sum over blocks of u.z / 128 with z = H_128 (s * x)), and each
+ * rotated block is stored as ternary codes {-1, 0, 1} (threshold 0.7 mean|u|, the codes' sign),
+ * an FP16 scale (the mean |u| over the nonzero codes) and rho, the block's mean squared
+ * quantization error (FP16).  Per token: x is rotated once, only the 80 coordinates of largest
+ * |z| of each block are scanned (ties to the lower coordinate), the estimates g^, v^ give the
+ * eq.-1 score w_e ||d_j|| |silu(g^) v^| (mode MOE_SCORE_GATE_DNORM drops w_e), the `keep` best
+ * of the k*I candidates (ties to the lower e*I + j) are computed exactly from their full gate,
+ * up and down rows, and the rest are not read.
+ *
+ * moe_sketch_bytes: bytes of the sketch of a layer with this descriptor (0 if it has none:
+ * SWIGLU experts in BF16 or F32, hidden a multiple of 128 and at most 4096).  Host only.
+ * Layout of the buffer: 2-bit codes of G then V [E*I][H/16] uint32 (coordinate c of a row at
+ * bits 2 (c % 16) of word c / 16: 0 -> 00, +1 -> 01, -1 -> 11), then FP16 scales of G, of V,
+ * rho of G, of V [E*I][H/128], each region 256-byte aligned. */
+size_t moe_sketch_bytes(const moe_layer_desc* desc);
+
+/* Build the sketch of the layer's routed gate and up rows into the caller's device buffer
+ * `sketch` (256-byte aligned, at least moe_sketch_bytes) from the rotation signs `signs` [H]
+ * (int8 device memory, +1 or -1), and bind both to the layer (they must outlive it).
+ * Enqueues on `stream`. */
+moe_status moe_layer_build_sketch(moe_layer layer, const int8_t* signs, void* sketch,
+                                  size_t sketch_bytes, void* stream);
+
+/* moe_channel_select with the sketch screen in place of the exact gate pass: the same
+ * arguments and outputs (kept [keep]: ascending ids e*I + j); needs moe_layer_build_sketch. */
+moe_status moe_channel_select_sketch(moe_layer layer, const float* x, const int32_t* ids,
+                                     const float* w, int32_t keep, int32_t mode, int32_t* kept,
+                                     float* y, void* stream);
+
 /* Touched-expert union of a batch (the "experts touched by a batch" count of the
  * 501B/23B post, section 2).  ids [B][k] with distinct experts per token, 0 <= id < E.
  * Writes n_touched [1], touched [E] (ascending; first n_touched valid), offsets [E+1]

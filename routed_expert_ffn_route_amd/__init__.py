@@ -26,7 +26,8 @@ DTYPES = {None: DTYPE_NONE, "f32": F32, "bf16": BF16, "mxfp4": MXFP4}
 EXPORTS = (
     "moe_layer_workspace_bytes", "moe_layer_create", "moe_layer_destroy", "moe_route",
     "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_channel_select", "moe_union_experts",
-    "moe_layer_routing",
+    "moe_layer_routing", "moe_sketch_bytes", "moe_layer_build_sketch",
+    "moe_channel_select_sketch",
     "moe_layer_check", "moe_layer_geometry", "moe_status_string", "moe_last_error",
 )
 # The phase-timeline build (libmoe_ffn_timeline.so) exports one more, for measurement only.
@@ -96,6 +97,12 @@ def lib():
         L.moe_union_experts.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.moe_layer_routing.restype = i32
         L.moe_layer_routing.argtypes = [vp, i32, vp, vp, vp]
+        L.moe_sketch_bytes.restype = sz
+        L.moe_sketch_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
+        L.moe_layer_build_sketch.restype = i32
+        L.moe_layer_build_sketch.argtypes = [vp, vp, vp, sz, vp]
+        L.moe_channel_select_sketch.restype = i32
+        L.moe_channel_select_sketch.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp]
         L.moe_layer_check.restype = i32
         L.moe_layer_check.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.moe_layer_geometry.restype = i32
@@ -231,8 +238,26 @@ class Layer:
         _check(lib().moe_ffn_forward(self.handle, _ptr(x), B, _ptr(ids), _ptr(w), _ptr(y),
                                      _stream(stream)))
 
+    def build_sketch(self, signs, stream=None):
+        """moe_layer_build_sketch: allocate the sketch buffer (torch) and build it from the
+        rotation signs (int8 [H] on the device); both are kept alive by the handle."""
+        import torch
+        d = self.desc
+        _need(signs, "signs", torch.int8, min_numel=d.hidden)
+        n = lib().moe_sketch_bytes(ctypes.byref(d))
+        if n == 0:
+            raise MoeError(MOE_ERR_UNSUPPORTED, "this layer has no sketch form")
+        buf = torch.empty(n + 256, dtype=torch.uint8, device=signs.device)
+        off = (-buf.data_ptr()) % 256
+        self._sketch = (buf, signs, off)
+        _check(lib().moe_layer_build_sketch(self.handle, _ptr(signs),
+                                            ctypes.c_void_p(buf.data_ptr() + off), n,
+                                            _stream(stream)))
+        return buf[off:off + n]
+
     def channel_select(self, x, keep, kept, y=None, ids=None, w=None,
-                       mode=SCORE_GATE_DNORM, stream=None):
+                       mode=SCORE_GATE_DNORM, stream=None, sketch=False):
+        """moe_channel_select, or with sketch=True moe_channel_select_sketch."""
         import torch
         d = self.desc
         _need(x, "x", torch.float32, min_numel=d.hidden)
@@ -244,8 +269,9 @@ class Layer:
             _need(ids, "ids", torch.int32, min_numel=d.top_k)
         if w is not None:
             _need(w, "w", torch.float32, min_numel=d.top_k)
-        _check(lib().moe_channel_select(self.handle, _ptr(x), _ptr(ids), _ptr(w), keep, mode,
-                                        _ptr(kept), _ptr(y), _stream(stream)))
+        fn = lib().moe_channel_select_sketch if sketch else lib().moe_channel_select
+        _check(fn(self.handle, _ptr(x), _ptr(ids), _ptr(w), keep, mode, _ptr(kept), _ptr(y),
+                  _stream(stream)))
 
     def routing(self, ids, w, B=1, stream=None):
         """Copy the routing the last call used into ids, w [B][k] (moe_layer_routing)."""

@@ -14,7 +14,8 @@ LIB = os.path.join(HERE, "libmoe_ffn.so")
 LIB_TIMELINE = os.path.join(HERE, "libmoe_ffn_timeline.so")
 LIB_PROBE = os.path.join(HERE, "libmoe_probe.so")  # the benchmark's measurement kernels
 SOURCES = ["moe_host.hip", "expert_b1.hip", "channel_sparse.hip", "route.hip",
-           "batched_swiglu.hip", "linear_mfma.hip", "linear_gemv.hip", "grouped_tn.hip"]
+           "batched_swiglu.hip", "linear_mfma.hip", "linear_gemv.hip", "grouped_tn.hip",
+           "sketch.hip"]
 
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

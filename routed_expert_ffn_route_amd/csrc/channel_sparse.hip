@@ -26,6 +26,8 @@
 //     scan over all candidates in that order), with g from LDS;
 //  6. the deterministic cross-workgroup sum of the partial outputs; after its partial is out,
 //     workgroup 0 writes the kept list in ascending e*I + j and the threshold hint.
+#include <hip/hip_fp16.h>
+
 #include "layer_common.h"
 
 namespace moe {
@@ -44,6 +46,11 @@ constexpr int kSlotPad = kMaxSlots + 4;  // slot tables of kMaxSlots + 1 ints, p
 struct CSLaunch {
   B1Args a;
   const float* dnorm;  // [E*I]
+  // ternary sketch (null: exact gate values): codes [E*I][H/16] and FP16 scales [E*I][H/128]
+  // of the gate and up rows, and the rotation's signs [H]
+  const uint32_t *sk_g, *sk_v;
+  const uint16_t *sk_ag, *sk_av;
+  const int8_t* signs;
   uint64_t* g_ws;      // channel scores with the launch parity, one copy per XCD
   int32_t* kept_out;   // [K]
   int K, mode, R, SW, tsz;
@@ -349,7 +356,92 @@ __device__ inline uint32_t kept_in_order(const uint32_t (&sb)[kCh], bool mine, i
   return mask;
 }
 
-template <DT ET, DT ST, DT RT, int C, int CPT>
+// The token side of the sketch screen: z = H_128 (s * x) per 128-block (fp32 butterflies,
+// stages h = 1 .. 64, (a, b) -> (a + b, a - b)), and per block only the 80 coordinates of
+// largest |z| kept (ties to the lower coordinate), the others zeroed, into zs [H] (LDS).  One
+// wave per block: lane l holds coordinates l and l + 64; the 80th largest |z| is found bit by
+// bit from the top with ballot counts, the ties at it in coordinate order with lane counts.
+constexpr int kScan = 80;
+__device__ inline void rotate_scan(const float* x, const int8_t* signs, float* zs, int H,
+                                   const Ctx& c) {
+#pragma clang fp contract(off)
+  const int nb = H / 128, wave = c.tid / kWave, nw = c.nthreads / kWave, lane = c.lane;
+  for (int b = wave; b < nb; b += nw) {
+    float lo = x[b * 128 + lane] * (float)signs[b * 128 + lane];
+    float hi = x[b * 128 + lane + 64] * (float)signs[b * 128 + lane + 64];
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+      const float plo = __shfl_xor(lo, h, kWave), phi = __shfl_xor(hi, h, kWave);
+      const bool upper = (lane & h) != 0;
+      lo = upper ? plo - lo : lo + plo;
+      hi = upper ? phi - hi : hi + phi;
+    }
+    const float z0 = lo + hi, z1 = lo - hi;
+    const uint32_t a0 = __float_as_uint(z0) & 0x7FFFFFFFu, a1 = __float_as_uint(z1) & 0x7FFFFFFFu;
+    uint32_t t = 0;  // the largest pattern with at least kScan values at or above it
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      const int cnt = __popcll(__ballot(a0 >= cand)) + __popcll(__ballot(a1 >= cand));
+      t = cnt >= kScan ? cand : t;
+    }
+    const int need = kScan - (__popcll(__ballot(a0 > t)) + __popcll(__ballot(a1 > t)));
+    const uint64_t e0 = __ballot(a0 == t), e1 = __ballot(a1 == t);
+    const int r0 = __builtin_amdgcn_mbcnt_hi((uint32_t)(e0 >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)e0, 0));
+    const int r1 = __popcll(e0) + __builtin_amdgcn_mbcnt_hi(
+                                      (uint32_t)(e1 >> 32),
+                                      __builtin_amdgcn_mbcnt_lo((uint32_t)e1, 0));
+    const bool k0 = a0 > t || (a0 == t && r0 < need);
+    const bool k1 = a1 > t || (a1 == t && r1 < need);
+    zs[b * 128 + lane] = k0 ? z0 : 0.0f;
+    zs[b * 128 + lane + 64] = k1 ? z1 : 0.0f;
+  }
+}
+
+// Sketch estimate of one row for this lane's share: coordinates [32q, 32q + 32) for q = lane,
+// lane + 64 (H <= 4096): the 2-bit codes (two words per q) times zs, times the block's scale.
+struct SketchPiece {
+  uint32_t w[2][2];
+  uint16_t a[2];
+};
+__device__ __forceinline__ void sketch_load(const uint32_t* codes, const uint16_t* alpha,
+                                            int H, int lane, SketchPiece& p) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = lane + kWave * h;
+    const bool ok = codes != nullptr && q < H / 32;
+    p.w[h][0] = ok ? codes[2 * q] : 0u;
+    p.w[h][1] = ok ? codes[2 * q + 1] : 0u;
+    p.a[h] = ok ? alpha[q >> 2] : (uint16_t)0;
+  }
+}
+__device__ __forceinline__ float sketch_dot(const SketchPiece& p, const float* zs, int H,
+                                            int lane) {
+  float part = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = lane + kWave * h;
+    if (q < H / 32) {
+      const f32x4* zp = reinterpret_cast<const f32x4*>(zs + 32 * q);
+      float acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const f32x4 z = zp[u];
+        const uint32_t w = p.w[h][u >> 2];
+        const int sh = 8 * (u & 3);  // codes of coordinates 4u .. 4u + 3 of this q
+        // a 2-bit field sign-extended: 00 -> 0, 01 -> +1, 11 -> -1
+        acc = fmaf((float)((int)(w << (30 - sh)) >> 30), z.x, acc);
+        acc = fmaf((float)((int)(w << (28 - sh)) >> 30), z.y, acc);
+        acc = fmaf((float)((int)(w << (26 - sh)) >> 30), z.z, acc);
+        acc = fmaf((float)((int)(w << (24 - sh)) >> 30), z.w, acc);
+      }
+      part = fmaf(__half2float(__ushort_as_half(p.a[h])), acc, part);
+    }
+  }
+  return part;
+}
+
+template <DT ET, DT ST, DT RT, int C, int CPT, bool SK>
 __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   const B1Args& a = L.a;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -385,8 +477,10 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   float* own_dn = reinterpret_cast<float*>(own_s + kOwnMax);        // [kOwnMax] ||d_j||
   int* own_keep = reinterpret_cast<int*>(own_dn + kOwnMax);         // [kOwnMax] kept flags
   int* klist = own_keep + kOwnMax;                                  // [kOwnMax] kept, in order
-  uint32_t* sv = reinterpret_cast<uint32_t*>(klist + kOwnMax);      // [n] score patterns
-  float* big = reinterpret_cast<float*>(sv + ((n + 3) & ~3));
+  float* est = reinterpret_cast<float*>(klist + kOwnMax);           // [2 kOwnMax] sketch
+  uint32_t* sv = reinterpret_cast<uint32_t*>(est + 2 * kOwnMax);    // [n] score patterns
+  float* zs = reinterpret_cast<float*>(sv + ((n + 3) & ~3));        // [H] scanned R x
+  float* big = zs + a.H;
   Ctrl* ctrl = a.ctrl;
   // channel-selection launches on this workspace so far: its scores carry the parity
   const uint32_t cs_ep = load_relaxed_dev(&ctrl->cs_epoch);
@@ -466,7 +560,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
       }
     }
   };
-  {
+  if constexpr (!SK) {
     TeamRows<ET, kGateBatch, CPT> gr;
     long long rows[kGateBatch];
     gate_rows(g0, rows);
@@ -479,6 +573,57 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
       gate_rows(base, rows);
       team_dots<ET, kGateBatch, CPT>(a.gate, a.gate_s, rows, xv, c, g);
       publish(base, g);
+    }
+  } else {
+    // the sketch screen (stage 1 of the reader): the own candidates' sketch rows of G and V
+    // (one wave per row, up to four rows per wave in flight) are loaded first; x is rotated
+    // and scanned meanwhile; each estimate is sum_b alpha_b sum_(scanned i) code_i z_i / 128;
+    // the score is eq. 1, w_e ||d_j|| |silu(g^) v^| (without w_e in the gate-dnorm mode)
+    const int nw = c.nthreads / kWave, wave = c.tid / kWave, ntask = 2 * nown;
+    for (int t0 = 0; t0 < ntask; t0 += 4 * nw) {
+      SketchPiece pc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int task = t0 + wave + nw * u;
+        const uint32_t* cw = nullptr;
+        const uint16_t* al = nullptr;
+        if (task < ntask) {
+          const int f = g0 + (task >> 1), sl = divI.div(f), e = s_ids[sl];
+          if (e >= 0) {
+            const size_t row = (size_t)e * I + (f - sl * I);
+            cw = ((task & 1) ? L.sk_v : L.sk_g) + row * (size_t)(a.H / 16);
+            al = ((task & 1) ? L.sk_av : L.sk_ag) + row * (size_t)(a.H / 128);
+          }
+        }
+        sketch_load(cw, al, a.H, c.lane, pc[u]);
+      }
+      if (t0 == 0) {
+        if (c.tid < nown) own_dn[c.tid] = dnv;
+        rotate_scan(a.x, L.signs, zs, a.H, c);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int task = t0 + wave + nw * u;
+        const float v = wave_sum(sketch_dot(pc[u], zs, a.H, c.lane)) * (1.0f / 128.0f);
+        if (task < ntask && c.lane == 0) est[task] = v;
+      }
+    }
+    if (ntask == 0) {
+      rotate_scan(a.x, L.signs, zs, a.H, c);  // (keeps the barrier count uniform)
+      __syncthreads();
+    }
+    __syncthreads();
+    if (c.tid < nown) {
+      const int f = g0 + c.tid;
+      const float wsl = L.mode == 1 ? s_w[divI.div(f)] : 1.0f;
+      const float gh = est[2 * c.tid], vh = est[2 * c.tid + 1];
+      const uint32_t sp = __float_as_uint(fabsf(silu(gh) * vh) * own_dn[c.tid] * wsl) & ~1u;
+#pragma unroll
+      for (int x = 0; x < kPollCopies; ++x)
+        __hip_atomic_store(scores + (size_t)x * npad + f, sp | gpar, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      own_s[c.tid] = sp;
     }
   }
   __syncthreads();
@@ -495,6 +640,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   auto warm_kept = [&] {
     if (t_prev > 0.0f && L.K > 0 && L.K < n) {
       const uint32_t rb = (uint32_t)Fmt<ET>::row_bytes(a.H), lines = (rb + 127) / 128;
+      const uint32_t nrow = SK ? 3u : 2u;  // (gate,) up and down rows
       const int nw = c.nthreads / kWave;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -503,14 +649,17 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
           const int f = g0 + o, sl = divI.div(f), e = s_ids[sl];
           if (e >= 0) {
             const size_t row = (size_t)e * I + (f - sl * I);
-            const uint8_t* vr = reinterpret_cast<const uint8_t*>(a.up) + row * rb;
-            const uint8_t* dr = reinterpret_cast<const uint8_t*>(a.down_t) + row * rb;
+            const uint8_t* base[3] = {reinterpret_cast<const uint8_t*>(a.up) + row * rb,
+                                      reinterpret_cast<const uint8_t*>(a.down_t) + row * rb,
+                                      reinterpret_cast<const uint8_t*>(a.gate) + row * rb};
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const uint32_t l = c.lane + kWave * h;
-              if (l < 2 * lines) {
-                const uint8_t* p = l < lines ? vr + 128ull * l : dr + 128ull * (l - lines);
-                warm2[u][h] = *reinterpret_cast<const uint32_t*>(p);
+              if (l < nrow * lines) {
+                const uint32_t which = l / lines;
+                warm2[u][h] = *reinterpret_cast<const uint32_t*>(
+                    (which == 0 ? base[0] : which == 1 ? base[1] : base[2]) +
+                    128ull * (l - which * lines));
               }
             }
           }
@@ -634,8 +783,9 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   MOE_STAMP(c.stamps, 23);
 
   // 7. the own kept channels: up row and down row only, g from LDS
-  stream_channels<ET, C, CPT, false, false>(
-      nullptr, a.up, a.down_t, nullptr, a.up_s, a.down_s, 0, nkept,
+  stream_channels<ET, C, CPT, SK, false>(
+      SK ? a.gate : nullptr, a.up, a.down_t, SK ? a.gate_s : nullptr, a.up_s, a.down_s, 0,
+      nkept,
       [=](int i, long long& row, float& wt, float& gvv) {
         // i is wave-uniform, so are the candidate, its slot and expert: scalar arithmetic
         const int o = __builtin_amdgcn_readfirstlane(klist[i]);
@@ -677,10 +827,10 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
                     warm2[1][1]);  // keeps the warming loads
 }
 
-template <DT ET, DT ST, DT RT, int C, int CPT>
+template <DT ET, DT ST, DT RT, int C, int CPT, bool SK>
 hipError_t launch_t(const CSLaunch& L, int wgs, int threads, int lds, hipStream_t s,
                     int* occ) {
-  auto fn = cs_kernel<ET, ST, RT, C, CPT>;
+  auto fn = cs_kernel<ET, ST, RT, C, CPT, SK>;
   static bool lds_set = false;
   if (!lds_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -699,9 +849,10 @@ template <DT ET, DT ST, DT RT>
 hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStream_t s,
                       int* occ) {
   const int cpt = (L.a.H / 8 + L.tsz - 1) / L.tsz;
-  if (cpt <= 1 && ET != DT::F32) return launch_t<ET, ST, RT, 2, 1>(L, wgs, threads, lds, s, occ);
-  if (cpt <= 1) return launch_t<ET, ST, RT, 1, 1>(L, wgs, threads, lds, s, occ);
-  return hipErrorInvalidValue;
+  if (cpt > 1) return hipErrorInvalidValue;
+  constexpr int C = ET != DT::F32 ? 2 : 1;
+  if (L.sk_g) return launch_t<ET, ST, RT, C, 1, true>(L, wgs, threads, lds, s, occ);
+  return launch_t<ET, ST, RT, C, 1, false>(L, wgs, threads, lds, s, occ);
 }
 
 }  // namespace
@@ -714,8 +865,8 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K) {
   const int nteams = threads / team_size(H);
   const int n = k * I;
   const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + 96) * 4 +
-                    2 * kSlotPad * 4 + kSelBins * 4 + kSelCand * 4 + 5 * kOwnMax * 4 +
-                    ((n + 3) & ~3) * 4;
+                    2 * kSlotPad * 4 + kSelBins * 4 + kSelCand * 4 + 7 * kOwnMax * 4 +
+                    ((n + 3) & ~3) * 4 + H * 4;
   const int ybuf = nteams * H * 4;
   const int topk = topk_lds_bytes(E, k);
   const int router = ((E + wgs - 1) / wgs) * 4;
@@ -727,7 +878,7 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K) {
 
 hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_t* kept, int K,
                      int mode, DT et, DT st, DT rt, int wgs, int threads, hipStream_t s,
-                     int* occ) {
+                     int* occ, const CsSketch* sketch) {
   // the selection's bin scan holds at most four bins per thread
   const long long n = (long long)a.k * a.I;
   if (a.k > kMaxSlots || n > (long long)kCh * threads || a.I % kCh != 0 ||
@@ -741,6 +892,19 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_
   L.K = K;
   L.mode = mode;
   L.tsz = team_size(a.H);
+  L.sk_g = L.sk_v = nullptr;
+  L.sk_ag = L.sk_av = nullptr;
+  L.signs = nullptr;
+  if (sketch) {
+    if (a.H % 128 != 0 || a.H > 4096 || !sketch->g || !sketch->v || !sketch->ag ||
+        !sketch->av || !sketch->signs)
+      return hipErrorInvalidValue;
+    L.sk_g = sketch->g;
+    L.sk_v = sketch->v;
+    L.sk_ag = sketch->ag;
+    L.sk_av = sketch->av;
+    L.signs = sketch->signs;
+  }
   lc::reducer_split(a.H, wgs, &L.R, &L.SW);
   const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I, wgs, K);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)

@@ -44,9 +44,22 @@ int team_size(int H);
 // Channel-sparse batch-1 layer (fixed-count top-K keep rule over the k*I candidates).
 // kept [K] receives the kept channels as ascending ids e*I + j (-1 for a channel of a
 // skipped given id); g_ws [k*I] (32-bit words) holds the gate values with the launch parity.
+// sketch != null: the candidates are scored from the ternary sketch of their gate and up
+// rows (eq. 1 with the estimates) instead of their exact gate values, and kept channels
+// read their gate row too.
+struct CsSketch {
+  const uint32_t *g, *v;    // 2-bit codes [E*I][H/16]
+  const uint16_t *ag, *av;  // FP16 scales [E*I][H/128]
+  const int8_t* signs;      // rotation signs [H]
+};
 hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_t* kept,
                      int K, int mode, DT et, DT st, DT rt, int workgroups, int threads,
-                     hipStream_t s, int* occupancy = nullptr);
+                     hipStream_t s, int* occupancy = nullptr, const CsSketch* sketch = nullptr);
+// Ternary sketch of nrows rows of H (H % 128 == 0, BF16 or F32): codes [nrows][H/16],
+// alpha and rho [nrows][H/128] (FP16 bits), with the rotation signs [H].
+hipError_t launch_sketch_build(const void* rows, DT dt, size_t nrows, int H,
+                               const int8_t* signs, uint32_t* codes, uint16_t* alpha,
+                               uint16_t* rho, hipStream_t s);
 int cs_lds_bytes(int H, int threads, int E, int k, int I, int workgroups, int K);
 constexpr int kCsMaxPerThread = 8;  // k*I <= 8 * threads
 constexpr int kCsOwnMax = 64;       // ceil(k*I / workgroups) <= 64 (own candidates)

@@ -168,6 +168,7 @@ struct moe_layer_s {
   int workgroups;
   int threads;
   uint32_t magic;
+  CsSketch sketch{};  // bound by moe_layer_build_sketch (all null until then)
   template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
   Ctrl* ctrl() const { return at<Ctrl>(L.ctrl); }
 };
@@ -691,10 +692,9 @@ moe_status moe_ffn_forward_noalloc(const moe_layer_desc* desc, const moe_weights
   return forward_impl(&l, x, B, ids, w, y, stream);
 }
 
-moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* ids,
-                              const float* w, int32_t keep, int32_t mode, int32_t* kept,
-                              float* y, void* stream) {
-  if (moe_status st = check_layer(layer)) return st;
+static moe_status channel_select_impl(moe_layer layer, const float* x, const int32_t* ids,
+                                      const float* w, int32_t keep, int32_t mode, int32_t* kept,
+                                      float* y, void* stream, const CsSketch* sketch) {
   const moe_layer_desc& d = layer->d;
   if (d.kind != MOE_EXPERT_SWIGLU) return fail(MOE_ERR_ARG, "channel selection needs SWIGLU experts");
   if (!x || !aligned16(x)) return fail(MOE_ERR_ARG, "x must be given and 16-byte aligned");
@@ -722,9 +722,94 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
   B1Args a = b1_args(layer, x, ids, w, y ? y : layer->at<float>(layer->L.cs_y));
   hipError_t e = launch_cs(a, layer->at<float>(layer->L.dnorm),
                            layer->at<uint64_t>(layer->L.cs_s), kept, keep, mode, et, st, rt,
-                           layer->workgroups, layer->threads, reinterpret_cast<hipStream_t>(stream));
+                           layer->workgroups, layer->threads, reinterpret_cast<hipStream_t>(stream),
+                           nullptr, sketch);
   if (e != hipSuccess) return device_fail(e, "channel-sparse layer launch");
   return ok();
+}
+
+moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* ids,
+                              const float* w, int32_t keep, int32_t mode, int32_t* kept,
+                              float* y, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  return channel_select_impl(layer, x, ids, w, keep, mode, kept, y, stream, nullptr);
+}
+
+// Sketch buffer layout: codes of G then V [E*I][H/16] uint32, then alpha of G, alpha of V,
+// rho of G, rho of V [E*I][H/128] FP16; each region 256-byte aligned.
+struct SketchLayout {
+  size_t cg, cv, ag, av, rg, rv, total;
+};
+static bool sketch_layout(const moe_layer_desc* d, SketchLayout* S) {
+  if (!desc_valid(d, nullptr) || d->kind != MOE_EXPERT_SWIGLU || d->expert_dtype == MOE_MXFP4 ||
+      d->hidden % 128 != 0 || d->hidden > 4096)
+    return false;
+  const size_t rows = (size_t)d->n_experts * d->inter;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  S->cg = take(rows * (d->hidden / 16) * 4);
+  S->cv = take(rows * (d->hidden / 16) * 4);
+  S->ag = take(rows * (d->hidden / 128) * 2);
+  S->av = take(rows * (d->hidden / 128) * 2);
+  S->rg = take(rows * (d->hidden / 128) * 2);
+  S->rv = take(rows * (d->hidden / 128) * 2);
+  S->total = o;
+  return true;
+}
+
+size_t moe_sketch_bytes(const moe_layer_desc* desc) {
+  SketchLayout S;
+  return sketch_layout(desc, &S) ? S.total : 0;
+}
+
+moe_status moe_layer_build_sketch(moe_layer layer, const int8_t* signs, void* sketch,
+                                  size_t sketch_bytes, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const moe_layer_desc& d = layer->d;
+  SketchLayout S;
+  if (!sketch_layout(&d, &S))
+    return fail(MOE_ERR_UNSUPPORTED, "the sketch needs SWIGLU experts in BF16 or F32 and hidden "
+                "a multiple of 128, at most 4096");
+  if (!signs || !sketch) return fail(MOE_ERR_ARG, "signs and sketch must be given");
+  if (((uintptr_t)sketch % kAlign) != 0)
+    return fail(MOE_ERR_WORKSPACE, "the sketch buffer must be 256-byte aligned");
+  if (sketch_bytes < S.total)
+    return fail(MOE_ERR_WORKSPACE, "sketch buffer has %zu bytes, needs %zu", sketch_bytes, S.total);
+  unsigned char* base = reinterpret_cast<unsigned char*>(sketch);
+  CsSketch sk;
+  sk.g = reinterpret_cast<const uint32_t*>(base + S.cg);
+  sk.v = reinterpret_cast<const uint32_t*>(base + S.cv);
+  sk.ag = reinterpret_cast<const uint16_t*>(base + S.ag);
+  sk.av = reinterpret_cast<const uint16_t*>(base + S.av);
+  sk.signs = signs;
+  const size_t rows = (size_t)d.n_experts * d.inter;
+  const DT et = to_dt(d.expert_dtype);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_sketch_build(layer->w.gate, et, rows, d.hidden, signs,
+                                     reinterpret_cast<uint32_t*>(base + S.cg),
+                                     reinterpret_cast<uint16_t*>(base + S.ag),
+                                     reinterpret_cast<uint16_t*>(base + S.rg), s);
+  if (e == hipSuccess)
+    e = launch_sketch_build(layer->w.up, et, rows, d.hidden, signs,
+                            reinterpret_cast<uint32_t*>(base + S.cv),
+                            reinterpret_cast<uint16_t*>(base + S.av),
+                            reinterpret_cast<uint16_t*>(base + S.rv), s);
+  if (e != hipSuccess) return device_fail(e, "sketch construction");
+  layer->sketch = sk;
+  return ok();
+}
+
+moe_status moe_channel_select_sketch(moe_layer layer, const float* x, const int32_t* ids,
+                                     const float* w, int32_t keep, int32_t mode, int32_t* kept,
+                                     float* y, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  if (!layer->sketch.g)
+    return fail(MOE_ERR_ARG, "no sketch: call moe_layer_build_sketch first");
+  return channel_select_impl(layer, x, ids, w, keep, mode, kept, y, stream, &layer->sketch);
 }
 
 moe_status moe_union_experts(const int32_t* ids, int32_t B, int32_t k, int32_t E,
