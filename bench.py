@@ -46,7 +46,7 @@ def kernel_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def layer_weight_bytes(wl, keep=None, n_read=None) -> float:
+def layer_weight_bytes(wl, keep=None, n_read=None, sketch=False) -> float:
     """Algorithmic weight bytes one token (or one batch step) reads in one layer: the router,
     the routed experts (k of them; n_read for a batch: the touched ones) and the shared
     experts, 3 matrices of H x I each (linear experts: one matrix, no router).  With a keep
@@ -60,6 +60,11 @@ def layer_weight_bytes(wl, keep=None, n_read=None) -> float:
         return n * wl.H * wl.I * be
     if keep is None:
         routed = n * 3 * wl.H * wl.I * be
+    elif sketch:
+        # the sketch of every candidate's gate and up rows (2-bit codes + an FP16 scale per
+        # 128-block), then the kept channels' full gate, up and down rows, and the norms
+        routed = (wl.k * wl.I * 2 * (wl.H // 128) * (32 + 2) + 3 * keep * wl.H * be +
+                  4 * wl.k * wl.I)
     else:
         routed = wl.k * wl.I * wl.H * be + 2 * keep * wl.H * be + 4 * wl.k * wl.I
     return routed + wl.n_shared * 3 * wl.H * wl.I_shared * bs + wl.E * wl.H * br
@@ -255,7 +260,8 @@ def timed(fn, steps, graph_ok=True):
 
 
 def run_stack(args, wl, keep=None):
-    """Batch-1 decode through a stack of layers (dense or channel-sparse)."""
+    """Batch-1 decode through a stack of layers (dense, channel-sparse, or channel-sparse with
+    the ternary-sketch screen)."""
     import numpy as np
     import torch
     import routed_expert_ffn_route_amd as M
@@ -272,6 +278,8 @@ def run_stack(args, wl, keep=None):
         ys.append(torch.empty_like(xs[-1]))
         if keep is not None:
             kepts.append(torch.empty((ntok, max(keep, 1)), dtype=torch.int32, device="cuda"))
+        if args.sketch:
+            layers[-1].build_sketch(torch.from_numpy(T.rotation_signs(wl, l)).cuda())
     torch.cuda.synchronize()
     print(f"# {wl.name}: generated {wl.layers} layers in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
@@ -283,7 +291,8 @@ def run_stack(args, wl, keep=None):
                 layers[l].forward(xs[l][tt:tt + 1], ys[l][tt:tt + 1], B=1)
             else:
                 layers[l].channel_select(xs[l][tt:tt + 1], keep, kepts[l][tt],
-                                         y=ys[l][tt:tt + 1])
+                                         y=ys[l][tt:tt + 1], sketch=args.sketch,
+                                         mode=1 if args.sketch else 0)
 
     for t in range(args.warmup):
         step(t)
@@ -296,11 +305,12 @@ def run_stack(args, wl, keep=None):
         assert L.check() == 0, "device error word set"
     launches = K * wl.layers
     per_launch_s = gpu_ms / 1e3 / launches
-    bytes_layer = layer_weight_bytes(wl, keep=keep)
+    bytes_layer = layer_weight_bytes(wl, keep=keep, sketch=args.sketch)
     achieved = bytes_layer / per_launch_s / 1e9
     kind = "b1" if keep is None else "cs"
     khash = kernel_hash(kind)
-    name = f"{kind}_layer_{wl.name}" + ("" if keep is None else f"_keep{keep}")
+    name = f"{kind}_layer_{wl.name}" + ("" if keep is None else f"_keep{keep}") + \
+        ("_sketch" if args.sketch else "")
     out = {
         "metric": METRIC,
         "value": round(K / (gpu_ms / 1e3), 2),
@@ -317,6 +327,8 @@ def run_stack(args, wl, keep=None):
         "config": {"workload": wl.name, "layers": wl.layers, "hidden": wl.H, "experts": wl.E,
                    "top_k": wl.k, "inter": wl.I, "shared": wl.n_shared,
                    "weights": wl.expert_dtype, "batch": 1, "keep": keep,
+                   "screen": ("ternary sketch, eq. 1" if args.sketch else
+                              "exact gates" if keep is not None else None),
                    "graph": not args.eager},
         "hbm_gb_s": round(achieved, 1),
         "hbm_pct_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
@@ -331,7 +343,7 @@ def run_stack(args, wl, keep=None):
     }
     wgs, thr = layers[0].geometry()
     out.update(platform_figures(achieved, wgs, thr))
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.sketch:
         cb, outs = cpu_baseline(wl, min(args.cpu_layers, wl.layers), token=0, keep=keep)
         worst = 0.0
         for l, y_ref in enumerate(outs):
@@ -385,6 +397,8 @@ def run_timeline(args, wl, keep=None):
         ys.append(torch.empty_like(xs[-1]))
         if keep is not None:
             kepts.append(torch.empty((ntok, max(keep, 1)), dtype=torch.int32, device="cuda"))
+        if args.sketch:
+            layers[-1].build_sketch(torch.from_numpy(T.rotation_signs(wl, l)).cuda())
     P = layers[0].geometry()[0]
     K = args.steps
     nl = K * wl.layers
@@ -397,7 +411,8 @@ def run_timeline(args, wl, keep=None):
         if keep is None:
             layers[l].forward(xs[l][tt:tt + 1], ys[l][tt:tt + 1], B=1)
         else:
-            layers[l].channel_select(xs[l][tt:tt + 1], keep, kepts[l][tt], y=ys[l][tt:tt + 1])
+            layers[l].channel_select(xs[l][tt:tt + 1], keep, kepts[l][tt], y=ys[l][tt:tt + 1],
+                                     sketch=args.sketch, mode=1 if args.sketch else 0)
 
     for t in range(args.warmup):
         for l in range(wl.layers):
@@ -646,6 +661,9 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="batch-1 stacks: per-phase timeline from the timeline build of the "
                          "library (libmoe_ffn_timeline.so) instead of the throughput line")
+    ap.add_argument("--sketch", action="store_true",
+                    help="channel-sparse workload: score channels from the ternary sketch "
+                         "(moe_channel_select_sketch, eq.-1 scores) instead of exact gates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=40, help="layers in the oracle sample")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",

@@ -174,7 +174,8 @@ size_t moe_sketch_bytes(const moe_layer_desc* desc);
 
 /* Build the sketch of the layer's routed gate and up rows into the caller's device buffer
  * `sketch` (256-byte aligned, at least moe_sketch_bytes) from the rotation signs `signs` [H]
- * (int8 device memory, +1 or -1), and bind both to the layer (they must outlive it).
+ * (int8 device memory, +1 or -1, 4-byte aligned), and bind both to the layer (they must
+ * outlive it).
  * Enqueues on `stream`. */
 moe_status moe_layer_build_sketch(moe_layer layer, const int8_t* signs, void* sketch,
                                   size_t sketch_bytes, void* stream);

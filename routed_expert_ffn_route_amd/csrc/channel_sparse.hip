@@ -367,8 +367,12 @@ __device__ inline void rotate_scan(const float* x, const int8_t* signs, float* z
 #pragma clang fp contract(off)
   const int nb = H / 128, wave = c.tid / kWave, nw = c.nthreads / kWave, lane = c.lane;
   for (int b = wave; b < nb; b += nw) {
-    float lo = x[b * 128 + lane] * (float)signs[b * 128 + lane];
-    float hi = x[b * 128 + lane + 64] * (float)signs[b * 128 + lane + 64];
+    // the signs as 32-bit words (four per word), extracted after both loads are out
+    const uint32_t* s32 = reinterpret_cast<const uint32_t*>(signs) + b * 32;
+    const uint32_t wlo = s32[lane >> 2], whi = s32[16 + (lane >> 2)];
+    const float xlo = x[b * 128 + lane], xhi = x[b * 128 + lane + 64];
+    float lo = xlo * (float)(int8_t)(wlo >> (8 * (lane & 3)));
+    float hi = xhi * (float)(int8_t)(whi >> (8 * (lane & 3)));
 #pragma unroll
     for (int h = 1; h < 64; h <<= 1) {
       const float plo = __shfl_xor(lo, h, kWave), phi = __shfl_xor(hi, h, kWave);
@@ -401,18 +405,21 @@ __device__ inline void rotate_scan(const float* x, const int8_t* signs, float* z
 // Sketch estimate of one row for this lane's share: coordinates [32q, 32q + 32) for q = lane,
 // lane + 64 (H <= 4096): the 2-bit codes (two words per q) times zs, times the block's scale.
 struct SketchPiece {
-  uint32_t w[2][2];
-  uint16_t a[2];
+  uint2 w[2];      // the 32 codes of coordinates [32q, 32q + 32)
+  uint32_t a[2];   // the FP16 scale of their block in the low half (0: no contribution)
 };
+// All loads unconditional and at least 4 bytes wide (a narrower load, or one under a branch,
+// makes the compiler wait for it at once): an invalid row reads row 0 and gets scale 0.
 __device__ __forceinline__ void sketch_load(const uint32_t* codes, const uint16_t* alpha,
-                                            int H, int lane, SketchPiece& p) {
+                                            bool valid, int H, int lane, SketchPiece& p) {
+  const uint32_t* a32 = reinterpret_cast<const uint32_t*>(alpha);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int q = lane + kWave * h;
-    const bool ok = codes != nullptr && q < H / 32;
-    p.w[h][0] = ok ? codes[2 * q] : 0u;
-    p.w[h][1] = ok ? codes[2 * q + 1] : 0u;
-    p.a[h] = ok ? alpha[q >> 2] : (uint16_t)0;
+    const int qq = min(q, H / 32 - 1);
+    p.w[h] = reinterpret_cast<const uint2*>(codes)[qq];
+    const uint32_t a2 = a32[qq >> 3];
+    p.a[h] = (valid && q < H / 32) ? (a2 >> (16 * ((qq >> 2) & 1))) & 0xFFFFu : 0u;
   }
 }
 __device__ __forceinline__ float sketch_dot(const SketchPiece& p, const float* zs, int H,
@@ -427,7 +434,7 @@ __device__ __forceinline__ float sketch_dot(const SketchPiece& p, const float* z
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const f32x4 z = zp[u];
-        const uint32_t w = p.w[h][u >> 2];
+        const uint32_t w = (u >> 2) ? p.w[h].y : p.w[h].x;
         const int sh = 8 * (u & 3);  // codes of coordinates 4u .. 4u + 3 of this q
         // a 2-bit field sign-extended: 00 -> 0, 01 -> +1, 11 -> -1
         acc = fmaf((float)((int)(w << (30 - sh)) >> 30), z.x, acc);
@@ -435,7 +442,7 @@ __device__ __forceinline__ float sketch_dot(const SketchPiece& p, const float* z
         acc = fmaf((float)((int)(w << (26 - sh)) >> 30), z.z, acc);
         acc = fmaf((float)((int)(w << (24 - sh)) >> 30), z.w, acc);
       }
-      part = fmaf(__half2float(__ushort_as_half(p.a[h])), acc, part);
+      part = fmaf(__half2float(__ushort_as_half((uint16_t)p.a[h])), acc, part);
     }
   }
   return part;
@@ -585,17 +592,16 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int task = t0 + wave + nw * u;
-        const uint32_t* cw = nullptr;
-        const uint16_t* al = nullptr;
+        size_t row = 0;
+        bool valid = false;
         if (task < ntask) {
           const int f = g0 + (task >> 1), sl = divI.div(f), e = s_ids[sl];
-          if (e >= 0) {
-            const size_t row = (size_t)e * I + (f - sl * I);
-            cw = ((task & 1) ? L.sk_v : L.sk_g) + row * (size_t)(a.H / 16);
-            al = ((task & 1) ? L.sk_av : L.sk_ag) + row * (size_t)(a.H / 128);
-          }
+          valid = e >= 0;
+          row = valid ? (size_t)e * I + (f - sl * I) : 0;
         }
-        sketch_load(cw, al, a.H, c.lane, pc[u]);
+        sketch_load(((task & 1) ? L.sk_v : L.sk_g) + row * (size_t)(a.H / 16),
+                    ((task & 1) ? L.sk_av : L.sk_ag) + row * (size_t)(a.H / 128), valid, a.H,
+                    c.lane, pc[u]);
       }
       if (t0 == 0) {
         if (c.tid < nown) own_dn[c.tid] = dnv;

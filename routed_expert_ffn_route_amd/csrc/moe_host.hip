@@ -775,6 +775,7 @@ moe_status moe_layer_build_sketch(moe_layer layer, const int8_t* signs, void* sk
     return fail(MOE_ERR_UNSUPPORTED, "the sketch needs SWIGLU experts in BF16 or F32 and hidden "
                 "a multiple of 128, at most 4096");
   if (!signs || !sketch) return fail(MOE_ERR_ARG, "signs and sketch must be given");
+  if (((uintptr_t)signs % 4) != 0) return fail(MOE_ERR_ARG, "signs must be 4-byte aligned");
   if (((uintptr_t)sketch % kAlign) != 0)
     return fail(MOE_ERR_WORKSPACE, "the sketch buffer must be 256-byte aligned");
   if (sketch_bytes < S.total)
