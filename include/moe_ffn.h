@@ -169,7 +169,8 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
  * SWIGLU experts in BF16 or F32, hidden a multiple of 128 and at most 4096).  Host only.
  * Layout of the buffer: 2-bit codes of G then V [E*I][H/16] uint32 (coordinate c of a row at
  * bits 2 (c % 16) of word c / 16: 0 -> 00, +1 -> 01, -1 -> 11), then FP16 scales of G, of V,
- * rho of G, of V [E*I][H/128], each region 256-byte aligned. */
+ * rho of G, of V [E*I][nbp] with nbp = H/128 rounded up to a multiple of 8 (each row 16-byte
+ * aligned; the padding holds zeros), each region 256-byte aligned. */
 size_t moe_sketch_bytes(const moe_layer_desc* desc);
 
 /* Build the sketch of the layer's routed gate and up rows into the caller's device buffer

@@ -26,7 +26,14 @@
 //     scan over all candidates in that order), with g from LDS;
 //  6. the deterministic cross-workgroup sum of the partial outputs; after its partial is out,
 //     workgroup 0 writes the kept list in ascending e*I + j and the threshold hint.
+//
+// With a ternary sketch of the gate and up rows ("The weights-only reader", stages 1 and 2)
+// phase 2 scores from the sketch instead of the gate rows: waves 1.. rotate and scan x while
+// wave 0 finishes the top-k, and each own candidate's two sketch rows give the estimates
+// g^ and v^ of eq. 1.  Phase 5 then reads the gate, up and down rows of every kept channel,
+// so the kept channels are shared out evenly over the workgroups rather than by owner.
 #include <hip/hip_fp16.h>
+#include <type_traits>
 
 #include "layer_common.h"
 
@@ -46,11 +53,12 @@ constexpr int kSlotPad = kMaxSlots + 4;  // slot tables of kMaxSlots + 1 ints, p
 struct CSLaunch {
   B1Args a;
   const float* dnorm;  // [E*I]
-  // ternary sketch (null: exact gate values): codes [E*I][H/16] and FP16 scales [E*I][H/128]
+  // ternary sketch (null: exact gate values): codes [E*I][H/16] and FP16 scales [E*I][nbp]
   // of the gate and up rows, and the rotation's signs [H]
   const uint32_t *sk_g, *sk_v;
   const uint16_t *sk_ag, *sk_av;
   const int8_t* signs;
+  uint64_t* sk_mask;   // launch-tagged scan masks, one copy per XCD (kSkMaskWords each)
   uint64_t* g_ws;      // channel scores with the launch parity, one copy per XCD
   int32_t* kept_out;   // [K]
   int K, mode, R, SW, tsz;
@@ -356,96 +364,245 @@ __device__ inline uint32_t kept_in_order(const uint32_t (&sb)[kCh], bool mine, i
   return mask;
 }
 
-// The token side of the sketch screen: z = H_128 (s * x) per 128-block (fp32 butterflies,
-// stages h = 1 .. 64, (a, b) -> (a + b, a - b)), and per block only the 80 coordinates of
-// largest |z| kept (ties to the lower coordinate), the others zeroed, into zs [H] (LDS).  One
-// wave per block: lane l holds coordinates l and l + 64; the 80th largest |z| is found bit by
-// bit from the top with ballot counts, the ties at it in coordinate order with lane counts.
+// The token side of the sketch screen, in two steps that hide behind other waits.
+// rotate_*: z = H_128 (s * x) per 128-block into zs [H] (LDS), one wave per block, lane l
+// holding coordinates l and l + 64; fp32 butterflies, stages h = 1 .. 64, each pair
+// (i, i + h) -> (a + b, a - b).  scan_blocks: per block only the 80 coordinates of largest |z|
+// kept (ties to the lower coordinate), the others zeroed, in place.
 constexpr int kScan = 80;
-__device__ inline void rotate_scan(const float* x, const int8_t* signs, float* zs, int H,
-                                   const Ctx& c) {
-#pragma clang fp contract(off)
-  const int nb = H / 128, wave = c.tid / kWave, nw = c.nthreads / kWave, lane = c.lane;
-  for (int b = wave; b < nb; b += nw) {
-    // the signs as 32-bit words (four per word), extracted after both loads are out
-    const uint32_t* s32 = reinterpret_cast<const uint32_t*>(signs) + b * 32;
-    const uint32_t wlo = s32[lane >> 2], whi = s32[16 + (lane >> 2)];
-    const float xlo = x[b * 128 + lane], xhi = x[b * 128 + lane + 64];
-    float lo = xlo * (float)(int8_t)(wlo >> (8 * (lane & 3)));
-    float hi = xhi * (float)(int8_t)(whi >> (8 * (lane & 3)));
+constexpr int kRotHeld = 2;  // blocks per wave whose x and signs are loaded ahead
+struct RotIn {
+  float x[kRotHeld][2];     // x at coordinates l and l + 64 of the block
+  uint32_t s[kRotHeld][2];  // the sign words holding those coordinates' signs
+};
+// the loads for blocks wave, wave + nw (always in range: a block past the end reads the last)
+__device__ inline void rotate_load(const float* x, const int8_t* signs, int H, int lane,
+                                   int wave, int nw, RotIn& r) {
+  const int nb = H / 128;
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(signs);
 #pragma unroll
-    for (int h = 1; h < 64; h <<= 1) {
-      const float plo = __shfl_xor(lo, h, kWave), phi = __shfl_xor(hi, h, kWave);
-      const bool upper = (lane & h) != 0;
-      lo = upper ? plo - lo : lo + plo;
-      hi = upper ? phi - hi : hi + phi;
-    }
-    const float z0 = lo + hi, z1 = lo - hi;
-    const uint32_t a0 = __float_as_uint(z0) & 0x7FFFFFFFu, a1 = __float_as_uint(z1) & 0x7FFFFFFFu;
-    uint32_t t = 0;  // the largest pattern with at least kScan values at or above it
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = t | (1u << bit);
-      const int cnt = __popcll(__ballot(a0 >= cand)) + __popcll(__ballot(a1 >= cand));
-      t = cnt >= kScan ? cand : t;
-    }
-    const int need = kScan - (__popcll(__ballot(a0 > t)) + __popcll(__ballot(a1 > t)));
-    const uint64_t e0 = __ballot(a0 == t), e1 = __ballot(a1 == t);
-    const int r0 = __builtin_amdgcn_mbcnt_hi((uint32_t)(e0 >> 32),
-                                             __builtin_amdgcn_mbcnt_lo((uint32_t)e0, 0));
-    const int r1 = __popcll(e0) + __builtin_amdgcn_mbcnt_hi(
-                                      (uint32_t)(e1 >> 32),
-                                      __builtin_amdgcn_mbcnt_lo((uint32_t)e1, 0));
-    const bool k0 = a0 > t || (a0 == t && r0 < need);
-    const bool k1 = a1 > t || (a1 == t && r1 < need);
-    zs[b * 128 + lane] = k0 ? z0 : 0.0f;
-    zs[b * 128 + lane + 64] = k1 ? z1 : 0.0f;
+  for (int i = 0; i < kRotHeld; ++i) {
+    const int b = min(wave + nw * i, nb - 1);
+    r.x[i][0] = x[b * 128 + lane];
+    r.x[i][1] = x[b * 128 + lane + 64];
+    r.s[i][0] = s32[b * 32 + (lane >> 2)];
+    r.s[i][1] = s32[b * 32 + 16 + (lane >> 2)];
   }
+}
+// the value of lane ^ h (the lane permutations of the top-k's xor_lane64, on 32 bits)
+template <int h>
+__device__ __forceinline__ float xor_lane_f32(float v) {
+  const int u = __float_as_int(v);
+  int r;
+  if constexpr (h == 1) r = __builtin_amdgcn_mov_dpp(u, 0xB1, 0xf, 0xf, true);
+  else if constexpr (h == 2) r = __builtin_amdgcn_mov_dpp(u, 0x4E, 0xf, 0xf, true);
+  else if constexpr (h == 4)
+    r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(u, 0x1B, 0xf, 0xf, true), 0x141, 0xf,
+                                 0xf, true);
+  else if constexpr (h == 8) r = __builtin_amdgcn_mov_dpp(u, 0x128, 0xf, 0xf, true);
+  else r = (int)swap_rows32<h>((uint32_t)u);
+  return __int_as_float(r);
+}
+template <int h>
+__device__ __forceinline__ void butterfly_stage(float& lo, float& hi, int lane) {
+#pragma clang fp contract(off)
+  const bool upper = (lane & h) != 0;
+  const float plo = xor_lane_f32<h>(lo), phi = xor_lane_f32<h>(hi);
+  lo = upper ? plo - lo : lo + plo;
+  hi = upper ? phi - hi : hi + phi;
+}
+__device__ inline void rotate_block(float xlo, float xhi, uint32_t wlo, uint32_t whi, int lane,
+                                    float* zb) {
+#pragma clang fp contract(off)
+  float lo = xlo * (float)(int8_t)(wlo >> (8 * (lane & 3)));  // s * x (exact)
+  float hi = xhi * (float)(int8_t)(whi >> (8 * (lane & 3)));
+  butterfly_stage<1>(lo, hi, lane);
+  butterfly_stage<2>(lo, hi, lane);
+  butterfly_stage<4>(lo, hi, lane);
+  butterfly_stage<8>(lo, hi, lane);
+  butterfly_stage<16>(lo, hi, lane);
+  butterfly_stage<32>(lo, hi, lane);
+  zb[lane] = lo + hi;  // stage h = 64 inside the lane
+  zb[lane + 64] = lo - hi;
+}
+__device__ inline void rotate_compute(const RotIn& r, const float* x, const int8_t* signs,
+                                      float* zs, int H, int lane, int wave, int nw) {
+  const int nb = H / 128;
+#pragma unroll
+  for (int i = 0; i < kRotHeld; ++i) {
+    const int b = wave + nw * i;
+    if (b < nb) rotate_block(r.x[i][0], r.x[i][1], r.s[i][0], r.s[i][1], lane, zs + b * 128);
+  }
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(signs);
+  for (int b = wave + nw * kRotHeld; b < nb; b += nw)  // more blocks than loaded ahead
+    rotate_block(x[b * 128 + lane], x[b * 128 + lane + 64], s32[b * 32 + (lane >> 2)],
+                 s32[b * 32 + 16 + (lane >> 2)], lane, zs + b * 128);
+}
+// The 80th largest |z| of a block is found bit by bit from the top with ballot counts (a
+// pattern with exactly 80 values at or above it already separates them, so the search stops
+// there), the ties at it in coordinate order with lane counts.  Two blocks' searches run
+// interleaved (`two`: the second is live).
+__device__ inline void search_two(uint32_t aA0, uint32_t aA1, uint32_t aB0, uint32_t aB1,
+                                  bool two, uint32_t& tA, uint32_t& tB) {
+  tA = 0;  // the largest pattern with at least kScan values at or above it
+  tB = 0;
+  bool dA = false, dB = !two;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cA = tA | (1u << bit), cB = tB | (1u << bit);
+    const int nA = __popcll(__ballot(aA0 >= cA)) + __popcll(__ballot(aA1 >= cA));
+    const int nB = __popcll(__ballot(aB0 >= cB)) + __popcll(__ballot(aB1 >= cB));
+    tA = !dA && nA >= kScan ? cA : tA;
+    tB = !dB && nB >= kScan ? cB : tB;
+    dA = dA || nA == kScan;
+    dB = dB || nB == kScan;
+    if (dA && dB) break;
+  }
+}
+// which of this lane's two coordinates (l, l + 64) are kept, given the 80th largest pattern t
+__device__ inline void keep_bits(uint32_t a0, uint32_t a1, uint32_t t, bool& k0, bool& k1) {
+  const int need = kScan - (__popcll(__ballot(a0 > t)) + __popcll(__ballot(a1 > t)));
+  const uint64_t e0 = __ballot(a0 == t), e1 = __ballot(a1 == t);
+  const int r0 = __builtin_amdgcn_mbcnt_hi((uint32_t)(e0 >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)e0, 0));
+  const int r1 = __popcll(e0) + __builtin_amdgcn_mbcnt_hi(
+                                    (uint32_t)(e1 >> 32),
+                                    __builtin_amdgcn_mbcnt_lo((uint32_t)e1, 0));
+  k0 = a0 > t || (a0 == t && r0 < need);
+  k1 = a1 > t || (a1 == t && r1 < need);
+}
+__device__ __forceinline__ uint32_t abs_bits(float z) { return __float_as_uint(z) & 0x7FFFFFFFu; }
+// Block b of z, its kept coordinates given, to 24-bit fixed point in place: each kept value
+// times 2^e (e[b] = 148 - the biased exponent of the largest kept |z|, so that every scaled
+// value is below 2^22 in magnitude), rounded to the nearest integer; the others 0.  The
+// estimates then add codes times these integers exactly (24-bit multiply-adds) and scale by
+// 2^-e once per block.
+__device__ inline void finish_block(float* zs, int* ebs, int b, int lane, float z0, float z1,
+                                    bool k0, bool k1) {
+  const float v0 = k0 ? z0 : 0.0f, v1 = k1 ? z1 : 0.0f;
+  const uint32_t mb = wave_max_u32(max(abs_bits(v0), abs_bits(v1)));
+  const int e = 148 - max((int)(mb >> 23), 1);
+  int* zi = reinterpret_cast<int*>(zs) + b * 128;
+  zi[lane] = (int)rintf(ldexpf(v0, e));
+  zi[lane + 64] = (int)rintf(ldexpf(v1, e));
+  if (lane == 0) ebs[b] = e;
+}
+// Scan and finish blocks bA and bB (bB >= nb: none; bA >= nb: nothing to do) in place.
+__device__ inline void scan_finish_two(float* zs, int* ebs, int lane, int bA, int bB, int nb) {
+  if (bA >= nb) return;
+  const bool two = bB < nb;
+  const int b2 = two ? bB : bA;
+  const float zA0 = zs[bA * 128 + lane], zA1 = zs[bA * 128 + lane + 64];
+  const float zB0 = zs[b2 * 128 + lane], zB1 = zs[b2 * 128 + lane + 64];
+  const uint32_t aA0 = abs_bits(zA0), aA1 = abs_bits(zA1), aB0 = abs_bits(zB0), aB1 = abs_bits(zB1);
+  uint32_t tA, tB;
+  search_two(aA0, aA1, aB0, aB1, two, tA, tB);
+  bool k0, k1;
+  keep_bits(aA0, aA1, tA, k0, k1);
+  finish_block(zs, ebs, bA, lane, zA0, zA1, k0, k1);
+  if (two) {
+    keep_bits(aB0, aB1, tB, k0, k1);
+    finish_block(zs, ebs, bB, lane, zB0, zB1, k0, k1);
+  }
+}
+// The scan of block b, computed once per launch (by workgroup b) and handed to every
+// workgroup: its keep mask as four 32-bit words (coordinates 0-31, 32-63, 64-95, 96-127),
+// each in a 64-bit word whose upper half is the launch tag, written to every per-XCD copy.
+__device__ inline void scan_publish(const float* zs, int lane, int b, uint64_t* mask,
+                                    uint32_t tag) {
+  const uint32_t a0 = abs_bits(zs[b * 128 + lane]), a1 = abs_bits(zs[b * 128 + lane + 64]);
+  uint32_t t, t_unused;
+  search_two(a0, a1, a0, a1, false, t, t_unused);
+  bool k0, k1;
+  keep_bits(a0, a1, t, k0, k1);
+  const uint64_t m0 = __ballot(k0), m1 = __ballot(k1);
+  if (lane < 4 * kPollCopies) {
+    const int word = lane & 3;
+    const uint64_t m = word < 2 ? m0 : m1;
+    const uint32_t v = (word & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
+    st_dev64(mask + (size_t)(lane >> 2) * kSkMaskWords + 4 * b + word,
+             ((uint64_t)tag << 32) | v);
+  }
+}
+// Block b's published mask (every lane holds word lane % 4 of this workgroup's copy, `w`,
+// loaded ahead; re-polled if it is not this launch's yet) and block b finished with it.
+__device__ inline void consume_finish(float* zs, int* ebs, int lane, int b, uint64_t w,
+                                      const uint64_t* mcopy, uint32_t tag, uint32_t* err) {
+  if ((uint32_t)(w >> 32) != tag) w = wait_tagged(mcopy + 4 * b + (lane & 3), tag, err, kErrPhaseWait);
+  const uint32_t mw0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)w, 0);
+  const uint32_t mw1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)w, 1);
+  const uint32_t mw2 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)w, 2);
+  const uint32_t mw3 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)w, 3);
+  const bool k0 = (((lane < 32 ? mw0 : mw1) >> (lane & 31)) & 1u) != 0;
+  const bool k1 = (((lane < 32 ? mw2 : mw3) >> (lane & 31)) & 1u) != 0;
+  finish_block(zs, ebs, b, lane, zs[b * 128 + lane], zs[b * 128 + lane + 64], k0, k1);
 }
 
-// Sketch estimate of one row for this lane's share: coordinates [32q, 32q + 32) for q = lane,
-// lane + 64 (H <= 4096): the 2-bit codes (two words per q) times zs, times the block's scale.
-struct SketchPiece {
-  uint2 w[2];      // the 32 codes of coordinates [32q, 32q + 32)
-  uint32_t a[2];   // the FP16 scale of their block in the low half (0: no contribution)
-};
-// All loads unconditional and at least 4 bytes wide (a narrower load, or one under a branch,
-// makes the compiler wait for it at once): an invalid row reads row 0 and gets scale 0.
-__device__ __forceinline__ void sketch_load(const uint32_t* codes, const uint16_t* alpha,
-                                            bool valid, int H, int lane, SketchPiece& p) {
-  const uint32_t* a32 = reinterpret_cast<const uint32_t*>(alpha);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int q = lane + kWave * h;
-    const int qq = min(q, H / 32 - 1);
-    p.w[h] = reinterpret_cast<const uint2*>(codes)[qq];
-    const uint32_t a2 = a32[qq >> 3];
-    p.a[h] = (valid && q < H / 32) ? (a2 >> (16 * ((qq >> 2) & 1))) & 0xFFFFu : 0u;
-  }
+// Sketch staging in LDS: the codes of each task's row (task 2o + t: own candidate o, t = 0
+// gate, 1 up), H/4 bytes each, then their FP16 scales, nbp (the scale row stride) each.
+__host__ __device__ constexpr int sketch_nbp(int H) { return (H / 128 + 7) & ~7; }
+__host__ __device__ constexpr int sketch_stage_bytes(int H, int ntask) {
+  return ntask * (H / 4 + 2 * sketch_nbp(H));
 }
-__device__ __forceinline__ float sketch_dot(const SketchPiece& p, const float* zs, int H,
-                                            int lane) {
-  float part = 0.0f;
+// a * b + c on 24-bit signed a and b in one instruction (as an integer sum the compiler would
+// otherwise regroup into separate multiplies and three-way adds)
+__device__ __forceinline__ int mad24(int a, int b, int c) {
+  int d;
+  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+// The estimates sum_b alpha_b sum_(scanned i in b) code_i z_i / 128 of G staged rows (tasks
+// t0, t0 + step, ...; those past ntask are computed for task t0 and not used), in every lane:
+// lane l takes coordinates [32q, 32q + 32) for q = l, l + 64 (H <= 4096), each piece of z read
+// once for all G rows; z as the fixed-point integers of finish_block (zi) with their block
+// exponents (ebs).
+template <int G>
+__device__ inline void sketch_estimates(const uint8_t* st_codes, const uint16_t* st_alpha,
+                                        int nbp, int t0, int step, int ntask, const int* zi,
+                                        const int* ebs, int H, int lane, float (&out)[G]) {
+  const int nq = H / 32;
+  // the eight 16-byte pieces of zi in an order rotated by lane: lanes 32 words apart taking
+  // the same piece would all hit the same LDS banks; the codes are rotated to match
+  const int rot = (lane + (lane >> 3)) & 7;
+  float part[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) part[g] = 0.0f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int q = lane + kWave * h;
-    if (q < H / 32) {
-      const f32x4* zp = reinterpret_cast<const f32x4*>(zs + 32 * q);
-      float acc = 0.0f;
+    if (q < nq) {
+      uint64_t wr[G];
+      float al[G];
+      int acc[G];  // |acc| < 32 * 2^22
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int t = t0 + g * step < ntask ? t0 + g * step : t0;
+        const uint2 w = reinterpret_cast<const uint2*>(st_codes + (size_t)t * (H / 4))[q];
+        wr[g] = __builtin_rotateright64(((uint64_t)w.y << 32) | w.x, 8 * rot);
+        al[g] = __half2float(__ushort_as_half(st_alpha[t * nbp + (q >> 2)]));
+        acc[g] = 0;
+      }
+      const i32x4* zp = reinterpret_cast<const i32x4*>(zi + 32 * q);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const f32x4 z = zp[u];
-        const uint32_t w = (u >> 2) ? p.w[h].y : p.w[h].x;
-        const int sh = 8 * (u & 3);  // codes of coordinates 4u .. 4u + 3 of this q
-        // a 2-bit field sign-extended: 00 -> 0, 01 -> +1, 11 -> -1
-        acc = fmaf((float)((int)(w << (30 - sh)) >> 30), z.x, acc);
-        acc = fmaf((float)((int)(w << (28 - sh)) >> 30), z.y, acc);
-        acc = fmaf((float)((int)(w << (26 - sh)) >> 30), z.z, acc);
-        acc = fmaf((float)((int)(w << (24 - sh)) >> 30), z.w, acc);
+        const i32x4 z = zp[(u + rot) & 7];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          // the codes of that piece's four coordinates; a 2-bit field sign-extended:
+          // 00 -> 0, 01 -> +1, 11 -> -1
+          const int b = (int)(uint32_t)(wr[g] >> (8 * u));
+          acc[g] = mad24(__builtin_amdgcn_sbfe(b, 0, 2), z.x, acc[g]);
+          acc[g] = mad24(__builtin_amdgcn_sbfe(b, 2, 2), z.y, acc[g]);
+          acc[g] = mad24(__builtin_amdgcn_sbfe(b, 4, 2), z.z, acc[g]);
+          acc[g] = mad24(__builtin_amdgcn_sbfe(b, 6, 2), z.w, acc[g]);
+        }
       }
-      part = fmaf(__half2float(__ushort_as_half((uint16_t)p.a[h])), acc, part);
+      const int e = ebs[q >> 2];
+#pragma unroll
+      for (int g = 0; g < G; ++g) part[g] = fmaf(al[g], ldexpf((float)acc[g], -e), part[g]);
     }
   }
-  return part;
+#pragma unroll
+  for (int g = 0; g < G; ++g) out[g] = wave_sum(part[g]) * (1.0f / 128.0f);
 }
 
 template <DT ET, DT ST, DT RT, int C, int CPT, bool SK>
@@ -485,8 +642,10 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   int* own_keep = reinterpret_cast<int*>(own_dn + kOwnMax);         // [kOwnMax] kept flags
   int* klist = own_keep + kOwnMax;                                  // [kOwnMax] kept, in order
   float* est = reinterpret_cast<float*>(klist + kOwnMax);           // [2 kOwnMax] sketch
-  uint32_t* sv = reinterpret_cast<uint32_t*>(est + 2 * kOwnMax);    // [n] score patterns
-  float* zs = reinterpret_cast<float*>(sv + ((n + 3) & ~3));        // [H] scanned R x
+  int* ebs = reinterpret_cast<int*>(est + 2 * kOwnMax);             // [32] block exponents
+  uint32_t* sv = reinterpret_cast<uint32_t*>(ebs + 32);             // [n] score patterns
+  float* zs = reinterpret_cast<float*>(sv + ((n + 3) & ~3));        // [H] R x, then scanned
+                                                                    // (fixed point)
   float* big = zs + a.H;
   Ctrl* ctrl = a.ctrl;
   // channel-selection launches on this workspace so far: its scores carry the parity
@@ -501,11 +660,16 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   load_x<8, CPT>(a.x, c, xv);
 #pragma unroll
   for (int i = 0; i < CPT * 8; ++i) yv[i] = 0.0f;
+  RotIn rin;  // (sketch) x and the signs for the rotation, loaded ahead of the router rows
+  if constexpr (SK) rotate_load(a.x, L.signs, a.H, c.lane, c.tid / kWave, c.nthreads / kWave, rin);
   read_epoch(ctrl, c);
 
-  // 1. router rows, then the routing; the shared-expert rows are warmed meanwhile
+  // 1. router rows, then the routing; the shared-expert rows are warmed meanwhile.  (Sketch:
+  // z = R x is computed while the router rows are in flight, and scanned during the top-k.)
   RouterRound<RT, CPT> rr;
   router_issue<RT, CPT>(a.route_inside, a.router, a.E, c, rr);
+  if constexpr (SK)
+    rotate_compute(rin, a.x, L.signs, zs, a.H, c.lane, c.tid / kWave, c.nthreads / kWave);
   router_finish<RT, CPT>(rr, a.router, a.E, xv, a.rlog, big, reinterpret_cast<uint32_t*>(s_int),
                          c);
   MOE_STAMP(c.stamps, 1);
@@ -521,8 +685,34 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
                 reinterpret_cast<const uint8_t*>(a.sh_down_t), s0, s1,
                 (uint32_t)Fmt<ST>::row_bytes(a.H), kWave, c, warm);
   };
+  // (sketch) the scan of z.  With the router inside and P >= H/128 workgroups, block b is
+  // scanned once per launch, by workgroup b in a wave that reads no router keys, and its mask
+  // handed to every workgroup (read while the sketch rows load).  Otherwise each workgroup
+  // scans every block itself in the top-k's idle moments: blocks [0, sb_pre) by the waves that
+  // read no keys, two each; [sb_pre, sb_hook) by waves 1.., one each, before they warm the
+  // shared rows; the rest while the sketch rows load.
+  const int nbk = a.H / 128, nwv = c.nthreads / kWave;
+  const int nidle = SK && a.route_inside ? max(0, nwv - (a.E + kWave - 1) / kWave) : 0;
+  const bool pub = nidle >= 1 && c.P >= nbk;
+  const int sb_pre = pub ? 0 : min(nbk, 2 * nidle);
+  const int sb_hook = SK && a.route_inside && !pub ? min(nbk, sb_pre + nwv - 1) : 0;
+  auto hooks = topk_hooks(
+      [&] {
+        if constexpr (SK)
+          scan_finish_two(zs, ebs, c.lane, sb_pre + c.tid / kWave - 1, sb_hook, sb_hook);
+        warm_shared();
+      },
+      [&](int i, int ni) {
+        if constexpr (SK) {
+          if (pub) {
+            if (i == 0 && c.wg < nbk) scan_publish(zs, c.lane, c.wg, L.sk_mask, c.epoch + 1u);
+          } else {
+            scan_finish_two(zs, ebs, c.lane, i, i + ni, sb_pre);
+          }
+        }
+      });
   fetch_routing(a.route_inside, a.rlog, a.ids_in, a.w_in, a.E, k, ctrl,
-                reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c, warm_shared);
+                reinterpret_cast<uint64_t*>(big), s_ids, s_w, a.ids_ws, a.w_ws, c, hooks);
   MOE_STAMP(c.stamps, 3);
 
   // 2. gate pass over this workgroup's own candidates [g0, g1) (flat f = slot * I + j): the
@@ -582,43 +772,96 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
       publish(base, g);
     }
   } else {
-    // the sketch screen (stage 1 of the reader): the own candidates' sketch rows of G and V
-    // (one wave per row, up to four rows per wave in flight) are loaded first; x is rotated
-    // and scanned meanwhile; each estimate is sum_b alpha_b sum_(scanned i) code_i z_i / 128;
-    // the score is eq. 1, w_e ||d_j|| |silu(g^) v^| (without w_e in the gate-dnorm mode)
-    const int nw = c.nthreads / kWave, wave = c.tid / kWave, ntask = 2 * nown;
-    for (int t0 = 0; t0 < ntask; t0 += 4 * nw) {
-      SketchPiece pc[4];
+    // the sketch screen (stage 1 of the reader): the sketch rows of G and V of the own
+    // candidates are staged in LDS (`big`, free until the output reduction) by the whole
+    // workgroup, 16 bytes a thread and load; then one wave per row forms its estimate
+    // sum_b alpha_b sum_(scanned i) code_i z_i / 128; the score is eq. 1,
+    // w_e ||d_j|| |silu(g^) v^| (without w_e in the gate-dnorm mode)
+    const int ntask = 2 * nown, nbp = sketch_nbp(a.H);
+    const int cpr = a.H / 64, ppr = cpr + nbp / 8;  // 16-byte pieces per row: codes, all
+    const int npieces = ntask * ppr;
+    uint8_t* st_codes = reinterpret_cast<uint8_t*>(big);
+    uint8_t* st_alpha = st_codes + (size_t)ntask * (a.H / 4);
+    const DivI divP(ppr);
+    const int wave = c.tid / kWave;
+    // (the published masks of this wave's blocks are requested first, one word a lane, so
+    // that waiting for them does not wait for the sketch rows requested after them; the loads
+    // are made in either case, from the workspace's mask words)
+    const uint64_t* mcopy = L.sk_mask + (size_t)(c.wg % kPollCopies) * kSkMaskWords;
+    uint64_t mw[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int task = t0 + wave + nw * u;
-        size_t row = 0;
-        bool valid = false;
-        if (task < ntask) {
-          const int f = g0 + (task >> 1), sl = divI.div(f), e = s_ids[sl];
-          valid = e >= 0;
-          row = valid ? (size_t)e * I + (f - sl * I) : 0;
-        }
-        sketch_load(((task & 1) ? L.sk_v : L.sk_g) + row * (size_t)(a.H / 16),
-                    ((task & 1) ? L.sk_av : L.sk_ag) + row * (size_t)(a.H / 128), valid, a.H,
-                    c.lane, pc[u]);
-      }
-      if (t0 == 0) {
-        if (c.tid < nown) own_dn[c.tid] = dnv;
-        rotate_scan(a.x, L.signs, zs, a.H, c);
-        __syncthreads();
-      }
+    for (int i = 0; i < 2; ++i) mw[i] = ld_dev64(mcopy + 4 * min(wave + nwv * i, nbk - 1) + (c.lane & 3));
+    // every sketch-row load and LDS store unconditional (a load or store under a branch makes
+    // the compiler's later waits wait for every load in flight): a piece past the end is the
+    // last one again, stored twice with the same bytes; a slot without an expert reads row 0
+    // and stores zeros
+    const int np1 = max(npieces, 1);
+    auto issue = [&](int p0, u32x4(&v)[2], bool(&ok)[2], int(&dst)[2]) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int task = t0 + wave + nw * u;
-        const float v = wave_sum(sketch_dot(pc[u], zs, a.H, c.lane)) * (1.0f / 128.0f);
-        if (task < ntask && c.lane == 0) est[task] = v;
+      for (int u = 0; u < 2; ++u) {
+        const int p = p0 + c.tid + u * c.nthreads, pc = min(p, np1 - 1);
+        const int task = divP.div(pc), piece = pc - task * ppr;
+        const int f = g0 + (task >> 1), sl = divI.div(f), e = s_ids[sl];
+        const size_t row = e >= 0 ? (size_t)e * I + (f - sl * I) : 0;
+        const bool code = piece < cpr;
+        const uint8_t* src =
+            code ? reinterpret_cast<const uint8_t*>((task & 1) ? L.sk_v : L.sk_g) +
+                       row * (size_t)(a.H / 4) + 16 * piece
+                 : reinterpret_cast<const uint8_t*>((task & 1) ? L.sk_av : L.sk_ag) +
+                       row * (size_t)(2 * nbp) + 16 * (piece - cpr);
+        v[u] = *reinterpret_cast<const u32x4*>(src);
+        ok[u] = e >= 0 && npieces > 0;
+        dst[u] = code ? task * (a.H / 4) + 16 * piece
+                      : ntask * (a.H / 4) + task * 2 * nbp + 16 * (piece - cpr);
       }
+    };
+    auto store = [&](const u32x4(&v)[2], const bool(&ok)[2], const int(&dst)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<u32x4*>(st_codes + dst[u]) = ok[u] ? v[u] : u32x4{0u, 0u, 0u, 0u};
+    };
+    u32x4 v[2];
+    bool ok[2];
+    int dst[2];
+    issue(0, v, ok, dst);
+    // the blocks of z not finished during the top-k, while the sketch rows are in flight
+    if (pub) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (wave + nwv * i < nbk)
+          consume_finish(zs, ebs, c.lane, wave + nwv * i, mw[i], mcopy, c.epoch + 1u, &ctrl->err);
+      for (int b = wave + 2 * nwv; b < nbk; b += nwv)  // (fewer than 16 waves)
+        consume_finish(zs, ebs, c.lane, b, ld_dev64(mcopy + 4 * b + (c.lane & 3)), mcopy,
+                       c.epoch + 1u, &ctrl->err);
+    } else {
+      for (int b = sb_hook + wave; b < nbk; b += 2 * nwv)
+        scan_finish_two(zs, ebs, c.lane, b, b + nwv, nbk);
     }
-    if (ntask == 0) {
-      rotate_scan(a.x, L.signs, zs, a.H, c);  // (keeps the barrier count uniform)
-      __syncthreads();
+    store(v, ok, dst);
+    for (int p0 = 2 * c.nthreads; p0 < npieces; p0 += 2 * c.nthreads) {
+      issue(p0, v, ok, dst);
+      store(v, ok, dst);
     }
+    if (c.tid < nown) own_dn[c.tid] = dnv;
+    __syncthreads();
+    // one wave per row, up to four rows of a wave at once (each piece of z read once for
+    // them); the group is as large as the rows per wave, as every row in it is computed
+    auto estimates = [&](auto gtag) {
+      constexpr int G = decltype(gtag)::value;
+      for (int t0 = wave; t0 < ntask; t0 += G * nwv) {
+        float ev[G];
+        sketch_estimates<G>(st_codes, reinterpret_cast<const uint16_t*>(st_alpha), nbp, t0, nwv,
+                            ntask, reinterpret_cast<const int*>(zs), ebs, a.H, c.lane, ev);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          if (c.lane == 0 && t0 + g * nwv < ntask) est[t0 + g * nwv] = ev[g];
+      }
+    };
+    const int per_wave = (ntask + nwv - 1) / nwv;
+    if (per_wave <= 1) estimates(std::integral_constant<int, 1>{});
+    else if (per_wave == 2) estimates(std::integral_constant<int, 2>{});
+    else if (per_wave == 3) estimates(std::integral_constant<int, 3>{});
+    else estimates(std::integral_constant<int, 4>{});
     __syncthreads();
     if (c.tid < nown) {
       const int f = g0 + c.tid;
@@ -756,6 +999,36 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   // takes the output-order scan over all candidates
   int* slot_tk = hist;                // [k] (hist is free now)
   int* slot_base = hist + kMaxSlots;  // [k]
+  int nkept = 0;
+  if constexpr (SK) {
+    // with the sketch every kept channel is computed from its full rows, so any workgroup
+    // can take it: the kept candidates are shared out evenly instead, workgroup w taking
+    // those of ranks [N w / P, N (w + 1) / P) in candidate order (N kept in all); klist
+    // holds their flat candidate indices
+    uint32_t m = 0;
+    if (!all && !none && need < ties) {
+      int pos[kCh];
+      m = kept_in_order(sb, mine, sl0, j0, T, need, all, none, k, a.E, s_ids, sh, slot_gt,
+                        slot_eq, slot_tk, slot_base, c, pos);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kCh; ++i)
+        if (mine && !none && (all || sb[i] > T || (sb[i] == T && need == ties))) m |= 1u << i;
+    }
+    int tot;
+    int r = block_excl_scan(__popc(m), sh + 48, c, &tot);
+    const int p0 = (int)((long long)tot * c.wg / c.P);
+    const int p1 = (int)((long long)tot * (c.wg + 1) / c.P);
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      if ((m >> i) & 1u) {
+        if (r >= p0 && r < p1) klist[r - p0] = c0 + i;
+        ++r;
+      }
+    }
+    nkept = p1 - p0;  // at most ceil(n / P) <= kOwnMax
+    __syncthreads();
+  } else {
   if (!all && !none && need < ties) {
     int pos[kCh];
     const uint32_t m = kept_in_order(sb, mine, sl0, j0, T, need, all, none, k, a.E, s_ids, sh,
@@ -785,23 +1058,25 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
     if (c.lane == 0) s_int[14] = nk;
   }
   __syncthreads();
-  const int nkept = s_int[14];
+  nkept = s_int[14];
+  }
   MOE_STAMP(c.stamps, 23);
 
-  // 7. the own kept channels: up row and down row only, g from LDS
+  // 7. the kept channels: the own ones' up and down rows with g from LDS, or (sketch) this
+  // workgroup's share's gate, up and down rows
   stream_channels<ET, C, CPT, SK, false>(
       SK ? a.gate : nullptr, a.up, a.down_t, SK ? a.gate_s : nullptr, a.up_s, a.down_s, 0,
       nkept,
       [=](int i, long long& row, float& wt, float& gvv) {
         // i is wave-uniform, so are the candidate, its slot and expert: scalar arithmetic
         const int o = __builtin_amdgcn_readfirstlane(klist[i]);
-        const int f = g0 + o;
+        const int f = SK ? o : g0 + o;
         const int sl = divI.div(f);
         const int e = __builtin_amdgcn_readfirstlane(s_ids[sl]);
         if (e >= 0) {
           row = (long long)e * I + (f - sl * I);
           wt = s_w[sl];
-          gvv = own_g[o];
+          if constexpr (!SK) gvv = own_g[o];
         }
       },
       xv, yv, c);
@@ -866,12 +1141,12 @@ hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStrea
 // LDS of the channel-sparse kernel: team-reduction buffers, routing, selection words, slot
 // tables, histogram, bin members, this workgroup's kept list, the gate values and score
 // patterns of all k*I candidates, and the larger of the router / top-k / output scratch.
-int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K) {
+int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K, bool sketch) {
   (void)K;
   const int nteams = threads / team_size(H);
   const int n = k * I;
   const int fixed = 2 * (threads / kWave) * kMaxNP * 4 + (16 + 64 + 64 + 96) * 4 +
-                    2 * kSlotPad * 4 + kSelBins * 4 + kSelCand * 4 + 7 * kOwnMax * 4 +
+                    2 * kSlotPad * 4 + kSelBins * 4 + kSelCand * 4 + 7 * kOwnMax * 4 + 32 * 4 +
                     ((n + 3) & ~3) * 4 + H * 4;
   const int ybuf = nteams * H * 4;
   const int topk = topk_lds_bytes(E, k);
@@ -879,6 +1154,9 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K) {
   int big = ybuf > topk ? ybuf : topk;
   big = big > threads * 8 ? big : threads * 8;
   big = big > router ? big : router;
+  // (sketch) the own candidates' sketch rows staged
+  const int stage = sketch ? sketch_stage_bytes(H, 2 * ((n + wgs - 1) / wgs)) : 0;
+  big = big > stage ? big : stage;
   return fixed + (big + 15) / 16 * 16;
 }
 
@@ -901,18 +1179,20 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_
   L.sk_g = L.sk_v = nullptr;
   L.sk_ag = L.sk_av = nullptr;
   L.signs = nullptr;
+  L.sk_mask = nullptr;
   if (sketch) {
     if (a.H % 128 != 0 || a.H > 4096 || !sketch->g || !sketch->v || !sketch->ag ||
-        !sketch->av || !sketch->signs)
+        !sketch->av || !sketch->signs || !sketch->mask)
       return hipErrorInvalidValue;
     L.sk_g = sketch->g;
     L.sk_v = sketch->v;
     L.sk_ag = sketch->ag;
     L.sk_av = sketch->av;
     L.signs = sketch->signs;
+    L.sk_mask = sketch->mask;
   }
   lc::reducer_split(a.H, wgs, &L.R, &L.SW);
-  const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I, wgs, K);
+  const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I, wgs, K, sketch != nullptr);
   if (et == DT::F32 && st == DT::F32 && rt == DT::F32)
     return launch_cpt<DT::F32, DT::F32, DT::F32>(L, wgs, threads, lds, s, occ);
   if (et == DT::BF16 && st == DT::BF16 && rt == DT::BF16)

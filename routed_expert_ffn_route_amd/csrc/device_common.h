@@ -10,6 +10,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Pointers typed as LDS (address space 3).  Buffers chosen at run time among several LDS
@@ -537,6 +538,25 @@ __device__ __forceinline__ uint64_t merge_two(uint64_t r, uint64_t s, int lane) 
 struct NoHook {
   __device__ void operator()() const {}
 };
+// A hook with an idle(i, n) member as well: run by the n waves that read no keys, i = 0 ..
+// n - 1, while the others poll and sort theirs (before the barrier).
+template <typename After, typename Idle>
+struct TopkHooks {
+  After after;
+  Idle idle_fn;
+  __device__ void operator()() const { after(); }
+  __device__ void idle(int i, int n) const { idle_fn(i, n); }
+};
+template <typename After, typename Idle>
+__device__ inline TopkHooks<After, Idle> topk_hooks(After a, Idle i) {
+  return TopkHooks<After, Idle>{a, i};
+}
+template <typename H>
+__device__ inline auto call_idle(const H& h, int i, int n, int) -> decltype(h.idle(i, n), void()) {
+  h.idle(i, n);
+}
+template <typename H>
+__device__ inline void call_idle(const H&, int, int, long) {}
 // after_keys() runs in every wave but wave 0 once all keys have been read (after the barrier
 // that follows the per-wave runs), while wave 0 merges the runs.
 template <int KP, typename KeyOf, typename AfterKeys = NoHook>
@@ -558,6 +578,7 @@ __device__ inline uint64_t wg_topk_bitonic(int n, KeyOf key_of, uint64_t* cand,
     top = ch == wave ? x : merge_two<KP>(top, x, lane);
   }
   if (wave == 0) MOE_STAMP(stamps, kStampWaveTop);
+  if (wave >= chunks) call_idle(after_keys, wave - chunks, nwaves - chunks, 0);
   const int runs = min(nwaves, chunks);
   if (wave < runs && lane < KP) cand[wave * KP + lane] = top;
   __syncthreads();

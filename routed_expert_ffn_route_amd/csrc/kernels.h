@@ -49,9 +49,11 @@ int team_size(int H);
 // read their gate row too.
 struct CsSketch {
   const uint32_t *g, *v;    // 2-bit codes [E*I][H/16]
-  const uint16_t *ag, *av;  // FP16 scales [E*I][H/128]
+  const uint16_t *ag, *av;  // FP16 scales [E*I][nbp]
   const int8_t* signs;      // rotation signs [H]
+  uint64_t* mask;           // workspace: launch-tagged scan masks, kPollCopies x kSkMaskWords
 };
+constexpr int kSkMaskWords = 128;  // words per copy: 4 per 128-block, H <= 4096
 hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_t* kept,
                      int K, int mode, DT et, DT st, DT rt, int workgroups, int threads,
                      hipStream_t s, int* occupancy = nullptr, const CsSketch* sketch = nullptr);
@@ -60,7 +62,7 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_
 hipError_t launch_sketch_build(const void* rows, DT dt, size_t nrows, int H,
                                const int8_t* signs, uint32_t* codes, uint16_t* alpha,
                                uint16_t* rho, hipStream_t s);
-int cs_lds_bytes(int H, int threads, int E, int k, int I, int workgroups, int K);
+int cs_lds_bytes(int H, int threads, int E, int k, int I, int workgroups, int K, bool sketch);
 constexpr int kCsMaxPerThread = 8;  // k*I <= 8 * threads
 constexpr int kCsOwnMax = 64;       // ceil(k*I / workgroups) <= 64 (own candidates)
 

@@ -692,11 +692,11 @@ template <DT RT, int CPT>
 __device__ inline void router_issue(bool compute, const void* router, int E, const Ctx& c,
                                     RouterRound<RT, CPT>& rr) {
   rr.nrows = compute && c.wg < E ? (E - 1 - c.wg) / c.P + 1 : 0;
-  if (rr.nrows > 0) {
-    const long long rows[1] = {c.team < rr.nrows ? (long long)c.wg + (long long)c.P * c.team
-                                                 : -1ll};
-    team_dots_load<RT, 1, CPT>(router, nullptr, rows, c, rr.tr);
-  }
+  // issued by every team (a row of -1 loads nothing): not under a branch, so that waits for
+  // loads issued before it need not wait for it
+  const long long rows[1] = {c.team < rr.nrows ? (long long)c.wg + (long long)c.P * c.team
+                                               : -1ll};
+  team_dots_load<RT, 1, CPT>(router, nullptr, rows, c, rr.tr);
 }
 template <DT RT, int CPT>
 __device__ inline void router_finish(const RouterRound<RT, CPT>& rr, const void* router, int E,
@@ -1019,9 +1019,9 @@ __device__ inline void reduce_output(const float (&yv)[CPT * E], float* partials
 // Read the epoch (launches completed on this workspace) at the start of a launch.  Only
 // thread 0 waits on counters, so only it needs the value; no barrier, so the load's
 // latency overlaps the first weight loads.
-__device__ inline void read_epoch(Ctrl* ctrl, Ctx& c) {
-  c.epoch = c.tid == 0 ? load_relaxed_dev(&ctrl->epoch) : 0u;
-}
+// (every thread loads it: a load under a branch makes the compiler's waits for the loads
+// before it wait for everything in flight)
+__device__ inline void read_epoch(Ctrl* ctrl, Ctx& c) { c.epoch = load_relaxed_dev(&ctrl->epoch); }
 
 // Reducer count and slice width for H columns over P workgroups: power-of-two slices of at
 // least 32 columns, at most P/2 reducers.

@@ -51,7 +51,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, rlog, zrow, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, cs_s, cs_y, xh, xl, x16, xsc, act, part, total;
+      union_slots, cs_s, sk_mask, cs_y, xh, xl, x16, xsc, act, part, total;
 };
 
 bool desc_valid(const moe_layer_desc* d, std::string* why) {
@@ -129,6 +129,10 @@ Layout layout_of(const moe_layer_desc* d, bool with_dnorm = true) {
   // channel selection: the launch-tagged scores [k*I] (32-bit), one copy per XCD, each padded
   // to 64 words
   L.cs_s = take(kI ? (size_t)kPollCopies * ((kI + 63) / 64) * 64 * 4 : 0);
+  // the sketch screen's launch-tagged scan masks (4 words per 128-block), one copy per XCD
+  L.sk_mask = take(kI && d->hidden % 128 == 0 && d->hidden <= 4096
+                       ? (size_t)kPollCopies * kSkMaskWords * 8
+                       : 0);
   L.cs_y = take(d->kind == MOE_EXPERT_SWIGLU ? (size_t)d->hidden * 4 : 0);
   const bool batched_swiglu = d->kind == MOE_EXPERT_SWIGLU && B > 1;
   const size_t xs =
@@ -717,13 +721,18 @@ static moe_status channel_select_impl(moe_layer layer, const float* x, const int
     return fail(MOE_ERR_UNSUPPORTED, "channel selection needs k <= 64, k*I <= %d and at most "
                 "%d candidates per workgroup", kCsMaxPerThread * layer->threads, kCsOwnMax);
   if (cs_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k, d.inter, layer->workgroups,
-                   keep) > 160 * 1024)
+                   keep, sketch != nullptr) > 160 * 1024)
     return fail(MOE_ERR_UNSUPPORTED, "k*I=%lld candidates exceed the selection LDS budget", n);
   B1Args a = b1_args(layer, x, ids, w, y ? y : layer->at<float>(layer->L.cs_y));
+  CsSketch sk{};
+  if (sketch) {
+    sk = *sketch;
+    sk.mask = layer->at<uint64_t>(layer->L.sk_mask);
+  }
   hipError_t e = launch_cs(a, layer->at<float>(layer->L.dnorm),
                            layer->at<uint64_t>(layer->L.cs_s), kept, keep, mode, et, st, rt,
                            layer->workgroups, layer->threads, reinterpret_cast<hipStream_t>(stream),
-                           nullptr, sketch);
+                           nullptr, sketch ? &sk : nullptr);
   if (e != hipSuccess) return device_fail(e, "channel-sparse layer launch");
   return ok();
 }
@@ -736,7 +745,8 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
 }
 
 // Sketch buffer layout: codes of G then V [E*I][H/16] uint32, then alpha of G, alpha of V,
-// rho of G, rho of V [E*I][H/128] FP16; each region 256-byte aligned.
+// rho of G, rho of V [E*I][nbp] FP16 (nbp = H/128 rounded up to a multiple of 8); each region
+// 256-byte aligned.
 struct SketchLayout {
   size_t cg, cv, ag, av, rg, rv, total;
 };
@@ -753,10 +763,11 @@ static bool sketch_layout(const moe_layer_desc* d, SketchLayout* S) {
   };
   S->cg = take(rows * (d->hidden / 16) * 4);
   S->cv = take(rows * (d->hidden / 16) * 4);
-  S->ag = take(rows * (d->hidden / 128) * 2);
-  S->av = take(rows * (d->hidden / 128) * 2);
-  S->rg = take(rows * (d->hidden / 128) * 2);
-  S->rv = take(rows * (d->hidden / 128) * 2);
+  const size_t nbp = (size_t)((d->hidden / 128 + 7) & ~7);
+  S->ag = take(rows * nbp * 2);
+  S->av = take(rows * nbp * 2);
+  S->rg = take(rows * nbp * 2);
+  S->rv = take(rows * nbp * 2);
   S->total = o;
   return true;
 }
@@ -787,6 +798,7 @@ moe_status moe_layer_build_sketch(moe_layer layer, const int8_t* signs, void* sk
   sk.ag = reinterpret_cast<const uint16_t*>(base + S.ag);
   sk.av = reinterpret_cast<const uint16_t*>(base + S.av);
   sk.signs = signs;
+  sk.mask = nullptr;  // the layer workspace's, bound at each launch
   const size_t rows = (size_t)d.n_experts * d.inter;
   const DT et = to_dt(d.expert_dtype);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

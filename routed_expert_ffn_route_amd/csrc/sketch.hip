@@ -18,7 +18,8 @@
 // moved rho by an FP16 ulp), so the result is one defined fp32 computation.
 //
 // Layout: codes [rows][H/16] 32-bit words, coordinate i of a row at bits 2 (i % 16) of word
-// i / 16 (0 -> 00, +1 -> 01, -1 -> 11); alpha and rho [rows][H/128] FP16 bits.
+// i / 16 (0 -> 00, +1 -> 01, -1 -> 11); alpha and rho [rows][nbp] FP16 bits, nbp = H/128
+// rounded up to a multiple of 8 (16-byte rows; the padding holds zeros).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void sketch_build_kernel(const void* rows, siz
   // no fused multiply-adds: each product below is rounded on its own, as stated
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & (kWave - 1);
-  const int nb = H / 128;
+  const int nb = H / 128, nbp = (nb + 7) & ~7;
   const size_t task = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (task >= nrows * (size_t)nb) return;  // whole waves leave together
   const size_t r = task / nb;
@@ -102,8 +103,12 @@ __global__ __launch_bounds__(256) void sketch_build_kernel(const void* rows, siz
     crow[4 + (lane >> 4)] = w1;
   }
   if (lane == 0) {
-    alpha[r * nb + b] = __half_as_ushort(a16);
-    rho[r * nb + b] = __half_as_ushort(__float2half_rn(mse));
+    alpha[r * nbp + b] = __half_as_ushort(a16);
+    rho[r * nbp + b] = __half_as_ushort(__float2half_rn(mse));
+  }
+  if (b == 0 && lane >= nb && lane < nbp) {  // the row's padding
+    alpha[r * nbp + lane] = 0;
+    rho[r * nbp + lane] = 0;
   }
 }
 

@@ -32,11 +32,16 @@ def _build(L, wl, layer=0):
     return buf, signs
 
 
+def _nbp(wl):
+    """Row stride of the FP16 scales and rho: H/128 rounded up to a multiple of 8."""
+    return (wl.H // 128 + 7) // 8 * 8
+
+
 def _regions(wl):
     """Byte offsets of the sketch buffer's regions (the header's layout)."""
     rows = wl.E * wl.I
     al = lambda n: (n + 255) // 256 * 256
-    cb, sb = rows * (wl.H // 16) * 4, rows * (wl.H // 128) * 2
+    cb, sb = rows * (wl.H // 16) * 4, rows * _nbp(wl) * 2
     o, offs = 0, []
     for n in (cb, cb, sb, sb, sb, sb):
         offs.append((o, n))
@@ -57,8 +62,11 @@ def _unpack(buf, wl, rows):
         codes = np.where(fields == 3, -1, fields).astype(np.int8).reshape(len(rows), wl.H)
         oa, na = offs[2 + t]
         orr, nr = offs[4 + t]
-        alpha = b[oa:oa + na].view(np.uint16).reshape(wl.E * wl.I, wl.H // 128)[rows]
-        rho = b[orr:orr + nr].view(np.uint16).reshape(wl.E * wl.I, wl.H // 128)[rows]
+        nb = wl.H // 128
+        alpha = b[oa:oa + na].view(np.uint16).reshape(wl.E * wl.I, _nbp(wl))[rows]
+        rho = b[orr:orr + nr].view(np.uint16).reshape(wl.E * wl.I, _nbp(wl))[rows]
+        assert not np.any(alpha[:, nb:]) and not np.any(rho[:, nb:]), "padding not zero"
+        alpha, rho = alpha[:, :nb], rho[:, :nb]
         out.append((codes, alpha, rho))
     return out
 
@@ -149,12 +157,18 @@ def _pick(wl, hl, token, keep, mode, signs_np, sk_cache, layer=0):
     raise RuntimeError("no margin-satisfying draw")
 
 
-def _screen(L, x_np, keep, mode):
+def _screen(L, x_np, keep, mode, ids=None, w=None):
+    """The screened layer on the GPU; with ids and w the routing is given (no router inside:
+    every workgroup scans z itself instead of sharing the scans)."""
     import torch
     x = torch.from_numpy(np.asarray(x_np, dtype=np.float32)).cuda().reshape(1, -1)
     y = torch.empty_like(x)
     kept = torch.full((max(keep, 1),), -1, dtype=torch.int32, device="cuda")
-    L.channel_select(x, keep, kept, y=y, mode=mode, sketch=True)
+    kw = {}
+    if ids is not None:
+        kw = dict(ids=torch.from_numpy(np.asarray(ids, dtype=np.int32)).cuda().reshape(1, -1),
+                  w=torch.from_numpy(np.asarray(w, dtype=np.float32)).cuda().reshape(1, -1))
+    L.channel_select(x, keep, kept, y=y, mode=mode, sketch=True, **kw)
     assert L.check() == 0
     return kept.cpu().numpy()[:keep], y.cpu().numpy()[0]
 
@@ -173,6 +187,26 @@ def test_sketch_screen_small(wl, mode):
         kept_ref, y_ref = S.sketch_select_token(x, ids, w, hl.expert, sketch_of, dnorm_of, keep,
                                                 signs_np, hl.shared, mode)
         kept, y = _screen(L, x, keep, MODES[mode])
+        assert kept.tolist() == kept_ref.tolist(), (tok, keep)
+        assert rel_err(y, y_ref) <= TOL_BF16, (tok, keep, rel_err(y, y_ref))
+
+
+@pytest.mark.parametrize("wl", SMALL[:2], ids=lambda w: f"H{w.H}E{w.E}I{w.I}{w.expert_dtype}")
+def test_sketch_screen_given_routing(wl):
+    """Routing passed in (the oracle's top-k ids and softmax weights): the path where each
+    workgroup scans every block of z itself."""
+    L = _layer(wl)
+    hl = HostLayer(wl)
+    _build(L, wl)
+    signs_np = T.rotation_signs(wl, 0)
+    cache = {}
+    n = wl.k * wl.I
+    for tok, keep in enumerate([1, n // 3 + 1, n - 1]):
+        x, ids, w, dnorm_of, sketch_of = _pick(wl, hl, 40 + tok, keep, "router_weighted",
+                                               signs_np, cache)
+        kept_ref, y_ref = S.sketch_select_token(x, ids, w, hl.expert, sketch_of, dnorm_of, keep,
+                                                signs_np, hl.shared, "router_weighted")
+        kept, y = _screen(L, x, keep, 1, ids=ids, w=w)
         assert kept.tolist() == kept_ref.tolist(), (tok, keep)
         assert rel_err(y, y_ref) <= TOL_BF16, (tok, keep, rel_err(y, y_ref))
 
