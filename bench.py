@@ -641,6 +641,78 @@ def run_linear_sweep(args, wl):
     return lines
 
 
+def run_linear_ek_sweep(args, wl):
+    """The batch-1 linearity sub-sweep over (E, k) ("501B of which 23B are switched on",
+    section 3[A]: batch-1 time against the expert count and top-k): E = 8, 16, 32, 64 and
+    k = 1, 2, 4, 8 linear experts of 8192 x 8192 bf16 (the workload's first E experts), one
+    token routed by iid logits, the MALL flushed before each step.  The time should not depend
+    on E and should grow linearly in k; the last line fits time = a + b k over all points."""
+    import numpy as np
+    import torch
+    import routed_expert_ffn_route_amd as M
+    from synth import tensors as T
+    weights = T.device_layer(wl, 0)  # all 64 experts; a layer of E experts reads the first E
+    flush = torch.zeros(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(512 * 2**20 // 64, dtype=torch.float32, device="cuda")
+
+    def evict(t):
+        sink.copy_(flush.view(-1, 16)[:, 0])
+
+    probe = stream_probe()
+    lines, pts = [], []
+    nsteps = max(4, min(args.steps, 64))
+    for E in (8, 16, 32, 64):
+        for k in (1, 2, 4, 8):
+            desc = M.make_desc(wl.H, E, k, wl.I, kind=M.LINEAR, router_dtype=None,
+                               expert_dtype="bf16", max_batch=1)
+            L = M.Layer(desc, weights)
+            logits = [T.device_logits(wl, [0], case=3 + s)[:, :E].contiguous()
+                      for s in range(4)]
+            x = [T.device_x(wl, [0], case=3 + s) for s in range(4)]
+            ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
+            w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+            y = torch.empty((1, wl.I), dtype=torch.float32, device="cuda")
+
+            def step(t):
+                evict(t)
+                L.route(logits_in=logits[t % 4], ids=ids, w=w)
+                L.forward(x[t % 4], y, ids=ids, w=w)
+
+            for t in range(2):
+                step(t)
+            torch.cuda.synchronize()
+            fl_ms, _ = timed(evict, nsteps, graph_ok=not args.eager)
+            gpu_ms, _ = timed(step, nsteps, graph_ok=not args.eager)
+            assert L.check() == 0
+            step_s = (gpu_ms - fl_ms) / 1e3 / nsteps
+            nbytes = k * wl.H * wl.I * 2
+            pts.append((k, step_s))
+            lines.append({
+                "metric": "linear-expert batch-1 step time", "workload": wl.name,
+                "experts": E, "top_k": k, "us_per_step": round(step_s * 1e6, 2),
+                "bytes_per_step": nbytes, "hbm_gb_s": round(nbytes / step_s / 1e9, 1),
+                "pct_of_probe": round(100 * nbytes / step_s / 1e9 / probe, 2), "steps": nsteps,
+                "note": "MALL flushed before each step (512 MB read, timed separately and "
+                        "subtracted)"})
+            L.close()
+            del L
+    ks = np.array([p[0] for p in pts], dtype=np.float64)
+    ts = np.array([p[1] for p in pts], dtype=np.float64) * 1e6
+    b, a = np.polyfit(ks, ts, 1)
+    resid = ts - (a + b * ks)
+    per_e = {}
+    for (k, t), line in zip(pts, lines):
+        per_e.setdefault(k, []).append(t * 1e6)
+    lines.append({
+        "metric": "linear-expert batch-1 linearity fit", "workload": wl.name,
+        "fit": "us = a + b * k over E in (8, 16, 32, 64), k in (1, 2, 4, 8)",
+        "a_us": round(float(a), 2), "b_us_per_expert": round(float(b), 2),
+        "max_abs_residual_us": round(float(np.max(np.abs(resid))), 2),
+        "spread_over_E_us": {str(k): round(max(v) - min(v), 2) for k, v in per_e.items()},
+        "bytes_per_expert": wl.H * wl.I * 2, "probe_gb_s": round(probe, 1)})
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -658,6 +730,8 @@ def main():
     ap.add_argument("--batch", type=int, default=1,
                     help="SwiGLU stacks: tokens per step (B > 1 runs the batched layer)")
     ap.add_argument("--eager", action="store_true", help="launch without a HIP graph")
+    ap.add_argument("--sweep-ek", action="store_true",
+                    help="linear workload: the batch-1 (E, k) linearity sub-sweep")
     ap.add_argument("--timeline", action="store_true",
                     help="batch-1 stacks: per-phase timeline from the timeline build of the "
                          "library (libmoe_ffn_timeline.so) instead of the throughput line")
@@ -694,7 +768,8 @@ def main():
     if args.layers:
         wl = T.reduced(wl, layers=args.layers)
     if wl.kind == "linear":
-        for line in run_linear_sweep(args, wl):
+        run = run_linear_ek_sweep if args.sweep_ek else run_linear_sweep
+        for line in run(args, wl):
             print(json.dumps(line), flush=True)
         return
     if args.batch > 1:
