@@ -354,6 +354,105 @@ def run_stack(args, wl, keep=None):
     return out
 
 
+def run_threshold(args, wl):
+    """The threshold keep rule through the 40-layer stack ("Background: channels and keep
+    rules" and the calibration discussion of the reader review).  Per layer, tau is
+    calibrated so that a fraction `--threshold` of the pooled exact scores of 16 calibration
+    tokens is at or above it (the scores read back with moe_layer_scores); then held-out
+    tokens are timed, and the per-token kept fraction is reported for them and for a shifted
+    set (the same tokens with x scaled by 0.8: smaller activations, smaller scores -- a
+    synthetic stand-in for the review's chat-to-benchmark shift)."""
+    import numpy as np
+    import torch
+    import routed_expert_ffn_route_amd as M
+    from synth import tensors as T
+    frac = args.threshold
+    n = wl.k * wl.I
+    ncal = 16
+    ntok = min(wl.tokens - ncal, max(args.steps, 1))
+    desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, wl.n_shared, wl.I_shared,
+                       router_dtype=wl.router_dtype, expert_dtype=wl.expert_dtype,
+                       shared_dtype=wl.shared_dtype, max_batch=1)
+    layers, xs, ys, taus = [], [], [], []
+    kept = torch.empty(n, dtype=torch.int32, device="cuda")
+    sc = torch.empty(n, dtype=torch.float32, device="cuda")
+    K0 = int(np.floor(frac * n + 0.5))
+    for l in range(wl.layers):
+        L = M.Layer(desc, T.device_layer(wl, l))
+        layers.append(L)
+        xcal = T.device_x(wl, list(range(ncal)), l)
+        pooled = []
+        for t in range(ncal):  # calibration tokens 0 .. 15
+            L.channel_select(xcal[t:t + 1], K0, kept, mode=1)
+            L.scores(sc)
+            pooled.append(sc.cpu().numpy().astype(np.float64))
+        pooled = np.sort(np.concatenate(pooled))[::-1]
+        taus.append(float(pooled[int(np.floor(frac * pooled.size + 0.5)) - 1]))
+        xs.append(T.device_x(wl, list(range(ncal, ncal + ntok)), l))  # held-out tokens
+        ys.append(torch.empty_like(xs[-1]))
+    torch.cuda.synchronize()
+    counts = torch.zeros((2, ntok, wl.layers), dtype=torch.int32, device="cuda")
+    kepts = torch.empty((wl.layers, n), dtype=torch.int32, device="cuda")
+
+    def step_on(xsrc, which):
+        def step(t):
+            tt = t % ntok
+            for l in range(wl.layers):
+                layers[l].channel_select_threshold(xsrc[l][tt:tt + 1], taus[l], kepts[l],
+                                                   counts[which, tt, l:l + 1],
+                                                   y=ys[l][tt:tt + 1], mode=1)
+        return step
+
+    step = step_on(xs, 0)
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    K = ntok
+    gpu_ms, wall_ms = timed(step, K, graph_ok=not args.eager)
+    for L in layers:
+        assert L.check() == 0, "device error word set"
+    shifted = [0.8 * x for x in xs]
+    sstep = step_on(shifted, 1)
+    for t in range(ntok):
+        sstep(t)
+    torch.cuda.synchronize()
+    for L in layers:
+        assert L.check() == 0, "device error word set"
+    c = counts.cpu().numpy().astype(np.float64) / n
+
+    def dist(a):
+        a = a.ravel()
+        return {"mean": round(float(a.mean()), 4), "min": round(float(a.min()), 4),
+                "p5": round(float(np.percentile(a, 5)), 4),
+                "p50": round(float(np.percentile(a, 50)), 4),
+                "p95": round(float(np.percentile(a, 95)), 4), "max": round(float(a.max()), 4)}
+
+    mean_kept = float(c[0].mean()) * n
+    bytes_layer = layer_weight_bytes(wl, keep=mean_kept)
+    per_launch_s = gpu_ms / 1e3 / (K * wl.layers)
+    achieved = bytes_layer / per_launch_s / 1e9
+    return {
+        "metric": METRIC, "value": round(K / (gpu_ms / 1e3), 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(gpu_ms / K, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "batch": 1,
+                   "keep_rule": "threshold", "calibrated_fraction": frac,
+                   "calibration_tokens": ncal, "score": "router-weighted, exact gates",
+                   "graph": not args.eager},
+        "kept_fraction_held_out": dist(c[0]),
+        "kept_fraction_shifted_x0.8": dist(c[1]),
+        "tau_per_layer_first4": [round(t, 6) for t in taus[:4]],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "cs_kernel (one launch per layer)",
+                     "bytes_per_launch": bytes_layer,
+                     "us_per_launch": round(per_launch_s * 1e6, 3),
+                     "kernel_hash": kernel_hash("cs")},
+        "cpu_baseline": None,
+    }
+
+
 PHASES = {
     "b1": {0: "start", 1: "router rows published", 2: "shared experts streamed",
            3: "routing known (top-k + softmax)", 4: "routed stream done",
@@ -735,6 +834,9 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="batch-1 stacks: per-phase timeline from the timeline build of the "
                          "library (libmoe_ffn_timeline.so) instead of the throughput line")
+    ap.add_argument("--threshold", type=float, default=0.0, metavar="FRAC",
+                    help="sparse workload: the threshold keep rule, tau calibrated per layer "
+                         "to keep FRAC of the calibration tokens' candidates")
     ap.add_argument("--sketch", action="store_true",
                     help="channel-sparse workload: score channels from the ternary sketch "
                          "(moe_channel_select_sketch, eq.-1 scores) instead of exact gates")
@@ -778,6 +880,11 @@ def main():
     keep = None
     if wl.keep_fracs:
         keep = args.keep if args.keep >= 0 else wl.keep_counts()[0]
+    if args.threshold > 0:
+        if not wl.keep_fracs:
+            raise SystemExit("--threshold needs the channel-sparse workload")
+        print(json.dumps(run_threshold(args, wl)), flush=True)
+        return
     if args.timeline:
         print(json.dumps(run_timeline(args, wl, keep)), flush=True)
         return

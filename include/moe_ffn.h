@@ -152,6 +152,26 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
                               const float* w, int32_t keep, int32_t mode, int32_t* kept,
                               float* y, void* stream);
 
+/* The channel-sparse layer under the threshold keep rule (the review's section "Background:
+ * channels and keep rules", the rule of its first row, and the calibration discussion that
+ * follows it): every candidate whose score (the same exact output-unit score as
+ * moe_channel_select, mode as there) is at least `tau` is kept, so the number kept -- and the
+ * bytes read -- vary per token.  A tau at or below 0 keeps every candidate; NaN is rejected.
+ * kept [k*I] receives the kept ids ascending (e*I + j), kept_count [1] (device int32) their
+ * number; both must be given.  y [H] (may be NULL).  ids/w as for moe_channel_select.  Each
+ * workgroup streams its own kept channels as soon as its own scores are known (no global
+ * selection). */
+moe_status moe_channel_select_threshold(moe_layer layer, const float* x, const int32_t* ids,
+                                        const float* w, float tau, int32_t mode, int32_t* kept,
+                                        int32_t* kept_count, float* y, void* stream);
+
+/* The k*I channel scores of the layer's last moe_channel_select(_threshold, _sketch) call,
+ * read back (for calibrating tau): enqueues on `stream` a copy into scores [k*I] (fp32,
+ * device) in candidate order, slot-major: slot s (the routing order of moe_layer_routing)
+ * times I plus channel j.  The lowest mantissa bit of each score is cleared (inside the call it
+ * carries the launch parity). */
+moe_status moe_layer_scores(moe_layer layer, float* scores, void* stream);
+
 /* The ternary-sketch channel screen (the review of arXiv:2610.37386, "The weights-only
  * reader", stages 1 and 2).  Load time, once: every routed channel's gate row and up row is
  * rotated in blocks of 128 coordinates by a randomized Hadamard transform (unnormalized:

@@ -250,6 +250,41 @@ def channel_select_token(x, ids, w, get_expert, dnorm_of, keep, shared=(),
     return np.sort(cid[order]), y
 
 
+def channel_select_threshold_token(x, ids, w, get_expert, dnorm_of, tau, shared=(),
+                                   mode="gate_dnorm"):
+    """Threshold keep rule over the k*I candidates of one token [Reader, "Background: channels
+    and keep rules", the first row of its table: every channel whose score is at least tau
+    passes, so the number kept -- and the bytes read -- change from token to token].  The same
+    scores and the same exact computation of the kept channels as channel_select_token.
+    Returns (kept channel ids e*I + j ascending, y [H])."""
+    x = np.asarray(x, dtype=np.float64).reshape(-1)
+    s, g = channel_scores(x, ids, w, get_expert, dnorm_of, mode)
+    k, I = s.shape
+    cid = (np.asarray(ids, dtype=np.int64)[:, None] * I + np.arange(I)[None, :]).reshape(-1)
+    keep = np.nonzero(s.reshape(-1) >= tau)[0]
+    y = np.zeros_like(x)
+    for f in keep:
+        i, j = divmod(int(f), I)
+        _, V, Dt = get_expert(int(ids[i]))
+        a = silu(g[i, j]) * float(to_f64(_row(V, j)).reshape(-1) @ x)
+        y += w[i] * a * to_f64(_row(Dt, j)).reshape(-1)
+    for (gs, us, ds) in shared:
+        y += expert_output(x, gs, us, ds)
+    return np.sort(cid[keep]), y
+
+
+def calibrate_tau(score_sets, frac):
+    """The threshold calibrated on a set of tokens [Reader, calibration discussion: tau is set
+    on calibration data so that the kept fraction meets the budget on average]: the m-th
+    largest of the pooled scores of all calibration tokens, m = round(frac * total) (half up),
+    so that (with distinct scores) exactly m pooled candidates score at or above it.  Returns
+    +inf when m = 0."""
+    pooled = np.sort(np.concatenate([np.ravel(np.asarray(t, dtype=np.float64))
+                                     for t in score_sets]))[::-1]
+    m = int(np.floor(frac * pooled.size + 0.5))
+    return float(pooled[m - 1]) if m > 0 else float("inf")
+
+
 def _row(t, j):
     """Row j of a stored [I, H] tensor, keeping its storage form."""
     if isinstance(t, tuple):

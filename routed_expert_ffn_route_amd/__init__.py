@@ -27,7 +27,7 @@ EXPORTS = (
     "moe_layer_workspace_bytes", "moe_layer_create", "moe_layer_destroy", "moe_route",
     "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_channel_select", "moe_union_experts",
     "moe_layer_routing", "moe_sketch_bytes", "moe_layer_build_sketch",
-    "moe_channel_select_sketch",
+    "moe_channel_select_sketch", "moe_channel_select_threshold", "moe_layer_scores",
     "moe_layer_check", "moe_layer_geometry", "moe_status_string", "moe_last_error",
 )
 # The phase-timeline build (libmoe_ffn_timeline.so) exports one more, for measurement only.
@@ -103,6 +103,11 @@ def lib():
         L.moe_layer_build_sketch.argtypes = [vp, vp, vp, sz, vp]
         L.moe_channel_select_sketch.restype = i32
         L.moe_channel_select_sketch.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp]
+        L.moe_channel_select_threshold.restype = i32
+        L.moe_channel_select_threshold.argtypes = [vp, vp, vp, vp, ctypes.c_float, i32, vp, vp,
+                                                   vp, vp]
+        L.moe_layer_scores.restype = i32
+        L.moe_layer_scores.argtypes = [vp, vp, vp]
         L.moe_layer_check.restype = i32
         L.moe_layer_check.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.moe_layer_geometry.restype = i32
@@ -272,6 +277,30 @@ class Layer:
         fn = lib().moe_channel_select_sketch if sketch else lib().moe_channel_select
         _check(fn(self.handle, _ptr(x), _ptr(ids), _ptr(w), keep, mode, _ptr(kept), _ptr(y),
                   _stream(stream)))
+
+    def channel_select_threshold(self, x, tau, kept, kept_count, y=None, ids=None, w=None,
+                                 mode=SCORE_GATE_DNORM, stream=None):
+        """moe_channel_select_threshold: keep every candidate scoring at least tau."""
+        import torch
+        d = self.desc
+        _need(x, "x", torch.float32, min_numel=d.hidden)
+        _need(kept, "kept", torch.int32, min_numel=d.top_k * d.inter)
+        _need(kept_count, "kept_count", torch.int32, min_numel=1)
+        if y is not None:
+            _need(y, "y", torch.float32, min_numel=d.hidden)
+        if ids is not None:
+            _need(ids, "ids", torch.int32, min_numel=d.top_k)
+        if w is not None:
+            _need(w, "w", torch.float32, min_numel=d.top_k)
+        _check(lib().moe_channel_select_threshold(self.handle, _ptr(x), _ptr(ids), _ptr(w),
+                                                  float(tau), mode, _ptr(kept),
+                                                  _ptr(kept_count), _ptr(y), _stream(stream)))
+
+    def scores(self, out, stream=None):
+        """moe_layer_scores: the last channel-selection call's k*I scores, slot-major."""
+        import torch
+        _need(out, "scores", torch.float32, min_numel=self.desc.top_k * self.desc.inter)
+        _check(lib().moe_layer_scores(self.handle, _ptr(out), _stream(stream)))
 
     def routing(self, ids, w, B=1, stream=None):
         """Copy the routing the last call used into ids, w [B][k] (moe_layer_routing)."""

@@ -60,8 +60,10 @@ struct CSLaunch {
   const int8_t* signs;
   uint64_t* sk_mask;   // launch-tagged scan masks, one copy per XCD (kSkMaskWords each)
   uint64_t* g_ws;      // channel scores with the launch parity, one copy per XCD
-  int32_t* kept_out;   // [K]
-  int K, mode, R, SW, tsz;
+  int32_t* kept_out;   // [K] ([k*I] under the threshold rule)
+  int32_t* kept_count; // (threshold rule) how many were kept
+  uint32_t tau;        // (threshold rule) the score threshold's bit pattern (non-negative)
+  int K, mode, R, SW, tsz, thr;
 };
 
 // Exclusive prefix sum over the workgroup (sh: LDS of nwaves+1 ints).  *total = sum.
@@ -933,7 +935,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   const bool mine = c0 < n;
   const int sl0 = mine ? divI.div(c0) : 0, j0 = c0 - sl0 * I;
   uint32_t sb[kCh];
-  {
+  auto gather = [&] {
     const rsrc_t gsrc = make_rsrc(scores + (size_t)(c.wg % kPollCopies) * npad, (uint32_t)n * 4u);
     u32x4 w4[2];
 #pragma unroll
@@ -982,17 +984,29 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
       sh[20 + (c.tid >> 6)] = (int)hi;
     }
     if (c.tid == 0) sh[44] = 0;
+      __syncthreads();
+  };
+  // (threshold rule: a workgroup's own kept channels follow from its own scores, so only
+  // workgroup 0 gathers them, after its partial output is out, for the kept list)
+  const bool thr = L.thr != 0;
+  if (!thr) {
+    gather();
+    MOE_STAMP(c.stamps, 5);
+    warm_kept();  // its loads land in L2 during the selection, which issues no memory loads
   }
-  __syncthreads();
-  MOE_STAMP(c.stamps, 5);
-  warm_kept();  // its loads land in L2 during the selection, which issues no memory loads
 
   // 6. the threshold: T = the K-th largest score (all kept when K >= n, none when K = 0), how
-  // many of the scores equal to T are kept (need) and how many there are (ties)
+  // many of the scores equal to T are kept (need) and how many there are (ties); under the
+  // threshold rule T = tau and every score at or above it is kept
   uint32_t T = 0u;
   int need = 0, ties = 0;
-  if (L.K > 0 && L.K < n) T = select_kth(sv, sb, mine, n, L.K, &need, &ties, hist, mem, sh, c);
-  const bool all = L.K >= n, none = L.K == 0;
+  if (thr) {
+    T = L.tau;
+    need = ties = n;
+  } else if (L.K > 0 && L.K < n) {
+    T = select_kth(sv, sb, mine, n, L.K, &need, &ties, hist, mem, sh, c);
+  }
+  const bool all = !thr && L.K >= n, none = !thr && L.K == 0;
   MOE_STAMP(c.stamps, 6);
   // this workgroup's own kept candidates: above T, or at T when every tie is kept; when only
   // some ties are (equal scores straddling the K-th place), the lowest e*I + j of them, which
@@ -1090,8 +1104,9 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
   // 9. workgroup 0 (not a reducer) writes the kept list after its partial output is out: every
   // kept candidate's id e*I + j at its place in ascending order (-1 for a skipped given id),
   // and the threshold as the next launch's prefetch hint
-  if (c.wg == 0 && !none && L.K > 0) {
+  if (c.wg == 0 && (thr || (!none && L.K > 0))) {
     __syncthreads();
+    if (thr) gather();
     uint32_t sb2[kCh];
 #pragma unroll
     for (int i = 0; i < kCh; ++i) sb2[i] = mine ? sv[c0 + i] : 0u;
@@ -1102,7 +1117,12 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
 #pragma unroll
     for (int i = 0; i < kCh; ++i)
       if ((m >> i) & 1u) L.kept_out[pos[i]] = e0 >= 0 ? e0 * I + j0 + i : -1;
-    if (c.tid == 0 && !all) store_relaxed_dev(&ctrl->cs_tprev, T);
+    if (thr) {  // how many the threshold kept
+      int tot;
+      (void)block_excl_scan(__popc(m), sh + 48, c, &tot);
+      if (c.tid == 0) *L.kept_count = tot;
+    }
+    if (c.tid == 0 && !all && !thr) store_relaxed_dev(&ctrl->cs_tprev, T);
   }
   s_int[15] = (int)(warm[0] ^ warm[1] ^ warm2[0][0] ^ warm2[0][1] ^ warm2[1][0] ^
                     warm2[1][1]);  // keeps the warming loads
@@ -1162,7 +1182,7 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K, bool s
 
 hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_t* kept, int K,
                      int mode, DT et, DT st, DT rt, int wgs, int threads, hipStream_t s,
-                     int* occ, const CsSketch* sketch) {
+                     int* occ, const CsSketch* sketch, const CsThreshold* thr) {
   // the selection's bin scan holds at most four bins per thread
   const long long n = (long long)a.k * a.I;
   if (a.k > kMaxSlots || n > (long long)kCh * threads || a.I % kCh != 0 ||
@@ -1175,6 +1195,10 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_
   L.kept_out = kept;
   L.K = K;
   L.mode = mode;
+  L.thr = thr != nullptr;
+  L.tau = thr ? thr->tau_bits : 0u;
+  L.kept_count = thr ? thr->count : nullptr;
+  if (thr && (sketch || !kept || !thr->count)) return hipErrorInvalidValue;
   L.tsz = team_size(a.H);
   L.sk_g = L.sk_v = nullptr;
   L.sk_ag = L.sk_av = nullptr;

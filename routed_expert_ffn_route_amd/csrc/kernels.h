@@ -54,9 +54,16 @@ struct CsSketch {
   uint64_t* mask;           // workspace: launch-tagged scan masks, kPollCopies x kSkMaskWords
 };
 constexpr int kSkMaskWords = 128;  // words per copy: 4 per 128-block, H <= 4096
+// The threshold keep rule: every candidate whose score pattern is at least tau_bits is kept;
+// their number goes to count (device).
+struct CsThreshold {
+  uint32_t tau_bits;
+  int32_t* count;
+};
 hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_t* kept,
                      int K, int mode, DT et, DT st, DT rt, int workgroups, int threads,
-                     hipStream_t s, int* occupancy = nullptr, const CsSketch* sketch = nullptr);
+                     hipStream_t s, int* occupancy = nullptr, const CsSketch* sketch = nullptr,
+                     const CsThreshold* thr = nullptr);
 // Ternary sketch of nrows rows of H (H % 128 == 0, BF16 or F32): codes [nrows][H/16],
 // alpha and rho [nrows][H/128] (FP16 bits), with the rotation signs [H].
 hipError_t launch_sketch_build(const void* rows, DT dt, size_t nrows, int H,

@@ -698,12 +698,17 @@ moe_status moe_ffn_forward_noalloc(const moe_layer_desc* desc, const moe_weights
 
 static moe_status channel_select_impl(moe_layer layer, const float* x, const int32_t* ids,
                                       const float* w, int32_t keep, int32_t mode, int32_t* kept,
-                                      float* y, void* stream, const CsSketch* sketch) {
+                                      float* y, void* stream, const CsSketch* sketch,
+                                      const CsThreshold* thr = nullptr) {
   const moe_layer_desc& d = layer->d;
   if (d.kind != MOE_EXPERT_SWIGLU) return fail(MOE_ERR_ARG, "channel selection needs SWIGLU experts");
   if (!x || !aligned16(x)) return fail(MOE_ERR_ARG, "x must be given and 16-byte aligned");
   if (y && !aligned16(y)) return fail(MOE_ERR_ARG, "y must be 16-byte aligned");
   const long long n = (long long)d.top_k * d.inter;
+  if (thr) {
+    if (!kept || !thr->count) return fail(MOE_ERR_ARG, "kept and kept_count must be given");
+    keep = (int32_t)n;  // (the kept list's capacity)
+  }
   if (keep < 0 || keep > n) return fail(MOE_ERR_ARG, "keep=%d outside [0, k*I=%lld]", keep, n);
   if (keep > 0 && !kept) return fail(MOE_ERR_ARG, "kept must be given when keep > 0");
   if (mode != MOE_SCORE_GATE_DNORM && mode != MOE_SCORE_ROUTER_WEIGHTED)
@@ -732,7 +737,7 @@ static moe_status channel_select_impl(moe_layer layer, const float* x, const int
   hipError_t e = launch_cs(a, layer->at<float>(layer->L.dnorm),
                            layer->at<uint64_t>(layer->L.cs_s), kept, keep, mode, et, st, rt,
                            layer->workgroups, layer->threads, reinterpret_cast<hipStream_t>(stream),
-                           nullptr, sketch ? &sk : nullptr);
+                           nullptr, sketch ? &sk : nullptr, thr);
   if (e != hipSuccess) return device_fail(e, "channel-sparse layer launch");
   return ok();
 }
@@ -742,6 +747,39 @@ moe_status moe_channel_select(moe_layer layer, const float* x, const int32_t* id
                               float* y, void* stream) {
   if (moe_status st = check_layer(layer)) return st;
   return channel_select_impl(layer, x, ids, w, keep, mode, kept, y, stream, nullptr);
+}
+
+moe_status moe_channel_select_threshold(moe_layer layer, const float* x, const int32_t* ids,
+                                        const float* w, float tau, int32_t mode, int32_t* kept,
+                                        int32_t* kept_count, float* y, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  if (!(tau == tau)) return fail(MOE_ERR_ARG, "tau is NaN");
+  // scores are non-negative: their bit patterns order like the values, and a tau at or below
+  // zero keeps every candidate
+  uint32_t bits;
+  const float t = tau > 0.0f ? tau : 0.0f;
+  memcpy(&bits, &t, 4);
+  CsThreshold thr{bits, kept_count};
+  return channel_select_impl(layer, x, ids, w, 0, mode, kept, y, stream, nullptr, &thr);
+}
+
+__global__ void scores_copy_kernel(const uint32_t* src, float* dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = __uint_as_float(src[i] & ~1u);
+}
+
+moe_status moe_layer_scores(moe_layer layer, float* scores, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const moe_layer_desc& d = layer->d;
+  if (d.kind != MOE_EXPERT_SWIGLU) return fail(MOE_ERR_ARG, "channel scores need SWIGLU experts");
+  if (!scores) return fail(MOE_ERR_ARG, "scores must be given");
+  const int n = d.top_k * d.inter;
+  hipLaunchKernelGGL(scores_copy_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream),
+                     layer->at<uint32_t>(layer->L.cs_s), scores, n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return device_fail(e, "moe_layer_scores copy");
+  return ok();
 }
 
 // Sketch buffer layout: codes of G then V [E*I][H/16] uint32, then alpha of G, alpha of V,
