@@ -46,7 +46,7 @@ def kernel_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def layer_weight_bytes(wl, keep=None, n_read=None, sketch=False) -> float:
+def layer_weight_bytes(wl, keep=None, n_read=None, sketch=False, recover=False) -> float:
     """Algorithmic weight bytes one token (or one batch step) reads in one layer: the router,
     the routed experts (k of them; n_read for a batch: the touched ones) and the shared
     experts, 3 matrices of H x I each (linear experts: one matrix, no router).  With a keep
@@ -65,6 +65,8 @@ def layer_weight_bytes(wl, keep=None, n_read=None, sketch=False) -> float:
         # 128-block), then the kept channels' full gate, up and down rows, and the norms
         routed = (wl.k * wl.I * 2 * (wl.H // 128) * (32 + 2) + 3 * keep * wl.H * be +
                   4 * wl.k * wl.I)
+        if recover:  # (reader) b_j of every dropped candidate (32 FP16) and U (H x 32 fp32)
+            routed += (wl.k * wl.I - keep) * 32 * 2 + wl.H * 32 * 4
     else:
         routed = wl.k * wl.I * wl.H * be + 2 * keep * wl.H * be + 4 * wl.k * wl.I
     return routed + wl.n_shared * 3 * wl.H * wl.I_shared * bs + wl.E * wl.H * br
@@ -280,6 +282,8 @@ def run_stack(args, wl, keep=None):
             kepts.append(torch.empty((ntok, max(keep, 1)), dtype=torch.int32, device="cuda"))
         if args.sketch:
             layers[-1].build_sketch(torch.from_numpy(T.rotation_signs(wl, l)).cuda())
+        if args.recover:
+            layers[-1].build_recovery(recovery_basis_device(layers[-1].tensors["down_t"], wl))
     torch.cuda.synchronize()
     print(f"# {wl.name}: generated {wl.layers} layers in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
@@ -292,7 +296,7 @@ def run_stack(args, wl, keep=None):
             else:
                 layers[l].channel_select(xs[l][tt:tt + 1], keep, kepts[l][tt],
                                          y=ys[l][tt:tt + 1], sketch=args.sketch,
-                                         mode=1 if args.sketch else 0)
+                                         reader=args.recover, mode=1 if args.sketch else 0)
 
     for t in range(args.warmup):
         step(t)
@@ -305,7 +309,7 @@ def run_stack(args, wl, keep=None):
         assert L.check() == 0, "device error word set"
     launches = K * wl.layers
     per_launch_s = gpu_ms / 1e3 / launches
-    bytes_layer = layer_weight_bytes(wl, keep=keep, sketch=args.sketch)
+    bytes_layer = layer_weight_bytes(wl, keep=keep, sketch=args.sketch, recover=args.recover)
     achieved = bytes_layer / per_launch_s / 1e9
     kind = "b1" if keep is None else "cs"
     khash = kernel_hash(kind)
@@ -327,7 +331,9 @@ def run_stack(args, wl, keep=None):
         "config": {"workload": wl.name, "layers": wl.layers, "hidden": wl.H, "experts": wl.E,
                    "top_k": wl.k, "inter": wl.I, "shared": wl.n_shared,
                    "weights": wl.expert_dtype, "batch": 1, "keep": keep,
-                   "screen": ("ternary sketch, eq. 1" if args.sketch else
+                   "screen": ("ternary sketch, eq. 1, rank-32 recovery (eq. 2)"
+                              if args.recover else
+                              "ternary sketch, eq. 1" if args.sketch else
                               "exact gates" if keep is not None else None),
                    "graph": not args.eager},
         "hbm_gb_s": round(achieved, 1),
@@ -352,6 +358,20 @@ def run_stack(args, wl, keep=None):
         cb["token0_max_rel_err_vs_oracle"] = worst
         out["cpu_baseline"] = cb
     return out
+
+
+def recovery_basis_device(down_t, wl, rank=32):
+    """U [H][rank] for a layer (load-time preparation, outside any timed region): the top
+    eigenvectors of sum_j d_j d_j^T over its stacked down columns, by torch on the GPU."""
+    import torch
+    D = down_t.view(torch.bfloat16).reshape(-1, wl.H) if down_t.dtype != torch.float32 else \
+        down_t.reshape(-1, wl.H)
+    G = torch.zeros((wl.H, wl.H), dtype=torch.float64, device=down_t.device)
+    for i in range(0, D.shape[0], 16384):
+        blk = D[i:i + 16384].to(torch.float32)
+        G += (blk.T @ blk).to(torch.float64)
+    vals, vecs = torch.linalg.eigh(G)
+    return vecs[:, -rank:].flip(1).to(torch.float32).contiguous()
 
 
 def run_threshold(args, wl):
@@ -837,6 +857,8 @@ def main():
     ap.add_argument("--threshold", type=float, default=0.0, metavar="FRAC",
                     help="sparse workload: the threshold keep rule, tau calibrated per layer "
                          "to keep FRAC of the calibration tokens' candidates")
+    ap.add_argument("--recover", action="store_true",
+                    help="with --sketch: the reader's rank-32 recovery of the dropped channels")
     ap.add_argument("--sketch", action="store_true",
                     help="channel-sparse workload: score channels from the ternary sketch "
                          "(moe_channel_select_sketch, eq.-1 scores) instead of exact gates")

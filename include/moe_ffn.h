@@ -207,6 +207,32 @@ moe_status moe_channel_select_sketch(moe_layer layer, const float* x, const int3
                                      const float* w, int32_t keep, int32_t mode, int32_t* kept,
                                      float* y, void* stream);
 
+/* The reader's stage 3 (the review's "The weights-only reader", stage 3, eq. 2): the
+ * dropped channels S are added back through a rank-32 map, y^ = sum_K w_j d_j a_j +
+ * U sum_S w_j b_j p_j, with U [H][32] the top-32 left singular vectors of the layer's stacked
+ * down columns d_j, b_j = U^T d_j per routed channel, and p_j = silu(g^_j) v^_j the screen's
+ * own activation estimates (no further reads of gate or up rows).
+ *
+ * moe_recovery_bytes: bytes of a layer's recovery buffer (0 if it has no sketch form). Host
+ * only.  Layout: U [H][32] fp32, then b [E*I][32] FP16, each 256-byte aligned.
+ *
+ * moe_layer_build_recovery: U [H][rank] (fp32 device memory, 4-byte aligned, computed by the
+ * caller; rank must be 32) is copied into the caller's buffer `rec` (256-byte aligned, at
+ * least moe_recovery_bytes), b_j = U^T d_j is computed there (fp32 sums, stored FP16), and the
+ * buffer is bound to the layer (it must outlive it).  Enqueues on `stream`.
+ *
+ * moe_channel_select_reader: moe_channel_select_sketch (the same arguments and kept list)
+ * with the dropped channels recovered into y [H] (NULL: the workspace's output row); needs
+ * moe_layer_build_sketch and moe_layer_build_recovery.  Two launches on `stream`: the
+ * screen, which also leaves each workgroup's sum over its dropped candidates of w_e b_j p_j
+ * in the workspace, then y += U times their total. */
+size_t moe_recovery_bytes(const moe_layer_desc* desc);
+moe_status moe_layer_build_recovery(moe_layer layer, const float* U, int32_t rank, void* rec,
+                                    size_t rec_bytes, void* stream);
+moe_status moe_channel_select_reader(moe_layer layer, const float* x, const int32_t* ids,
+                                     const float* w, int32_t keep, int32_t mode, int32_t* kept,
+                                     float* y, void* stream);
+
 /* Touched-expert union of a batch (the "experts touched by a batch" count of the
  * 501B/23B post, section 2).  ids [B][k] with distinct experts per token, 0 <= id < E.
  * Writes n_touched [1], touched [E] (ascending; first n_touched valid), offsets [E+1]

@@ -196,6 +196,62 @@ def sketch_select_token(x, ids, w, get_expert, sketch_of, dnorm_of, keep, signs,
     return np.sort(cid[order]), y
 
 
+# ------------------------------------------------------------------ stage 3: recovery
+RANK = 32
+
+
+def recovery_basis(down_rows_iter, H, rank=RANK):
+    """U [H][rank]: the top-`rank` left singular vectors of the layer's stacked down columns
+    d_j (every routed channel of every expert), as eigenvectors of sum_j d_j d_j^T (fp64),
+    largest eigenvalue first; each column's sign fixed so that its largest-magnitude entry is
+    positive.  `down_rows_iter` yields [rows][H] blocks of d_j (any storage form)."""
+    G = np.zeros((H, H), dtype=np.float64)
+    for blk in down_rows_iter:
+        D = to_f64(blk).reshape(-1, H)
+        G += D.T @ D
+    vals, vecs = np.linalg.eigh(G)
+    U = vecs[:, ::-1][:, :rank].copy()
+    for c in range(U.shape[1]):
+        i = int(np.argmax(np.abs(U[:, c])))
+        if U[i, c] < 0:
+            U[:, c] = -U[:, c]
+    return U
+
+
+def recovery_coeffs(down_t, U):
+    """b_j = U^T d_j for the rows of one expert's D^T [I][H] -> [I][rank] (fp64)."""
+    return to_f64(down_t).reshape(-1, U.shape[0]) @ U
+
+
+def reader_token(x, ids, w, get_expert, sketch_of, dnorm_of, keep, signs, U, coeffs_of,
+                 shared=(), mode="router_weighted", scan=SCAN, p_exact=False):
+    """The reader for one token (stages 1-3, eq. 2): the screen of sketch_select_token, then
+    the dropped channels S added through the rank-r map: y^ = sum_K w_j d_j a_j
+    + U sum_S w_j b_j p_j, with p_j = silu(g^_j) v^_j the screen's own activation estimates
+    (p_exact: the exact a_j instead, for pins).  coeffs_of(e) -> b [I][rank] of expert e.
+    Returns (kept ids ascending, y [H])."""
+    x64 = np.asarray(x, dtype=np.float64).reshape(-1)
+    kept, y = sketch_select_token(x, ids, w, get_expert, sketch_of, dnorm_of, keep, signs,
+                                  shared, mode, scan)
+    _, gh, vh = sketch_scores(x, ids, w, sketch_of, dnorm_of, signs, mode, scan)
+    k, I = gh.shape
+    keptset = set(int(c) for c in kept)
+    r = np.zeros(U.shape[1], dtype=np.float64)
+    for i, e in enumerate(ids):
+        b = coeffs_of(int(e))
+        for j in range(I):
+            if int(e) * I + j in keptset:
+                continue
+            if p_exact:
+                G, V, _ = get_expert(int(e))
+                p = silu(float(to_f64(_row(G, j)).reshape(-1) @ x64)) * \
+                    float(to_f64(_row(V, j)).reshape(-1) @ x64)
+            else:
+                p = silu(gh[i, j]) * vh[i, j]
+            r += w[i] * p * b[j]
+    return kept, y + U @ r
+
+
 def sketch_bytes(H, I, k, keep, b_e=2.0, scan=SCAN):
     """Bytes one token reads in the screen of one layer's routed experts: the sketch of every
     candidate's gate and up rows (2-bit codes, all coordinates of a block lie in its 32 code

@@ -28,6 +28,7 @@ EXPORTS = (
     "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_channel_select", "moe_union_experts",
     "moe_layer_routing", "moe_sketch_bytes", "moe_layer_build_sketch",
     "moe_channel_select_sketch", "moe_channel_select_threshold", "moe_layer_scores",
+    "moe_recovery_bytes", "moe_layer_build_recovery", "moe_channel_select_reader",
     "moe_layer_check", "moe_layer_geometry", "moe_status_string", "moe_last_error",
 )
 # The phase-timeline build (libmoe_ffn_timeline.so) exports one more, for measurement only.
@@ -108,6 +109,12 @@ def lib():
                                                    vp, vp]
         L.moe_layer_scores.restype = i32
         L.moe_layer_scores.argtypes = [vp, vp, vp]
+        L.moe_recovery_bytes.restype = sz
+        L.moe_recovery_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
+        L.moe_layer_build_recovery.restype = i32
+        L.moe_layer_build_recovery.argtypes = [vp, vp, i32, vp, sz, vp]
+        L.moe_channel_select_reader.restype = i32
+        L.moe_channel_select_reader.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp]
         L.moe_layer_check.restype = i32
         L.moe_layer_check.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.moe_layer_geometry.restype = i32
@@ -260,9 +267,27 @@ class Layer:
                                             _stream(stream)))
         return buf[off:off + n]
 
+    def build_recovery(self, U, stream=None):
+        """moe_layer_build_recovery: allocate the recovery buffer (torch) and build it from U
+        (float32 [H][32] on the device); both are kept alive by the handle."""
+        import torch
+        d = self.desc
+        _need(U, "U", torch.float32, min_numel=d.hidden * 32)
+        n = lib().moe_recovery_bytes(ctypes.byref(d))
+        if n == 0:
+            raise MoeError(MOE_ERR_UNSUPPORTED, "this layer has no recovery form")
+        buf = torch.empty(n + 256, dtype=torch.uint8, device=U.device)
+        off = (-buf.data_ptr()) % 256
+        self._recovery = (buf, U)
+        _check(lib().moe_layer_build_recovery(self.handle, _ptr(U), 32,
+                                              ctypes.c_void_p(buf.data_ptr() + off), n,
+                                              _stream(stream)))
+        return buf[off:off + n]
+
     def channel_select(self, x, keep, kept, y=None, ids=None, w=None,
-                       mode=SCORE_GATE_DNORM, stream=None, sketch=False):
-        """moe_channel_select, or with sketch=True moe_channel_select_sketch."""
+                       mode=SCORE_GATE_DNORM, stream=None, sketch=False, reader=False):
+        """moe_channel_select, with sketch=True moe_channel_select_sketch, with reader=True
+        moe_channel_select_reader (sketch screen plus recovery)."""
         import torch
         d = self.desc
         _need(x, "x", torch.float32, min_numel=d.hidden)
@@ -274,7 +299,8 @@ class Layer:
             _need(ids, "ids", torch.int32, min_numel=d.top_k)
         if w is not None:
             _need(w, "w", torch.float32, min_numel=d.top_k)
-        fn = lib().moe_channel_select_sketch if sketch else lib().moe_channel_select
+        fn = (lib().moe_channel_select_reader if reader else
+              lib().moe_channel_select_sketch if sketch else lib().moe_channel_select)
         _check(fn(self.handle, _ptr(x), _ptr(ids), _ptr(w), keep, mode, _ptr(kept), _ptr(y),
                   _stream(stream)))
 

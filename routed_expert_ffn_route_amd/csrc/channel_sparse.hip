@@ -59,6 +59,8 @@ struct CSLaunch {
   const uint16_t *sk_ag, *sk_av;
   const int8_t* signs;
   uint64_t* sk_mask;   // launch-tagged scan masks, one copy per XCD (kSkMaskWords each)
+  const uint16_t* rec_b;  // (reader) recovery coefficients b_j, FP16 [E*I][kRecRank]
+  float* rec_r;           // (reader) this launch's per-workgroup sums r [P][kRecRank]
   uint64_t* g_ws;      // channel scores with the launch parity, one copy per XCD
   int32_t* kept_out;   // [K] ([k*I] under the threshold rule)
   int32_t* kept_count; // (threshold rule) how many were kept
@@ -826,6 +828,18 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
     bool ok[2];
     int dst[2];
     issue(0, v, ok, dst);
+    // (reader) the own candidates' recovery coefficients: 64 bytes each, four 16-byte pieces
+    const bool rec = L.rec_b != nullptr;
+    uint8_t* st_b = st_alpha + (size_t)ntask * 2 * nbp;
+    u32x4 bv = u32x4{0u, 0u, 0u, 0u};
+    bool bok = false;
+    if (rec) {
+      const int o = min(c.tid >> 2, max(nown - 1, 0));
+      const int f = g0 + o, sl = divI.div(f), e = s_ids[sl];
+      const size_t row = e >= 0 ? (size_t)e * I + (f - sl * I) : 0;
+      bv = reinterpret_cast<const u32x4*>(L.rec_b + row * kRecRank)[c.tid & 3];
+      bok = e >= 0 && (c.tid >> 2) < nown;
+    }
     // the blocks of z not finished during the top-k, while the sketch rows are in flight
     if (pub) {
 #pragma unroll
@@ -840,6 +854,8 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
         scan_finish_two(zs, ebs, c.lane, b, b + nwv, nbk);
     }
     store(v, ok, dst);
+    if (rec && (c.tid >> 2) < nown)
+      reinterpret_cast<u32x4*>(st_b)[c.tid] = bok ? bv : u32x4{0u, 0u, 0u, 0u};
     for (int p0 = 2 * c.nthreads; p0 < npieces; p0 += 2 * c.nthreads) {
       issue(p0, v, ok, dst);
       store(v, ok, dst);
@@ -1041,7 +1057,32 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
       }
     }
     nkept = p1 - p0;  // at most ceil(n / P) <= kOwnMax
+    if (L.rec_b) {  // (reader) which own candidates were dropped
+#pragma unroll
+      for (int i = 0; i < kCh; ++i) {
+        const int f = c0 + i;
+        if (mine && f >= g0 && f < g1) own_keep[f - g0] = (int)((m >> i) & 1u);
+      }
+    }
     __syncthreads();
+    if (L.rec_b && c.tid < kWave) {
+      // (reader, stage 3) r = sum over the own dropped candidates of w_e b_j p_j, with p_j =
+      // silu(g^_j) v^_j the screen's estimates; lane q < kRecRank holds component q
+      const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(
+          reinterpret_cast<const uint8_t*>(big) + (size_t)(2 * nown) * (a.H / 4) +
+          (size_t)(2 * nown) * 2 * sketch_nbp(a.H));
+      float rq = 0.0f;
+      for (int o = 0; o < nown; ++o) {
+        if (own_keep[o]) continue;  // (uniform)
+        const float p = silu(est[2 * o]) * est[2 * o + 1];
+        const float we = s_w[divI.div(g0 + o)];
+        const float bq = c.lane < kRecRank
+                             ? __half2float(__ushort_as_half(sb16[o * kRecRank + c.lane]))
+                             : 0.0f;
+        rq = fmaf(we * p, bq, rq);
+      }
+      if (c.lane < kRecRank) L.rec_r[(size_t)c.wg * kRecRank + c.lane] = rq;
+    }
   } else {
   if (!all && !none && need < ties) {
     int pos[kCh];
@@ -1175,7 +1216,9 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I, int wgs, int K, bool s
   big = big > threads * 8 ? big : threads * 8;
   big = big > router ? big : router;
   // (sketch) the own candidates' sketch rows staged
-  const int stage = sketch ? sketch_stage_bytes(H, 2 * ((n + wgs - 1) / wgs)) : 0;
+  const int stage = sketch ? sketch_stage_bytes(H, 2 * ((n + wgs - 1) / wgs)) +
+                                 ((n + wgs - 1) / wgs) * kRecRank * 2
+                           : 0;
   big = big > stage ? big : stage;
   return fixed + (big + 15) / 16 * 16;
 }
@@ -1204,6 +1247,8 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_
   L.sk_ag = L.sk_av = nullptr;
   L.signs = nullptr;
   L.sk_mask = nullptr;
+  L.rec_b = nullptr;
+  L.rec_r = nullptr;
   if (sketch) {
     if (a.H % 128 != 0 || a.H > 4096 || !sketch->g || !sketch->v || !sketch->ag ||
         !sketch->av || !sketch->signs || !sketch->mask)
@@ -1214,6 +1259,9 @@ hipError_t launch_cs(const B1Args& a, const float* dnorm, uint64_t* g_ws, int32_
     L.sk_av = sketch->av;
     L.signs = sketch->signs;
     L.sk_mask = sketch->mask;
+    L.rec_b = sketch->rec_b;
+    L.rec_r = sketch->rec_r;
+    if ((L.rec_b == nullptr) != (L.rec_r == nullptr)) return hipErrorInvalidValue;
   }
   lc::reducer_split(a.H, wgs, &L.R, &L.SW);
   const int lds = cs_lds_bytes(a.H, threads, a.E, a.k, a.I, wgs, K, sketch != nullptr);

@@ -52,8 +52,19 @@ struct CsSketch {
   const uint16_t *ag, *av;  // FP16 scales [E*I][nbp]
   const int8_t* signs;      // rotation signs [H]
   uint64_t* mask;           // workspace: launch-tagged scan masks, kPollCopies x kSkMaskWords
+  // the reader's recovery (null: none): b_j FP16 [E*I][kRecRank]; per-workgroup sums r
+  // [workgroups][kRecRank] (workspace)
+  const uint16_t* rec_b;
+  float* rec_r;
 };
 constexpr int kSkMaskWords = 128;  // words per copy: 4 per 128-block, H <= 4096
+constexpr int kRecRank = 32;       // rank of the reader's recovery map
+// b_j = U^T d_j (FP16 [nrows][kRecRank]) from D^T [nrows][H] and U [H][kRecRank] (fp32)
+hipError_t launch_rec_build(const void* down_t, DT dt, size_t nrows, int H, const float* U,
+                            uint16_t* b, hipStream_t s);
+// y [H] += U R, R = the sum over P workgroups of r [P][kRecRank]
+hipError_t launch_rec_apply(float* y, const float* U, const float* r, int P, int H,
+                            hipStream_t s);
 // The threshold keep rule: every candidate whose score pattern is at least tau_bits is kept;
 // their number goes to count (device).
 struct CsThreshold {

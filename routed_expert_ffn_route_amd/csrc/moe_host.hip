@@ -51,7 +51,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, rlog, zrow, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, cs_s, sk_mask, cs_y, xh, xl, x16, xsc, act, part, total;
+      union_slots, cs_s, sk_mask, cs_y, rec_r, xh, xl, x16, xsc, act, part, total;
 };
 
 bool desc_valid(const moe_layer_desc* d, std::string* why) {
@@ -134,6 +134,8 @@ Layout layout_of(const moe_layer_desc* d, bool with_dnorm = true) {
                        ? (size_t)kPollCopies * kSkMaskWords * 8
                        : 0);
   L.cs_y = take(d->kind == MOE_EXPERT_SWIGLU ? (size_t)d->hidden * 4 : 0);
+  // the reader's per-workgroup recovery sums [workgroups][kRecRank] (written every launch)
+  L.rec_r = take(kI ? (size_t)kMaxWorkgroups * kRecRank * 4 : 0);
   const bool batched_swiglu = d->kind == MOE_EXPERT_SWIGLU && B > 1;
   const size_t xs =
       d->kind == MOE_EXPERT_LINEAR || batched_swiglu ? B * (size_t)d->hidden * 2 : 0;
@@ -173,6 +175,8 @@ struct moe_layer_s {
   int threads;
   uint32_t magic;
   CsSketch sketch{};  // bound by moe_layer_build_sketch (all null until then)
+  const float* rec_U = nullptr;     // bound by moe_layer_build_recovery: U [H][kRecRank]
+  const uint16_t* rec_b = nullptr;  // and b [E*I][kRecRank] FP16
   template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
   Ctrl* ctrl() const { return at<Ctrl>(L.ctrl); }
 };
@@ -830,7 +834,7 @@ moe_status moe_layer_build_sketch(moe_layer layer, const int8_t* signs, void* sk
   if (sketch_bytes < S.total)
     return fail(MOE_ERR_WORKSPACE, "sketch buffer has %zu bytes, needs %zu", sketch_bytes, S.total);
   unsigned char* base = reinterpret_cast<unsigned char*>(sketch);
-  CsSketch sk;
+  CsSketch sk{};
   sk.g = reinterpret_cast<const uint32_t*>(base + S.cg);
   sk.v = reinterpret_cast<const uint32_t*>(base + S.cv);
   sk.ag = reinterpret_cast<const uint16_t*>(base + S.ag);
@@ -851,6 +855,70 @@ moe_status moe_layer_build_sketch(moe_layer layer, const int8_t* signs, void* sk
                             reinterpret_cast<uint16_t*>(base + S.rv), s);
   if (e != hipSuccess) return device_fail(e, "sketch construction");
   layer->sketch = sk;
+  return ok();
+}
+
+// Recovery buffer layout: U [H][kRecRank] fp32, then b [E*I][kRecRank] FP16, 256-byte aligned.
+static bool recovery_layout(const moe_layer_desc* d, size_t* b_off, size_t* total) {
+  SketchLayout S;
+  if (!sketch_layout(d, &S)) return false;
+  *b_off = align_up((size_t)d->hidden * kRecRank * 4);
+  *total = align_up(*b_off + (size_t)d->n_experts * d->inter * kRecRank * 2);
+  return true;
+}
+
+size_t moe_recovery_bytes(const moe_layer_desc* desc) {
+  size_t b_off, total;
+  return recovery_layout(desc, &b_off, &total) ? total : 0;
+}
+
+moe_status moe_layer_build_recovery(moe_layer layer, const float* U, int32_t rank, void* rec,
+                                    size_t rec_bytes, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const moe_layer_desc& d = layer->d;
+  size_t b_off, total;
+  if (!recovery_layout(&d, &b_off, &total))
+    return fail(MOE_ERR_UNSUPPORTED, "the recovery map needs a layer with a sketch form");
+  if (rank != kRecRank) return fail(MOE_ERR_UNSUPPORTED, "rank must be %d", kRecRank);
+  if (!U || !rec) return fail(MOE_ERR_ARG, "U and rec must be given");
+  if (((uintptr_t)U % 4) != 0) return fail(MOE_ERR_ARG, "U must be 4-byte aligned");
+  if (((uintptr_t)rec % kAlign) != 0)
+    return fail(MOE_ERR_WORKSPACE, "the recovery buffer must be 256-byte aligned");
+  if (rec_bytes < total)
+    return fail(MOE_ERR_WORKSPACE, "recovery buffer has %zu bytes, needs %zu", rec_bytes, total);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* base = reinterpret_cast<unsigned char*>(rec);
+  hipError_t e = hipMemcpyAsync(base, U, (size_t)d.hidden * kRecRank * 4,
+                                hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_rec_build(layer->w.down_t, to_dt(d.expert_dtype),
+                         (size_t)d.n_experts * d.inter, d.hidden,
+                         reinterpret_cast<const float*>(base),
+                         reinterpret_cast<uint16_t*>(base + b_off), s);
+  if (e != hipSuccess) return device_fail(e, "recovery map construction");
+  layer->rec_U = reinterpret_cast<const float*>(base);
+  layer->rec_b = reinterpret_cast<const uint16_t*>(base + b_off);
+  return ok();
+}
+
+moe_status moe_channel_select_reader(moe_layer layer, const float* x, const int32_t* ids,
+                                     const float* w, int32_t keep, int32_t mode, int32_t* kept,
+                                     float* y, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  if (!layer->sketch.g)
+    return fail(MOE_ERR_ARG, "no sketch: call moe_layer_build_sketch first");
+  if (!layer->rec_b)
+    return fail(MOE_ERR_ARG, "no recovery map: call moe_layer_build_recovery first");
+  CsSketch sk = layer->sketch;
+  sk.rec_b = layer->rec_b;
+  sk.rec_r = layer->at<float>(layer->L.rec_r);
+  float* yy = y ? y : layer->at<float>(layer->L.cs_y);
+  if (moe_status st = channel_select_impl(layer, x, ids, w, keep, mode, kept, yy, stream, &sk))
+    return st;
+  const hipError_t e = launch_rec_apply(yy, layer->rec_U, layer->at<float>(layer->L.rec_r),
+                                        layer->workgroups, layer->d.hidden,
+                                        reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "recovery launch");
   return ok();
 }
 

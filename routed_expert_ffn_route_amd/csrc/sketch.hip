@@ -1,5 +1,7 @@
 // sketch.hip -- load-time construction of the ternary sketch of every routed channel's gate
-// and up rows (the review of arXiv:2610.37386, "The weights-only reader", stage 1).
+// and up rows (the review of arXiv:2610.37386, "The weights-only reader", stage 1), and the
+// two small pieces of its stage 3 (the rank-32 recovery): the coefficients b_j = U^T d_j at
+// load time, and the final y += U R after the screen.
 //
 // Each row is rotated in blocks of 128 coordinates by a randomized Hadamard transform, kept
 // unnormalized: u = H_128 (s * w) per block (s the layer's fixed random signs, H_128 the
@@ -112,7 +114,92 @@ __global__ __launch_bounds__(256) void sketch_build_kernel(const void* rows, siz
   }
 }
 
+// The recovery coefficients b_j = U^T d_j of the reader's stage 3 (rank kRecRank): one thread
+// per (row j of D^T, component c), an fp32 sum over h in index order, stored as FP16.
+template <DT dt>
+__global__ __launch_bounds__(256) void rec_build_kernel(const void* down_t, size_t nrows, int H,
+                                                        const float* U, uint16_t* b) {
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nrows * kRecRank) return;
+  const size_t j = t / kRecRank;
+  const int cc = (int)(t % kRecRank);
+  float acc = 0.0f;
+  for (int h = 0; h < H; ++h)
+    acc = fmaf(U[(size_t)h * kRecRank + cc], load_elem<dt>(down_t, j * (size_t)H + h), acc);
+  b[t] = __half_as_ushort(__float2half_rn(acc));
+}
+
+// y[h] += sum_c U[h][c] R[c] with R = sum over the P workgroups' vectors r[w][c] (in workgroup
+// order), the stage-3 term U sum_S w_j b_j p_j whose inner sums the screen left in r.
+__global__ __launch_bounds__(256) void rec_apply_kernel(float* y, const float* U, const float* r,
+                                                        int P, int H) {
+  __shared__ float part[8][kRecRank];
+  __shared__ float R[kRecRank];
+  const int tid = threadIdx.x, cc = tid % kRecRank, g = tid / kRecRank;  // 8 groups
+  // workgroups g, g + 8, ... in batches of 32 independent loads, one round trip for up to
+  // 256 workgroups (a plain loop would wait for each load before issuing the next); U's row
+  // is requested first
+  const int h = blockIdx.x * blockDim.x + tid;
+  const float4* u4 = reinterpret_cast<const float4*>(U + (size_t)min(h, H - 1) * kRecRank);
+  float4 uv[kRecRank / 4];
+#pragma unroll
+  for (int q = 0; q < kRecRank / 4; ++q) uv[q] = u4[q];
+  float s = 0.0f;
+  for (int w0 = g; w0 < P; w0 += 256) {
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int w = min(w0 + 8 * u, P - 1);
+      v[u] = r[(size_t)w * kRecRank + cc];
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) s += w0 + 8 * u < P ? v[u] : 0.0f;
+  }
+  part[g][cc] = s;
+  __syncthreads();
+  if (tid < kRecRank) {
+    float t = 0.0f;
+    for (int q = 0; q < 8; ++q) t += part[q][tid];
+    R[tid] = t;
+  }
+  __syncthreads();
+  if (h < H) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kRecRank / 4; ++q) {
+      acc = fmaf(uv[q].x, R[4 * q], acc);
+      acc = fmaf(uv[q].y, R[4 * q + 1], acc);
+      acc = fmaf(uv[q].z, R[4 * q + 2], acc);
+      acc = fmaf(uv[q].w, R[4 * q + 3], acc);
+    }
+    y[h] += acc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rec_build(const void* down_t, DT dt, size_t nrows, int H, const float* U,
+                            uint16_t* b, hipStream_t s) {
+  if (dt != DT::BF16 && dt != DT::F32) return hipErrorInvalidValue;
+  const size_t n = nrows * kRecRank;
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(rec_build_kernel<DT::BF16>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       down_t, nrows, H, U, b);
+  else
+    hipLaunchKernelGGL(rec_build_kernel<DT::F32>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       down_t, nrows, H, U, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_rec_apply(float* y, const float* U, const float* r, int P, int H,
+                            hipStream_t s) {
+  if (H <= 0 || P <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rec_apply_kernel, dim3((H + 255) / 256), dim3(256), 0, s, y, U, r, P, H);
+  return hipGetLastError();
+}
 
 hipError_t launch_sketch_build(const void* rows, DT dt, size_t nrows, int H, const int8_t* signs,
                                uint32_t* codes, uint16_t* alpha, uint16_t* rho, hipStream_t s) {

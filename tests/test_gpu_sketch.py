@@ -234,3 +234,79 @@ def test_sketch_screen_full_size(keep):
     L.close()
     del L
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ stage 3: the reader
+def _basis(wl, hl):
+    """U from the layer's stacked down columns (every routed channel), by the oracle."""
+    return S.recovery_basis((hl.expert(e)[2] for e in range(wl.E)), wl.H)
+
+
+def _reader(L, x_np, keep, mode):
+    import torch
+    x = torch.from_numpy(np.asarray(x_np, dtype=np.float32)).cuda().reshape(1, -1)
+    y = torch.empty_like(x)
+    kept = torch.full((max(keep, 1),), -1, dtype=torch.int32, device="cuda")
+    L.channel_select(x, keep, kept, y=y, mode=mode, reader=True)
+    assert L.check() == 0
+    return kept.cpu().numpy()[:keep], y.cpu().numpy()[0]
+
+
+@pytest.mark.parametrize("wl", SMALL[:2], ids=lambda w: f"H{w.H}E{w.E}I{w.I}{w.expert_dtype}")
+def test_reader_recovery_small(wl):
+    import torch
+    L = _layer(wl)
+    hl = HostLayer(wl)
+    _build(L, wl)
+    U = _basis(wl, hl)
+    L.build_recovery(torch.from_numpy(U.astype(np.float32)).cuda())
+    coeffs = {}
+
+    def coeffs_of(e):
+        if e not in coeffs:
+            coeffs[e] = S.recovery_coeffs(hl.expert(e)[2], U.astype(np.float32))
+        return coeffs[e]
+
+    signs_np = T.rotation_signs(wl, 0)
+    cache = {}
+    n = wl.k * wl.I
+    for tok, keep in enumerate([1, n // 8, n // 3 + 1, n]):
+        x, ids, w, dnorm_of, sketch_of = _pick(wl, hl, 50 + tok, keep, "router_weighted",
+                                               signs_np, cache)
+        kept_ref, y_ref = S.reader_token(x, ids, w, hl.expert, sketch_of, dnorm_of, keep,
+                                         signs_np, U.astype(np.float32), coeffs_of, hl.shared,
+                                         "router_weighted")
+        kept, y = _reader(L, x, keep, 1)
+        assert kept.tolist() == kept_ref.tolist(), (tok, keep)
+        assert rel_err(y, y_ref) <= TOL_BF16, (tok, keep, rel_err(y, y_ref))
+
+
+def test_reader_recovery_full_size():
+    """The stack's shapes: U of the layer's 196,608 down columns, keep 799."""
+    import torch
+    wl = WORKLOADS["qwen35_a3b_sparse"]
+    L = _layer(wl, 4)
+    hl = HostLayer(wl, 4)
+    _build(L, wl, 4)
+    U = _basis(wl, hl).astype(np.float32)
+    L.build_recovery(torch.from_numpy(U).cuda())
+    signs_np = T.rotation_signs(wl, 4)
+    cache, coeffs = {}, {}
+
+    def coeffs_of(e):
+        if e not in coeffs:
+            coeffs[e] = S.recovery_coeffs(hl.expert(e)[2], U)
+        return coeffs[e]
+
+    x, ids, w, dnorm_of, sketch_of = _pick(wl, hl, 3, 799, "router_weighted", signs_np, cache,
+                                           layer=4)
+    kept_ref, y_ref = S.reader_token(x, ids, w, hl.expert, sketch_of, dnorm_of, 799, signs_np,
+                                     U, coeffs_of, hl.shared, "router_weighted")
+    kept, y = _reader(L, x, 799, 1)
+    assert kept.tolist() == kept_ref.tolist()
+    err = rel_err(y, y_ref)
+    print(f"reader keep 799: max|dy|/||y||inf = {err:.3e}")
+    assert err <= TOL_BF16
+    L.close()
+    del L
+    torch.cuda.empty_cache()

@@ -186,3 +186,64 @@ def test_sketch_scores_follow_eq1():
 def test_sketch_bytes_arithmetic():
     # per candidate: 2 rows x 16 blocks x (32 code bytes + 2 scale bytes); kept: 3 full rows
     assert S.sketch_bytes(2048, 768, 8, 799) == 8 * 768 * 2 * 16 * 34 + 3 * 799 * 4096
+
+
+# ------------------------------------------------------------------ stage 3: recovery
+def _tiny_reader(rng, H=B, E=3, I=4):
+    s = _signs(rng, H)
+    experts = [tuple(rng.normal(0, 0.3, size=(I, H)) for _ in range(3)) for _ in range(E)]
+    sk = {e: (S.sketch_rows(experts[e][0], s), S.sketch_rows(experts[e][1], s))
+          for e in range(E)}
+    sketch_of = lambda e: sk[e]
+    dn = {e: np.linalg.norm(experts[e][2], axis=1) for e in range(E)}
+    return s, experts, sketch_of, dn
+
+
+def test_full_rank_map_with_exact_activations_is_the_dense_layer():
+    """Rank H with p = a: the recovery adds back every dropped channel exactly, so the output
+    is the dense layer's for any keep."""
+    rng = np.random.default_rng(21)
+    s, experts, sketch_of, dn = _tiny_reader(rng)
+    U = np.linalg.qr(rng.normal(size=(B, B)))[0]          # any orthonormal basis of R^H
+    coeffs = {e: S.recovery_coeffs(experts[e][2], U) for e in range(3)}
+    ids, w = np.array([2, 0]), np.array([0.7, 0.3])
+    x = rng.normal(size=B)
+    from oracle import moe_oracle as O
+    dense = O.moe_layer_given(x, ids, w, lambda e: experts[e])
+    for keep in (0, 1, 5, 8):
+        _, y = S.reader_token(x, ids, w, lambda e: experts[e], sketch_of, dn.__getitem__, keep,
+                              s, U, coeffs.__getitem__, p_exact=True)
+        assert np.allclose(y, dense, rtol=0, atol=1e-10 * np.max(np.abs(dense)))
+
+
+def test_keep_all_adds_nothing_and_keep_none_is_the_map_alone():
+    rng = np.random.default_rng(22)
+    s, experts, sketch_of, dn = _tiny_reader(rng)
+    U = np.linalg.qr(rng.normal(size=(B, 8)))[0]
+    coeffs = {e: S.recovery_coeffs(experts[e][2], U) for e in range(3)}
+    ids, w = np.array([1, 2]), np.array([0.4, 0.6])
+    x = rng.normal(size=B)
+    kept, y = S.reader_token(x, ids, w, lambda e: experts[e], sketch_of, dn.__getitem__, 8, s,
+                             U, coeffs.__getitem__)
+    _, y_screen = S.sketch_select_token(x, ids, w, lambda e: experts[e], sketch_of,
+                                        dn.__getitem__, 8, s)
+    assert kept.size == 8 and np.allclose(y, y_screen, rtol=0, atol=1e-12)
+    # keep 0: y = U sum_all w b p with the screen's estimates
+    _, gh, vh = S.sketch_scores(x, ids, w, sketch_of, dn.__getitem__, s)
+    r = sum(w[i] * (gh[i, j] / (1 + np.exp(-gh[i, j]))) * vh[i, j] * coeffs[int(e)][j]
+            for i, e in enumerate(ids) for j in range(4))
+    _, y0 = S.reader_token(x, ids, w, lambda e: experts[e], sketch_of, dn.__getitem__, 0, s,
+                           U, coeffs.__getitem__)
+    assert np.allclose(y0, U @ r, rtol=0, atol=1e-12)
+
+
+def test_recovery_basis_is_the_top_singular_subspace():
+    rng = np.random.default_rng(23)
+    H = 16
+    D = rng.normal(size=(40, H)) @ np.diag(np.linspace(3.0, 0.1, H))   # distinct spectrum
+    U = S.recovery_basis([D[:17], D[17:]], H, rank=5)
+    assert np.allclose(U.T @ U, np.eye(5), atol=1e-12)
+    Us = np.linalg.svd(D.T, full_matrices=False)[0][:, :5]
+    assert np.allclose(U @ U.T, Us @ Us.T, atol=1e-10)     # the same subspace
+    for c in range(5):
+        assert U[np.argmax(np.abs(U[:, c])), c] > 0
