@@ -686,6 +686,102 @@ def run_batched_stack(args, wl, B):
     }
 
 
+def run_batch_select(args, wl, B, keep_tok):
+    """Batch-wide channel selection through the channel-sparse stack (the reader review's
+    "Limits": one kept set for the whole batch).  Per layer and step of B tokens: routing, the
+    touched-expert union, the batch scores from every touched gate row, the selection of
+    keep = B * keep_tok channels, the kept channels' activations and down products for the
+    tokens routed to them, the shared experts for every token."""
+    import torch
+    import routed_expert_ffn_route_amd as M
+    from synth import tensors as T
+    nb = max(1, min(wl.tokens // B, max(args.steps, 1)))
+    keep = B * keep_tok
+    desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, wl.n_shared, wl.I_shared,
+                       router_dtype=wl.router_dtype, expert_dtype=wl.expert_dtype,
+                       shared_dtype=wl.shared_dtype, max_batch=B)
+    layers, xs, ys = [], [], []
+    for l in range(wl.layers):
+        layers.append(M.Layer(desc, T.device_layer(wl, l)))
+        xs.append(T.device_x(wl, list(range(nb * B)), l))
+        ys.append(torch.empty_like(xs[-1]))
+    kept = torch.empty(keep, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids = torch.empty((B, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((B, wl.k), dtype=torch.float32, device="cuda")
+    nt_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t_dev = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+    o_dev = torch.empty(wl.E + 1, dtype=torch.int32, device="cuda")
+    s_dev = torch.empty(B * wl.k, dtype=torch.int32, device="cuda")
+    touched = {}
+    for l in range(wl.layers):
+        for i in range(nb):
+            layers[l].route(x=xs[l][i * B:(i + 1) * B], ids=ids, w=w)
+            M.union_experts(ids, wl.E, nt_dev, t_dev, o_dev, s_dev)
+            touched[(l, i)] = int(nt_dev.item())
+    torch.cuda.synchronize()
+
+    def step(t):
+        i = t % nb
+        for l in range(wl.layers):
+            layers[l].channel_select_batch(xs[l][i * B:(i + 1) * B], keep, kept,
+                                           ys[l][i * B:(i + 1) * B], kept_count=cnt)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    for L in layers:
+        assert L.check() == 0, "device error word set"
+    K = args.steps
+    gpu_ms, wall_ms = timed(step, K, graph_ok=not args.eager)
+    for L in layers:
+        assert L.check() == 0, "device error word set"
+    be = BYTES_PER_ELEM[wl.expert_dtype]
+    bs = BYTES_PER_ELEM.get(wl.shared_dtype, 0.0)
+    br = BYTES_PER_ELEM.get(wl.router_dtype, 0.0)
+
+    def layer_bytes(nt):
+        # every touched gate row and its norm, the kept up and down rows, shared, router
+        kk = min(keep, nt * wl.I)
+        return (nt * wl.I * (wl.H * be + 4) + 2 * kk * wl.H * be +
+                wl.n_shared * 3 * wl.H * wl.I_shared * bs + wl.E * wl.H * br)
+
+    step_bytes = sum(layer_bytes(touched[(l, t % nb)])
+                     for t in range(K) for l in range(wl.layers)) / K
+    mean_touched = sum(touched.values()) / len(touched)
+    achieved = step_bytes / (gpu_ms / 1e3 / K) / 1e9
+    return {
+        "metric": "MoE-stack batched decode tokens/s (aggregate over the batch)",
+        "value": round(K * B / (gpu_ms / 1e3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(gpu_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "hidden": wl.H, "experts": wl.E,
+                   "top_k": wl.k, "inter": wl.I, "shared": wl.n_shared,
+                   "weights": wl.expert_dtype, "batch": B, "keep": keep,
+                   "screen": "batch-wide exact gates (summed router-weighted scores)",
+                   "graph": not args.eager},
+        "mean_touched_experts": round(mean_touched, 2),
+        "hbm_gb_s": round(achieved, 1),
+        "hbm_pct_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "wall_ms_per_step": round(wall_ms / K, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "route + union + scores + select + act + down + sum per layer",
+                     "bytes_per_step": step_bytes,
+                     "us_per_layer_step": round(gpu_ms * 1e3 / K / wl.layers, 3)},
+        "cpu_baseline": None,
+    }
+
+
 def run_linear_sweep(args, wl):
     """The linear-expert batch sweep: per batch, one step = route (given iid logits), union,
     and the MFMA grouped product; each step's touched experts are read once."""
@@ -849,6 +945,9 @@ def main():
     ap.add_argument("--batch", type=int, default=1,
                     help="SwiGLU stacks: tokens per step (B > 1 runs the batched layer)")
     ap.add_argument("--eager", action="store_true", help="launch without a HIP graph")
+    ap.add_argument("--batch-select", action="store_true",
+                    help="sparse workload with --batch B: batch-wide channel selection, "
+                         "B * keep channels for the batch (moe_channel_select_batch)")
     ap.add_argument("--sweep-ek", action="store_true",
                     help="linear workload: the batch-1 (E, k) linearity sub-sweep")
     ap.add_argument("--timeline", action="store_true",
@@ -896,12 +995,15 @@ def main():
         for line in run(args, wl):
             print(json.dumps(line), flush=True)
         return
-    if args.batch > 1:
-        print(json.dumps(run_batched_stack(args, wl, args.batch)), flush=True)
-        return
     keep = None
     if wl.keep_fracs:
         keep = args.keep if args.keep >= 0 else wl.keep_counts()[0]
+    if args.batch > 1 and keep is not None and args.batch_select:
+        print(json.dumps(run_batch_select(args, wl, args.batch, keep)), flush=True)
+        return
+    if args.batch > 1:
+        print(json.dumps(run_batched_stack(args, wl, args.batch)), flush=True)
+        return
     if args.threshold > 0:
         if not wl.keep_fracs:
             raise SystemExit("--threshold needs the channel-sparse workload")

@@ -233,6 +233,29 @@ moe_status moe_channel_select_reader(moe_layer layer, const float* x, const int3
                                      const float* w, int32_t keep, int32_t mode, int32_t* kept,
                                      float* y, void* stream);
 
+/* Batch-wide channel selection for B tokens (the review of arXiv:2610.37386, "Limits":
+ * choosing the channels for a whole batch at once is left by the authors as future work; its
+ * Table 7 runs the per-token reader at B = 4 and 8).  Reading taken: the candidates are the
+ * channels (e, j) of every expert that some token of the batch routes to (candidate order:
+ * ascending e*I + j); a channel's batch score is ||d_j|| times the sum, over the tokens b
+ * routed to e, of w_{b,e} |silu(g_j . x_b)| (the router-weighted output-unit score, summed);
+ * the `keep` best batch scores are kept (ties to the lower e*I + j); each kept channel is
+ * computed exactly for every token routed to its expert, its three rows read once for the
+ * batch; dropped channels add nothing; shared experts are computed in full for every token.
+ *
+ * x [B][H] fp32, 1 <= B <= min(max_batch, 16); ids/w [B][k] as for moe_ffn_forward (NULL:
+ * routed inside the call; given ids must be distinct per token and in [0, E)).  0 <= keep <=
+ * min(E, B*k)*I (kept are min(keep, n_touched*I)).  kept [keep] (device int32, may be NULL when
+ * keep is 0) receives the kept ids ascending, -1 past the kept count; kept_count [1] (device
+ * int32, may be NULL) their number.  y [B][H] fp32 (must be given).  BF16 or F32 experts
+ * (MOE_ERR_UNSUPPORTED for MXFP4, or for more than 262144 candidates).  Enqueues on `stream`
+ * the routing (when ids is NULL), the touched-expert union and five launches: batch scores
+ * (one wave per candidate), the selection (one workgroup), the kept and shared channels'
+ * activations (one wave per channel), the down products in 32 channel chunks, their sum. */
+moe_status moe_channel_select_batch(moe_layer layer, const float* x, int32_t B,
+                                    const int32_t* ids, const float* w, int32_t keep,
+                                    int32_t* kept, int32_t* kept_count, float* y, void* stream);
+
 /* Touched-expert union of a batch (the "experts touched by a batch" count of the
  * 501B/23B post, section 2).  ids [B][k] with distinct experts per token, 0 <= id < E.
  * Writes n_touched [1], touched [E] (ascending; first n_touched valid), offsets [E+1]

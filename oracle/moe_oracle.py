@@ -273,6 +273,68 @@ def channel_select_threshold_token(x, ids, w, get_expert, dnorm_of, tau, shared=
     return np.sort(cid[keep]), y
 
 
+def batch_channel_scores(X, ids, w, get_expert, dnorm_of):
+    """The batch scores of batch-wide channel selection [Reader, "Limits"; the score is the
+    router-weighted output-unit score of "Background: channels and keep rules", summed over
+    the batch].  Reading taken: the candidates are the channels (e, j) of the experts any
+    token of the batch routes to, in ascending e*I + j; a channel's batch score is the sum over
+    the tokens b routed to e of w_{b,e} ||d_j|| |silu(g_j.x_b)|.  Returns (candidate ids e*I + j,
+    their scores, the activations {(e, b): (w_{b,e}, silu(g.x_b) * (v.x_b) over the channels)})."""
+    X = np.asarray(X, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    w = np.asarray(w, dtype=np.float64)
+    B = ids.shape[0]
+    touched = sorted(set(int(e) for e in ids.ravel()))
+    cids, svals, acts = [], [], {}
+    for e in touched:
+        G, V, _ = get_expert(e)
+        Gm, Vm = to_f64(G), to_f64(V)
+        I = Gm.shape[0]
+        dn = np.asarray(dnorm_of(e), dtype=np.float64)
+        sc = np.zeros(I)
+        for b in range(B):
+            hit = np.nonzero(ids[b] == e)[0]
+            if hit.size == 0:
+                continue
+            wb = w[b, hit[0]]
+            g = Gm @ X[b]
+            sc += wb * dn * np.abs(silu(g))
+            acts[(e, b)] = (wb, silu(g) * (Vm @ X[b]))
+        cids.append(e * I + np.arange(I))
+        svals.append(sc)
+    if not touched:
+        return np.zeros(0, dtype=np.int64), np.zeros(0), acts
+    return np.concatenate(cids), np.concatenate(svals), acts
+
+
+def batch_channel_select(X, ids, w, get_expert, dnorm_of, keep, shared=()):
+    """Batch-wide channel selection for B tokens [Reader, "Limits": selecting the whole
+    batch's channels at once is the authors' future work; Table 7 measures the per-token
+    reader at B = 4 and 8].  Reading taken: the candidates and batch scores of
+    batch_channel_scores; the `keep` best batch scores are kept (ties to the lower e*I + j),
+    and each kept channel is computed exactly for every token routed to its expert (its rows
+    read once for the batch); dropped channels contribute nothing; shared experts are computed
+    in full for every token.  Returns (kept ids e*I + j ascending, Y [B][H])."""
+    X = np.asarray(X, dtype=np.float64)
+    B = X.shape[0]
+    cid, sv, acts = batch_channel_scores(X, ids, w, get_expert, dnorm_of)
+    order = np.lexsort((cid, -sv))[:keep]
+    kept = np.sort(cid[order])
+    Y = np.zeros_like(X)
+    I = acts[next(iter(acts))][1].size if acts else 1
+    for c in kept:
+        e, j = divmod(int(c), I)
+        dj = to_f64(_row(get_expert(e)[2], j)).reshape(-1)
+        for b in range(B):
+            if (e, b) in acts:
+                wb, a = acts[(e, b)]
+                Y[b] += wb * a[j] * dj
+    for b in range(B):
+        for (gs, us, ds) in shared:
+            Y[b] += expert_output(X[b], gs, us, ds)
+    return kept, Y
+
+
 def calibrate_tau(score_sets, frac):
     """The threshold calibrated on a set of tokens [Reader, calibration discussion: tau is set
     on calibration data so that the kept fraction meets the budget on average]: the m-th

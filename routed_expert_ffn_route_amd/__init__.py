@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_layer_routing", "moe_sketch_bytes", "moe_layer_build_sketch",
     "moe_channel_select_sketch", "moe_channel_select_threshold", "moe_layer_scores",
     "moe_recovery_bytes", "moe_layer_build_recovery", "moe_channel_select_reader",
-    "moe_layer_check", "moe_layer_geometry", "moe_status_string", "moe_last_error",
+    "moe_channel_select_batch", "moe_layer_check", "moe_layer_geometry", "moe_status_string", "moe_last_error",
 )
 # The phase-timeline build (libmoe_ffn_timeline.so) exports one more, for measurement only.
 TIMELINE_LIB_PATH = os.path.join(_HERE, "libmoe_ffn_timeline.so")
@@ -115,6 +115,8 @@ def lib():
         L.moe_layer_build_recovery.argtypes = [vp, vp, i32, vp, sz, vp]
         L.moe_channel_select_reader.restype = i32
         L.moe_channel_select_reader.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp]
+        L.moe_channel_select_batch.restype = i32
+        L.moe_channel_select_batch.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp, vp]
         L.moe_layer_check.restype = i32
         L.moe_layer_check.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.moe_layer_geometry.restype = i32
@@ -321,6 +323,26 @@ class Layer:
         _check(lib().moe_channel_select_threshold(self.handle, _ptr(x), _ptr(ids), _ptr(w),
                                                   float(tau), mode, _ptr(kept),
                                                   _ptr(kept_count), _ptr(y), _stream(stream)))
+
+    def channel_select_batch(self, x, keep, kept, y, kept_count=None, ids=None, w=None,
+                             stream=None):
+        """moe_channel_select_batch: one kept channel set for the batch x [B][H]."""
+        import torch
+        d = self.desc
+        B = x.shape[0]
+        _need(x, "x", torch.float32, min_numel=B * d.hidden)
+        _need(y, "y", torch.float32, min_numel=B * d.hidden)
+        if kept is not None or keep > 0:
+            _need(kept, "kept", torch.int32, min_numel=keep)
+        if kept_count is not None:
+            _need(kept_count, "kept_count", torch.int32, min_numel=1)
+        if ids is not None:
+            _need(ids, "ids", torch.int32, min_numel=B * d.top_k)
+        if w is not None:
+            _need(w, "w", torch.float32, min_numel=B * d.top_k)
+        _check(lib().moe_channel_select_batch(self.handle, _ptr(x), B, _ptr(ids), _ptr(w), keep,
+                                              _ptr(kept), _ptr(kept_count), _ptr(y),
+                                              _stream(stream)))
 
     def scores(self, out, stream=None):
         """moe_layer_scores: the last channel-selection call's k*I scores, slot-major."""

@@ -1197,7 +1197,259 @@ hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStrea
   return launch_t<ET, ST, RT, C, 1, false>(L, wgs, threads, lds, s, occ);
 }
 
+// ------------------------------------------------------------------------------------
+// Batch-wide channel selection (the review's "Limits": choosing the whole batch's channels at
+// once is the authors' future work).  For B tokens routed independently, the candidates are
+// the channels of the touched experts (candidate index t*I + j: channel j of the t-th touched
+// expert, ascending expert id, so ascending e*I + j); a channel's batch score is the sum over
+// the tokens routed to its expert of w_{b,e} |silu(g_j.x_b)|, times ||d_j||; the `keep` best
+// are computed exactly for every token routed to their expert, each row read once for the
+// batch, and the shared experts for every token.  Five small launches after the routing and
+// the union: scores (one wave per candidate), selection (one workgroup), activations (one wave
+// per kept or shared channel), down products (channel chunks x column blocks, partial rows)
+// and their sum in chunk order.
+struct BselArgs {
+  const float* x;                                     // [B][H]
+  const int32_t* ids;                                 // [B][k]
+  const float* w;                                     // [B][k]
+  const int32_t *n_touched, *touched, *offsets, *slots;  // the union
+  const void *gate, *up, *down_t, *sh_gate, *sh_up, *sh_down_t;
+  const float* dnorm;                                 // [E*I]
+  float* S;                                           // [n_t*I] batch scores
+  int32_t* kc;                                        // [keep] kept candidate indices
+  int32_t* kept_out;                                  // [keep] kept ids e*I + j
+  int32_t* nkept;                                     // [1]
+  float* A;                                           // [keep + NS*IS][B] activations x w
+  float* part;                                        // [nchunk][B][H]
+  float* y;                                           // [B][H]
+  int H, I, E, k, B, NS, IS, keep, nchunk;
+};
+constexpr int kBselMaxB = kBselMaxBatch;
+constexpr int kBselChunks = kBselPartChunks;
+
+template <DT dt>
+__device__ __forceinline__ float bsel_elem(const void* base, size_t i) {
+  if constexpr (dt == DT::BF16)
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[i] << 16);
+  else
+    return reinterpret_cast<const float*>(base)[i];
+}
+// row . x_b over H (8-element chunks per lane, fp32 sums), in every lane
+template <DT dt>
+__device__ inline float bsel_dot(const void* rows, size_t row, const float* xb, int H,
+                                 int lane) {
+  float acc = 0.0f;
+  for (int ch = lane; ch < H / 8; ch += kWave) {
+    const size_t o = row * (size_t)H + 8 * (size_t)ch;
+    const f32x4 x0 = reinterpret_cast<const f32x4*>(xb)[2 * ch];
+    const f32x4 x1 = reinterpret_cast<const f32x4*>(xb)[2 * ch + 1];
+    acc = fmaf(bsel_elem<dt>(rows, o), x0.x, acc);
+    acc = fmaf(bsel_elem<dt>(rows, o + 1), x0.y, acc);
+    acc = fmaf(bsel_elem<dt>(rows, o + 2), x0.z, acc);
+    acc = fmaf(bsel_elem<dt>(rows, o + 3), x0.w, acc);
+    acc = fmaf(bsel_elem<dt>(rows, o + 4), x1.x, acc);
+    acc = fmaf(bsel_elem<dt>(rows, o + 5), x1.y, acc);
+    acc = fmaf(bsel_elem<dt>(rows, o + 6), x1.z, acc);
+    acc = fmaf(bsel_elem<dt>(rows, o + 7), x1.w, acc);
+  }
+  return wave_sum(acc);
+}
+
+template <DT ET>
+__global__ __launch_bounds__(256) void bsel_score_kernel(BselArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (c >= *a.n_touched * a.I) return;  // whole waves
+  const int t = c / a.I, j = c - t * a.I, e = a.touched[t];
+  const size_t row = (size_t)e * a.I + j;
+  float sc = 0.0f;
+  for (int s = a.offsets[e]; s < a.offsets[e + 1]; ++s) {
+    const int slot = a.slots[s], b = slot / a.k;
+    const float g = bsel_dot<ET>(a.gate, row, a.x + (size_t)b * a.H, a.H, lane);
+    sc = fmaf(a.w[slot], fabsf(silu(g)), sc);
+  }
+  if (lane == 0) a.S[c] = sc * a.dnorm[row];
+}
+
+// One workgroup: K = min(keep, m) kept, T the K-th largest batch score (select_threshold),
+// then a compaction in candidate order (ties to the lower candidate): each thread counts the
+// values above T and equal to T in its contiguous share, block scans place them.
+__global__ __launch_bounds__(1024) void bsel_select_kernel(BselArgs a) {
+  __shared__ int hist[kSelBins];
+  __shared__ int sh[96];
+  Ctx c;
+  c.tid = threadIdx.x;
+  c.nthreads = blockDim.x;
+  c.lane = c.tid & (kWave - 1);
+  const int m = *a.n_touched * a.I;
+  const int K = min(a.keep, m);
+  const uint32_t* u = reinterpret_cast<const uint32_t*>(a.S);  // non-negative: patterns order
+  const bool every = K >= m;
+  uint32_t T = 0;
+  int need = 0, ties = 0;
+  if (K > 0 && !every) T = select_threshold(u, m, K, &need, &ties, hist, sh, c);
+  const int per = (m + c.nthreads - 1) / c.nthreads;
+  const int f0 = min(c.tid * per, m), f1 = min(f0 + per, m);
+  int gt = 0, eq = 0;
+  if (K > 0) {
+    for (int f = f0; f < f1; ++f) {
+      const uint32_t v = u[f];
+      gt += (every || v > T) ? 1 : 0;
+      eq += (!every && v == T) ? 1 : 0;
+    }
+  }
+  int tot;
+  int gb = block_excl_scan(gt, sh + 48, c, &tot);
+  int eb = block_excl_scan(eq, sh + 48, c, &tot);
+  if (K > 0) {
+    for (int f = f0; f < f1; ++f) {
+      const uint32_t v = u[f];
+      const bool above = every || v > T;
+      const bool tie = !every && v == T;
+      if (above || (tie && eb < need)) {
+        const int pos = gb + min(eb, need);
+        const int t = f / a.I;
+        a.kc[pos] = f;
+        a.kept_out[pos] = a.touched[t] * a.I + (f - t * a.I);
+      }
+      gb += above ? 1 : 0;
+      eb += tie ? 1 : 0;
+    }
+  }
+  for (int i = K + c.tid; i < a.keep; i += c.nthreads) a.kept_out[i] = -1;
+  if (c.tid == 0) *a.nkept = K;
+}
+
+// One wave per channel: kept routed channels [0, nk), then the shared ones; lane b < B ends
+// holding w_{b,e} silu(g.x_b) (v.x_b) (0 for a token not routed to the channel's expert).
+template <DT ET, DT ST>
+__global__ __launch_bounds__(256) void bsel_act_kernel(BselArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ch = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int nk = *a.nkept, C = nk + a.NS * a.IS;
+  if (ch >= C) return;
+  float val = 0.0f;
+  if (ch < nk) {
+    const int f = a.kc[ch], t = f / a.I, j = f - t * a.I, e = a.touched[t];
+    const size_t row = (size_t)e * a.I + j;
+    for (int s = a.offsets[e]; s < a.offsets[e + 1]; ++s) {
+      const int slot = a.slots[s], b = slot / a.k;
+      const float* xb = a.x + (size_t)b * a.H;
+      const float g = bsel_dot<ET>(a.gate, row, xb, a.H, lane);
+      const float v = bsel_dot<ET>(a.up, row, xb, a.H, lane);
+      if (lane == b) val = a.w[slot] * silu(g) * v;
+    }
+  } else {
+    const size_t row = (size_t)(ch - nk);
+    for (int b = 0; b < a.B; ++b) {
+      const float* xb = a.x + (size_t)b * a.H;
+      const float g = bsel_dot<ST>(a.sh_gate, row, xb, a.H, lane);
+      const float v = bsel_dot<ST>(a.sh_up, row, xb, a.H, lane);
+      if (lane == b) val = silu(g) * v;
+    }
+  }
+  if (lane < a.B) a.A[(size_t)ch * a.B + lane] = val;
+}
+
+// Channel chunk q of kBselChunks x a column block of 256: part[q][b][h] = sum over the
+// chunk's channels (in order) of A[ch][b] d_ch[h].  The chunk's A rows and row offsets are
+// staged in LDS kBselStage channels at a time; the channels are taken eight at a time, their
+// loads issued together.
+constexpr int kBselStage = 512;
+template <DT ET, DT ST>
+__global__ __launch_bounds__(256) void bsel_down_kernel(BselArgs a) {
+  __shared__ float As[kBselStage * kBselMaxB];
+  __shared__ size_t rows[kBselStage];
+  const int h = blockIdx.x * 256 + threadIdx.x, q = blockIdx.y;
+  const int nk = *a.nkept, C = nk + a.NS * a.IS;
+  const int c0 = (int)((long long)C * q / a.nchunk), c1 = (int)((long long)C * (q + 1) / a.nchunk);
+  constexpr size_t kShared = (size_t)1 << 62;  // marks a shared expert's row
+  float acc[kBselMaxB];
+#pragma unroll
+  for (int b = 0; b < kBselMaxB; ++b) acc[b] = 0.0f;
+  const int hh = min(h, a.H - 1);
+  for (int base = c0; base < c1; base += kBselStage) {
+    const int nc = min(kBselStage, c1 - base);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nc * a.B; i += 256) As[i] = a.A[(size_t)base * a.B + i];
+    for (int i = threadIdx.x; i < nc; i += 256) {
+      const int ch = base + i;
+      if (ch < nk) {
+        const int f = a.kc[ch], t = f / a.I, j = f - t * a.I;
+        rows[i] = (size_t)a.touched[t] * a.I + j;
+      } else {
+        rows[i] = (size_t)(ch - nk) | kShared;
+      }
+    }
+    __syncthreads();
+    for (int i0 = 0; i0 < nc; i0 += 8) {
+      float d[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const size_t r = rows[min(i0 + u, nc - 1)];
+        d[u] = (r & kShared) ? bsel_elem<ST>(a.sh_down_t, (r & (kShared - 1)) * a.H + hh)
+                             : bsel_elem<ET>(a.down_t, r * a.H + hh);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + u < nc) {
+#pragma unroll
+          for (int b = 0; b < kBselMaxB; ++b)
+            if (b < a.B) acc[b] = fmaf(As[(i0 + u) * a.B + b], d[u], acc[b]);
+        }
+      }
+    }
+  }
+  if (h < a.H) {
+#pragma unroll
+    for (int b = 0; b < kBselMaxB; ++b)
+      if (b < a.B) a.part[((size_t)q * a.B + b) * a.H + h] = acc[b];
+  }
+}
+
+__global__ __launch_bounds__(256) void bsel_sum_kernel(BselArgs a) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t n = (size_t)a.B * a.H;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int q = 0; q < a.nchunk; ++q) s += a.part[(size_t)q * n + i];
+  a.y[i] = s;
+}
+
+template <DT ET, DT ST>
+hipError_t launch_bsel_t(const BselArgs& a, int maxcand, hipStream_t s) {
+  hipLaunchKernelGGL(bsel_score_kernel<ET>, dim3((maxcand + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bsel_select_kernel, dim3(1), dim3(1024), 0, s, a);
+  const int cmax = min(a.keep, maxcand) + a.NS * a.IS;
+  if (cmax > 0)
+    hipLaunchKernelGGL((bsel_act_kernel<ET, ST>), dim3((cmax + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bsel_down_kernel<ET, ST>), dim3((a.H + 255) / 256, a.nchunk), dim3(256),
+                     0, s, a);
+  hipLaunchKernelGGL(bsel_sum_kernel, dim3((a.B * a.H + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_bsel(const BselLaunch& L, DT et, DT st, hipStream_t s) {
+  BselArgs a;
+  a.x = L.x; a.ids = L.ids; a.w = L.w;
+  a.n_touched = L.n_touched; a.touched = L.touched; a.offsets = L.offsets; a.slots = L.slots;
+  a.gate = L.gate; a.up = L.up; a.down_t = L.down_t;
+  a.sh_gate = L.sh_gate; a.sh_up = L.sh_up; a.sh_down_t = L.sh_down_t;
+  a.dnorm = L.dnorm; a.S = L.S; a.kc = L.kc; a.kept_out = L.kept_out; a.nkept = L.nkept;
+  a.A = L.A; a.part = L.part; a.y = L.y;
+  a.H = L.H; a.I = L.I; a.E = L.E; a.k = L.k; a.B = L.B; a.NS = L.NS; a.IS = L.IS;
+  a.keep = L.keep; a.nchunk = kBselChunks;
+  if (a.B < 1 || a.B > kBselMaxB || a.H % 8 != 0 || a.keep < 0) return hipErrorInvalidValue;
+  const int maxcand = min(a.E, a.B * a.k) * a.I;
+  if (maxcand > kBselMaxCandidates || a.keep > maxcand) return hipErrorInvalidValue;
+  if (et == DT::BF16 && st == DT::BF16) return launch_bsel_t<DT::BF16, DT::BF16>(a, maxcand, s);
+  if (et == DT::BF16 && st == DT::F32) return launch_bsel_t<DT::BF16, DT::F32>(a, maxcand, s);
+  if (et == DT::F32 && st == DT::F32) return launch_bsel_t<DT::F32, DT::F32>(a, maxcand, s);
+  if (et == DT::F32 && st == DT::BF16) return launch_bsel_t<DT::F32, DT::BF16>(a, maxcand, s);
+  return hipErrorInvalidValue;
+}
 
 // LDS of the channel-sparse kernel: team-reduction buffers, routing, selection words, slot
 // tables, histogram, bin members, this workgroup's kept list, the gate values and score

@@ -84,6 +84,32 @@ int cs_lds_bytes(int H, int threads, int E, int k, int I, int workgroups, int K,
 constexpr int kCsMaxPerThread = 8;  // k*I <= 8 * threads
 constexpr int kCsOwnMax = 64;       // ceil(k*I / workgroups) <= 64 (own candidates)
 
+// Batch-wide channel selection for B <= kBselMaxBatch tokens, after the routing and the
+// union: batch scores S [min(E, B*k)*I], kept candidate indices kc [same], kept ids
+// kept_out [keep] (-1 past the kept count, which goes to nkept), activations A [(kept + NS*IS)
+// * B], partial outputs part [kBselPartChunks][B][H], y [B][H].  keep <= min(E, B*k)*I and
+// min(E, B*k)*I <= kBselMaxCandidates.
+struct BselLaunch {
+  const float* x;
+  const int32_t* ids;
+  const float* w;
+  const int32_t *n_touched, *touched, *offsets, *slots;
+  const void *gate, *up, *down_t, *sh_gate, *sh_up, *sh_down_t;
+  const float* dnorm;
+  float* S;
+  int32_t* kc;
+  int32_t* kept_out;
+  int32_t* nkept;
+  float* A;
+  float* part;
+  float* y;
+  int H, I, E, k, B, NS, IS, keep;
+};
+constexpr int kBselMaxBatch = 16;
+constexpr int kBselPartChunks = 32;
+constexpr int kBselMaxCandidates = 256 * 1024;
+hipError_t launch_bsel(const BselLaunch& L, DT et, DT st, hipStream_t s);
+
 // Routing: router GEMV for B tokens, then one workgroup per token for top-k + softmax.
 struct RouteArgs {
   const float* x;          // [B][H] or null

@@ -51,7 +51,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, rlog, zrow, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, cs_s, sk_mask, cs_y, rec_r, xh, xl, x16, xsc, act, part, total;
+      union_slots, cs_s, sk_mask, cs_y, rec_r, bsel_s, bsel_kc, bsel_nk, bsel_a, bsel_part, xh,
+      xl, x16, xsc, act, part, total;
 };
 
 bool desc_valid(const moe_layer_desc* d, std::string* why) {
@@ -136,6 +137,18 @@ Layout layout_of(const moe_layer_desc* d, bool with_dnorm = true) {
   L.cs_y = take(d->kind == MOE_EXPERT_SWIGLU ? (size_t)d->hidden * 4 : 0);
   // the reader's per-workgroup recovery sums [workgroups][kRecRank] (written every launch)
   L.rec_r = take(kI ? (size_t)kMaxWorkgroups * kRecRank * 4 : 0);
+  // batch-wide channel selection (up to kBselMaxBatch tokens): batch scores and kept candidate
+  // indices [min(E, mb*k)*I], the kept count, activations [(min(E, mb*k)*I + NS*IS)][mb] and
+  // partial outputs [kBselPartChunks][mb][H]
+  const size_t mb = B < (size_t)kBselMaxBatch ? B : (size_t)kBselMaxBatch;
+  const size_t bcand =
+      kI && with_dnorm ? (E < mb * k ? E : mb * k) * (size_t)d->inter : 0;
+  const size_t bsh = (size_t)d->n_shared * (size_t)(d->n_shared > 0 ? d->shared_inter : 0);
+  L.bsel_s = take(bcand * 4);
+  L.bsel_kc = take(bcand * 4);
+  L.bsel_nk = take(bcand ? 4 : 0);
+  L.bsel_a = take(bcand ? (bcand + bsh) * mb * 4 : 0);
+  L.bsel_part = take(bcand ? (size_t)kBselPartChunks * mb * d->hidden * 4 : 0);
   const bool batched_swiglu = d->kind == MOE_EXPERT_SWIGLU && B > 1;
   const size_t xs =
       d->kind == MOE_EXPERT_LINEAR || batched_swiglu ? B * (size_t)d->hidden * 2 : 0;
@@ -929,6 +942,94 @@ moe_status moe_channel_select_sketch(moe_layer layer, const float* x, const int3
   if (!layer->sketch.g)
     return fail(MOE_ERR_ARG, "no sketch: call moe_layer_build_sketch first");
   return channel_select_impl(layer, x, ids, w, keep, mode, kept, y, stream, &layer->sketch);
+}
+
+moe_status moe_channel_select_batch(moe_layer layer, const float* x, int32_t B,
+                                    const int32_t* ids, const float* w, int32_t keep,
+                                    int32_t* kept, int32_t* kept_count, float* y, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const moe_layer_desc& d = layer->d;
+  if (d.kind != MOE_EXPERT_SWIGLU) return fail(MOE_ERR_ARG, "channel selection needs SWIGLU experts");
+  if (!x || !y || !aligned16(x) || !aligned16(y))
+    return fail(MOE_ERR_ARG, "x and y must be given and 16-byte aligned");
+  const int mb = d.max_batch < kBselMaxBatch ? d.max_batch : kBselMaxBatch;
+  if (B < 1 || B > mb) return fail(MOE_ERR_ARG, "B=%d outside [1, min(max_batch, %d)=%d]", B,
+                                   kBselMaxBatch, mb);
+  if ((ids == nullptr) != (w == nullptr))
+    return fail(MOE_ERR_ARG, "ids and w must both be given or both be null");
+  if (!ids && d.router_dtype == MOE_DTYPE_NONE)
+    return fail(MOE_ERR_ARG, "routing inside the call needs a router");
+  const long long maxcand =
+      (long long)(d.n_experts < B * d.top_k ? d.n_experts : B * d.top_k) * d.inter;
+  if (keep < 0 || keep > maxcand)
+    return fail(MOE_ERR_ARG, "keep=%d outside [0, min(E, B*k)*I=%lld]", keep, maxcand);
+  if (keep > 0 && !kept) return fail(MOE_ERR_ARG, "kept must be given when keep > 0");
+  DT et, st, rt;
+  if (moe_status e = b1_types(layer, &et, &st, &rt)) return e;
+  if (et == DT::MXFP4) return fail(MOE_ERR_UNSUPPORTED, "channel selection for MXFP4 experts");
+  if (maxcand > kBselMaxCandidates)
+    return fail(MOE_ERR_UNSUPPORTED, "min(E, B*k)*I=%lld candidates exceed %d", maxcand,
+                kBselMaxCandidates);
+  if (union_lds_bytes(B, d.n_experts) > kUnionMaxLds)
+    return fail(MOE_ERR_UNSUPPORTED, "E*(ceil(B/32)|1)*8 + 8E bytes exceed the union LDS budget (144 KiB)");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int32_t* rid = ids;
+  const float* rw = w;
+  hipError_t e = hipSuccess;
+  if (!ids) {
+    RouteArgs r;
+    r.x = x;
+    r.logits_in = nullptr;
+    r.router = layer->w.router;
+    r.logits = layer->at<float>(layer->L.logits);
+    r.ids = layer->at<int32_t>(layer->L.ids);
+    r.w = layer->at<float>(layer->L.w);
+    r.H = d.hidden;
+    r.E = d.n_experts;
+    r.k = d.top_k;
+    r.B = B;
+    e = launch_route(r, rt, s);
+    rid = r.ids;
+    rw = r.w;
+  }
+  BselLaunch L;
+  L.x = x;
+  L.ids = rid;
+  L.w = rw;
+  L.n_touched = layer->at<int32_t>(layer->L.union_n);
+  L.touched = layer->at<int32_t>(layer->L.union_touched);
+  L.offsets = layer->at<int32_t>(layer->L.union_offsets);
+  L.slots = layer->at<int32_t>(layer->L.union_slots);
+  L.gate = layer->w.gate;
+  L.up = layer->w.up;
+  L.down_t = layer->w.down_t;
+  L.sh_gate = layer->w.sh_gate;
+  L.sh_up = layer->w.sh_up;
+  L.sh_down_t = layer->w.sh_down_t;
+  L.dnorm = layer->at<float>(layer->L.dnorm);
+  L.S = layer->at<float>(layer->L.bsel_s);
+  L.kc = layer->at<int32_t>(layer->L.bsel_kc);
+  L.kept_out = kept;
+  L.nkept = kept_count ? kept_count : layer->at<int32_t>(layer->L.bsel_nk);
+  L.A = layer->at<float>(layer->L.bsel_a);
+  L.part = layer->at<float>(layer->L.bsel_part);
+  L.y = y;
+  L.H = d.hidden;
+  L.I = d.inter;
+  L.E = d.n_experts;
+  L.k = d.top_k;
+  L.B = B;
+  L.NS = d.n_shared;
+  L.IS = d.n_shared > 0 ? d.shared_inter : 0;
+  L.keep = keep;
+  if (e == hipSuccess)
+    e = launch_union(rid, B, d.top_k, d.n_experts, layer->at<int32_t>(layer->L.union_n),
+                     layer->at<int32_t>(layer->L.union_touched),
+                     layer->at<int32_t>(layer->L.union_offsets),
+                     layer->at<int32_t>(layer->L.union_slots), layer->ctrl(), s);
+  if (e == hipSuccess) e = launch_bsel(L, et, st, s);
+  if (e != hipSuccess) return device_fail(e, "batch channel selection launch");
+  return ok();
 }
 
 moe_status moe_union_experts(const int32_t* ids, int32_t B, int32_t k, int32_t E,

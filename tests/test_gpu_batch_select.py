@@ -1,0 +1,161 @@
+"""GPU parity of batch-wide channel selection (moe_channel_select_batch) against the oracle:
+kept ids and their count exactly (entries past the count -1), y of every token within
+tolerance, at small ragged shapes for B = 1, 4, 8 and 16 (keep at several fractions with a gap
+between the keep-th and (keep+1)-th batch scores, keep 0, keep past the candidates), with the
+routing given and routed inside the call, and at the full shapes for B = 8."""
+import numpy as np
+import pytest
+
+from gpu_common import CH_MARGIN_REL, MARGIN, TOL_BF16, HostLayer, cuda_ok, rel_err
+from synth import tensors as T
+from synth.workloads import WORKLOADS
+from oracle import moe_oracle as O
+from test_gpu_channel import SMALL
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not cuda_ok(), reason="needs a GPU")]
+
+
+def _layer(wl, layer=0, max_batch=16):
+    import routed_expert_ffn_route_amd as M
+    desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, wl.n_shared, wl.I_shared,
+                       router_dtype=wl.router_dtype, expert_dtype=wl.expert_dtype,
+                       shared_dtype=wl.shared_dtype, max_batch=max_batch)
+    return M.Layer(desc, T.device_layer(wl, layer))
+
+
+def _batch(wl, hl, B, first, layer=0):
+    """B tokens, each the first redraw with a top-k router margin, routed by the oracle."""
+    X, ids, w = [], [], []
+    for b in range(B):
+        for a in range(64):
+            x = T.x(wl, first + b, layer, a)
+            logits = O.router_logits(x, hl.router)[0]
+            if O.topk_margin(logits, wl.k) >= MARGIN:
+                break
+        else:
+            raise RuntimeError("no margin-satisfying draw")
+        i, ww = O.route(logits[None], wl.k)
+        X.append(x)
+        ids.append(i[0])
+        w.append(ww[0])
+    return np.stack(X), np.stack(ids), np.stack(w)
+
+
+def _dnorm(hl):
+    dn = {}
+
+    def dnorm_of(e):
+        if e not in dn:
+            dn[e] = O.down_norms(hl.expert(e)[2])
+        return dn[e]
+
+    return dnorm_of
+
+
+def _keeps(sv, wanted):
+    """For each wanted keep, the nearest keep in [1, m) whose keep-th and (keep+1)-th batch
+    scores differ by the channel margin (the two sides order candidates alike there)."""
+    srt = np.sort(sv)[::-1]
+    m = srt.size
+    gap = 2 * CH_MARGIN_REL * srt[0]
+    out = []
+    for want in wanted:
+        want = min(max(want, 1), m - 1)
+        for d in range(m):
+            hit = [c for c in (want - d, want + d) if 1 <= c < m and srt[c - 1] - srt[c] >= gap]
+            if hit:
+                out.append(hit[0])
+                break
+    return out
+
+
+def _run(L, wl, X, keep, ids=None, w=None):
+    import torch
+    B = X.shape[0]
+    x = torch.from_numpy(np.asarray(X, dtype=np.float32)).cuda().contiguous()
+    y = torch.empty_like(x)
+    kept = torch.full((max(keep, 1),), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    ti = None if ids is None else torch.from_numpy(ids.astype(np.int32)).cuda()
+    tw = None if w is None else torch.from_numpy(np.asarray(w, np.float32)).cuda()
+    L.channel_select_batch(x, keep, kept, y, kept_count=cnt, ids=ti, w=tw)
+    assert L.check() == 0
+    return kept.cpu().numpy()[:keep], int(cnt.item()), y.cpu().numpy()
+
+
+def _check(L, wl, hl, X, ids, w, keep, given=True):
+    dnorm_of = _dnorm(hl)
+    kept_ref, Y_ref = O.batch_channel_select(X, ids, w, hl.expert, dnorm_of, keep, hl.shared)
+    kept, cnt, Y = _run(L, wl, X, keep, ids if given else None, w if given else None)
+    assert cnt == kept_ref.size, (keep, cnt, kept_ref.size)
+    assert kept[:cnt].tolist() == kept_ref.tolist(), keep
+    assert np.all(kept[cnt:] == -1), keep
+    for b in range(X.shape[0]):
+        assert rel_err(Y[b], Y_ref[b]) <= TOL_BF16, (keep, b, rel_err(Y[b], Y_ref[b]))
+
+
+@pytest.mark.parametrize("B", [1, 4, 8, 16])
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: f"H{w.H}E{w.E}k{w.k}I{w.I}{w.expert_dtype}")
+def test_batch_select_small(wl, B):
+    L = _layer(wl)
+    hl = HostLayer(wl)
+    X, ids, w = _batch(wl, hl, B, 40)
+    cid, sv, _ = O.batch_channel_scores(X, ids, w, hl.expert, _dnorm(hl))
+    m = cid.size
+    for keep in _keeps(sv, [1, m // 8, m // 3 + 1, m - 1]):
+        _check(L, wl, hl, X, ids, w, keep)
+    # every candidate, keep past the touched candidates, nothing
+    _check(L, wl, hl, X, ids, w, m)
+    maxcand = min(wl.E, B * wl.k) * wl.I
+    _check(L, wl, hl, X, ids, w, maxcand)
+    _check(L, wl, hl, X, ids, w, 0)
+    L.close()
+
+
+@pytest.mark.parametrize("wl", SMALL[:2], ids=lambda w: f"H{w.H}E{w.E}k{w.k}I{w.I}")
+def test_batch_select_routed_inside(wl):
+    """ids = NULL: the layer routes the batch itself (tokens drawn with a router margin)."""
+    L = _layer(wl)
+    hl = HostLayer(wl)
+    X, ids, w = _batch(wl, hl, 5, 60)
+    cid, sv, _ = O.batch_channel_scores(X, ids, w, hl.expert, _dnorm(hl))
+    for keep in _keeps(sv, [cid.size // 4]):
+        _check(L, wl, hl, X, ids, w, keep, given=False)
+    L.close()
+
+
+def test_batch_select_rejects():
+    import routed_expert_ffn_route_amd as M
+    import torch
+    wl = SMALL[0]
+    L = _layer(wl, max_batch=4)
+    x = torch.zeros((5, wl.H), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    kept = torch.empty(16, dtype=torch.int32, device="cuda")
+    with pytest.raises(M.MoeError):  # B above max_batch
+        L.channel_select_batch(x, 4, kept, y)
+    with pytest.raises(M.MoeError):  # keep above min(E, B*k)*I
+        L.channel_select_batch(x[:1], wl.k * wl.I + 1, kept, y[:1])
+    L.close()
+
+
+def test_batch_select_full_size():
+    """The stack's shapes (H=2048, E=256, k=8, I=768, one shared expert) at B = 8, keep = 8 *
+    799 (the per-token budget times the batch) moved to the nearest score gap."""
+    import torch
+    wl = WORKLOADS["qwen35_a3b_sparse"]
+    L = _layer(wl, 2, max_batch=8)
+    hl = HostLayer(wl, 2)
+    X, ids, w = _batch(wl, hl, 8, 0, layer=2)
+    cid, sv, _ = O.batch_channel_scores(X, ids, w, hl.expert, _dnorm(hl))
+    (keep,) = _keeps(sv, [8 * 799])
+    dnorm_of = _dnorm(hl)
+    kept_ref, Y_ref = O.batch_channel_select(X, ids, w, hl.expert, dnorm_of, keep, hl.shared)
+    kept, cnt, Y = _run(L, wl, X, keep, ids, w)
+    assert cnt == keep and kept.tolist() == kept_ref.tolist()
+    err = max(rel_err(Y[b], Y_ref[b]) for b in range(8))
+    print(f"batch select B=8 keep={keep} of {cid.size}: max rel err {err:.3e}")
+    assert err <= TOL_BF16
+    L.close()
+    del L
+    torch.cuda.empty_cache()
