@@ -248,7 +248,7 @@ moe_status moe_channel_select_reader(moe_layer layer, const float* x, const int3
  * min(E, B*k)*I (kept are min(keep, n_touched*I)).  kept [keep] (device int32, may be NULL when
  * keep is 0) receives the kept ids ascending, -1 past the kept count; kept_count [1] (device
  * int32, may be NULL) their number.  y [B][H] fp32 (must be given).  BF16 or F32 experts
- * (MOE_ERR_UNSUPPORTED for MXFP4, or for more than 262144 candidates).  Enqueues on `stream`
+ * (MOE_ERR_UNSUPPORTED for MXFP4, or for min(E, B*k)*I above 98304).  Enqueues on `stream`
  * the routing (when ids is NULL), the touched-expert union and five launches: batch scores
  * (one wave per candidate), the selection (one workgroup), the kept and shared channels'
  * activations (one wave per channel), the down products in 32 channel chunks, their sum. */

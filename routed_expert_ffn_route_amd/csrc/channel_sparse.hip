@@ -1204,10 +1204,10 @@ hipError_t launch_cpt(const CSLaunch& L, int wgs, int threads, int lds, hipStrea
 // expert, ascending expert id, so ascending e*I + j); a channel's batch score is the sum over
 // the tokens routed to its expert of w_{b,e} |silu(g_j.x_b)|, times ||d_j||; the `keep` best
 // are computed exactly for every token routed to their expert, each row read once for the
-// batch, and the shared experts for every token.  Five small launches after the routing and
-// the union: scores (one wave per candidate), selection (one workgroup), activations (one wave
-// per kept or shared channel), down products (channel chunks x column blocks, partial rows)
-// and their sum in chunk order.
+// batch, and the shared experts for every token.  Five launches after the routing and the
+// union: scores (each gate row read once for all its tokens; the gate values kept), selection
+// (one workgroup), activations (the kept up rows and the shared experts' rows), down products
+// (channel chunks x column blocks, partial rows) and their sum in chunk order.
 struct BselArgs {
   const float* x;                                     // [B][H]
   const int32_t* ids;                                 // [B][k]
@@ -1216,215 +1216,530 @@ struct BselArgs {
   const void *gate, *up, *down_t, *sh_gate, *sh_up, *sh_down_t;
   const float* dnorm;                                 // [E*I]
   float* S;                                           // [n_t*I] batch scores
-  int32_t* kc;                                        // [keep] kept candidate indices
+  float* G;                                           // [n_t*I][B] gate values, by slot rank
+  i32x4* desc;  // [keep] per kept channel: row e*I + j, candidate, first slot, slots (-1 past)
   int32_t* kept_out;                                  // [keep] kept ids e*I + j
   int32_t* nkept;                                     // [1]
-  float* A;                                           // [keep + NS*IS][B] activations x w
+  float* A;                                           // [NS*IS + keep][B] activations x w
   float* part;                                        // [nchunk][B][H]
   float* y;                                           // [B][H]
   int H, I, E, k, B, NS, IS, keep, nchunk;
+  int nkmax;  // min(keep, min(E, B*k)*I): descriptors written
 };
 constexpr int kBselMaxB = kBselMaxBatch;
 constexpr int kBselChunks = kBselPartChunks;
 
+// Eight consecutive weights of a row (BF16: one 16-byte load; F32: two), as raw words.
 template <DT dt>
-__device__ __forceinline__ float bsel_elem(const void* base, size_t i) {
-  if constexpr (dt == DT::BF16)
-    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[i] << 16);
-  else
-    return reinterpret_cast<const float*>(base)[i];
-}
-// row . x_b over H (8-element chunks per lane, fp32 sums), in every lane
+struct Row8 {
+  u32x4 a, b;
+};
 template <DT dt>
-__device__ inline float bsel_dot(const void* rows, size_t row, const float* xb, int H,
-                                 int lane) {
-  float acc = 0.0f;
-  for (int ch = lane; ch < H / 8; ch += kWave) {
-    const size_t o = row * (size_t)H + 8 * (size_t)ch;
-    const f32x4 x0 = reinterpret_cast<const f32x4*>(xb)[2 * ch];
-    const f32x4 x1 = reinterpret_cast<const f32x4*>(xb)[2 * ch + 1];
-    acc = fmaf(bsel_elem<dt>(rows, o), x0.x, acc);
-    acc = fmaf(bsel_elem<dt>(rows, o + 1), x0.y, acc);
-    acc = fmaf(bsel_elem<dt>(rows, o + 2), x0.z, acc);
-    acc = fmaf(bsel_elem<dt>(rows, o + 3), x0.w, acc);
-    acc = fmaf(bsel_elem<dt>(rows, o + 4), x1.x, acc);
-    acc = fmaf(bsel_elem<dt>(rows, o + 5), x1.y, acc);
-    acc = fmaf(bsel_elem<dt>(rows, o + 6), x1.z, acc);
-    acc = fmaf(bsel_elem<dt>(rows, o + 7), x1.w, acc);
+__device__ __forceinline__ Row8<dt> ld_row8(const void* base, size_t e) {
+  Row8<dt> r;
+  if constexpr (dt == DT::BF16) {
+    r.a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + e);
+    r.b = r.a;
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(base) + e);
+    r.a = p[0];
+    r.b = p[1];
   }
-  return wave_sum(acc);
+  return r;
+}
+// sum over the eight of weight * x
+template <DT dt>
+__device__ __forceinline__ float dot_row8(const Row8<dt>& r, f32x4 x0, f32x4 x1, float acc) {
+  if constexpr (dt == DT::BF16) {
+    acc = fmaf(__uint_as_float(r.a.x << 16), x0.x, acc);
+    acc = fmaf(__uint_as_float(r.a.x & 0xFFFF0000u), x0.y, acc);
+    acc = fmaf(__uint_as_float(r.a.y << 16), x0.z, acc);
+    acc = fmaf(__uint_as_float(r.a.y & 0xFFFF0000u), x0.w, acc);
+    acc = fmaf(__uint_as_float(r.a.z << 16), x1.x, acc);
+    acc = fmaf(__uint_as_float(r.a.z & 0xFFFF0000u), x1.y, acc);
+    acc = fmaf(__uint_as_float(r.a.w << 16), x1.z, acc);
+    acc = fmaf(__uint_as_float(r.a.w & 0xFFFF0000u), x1.w, acc);
+  } else {
+    acc = fmaf(__uint_as_float(r.a.x), x0.x, acc);
+    acc = fmaf(__uint_as_float(r.a.y), x0.y, acc);
+    acc = fmaf(__uint_as_float(r.a.z), x0.z, acc);
+    acc = fmaf(__uint_as_float(r.a.w), x0.w, acc);
+    acc = fmaf(__uint_as_float(r.b.x), x1.x, acc);
+    acc = fmaf(__uint_as_float(r.b.y), x1.y, acc);
+    acc = fmaf(__uint_as_float(r.b.z), x1.z, acc);
+    acc = fmaf(__uint_as_float(r.b.w), x1.w, acc);
+  }
+  return acc;
+}
+// Chunks of eight per lane per pass over a row (registers of NR rows in flight).
+template <DT dt>
+constexpr int bsel_cpl() { return dt == DT::BF16 ? 4 : 2; }
+
+// Dots of NR rows (row r: element offset ro[r] in tensor w[r]) with up to four tokens' x (xb[i],
+// nt of them), over H: acc[r][i], summed over the wave (every lane).  Each lane takes chunks
+// of eight, CPL per pass, rows loaded once per pass for all tokens.
+template <DT dt, int NR>
+__device__ __forceinline__ void bsel_dots(const void* const (&w)[NR], const size_t (&ro)[NR],
+                                          const float* const (&xb)[4], int nt, int H, int lane,
+                                          float (&acc)[NR][4]) {
+  constexpr int CPL = bsel_cpl<dt>();
+  const int nch = H / 8;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[r][i] = 0.0f;
+  for (int c0 = 0; c0 < nch; c0 += kWave * CPL) {
+    Row8<dt> rv[NR][CPL];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int ch = min(c0 + kWave * q + lane, nch - 1);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) rv[r][q] = ld_row8<dt>(w[r], ro[r] + 8 * (size_t)ch);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < nt) {
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+          const int chr = c0 + kWave * q + lane;
+          const int ch = min(chr, nch - 1);
+          f32x4 x0 = reinterpret_cast<const f32x4*>(xb[i])[2 * ch];
+          f32x4 x1 = reinterpret_cast<const f32x4*>(xb[i])[2 * ch + 1];
+          if (chr >= nch) x0 = x1 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int r = 0; r < NR; ++r) acc[r][i] = dot_row8<dt>(rv[r][q], x0, x1, acc[r][i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < nt) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r][i] = wave_sum(acc[r][i]);
+    }
 }
 
+// Scores: workgroup = 4 waves x 4 consecutive channels of one touched expert; each gate row is
+// read once for all the expert's tokens (groups of four).  S[c] = ||d_j|| sum w |silu(g)|;
+// G[c][r] = g for the expert's r-th slot (slot order of the union).
+constexpr int kBselScoreRows = 16;  // channels per workgroup
 template <DT ET>
 __global__ __launch_bounds__(256) void bsel_score_kernel(BselArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int c = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (c >= *a.n_touched * a.I) return;  // whole waves
-  const int t = c / a.I, j = c - t * a.I, e = a.touched[t];
-  const size_t row = (size_t)e * a.I + j;
-  float sc = 0.0f;
-  for (int s = a.offsets[e]; s < a.offsets[e + 1]; ++s) {
-    const int slot = a.slots[s], b = slot / a.k;
-    const float g = bsel_dot<ET>(a.gate, row, a.x + (size_t)b * a.H, a.H, lane);
-    sc = fmaf(a.w[slot], fabsf(silu(g)), sc);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nblk = (a.I + kBselScoreRows - 1) / kBselScoreRows;
+  const int t = blockIdx.x / nblk, blk = blockIdx.x - t * nblk;
+  if (t >= *a.n_touched) return;  // whole workgroups
+  const int e = a.touched[t];
+  const int s0 = a.offsets[e], ne = a.offsets[e + 1] - s0;
+  const int j0 = blk * kBselScoreRows + wave * 4;
+  size_t ro[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ro[r] = ((size_t)e * a.I + min(j0 + r, a.I - 1)) * a.H;
+  float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int tg = 0; tg < ne; tg += 4) {
+    const int nt = min(4, ne - tg);
+    int slot[4];
+    const float* xb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      slot[i] = a.slots[s0 + tg + min(i, nt - 1)];
+      xb[i] = a.x + (size_t)(slot[i] / a.k) * a.H;
+    }
+    float acc[4][4];
+    const void* const wr[4] = {a.gate, a.gate, a.gate, a.gate};
+    bsel_dots<ET, 4>(wr, ro, xb, nt, a.H, lane, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < nt) {
+        const float wi = a.w[slot[i]];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sc[r] = fmaf(wi, fabsf(silu(acc[r][i])), sc[r]);
+          if (lane == r && j0 + r < a.I)
+            a.G[((size_t)t * a.I + j0 + r) * a.B + tg + i] = acc[r][i];
+        }
+      }
+    }
   }
-  if (lane == 0) a.S[c] = sc * a.dnorm[row];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (lane == r && j0 + r < a.I)
+      a.S[(size_t)t * a.I + j0 + r] = sc[r] * a.dnorm[(size_t)e * a.I + j0 + r];
 }
 
-// One workgroup: K = min(keep, m) kept, T the K-th largest batch score (select_threshold),
-// then a compaction in candidate order (ties to the lower candidate): each thread counts the
-// values above T and equal to T in its contiguous share, block scans place them.
+// One wave (every lane): over nb LDS bins (nb = 64 times a power of two; lane l sums the nb/64
+// bins [nb - seg (l + 1), nb - seg l), counted from the top), the bin where the count from the
+// top reaches Kp (0 < Kp <= the total) and Kp minus the count above that bin.
+__device__ __forceinline__ void wave_find_digit(const int* hist, int nb, int Kp, int lane,
+                                                int* bin, int* rem) {
+  const int seg = nb / kWave;
+  const int top = nb - seg * (lane + 1);
+  int cnt = 0;
+  for (int q = 0; q < seg; ++q) cnt += hist[top + ((q + lane) & (seg - 1))];  // rotated reads
+  const int incl = wave_incl_scan(cnt);
+  const int excl = incl - cnt;
+  const uint64_t bal = __ballot(excl < Kp && Kp <= incl);
+  const int L = (int)__builtin_ctzll(bal);
+  const int before = __builtin_amdgcn_readlane(excl, L);
+  const int b = nb - seg * L - 1 - lane;
+  const int hv = lane < seg ? hist[b] : 0;
+  const int incl2 = wave_incl_scan(hv) + before;
+  const int excl2 = incl2 - hv;
+  const uint64_t bal2 = __ballot(lane < seg && excl2 < Kp && Kp <= incl2);
+  const int L2 = (int)__builtin_ctzll(bal2);
+  *bin = nb - seg * L - 1 - L2;
+  *rem = Kp - __builtin_amdgcn_readlane(excl2, L2);
+}
+
+// One workgroup: K = min(keep, m) kept, T the K-th largest batch score, then a compaction in
+// candidate order (ties to the lower candidate).  Thread t holds the scores of candidates
+// [NV t, NV t + NV) in registers, as offsets o = pattern - lo (lo, hi: the smallest and largest
+// pattern).  The offset of T is found digit by digit: the first digit is o >> s1, s1 the
+// smallest shift with (hi - lo) >> s1 < 2048 (the scores spread over at least 1024 bins); each
+// later digit holds the next (up to) 11 bits; each digit comes from an LDS histogram of the
+// offsets that match the digits found so far, and the rank left after the last digit is how
+// many of the values equal to T are kept.  Compaction: each thread counts its values above T
+// and equal to T, block scans give the counts before it, and it writes its kept candidates
+// in order (the touched list staged in LDS; expert and channel tracked without division).
+constexpr uint32_t kNoScore = 0xFFFFFFFFu;
+template <int NV>
 __global__ __launch_bounds__(1024) void bsel_select_kernel(BselArgs a) {
-  __shared__ int hist[kSelBins];
+  static_assert(NV % 4 == 0, "scores are loaded four at a time");
+  constexpr int kT = 1024, kNW = kT / kWave;
+  __shared__ int hist[2048];
   __shared__ int sh[96];
+  __shared__ int tch[kBselMaxCandidates / 8];  // touched experts (at most B*k <= n / 8)
+  __shared__ int offs[kBselMaxExperts + 1];     // the union's slot offsets per expert
   Ctx c;
   c.tid = threadIdx.x;
-  c.nthreads = blockDim.x;
+  c.nthreads = kT;
   c.lane = c.tid & (kWave - 1);
-  const int m = *a.n_touched * a.I;
+  const int wave = c.tid / kWave;
+  const int nt = *a.n_touched;
+  const int m = nt * a.I;  // a multiple of 8
   const int K = min(a.keep, m);
-  const uint32_t* u = reinterpret_cast<const uint32_t*>(a.S);  // non-negative: patterns order
   const bool every = K >= m;
-  uint32_t T = 0;
-  int need = 0, ties = 0;
-  if (K > 0 && !every) T = select_threshold(u, m, K, &need, &ties, hist, sh, c);
-  const int per = (m + c.nthreads - 1) / c.nthreads;
-  const int f0 = min(c.tid * per, m), f1 = min(f0 + per, m);
+  const int f0 = c.tid * NV;
+  uint32_t v[NV];
+  {
+    const u32x4* u4 = reinterpret_cast<const u32x4*>(a.S);  // non-negative: patterns order
+#pragma unroll
+    for (int q = 0; q < NV / 4; ++q) {
+      const u32x4 x = u4[min(f0 / 4 + q, m / 4 - 1)];
+      v[4 * q] = x.x;
+      v[4 * q + 1] = x.y;
+      v[4 * q + 2] = x.z;
+      v[4 * q + 3] = x.w;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)  // past m: a pattern no score has (a negative NaN)
+      if (f0 + i >= m) v[i] = kNoScore;
+  }
+  for (int i = c.tid; i < nt; i += kT) tch[i] = a.touched[i];
+  for (int i = c.tid; i <= a.E; i += kT) offs[i] = a.offsets[i];
+  // the scores' range; each value becomes its offset from the smallest (past m: above span)
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    lo = min(lo, v[i]);
+    hi = max(hi, v[i] != kNoScore ? v[i] : 0u);
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (c.lane == 0) {
+    sh[4 + wave] = (int)lo;
+    sh[20 + wave] = (int)hi;
+  }
+  __syncthreads();
+  lo = c.lane < kNW ? (uint32_t)sh[4 + c.lane] : 0xFFFFFFFFu;
+  hi = c.lane < kNW ? (uint32_t)sh[20 + c.lane] : 0u;
+  lo = __builtin_amdgcn_readfirstlane(wave_min_u32(lo));
+  hi = __builtin_amdgcn_readfirstlane(wave_max_u32(hi));
+  const uint32_t span = hi - lo;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] -= lo;
+  // (a score is finite and non-negative, so lo <= 0x7FC00000 and a missing value's offset,
+  // at least 0x803FFFFF, exceeds span; shifted right by at most 21 it still exceeds it)
+  uint32_t To = 0;  // the offset of T
+  int need = 0;
+  if (K > 0 && !every) {
+    int shift = 0;
+    while (shift < 32 && (span >> shift) >= 2048u) ++shift;
+    // the first digit: offsets >> shift (below 2048)
+    for (int i = c.tid; i < 2048; i += kT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (v[i] <= span) atomicAdd(&hist[v[i] >> shift], 1);
+    // P: the offset of T shifted right by `prev` (the digits found so far)
+    uint32_t P = 0;
+    int prev = shift;
+    int rem = K;
+    for (;;) {
+      __syncthreads();
+      if (c.tid < kWave) {
+        int d, r;
+        wave_find_digit(hist, 2048, rem, c.lane, &d, &r);
+        if (c.lane == 0) {
+          sh[0] = d;
+          sh[1] = r;
+        }
+      }
+      __syncthreads();
+      P += (uint32_t)sh[0];
+      rem = sh[1];
+      if (prev == 0) break;
+      // the next digit: bits [shift, prev) of the offsets whose bits from prev up are P's
+      shift = prev > 11 ? prev - 11 : 0;
+      const uint32_t base = P << (prev - shift);
+      for (int i = c.tid; i < 2048; i += kT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if ((v[i] >> prev) == P) atomicAdd(&hist[(v[i] >> shift) - base], 1);
+      P = base;
+      prev = shift;
+    }
+    To = P;
+    need = rem;
+  }
+  // compaction in candidate order
   int gt = 0, eq = 0;
   if (K > 0) {
-    for (int f = f0; f < f1; ++f) {
-      const uint32_t v = u[f];
-      gt += (every || v > T) ? 1 : 0;
-      eq += (!every && v == T) ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool ok = v[i] <= span;
+      gt += ok && (every || v[i] > To) ? 1 : 0;
+      eq += ok && !every && v[i] == To ? 1 : 0;
     }
   }
   int tot;
   int gb = block_excl_scan(gt, sh + 48, c, &tot);
   int eb = block_excl_scan(eq, sh + 48, c, &tot);
-  if (K > 0) {
-    for (int f = f0; f < f1; ++f) {
-      const uint32_t v = u[f];
-      const bool above = every || v > T;
-      const bool tie = !every && v == T;
+  if (K > 0 && f0 < m) {
+    int t = f0 / a.I, j = f0 - t * a.I;
+    int e = tch[t], s0 = offs[e], ne = offs[e + 1] - s0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool ok = v[i] <= span;
+      const bool above = ok && (every || v[i] > To);
+      const bool tie = ok && !every && v[i] == To;
       if (above || (tie && eb < need)) {
         const int pos = gb + min(eb, need);
-        const int t = f / a.I;
-        a.kc[pos] = f;
-        a.kept_out[pos] = a.touched[t] * a.I + (f - t * a.I);
+        a.kept_out[pos] = e * a.I + j;
+        a.desc[pos] = i32x4{e * a.I + j, f0 + i, s0, ne};
       }
       gb += above ? 1 : 0;
       eb += tie ? 1 : 0;
+      if (++j == a.I && f0 + i + 1 < m) {
+        j = 0;
+        ++t;
+        e = tch[t];
+        s0 = offs[e];
+        ne = offs[e + 1] - s0;
+      }
     }
   }
-  for (int i = K + c.tid; i < a.keep; i += c.nthreads) a.kept_out[i] = -1;
+  for (int i = K + c.tid; i < a.keep; i += kT) {
+    a.kept_out[i] = -1;
+    a.desc[i] = i32x4{-1, -1, 0, 0};
+  }
   if (c.tid == 0) *a.nkept = K;
 }
 
-// One wave per channel: kept routed channels [0, nk), then the shared ones; lane b < B ends
-// holding w_{b,e} silu(g.x_b) (v.x_b) (0 for a token not routed to the channel's expert).
+// One wave per channel: the shared experts' channels first (gate and up rows, every token;
+// these waves depend on nothing else and are the longest), then the kept routed channels (from
+// their descriptors: the up row, the gate values kept by the scores; waves past the kept
+// count exit).  Channel c (shared: c < NS*IS; kept: NS*IS + its rank) ends with lane b < B
+// holding w_{b,e} silu(g.x_b) (v.x_b) (0 for a token not routed to the channel's expert) and
+// writing A[c][b].
 template <DT ET, DT ST>
 __global__ __launch_bounds__(256) void bsel_act_kernel(BselArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int ch = blockIdx.x * 4 + threadIdx.x / kWave;
-  const int nk = *a.nkept, C = nk + a.NS * a.IS;
-  if (ch >= C) return;
+  const int NSI = a.NS * a.IS;
   float val = 0.0f;
-  if (ch < nk) {
-    const int f = a.kc[ch], t = f / a.I, j = f - t * a.I, e = a.touched[t];
-    const size_t row = (size_t)e * a.I + j;
-    for (int s = a.offsets[e]; s < a.offsets[e + 1]; ++s) {
-      const int slot = a.slots[s], b = slot / a.k;
-      const float* xb = a.x + (size_t)b * a.H;
-      const float g = bsel_dot<ET>(a.gate, row, xb, a.H, lane);
-      const float v = bsel_dot<ET>(a.up, row, xb, a.H, lane);
-      if (lane == b) val = a.w[slot] * silu(g) * v;
+  if (ch < NSI) {
+    const size_t ro[2] = {(size_t)ch * a.H, (size_t)ch * a.H};
+    const void* const wr[2] = {a.sh_gate, a.sh_up};
+    for (int tg = 0; tg < a.B; tg += 4) {
+      const int nt = min(4, a.B - tg);
+      const float* xb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xb[i] = a.x + (size_t)(tg + min(i, nt - 1)) * a.H;
+      float gv[2][4];
+      bsel_dots<ST, 2>(wr, ro, xb, nt, a.H, lane, gv);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nt && lane == tg + i) val = silu(gv[0][i]) * gv[1][i];
     }
   } else {
-    const size_t row = (size_t)(ch - nk);
-    for (int b = 0; b < a.B; ++b) {
-      const float* xb = a.x + (size_t)b * a.H;
-      const float g = bsel_dot<ST>(a.sh_gate, row, xb, a.H, lane);
-      const float v = bsel_dot<ST>(a.sh_up, row, xb, a.H, lane);
-      if (lane == b) val = silu(g) * v;
+    // past the descriptors written (the grid's last workgroup), or past the kept count
+    if (ch - NSI >= a.nkmax) return;  // whole waves
+    const i32x4 d = a.desc[ch - NSI];
+    if (d.x < 0) return;
+    const int f = d.y, s0 = d.z, ne = d.w;
+    const size_t ro[1] = {(size_t)d.x * a.H};
+    const void* const wr[1] = {a.up};
+    for (int tg = 0; tg < ne; tg += 4) {
+      const int nt = min(4, ne - tg);
+      int slot[4];
+      const float* xb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        slot[i] = a.slots[s0 + tg + min(i, nt - 1)];
+        xb[i] = a.x + (size_t)(slot[i] / a.k) * a.H;
+      }
+      float acc[1][4];
+      bsel_dots<ET, 1>(wr, ro, xb, nt, a.H, lane, acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < nt && lane == slot[i] / a.k) {
+          const float g = a.G[(size_t)f * a.B + tg + i];
+          val = a.w[slot[i]] * silu(g) * acc[0][i];
+        }
+      }
     }
   }
   if (lane < a.B) a.A[(size_t)ch * a.B + lane] = val;
 }
 
-// Channel chunk q of kBselChunks x a column block of 256: part[q][b][h] = sum over the
-// chunk's channels (in order) of A[ch][b] d_ch[h].  The chunk's A rows and row offsets are
-// staged in LDS kBselStage channels at a time; the channels are taken eight at a time, their
-// loads issued together.
-constexpr int kBselStage = 512;
+// Down products: workgroup = 16 waves over one column block of 256 (lane: four consecutive
+// columns) and channel chunk q of kBselChunks (channels in A's order: the shared ones, then the
+// kept ones); wave w takes the w-th sixteenth of the chunk (in order), its A rows and row
+// offsets staged in LDS by the workgroup; tokens in blocks of eight; the 16 waves' sums are
+// added in wave order through LDS, every wave adding its share of the outputs.
+// part[q][b][h] = that chunk's sum of A[c][b] d_c[h].
+constexpr int kBselDownWaves = 16;
+constexpr int kBselStage = 256;   // channels staged at a time
+constexpr int kBselTB = 8;        // tokens per block
+constexpr int kBselDownU = 8;     // rows in flight per lane
+template <DT dt>
+__device__ __forceinline__ f32x4 ld4(const void* base, size_t e) {
+  if constexpr (dt == DT::BF16) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(base) + e);
+    return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + e);
+  }
+}
 template <DT ET, DT ST>
-__global__ __launch_bounds__(256) void bsel_down_kernel(BselArgs a) {
+__global__ __launch_bounds__(1024) void bsel_down_kernel(BselArgs a) {
   __shared__ float As[kBselStage * kBselMaxB];
-  __shared__ size_t rows[kBselStage];
-  const int h = blockIdx.x * 256 + threadIdx.x, q = blockIdx.y;
-  const int nk = *a.nkept, C = nk + a.NS * a.IS;
+  __shared__ uint64_t rows[kBselStage];
+  __shared__ f32x4 red[kBselDownWaves * kBselTB * kWave];  // [wave][token][lane]
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int h0 = (blockIdx.x * kWave + lane) * 4;
+  const int hh = min(h0, a.H - 4);
+  const int q = blockIdx.y;
+  const int NSI = a.NS * a.IS;
+  const int C = NSI + *a.nkept;
   const int c0 = (int)((long long)C * q / a.nchunk), c1 = (int)((long long)C * (q + 1) / a.nchunk);
-  constexpr size_t kShared = (size_t)1 << 62;  // marks a shared expert's row
-  float acc[kBselMaxB];
+  constexpr uint64_t kShared = (uint64_t)1 << 62;  // marks a shared expert's row
+  for (int tb = 0; tb < a.B; tb += kBselTB) {
+    const int nb = min(kBselTB, a.B - tb);
+    f32x4 acc[kBselTB];
 #pragma unroll
-  for (int b = 0; b < kBselMaxB; ++b) acc[b] = 0.0f;
-  const int hh = min(h, a.H - 1);
-  for (int base = c0; base < c1; base += kBselStage) {
-    const int nc = min(kBselStage, c1 - base);
-    __syncthreads();
-    for (int i = threadIdx.x; i < nc * a.B; i += 256) As[i] = a.A[(size_t)base * a.B + i];
-    for (int i = threadIdx.x; i < nc; i += 256) {
-      const int ch = base + i;
-      if (ch < nk) {
-        const int f = a.kc[ch], t = f / a.I, j = f - t * a.I;
-        rows[i] = (size_t)a.touched[t] * a.I + j;
-      } else {
-        rows[i] = (size_t)(ch - nk) | kShared;
+    for (int b = 0; b < kBselTB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int base = c0; base < c1; base += kBselStage) {
+      const int nc = min(kBselStage, c1 - base);
+      __syncthreads();
+      for (int i = threadIdx.x; i < nc * a.B; i += blockDim.x) As[i] = a.A[(size_t)base * a.B + i];
+      for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+        const int c = base + i;
+        rows[i] = c < NSI ? ((uint64_t)c * a.H) | kShared
+                          : (uint64_t)a.kept_out[c - NSI] * a.H;
       }
-    }
-    __syncthreads();
-    for (int i0 = 0; i0 < nc; i0 += 8) {
-      float d[8];
+      __syncthreads();
+      const int i0 = nc * wave / kBselDownWaves, i1 = nc * (wave + 1) / kBselDownWaves;
+      for (int i = i0; i < i1; i += kBselDownU) {
+        f32x4 d[kBselDownU];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const size_t r = rows[min(i0 + u, nc - 1)];
-        d[u] = (r & kShared) ? bsel_elem<ST>(a.sh_down_t, (r & (kShared - 1)) * a.H + hh)
-                             : bsel_elem<ET>(a.down_t, r * a.H + hh);
-      }
+        for (int u = 0; u < kBselDownU; ++u) {
+          const uint64_t r = rows[min(i + u, i1 - 1)];
+          d[u] = (r & kShared) ? ld4<ST>(a.sh_down_t, (r & (kShared - 1)) + hh)
+                               : ld4<ET>(a.down_t, r + hh);
+        }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (i0 + u < nc) {
+        for (int u = 0; u < kBselDownU; ++u) {
+          if (i + u < i1) {
 #pragma unroll
-          for (int b = 0; b < kBselMaxB; ++b)
-            if (b < a.B) acc[b] = fmaf(As[(i0 + u) * a.B + b], d[u], acc[b]);
+            for (int b = 0; b < kBselTB; ++b) {
+              if (b < nb) {
+                const float av = As[(i + u) * a.B + tb + b];
+                acc[b].x = fmaf(av, d[u].x, acc[b].x);
+                acc[b].y = fmaf(av, d[u].y, acc[b].y);
+                acc[b].z = fmaf(av, d[u].z, acc[b].z);
+                acc[b].w = fmaf(av, d[u].w, acc[b].w);
+              }
+            }
+          }
         }
       }
     }
-  }
-  if (h < a.H) {
+    // the waves' sums in wave order: every wave writes its sums, then wave w adds, for token
+    // w % 8 and lanes of half w / 8, the 16 partials
+    __syncthreads();
 #pragma unroll
-    for (int b = 0; b < kBselMaxB; ++b)
-      if (b < a.B) a.part[((size_t)q * a.B + b) * a.H + h] = acc[b];
+    for (int b = 0; b < kBselTB; ++b) red[(wave * kBselTB + b) * kWave + lane] = acc[b];
+    __syncthreads();
+    {
+      const int b = wave % kBselTB, l0 = (wave / kBselTB) * (kWave / 2);
+      if (lane < kWave / 2 && b < nb) {
+        const int l = l0 + lane;
+        f32x4 s4 = red[b * kWave + l];
+#pragma unroll
+        for (int w2 = 1; w2 < kBselDownWaves; ++w2) {
+          const f32x4 o = red[(w2 * kBselTB + b) * kWave + l];
+          s4.x += o.x;
+          s4.y += o.y;
+          s4.z += o.z;
+          s4.w += o.w;
+        }
+        const int hcol = (blockIdx.x * kWave + l) * 4;
+        if (hcol < a.H)
+          *reinterpret_cast<f32x4*>(a.part + ((size_t)q * a.B + tb + b) * a.H + hcol) = s4;
+      }
+    }
   }
 }
 
+// y = the sum over the chunks, in chunk order (one element per thread, the loads in flight
+// together).
 __global__ __launch_bounds__(256) void bsel_sum_kernel(BselArgs a) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t n = (size_t)a.B * a.H;
   if (i >= n) return;
+  float v[kBselChunks];
+#pragma unroll
+  for (int q = 0; q < kBselChunks; ++q) v[q] = a.part[(size_t)q * n + i];
   float s = 0.0f;
-  for (int q = 0; q < a.nchunk; ++q) s += a.part[(size_t)q * n + i];
+#pragma unroll
+  for (int q = 0; q < kBselChunks; ++q) s += v[q];
   a.y[i] = s;
 }
 
 template <DT ET, DT ST>
 hipError_t launch_bsel_t(const BselArgs& a, int maxcand, hipStream_t s) {
-  hipLaunchKernelGGL(bsel_score_kernel<ET>, dim3((maxcand + 3) / 4), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(bsel_select_kernel, dim3(1), dim3(1024), 0, s, a);
-  const int cmax = min(a.keep, maxcand) + a.NS * a.IS;
+  const int nblk = (a.I + kBselScoreRows - 1) / kBselScoreRows;
+  const int maxt = maxcand / a.I;
+  hipLaunchKernelGGL(bsel_score_kernel<ET>, dim3(maxt * nblk), dim3(256), 0, s, a);
+  const int nv = (maxcand + 1023) / 1024;
+  if (nv <= 8)
+    hipLaunchKernelGGL(bsel_select_kernel<8>, dim3(1), dim3(1024), 0, s, a);
+  else if (nv <= 24)
+    hipLaunchKernelGGL(bsel_select_kernel<24>, dim3(1), dim3(1024), 0, s, a);
+  else if (nv <= 48)
+    hipLaunchKernelGGL(bsel_select_kernel<48>, dim3(1), dim3(1024), 0, s, a);
+  else
+    hipLaunchKernelGGL(bsel_select_kernel<96>, dim3(1), dim3(1024), 0, s, a);
+  const int cmax = a.NS * a.IS + min(a.keep, maxcand);
   if (cmax > 0)
     hipLaunchKernelGGL((bsel_act_kernel<ET, ST>), dim3((cmax + 3) / 4), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((bsel_down_kernel<ET, ST>), dim3((a.H + 255) / 256, a.nchunk), dim3(256),
-                     0, s, a);
+  hipLaunchKernelGGL((bsel_down_kernel<ET, ST>), dim3((a.H + 255) / 256, a.nchunk),
+                     dim3(kBselDownWaves * kWave), 0, s, a);
   hipLaunchKernelGGL(bsel_sum_kernel, dim3((a.B * a.H + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -1437,13 +1752,15 @@ hipError_t launch_bsel(const BselLaunch& L, DT et, DT st, hipStream_t s) {
   a.n_touched = L.n_touched; a.touched = L.touched; a.offsets = L.offsets; a.slots = L.slots;
   a.gate = L.gate; a.up = L.up; a.down_t = L.down_t;
   a.sh_gate = L.sh_gate; a.sh_up = L.sh_up; a.sh_down_t = L.sh_down_t;
-  a.dnorm = L.dnorm; a.S = L.S; a.kc = L.kc; a.kept_out = L.kept_out; a.nkept = L.nkept;
+  a.dnorm = L.dnorm; a.S = L.S; a.G = L.G; a.desc = reinterpret_cast<i32x4*>(L.desc); a.kept_out = L.kept_out; a.nkept = L.nkept;
   a.A = L.A; a.part = L.part; a.y = L.y;
   a.H = L.H; a.I = L.I; a.E = L.E; a.k = L.k; a.B = L.B; a.NS = L.NS; a.IS = L.IS;
   a.keep = L.keep; a.nchunk = kBselChunks;
-  if (a.B < 1 || a.B > kBselMaxB || a.H % 8 != 0 || a.keep < 0) return hipErrorInvalidValue;
+  if (a.B < 1 || a.B > kBselMaxB || a.H % 8 != 0 || a.H < 8 || a.keep < 0)
+    return hipErrorInvalidValue;
   const int maxcand = min(a.E, a.B * a.k) * a.I;
   if (maxcand > kBselMaxCandidates || a.keep > maxcand) return hipErrorInvalidValue;
+  a.nkmax = min(a.keep, maxcand);
   if (et == DT::BF16 && st == DT::BF16) return launch_bsel_t<DT::BF16, DT::BF16>(a, maxcand, s);
   if (et == DT::BF16 && st == DT::F32) return launch_bsel_t<DT::BF16, DT::F32>(a, maxcand, s);
   if (et == DT::F32 && st == DT::F32) return launch_bsel_t<DT::F32, DT::F32>(a, maxcand, s);

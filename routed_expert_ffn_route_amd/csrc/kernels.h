@@ -85,7 +85,8 @@ constexpr int kCsMaxPerThread = 8;  // k*I <= 8 * threads
 constexpr int kCsOwnMax = 64;       // ceil(k*I / workgroups) <= 64 (own candidates)
 
 // Batch-wide channel selection for B <= kBselMaxBatch tokens, after the routing and the
-// union: batch scores S [min(E, B*k)*I], kept candidate indices kc [same], kept ids
+// union: batch scores S [min(E, B*k)*I], gate values G [same][B], descriptors desc (4 ints
+// per kept channel) [min(E, B*k)*I], kept ids
 // kept_out [keep] (-1 past the kept count, which goes to nkept), activations A [(kept + NS*IS)
 // * B], partial outputs part [kBselPartChunks][B][H], y [B][H].  keep <= min(E, B*k)*I and
 // min(E, B*k)*I <= kBselMaxCandidates.
@@ -97,7 +98,8 @@ struct BselLaunch {
   const void *gate, *up, *down_t, *sh_gate, *sh_up, *sh_down_t;
   const float* dnorm;
   float* S;
-  int32_t* kc;
+  float* G;
+  int32_t* desc;
   int32_t* kept_out;
   int32_t* nkept;
   float* A;
@@ -106,8 +108,9 @@ struct BselLaunch {
   int H, I, E, k, B, NS, IS, keep;
 };
 constexpr int kBselMaxBatch = 16;
-constexpr int kBselPartChunks = 32;
-constexpr int kBselMaxCandidates = 256 * 1024;
+constexpr int kBselMaxExperts = 4096;  // (the descriptor's E bound)
+constexpr int kBselPartChunks = 32;  // channel chunks of the down products
+constexpr int kBselMaxCandidates = 96 * 1024;  // held in the selection's registers
 hipError_t launch_bsel(const BselLaunch& L, DT et, DT st, hipStream_t s);
 
 // Routing: router GEMV for B tokens, then one workgroup per token for top-k + softmax.

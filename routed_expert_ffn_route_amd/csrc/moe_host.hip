@@ -51,7 +51,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, rlog, zrow, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, cs_s, sk_mask, cs_y, rec_r, bsel_s, bsel_kc, bsel_nk, bsel_a, bsel_part, xh,
+      union_slots, cs_s, sk_mask, cs_y, rec_r, bsel_s, bsel_g, bsel_desc, bsel_nk, bsel_a, bsel_part, xh,
       xl, x16, xsc, act, part, total;
 };
 
@@ -137,15 +137,17 @@ Layout layout_of(const moe_layer_desc* d, bool with_dnorm = true) {
   L.cs_y = take(d->kind == MOE_EXPERT_SWIGLU ? (size_t)d->hidden * 4 : 0);
   // the reader's per-workgroup recovery sums [workgroups][kRecRank] (written every launch)
   L.rec_r = take(kI ? (size_t)kMaxWorkgroups * kRecRank * 4 : 0);
-  // batch-wide channel selection (up to kBselMaxBatch tokens): batch scores and kept candidate
-  // indices [min(E, mb*k)*I], the kept count, activations [(min(E, mb*k)*I + NS*IS)][mb] and
-  // partial outputs [kBselPartChunks][mb][H]
+  // batch-wide channel selection (up to kBselMaxBatch tokens): batch scores [min(E, mb*k)*I],
+  // the gate values [min(E, mb*k)*I][mb], kept-channel descriptors [min(E, mb*k)*I][4], the
+  // kept count, activations [(NS*IS + min(E, mb*k)*I)][mb] and partial outputs
+  // [kBselPartChunks][mb][H]
   const size_t mb = B < (size_t)kBselMaxBatch ? B : (size_t)kBselMaxBatch;
   const size_t bcand =
       kI && with_dnorm ? (E < mb * k ? E : mb * k) * (size_t)d->inter : 0;
   const size_t bsh = (size_t)d->n_shared * (size_t)(d->n_shared > 0 ? d->shared_inter : 0);
   L.bsel_s = take(bcand * 4);
-  L.bsel_kc = take(bcand * 4);
+  L.bsel_g = take(bcand * mb * 4);
+  L.bsel_desc = take(bcand * 16);
   L.bsel_nk = take(bcand ? 4 : 0);
   L.bsel_a = take(bcand ? (bcand + bsh) * mb * 4 : 0);
   L.bsel_part = take(bcand ? (size_t)kBselPartChunks * mb * d->hidden * 4 : 0);
@@ -1008,7 +1010,8 @@ moe_status moe_channel_select_batch(moe_layer layer, const float* x, int32_t B,
   L.sh_down_t = layer->w.sh_down_t;
   L.dnorm = layer->at<float>(layer->L.dnorm);
   L.S = layer->at<float>(layer->L.bsel_s);
-  L.kc = layer->at<int32_t>(layer->L.bsel_kc);
+  L.G = layer->at<float>(layer->L.bsel_g);
+  L.desc = layer->at<int32_t>(layer->L.bsel_desc);
   L.kept_out = kept;
   L.nkept = kept_count ? kept_count : layer->at<int32_t>(layer->L.bsel_nk);
   L.A = layer->at<float>(layer->L.bsel_a);

@@ -2,7 +2,7 @@
 kept ids and their count exactly (entries past the count -1), y of every token within
 tolerance, at small ragged shapes for B = 1, 4, 8 and 16 (keep at several fractions with a gap
 between the keep-th and (keep+1)-th batch scores, keep 0, keep past the candidates), with the
-routing given and routed inside the call, and at the full shapes for B = 8."""
+routing given and routed inside the call, and at the full shapes for B = 4, 8 and 16."""
 import numpy as np
 import pytest
 
@@ -139,22 +139,24 @@ def test_batch_select_rejects():
     L.close()
 
 
-def test_batch_select_full_size():
-    """The stack's shapes (H=2048, E=256, k=8, I=768, one shared expert) at B = 8, keep = 8 *
-    799 (the per-token budget times the batch) moved to the nearest score gap."""
+@pytest.mark.parametrize("B", [4, 8, 16])
+def test_batch_select_full_size(B):
+    """The stack's shapes (H=2048, E=256, k=8, I=768, one shared expert) at B = 4, 8, 16 (the
+    selection's register layouts for up to 24, 48 and 96 thousand candidates), keep = B * 799
+    (the per-token budget times the batch) moved to the nearest score gap."""
     import torch
     wl = WORKLOADS["qwen35_a3b_sparse"]
-    L = _layer(wl, 2, max_batch=8)
+    L = _layer(wl, 2, max_batch=B)
     hl = HostLayer(wl, 2)
-    X, ids, w = _batch(wl, hl, 8, 0, layer=2)
+    X, ids, w = _batch(wl, hl, B, 100 + B, layer=2)
     cid, sv, _ = O.batch_channel_scores(X, ids, w, hl.expert, _dnorm(hl))
-    (keep,) = _keeps(sv, [8 * 799])
+    (keep,) = _keeps(sv, [B * 799])
     dnorm_of = _dnorm(hl)
     kept_ref, Y_ref = O.batch_channel_select(X, ids, w, hl.expert, dnorm_of, keep, hl.shared)
     kept, cnt, Y = _run(L, wl, X, keep, ids, w)
     assert cnt == keep and kept.tolist() == kept_ref.tolist()
-    err = max(rel_err(Y[b], Y_ref[b]) for b in range(8))
-    print(f"batch select B=8 keep={keep} of {cid.size}: max rel err {err:.3e}")
+    err = max(rel_err(Y[b], Y_ref[b]) for b in range(B))
+    print(f"batch select B={B} keep={keep} of {cid.size}: max rel err {err:.3e}")
     assert err <= TOL_BF16
     L.close()
     del L
