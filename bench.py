@@ -485,7 +485,7 @@ PHASES = {
     "cs": {0: "start", 1: "router rows published", 3: "routing known (top-k + softmax)",
            4: "own scores published", 2: "shared experts streamed",
            5: "all scores gathered", 6: "threshold known", 23: "own kept list ready",
-           7: "kept rows streamed", 8: "top-k: wave 0 keys sorted in runs",
+           24: "kept rows streamed", 7: "reducer: every thread's partials seen", 8: "top-k: wave 0 keys sorted in runs",
            9: "top-k: wave 0 top of its keys", 10: "top-k: wave 0 keys polled",
            11: "top-k: ranked", 12: "router rows computed", 13: "partial output published",
            14: "reducer: all partials arrived", 15: "reducer: y written",

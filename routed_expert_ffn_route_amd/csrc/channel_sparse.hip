@@ -1135,7 +1135,7 @@ __global__ __launch_bounds__(1024) void cs_kernel(CSLaunch L) {
         }
       },
       xv, yv, c);
-  MOE_STAMP_AFTER(c.stamps, 7, yv[0]);
+  MOE_STAMP_AFTER(c.stamps, 24, yv[0]);  // (7 is the reducers' all-polled stamp)
   __syncthreads();  // `big` is reused by the reduction below
 
   // 8. deterministic cross-workgroup sum; its first reducer also advances the count of

@@ -570,14 +570,14 @@ __device__ inline uint64_t wg_topk_bitonic(int n, KeyOf key_of, uint64_t* cand,
   for (int ch = wave; ch < chunks; ch += nwaves) {
     const int i = ch * kWave + lane;
     uint64_t x = i < n ? key_of(i) : 0ull;
-    if (ch == wave) MOE_STAMP(stamps, kStampKeys);
+    if (ch == wave) MOE_STAMP_AFTER(stamps, kStampKeys, x);
     x = sort_runs<KP>(x, lane);
-    if (ch == wave) MOE_STAMP(stamps, kStampSorted);
+    if (ch == wave) MOE_STAMP_AFTER(stamps, kStampSorted, x);
     const int used = min(kWave, n - ch * kWave);
     x = merge_wave<KP>(x, lane, used);
     top = ch == wave ? x : merge_two<KP>(top, x, lane);
   }
-  if (wave == 0) MOE_STAMP(stamps, kStampWaveTop);
+  if (wave == 0) MOE_STAMP_AFTER(stamps, kStampWaveTop, top);
   if (wave >= chunks) call_idle(after_keys, wave - chunks, nwaves - chunks, 0);
   const int runs = min(nwaves, chunks);
   if (wave < runs && lane < KP) cand[wave * KP + lane] = top;

@@ -744,7 +744,7 @@ __device__ inline void topk_local_kp(const uint64_t* rlog, int E, int k, uint64_
         return make_key(__uint_as_float((uint32_t)v), (uint32_t)e);
       },
       keys, c.stamps, after_keys);
-  MOE_STAMP(c.stamps, kStampRanked);
+  MOE_STAMP_AFTER(c.stamps, kStampRanked, top);
   if (c.tid < kWave) {
     // the largest selected logit (lane 0's key) for a max-subtracted softmax
     const float l0 = from_ordered_bits(__builtin_amdgcn_readfirstlane((uint32_t)(top >> 32)));
