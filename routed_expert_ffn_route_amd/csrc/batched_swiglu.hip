@@ -903,7 +903,10 @@ __device__ __forceinline__ void dn_pass(const uint8_t* D, const uint8_t* Ds, int
   using F = Dn<dt>;
   constexpr int EPT = F::EPT;
   const size_t rb = F::row_bytes(H);
-  const int hc = live ? h : 0;  // dead lanes read column 0 and store nothing
+  // dead lanes (past the row's end) read the row's last chunk, which a live lane of the same
+  // wave loads too, and store nothing: column 0 would be a line that another XCD's workgroup
+  // reads, fetched from memory once more
+  const int hc = live ? h : H - F::EPT;
   const gbl_f32* ap[NT];
 #pragma unroll
   for (int p = 0; p < NT; ++p) {
@@ -947,18 +950,46 @@ __device__ __forceinline__ void dn_reduce_store(float (&acc)[NT][Dn<dt>::EPT], f
   }
 }
 
+// The down kernel's work: column block x (dn_cols columns), bucket y, and z = row slice +
+// kDownRowSlices * pass group.  A bucket's passes (at most B pairs) are spread over up to 8
+// pass groups.
+__host__ __device__ inline int dn_pass_groups(int B) {
+  const int g = (B + 7) / 8;
+  return g > 8 ? 8 : g;
+}
+// Blocks are numbered so that every column block of one (bucket, z) runs on the same XCD
+// (block L runs on XCD L % 8): L = 8 (NX (g / 8) + x) + g % 8 with g = y + items z.  The
+// column blocks of a row then share its lines in one L2 (an MXFP4 row's 224 scale bytes span
+// lines that neighbouring column blocks both read), and consecutive (bucket, z) pairs still
+// go round the XCDs.
+struct DnPos {
+  int x, y, z, nz;
+};
+__device__ __forceinline__ bool dn_pos(const BsArgs& a, int nx, DnPos& p) {
+  const int items = a.slots_max + a.NS;
+  p.nz = kDownRowSlices * dn_pass_groups(a.B);
+  const int L = blockIdx.x;
+  const int g = (L / (8 * nx)) * 8 + L % 8;
+  p.x = (L / 8) % nx;
+  if (g >= items * p.nz) return false;
+  p.y = g % items;
+  p.z = g / items;
+  return true;
+}
+
 template <DT dt>
 __device__ __forceinline__ void dn_item(const BsArgs& a, const Bucket& bk, const uint8_t* D,
-                                        const uint8_t* Ds, int rows, float* red, int* pslot) {
+                                        const uint8_t* Ds, int rows, float* red, int* pslot,
+                                        const DnPos& pos) {
   constexpr int EPT = Dn<dt>::EPT;
   constexpr int NTM = Dn<dt>::NTMAX;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.x * dn_cols<dt>() + EPT * lane;
+  const int h = pos.x * dn_cols<dt>() + EPT * lane;
   const bool live = h < a.H;  // H is a multiple of 32 and EPT divides 32
-  // blockIdx.z = row slice + kDownRowSlices * pass group: the slice's channels, split in
-  // kDnWaves contiguous ranges, and every pass group-th pass of the bucket
-  const int rs = blockIdx.z % kDownRowSlices, pg = blockIdx.z / kDownRowSlices;
-  const int ngroups = gridDim.z / kDownRowSlices;
+  // z = row slice + kDownRowSlices * pass group: the slice's channels, split in kDnWaves
+  // contiguous ranges, and every pass group-th pass of the bucket
+  const int rs = pos.z % kDownRowSlices, pg = pos.z / kDownRowSlices;
+  const int ngroups = pos.nz / kDownRowSlices;
   const int per_s = (rows + kDownRowSlices - 1) / kDownRowSlices;
   const int s0 = min(rows, rs * per_s), s1 = min(rows, s0 + per_s);
   const int per = (s1 - s0 + kDnWaves - 1) / kDnWaves;
@@ -1001,20 +1032,23 @@ __global__ __launch_bounds__(kDnWaves * 64) void bs_down_kernel(BsArgs a) {
   constexpr int EPT_MAX = Dn<et>::EPT > Dn<st>::EPT ? Dn<et>::EPT : Dn<st>::EPT;
   __shared__ __attribute__((aligned(16))) float red[(kDnWaves - 1) * EPT_MAX * 64];
   __shared__ int pslot[8];
-  const Bucket bk = bucket_of(a, blockIdx.y);
+  constexpr int cmin = dn_cols<et>() < dn_cols<st>() ? dn_cols<et>() : dn_cols<st>();
+  DnPos pos;
+  if (!dn_pos(a, (a.H + cmin - 1) / cmin, pos)) return;
+  const Bucket bk = bucket_of(a, pos.y);
   if (bk.count == 0) return;
   if (bk.shared) {
-    if (blockIdx.x * dn_cols<st>() >= a.H) return;
+    if (pos.x * dn_cols<st>() >= a.H) return;
     const uint8_t* D = reinterpret_cast<const uint8_t*>(a.sh_down_t) +
                        (size_t)bk.e * a.IS * Dn<st>::row_bytes(a.H);
-    dn_item<st>(a, bk, D, nullptr, a.IS, red, pslot);
+    dn_item<st>(a, bk, D, nullptr, a.IS, red, pslot, pos);
   } else {
-    if (blockIdx.x * dn_cols<et>() >= a.H) return;
+    if (pos.x * dn_cols<et>() >= a.H) return;
     const size_t off = (size_t)bk.e * a.I;
     const uint8_t* D =
         reinterpret_cast<const uint8_t*>(a.down_t) + off * Dn<et>::row_bytes(a.H);
     const uint8_t* Ds = a.down_s ? a.down_s + off * (a.H / 32) : nullptr;
-    dn_item<et>(a, bk, D, Ds, a.I, red, pslot);
+    dn_item<et>(a, bk, D, Ds, a.I, red, pslot, pos);
   }
 }
 
@@ -1071,12 +1105,13 @@ hipError_t launch_bs_typed(const BsArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int cmin = dn_cols<et>() < dn_cols<st>() ? dn_cols<et>() : dn_cols<st>();
-  // pass groups: a bucket's passes (at most B pairs) spread over up to 8 workgroups
-  int groups = (a.B + 7) / 8;
-  groups = groups > 8 ? 8 : groups;
-  hipLaunchKernelGGL((bs_down_kernel<et, st>),
-                     dim3((a.H + cmin - 1) / cmin, items, kDownRowSlices * groups),
-                     dim3(kDnWaves * 64), 0, s, a);
+  // column blocks x (bucket, slice, pass group) pairs, the latter padded to a multiple of 8
+  const long long nx = (a.H + cmin - 1) / cmin;
+  const long long ng = (long long)items * kDownRowSlices * dn_pass_groups(a.B);
+  const long long nblk = nx * ((ng + 7) / 8) * 8;
+  if (nblk > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bs_down_kernel<et, st>), dim3((unsigned)nblk), dim3(kDnWaves * 64), 0,
+                     s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t n = (size_t)a.B * (a.H / 4);
