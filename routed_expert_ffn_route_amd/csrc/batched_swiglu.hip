@@ -1057,24 +1057,28 @@ __global__ __launch_bounds__(kDnWaves * 64) void bs_down_kernel(BsArgs a) {
 // sum_s part[B*k + s*B + b], each partial row the sum of its row slices in slice order
 // ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bs_combine_kernel(BsArgs a) {
+  // workgroup (x, b): token b, columns 4 * [256 x, 256 (x + 1)); which of the token's choices
+  // were used is decided once per workgroup (k <= 64)
+  __shared__ int s_used[64];
   const int n4 = a.H / 4;
+  const int b = blockIdx.y;
+  if (threadIdx.x < a.k) s_used[threadIdx.x] = choice_used(a.ids + (size_t)b * a.k, threadIdx.x, a.E);
+  __syncthreads();
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n4) return;
   const size_t slice = (size_t)a.pairs * n4;  // f32x4 per row slice of the partials
-  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < (size_t)a.B * n4;
-       idx += (size_t)gridDim.x * blockDim.x) {
-    const int b = (int)(idx / n4), c = (int)(idx % n4);
-    const f32x4* P = reinterpret_cast<const f32x4*>(a.part);
-    f32x4 s = {0, 0, 0, 0};
-    for (int i = 0; i < a.k; ++i) {
-      if (!choice_used(a.ids + (size_t)b * a.k, i, a.E)) continue;  // partial not written
+  const f32x4* P = reinterpret_cast<const f32x4*>(a.part);
+  f32x4 s = {0, 0, 0, 0};
+  for (int i = 0; i < a.k; ++i) {
+    if (!s_used[i]) continue;  // partial not written
 #pragma unroll
-      for (int r = 0; r < kDownRowSlices; ++r) s += P[r * slice + (size_t)(b * a.k + i) * n4 + c];
-    }
-    for (int sh = 0; sh < a.NS; ++sh)
-#pragma unroll
-      for (int r = 0; r < kDownRowSlices; ++r)
-        s += P[r * slice + (size_t)(a.B * a.k + sh * a.B + b) * n4 + c];
-    reinterpret_cast<f32x4*>(a.y)[(size_t)b * n4 + c] = s;
+    for (int r = 0; r < kDownRowSlices; ++r) s += P[r * slice + (size_t)(b * a.k + i) * n4 + c];
   }
+  for (int sh = 0; sh < a.NS; ++sh)
+#pragma unroll
+    for (int r = 0; r < kDownRowSlices; ++r)
+      s += P[r * slice + (size_t)(a.B * a.k + sh * a.B + b) * n4 + c];
+  reinterpret_cast<f32x4*>(a.y)[(size_t)b * n4 + c] = s;
 }
 
 template <DT et, DT st>
@@ -1114,10 +1118,7 @@ hipError_t launch_bs_typed(const BsArgs& a, hipStream_t s) {
                      s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t n = (size_t)a.B * (a.H / 4);
-  int g = (int)((n + 255) / 256);
-  g = g > 2048 ? 2048 : g;
-  hipLaunchKernelGGL(bs_combine_kernel, dim3(g), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bs_combine_kernel, dim3((a.H / 4 + 255) / 256, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
