@@ -125,10 +125,12 @@ struct RouteArgs {
 };
 hipError_t launch_route(const RouteArgs& a, DT rt, hipStream_t s);
 
-// Touched-expert union: one workgroup.
+// Touched-expert union: one workgroup (with x: more workgroups split x [nx] into xh, xl as
+// launch_split_x does, in the same launch).
 hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touched,
                         int32_t* touched, int32_t* offsets, int32_t* slots, Ctrl* ctrl,
-                        hipStream_t s);
+                        hipStream_t s, const float* x = nullptr, size_t nx = 0,
+                        uint16_t* xh = nullptr, uint16_t* xl = nullptr);
 int union_lds_bytes(int B, int E);
 constexpr int kUnionMaxLds = 144 * 1024;  // dynamic LDS the union kernel may use
 

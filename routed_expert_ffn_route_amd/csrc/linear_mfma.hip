@@ -19,6 +19,7 @@
 //
 // MFMA v_mfma_f32_16x16x32_bf16 lane layout (checked on gfx950): lane l holds
 // A[l%16][8*(l/16) .. +8], B[8*(l/16) .. +8][l%16] and D[4*(l/16) .. +4][l%16].
+#include "bf16_split.h"
 #include "kernels.h"
 
 namespace moe {
@@ -29,22 +30,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kRows = 32;   // output rows per workgroup
 constexpr int kSplitK = 8;  // K slices per workgroup (waves = 2 row tiles x 8 slices)
 
-__device__ __forceinline__ uint16_t bf16_rne_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 
 // x [B][H] fp32 -> hi, lo [B][H] bf16 with hi + lo ~= x.
 __global__ __launch_bounds__(256) void split_x_kernel(const float* x, size_t n, uint16_t* hi,
                                                       uint16_t* lo) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const float f = x[i];
-    const uint16_t h = bf16_rne_bits(f);
-    hi[i] = h;
-    lo[i] = bf16_rne_bits(f - __uint_as_float((uint32_t)h << 16));
-  }
+  split_x_range(x, n, hi, lo, blockIdx.x * (size_t)blockDim.x + threadIdx.x,
+                (size_t)gridDim.x * blockDim.x);
 }
 
 struct LinArgs {

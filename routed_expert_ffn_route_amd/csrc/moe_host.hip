@@ -446,10 +446,9 @@ static moe_status forward_impl(moe_layer layer, const float* x, int32_t B, const
       e = launch_union(rid, B, d.top_k, d.n_experts, layer->at<int32_t>(layer->L.union_n),
                        layer->at<int32_t>(layer->L.union_touched),
                        layer->at<int32_t>(layer->L.union_offsets),
-                       layer->at<int32_t>(layer->L.union_slots), layer->ctrl(), s);
-    if (e == hipSuccess)
-      e = launch_split_x(x, (size_t)B * d.hidden, layer->at<uint16_t>(layer->L.xh),
-                         layer->at<uint16_t>(layer->L.xl), s);
+                       layer->at<int32_t>(layer->L.union_slots), layer->ctrl(), s, x,
+                       (size_t)B * d.hidden, layer->at<uint16_t>(layer->L.xh),
+                       layer->at<uint16_t>(layer->L.xl));
     if (e == hipSuccess) e = launch_batched_swiglu(a, et, st, s);
     if (e != hipSuccess) return device_fail(e, "batched SwiGLU layer launch");
     return ok();

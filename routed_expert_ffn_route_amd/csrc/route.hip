@@ -10,6 +10,7 @@
 // Union: the distinct experts a batch touches, E[1-(1-k/E)^B] on average for uniform
 // routing ("501B of which 23B are switched on", section 2), with each expert's token
 // list, so that a batched layer reads every touched expert once.
+#include "bf16_split.h"
 #include "kernels.h"
 
 namespace moe {
@@ -118,10 +119,18 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* logits, float* 
 // bitmap rows are padded to an odd word count, so that threads reading the same word of
 // different experts hit different banks, and the count pass also keeps each row's running
 // popcount per word, so a rank is two reads however large the batch.
+// With x given, workgroups 1.. meanwhile split x [nx] into bf16 hi, lo (the batched MFMA
+// paths' operand), which saves that step a launch of its own.
 __global__ __launch_bounds__(1024) void union_kernel(const int32_t* ids, int B, int k, int E,
                                                      int32_t* n_touched, int32_t* touched,
                                                      int32_t* offsets, int32_t* slots,
-                                                     Ctrl* ctrl) {
+                                                     Ctrl* ctrl, const float* x, size_t nx,
+                                                     uint16_t* xh, uint16_t* xl) {
+  if (blockIdx.x > 0) {
+    split_x_range(x, nx, xh, xl, (blockIdx.x - 1) * (size_t)blockDim.x + threadIdx.x,
+                  (size_t)(gridDim.x - 1) * blockDim.x);
+    return;
+  }
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int W = (B + 31) / 32, Wp = W | 1;
   uint32_t* bits = reinterpret_cast<uint32_t*>(smem);                // [E][Wp]
@@ -302,7 +311,7 @@ int union_lds_bytes(int B, int E) {
 
 hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touched,
                         int32_t* touched, int32_t* offsets, int32_t* slots, Ctrl* ctrl,
-                        hipStream_t s) {
+                        hipStream_t s, const float* x, size_t nx, uint16_t* xh, uint16_t* xl) {
   const int lds = union_lds_bytes(B, E);
   static int lds_set = 0;
   if (lds > lds_set) {
@@ -311,8 +320,11 @@ hipError_t launch_union(const int32_t* ids, int B, int k, int E, int32_t* n_touc
     if (e != hipSuccess) return e;
     lds_set = kUnionMaxLds;
   }
-  hipLaunchKernelGGL(union_kernel, dim3(1), dim3(1024), lds, s, ids, B, k, E, n_touched,
-                     touched, offsets, slots, ctrl);
+  // one split workgroup per 8192 elements (8 per thread), at most 64
+  const size_t nsplit = x && nx ? (nx + 8191) / 8192 : 0;
+  const unsigned grid = 1u + (unsigned)(nsplit < 64 ? nsplit : 64);
+  hipLaunchKernelGGL(union_kernel, dim3(grid), dim3(1024), lds, s, ids, B, k, E, n_touched,
+                     touched, offsets, slots, ctrl, x, nx, xh, xl);
   return hipGetLastError();
 }
 
