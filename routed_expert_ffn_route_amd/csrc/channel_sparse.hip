@@ -1220,6 +1220,7 @@ struct BselArgs {
   i32x4* desc;  // [keep] per kept channel: row e*I + j, candidate, first slot, slots (-1 past)
   int32_t* kept_out;                                  // [keep] kept ids e*I + j
   int32_t* nkept;                                     // [1]
+  int32_t* sel;  // [4] T's score pattern, need, K, every; then [chunks][2] above, tie counts
   float* A;                                           // [NS*IS + keep][B] activations x w
   float* part;                                        // [nchunk][B][H]
   float* y;                                           // [B][H]
@@ -1392,16 +1393,15 @@ __device__ __forceinline__ void wave_find_digit(const int* hist, int nb, int Kp,
   *rem = Kp - __builtin_amdgcn_readlane(excl2, L2);
 }
 
-// One workgroup: K = min(keep, m) kept, T the K-th largest batch score, then a compaction in
-// candidate order (ties to the lower candidate).  Thread t holds the scores of candidates
-// [NV t, NV t + NV) in registers, as offsets o = pattern - lo (lo, hi: the smallest and largest
-// pattern).  The offset of T is found digit by digit: the first digit is o >> s1, s1 the
-// smallest shift with (hi - lo) >> s1 < 2048 (the scores spread over at least 1024 bins); each
-// later digit holds the next (up to) 11 bits; each digit comes from an LDS histogram of the
-// offsets that match the digits found so far, and the rank left after the last digit is how
-// many of the values equal to T are kept.  Compaction: each thread counts its values above T
-// and equal to T, block scans give the counts before it, and it writes its kept candidates
-// in order (the touched list staged in LDS; expert and channel tracked without division).
+// One workgroup: K = min(keep, m) kept and T the K-th largest batch score.  Thread t holds
+// the scores of candidates [NV t, NV t + NV) in registers, as offsets o = pattern - lo (lo,
+// hi: the smallest and largest pattern).  The offset of T is found digit by digit: the first
+// digit is o >> s1, s1 the smallest shift with (hi - lo) >> s1 < 2048 (the scores spread over
+// at least 1024 bins); each later digit holds the next (up to) 11 bits; each digit comes from
+// an LDS histogram of the offsets that match the digits found so far, and the rank left after
+// the last digit is how many of the values equal to T are kept.  The kept list itself is
+// written by bsel_count_kernel and bsel_write_kernel over many workgroups: one workgroup
+// walking every candidate again to compact them took longer than finding T.
 constexpr uint32_t kNoScore = 0xFFFFFFFFu;
 template <int NV>
 __global__ __launch_bounds__(1024) void bsel_select_kernel(BselArgs a) {
@@ -1409,8 +1409,6 @@ __global__ __launch_bounds__(1024) void bsel_select_kernel(BselArgs a) {
   constexpr int kT = 1024, kNW = kT / kWave;
   __shared__ int hist[2048];
   __shared__ int sh[96];
-  __shared__ int tch[kBselMaxCandidates / 8];  // touched experts (at most B*k <= n / 8)
-  __shared__ int offs[kBselMaxExperts + 1];     // the union's slot offsets per expert
   Ctx c;
   c.tid = threadIdx.x;
   c.nthreads = kT;
@@ -1436,8 +1434,6 @@ __global__ __launch_bounds__(1024) void bsel_select_kernel(BselArgs a) {
     for (int i = 0; i < NV; ++i)  // past m: a pattern no score has (a negative NaN)
       if (f0 + i >= m) v[i] = kNoScore;
   }
-  for (int i = c.tid; i < nt; i += kT) tch[i] = a.touched[i];
-  for (int i = c.tid; i <= a.E; i += kT) offs[i] = a.offsets[i];
   // the scores' range; each value becomes its offset from the smallest (past m: above span)
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
@@ -1504,48 +1500,114 @@ __global__ __launch_bounds__(1024) void bsel_select_kernel(BselArgs a) {
     To = P;
     need = rem;
   }
-  // compaction in candidate order
-  int gt = 0, eq = 0;
-  if (K > 0) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const bool ok = v[i] <= span;
-      gt += ok && (every || v[i] > To) ? 1 : 0;
-      eq += ok && !every && v[i] == To ? 1 : 0;
-    }
-  }
-  int tot;
-  int gb = block_excl_scan(gt, sh + 48, c, &tot);
-  int eb = block_excl_scan(eq, sh + 48, c, &tot);
-  if (K > 0 && f0 < m) {
-    int t = f0 / a.I, j = f0 - t * a.I;
-    int e = tch[t], s0 = offs[e], ne = offs[e + 1] - s0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const bool ok = v[i] <= span;
-      const bool above = ok && (every || v[i] > To);
-      const bool tie = ok && !every && v[i] == To;
-      if (above || (tie && eb < need)) {
-        const int pos = gb + min(eb, need);
-        a.kept_out[pos] = e * a.I + j;
-        a.desc[pos] = i32x4{e * a.I + j, f0 + i, s0, ne};
-      }
-      gb += above ? 1 : 0;
-      eb += tie ? 1 : 0;
-      if (++j == a.I && f0 + i + 1 < m) {
-        j = 0;
-        ++t;
-        e = tch[t];
-        s0 = offs[e];
-        ne = offs[e + 1] - s0;
-      }
-    }
+  // the threshold for the kept-list kernels: T's score pattern, how many scores equal to T
+  // are kept, K, and whether every candidate is
+  if (c.tid == 0) {
+    a.sel[0] = (int32_t)(To + lo);
+    a.sel[1] = need;
+    a.sel[2] = K;
+    a.sel[3] = every ? 1 : 0;
   }
   for (int i = K + c.tid; i < a.keep; i += kT) {
     a.kept_out[i] = -1;
     a.desc[i] = i32x4{-1, -1, 0, 0};
   }
   if (c.tid == 0) *a.nkept = K;
+}
+
+// The kept list in candidate order (ties to the lower candidate), over chunks of
+// kBselChunkCand candidates, one workgroup of 256 threads (four candidates each) per chunk.
+// bsel_count_kernel: how many of the chunk's candidates are above T and how many equal it.
+__global__ __launch_bounds__(256) void bsel_count_kernel(BselArgs a) {
+  __shared__ int sh[2][8];
+  const int m = *a.n_touched * a.I;  // a multiple of 8
+  const uint32_t T = (uint32_t)a.sel[0];
+  const int K = a.sel[2];
+  const bool every = a.sel[3] != 0;
+  const int f0 = blockIdx.x * kBselChunkCand + threadIdx.x * 4;
+  int above = 0, tie = 0;
+  if (K > 0 && f0 < m) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(a.S)[f0 / 4];
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      above += every || p[q] > T ? 1 : 0;
+      tie += !every && p[q] == T ? 1 : 0;
+    }
+  }
+  Ctx c;
+  c.tid = threadIdx.x;
+  c.nthreads = blockDim.x;
+  c.lane = c.tid & (kWave - 1);
+  int na, nq;
+  (void)block_excl_scan(above, sh[0], c, &na);
+  (void)block_excl_scan(tie, sh[1], c, &nq);
+  if (c.tid == 0) {
+    a.sel[4 + 2 * blockIdx.x] = na;
+    a.sel[5 + 2 * blockIdx.x] = nq;
+  }
+}
+
+// bsel_write_kernel: the counts of the chunks before this one give its first places; within
+// the chunk, block scans give each thread's; a kept candidate's place is (kept above T
+// before it) + min(equal to T before it, need), and it is kept when above T or one of the
+// first `need` equal to T.  It writes the id e*I + j and the descriptor (row, candidate, first
+// slot, slots) of each kept candidate.
+__global__ __launch_bounds__(256) void bsel_write_kernel(BselArgs a) {
+  __shared__ int sh[2][8];
+  const int m = *a.n_touched * a.I;
+  const uint32_t T = (uint32_t)a.sel[0];
+  const int need = a.sel[1], K = a.sel[2];
+  const bool every = a.sel[3] != 0;
+  if (K <= 0 || blockIdx.x * kBselChunkCand >= m) return;  // (uniform)
+  Ctx c;
+  c.tid = threadIdx.x;
+  c.nthreads = blockDim.x;
+  c.lane = c.tid & (kWave - 1);
+  int ba = 0, bt = 0;
+  for (int i = c.tid; i < (int)blockIdx.x; i += c.nthreads) {
+    ba += a.sel[4 + 2 * i];
+    bt += a.sel[5 + 2 * i];
+  }
+  int tot;
+  ba = block_excl_scan(ba, sh[0], c, &tot);
+  ba = tot;
+  bt = block_excl_scan(bt, sh[1], c, &tot);
+  bt = tot;
+  const int f0 = blockIdx.x * kBselChunkCand + c.tid * 4;
+  bool up[4] = {false, false, false, false}, eq[4] = {false, false, false, false};
+  if (f0 < m) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(a.S)[f0 / 4];
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      up[q] = every || p[q] > T;
+      eq[q] = !every && p[q] == T;
+    }
+  }
+  int gb = block_excl_scan((int)up[0] + up[1] + up[2] + up[3], sh[0], c, &tot) + ba;
+  int eb = block_excl_scan((int)eq[0] + eq[1] + eq[2] + eq[3], sh[1], c, &tot) + bt;
+  if (f0 < m) {
+    int t = f0 / a.I, j = f0 - t * a.I;
+    int e = a.touched[t], s0 = a.offsets[e], ne = a.offsets[e + 1] - s0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (up[q] || (eq[q] && eb < need)) {
+        const int pos = gb + min(eb, need);
+        a.kept_out[pos] = e * a.I + j;
+        a.desc[pos] = i32x4{e * a.I + j, f0 + q, s0, ne};
+      }
+      gb += up[q] ? 1 : 0;
+      eb += eq[q] ? 1 : 0;
+      if (++j == a.I && q < 3) {  // (I is a multiple of 8: f0 + q + 1 < m)
+        j = 0;
+        ++t;
+        e = a.touched[t];
+        s0 = a.offsets[e];
+        ne = a.offsets[e + 1] - s0;
+      }
+    }
+  }
 }
 
 // One wave per channel: the shared experts' channels first (gate and up rows, every token;
@@ -1735,6 +1797,9 @@ hipError_t launch_bsel_t(const BselArgs& a, int maxcand, hipStream_t s) {
     hipLaunchKernelGGL(bsel_select_kernel<48>, dim3(1), dim3(1024), 0, s, a);
   else
     hipLaunchKernelGGL(bsel_select_kernel<96>, dim3(1), dim3(1024), 0, s, a);
+  const int nchunks = (maxcand + kBselChunkCand - 1) / kBselChunkCand;
+  hipLaunchKernelGGL(bsel_count_kernel, dim3(nchunks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bsel_write_kernel, dim3(nchunks), dim3(256), 0, s, a);
   const int cmax = a.NS * a.IS + min(a.keep, maxcand);
   if (cmax > 0)
     hipLaunchKernelGGL((bsel_act_kernel<ET, ST>), dim3((cmax + 3) / 4), dim3(256), 0, s, a);
@@ -1753,6 +1818,7 @@ hipError_t launch_bsel(const BselLaunch& L, DT et, DT st, hipStream_t s) {
   a.gate = L.gate; a.up = L.up; a.down_t = L.down_t;
   a.sh_gate = L.sh_gate; a.sh_up = L.sh_up; a.sh_down_t = L.sh_down_t;
   a.dnorm = L.dnorm; a.S = L.S; a.G = L.G; a.desc = reinterpret_cast<i32x4*>(L.desc); a.kept_out = L.kept_out; a.nkept = L.nkept;
+  a.sel = L.sel;
   a.A = L.A; a.part = L.part; a.y = L.y;
   a.H = L.H; a.I = L.I; a.E = L.E; a.k = L.k; a.B = L.B; a.NS = L.NS; a.IS = L.IS;
   a.keep = L.keep; a.nchunk = kBselChunks;

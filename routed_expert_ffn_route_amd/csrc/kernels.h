@@ -89,7 +89,8 @@ constexpr int kCsOwnMax = 64;       // ceil(k*I / workgroups) <= 64 (own candida
 // per kept channel) [min(E, B*k)*I], kept ids
 // kept_out [keep] (-1 past the kept count, which goes to nkept), activations A [(kept + NS*IS)
 // * B], partial outputs part [kBselPartChunks][B][H], y [B][H].  keep <= min(E, B*k)*I and
-// min(E, B*k)*I <= kBselMaxCandidates.
+// min(E, B*k)*I <= kBselMaxCandidates.  sel: the threshold's words (4 ints) and the kept
+// counts of every chunk of kBselChunkCand candidates (2 ints each).
 struct BselLaunch {
   const float* x;
   const int32_t* ids;
@@ -102,6 +103,7 @@ struct BselLaunch {
   int32_t* desc;
   int32_t* kept_out;
   int32_t* nkept;
+  int32_t* sel;
   float* A;
   float* part;
   float* y;
@@ -111,6 +113,10 @@ constexpr int kBselMaxBatch = 16;
 constexpr int kBselMaxExperts = 4096;  // (the descriptor's E bound)
 constexpr int kBselPartChunks = 32;  // channel chunks of the down products
 constexpr int kBselMaxCandidates = 96 * 1024;  // held in the selection's registers
+constexpr int kBselChunkCand = 1024;  // candidates per workgroup of the kept-list kernels
+inline size_t bsel_sel_bytes(size_t cand) {
+  return cand ? 16 + ((cand + kBselChunkCand - 1) / kBselChunkCand) * 8 : 0;
+}
 hipError_t launch_bsel(const BselLaunch& L, DT et, DT st, hipStream_t s);
 
 // Routing: router GEMV for B tokens, then one workgroup per token for top-k + softmax.

@@ -51,7 +51,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
   size_t ctrl, rlog, zrow, logits, ids, w, dnorm, partials, union_n, union_touched, union_offsets,
-      union_slots, cs_s, sk_mask, cs_y, rec_r, bsel_s, bsel_g, bsel_desc, bsel_nk, bsel_a, bsel_part, xh,
+      union_slots, cs_s, sk_mask, cs_y, rec_r, bsel_s, bsel_g, bsel_desc, bsel_nk, bsel_sel, bsel_a, bsel_part, xh,
       xl, x16, xsc, act, part, total;
 };
 
@@ -149,6 +149,7 @@ Layout layout_of(const moe_layer_desc* d, bool with_dnorm = true) {
   L.bsel_g = take(bcand * mb * 4);
   L.bsel_desc = take(bcand * 16);
   L.bsel_nk = take(bcand ? 4 : 0);
+  L.bsel_sel = take(bsel_sel_bytes(bcand));
   L.bsel_a = take(bcand ? (bcand + bsh) * mb * 4 : 0);
   L.bsel_part = take(bcand ? (size_t)kBselPartChunks * mb * d->hidden * 4 : 0);
   const bool batched_swiglu = d->kind == MOE_EXPERT_SWIGLU && B > 1;
@@ -1013,6 +1014,7 @@ moe_status moe_channel_select_batch(moe_layer layer, const float* x, int32_t B,
   L.desc = layer->at<int32_t>(layer->L.bsel_desc);
   L.kept_out = kept;
   L.nkept = kept_count ? kept_count : layer->at<int32_t>(layer->L.bsel_nk);
+  L.sel = layer->at<int32_t>(layer->L.bsel_sel);
   L.A = layer->at<float>(layer->L.bsel_a);
   L.part = layer->at<float>(layer->L.bsel_part);
   L.y = y;
