@@ -792,7 +792,18 @@ def run_linear_sweep(args, wl):
     bmax = max(batches)
     desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, kind=M.LINEAR, router_dtype=None,
                        expert_dtype="bf16", max_batch=bmax)
-    L = M.Layer(desc, T.device_layer(wl, 0))
+    gen = None
+    if args.torch_inputs:
+        # the same shapes and distributions from torch's own device generator (seeded), so
+        # that a profiled run launches no kernel of the input generator library
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(wl.seed)
+        mat = torch.empty((wl.E * wl.I, wl.H), dtype=torch.bfloat16, device="cuda")
+        for r0 in range(0, wl.E * wl.I, 8192):
+            mat[r0:r0 + 8192].normal_(0.0, wl.sigma_gate, generator=gen)
+        L = M.Layer(desc, {"linear": mat})
+    else:
+        L = M.Layer(desc, T.device_layer(wl, 0))
     flush = torch.zeros(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
     sink = torch.empty(512 * 2**20 // 64, dtype=torch.float32, device="cuda")
 
@@ -810,8 +821,14 @@ def run_linear_sweep(args, wl):
     for B in batches:
         nsteps = max(2, min(args.steps, 64 if B <= 64 else 16))
         tokens = list(range(B))
-        logits = [T.device_logits(wl, tokens, case=3 + s % 4) for s in range(4)]
-        x = [T.device_x(wl, tokens, case=3 + s % 4) for s in range(4)]
+        if gen is not None:
+            logits = [torch.randn((B, wl.E), generator=gen, device="cuda") * wl.sigma_logits
+                      for _ in range(4)]
+            x = [torch.randn((B, wl.H), generator=gen, device="cuda") * wl.sigma_x
+                 for _ in range(4)]
+        else:
+            logits = [T.device_logits(wl, tokens, case=3 + s % 4) for s in range(4)]
+            x = [T.device_x(wl, tokens, case=3 + s % 4) for s in range(4)]
         ids = torch.empty((B, wl.k), dtype=torch.int32, device="cuda")
         w = torch.empty((B, wl.k), dtype=torch.float32, device="cuda")
         y = torch.empty((B, wl.I), dtype=torch.float32, device="cuda")
@@ -962,6 +979,9 @@ def main():
                     help="channel-sparse workload: score channels from the ternary sketch "
                          "(moe_channel_select_sketch, eq.-1 scores) instead of exact gates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--torch-inputs", action="store_true",
+                    help="linear sweep: weights, x and logits from torch's device generator "
+                         "(no input-generator kernels in the run)")
     ap.add_argument("--cpu-layers", type=int, default=40, help="layers in the oracle sample")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB ten times (the "
