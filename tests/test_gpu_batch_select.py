@@ -161,3 +161,61 @@ def test_batch_select_full_size(B):
     L.close()
     del L
     torch.cuda.empty_cache()
+
+
+def test_batch_select_ties_at_threshold():
+    """Equal batch scores straddling the keep-th place: four channels of one touched expert are
+    given the same gate and down rows (so both sides compute the same score for each of
+    them, bit for bit on the GPU), and keep is set so that only the first two of them are
+    kept; both sides keep the lower candidates (e*I + j) of a tie."""
+    import torch
+    import routed_expert_ffn_route_amd as M
+    wl = SMALL[-1]
+    hl = HostLayer(wl)
+    X, ids, w = _batch(wl, hl, 4, 140)
+    touched = sorted(set(int(e) for e in ids.ravel()))
+    e0 = touched[len(touched) // 2]
+    dev = T.device_layer(wl, 0)
+    base = {e: hl.expert(e) for e in touched}
+    for j0 in range(0, wl.I - 4, 5):
+        mod = {}
+        for e in touched:
+            # storage form: (dtype tag, rows [I][H])
+            g, v, d = ((a[0], np.array(a[1], copy=True)) for a in base[e])
+            if e == e0:
+                for arr in (g[1], d[1]):
+                    arr[j0 + 1:j0 + 4] = arr[j0]
+            mod[e] = (g, v, d)
+        get = lambda e: mod[e] if e in mod else hl.expert(e)
+        dn = {}
+
+        def dnorm_of(e):
+            if e not in dn:
+                dn[e] = O.down_norms(get(e)[2])
+            return dn[e]
+
+        cid, sv, _ = O.batch_channel_scores(X, ids, w, get, dnorm_of)
+        tie = sv[np.searchsorted(cid, e0 * wl.I + j0)]
+        above = int(np.sum(sv > tie))
+        others = sv[sv != tie]
+        # the tied value is apart from every other score by the channel margin
+        if np.all(np.abs(others - tie) >= 2 * CH_MARGIN_REL * sv.max()):
+            break
+    else:
+        pytest.skip("no isolated score to tie")
+    r0 = e0 * wl.I + j0
+    for key in ("gate", "down_t"):
+        dev[key][r0 + 1:r0 + 4] = dev[key][r0]
+    desc = M.make_desc(wl.H, wl.E, wl.k, wl.I, wl.n_shared, wl.I_shared,
+                       router_dtype=wl.router_dtype, expert_dtype=wl.expert_dtype,
+                       shared_dtype=wl.shared_dtype, max_batch=16)
+    L = M.Layer(desc, dev)
+    torch.cuda.synchronize()
+    keep = above + 2  # two of the four tied channels
+    kept_ref, Y_ref = O.batch_channel_select(X, ids, w, get, dnorm_of, keep, hl.shared)
+    assert e0 * wl.I + j0 + 1 in kept_ref.tolist() and e0 * wl.I + j0 + 2 not in kept_ref
+    kept, cnt, Y = _run(L, wl, X, keep, ids, w)
+    assert cnt == keep and kept.tolist() == kept_ref.tolist()
+    for b in range(X.shape[0]):
+        assert rel_err(Y[b], Y_ref[b]) <= TOL_BF16, (b, rel_err(Y[b], Y_ref[b]))
+    L.close()
