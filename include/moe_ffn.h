@@ -118,8 +118,10 @@ moe_status moe_route(moe_layer layer, const float* x, const float* logits_in, in
 /* The layer.  x [B][H]; y [B][H] (LINEAR: [B][inter]) is overwritten.
  * ids/w: both NULL to route inside the call (needs a router), or both given [B][k].
  * B = 1 runs as one persistent launch (router, top-k, shared and routed experts, and
- * the deterministic cross-workgroup reduction); B > 1 reads each touched expert once
- * for all the tokens routed to it. */
+ * the deterministic cross-workgroup reduction); B = 2 (SWIGLU, hidden <= 8192) as two such
+ * launches, one per token; larger B reads each touched expert once for all the tokens
+ * routed to it (BF16 or MXFP4 experts with BF16 shared experts: otherwise
+ * MOE_ERR_UNSUPPORTED). */
 moe_status moe_ffn_forward(moe_layer layer, const float* x, int32_t B, const int32_t* ids,
                            const float* w, float* y, void* stream);
 
@@ -269,9 +271,10 @@ moe_status moe_union_experts(const int32_t* ids, int32_t B, int32_t k, int32_t E
 /* The routing a layer call last used, read back for checking: enqueues on `stream` a copy
  * of B rows of ids [B][k] (int32, routing order) and w [B][k] (fp32) from the workspace
  * into the caller's device buffers.  Valid after a moe_ffn_forward or moe_channel_select
- * call that routed inside the call (ids == NULL): at B = 1 the top-k chosen inside the
- * single launch, for B > 1 that of the routing step in front of the batched kernels.  At
- * B = 1 with given ids it holds the ids the launch used (-1 for a skipped id).  Other
+ * call that routed inside the call (ids == NULL): at B <= 2 the top-k chosen inside each
+ * token's single launch, for larger B that of the routing step in front of the batched
+ * kernels.  At B <= 2 with given ids it holds the ids the launches used (-1 for a skipped
+ * id).  Other
  * rows, and rows past the last call's B, are unspecified.  Routing k of E experts per
  * token, re-chosen in every layer: "Mixture of Experts Changes the Arithmetic", section
  * "Two Numbers Instead of One".  1 <= B <= max_batch; ids and w must be given. */

@@ -40,6 +40,10 @@ moe_status device_fail(hipError_t e, const char* what) {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxWorkgroups = 512;   // partial-sum rows reserved in the workspace
+#ifndef MOE_B1_LOOP_MAX
+#define MOE_B1_LOOP_MAX 2
+#endif
+constexpr int kB1LoopMax = MOE_B1_LOOP_MAX;  // batches run token by token on the batch-1 kernel
 constexpr int kThreads = 1024;
 // From this batch size on, linear experts use the tiled kernel (x staged in LDS, many tokens
 // per expert); below it the row-owner kernel, which needs no partial rows.
@@ -372,16 +376,24 @@ static moe_status forward_impl(moe_layer layer, const float* x, int32_t B, const
   if (!ids && d.router_dtype == MOE_DTYPE_NONE)
     return fail(MOE_ERR_ARG, "routing inside the call needs a router");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (d.kind == MOE_EXPERT_SWIGLU && B == 1) {
+  // Up to kB1LoopMax tokens run as that many launches of the single-launch layer, one token
+  // each (its routing inside or the token's row of ids and w): below that batch the batched
+  // path's separate routing, union and product launches cost more than the second token saves.
+  if (d.kind == MOE_EXPERT_SWIGLU && (B == 1 || (B <= kB1LoopMax && d.hidden <= 8192))) {
     DT et, st, rt;
     if (moe_status e = b1_types(layer, &et, &st, &rt)) return e;
     if (d.hidden > 8192) return fail(MOE_ERR_UNSUPPORTED, "batch-1 kernel needs hidden <= 8192");
     if (b1_lds_bytes(d.hidden, layer->threads, d.n_experts, d.top_k, et == DT::MXFP4) >
         160 * 1024)
       return fail(MOE_ERR_UNSUPPORTED, "batch-1 kernel LDS exceeds 160 KiB");
-    B1Args a = b1_args(layer, x, ids, w, y);
-    hipError_t e = launch_b1(a, et, st, rt, layer->workgroups, layer->threads, s);
-    if (e != hipSuccess) return device_fail(e, "batch-1 layer launch");
+    for (int b = 0; b < B; ++b) {
+      const size_t xo = (size_t)b * d.hidden, ro = (size_t)b * d.top_k;
+      B1Args a = b1_args(layer, x + xo, ids ? ids + ro : nullptr, w ? w + ro : nullptr, y + xo);
+      a.ids_ws += ro;  // the routing read back: row b
+      a.w_ws += ro;
+      hipError_t e = launch_b1(a, et, st, rt, layer->workgroups, layer->threads, s);
+      if (e != hipSuccess) return device_fail(e, "batch-1 layer launch");
+    }
     return ok();
   }
   if (d.kind == MOE_EXPERT_SWIGLU) {

@@ -68,10 +68,11 @@ def test_random_shapes_match_oracle(p):
         L.routing(ids, w, B=1)
         assert ids.cpu().numpy()[0].tolist() == refs[0][1].tolist()
         assert np.max(np.abs(w.cpu().numpy()[0] - refs[0][2])) <= 1e-6
-        # the batch (the batched layer takes bf16 experts; fp32 ones are refused as documented)
+        # the batch (the batched layer takes bf16 experts; fp32 ones are refused as documented,
+        # except at B = 2, which runs token by token on the batch-1 kernel)
         xb = torch.from_numpy(xs).cuda()
         yb = torch.empty_like(xb)
-        if p["f32"]:
+        if p["f32"] and p["B"] > 2:
             with pytest.raises(M.MoeError) as ei:
                 L.forward(xb, yb, B=p["B"])
             assert ei.value.status == M.MOE_ERR_UNSUPPORTED
@@ -81,6 +82,13 @@ def test_random_shapes_match_oracle(p):
             yb = yb.cpu().numpy()
             for b in range(p["B"]):
                 assert rel_err(yb[b], refs[b][0]) <= TOL_BF16, b
+            if p["B"] <= 2:  # token by token: each launch's own routing, in its row
+                idb = torch.empty((p["B"], wl.k), dtype=torch.int32, device="cuda")
+                wb = torch.empty((p["B"], wl.k), dtype=torch.float32, device="cuda")
+                L.routing(idb, wb, B=p["B"])
+                for b in range(p["B"]):
+                    assert idb.cpu().numpy()[b].tolist() == refs[b][1].tolist(), b
+                    assert np.max(np.abs(wb.cpu().numpy()[b] - refs[b][2])) <= 1e-6, b
         # channel-sparse layer at a random keep count (token 0, when its K-th score is unique)
         n = wl.k * wl.I
         keep = int(round(p["keep_frac"] * n))
