@@ -19,9 +19,9 @@ namespace {
 // Router GEMV for B tokens: one team (256 threads) per R router rows, held in registers;
 // each x chunk load serves the R rows (x is read from L2 once per R rows, not per row), and
 // R rows x TB tokens are reduced per LDS round.
-template <DT RT, int CPT>
+template <DT RT, int CPT, int R>
 __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
-  constexpr int R = 4, TB = 4, NP = R * TB;
+  constexpr int TB = 4, NP = R * TB;
   __shared__ float red[2][4][NP];
   const int t = threadIdx.x, lane = t & 63, wit = t >> 6;
   const int nch = a.H / 8;
@@ -251,18 +251,27 @@ int cpt_for(int H) {
   return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : c <= 8 ? 8 : 0;
 }
 
-template <DT RT>
-hipError_t launch_gemv(const RouteArgs& a, hipStream_t s) {
-  const int rows = (a.E + 3) / 4;  // four router rows per workgroup pass
+template <DT RT, int R>
+hipError_t launch_gemv_r(const RouteArgs& a, hipStream_t s) {
+  const int rows = (a.E + R - 1) / R;  // R router rows per workgroup pass
   const int grid = rows < 2048 ? rows : 2048;
   switch (cpt_for(a.H)) {
-    case 1: hipLaunchKernelGGL((router_gemv_kernel<RT, 1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((router_gemv_kernel<RT, 2>), dim3(grid), dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((router_gemv_kernel<RT, 4>), dim3(grid), dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((router_gemv_kernel<RT, 8>), dim3(grid), dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((router_gemv_kernel<RT, 1, R>), dim3(grid), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((router_gemv_kernel<RT, 2, R>), dim3(grid), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((router_gemv_kernel<RT, 4, R>), dim3(grid), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((router_gemv_kernel<RT, 8, R>), dim3(grid), dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+// Rows per workgroup: four where that still gives most CUs a workgroup (each x load then
+// serves four rows), fewer for small routers (E = 256 with four rows per workgroup left
+// three quarters of the CUs idle).
+template <DT RT>
+hipError_t launch_gemv(const RouteArgs& a, hipStream_t s) {
+  if (a.E >= 768) return launch_gemv_r<RT, 4>(a, s);
+  if (a.E >= 384) return launch_gemv_r<RT, 2>(a, s);
+  return launch_gemv_r<RT, 1>(a, s);
 }
 
 template <DT dt>
