@@ -1056,6 +1056,7 @@ __global__ __launch_bounds__(kDnWaves * 64) void bs_down_kernel(BsArgs a) {
 // Combine: y[b] = sum_i part[b*k + i] (routing order, the choices that were used) +
 // sum_s part[B*k + s*B + b], each partial row the sum of its row slices in slice order
 // ------------------------------------------------------------------------------------
+constexpr int kCombineChunk = 8;  // choices whose partial rows are loaded together
 __global__ __launch_bounds__(256) void bs_combine_kernel(BsArgs a) {
   // workgroup (x, b): token b, columns 4 * [256 x, 256 (x + 1)); which of the token's choices
   // were used is decided once per workgroup (k <= 64)
@@ -1068,11 +1069,26 @@ __global__ __launch_bounds__(256) void bs_combine_kernel(BsArgs a) {
   if (c >= n4) return;
   const size_t slice = (size_t)a.pairs * n4;  // f32x4 per row slice of the partials
   const f32x4* P = reinterpret_cast<const f32x4*>(a.part);
-  f32x4 s = {0, 0, 0, 0};
-  for (int i = 0; i < a.k; ++i) {
-    if (!s_used[i]) continue;  // partial not written
+  const f32x4 zero = {0, 0, 0, 0};
+  f32x4 s = zero;
+  // kCombineChunk choices at a time: every row of the chunk is loaded before any is added,
+  // so the loads are in flight together (a load behind the used test would wait for the
+  // previous sum).  Rows past k are clamped to row k - 1 and rows of unused choices, which
+  // hold an earlier call's data, are read and dropped; every row lies in the partials buffer.
+  for (int i0 = 0; i0 < a.k; i0 += kCombineChunk) {
+    f32x4 v[kCombineChunk][kDownRowSlices];
 #pragma unroll
-    for (int r = 0; r < kDownRowSlices; ++r) s += P[r * slice + (size_t)(b * a.k + i) * n4 + c];
+    for (int j = 0; j < kCombineChunk; ++j) {
+      const size_t row = (size_t)b * a.k + min(i0 + j, a.k - 1);
+#pragma unroll
+      for (int r = 0; r < kDownRowSlices; ++r) v[j][r] = P[r * slice + row * n4 + c];
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j) {
+      const bool u = i0 + j < a.k && s_used[min(i0 + j, a.k - 1)];
+#pragma unroll
+      for (int r = 0; r < kDownRowSlices; ++r) s += u ? v[j][r] : zero;
+    }
   }
   for (int sh = 0; sh < a.NS; ++sh)
 #pragma unroll

@@ -303,6 +303,7 @@ __global__ __launch_bounds__(kWaves * 64) void tn_kernel(TnArgs a) {
 
 // y[b][r] = sum_i part[b*k + i][r], i in routing order, over the choices that were used
 // (choice_used: a skipped id's partial row was not written by this call).
+constexpr int kTnCombineChunk = 8;  // choices whose partial rows are loaded together
 __global__ __launch_bounds__(256) void tn_combine_kernel(const float* part, const int32_t* ids,
                                                          float* y, int B, int k, int I,
                                                          int E) {
@@ -311,9 +312,21 @@ __global__ __launch_bounds__(256) void tn_combine_kernel(const float* part, cons
        idx += (size_t)gridDim.x * blockDim.x) {
     const int b = (int)(idx / n4), c = (int)(idx % n4);
     const f32x4* P = reinterpret_cast<const f32x4*>(part);
-    f32x4 s = {0, 0, 0, 0};
-    for (int i = 0; i < k; ++i)
-      if (choice_used(ids + (size_t)b * k, i, E)) s += P[(size_t)(b * k + i) * n4 + c];
+    const f32x4 zero = {0, 0, 0, 0};
+    f32x4 s = zero;
+    // kTnCombineChunk rows loaded before any is added (rows past k clamped to row k - 1;
+    // rows of unused choices, which hold an earlier call's data, read and dropped)
+    for (int i0 = 0; i0 < k; i0 += kTnCombineChunk) {
+      f32x4 v[kTnCombineChunk];
+#pragma unroll
+      for (int j = 0; j < kTnCombineChunk; ++j)
+        v[j] = P[((size_t)b * k + min(i0 + j, k - 1)) * n4 + c];
+#pragma unroll
+      for (int j = 0; j < kTnCombineChunk; ++j) {
+        const bool u = i0 + j < k && choice_used(ids + (size_t)b * k, min(i0 + j, k - 1), E);
+        s += u ? v[j] : zero;
+      }
+    }
     reinterpret_cast<f32x4*>(y)[(size_t)b * n4 + c] = s;
   }
 }
