@@ -19,9 +19,10 @@ namespace {
 // Router GEMV for B tokens: one team (256 threads) per R router rows, held in registers;
 // each x chunk load serves the R rows (x is read from L2 once per R rows, not per row), and
 // R rows x TB tokens are reduced per LDS round.
-template <DT RT, int CPT, int R>
+template <DT RT, int CPT, int R, int TB>
 __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
-  constexpr int TB = 4, NP = R * TB;
+  constexpr int NP = R * TB;
+  static_assert(NP <= 16, "wave_multi_sum reduces at most 16 values");
   __shared__ float red[2][4][NP];
   const int t = threadIdx.x, lane = t & 63, wit = t >> 6;
   const int nch = a.H / 8;
@@ -255,13 +256,28 @@ template <DT RT, int R>
 hipError_t launch_gemv_r(const RouteArgs& a, hipStream_t s) {
   const int rows = (a.E + R - 1) / R;  // R router rows per workgroup pass
   const int grid = rows < 2048 ? rows : 2048;
+  // tokens per round: 4 for B <= 4, else 16 / max(R, CPT) (at least 4), so that a round's
+  // x loads (2 TB CPT 16-byte loads per thread) and R TB sums stay within 16 of each; 16
+  // tokens at H = 2048 and one row per workgroup are then one round (one x round trip and
+  // one LDS reduction instead of four)
+  const bool wide = a.B > 4;
+#define MOE_GEMV_CASE(C)                                                                   \
+  case C: {                                                                                \
+    constexpr int tbw = 16 / (R > C ? R : C) > 4 ? 16 / (R > C ? R : C) : 4;                \
+    if (wide)                                                                              \
+      hipLaunchKernelGGL((router_gemv_kernel<RT, C, R, tbw>), dim3(grid), dim3(256), 0, s, a); \
+    else                                                                                   \
+      hipLaunchKernelGGL((router_gemv_kernel<RT, C, R, 4>), dim3(grid), dim3(256), 0, s, a);   \
+    break;                                                                                 \
+  }
   switch (cpt_for(a.H)) {
-    case 1: hipLaunchKernelGGL((router_gemv_kernel<RT, 1, R>), dim3(grid), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((router_gemv_kernel<RT, 2, R>), dim3(grid), dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((router_gemv_kernel<RT, 4, R>), dim3(grid), dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((router_gemv_kernel<RT, 8, R>), dim3(grid), dim3(256), 0, s, a); break;
+    MOE_GEMV_CASE(1)
+    MOE_GEMV_CASE(2)
+    MOE_GEMV_CASE(4)
+    MOE_GEMV_CASE(8)
     default: return hipErrorInvalidValue;
   }
+#undef MOE_GEMV_CASE
   return hipGetLastError();
 }
 // Rows per workgroup: four where that still gives most CUs a workgroup (each x load then
